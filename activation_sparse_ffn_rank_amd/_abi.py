@@ -1,0 +1,152 @@
+"""ctypes binding of the C ABI in include/pi_sparse_ffn.h (argument marshalling only).
+
+Every step of the path runs in libpi.so's HIP kernels; this module only turns torch tensors
+into device pointers and the caller's current HIP stream into a ``hipStream_t``.  There is no
+fallback: if libpi.so is missing the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loaded first so libpi.so binds to the HIP runtime torch already uses
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpi.so")
+
+PI_OK, PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_DTYPE, PI_ERR_BATCH, PI_ERR_WORKSPACE, PI_ERR_ALIGN, PI_ERR_HIP = (
+    0, -1, -2, -3, -4, -5, -6, -7)
+PI_F16, PI_Q4_0 = 1, 2
+PI_MAX_BATCH = 8
+
+# Every function the header declares; the CPU tests check that libpi.so exports them all.
+EXPORTS = ("pi_workspace_bytes", "pi_predict", "pi_compact", "pi_sparse_ffn", "pi_ffn_layer",
+           "pi_status_string", "pi_version")
+
+
+class pi_predictor(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("d_ffn", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("p1", ctypes.c_void_p), ("p2", ctypes.c_void_p), ("c", ctypes.c_void_p)]
+
+
+class pi_ffn(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("d_ffn", ctypes.c_int32), ("gated", ctypes.c_int32),
+                ("wtype", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("slot_of", ctypes.c_void_p),
+                ("w_in", ctypes.c_void_p), ("w_down_t", ctypes.c_void_p), ("b_up", ctypes.c_void_p),
+                ("b_down", ctypes.c_void_p)]
+
+
+class PiError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} returned {code}: {pi_status_string(code)}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: the HIP library must be built "
+                               "(python -m activation_sparse_ffn_rank_amd.build); there is no fallback")
+        L = ctypes.CDLL(LIB_PATH)
+        P, vp, i32, sz = ctypes.POINTER, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        L.pi_workspace_bytes.restype = sz
+        L.pi_workspace_bytes.argtypes = [P(pi_predictor), P(pi_ffn), i32]
+        L.pi_predict.restype = ctypes.c_int
+        L.pi_predict.argtypes = [P(pi_predictor), vp, i32, vp, vp, vp, sz, vp]
+        L.pi_compact.restype = ctypes.c_int
+        L.pi_compact.argtypes = [vp, i32, vp, vp, vp, vp]
+        L.pi_sparse_ffn.restype = ctypes.c_int
+        L.pi_sparse_ffn.argtypes = [P(pi_ffn), vp, i32, vp, vp, vp, vp, sz, vp]
+        L.pi_ffn_layer.restype = ctypes.c_int
+        L.pi_ffn_layer.argtypes = [P(pi_predictor), P(pi_ffn), vp, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.pi_status_string.restype = ctypes.c_char_p
+        L.pi_status_string.argtypes = [ctypes.c_int]
+        L.pi_version.restype = ctypes.c_int
+        L.pi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+def _ptr(t) -> int | None:
+    """Device pointer of a tensor (None stays NULL; ints pass through as raw addresses)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _byref(s):
+    return None if s is None else ctypes.byref(s)
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != PI_OK:
+        raise PiError(fn, rc)
+
+
+def make_predictor(p1: torch.Tensor, p2: torch.Tensor, c: torch.Tensor) -> pi_predictor:
+    """Descriptor of a predictor from device tensors P1 [r][d], P2 [f][r], c [f] (fp16 storage)."""
+    r, d = p1.shape
+    f = p2.shape[0]
+    return pi_predictor(d, f, r, _ptr(p1), _ptr(p2), _ptr(c))
+
+
+def make_ffn(w_in: torch.Tensor, w_down_t: torch.Tensor, *, d_model: int, d_ffn: int, gated: bool, wtype: int,
+             slot_of: torch.Tensor | None = None, b_up: torch.Tensor | None = None,
+             b_down: torch.Tensor | None = None) -> pi_ffn:
+    """Descriptor of resident FFN weights (neuron-major rows, see the header)."""
+    return pi_ffn(d_model, d_ffn, int(gated), wtype, int(w_in.shape[0]), _ptr(slot_of), _ptr(w_in), _ptr(w_down_t),
+                  _ptr(b_up), _ptr(b_down))
+
+
+def pi_workspace_bytes(pred: pi_predictor | None, ffn: pi_ffn | None, batch: int) -> int:
+    return int(lib().pi_workspace_bytes(_byref(pred), _byref(ffn), batch))
+
+
+def pi_predict(pred, x, batch, mask, logits, ws, stream=None) -> None:
+    _check("pi_predict", lib().pi_predict(_byref(pred), _ptr(x), batch, _ptr(mask), _ptr(logits), _ptr(ws),
+                                          _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0,
+                                          _stream(stream)))
+
+
+def pi_compact(mask, d_ffn, slot_of, idx, counts, stream=None) -> None:
+    _check("pi_compact", lib().pi_compact(_ptr(mask), d_ffn, _ptr(slot_of), _ptr(idx), _ptr(counts),
+                                          _stream(stream)))
+
+
+def pi_sparse_ffn(ffn, x, batch, idx, counts, y, ws, stream=None) -> None:
+    _check("pi_sparse_ffn", lib().pi_sparse_ffn(_byref(ffn), _ptr(x), batch, _ptr(idx), _ptr(counts), _ptr(y),
+                                                _ptr(ws), _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0,
+                                                _stream(stream)))
+
+
+def pi_ffn_layer(pred, ffn, x, batch, y, mask_out, idx_out, counts_out, ws, stream=None) -> None:
+    _check("pi_ffn_layer", lib().pi_ffn_layer(_byref(pred), _byref(ffn), _ptr(x), batch, _ptr(y), _ptr(mask_out),
+                                              _ptr(idx_out), _ptr(counts_out), _ptr(ws),
+                                              _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0,
+                                              _stream(stream)))
+
+
+def pi_status_string(code: int) -> str:
+    return lib().pi_status_string(code).decode()
+
+
+def pi_version() -> int:
+    return int(lib().pi_version())

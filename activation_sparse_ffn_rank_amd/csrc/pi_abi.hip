@@ -1,0 +1,276 @@
+// pi_abi.hip -- host side of the C ABI declared in include/pi_sparse_ffn.h.
+//
+// Every entry point validates its arguments on the host before touching HIP, then enqueues
+// stream-ordered kernel launches on the caller's stream.  Nothing here allocates, frees,
+// synchronizes or issues memset/memcpy nodes, so the calls are safe inside HIP graph capture.
+// No C++ exception crosses the ABI.
+#include "pi_sparse_ffn.h"
+#include "pi_kernels.hpp"
+
+#include <algorithm>
+
+namespace {
+
+using namespace pik;
+
+constexpr size_t kAlign = 256;
+constexpr int kLdsXBytes = 64 * 1024;   // per-workgroup LDS budget for staged token vectors
+constexpr int kL2Rows = 8;              // predictor rows per wave in k_pred_l2
+constexpr int kUpMaxGroups = 512;       // workgroups of k_sparse_up
+constexpr int kDownTargetTiles = 512;   // (slab, chunk) tiles of k_sparse_down
+constexpr int kDownMaxChunks = 64;
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+int check_batch(int32_t B) { return (B >= 1 && B <= PI_MAX_BATCH) ? PI_OK : PI_ERR_BATCH; }
+
+int check_pred(const pi_predictor *p) {
+    if (!p) return PI_ERR_NULL;
+    if (!p->p1 || !p->p2 || !p->c) return PI_ERR_NULL;
+    if (p->d_model < 8 || p->d_model % 8 != 0 || p->d_ffn < 1 || p->rank < 8 || p->rank % 8 != 0 ||
+        p->rank > PI_MAX_RANK)
+        return PI_ERR_SHAPE;
+    if (!aligned16(p->p1) || !aligned16(p->p2)) return PI_ERR_ALIGN;
+    return PI_OK;
+}
+
+int64_t row_bytes_of(const pi_ffn *f) {
+    return f->wtype == PI_F16 ? 2 * (int64_t)f->d_model : (int64_t)f->d_model * 9 / 16;
+}
+
+int check_ffn(const pi_ffn *f) {
+    if (!f) return PI_ERR_NULL;
+    if (!f->w_in || !f->w_down_t) return PI_ERR_NULL;
+    if (f->wtype != PI_F16 && f->wtype != PI_Q4_0) return PI_ERR_DTYPE;
+    if (f->gated != 0 && f->gated != 1) return PI_ERR_DTYPE;
+    if (f->gated && f->wtype == PI_Q4_0) return PI_ERR_DTYPE;      // not a configuration of this library
+    if (f->gated && f->b_up) return PI_ERR_DTYPE;                  // the gated form has no up bias
+    if (f->d_ffn < 1 || f->n_slots < 0 || f->n_slots > f->d_ffn) return PI_ERR_SHAPE;
+    if (!f->slot_of && f->n_slots != f->d_ffn) return PI_ERR_SHAPE;
+    if (f->wtype == PI_F16 && (f->d_model < 8 || f->d_model % 8 != 0)) return PI_ERR_SHAPE;
+    if (f->wtype == PI_Q4_0 && (f->d_model < 256 || f->d_model % 256 != 0)) return PI_ERR_SHAPE;
+    if (!aligned16(f->w_in) || !aligned16(f->w_down_t)) return PI_ERR_ALIGN;
+    return PI_OK;
+}
+
+// Column chunk of staged token vectors: all of d when B*d fp16 fit the LDS budget.
+int x_chunk(int d, int B) {
+    const int fit = kLdsXBytes / (2 * B);
+    if (d <= fit) return d;
+    return std::max(512, fit / 512 * 512);
+}
+
+int down_slabs(int d) { return ceil_div(d, 512); }
+
+int down_chunks(int d) {
+    return std::min(kDownMaxChunks, std::max(1, ceil_div(kDownTargetTiles, down_slabs(d))));
+}
+
+size_t pred_ws(const pi_predictor *p, int B) { return align_up((size_t)B * p->rank * sizeof(float)); }
+
+size_t ffn_ws(const pi_ffn *f, int B) {
+    const size_t h = align_up((size_t)B * std::max(f->n_slots, 1) * sizeof(float));
+    const size_t part = align_up((size_t)down_chunks(f->d_model) * B * f->d_model * sizeof(float));
+    return h + part;
+}
+
+size_t layer_extra_ws(int f) {
+    return align_up((size_t)f) + align_up((size_t)f * sizeof(int32_t)) + align_up(2 * sizeof(int32_t));
+}
+
+int launch_status() { return hipGetLastError() == hipSuccess ? PI_OK : PI_ERR_HIP; }
+
+// ------------------------------------------------------------------ enqueue helpers
+
+template <int B>
+int enqueue_predict_b(const pi_predictor *p, const uint16_t *x, uint8_t *mask, float *logits, float *z,
+                      hipStream_t st) {
+    const int d = p->d_model, r = p->rank, f = p->d_ffn;
+    const int xch = x_chunk(d, B);
+    hipLaunchKernelGGL(k_pred_l1<B>, dim3(ceil_div(r, 4)), dim3(256), (size_t)B * xch * 2, st,
+                       static_cast<const uint16_t *>(p->p1), x, z, d, r, xch);
+    const int groups = ceil_div(f, 4 * kL2Rows);
+    const size_t lds = (size_t)B * r * sizeof(float);
+    const uint16_t *p2 = static_cast<const uint16_t *>(p->p2), *c = static_cast<const uint16_t *>(p->c);
+    if (r <= 512)
+        hipLaunchKernelGGL((k_pred_l2<B, 1, kL2Rows>), dim3(groups), dim3(256), lds, st, p2, c, z, r, f, logits, mask);
+    else if (r <= 1024)
+        hipLaunchKernelGGL((k_pred_l2<B, 2, kL2Rows>), dim3(groups), dim3(256), lds, st, p2, c, z, r, f, logits, mask);
+    else
+        hipLaunchKernelGGL((k_pred_l2<B, 4, kL2Rows>), dim3(groups), dim3(256), lds, st, p2, c, z, r, f, logits, mask);
+    return launch_status();
+}
+
+int enqueue_predict(const pi_predictor *p, const void *x, int B, uint8_t *mask, float *logits, float *z,
+                    hipStream_t st) {
+    const uint16_t *xx = static_cast<const uint16_t *>(x);
+    switch (B) {
+        case 1: return enqueue_predict_b<1>(p, xx, mask, logits, z, st);
+        case 2: return enqueue_predict_b<2>(p, xx, mask, logits, z, st);
+        case 3: return enqueue_predict_b<3>(p, xx, mask, logits, z, st);
+        case 4: return enqueue_predict_b<4>(p, xx, mask, logits, z, st);
+        case 5: return enqueue_predict_b<5>(p, xx, mask, logits, z, st);
+        case 6: return enqueue_predict_b<6>(p, xx, mask, logits, z, st);
+        case 7: return enqueue_predict_b<7>(p, xx, mask, logits, z, st);
+        case 8: return enqueue_predict_b<8>(p, xx, mask, logits, z, st);
+    }
+    return PI_ERR_BATCH;
+}
+
+int enqueue_compact(const uint8_t *mask, int f, const int32_t *slot_of, int32_t *idx, int32_t *counts,
+                    hipStream_t st) {
+    hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, mask, f, slot_of, idx, counts);
+    return launch_status();
+}
+
+template <int B, bool GATED, int WT>
+int enqueue_sparse_b(const pi_ffn *fn, const uint16_t *x, const int32_t *idx, const int32_t *counts, float *y,
+                     float *h, float *part, hipStream_t st) {
+    const int d = fn->d_model, f = fn->d_ffn, ns = fn->n_slots;
+    const int64_t rb = row_bytes_of(fn);
+    const int xch = x_chunk(d, B);
+    const int G = std::max(1, std::min(kUpMaxGroups, ceil_div(ns, 4)));
+    const int h_stride = std::max(ns, 1);
+    hipLaunchKernelGGL((k_sparse_up<B, GATED, WT>), dim3(G), dim3(256), (size_t)B * xch * 2, st,
+                       static_cast<const uint8_t *>(fn->w_in), rb, d, static_cast<const uint16_t *>(fn->b_up), x,
+                       idx, counts, fn->slot_of, f, ns, h, h_stride, xch);
+    const int C = down_chunks(d);
+    hipLaunchKernelGGL((k_sparse_down<B, WT>), dim3(down_slabs(d), C), dim3(256), 0, st,
+                       static_cast<const uint8_t *>(fn->w_down_t), rb, d, idx, counts, fn->slot_of, f, ns, h,
+                       h_stride, part, C);
+    const int Bd = B * d;
+    hipLaunchKernelGGL(k_reduce_y, dim3(ceil_div(Bd, 256)), dim3(256), 0, st, part, C, Bd, d,
+                       static_cast<const uint16_t *>(fn->b_down), y);
+    return launch_status();
+}
+
+template <int B>
+int enqueue_sparse_bt(const pi_ffn *fn, const uint16_t *x, const int32_t *idx, const int32_t *counts, float *y,
+                      float *h, float *part, hipStream_t st) {
+    if (fn->wtype == PI_Q4_0) return enqueue_sparse_b<B, false, WT_Q4_0>(fn, x, idx, counts, y, h, part, st);
+    if (fn->gated) return enqueue_sparse_b<B, true, WT_F16>(fn, x, idx, counts, y, h, part, st);
+    return enqueue_sparse_b<B, false, WT_F16>(fn, x, idx, counts, y, h, part, st);
+}
+
+int enqueue_sparse(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y,
+                   float *h, float *part, hipStream_t st) {
+    const uint16_t *xx = static_cast<const uint16_t *>(x);
+    switch (B) {
+        case 1: return enqueue_sparse_bt<1>(fn, xx, idx, counts, y, h, part, st);
+        case 2: return enqueue_sparse_bt<2>(fn, xx, idx, counts, y, h, part, st);
+        case 3: return enqueue_sparse_bt<3>(fn, xx, idx, counts, y, h, part, st);
+        case 4: return enqueue_sparse_bt<4>(fn, xx, idx, counts, y, h, part, st);
+        case 5: return enqueue_sparse_bt<5>(fn, xx, idx, counts, y, h, part, st);
+        case 6: return enqueue_sparse_bt<6>(fn, xx, idx, counts, y, h, part, st);
+        case 7: return enqueue_sparse_bt<7>(fn, xx, idx, counts, y, h, part, st);
+        case 8: return enqueue_sparse_bt<8>(fn, xx, idx, counts, y, h, part, st);
+    }
+    return PI_ERR_BATCH;
+}
+
+}  // namespace
+
+// ==================================================================== C ABI
+
+extern "C" {
+
+size_t pi_workspace_bytes(const pi_predictor *pred, const pi_ffn *ffn, int32_t batch) {
+    if (check_batch(batch) != PI_OK || (!pred && !ffn)) return 0;
+    if (pred && check_pred(pred) != PI_OK) return 0;
+    if (ffn && check_ffn(ffn) != PI_OK) return 0;
+    if (pred && ffn) {
+        if (pred->d_model != ffn->d_model || pred->d_ffn != ffn->d_ffn) return 0;
+        return pred_ws(pred, batch) + layer_extra_ws(pred->d_ffn) + ffn_ws(ffn, batch);
+    }
+    return pred ? pred_ws(pred, batch) : ffn_ws(ffn, batch);
+}
+
+int pi_predict(const pi_predictor *pred, const void *x, int32_t batch, uint8_t *mask, float *logits, void *ws,
+               size_t ws_bytes, void *stream) {
+    int rc = check_pred(pred);
+    if (rc) return rc;
+    if ((rc = check_batch(batch))) return rc;
+    if (!x || !mask) return PI_ERR_NULL;
+    if (!aligned16(x)) return PI_ERR_ALIGN;
+    if (!ws || ws_bytes < pred_ws(pred, batch)) return PI_ERR_WORKSPACE;
+    if (!aligned16(ws)) return PI_ERR_ALIGN;
+    return enqueue_predict(pred, x, batch, mask, logits, static_cast<float *>(ws), static_cast<hipStream_t>(stream));
+}
+
+int pi_compact(const uint8_t *mask, int32_t d_ffn, const int32_t *slot_of, int32_t *idx, int32_t *counts,
+               void *stream) {
+    if (!mask || !idx || !counts) return PI_ERR_NULL;
+    if (d_ffn < 1) return PI_ERR_SHAPE;
+    return enqueue_compact(mask, d_ffn, slot_of, idx, counts, static_cast<hipStream_t>(stream));
+}
+
+int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx, const int32_t *counts,
+                  float *y, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_ffn(ffn);
+    if (rc) return rc;
+    if ((rc = check_batch(batch))) return rc;
+    if (!x || !idx || !counts || !y) return PI_ERR_NULL;
+    if (!aligned16(x)) return PI_ERR_ALIGN;
+    if (!ws || ws_bytes < ffn_ws(ffn, batch)) return PI_ERR_WORKSPACE;
+    if (!aligned16(ws)) return PI_ERR_ALIGN;
+    char *base = static_cast<char *>(ws);
+    float *h = reinterpret_cast<float *>(base);
+    float *part = reinterpret_cast<float *>(base + align_up((size_t)batch * std::max(ffn->n_slots, 1) * sizeof(float)));
+    return enqueue_sparse(ffn, x, batch, idx, counts, y, h, part, static_cast<hipStream_t>(stream));
+}
+
+int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y,
+                 uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws, size_t ws_bytes,
+                 void *stream) {
+    int rc = check_pred(pred);
+    if (rc) return rc;
+    if ((rc = check_ffn(ffn))) return rc;
+    if ((rc = check_batch(batch))) return rc;
+    if (pred->d_model != ffn->d_model || pred->d_ffn != ffn->d_ffn) return PI_ERR_SHAPE;
+    if (!x || !y) return PI_ERR_NULL;
+    if (!aligned16(x)) return PI_ERR_ALIGN;
+    const size_t need = pi_workspace_bytes(pred, ffn, batch);
+    if (!ws || ws_bytes < need) return PI_ERR_WORKSPACE;
+    if (!aligned16(ws)) return PI_ERR_ALIGN;
+    const int f = pred->d_ffn;
+    char *p = static_cast<char *>(ws);
+    float *z = reinterpret_cast<float *>(p);
+    p += pred_ws(pred, batch);
+    uint8_t *mask = reinterpret_cast<uint8_t *>(p);
+    p += align_up((size_t)f);
+    int32_t *idx = reinterpret_cast<int32_t *>(p);
+    p += align_up((size_t)f * sizeof(int32_t));
+    int32_t *counts = reinterpret_cast<int32_t *>(p);
+    p += align_up(2 * sizeof(int32_t));
+    float *h = reinterpret_cast<float *>(p);
+    float *part = reinterpret_cast<float *>(p + align_up((size_t)batch * std::max(ffn->n_slots, 1) * sizeof(float)));
+    if (mask_out) mask = mask_out;
+    if (idx_out) idx = idx_out;
+    if (counts_out) counts = counts_out;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if ((rc = enqueue_predict(pred, x, batch, mask, nullptr, z, st))) return rc;
+    if ((rc = enqueue_compact(mask, f, ffn->slot_of, idx, counts, st))) return rc;
+    return enqueue_sparse(ffn, x, batch, idx, counts, y, h, part, st);
+}
+
+const char *pi_status_string(int status) {
+    switch (status) {
+        case PI_OK: return "ok";
+        case PI_ERR_NULL: return "a required pointer is NULL";
+        case PI_ERR_SHAPE: return "a size is out of range or inconsistent";
+        case PI_ERR_DTYPE: return "unsupported weight kind or gating combination";
+        case PI_ERR_BATCH: return "batch outside [1, 8]";
+        case PI_ERR_WORKSPACE: return "workspace missing or too small";
+        case PI_ERR_ALIGN: return "pointer or row not 16-byte aligned";
+        case PI_ERR_HIP: return "HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+int pi_version(void) { return 100; }
+
+}  // extern "C"

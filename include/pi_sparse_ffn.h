@@ -1,0 +1,133 @@
+/*
+ * pi_sparse_ffn.h -- C ABI of the predictor-gated, neuron-aware sparse FFN for MI355X (gfx950).
+ *
+ * The operation (PowerInfer: Fast Large Language Model Serving with a Consumer-grade GPU,
+ * arXiv 2312.12456 -- abstract, and the "method" and "key results" sections of the summary
+ * page): in a ReLU-family FFN only a small, input-dependent set of neurons fires for a token.
+ * A small predictor decides which ones will fire; a neuron-aware sparse operator then reads
+ * and computes only those neurons; a GPU placement index (the ".gpuidx" file of the project
+ * README's model-weights section) names the neurons whose weights are resident on the device,
+ * and the device computes only predicted neurons that are resident.  The README's FAQ lists
+ * ReLU / ReGLU activations and its quantization section Q4_0 INT4 weights.
+ *
+ * For tokens x_b (b < batch), with d = d_model, f = d_ffn, r = rank:
+ *   z_b  = max(0, P1 x_b)                       P1 [r][d]
+ *   l_b  = P2 z_b + c                           P2 [f][r], c [f]
+ *   M    = { i : l_b,i > 0 for some b }         strict threshold, union over the batch
+ *   M'   = { i in M : slot_of[i] >= 0 }         (all of M when slot_of is NULL)
+ *   idx  = members of M' in ascending order, n = |M'|
+ *   h_bk = max(0, W_up[s] x_b + b_up[s])                 gated == 0
+ *        = max(0, W_gate[s] x_b) * (W_up[s] x_b)         gated == 1      s = slot of idx[k]
+ *   y_b  = b_down + sum_k h_bk W_down^T[s]
+ *
+ * Conventions for every entry point:
+ *  - All pointers are DEVICE memory owned by the caller (e.g. torch tensors' data_ptr()),
+ *    except the descriptor structs themselves, which are host memory read during the call.
+ *    The library never allocates or frees; scratch comes from the caller's workspace `ws`
+ *    of `ws_bytes` bytes, which must stay alive and unused by others until the enqueued
+ *    work has finished.
+ *  - Calls only enqueue work on `stream` (a hipStream_t; NULL = the default stream) and never
+ *    synchronize.  Device-side counts stay on the device.  The enqueued kernels contain no
+ *    memset nodes, so the calls may be captured into a HIP graph.
+ *  - A nonzero return means nothing was enqueued (argument errors are detected on the host
+ *    before any HIP call), except PI_ERR_HIP, which reports a launch failure.
+ *  - fp16 is IEEE binary16.  y is fp32.  Accumulation is fp32.
+ *  - Layout: weights are neuron-major -- row s of w_in holds the input weights of the neuron
+ *    in slot s (gate row then up row when gated), row s of w_down_t holds its output
+ *    weights -- so each active neuron is one contiguous read.
+ *  - Q4_0 rows (32-weight blocks, one fp16 scale per block) of d weights are d/2 code bytes
+ *    (byte j: weight 2j in the low nibble, weight 2j+1 in the high nibble; weight value
+ *    scale*(code-8)) followed by d/32 fp16 scales: 9d/16 bytes per row.
+ *  - Alignment: p1, p2, x, w_in, w_down_t must be 16-byte aligned.  Shapes: 1 <= batch <= 8,
+ *    d_model % 8 == 0 (fp16) or d_model % 256 == 0 (Q4_0), rank % 8 == 0 and rank <= 2048,
+ *    d_ffn >= 1, 0 <= n_slots <= d_ffn.
+ */
+#ifndef PI_SPARSE_FFN_H
+#define PI_SPARSE_FFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PI_OK = 0,
+    PI_ERR_NULL = -1,       /* a required pointer is NULL */
+    PI_ERR_SHAPE = -2,      /* a size is out of range or inconsistent */
+    PI_ERR_DTYPE = -3,      /* unsupported weight kind or kind/gating combination */
+    PI_ERR_BATCH = -4,      /* batch outside [1, PI_MAX_BATCH] */
+    PI_ERR_WORKSPACE = -5,  /* ws NULL or ws_bytes < pi_workspace_bytes(...) */
+    PI_ERR_ALIGN = -6,      /* a pointer or row is not 16-byte aligned */
+    PI_ERR_HIP = -7         /* a HIP launch failed */
+} pi_status;
+
+typedef enum { PI_F16 = 1, PI_Q4_0 = 2 } pi_wtype;
+
+#define PI_MAX_BATCH 8
+#define PI_MAX_RANK 2048
+
+/* Low-rank predictor of one layer (the "adaptive predictor" of the method section; its shape
+ * -- a rank-r ReLU MLP with a per-neuron offset on the logits -- is this library's reading). */
+typedef struct pi_predictor {
+    int32_t d_model, d_ffn, rank;
+    const void *p1;   /* [rank][d_model] fp16, row-major */
+    const void *p2;   /* [d_ffn][rank]   fp16, row-major */
+    const void *c;    /* [d_ffn]         fp16 per-neuron logit offset */
+} pi_predictor;
+
+/* Resident FFN weights of one layer. */
+typedef struct pi_ffn {
+    int32_t d_model, d_ffn;
+    int32_t gated;             /* 0: ReLU(W_up x + b_up); 1: ReLU(W_gate x) * (W_up x) (ReGLU) */
+    int32_t wtype;             /* pi_wtype */
+    int32_t n_slots;           /* resident rows; must equal d_ffn when slot_of is NULL */
+    const int32_t *slot_of;    /* [d_ffn] slot of neuron i, -1 = not resident; NULL = identity */
+    const void *w_in;          /* [n_slots][gated ? 2 : 1][row] */
+    const void *w_down_t;      /* [n_slots][row] */
+    const void *b_up;          /* [n_slots] fp16, or NULL; must be NULL when gated */
+    const void *b_down;        /* [d_model] fp16, or NULL */
+} pi_ffn;
+
+/* Bytes of workspace the calls below need for this layer and batch (either descriptor may be
+ * NULL when only the other one's calls are used).  0 on invalid arguments. */
+size_t pi_workspace_bytes(const pi_predictor *pred, const pi_ffn *ffn, int32_t batch);
+
+/* Predictor (method section: online prediction of the neurons that fire).
+ * x [batch][d_model] fp16.  mask [d_ffn] u8 receives the batch union {0,1}.  logits
+ * [batch][d_ffn] fp32 receives l_b when non-NULL.  Uses the workspace for z. */
+int pi_predict(const pi_predictor *pred, const void *x, int32_t batch, uint8_t *mask,
+               float *logits, void *ws, size_t ws_bytes, void *stream);
+
+/* Placement restriction and compaction (README: GPU index of resident neurons).
+ * mask [d_ffn] u8 (nonzero = predicted); slot_of [d_ffn] or NULL.  idx [d_ffn] receives the
+ * ascending ids of predicted resident neurons (the first n entries are valid);
+ * counts [2] receives {n, number predicted}.  Single kernel, no workspace. */
+int pi_compact(const uint8_t *mask, int32_t d_ffn, const int32_t *slot_of, int32_t *idx,
+               int32_t *counts, void *stream);
+
+/* Neuron-aware sparse FFN over idx[0..counts[0]) (method section: sparse operators that
+ * compute only the active neurons).  idx and counts are device memory (as pi_compact writes
+ * them); n is clamped to [0, n_slots] and entries whose neuron or slot is out of range are
+ * skipped.  y [batch][d_model] fp32 is overwritten. */
+int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx,
+                  const int32_t *counts, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* Whole layer: pi_predict -> pi_compact -> pi_sparse_ffn.  pred and ffn must agree on
+ * d_model and d_ffn.  mask_out [d_ffn], idx_out [d_ffn] and counts_out [2] receive the
+ * intermediate results when non-NULL (otherwise they live in the workspace). */
+int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch,
+                 float *y, uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws,
+                 size_t ws_bytes, void *stream);
+
+/* Human-readable name of a pi_status value (static storage). */
+const char *pi_status_string(int status);
+
+/* ABI version of this header (major*100 + minor). */
+int pi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PI_SPARSE_FFN_H */

@@ -1,0 +1,115 @@
+"""C ABI checks that need no GPU: libpi.so loads, exports every function include/pi_sparse_ffn.h
+declares, and rejects bad arguments on the host with the documented codes before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from activation_sparse_ffn_rank_amd import _abi, build
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pi_sparse_ffn.h")
+
+A = 0x10000          # fake, 16-byte aligned device addresses: host validation never dereferences them
+U = 0x10008          # 8-byte aligned only
+
+
+@pytest.fixture(scope="module")
+def L():
+    if build.is_stale():
+        build.build()
+    return _abi.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pi_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(L):
+    names = declared_functions()
+    assert set(names) == set(_abi.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.pi_version() == 100
+
+
+def pred(d=1024, f=4096, r=128, p1=A, p2=A, c=A):
+    return _abi.pi_predictor(d, f, r, p1, p2, c)
+
+
+def ffn(d=1024, f=4096, gated=0, wtype=_abi.PI_F16, n_slots=None, slot_of=None, w_in=A, w_dn=A, b_up=None, b_down=None):
+    return _abi.pi_ffn(d, f, gated, wtype, f if n_slots is None else n_slots, slot_of, w_in, w_dn, b_up, b_down)
+
+
+def ws_for(L, p, f, B):
+    return L.pi_workspace_bytes(ctypes.byref(p) if p else None, ctypes.byref(f) if f else None, B)
+
+
+def test_workspace_sizes(L):
+    p, f = pred(), ffn()
+    both, only_p, only_f = ws_for(L, p, f, 1), ws_for(L, p, None, 1), ws_for(L, None, f, 1)
+    assert only_p > 0 and only_f > 0 and both >= only_p + only_f
+    assert ws_for(L, p, f, 8) > both
+    assert ws_for(L, p, f, 0) == 0 and ws_for(L, p, f, 9) == 0 and ws_for(L, None, None, 1) == 0
+    assert ws_for(L, pred(d=512), f, 1) == 0                      # d_model mismatch
+
+
+def test_predict_rejects(L):
+    p = pred()
+    big = ws_for(L, p, None, 1)
+    call = lambda pp, x=A, B=1, mask=A, ws=A, n=big: L.pi_predict(pp, x, B, mask, None, ws, n, None)
+    assert call(None) == _abi.PI_ERR_NULL
+    assert call(ctypes.byref(pred(p1=0))) == _abi.PI_ERR_NULL
+    assert call(ctypes.byref(p), x=0) == _abi.PI_ERR_NULL
+    assert call(ctypes.byref(p), mask=0) == _abi.PI_ERR_NULL
+    assert call(ctypes.byref(p), B=0) == _abi.PI_ERR_BATCH
+    assert call(ctypes.byref(p), B=9) == _abi.PI_ERR_BATCH
+    assert call(ctypes.byref(pred(r=100))) == _abi.PI_ERR_SHAPE       # rank % 8
+    assert call(ctypes.byref(pred(r=4096))) == _abi.PI_ERR_SHAPE      # rank > 2048
+    assert call(ctypes.byref(pred(d=1020))) == _abi.PI_ERR_SHAPE
+    assert call(ctypes.byref(pred(p1=U))) == _abi.PI_ERR_ALIGN
+    assert call(ctypes.byref(p), x=U) == _abi.PI_ERR_ALIGN
+    assert call(ctypes.byref(p), ws=0) == _abi.PI_ERR_WORKSPACE
+    assert call(ctypes.byref(p), n=big - 1) == _abi.PI_ERR_WORKSPACE
+
+
+def test_compact_rejects(L):
+    assert L.pi_compact(None, 10, None, A, A, None) == _abi.PI_ERR_NULL
+    assert L.pi_compact(A, 10, None, None, A, None) == _abi.PI_ERR_NULL
+    assert L.pi_compact(A, 0, None, A, A, None) == _abi.PI_ERR_SHAPE
+
+
+def test_sparse_ffn_rejects(L):
+    f = ffn()
+    big = ws_for(L, None, f, 1)
+    call = lambda ff, x=A, B=1, ws=A, n=big: L.pi_sparse_ffn(ff, x, B, A, A, A, ws, n, None)
+    assert call(None) == _abi.PI_ERR_NULL
+    assert call(ctypes.byref(ffn(w_in=0))) == _abi.PI_ERR_NULL
+    assert call(ctypes.byref(ffn(wtype=3))) == _abi.PI_ERR_DTYPE
+    assert call(ctypes.byref(ffn(gated=1, wtype=_abi.PI_Q4_0))) == _abi.PI_ERR_DTYPE
+    assert call(ctypes.byref(ffn(gated=1, b_up=A))) == _abi.PI_ERR_DTYPE
+    assert call(ctypes.byref(ffn(d=1000, wtype=_abi.PI_Q4_0))) == _abi.PI_ERR_SHAPE   # Q4_0 needs d % 256
+    assert call(ctypes.byref(ffn(n_slots=100))) == _abi.PI_ERR_SHAPE                  # slot_of NULL: n_slots == f
+    assert call(ctypes.byref(ffn(n_slots=5000, slot_of=A))) == _abi.PI_ERR_SHAPE      # n_slots > f
+    assert call(ctypes.byref(ffn(w_dn=U))) == _abi.PI_ERR_ALIGN
+    assert call(ctypes.byref(f), B=9) == _abi.PI_ERR_BATCH
+    assert call(ctypes.byref(f), n=big - 1) == _abi.PI_ERR_WORKSPACE
+
+
+def test_layer_rejects(L):
+    p, f = pred(), ffn()
+    big = ws_for(L, p, f, 2)
+    call = lambda pp, ff, B=2, n=big: L.pi_ffn_layer(pp, ff, A, B, A, None, None, None, A, n, None)
+    assert call(ctypes.byref(p), None) == _abi.PI_ERR_NULL
+    assert call(ctypes.byref(pred(f=4000)), ctypes.byref(f)) == _abi.PI_ERR_SHAPE
+    assert call(ctypes.byref(p), ctypes.byref(f), n=big - 1) == _abi.PI_ERR_WORKSPACE
+    assert call(ctypes.byref(p), ctypes.byref(f), B=0) == _abi.PI_ERR_BATCH
+
+
+def test_status_strings(L):
+    for code in range(0, -8, -1):
+        s = _abi.pi_status_string(code)
+        assert s and s != "unknown status"
+    assert _abi.pi_status_string(5) == "unknown status"
