@@ -15,10 +15,8 @@ using namespace pik;
 
 constexpr size_t kAlign = 256;
 constexpr int kLdsXBytes = 64 * 1024;   // per-workgroup LDS budget for staged token vectors
-constexpr int kL2Rows = 8;              // predictor rows per wave in k_pred_l2
 constexpr int kUpMaxGroups = 512;       // workgroups of k_sparse_up
-constexpr int kDownTargetTiles = 512;   // (slab, chunk) tiles of k_sparse_down
-constexpr int kDownMaxChunks = 64;
+constexpr int kDownTargetTiles = 384;   // (slab, chunk) tiles of k_sparse_down
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -72,10 +70,28 @@ int down_chunks(int d) {
 
 size_t pred_ws(const pi_predictor *p, int B) { return align_up((size_t)B * p->rank * sizeof(float)); }
 
+// Sparse-FFN scratch: h [B][max(n_slots,1)] fp32, chunk partials [C][B][d] fp32, slab tickets.
+struct FfnScratch {
+    float *h;
+    float *part;
+    int32_t *tickets;
+};
+
+size_t ffn_h_bytes(const pi_ffn *f, int B) { return align_up((size_t)B * std::max(f->n_slots, 1) * sizeof(float)); }
+size_t ffn_part_bytes(const pi_ffn *f, int B) {
+    return align_up((size_t)down_chunks(f->d_model) * B * f->d_model * sizeof(float));
+}
 size_t ffn_ws(const pi_ffn *f, int B) {
-    const size_t h = align_up((size_t)B * std::max(f->n_slots, 1) * sizeof(float));
-    const size_t part = align_up((size_t)down_chunks(f->d_model) * B * f->d_model * sizeof(float));
-    return h + part;
+    return ffn_h_bytes(f, B) + ffn_part_bytes(f, B) + align_up((size_t)down_slabs(f->d_model) * sizeof(int32_t));
+}
+
+FfnScratch ffn_scratch(const pi_ffn *f, int B, void *base) {
+    char *p = static_cast<char *>(base);
+    FfnScratch s;
+    s.h = reinterpret_cast<float *>(p);
+    s.part = reinterpret_cast<float *>(p + ffn_h_bytes(f, B));
+    s.tickets = reinterpret_cast<int32_t *>(p + ffn_h_bytes(f, B) + ffn_part_bytes(f, B));
+    return s;
 }
 
 size_t layer_extra_ws(int f) {
@@ -90,18 +106,16 @@ template <int B>
 int enqueue_predict_b(const pi_predictor *p, const uint16_t *x, uint8_t *mask, float *logits, float *z,
                       hipStream_t st) {
     const int d = p->d_model, r = p->rank, f = p->d_ffn;
-    const int xch = x_chunk(d, B);
-    hipLaunchKernelGGL(k_pred_l1<B>, dim3(ceil_div(r, 4)), dim3(256), (size_t)B * xch * 2, st,
-                       static_cast<const uint16_t *>(p->p1), x, z, d, r, xch);
-    const int groups = ceil_div(f, 4 * kL2Rows);
-    const size_t lds = (size_t)B * r * sizeof(float);
+    hipLaunchKernelGGL(k_pred_l1<B>, dim3(r), dim3(256), 0, st, static_cast<const uint16_t *>(p->p1), x, z, d, r);
+    constexpr int R = 8;                               // predictor rows per wave
+    const int groups = ceil_div(f, 4 * R);
     const uint16_t *p2 = static_cast<const uint16_t *>(p->p2), *c = static_cast<const uint16_t *>(p->c);
     if (r <= 512)
-        hipLaunchKernelGGL((k_pred_l2<B, 1, kL2Rows>), dim3(groups), dim3(256), lds, st, p2, c, z, r, f, logits, mask);
+        hipLaunchKernelGGL((k_pred_l2<B, 1, R>), dim3(groups), dim3(256), 0, st, p2, c, z, r, f, logits, mask);
     else if (r <= 1024)
-        hipLaunchKernelGGL((k_pred_l2<B, 2, kL2Rows>), dim3(groups), dim3(256), lds, st, p2, c, z, r, f, logits, mask);
+        hipLaunchKernelGGL((k_pred_l2<B, 2, R>), dim3(groups), dim3(256), 0, st, p2, c, z, r, f, logits, mask);
     else
-        hipLaunchKernelGGL((k_pred_l2<B, 4, kL2Rows>), dim3(groups), dim3(256), lds, st, p2, c, z, r, f, logits, mask);
+        hipLaunchKernelGGL((k_pred_l2<B, 4, R>), dim3(groups), dim3(256), 0, st, p2, c, z, r, f, logits, mask);
     return launch_status();
 }
 
@@ -129,45 +143,42 @@ int enqueue_compact(const uint8_t *mask, int f, const int32_t *slot_of, int32_t 
 
 template <int B, bool GATED, int WT>
 int enqueue_sparse_b(const pi_ffn *fn, const uint16_t *x, const int32_t *idx, const int32_t *counts, float *y,
-                     float *h, float *part, hipStream_t st) {
+                     const FfnScratch &sc, hipStream_t st) {
     const int d = fn->d_model, f = fn->d_ffn, ns = fn->n_slots;
     const int64_t rb = row_bytes_of(fn);
     const int xch = x_chunk(d, B);
-    const int G = std::max(1, std::min(kUpMaxGroups, ceil_div(ns, 4)));
+    const int G = std::max(1, std::min(kUpMaxGroups, ceil_div(ns, 8)));
     const int h_stride = std::max(ns, 1);
+    const int slabs = down_slabs(d), C = down_chunks(d);
     hipLaunchKernelGGL((k_sparse_up<B, GATED, WT>), dim3(G), dim3(256), (size_t)B * xch * 2, st,
                        static_cast<const uint8_t *>(fn->w_in), rb, d, static_cast<const uint16_t *>(fn->b_up), x,
-                       idx, counts, fn->slot_of, f, ns, h, h_stride, xch);
-    const int C = down_chunks(d);
-    hipLaunchKernelGGL((k_sparse_down<B, WT>), dim3(down_slabs(d), C), dim3(256), 0, st,
-                       static_cast<const uint8_t *>(fn->w_down_t), rb, d, idx, counts, fn->slot_of, f, ns, h,
-                       h_stride, part, C);
-    const int Bd = B * d;
-    hipLaunchKernelGGL(k_reduce_y, dim3(ceil_div(Bd, 256)), dim3(256), 0, st, part, C, Bd, d,
-                       static_cast<const uint16_t *>(fn->b_down), y);
+                       idx, counts, fn->slot_of, f, ns, sc.h, h_stride, xch, sc.tickets, slabs);
+    hipLaunchKernelGGL((k_sparse_down<B, WT>), dim3(slabs, C), dim3(256), 0, st,
+                       static_cast<const uint8_t *>(fn->w_down_t), rb, d, idx, counts, fn->slot_of, f, ns, sc.h,
+                       h_stride, sc.part, C, sc.tickets, static_cast<const uint16_t *>(fn->b_down), y);
     return launch_status();
 }
 
 template <int B>
 int enqueue_sparse_bt(const pi_ffn *fn, const uint16_t *x, const int32_t *idx, const int32_t *counts, float *y,
-                      float *h, float *part, hipStream_t st) {
-    if (fn->wtype == PI_Q4_0) return enqueue_sparse_b<B, false, WT_Q4_0>(fn, x, idx, counts, y, h, part, st);
-    if (fn->gated) return enqueue_sparse_b<B, true, WT_F16>(fn, x, idx, counts, y, h, part, st);
-    return enqueue_sparse_b<B, false, WT_F16>(fn, x, idx, counts, y, h, part, st);
+                      const FfnScratch &sc, hipStream_t st) {
+    if (fn->wtype == PI_Q4_0) return enqueue_sparse_b<B, false, WT_Q4_0>(fn, x, idx, counts, y, sc, st);
+    if (fn->gated) return enqueue_sparse_b<B, true, WT_F16>(fn, x, idx, counts, y, sc, st);
+    return enqueue_sparse_b<B, false, WT_F16>(fn, x, idx, counts, y, sc, st);
 }
 
 int enqueue_sparse(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y,
-                   float *h, float *part, hipStream_t st) {
+                   const FfnScratch &sc, hipStream_t st) {
     const uint16_t *xx = static_cast<const uint16_t *>(x);
     switch (B) {
-        case 1: return enqueue_sparse_bt<1>(fn, xx, idx, counts, y, h, part, st);
-        case 2: return enqueue_sparse_bt<2>(fn, xx, idx, counts, y, h, part, st);
-        case 3: return enqueue_sparse_bt<3>(fn, xx, idx, counts, y, h, part, st);
-        case 4: return enqueue_sparse_bt<4>(fn, xx, idx, counts, y, h, part, st);
-        case 5: return enqueue_sparse_bt<5>(fn, xx, idx, counts, y, h, part, st);
-        case 6: return enqueue_sparse_bt<6>(fn, xx, idx, counts, y, h, part, st);
-        case 7: return enqueue_sparse_bt<7>(fn, xx, idx, counts, y, h, part, st);
-        case 8: return enqueue_sparse_bt<8>(fn, xx, idx, counts, y, h, part, st);
+        case 1: return enqueue_sparse_bt<1>(fn, xx, idx, counts, y, sc, st);
+        case 2: return enqueue_sparse_bt<2>(fn, xx, idx, counts, y, sc, st);
+        case 3: return enqueue_sparse_bt<3>(fn, xx, idx, counts, y, sc, st);
+        case 4: return enqueue_sparse_bt<4>(fn, xx, idx, counts, y, sc, st);
+        case 5: return enqueue_sparse_bt<5>(fn, xx, idx, counts, y, sc, st);
+        case 6: return enqueue_sparse_bt<6>(fn, xx, idx, counts, y, sc, st);
+        case 7: return enqueue_sparse_bt<7>(fn, xx, idx, counts, y, sc, st);
+        case 8: return enqueue_sparse_bt<8>(fn, xx, idx, counts, y, sc, st);
     }
     return PI_ERR_BATCH;
 }
@@ -217,10 +228,7 @@ int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t
     if (!aligned16(x)) return PI_ERR_ALIGN;
     if (!ws || ws_bytes < ffn_ws(ffn, batch)) return PI_ERR_WORKSPACE;
     if (!aligned16(ws)) return PI_ERR_ALIGN;
-    char *base = static_cast<char *>(ws);
-    float *h = reinterpret_cast<float *>(base);
-    float *part = reinterpret_cast<float *>(base + align_up((size_t)batch * std::max(ffn->n_slots, 1) * sizeof(float)));
-    return enqueue_sparse(ffn, x, batch, idx, counts, y, h, part, static_cast<hipStream_t>(stream));
+    return enqueue_sparse(ffn, x, batch, idx, counts, y, ffn_scratch(ffn, batch, ws), static_cast<hipStream_t>(stream));
 }
 
 int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y,
@@ -246,15 +254,14 @@ int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int
     p += align_up((size_t)f * sizeof(int32_t));
     int32_t *counts = reinterpret_cast<int32_t *>(p);
     p += align_up(2 * sizeof(int32_t));
-    float *h = reinterpret_cast<float *>(p);
-    float *part = reinterpret_cast<float *>(p + align_up((size_t)batch * std::max(ffn->n_slots, 1) * sizeof(float)));
+    const FfnScratch sc = ffn_scratch(ffn, batch, p);
     if (mask_out) mask = mask_out;
     if (idx_out) idx = idx_out;
     if (counts_out) counts = counts_out;
     hipStream_t st = static_cast<hipStream_t>(stream);
     if ((rc = enqueue_predict(pred, x, batch, mask, nullptr, z, st))) return rc;
     if ((rc = enqueue_compact(mask, f, ffn->slot_of, idx, counts, st))) return rc;
-    return enqueue_sparse(ffn, x, batch, idx, counts, y, h, part, st);
+    return enqueue_sparse(ffn, x, batch, idx, counts, y, sc, st);
 }
 
 const char *pi_status_string(int status) {

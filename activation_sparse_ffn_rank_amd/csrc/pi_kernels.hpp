@@ -3,19 +3,21 @@
 // The method (PowerInfer, arXiv 2312.12456: abstract; "method" section of the summary page):
 // a low-rank predictor picks the FFN neurons that will fire for the current token(s), and a
 // neuron-aware operator reads and computes only those neurons; a GPU index of resident neurons
-// restricts the device to the neurons it holds.  At batch 1 every step is a GEMV whose weights
-// are read exactly once, so the whole path is HBM-bound: the kernels are built around wide,
-// coalesced 16-byte row reads with many loads in flight per wave, token vectors staged in LDS,
-// fp16 products accumulated in fp32 with v_dot2, wavefront reductions, and no MFMA (there is no
-// dense contraction to feed it at batch <= 8).
+// restricts the device to the neurons it holds.  At batch <= 8 every step is a GEMV whose weights
+// are read exactly once, so the path is HBM-bound and, at these sizes (a few MB to ~100 MB per
+// kernel), bound just as much by how many serialized memory round trips a wave makes.  The
+// kernels therefore issue every weight load a wave needs before anything else, overlap LDS
+// staging of the token vectors with those loads, fetch per-neuron metadata with one lane per
+// neuron, and accumulate fp16 products in fp32 with v_dot2.  No MFMA: there is no dense
+// contraction to feed it at batch <= 8.
 //
-// Kernels (one launch each, all stream-ordered, none needs a host sync):
-//   k_pred_l1     z = max(0, P1 x)                 one wave per row of P1, x in LDS
-//   k_pred_l2     l = P2 z + c, mask = OR_b [l > 0] several rows per wave, z in LDS
+// Kernels (all stream-ordered; none needs a host sync):
+//   k_pred_l1     z = max(0, P1 x)                   one workgroup per row of P1
+//   k_pred_l2     l = P2 z + c, mask = OR_b [l > 0]  R rows per wave, reduce-scatter sums
 //   k_compact     idx = ascending {i : mask_i, slot_of_i >= 0}, counts = {n, n_pred}
-//   k_sparse_up   h = ReLU(W_in[s] x + b) or ReLU(W_g x)(W_u x) for the active rows
-//   k_sparse_down partial y over (column slab, neuron chunk) tiles, fp32, waves reduced in LDS
-//   k_reduce_y    y = b_down + sum of the chunk partials (fixed order: deterministic)
+//   k_sparse_up   h = ReLU(W_in[s] x + b) or ReLU(W_g x)(W_u x) over the listed neurons
+//   k_sparse_down y over (512-column slab, neuron chunk) tiles; waves reduced in LDS, chunks
+//                 reduced by the last-arriving workgroup of each slab in fixed order
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,6 +26,7 @@
 namespace pik {
 
 constexpr int kWave = 64;
+constexpr int kDownMaxChunks = 32;   // chunk partials per slab summed by the last workgroup
 
 typedef _Float16 f16;
 typedef f16 h2 __attribute__((ext_vector_type(2)));
@@ -33,6 +36,8 @@ enum { WT_F16 = 1, WT_Q4_0 = 2 };
 // ------------------------------------------------------------------------------ helpers
 
 __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+__device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
 __device__ __forceinline__ float half_to_float(uint16_t b) { return (float)__builtin_bit_cast(f16, b); }
 
@@ -54,10 +59,34 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__device__ __forceinline__ int wave_sum_int(int v) {
+// Broadcast lane j's value (j wave-uniform) through a scalar register.
+__device__ __forceinline__ int bcast(int v, int j) { return __builtin_amdgcn_readlane(v, j); }
+__device__ __forceinline__ float bcastf(float v, int j) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), j));
+}
+
+// Sum N per-lane values over the wave, leaving the total of value j in every lane l with
+// j = l / (64/N) (so lanes 0, 64/N, 2*64/N, ... hold values 0, 1, 2, ...).  A reduce-scatter:
+// each xor step halves the values a lane carries, then the 64/N lanes that share a value
+// finish with plain xor steps -- log2(N) + N - 1 + log2(64/N) shuffles instead of 6N.
+template <int N>
+__device__ __forceinline__ float reduce_scatter(float (&v)[N], int lane) {
+    static_assert(N == 2 || N == 4 || N == 8 || N == 16, "N");
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    for (int lvl = 0; (N >> (lvl + 1)) >= 1; ++lvl) {
+        const int m = 32 >> lvl, half = N >> (lvl + 1);
+        const bool hi = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const float send = hi ? v[i] : v[i + half];
+            const float keep = hi ? v[i + half] : v[i];
+            v[i] = keep + __shfl_xor(send, m, kWave);
+        }
+    }
+    float t = v[0];
+#pragma unroll
+    for (int m = 32 / N; m >= 1; m >>= 1) t += __shfl_xor(t, m, kWave);
+    return t;
 }
 
 // Q4_0 codes: a 32-bit code word holds 8 consecutive weights, weight t in bits [4t, 4t+4).
@@ -80,6 +109,21 @@ __device__ __forceinline__ uint4 pair_for_q4(const uint4 &v) {
     return o;
 }
 
+// Dot of one Q4_0 block (16 code bytes) with 32 staged x values (q4-paired order), times scale.
+__device__ __forceinline__ float q4_block_dot(const uint4 &codes, const uint16_t *xq, float acc, float scale) {
+    const uint32_t wd[4] = {codes.x, codes.y, codes.z, codes.w};
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint4 xv = *reinterpret_cast<const uint4 *>(xq + g * 8);
+        s = fdot2(q4pair(wd[g], 0), xv.x, s);
+        s = fdot2(q4pair(wd[g], 4), xv.y, s);
+        s = fdot2(q4pair(wd[g], 8), xv.z, s);
+        s = fdot2(q4pair(wd[g], 12), xv.w, s);
+    }
+    return fmaf(scale, s, acc);
+}
+
 // Stage columns [c0, c0+cw) of x [B][d] (fp16) into LDS xs [B][xch]; cw % 8 == 0.
 template <int B, bool Q4ORDER>
 __device__ __forceinline__ void stage_x(uint16_t *xs, const uint16_t *__restrict__ x, int d, int c0, int cw,
@@ -93,311 +137,455 @@ __device__ __forceinline__ void stage_x(uint16_t *xs, const uint16_t *__restrict
     }
 }
 
-// ------------------------------------------------------------------------------ predictor
-
-// z[b][j] = max(0, P1[j] . x_b).  One wave per row j; 4 waves per workgroup; x staged in LDS in
-// column chunks of xch (a single chunk whenever B*d fp16 values fit the LDS budget).
-template <int B>
-__global__ __launch_bounds__(256) void k_pred_l1(const uint16_t *__restrict__ p1, const uint16_t *__restrict__ x,
-                                                 float *__restrict__ z, int d, int r, int xch) {
-    extern __shared__ __align__(16) uint16_t xs[];
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const int j = blockIdx.x * 4 + wave;
-    float acc[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = 0.f;
-    for (int c0 = 0; c0 < d; c0 += xch) {
-        const int cw = min(xch, d - c0);
-        stage_x<B, false>(xs, x, d, c0, cw, xch);
-        __syncthreads();
-        if (j < r) {
-            const uint16_t *row = p1 + (size_t)j * d + c0;
-            int col = lane * 8;
-            for (; col + 3 * 512 < cw; col += 4 * 512) {       // 4 loads in flight per lane
-                uint4 w[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) w[u] = ld16(row + col + u * 512);
-#pragma unroll
-                for (int u = 0; u < 4; ++u)
-#pragma unroll
-                    for (int b = 0; b < B; ++b)
-                        acc[b] = dot8(w[u], *reinterpret_cast<const uint4 *>(xs + b * xch + col + u * 512), acc[b]);
-            }
-            for (; col < cw; col += 512) {
-                uint4 w = ld16(row + col);
-#pragma unroll
-                for (int b = 0; b < B; ++b)
-                    acc[b] = dot8(w, *reinterpret_cast<const uint4 *>(xs + b * xch + col), acc[b]);
-            }
-        }
-        __syncthreads();
-    }
-    if (j < r) {
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            float s = wave_sum(acc[b]);
-            if (lane == 0) z[b * r + j] = fmaxf(s, 0.f);
-        }
-    }
+// Cross-workgroup exchange inside one kernel without L2-wide flushes: values are written with
+// agent-coherent stores (global_store ... sc1, which do not linger dirty in one XCD's L2), each
+// thread waits until its stores are acknowledged, and readers use agent-coherent loads (sc1),
+// which do not return a stale line from their own XCD's L2.  An agent-scope fence would do the
+// same with a whole-L2 writeback/invalidate (buffer_wbl2 / buffer_inv), far costlier here.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-// l[b][i] = P2[i] . z_b + c[i];  mask[i] = OR_b [l > 0].  z [B][r] staged in LDS (fp32).
-// Each wave handles RPW consecutive rows, NT 16-byte column groups per lane (r <= 512*NT).
-template <int B, int NT, int RPW>
-__global__ __launch_bounds__(256) void k_pred_l2(const uint16_t *__restrict__ p2, const uint16_t *__restrict__ c,
-                                                 const float *__restrict__ z, int r, int f,
-                                                 float *__restrict__ logits, uint8_t *__restrict__ mask) {
-    extern __shared__ __align__(16) float zs[];
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    for (int t = threadIdx.x; t < B * r / 4; t += blockDim.x)
-        reinterpret_cast<float4 *>(zs)[t] = reinterpret_cast<const float4 *>(z)[t];
-    __syncthreads();
-    const int row0 = (blockIdx.x * 4 + wave) * RPW;
-    if (row0 >= f) return;
-#pragma unroll 1
-    for (int rr = 0; rr < RPW; rr += 4) {
-        uint4 w[4][NT];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = row0 + rr + u;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int col = lane * 8 + t * 512;
-                w[u][t] = (i < f && col < r) ? ld16(p2 + (size_t)i * r + col) : make_uint4(0, 0, 0, 0);
-            }
-        }
-        float acc[4][B];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int b = 0; b < B; ++b) acc[u][b] = 0.f;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const int col = lane * 8 + t * 512;
-            if (col < r) {
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    const float4 za = *reinterpret_cast<const float4 *>(zs + b * r + col);
-                    const float4 zb = *reinterpret_cast<const float4 *>(zs + b * r + col + 4);
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const h2 a0 = __builtin_bit_cast(h2, w[u][t].x), a1 = __builtin_bit_cast(h2, w[u][t].y);
-                        const h2 a2 = __builtin_bit_cast(h2, w[u][t].z), a3 = __builtin_bit_cast(h2, w[u][t].w);
-                        float s = acc[u][b];
-                        s = fmaf((float)a0.x, za.x, s); s = fmaf((float)a0.y, za.y, s);
-                        s = fmaf((float)a1.x, za.z, s); s = fmaf((float)a1.y, za.w, s);
-                        s = fmaf((float)a2.x, zb.x, s); s = fmaf((float)a2.y, zb.y, s);
-                        s = fmaf((float)a3.x, zb.z, s); s = fmaf((float)a3.y, zb.w, s);
-                        acc[u][b] = s;
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int i = row0 + rr + u;
-            if (i >= f) break;                                   // wave-uniform
-            const float ci = half_to_float(c[i]);
-            uint8_t m = 0;
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const float l = wave_sum(acc[u][b]) + ci;
-                m |= (uint8_t)(l > 0.f);
-                if (logits != nullptr && lane == 0) logits[(size_t)b * f + i] = l;
-            }
-            if (lane == 0) mask[i] = m;
-        }
-    }
+__device__ __forceinline__ float load_coherent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void wait_stores_done() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// ------------------------------------------------------------------------------ compaction
-
-// One workgroup of 1024 threads walks the mask in tiles of 4096 entries: each thread flags 4
-// entries, a wave prefix sum plus a 16-entry LDS scan give every flagged entry its position,
-// so idx comes out in ascending order.  counts = {listed, predicted}.
-__global__ __launch_bounds__(1024) void k_compact(const uint8_t *__restrict__ mask, int f,
-                                                  const int32_t *__restrict__ slot_of, int32_t *__restrict__ idx,
-                                                  int32_t *__restrict__ counts) {
-    __shared__ int wsum[16];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    int base = 0, npred = 0;
-    for (int t0 = 0; t0 < f; t0 += 4096) {
-        const int i0 = t0 + tid * 4;
-        int flags = 0, cnt = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = i0 + e;
-            const bool m = i < f && mask[i] != 0;
-            const bool a = m && (slot_of == nullptr || slot_of[i] >= 0);
-            npred += m;
-            cnt += a;
-            flags |= (int)a << e;
-        }
-        int incl = cnt;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int v = __shfl_up(incl, o, kWave);
-            if (lane >= o) incl += v;
-        }
-        if (lane == kWave - 1) wsum[wave] = incl;
-        __syncthreads();
-        int before = 0, total = 0;
-#pragma unroll
-        for (int w = 0; w < 16; ++w) {
-            const int v = wsum[w];
-            before += (w < wave) ? v : 0;
-            total += v;
-        }
-        int pos = base + before + incl - cnt;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (flags >> e & 1) idx[pos++] = i0 + e;
-        base += total;
-        __syncthreads();
-    }
-    npred = wave_sum_int(npred);
-    if (lane == 0) wsum[wave] = npred;
-    __syncthreads();
-    if (tid == 0) {
-        int tot = 0;
-        for (int w = 0; w < 16; ++w) tot += wsum[w];
-        counts[0] = base;
-        counts[1] = tot;
-    }
-}
-
-// ------------------------------------------------------------------------------ sparse FFN
-
-// Slot of the k-th listed neuron, or -1 when the entry is out of range (then it is skipped).
-__device__ __forceinline__ int slot_for(const int32_t *__restrict__ idx, const int32_t *__restrict__ slot_of, int k,
-                                        int f, int n_slots) {
-    const int i = idx[k];
+// Slot of neuron id i, or -1 when i or its slot is out of range (then the entry is skipped).
+__device__ __forceinline__ int slot_of_id(int i, const int32_t *__restrict__ slot_of, int f, int n_slots) {
     if (i < 0 || i >= f) return -1;
     const int s = slot_of ? slot_of[i] : i;
     return (s >= 0 && s < n_slots) ? s : -1;
 }
 
-// Dot products of one resident row (d weights) with the B staged token chunks.
-template <int B, int WT>
-__device__ __forceinline__ void row_dot(const uint8_t *__restrict__ row, int d, int c0, int cw, const uint16_t *xs,
-                                        int xch, int lane, float (&acc)[B]) {
-    if (WT == WT_F16) {
-        const uint16_t *rw = reinterpret_cast<const uint16_t *>(row) + c0;
-        int col = lane * 8;
-        for (; col + 3 * 512 < cw; col += 4 * 512) {
-            uint4 w[4];
+// ------------------------------------------------------------------------------ predictor
+
+// z[b][j] = max(0, P1[j] . x_b).  One 256-thread workgroup per row j: every thread issues its
+// row loads first (they do not depend on x), then reads x through L2, then the four wave sums
+// meet in LDS.
+template <int B>
+__global__ __launch_bounds__(256) void k_pred_l1(const uint16_t *__restrict__ p1, const uint16_t *__restrict__ x,
+                                                 float *__restrict__ z, int d, int r) {
+    constexpr int U = 8;                      // 16-byte loads per thread per pass (16384 columns)
+    __shared__ float red[4][B];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int j = blockIdx.x;
+    const uint16_t *row = p1 + (size_t)j * d;
+    float acc[B];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) w[u] = ld16(rw + col + u * 512);
+    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    for (int c0 = 0; c0 < d; c0 += U * 2048) {
+        uint4 w[U];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int b = 0; b < B; ++b)
-                    acc[b] = dot8(w[u], *reinterpret_cast<const uint4 *>(xs + b * xch + col + u * 512), acc[b]);
+        for (int u = 0; u < U; ++u) {
+            const int col = c0 + tid * 8 + u * 2048;
+            w[u] = col < d ? ld16(row + col) : zero4();
         }
-        for (; col < cw; col += 512) {
-            const uint4 w = ld16(rw + col);
 #pragma unroll
-            for (int b = 0; b < B; ++b) acc[b] = dot8(w, *reinterpret_cast<const uint4 *>(xs + b * xch + col), acc[b]);
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int col = c0 + tid * 8 + u * 2048;
+                if (col < d) acc[b] = dot8(w[u], ld16(x + (size_t)b * d + col), acc[b]);
+            }
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const float s = wave_sum(acc[b]);
+        if (lane == 0) red[wave][b] = s;
+    }
+    __syncthreads();
+    if (tid < B) z[tid * r + j] = fmaxf(red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid], 0.f);
+}
+
+// l[b][i] = P2[i] . z_b + c[i];  mask[i] = OR_b [l > 0].  Each wave owns R consecutive rows and
+// issues all R*NT row loads at once; lane L covers columns L*8 + 512t (t < NT, r <= 512*NT), whose
+// z values it reads once per token and reuses for all R rows; the R sums are finished with one
+// reduce-scatter, after which lane (64/R)*i owns row i.
+template <int B, int NT, int R>
+__global__ __launch_bounds__(256) void k_pred_l2(const uint16_t *__restrict__ p2, const uint16_t *__restrict__ c,
+                                                 const float *__restrict__ z, int r, int f,
+                                                 float *__restrict__ logits, uint8_t *__restrict__ mask) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int row0 = (blockIdx.x * 4 + wave) * R;
+    if (row0 >= f) return;
+    uint4 w[R][NT];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int row = row0 + i, col = lane * 8 + t * 512;
+            w[i][t] = (row < f && col < r) ? ld16(p2 + (size_t)row * r + col) : zero4();
         }
-    } else {
-        // Lane handles whole 32-weight blocks q = c0/32 + lane + 64t: 16 code bytes + one scale.
-        const uint8_t *codes = row;
-        const uint16_t *scales = reinterpret_cast<const uint16_t *>(row + d / 2);
-        const int q0 = c0 / 32, nq = cw / 32;
-        for (int qq = lane; qq < nq; qq += kWave) {
-            const int q = q0 + qq;
-            const uint4 cw4 = ld16(codes + (size_t)q * 16);
-            const float sc = half_to_float(scales[q]);
-            const uint32_t words[4] = {cw4.x, cw4.y, cw4.z, cw4.w};
+    const float c_lane = (lane < R && row0 + lane < f) ? half_to_float(c[row0 + lane]) : 0.f;
+    constexpr int G = kWave / R;
+    const int ri = lane / G;                                  // row owned after the reduce-scatter
+    const bool owner = (lane % G) == 0 && row0 + ri < f;
+    const float ci = __shfl(c_lane, ri, kWave);
+    uint8_t m = 0;
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                float s = 0.f;
+    for (int b = 0; b < B; ++b) {
+        float zr[NT][8];
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint4 xv = *reinterpret_cast<const uint4 *>(xs + b * xch + qq * 32 + g * 8);
-                    s = fdot2(q4pair(words[g], 0), xv.x, s);
-                    s = fdot2(q4pair(words[g], 4), xv.y, s);
-                    s = fdot2(q4pair(words[g], 8), xv.z, s);
-                    s = fdot2(q4pair(words[g], 12), xv.w, s);
+        for (int t = 0; t < NT; ++t) {
+            const int col = lane * 8 + t * 512;
+            float4 za = make_float4(0.f, 0.f, 0.f, 0.f), zb = za;
+            if (col < r) {
+                za = *reinterpret_cast<const float4 *>(z + (size_t)b * r + col);
+                zb = *reinterpret_cast<const float4 *>(z + (size_t)b * r + col + 4);
+            }
+            zr[t][0] = za.x; zr[t][1] = za.y; zr[t][2] = za.z; zr[t][3] = za.w;
+            zr[t][4] = zb.x; zr[t][5] = zb.y; zr[t][6] = zb.z; zr[t][7] = zb.w;
+        }
+        float v[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            float s = 0.f;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const uint32_t q[4] = {w[i][t].x, w[i][t].y, w[i][t].z, w[i][t].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const h2 p = __builtin_bit_cast(h2, q[e]);
+                    s = fmaf((float)p.x, zr[t][2 * e], s);
+                    s = fmaf((float)p.y, zr[t][2 * e + 1], s);
                 }
-                acc[b] = fmaf(sc, s, acc[b]);
+            }
+            v[i] = s;
+        }
+        const float l = reduce_scatter<R>(v, lane) + ci;
+        if (owner) {
+            m |= (uint8_t)(l > 0.f);
+            if (logits != nullptr) logits[(size_t)b * f + row0 + ri] = l;
+        }
+    }
+    if (owner) mask[row0 + ri] = m;
+}
+
+// ------------------------------------------------------------------------------ compaction
+
+// One workgroup of 1024 threads.  Thread t owns the contiguous mask segment [t*seg, (t+1)*seg)
+// (seg a multiple of 16), reads it with 16-byte loads, keeps the flags of its first 64 entries in
+// a register (re-reading only beyond that), and a single block prefix sum over the per-thread
+// counts gives every listed neuron its position -- so idx is ascending.  counts = {listed,
+// predicted}.
+__global__ __launch_bounds__(1024) void k_compact(const uint8_t *__restrict__ mask, int f,
+                                                  const int32_t *__restrict__ slot_of, int32_t *__restrict__ idx,
+                                                  int32_t *__restrict__ counts) {
+    __shared__ int wsum[16], wpred[16];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int seg = (((f + 1023) / 1024) + 15) & ~15;
+    const int i0 = tid * seg;
+    const int i1 = min(i0 + seg, f);
+    const bool vec_ok = (reinterpret_cast<uintptr_t>(mask) & 15u) == 0;
+
+    // flags of 64 entries starting at base (bit e = entry base+e predicted), before placement
+    auto load_flags = [&](int base) -> uint64_t {
+        uint64_t fl = 0;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int i = base + v * 16;
+            if (i >= i1) break;
+            if (vec_ok && i + 16 <= i1) {
+                const uint4 q = ld16(mask + i);
+                const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    fl |= (uint64_t)(((wd[e >> 2] >> (8 * (e & 3))) & 0xFFu) != 0) << (v * 16 + e);
+            } else {
+                for (int e = 0; e < 16 && i + e < i1; ++e) fl |= (uint64_t)(mask[i + e] != 0) << (v * 16 + e);
             }
         }
+        return fl;
+    };
+    const bool so_vec = (reinterpret_cast<uintptr_t>(slot_of) & 15u) == 0;
+    // drop predicted entries that are not resident; the slot loads of a window are all issued
+    // before any of them is tested
+    auto restrict_flags = [&](uint64_t fl, int base) -> uint64_t {
+        if (slot_of == nullptr || fl == 0) return fl;
+        uint64_t keep = 0;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int i = base + v * 4;
+            const bool need = ((fl >> (v * 4)) & 0xFull) != 0 && i < i1;
+            int s0 = -1, s1 = -1, s2 = -1, s3 = -1;
+            if (need) {
+                if (so_vec && i + 4 <= i1) {
+                    const int4 q = *reinterpret_cast<const int4 *>(slot_of + i);
+                    s0 = q.x; s1 = q.y; s2 = q.z; s3 = q.w;
+                } else {
+                    s0 = slot_of[i];
+                    if (i + 1 < i1) s1 = slot_of[i + 1];
+                    if (i + 2 < i1) s2 = slot_of[i + 2];
+                    if (i + 3 < i1) s3 = slot_of[i + 3];
+                }
+            }
+            keep |= ((uint64_t)(s0 >= 0) | ((uint64_t)(s1 >= 0) << 1) | ((uint64_t)(s2 >= 0) << 2) |
+                     ((uint64_t)(s3 >= 0) << 3)) << (v * 4);
+        }
+        return fl & keep;
+    };
+
+    int cnt = 0, npred = 0;
+    uint64_t first_act = 0;
+    for (int base = i0; base < i1; base += 64) {
+        const uint64_t fl = load_flags(base);
+        const uint64_t act = restrict_flags(fl, base);
+        if (base == i0) first_act = act;
+        npred += __popcll(fl);
+        cnt += __popcll(act);
+    }
+    // block exclusive scan of cnt
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int v = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += v;
+    }
+    int wp = npred;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) wp += __shfl_xor(wp, o, kWave);
+    if (lane == kWave - 1) wsum[wave] = incl;
+    if (lane == 0) wpred[wave] = wp;
+    __syncthreads();
+    int before = 0, total = 0, tpred = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        before += (w < wave) ? wsum[w] : 0;
+        total += wsum[w];
+        tpred += wpred[w];
+    }
+    int pos = before + incl - cnt;
+    for (int base = i0; base < i1; base += 64) {
+        uint64_t act = (base == i0) ? first_act : restrict_flags(load_flags(base), base);
+        for (; act; act &= act - 1) idx[pos++] = base + __builtin_ctzll(act);
+    }
+    if (tid == 0) {
+        counts[0] = total;
+        counts[1] = tpred;
+    }
+}
+
+// ------------------------------------------------------------------------------ sparse FFN
+
+// One pass of a neuron's row dot products, split into "issue the loads" and "consume them" so
+// that callers can overlap the loads with other work (x staging, the next lookup).
+//   fp16: lane L covers columns c0 + L*8 + 512v, v < V (16 vectors of one row, or 8 of each of the
+//         gate and up rows so that both are in flight together).
+//   Q4_0: lane L covers 32-weight blocks q0 + L + 64v, v < V (16 code bytes + one scale each).
+template <int B, bool GATED, int WT>
+struct RowPass {
+    static constexpr int V = (WT == WT_F16) ? (GATED ? 8 : 16) : 8;
+    static constexpr int STEP = (WT == WT_F16) ? V * 512 : V * kWave;   // columns (fp16) or blocks (Q4_0) per pass
+    uint4 wu[V];
+    uint4 wg[GATED ? V : 1];
+    uint16_t sc[WT == WT_Q4_0 ? V : 1];
+
+    __device__ __forceinline__ static int extent(int d) { return WT == WT_F16 ? d : d / 32; }
+
+    __device__ __forceinline__ void issue(const uint8_t *__restrict__ row, int64_t row_bytes, int d, int p0,
+                                          int lane) {
+        if (WT == WT_F16) {
+            const uint16_t *gr = reinterpret_cast<const uint16_t *>(row);
+            const uint16_t *ur = reinterpret_cast<const uint16_t *>(row + (GATED ? row_bytes : 0));
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int col = p0 + lane * 8 + v * 512;
+                wu[v] = col < d ? ld16(ur + col) : zero4();
+                if (GATED) wg[GATED ? v : 0] = col < d ? ld16(gr + col) : zero4();
+            }
+        } else {
+            const uint16_t *scales = reinterpret_cast<const uint16_t *>(row + d / 2);
+            const int nq = d / 32;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int q = p0 + lane + v * kWave;
+                wu[v] = q < nq ? ld16(row + (size_t)q * 16) : zero4();
+                sc[WT == WT_Q4_0 ? v : 0] = q < nq ? scales[q] : (uint16_t)0;
+            }
+        }
+    }
+
+    __device__ __forceinline__ void consume(const uint16_t *xs, int xstride, int d, int p0, int lane, float (&ag)[B],
+                                            float (&au)[B]) const {
+        if (WT == WT_F16) {
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int col = p0 + lane * 8 + v * 512;
+                if (col < d) {
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        const uint4 xv = *reinterpret_cast<const uint4 *>(xs + b * xstride + col);
+                        au[b] = dot8(wu[v], xv, au[b]);
+                        if (GATED) ag[b] = dot8(wg[GATED ? v : 0], xv, ag[b]);
+                    }
+                }
+            }
+        } else {
+            const int nq = d / 32;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int q = p0 + lane + v * kWave;
+                if (q < nq) {
+                    const float s = half_to_float(sc[WT == WT_Q4_0 ? v : 0]);
+#pragma unroll
+                    for (int b = 0; b < B; ++b) au[b] = q4_block_dot(wu[v], xs + b * xstride + q * 32, au[b], s);
+                }
+            }
+        }
+    }
+};
+
+// All passes of one neuron's row dots against x staged in LDS (row: the neuron's w_in row).
+template <int B, bool GATED, int WT>
+__device__ __forceinline__ void neuron_dots(const uint8_t *__restrict__ row, int64_t row_bytes, int d,
+                                            const uint16_t *xs, int xstride, int lane, float (&ag)[B],
+                                            float (&au)[B]) {
+    using P = RowPass<B, GATED, WT>;
+    for (int p0 = 0; p0 < P::extent(d); p0 += P::STEP) {
+        P pass;
+        pass.issue(row, row_bytes, d, p0, lane);
+        pass.consume(xs, xstride, d, p0, lane, ag, au);
+    }
+}
+
+// Epilogue of one neuron: finish the wave sums and apply bias + ReLU (or the ReGLU product).
+template <int B, bool GATED>
+__device__ __forceinline__ void neuron_store(float (&ag)[B], float (&au)[B], int s, int k, const uint16_t *b_up,
+                                             float *__restrict__ h, int h_stride, int lane) {
+    const float bias = (!GATED && b_up != nullptr && s >= 0) ? half_to_float(b_up[s]) : 0.f;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        const float u = wave_sum(au[b]);
+        float hv;
+        if (GATED) {
+            const float g = wave_sum(ag[b]);
+            hv = fmaxf(g, 0.f) * u;
+        } else {
+            hv = fmaxf(u + bias, 0.f);
+        }
+        if (lane == 0) h[(size_t)b * h_stride + k] = (s >= 0) ? hv : 0.f;
     }
 }
 
 // h[b][k] for the listed neurons.  Neuron k goes to wave (k / G) % 4 of workgroup k % G in round
 // k / (4G), which spreads the listed neurons over every workgroup (and so every CU) first.
-// x is staged once per workgroup (in chunks of xch columns when B*d does not fit).
+// When B*d fp16 values fit the LDS budget (xch >= d), x is staged once per workgroup and its
+// global loads overlap the row loads of round 0; otherwise x is staged in column chunks and each
+// round walks the chunks.  Workgroup 0 also clears `zero_ptr[0..nzero)` (the down kernel's
+// slab tickets) -- the down kernel always runs after this one on the same stream.
 template <int B, bool GATED, int WT>
 __global__ __launch_bounds__(256) void k_sparse_up(const uint8_t *__restrict__ w_in, int64_t row_bytes, int d,
                                                    const uint16_t *__restrict__ b_up, const uint16_t *__restrict__ x,
                                                    const int32_t *__restrict__ idx, const int32_t *__restrict__ counts,
                                                    const int32_t *__restrict__ slot_of, int f, int n_slots,
-                                                   float *__restrict__ h, int h_stride, int xch) {
+                                                   float *__restrict__ h, int h_stride, int xch,
+                                                   int32_t *__restrict__ zero_ptr, int nzero) {
     extern __shared__ __align__(16) uint16_t xs[];
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (blockIdx.x == 0)
+        for (int t = threadIdx.x; t < nzero; t += blockDim.x) zero_ptr[t] = 0;
     const int G = gridDim.x;
     const int n = min(max(counts[0], 0), n_slots);
+    if ((int)blockIdx.x >= n) return;                           // no neuron for this workgroup
     const int per_round = 4 * G;
     const int rounds = (n + per_round - 1) / per_round;
-    const int nchunks = (d + xch - 1) / xch;
-    if (rounds == 0 || (int)blockIdx.x >= n) return;             // no neuron for this workgroup
     const int64_t in_stride = GATED ? 2 * row_bytes : row_bytes;
+
+    if (xch >= d) {
+        // x fits.  Round 0 overlaps its three latencies: the neuron's slot lookup, the first pass
+        // of its row loads, and the global loads of x for the LDS stage.
+        using P = RowPass<B, GATED, WT>;
+        {
+            const int k = __builtin_amdgcn_readfirstlane(wave * G + (int)blockIdx.x);
+            const int s = (k < n) ? slot_of_id(idx[k], slot_of, f, n_slots) : -1;
+            const uint8_t *row = w_in + (int64_t)(s >= 0 ? s : 0) * in_stride;
+            P pass;
+            if (s >= 0) pass.issue(row, row_bytes, d, 0, lane);
+            stage_x<B, WT == WT_Q4_0>(xs, x, d, 0, d, d);
+            __syncthreads();
+            if (k < n) {
+                float ag[B], au[B];
+#pragma unroll
+                for (int b = 0; b < B; ++b) ag[b] = au[b] = 0.f;
+                if (s >= 0) {
+                    pass.consume(xs, d, d, 0, lane, ag, au);
+                    for (int p0 = P::STEP; p0 < P::extent(d); p0 += P::STEP) {
+                        P nxt;
+                        nxt.issue(row, row_bytes, d, p0, lane);
+                        nxt.consume(xs, d, d, p0, lane, ag, au);
+                    }
+                }
+                neuron_store<B, GATED>(ag, au, s, k, b_up, h, h_stride, lane);
+            }
+        }
+        for (int rd = 1; rd < rounds; ++rd) {
+            const int k = __builtin_amdgcn_readfirstlane(rd * per_round + wave * G + (int)blockIdx.x);
+            if (k >= n) break;                                  // wave-uniform
+            const int s = slot_of_id(idx[k], slot_of, f, n_slots);
+            float ag[B], au[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) ag[b] = au[b] = 0.f;
+            if (s >= 0) neuron_dots<B, GATED, WT>(w_in + (int64_t)s * in_stride, row_bytes, d, xs, d, lane, ag, au);
+            neuron_store<B, GATED>(ag, au, s, k, b_up, h, h_stride, lane);
+        }
+        return;
+    }
+    // Chunked x: all waves of the workgroup walk the same chunks in lock-step.
+    const int nchunks = (d + xch - 1) / xch;
     for (int rd = 0; rd < rounds; ++rd) {
+        if (rd * per_round + (int)blockIdx.x >= n) break;       // workgroup-uniform
         const int k = rd * per_round + wave * G + blockIdx.x;
-        if (rd * per_round + blockIdx.x >= n) break;             // workgroup-uniform: nothing left
-        const int s = (k < n) ? slot_for(idx, slot_of, k, f, n_slots) : -1;
+        const int s = (k < n) ? slot_of_id(idx[k], slot_of, f, n_slots) : -1;
         float ag[B], au[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) ag[b] = au[b] = 0.f;
         for (int ch = 0; ch < nchunks; ++ch) {
             const int c0 = ch * xch, cw = min(xch, d - c0);
-            if (nchunks > 1 || rd == 0) {
-                if (nchunks > 1 && (rd > 0 || ch > 0)) __syncthreads();
-                stage_x<B, WT == WT_Q4_0>(xs, x, d, c0, cw, xch);
-                __syncthreads();
-            }
+            __syncthreads();
+            stage_x<B, WT == WT_Q4_0>(xs, x, d, c0, cw, xch);
+            __syncthreads();
             if (s >= 0) {
+                // the chunk [c0, c0+cw) of the row(s): cw is a multiple of 512, c0 of 32 (Q4_0 blocks)
                 const uint8_t *row = w_in + (int64_t)s * in_stride;
-                if (GATED) {
-                    row_dot<B, WT>(row, d, c0, cw, xs, xch, lane, ag);
-                    row_dot<B, WT>(row + row_bytes, d, c0, cw, xs, xch, lane, au);
+                if (WT == WT_F16) {
+                    const int64_t off = (int64_t)c0 * 2;
+                    neuron_dots<B, GATED, WT>(row + off, row_bytes, cw, xs, xch, lane, ag, au);
                 } else {
-                    row_dot<B, WT>(row, d, c0, cw, xs, xch, lane, au);
-                }
-            }
-        }
-        if (k < n) {
-            const float bias = (!GATED && b_up != nullptr && s >= 0) ? half_to_float(b_up[s]) : 0.f;
+                    // Q4_0 chunk: blocks c0/32 .. (c0+cw)/32 of this row
+                    const uint16_t *scales = reinterpret_cast<const uint16_t *>(row + d / 2);
+                    const int qa = c0 / 32, nq = cw / 32;
+                    for (int qq = lane; qq < nq; qq += kWave) {
+                        const uint4 cwv = ld16(row + (size_t)(qa + qq) * 16);
+                        const float sc = half_to_float(scales[qa + qq]);
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const float u = wave_sum(au[b]);
-                float hv;
-                if (GATED) {
-                    const float g = wave_sum(ag[b]);
-                    hv = fmaxf(g, 0.f) * u;
-                } else {
-                    hv = fmaxf(u + bias, 0.f);
+                        for (int b = 0; b < B; ++b) au[b] = q4_block_dot(cwv, xs + b * xch + qq * 32, au[b], sc);
+                    }
                 }
-                if (lane == 0) h[(size_t)b * h_stride + k] = (s >= 0) ? hv : 0.f;
             }
         }
+        if (k < n) neuron_store<B, GATED>(ag, au, s, k, b_up, h, h_stride, lane);
     }
 }
 
-// Partial y over a (512-column slab, neuron chunk) tile.  Every lane owns 8 columns of the slab;
-// the 4 waves take the chunk's neurons round-robin, 4 at a time so that 4 row reads are in
-// flight per lane; rows whose h is zero for every token are skipped (their contribution is an
-// exact zero).  The 4 wave partials are summed in LDS and written to part[chunk][b][d].
+// y over (512-column slab, neuron chunk) tiles.  Lane L owns columns slab*512 + 8L .. +8.  The
+// chunk's neurons are dealt round-robin to the 4 waves; a wave fetches the metadata (index, h,
+// slot) of up to 64 of its neurons at once, one lane per neuron, drops neurons whose h is zero
+// for every token (an exact zero contribution), and walks the rest 8 at a time with all 8 row
+// reads in flight.  The waves' partials meet in LDS; each chunk's partial goes to `part`, and
+// the last workgroup to finish a slab (slab ticket) sums the chunk partials in chunk order and
+// adds b_down, so y is deterministic.  Tickets must be zero on entry (k_sparse_up clears them)
+// and are left zero.
 template <int B, int WT>
 __global__ __launch_bounds__(256) void k_sparse_down(const uint8_t *__restrict__ w_dn, int64_t row_bytes, int d,
                                                      const int32_t *__restrict__ idx, const int32_t *__restrict__ counts,
                                                      const int32_t *__restrict__ slot_of, int f, int n_slots,
                                                      const float *__restrict__ h, int h_stride,
-                                                     float *__restrict__ part, int C) {
+                                                     float *__restrict__ part, int C, int32_t *__restrict__ tickets,
+                                                     const uint16_t *__restrict__ b_down, float *__restrict__ y) {
+    constexpr int U = 8;
     __shared__ float red[4][B][8][kWave];
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int slab = blockIdx.x, ck = blockIdx.y;
     const int n = min(max(counts[0], 0), n_slots);
     const int k0 = (int)((int64_t)n * ck / C), k1 = (int)((int64_t)n * (ck + 1) / C);
@@ -409,65 +597,74 @@ __global__ __launch_bounds__(256) void k_sparse_down(const uint8_t *__restrict__
 #pragma unroll
         for (int t = 0; t < 8; ++t) acc[b][t] = 0.f;
 
-    for (int kb = k0 + wave; kb < k1; kb += 16) {
-        int sl[4];
-        float hv[4][B];
+    for (int base = k0 + wave; base < k1; base += 4 * kWave) {
+        const int kk = base + 4 * lane;
+        const bool in = kk < k1;
+        const int id = in ? idx[kk] : -1;
+        float hv[B];
+        bool any = false;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int k = kb + 4 * u;
-            sl[u] = -1;
-            bool any = false;
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                hv[u][b] = (k < k1) ? h[(size_t)b * h_stride + k] : 0.f;
-                any |= hv[u][b] != 0.f;
-            }
-            if (k < k1 && any) sl[u] = slot_for(idx, slot_of, k, f, n_slots);
+        for (int b = 0; b < B; ++b) {
+            hv[b] = in ? h[(size_t)b * h_stride + kk] : 0.f;
+            any |= hv[b] != 0.f;
         }
-        if (WT == WT_F16) {
-            uint4 w[4];
+        const int sl = (in && any) ? slot_of_id(id, slot_of, f, n_slots) : -1;
+        uint64_t live = __ballot(sl >= 0);
+        while (live) {                                           // wave-uniform
+            int js[U];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                w[u] = (sl[u] >= 0 && colok) ? ld16(w_dn + (int64_t)sl[u] * row_bytes + (int64_t)col * 2)
-                                             : make_uint4(0, 0, 0, 0);
+            for (int u = 0; u < U; ++u) {
+                js[u] = live ? __builtin_ctzll(live) : -1;
+                if (live) live &= live - 1;
+            }
+            if (WT == WT_F16) {
+                uint4 wv[U];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (sl[u] < 0) continue;                                 // wave-uniform
-                const uint32_t wv[4] = {w[u].x, w[u].y, w[u].z, w[u].w};
+                for (int u = 0; u < U; ++u) {
+                    const int s = js[u] >= 0 ? bcast(sl, js[u]) : -1;
+                    wv[u] = (s >= 0 && colok) ? ld16(w_dn + (int64_t)s * row_bytes + (int64_t)col * 2) : zero4();
+                }
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const h2 pr = __builtin_bit_cast(h2, wv[p]);
-                    const float lo = (float)pr.x, hi = (float)pr.y;
+                for (int u = 0; u < U; ++u) {
+                    if (js[u] < 0) continue;                     // wave-uniform
+                    const uint32_t wq[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
 #pragma unroll
                     for (int b = 0; b < B; ++b) {
-                        acc[b][2 * p] = fmaf(hv[u][b], lo, acc[b][2 * p]);
-                        acc[b][2 * p + 1] = fmaf(hv[u][b], hi, acc[b][2 * p + 1]);
+                        const float hb = bcastf(hv[b], js[u]);
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) {
+                            const h2 pr = __builtin_bit_cast(h2, wq[p]);
+                            acc[b][2 * p] = fmaf(hb, (float)pr.x, acc[b][2 * p]);
+                            acc[b][2 * p + 1] = fmaf(hb, (float)pr.y, acc[b][2 * p + 1]);
+                        }
                     }
                 }
-            }
-        } else {
-            uint32_t cw[4];
-            float sc[4];
+            } else {
+                uint32_t cw[U];
+                uint16_t sc[U];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bool ok = sl[u] >= 0 && colok;
-                const uint8_t *row = w_dn + (int64_t)sl[u] * row_bytes;
-                cw[u] = ok ? *reinterpret_cast<const uint32_t *>(row + col / 2) : 0u;
-                sc[u] = ok ? half_to_float(*reinterpret_cast<const uint16_t *>(row + d / 2 + (col / 32) * 2)) : 0.f;
-            }
+                for (int u = 0; u < U; ++u) {
+                    const int s = js[u] >= 0 ? bcast(sl, js[u]) : -1;
+                    const bool ok = s >= 0 && colok;
+                    const uint8_t *row = w_dn + (int64_t)(ok ? s : 0) * row_bytes;
+                    cw[u] = ok ? *reinterpret_cast<const uint32_t *>(row + col / 2) : 0u;
+                    sc[u] = ok ? *reinterpret_cast<const uint16_t *>(row + d / 2 + (col / 32) * 2) : (uint16_t)0;
+                }
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                if (sl[u] < 0) continue;
+                for (int u = 0; u < U; ++u) {
+                    if (js[u] < 0) continue;
+                    const float scf = half_to_float(sc[u]);
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    // q4pair(w, 4p) = (code_p - 8, code_{p+4} - 8): columns p and p+4.
-                    const h2 pr = __builtin_bit_cast(h2, q4pair(cw[u], 4 * p));
-                    const float lo = (float)pr.x, hi = (float)pr.y;
+                    for (int p = 0; p < 4; ++p) {
+                        // q4pair(w, 4p) = (code_p - 8, code_{p+4} - 8): columns p and p+4.
+                        const h2 pr = __builtin_bit_cast(h2, q4pair(cw[u], 4 * p));
+                        const float lo = (float)pr.x, hi = (float)pr.y;
 #pragma unroll
-                    for (int b = 0; b < B; ++b) {
-                        const float cf = hv[u][b] * sc[u];
-                        acc[b][p] = fmaf(cf, lo, acc[b][p]);
-                        acc[b][p + 4] = fmaf(cf, hi, acc[b][p + 4]);
+                        for (int b = 0; b < B; ++b) {
+                            const float cf = bcastf(hv[b], js[u]) * scf;
+                            acc[b][p] = fmaf(cf, lo, acc[b][p]);
+                            acc[b][p + 4] = fmaf(cf, hi, acc[b][p + 4]);
+                        }
                     }
                 }
             }
@@ -478,25 +675,36 @@ __global__ __launch_bounds__(256) void k_sparse_down(const uint8_t *__restrict__
 #pragma unroll
         for (int t = 0; t < 8; ++t) red[wave][b][t][lane] = acc[b][t];
     __syncthreads();
-    for (int o = threadIdx.x; o < B * 512; o += blockDim.x) {
+    const int Bd = B * d;
+    for (int o = tid; o < B * 512; o += blockDim.x) {
         const int b = o / 512, cc = o - b * 512;
         const int ln = cc >> 3, t = cc & 7;
         const int gcol = slab * 512 + cc;
-        if (gcol < d) {
-            const float v = red[0][b][t][ln] + red[1][b][t][ln] + red[2][b][t][ln] + red[3][b][t][ln];
-            part[((size_t)ck * B + b) * d + gcol] = v;
-        }
+        if (gcol < d)
+            store_coherent(part + (size_t)ck * Bd + (size_t)b * d + gcol,
+                           red[0][b][t][ln] + red[1][b][t][ln] + red[2][b][t][ln] + red[3][b][t][ln]);
     }
-}
-
-// y[b][j] = b_down[j] + sum over chunks c (ascending) of part[c][b][j].
-__global__ __launch_bounds__(256) void k_reduce_y(const float *__restrict__ part, int C, int Bd, int d,
-                                                  const uint16_t *__restrict__ b_down, float *__restrict__ y) {
-    const int t = blockIdx.x * blockDim.x + threadIdx.x;
-    if (t >= Bd) return;
-    float s = b_down ? half_to_float(b_down[t % d]) : 0.f;
-    for (int c = 0; c < C; ++c) s += part[(size_t)c * Bd + t];
-    y[t] = s;
+    wait_stores_done();                                          // this thread's partials are out
+    __syncthreads();                                             // ... and so are everyone's
+    if (tid == 0) s_last = (atomicAdd(&tickets[slab], 1) == C - 1);
+    __syncthreads();
+    if (!s_last) return;
+    // Sum the chunk partials of this slab in chunk order.  All C loads of an output are issued
+    // before the first add (a load-add loop would wait out one memory round trip per chunk).
+    for (int o = tid; o < B * 512; o += blockDim.x) {
+        const int b = o / 512, cc = o - b * 512;
+        const int gcol = slab * 512 + cc;
+        const bool ok = gcol < d;
+        const size_t off = (size_t)b * d + (ok ? gcol : 0);
+        float v[kDownMaxChunks];
+#pragma unroll
+        for (int c = 0; c < kDownMaxChunks; ++c) v[c] = (ok && c < C) ? load_coherent(part + (size_t)c * Bd + off) : 0.f;
+        float s = (ok && b_down) ? half_to_float(b_down[gcol]) : 0.f;
+#pragma unroll
+        for (int c = 0; c < kDownMaxChunks; ++c) s += v[c];
+        if (ok) y[off] = s;
+    }
+    if (tid == 0) tickets[slab] = 0;
 }
 
 }  // namespace pik
