@@ -21,7 +21,7 @@ PI_MAX_BATCH = 8
 
 # Every function the header declares; the CPU tests check that libpi.so exports them all.
 EXPORTS = ("pi_workspace_bytes", "pi_predict", "pi_compact", "pi_sparse_ffn", "pi_ffn_layer",
-           "pi_status_string", "pi_version")
+           "pi_ffn_layer_fused", "pi_sparse_ffn_h_offset", "pi_status_string", "pi_version")
 
 
 class pi_predictor(ctypes.Structure):
@@ -63,6 +63,10 @@ def lib() -> ctypes.CDLL:
         L.pi_sparse_ffn.argtypes = [P(pi_ffn), vp, i32, vp, vp, vp, vp, sz, vp]
         L.pi_ffn_layer.restype = ctypes.c_int
         L.pi_ffn_layer.argtypes = [P(pi_predictor), P(pi_ffn), vp, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.pi_ffn_layer_fused.restype = ctypes.c_int
+        L.pi_ffn_layer_fused.argtypes = [P(pi_predictor), P(pi_ffn), vp, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.pi_sparse_ffn_h_offset.restype = sz
+        L.pi_sparse_ffn_h_offset.argtypes = [P(pi_ffn), i32, P(i32)]
         L.pi_status_string.restype = ctypes.c_char_p
         L.pi_status_string.argtypes = [ctypes.c_int]
         L.pi_version.restype = ctypes.c_int
@@ -142,6 +146,43 @@ def pi_ffn_layer(pred, ffn, x, batch, y, mask_out, idx_out, counts_out, ws, stre
                                               _ptr(idx_out), _ptr(counts_out), _ptr(ws),
                                               _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0,
                                               _stream(stream)))
+
+
+def pi_ffn_layer_fused(pred, ffn, x, batch, y, mask_out, idx_out, counts_out, ws, stream=None) -> None:
+    _check("pi_ffn_layer_fused", lib().pi_ffn_layer_fused(
+        _byref(pred), _byref(ffn), _ptr(x), batch, _ptr(y), _ptr(mask_out), _ptr(idx_out), _ptr(counts_out),
+        _ptr(ws), _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0, _stream(stream)))
+
+
+PI_WS_STATUS_OFFSET = 384      # byte offset of the layer workspace's sticky status word
+
+
+def workspace_status(ws) -> int:
+    """Sticky status word of a pi_ffn_layer workspace (0 = every cross-workgroup wait completed)."""
+    return int(ws[PI_WS_STATUS_OFFSET:PI_WS_STATUS_OFFSET + 4].view(torch.int32).item())
+
+
+def pi_sparse_ffn_h_offset(ffn, batch: int) -> tuple[int, int]:
+    """(byte offset, kind) of the h table a pi_sparse_ffn call leaves in its workspace."""
+    kind = ctypes.c_int32(0)
+    off = int(lib().pi_sparse_ffn_h_offset(_byref(ffn), batch, ctypes.byref(kind)))
+    if off == (1 << 64) - 1:
+        raise PiError("pi_sparse_ffn_h_offset", PI_ERR_SHAPE)
+    return off, int(kind.value)
+
+
+def sparse_ffn_h(ffn, batch: int, ws: torch.Tensor, n: int) -> tuple[torch.Tensor, torch.Tensor]:
+    """h [batch][n] (fp32) and the slot-valid flags [n] that the last pi_sparse_ffn call on `ws` left
+    for list positions 0..n-1 (a device-side view, for counting the rows that had to be read)."""
+    off, kind = pi_sparse_ffn_h_offset(ffn, batch)
+    if kind == 1:
+        words = ws[off: off + 8 * n * (1 + batch)].view(torch.int32).view(n, 2 * (1 + batch))
+        h = words[:, 2::2].contiguous().view(torch.float32).t()
+        ok = words[:, 0] >= 0
+        return h, ok
+    stride = max(int(ffn.n_slots), 1)
+    h = ws[off: off + 4 * batch * stride].view(torch.float32).view(batch, stride)[:, :n]
+    return h, torch.ones(n, dtype=torch.bool, device=ws.device)
 
 
 def pi_status_string(code: int) -> str:

@@ -13,32 +13,57 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libpi.so")
-SOURCES = [os.path.join(PKG, "csrc", "pi_abi.hip")]
-DEPENDS = SOURCES + [os.path.join(PKG, "csrc", "pi_kernels.hpp"), os.path.join(ROOT, "include", "pi_sparse_ffn.h")]
+CSRC = os.path.join(PKG, "csrc")
+SOURCES = [os.path.join(CSRC, "pi_abi.hip"), os.path.join(CSRC, "pi_fused_b.hip")]
+DEPENDS = SOURCES + [os.path.join(CSRC, "pi_kernels.hpp"), os.path.join(CSRC, "pi_fused.hpp"),
+                     os.path.join(ROOT, "include", "pi_sparse_ffn.h")]
+OBJDIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+NOISE = "is not a recognized feature for this target"
 
 
-def command(out: str = LIB) -> list[str]:
-    return [HIPCC, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            "-I", os.path.join(ROOT, "include"), "-o", out] + SOURCES
+def _units():
+    """(source, object, extra flags): the ABI unit plus one fused-kernel unit per batch width."""
+    units = [(SOURCES[0], os.path.join(OBJDIR, "pi_abi.o"), [])]
+    for b in range(1, 9):
+        units.append((SOURCES[1], os.path.join(OBJDIR, f"pi_fused_b{b}.o"), [f"-DPIK_B={b}"]))
+    return units
 
 
-def build(verbose: bool = False) -> str:
-    """Compile libpi.so (always; the build is the 'does it build' check)."""
+def _clean(stderr: str) -> str:
+    return "\n".join(l for l in stderr.splitlines() if NOISE not in l)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every unit (in parallel) and link libpi.so; always rebuilds."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    jobs = jobs or min(8, os.cpu_count() or 4)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    pending = [[HIPCC, *FLAGS, *inc, *extra, "-c", src, "-o", obj] for src, obj, extra in _units()]
+    running = []
+    while pending or running:
+        while pending and len(running) < jobs:
+            cmd = pending.pop(0)
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            running.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+        cmd, proc = running.pop(0)
+        out, err = proc.communicate()
+        if proc.returncode != 0:
+            for _, p in running:
+                p.wait()
+            raise RuntimeError(f"hipcc failed ({proc.returncode}) on {cmd[-3]}:\n{_clean(err)}")
     tmp = LIB + ".tmp"
-    cmd = command(tmp)
+    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp] + [obj for _, obj, _ in _units()]
     if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+        print(" ".join(link), flush=True)
+    res = subprocess.run(link, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
+        raise RuntimeError(f"link failed:\n{_clean(res.stderr)}")
     os.replace(tmp, LIB)
     return LIB
 

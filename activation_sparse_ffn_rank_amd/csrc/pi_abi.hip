@@ -6,6 +6,7 @@
 // No C++ exception crosses the ABI.
 #include "pi_sparse_ffn.h"
 #include "pi_kernels.hpp"
+#include "pi_fused.hpp"
 
 #include <algorithm>
 
@@ -81,8 +82,51 @@ size_t ffn_h_bytes(const pi_ffn *f, int B) { return align_up((size_t)B * std::ma
 size_t ffn_part_bytes(const pi_ffn *f, int B) {
     return align_up((size_t)down_chunks(f->d_model) * B * f->d_model * sizeof(float));
 }
-size_t ffn_ws(const pi_ffn *f, int B) {
+size_t ffn_legacy_ws(const pi_ffn *f, int B) {
     return ffn_h_bytes(f, B) + ffn_part_bytes(f, B) + align_up((size_t)down_slabs(f->d_model) * sizeof(int32_t));
+}
+
+// Both persistent kernels keep x [B][d] (fp16) in LDS next to their static arrays (4*B*8*64
+// floats of wave partials and ~2 KB of indices); all of it must fit one workgroup.
+bool persistent_fits(int d, int B) {
+    const size_t x = (size_t)B * d * 2, fixed = (size_t)B * 8192 + 4096;
+    return x <= (size_t)kLdsXBytes && x + fixed <= 160 * 1024;
+}
+
+// Geometry of the persistent sparse-FFN kernel: groups of 4 listed neurons (at most
+// ceil(n_slots / 4) of them), slab x chunk down tiles.  Scratch: the control block, one stamped
+// header per group, (1 + B) stamped words per entry, stamped chunk partials [C][B][d].
+struct SparseGeom {
+    int slabs, C, NE, NDmax;
+    size_t ctl, ghead, ent, part;
+};
+
+size_t ctl_bytes(int d) { return align_up((size_t)(CTL_LAYER0 + ctl_layer_stride(down_slabs(d))) * sizeof(int32_t)); }
+
+SparseGeom sparse_geom(const pi_ffn *fn, int B) {
+    SparseGeom g;
+    const int d = fn->d_model;
+    g.NDmax = std::max(1, ceil_div(fn->n_slots, 4));
+    g.slabs = down_slabs(d);
+    g.C = std::min(kFusedMaxChunks, std::max(1, std::min(g.NDmax, ceil_div(kDownTargetTiles, g.slabs))));
+    g.NE = g.slabs * g.C;
+    g.ctl = ctl_bytes(d);
+    g.ghead = align_up((size_t)g.NDmax * sizeof(uint64_t));
+    g.ent = align_up((size_t)g.NDmax * 4 * (1 + B) * sizeof(uint64_t));
+    g.part = align_up((size_t)g.C * B * d * sizeof(uint64_t));
+    return g;
+}
+
+bool sparse_persistent(const pi_ffn *fn, int B) { return persistent_fits(fn->d_model, B); }
+
+// Scratch of pi_sparse_ffn: the persistent kernel's regions (control block first, so that the
+// status word sits at a fixed offset), or the two-kernel path's when x does not fit LDS.
+size_t ffn_ws(const pi_ffn *f, int B) {
+    if (sparse_persistent(f, B)) {
+        const SparseGeom g = sparse_geom(f, B);
+        return g.ctl + g.ghead + g.ent + g.part;
+    }
+    return ffn_legacy_ws(f, B);
 }
 
 FfnScratch ffn_scratch(const pi_ffn *f, int B, void *base) {
@@ -96,6 +140,41 @@ FfnScratch ffn_scratch(const pi_ffn *f, int B, void *base) {
 
 size_t layer_extra_ws(int f) {
     return align_up((size_t)f) + align_up((size_t)f * sizeof(int32_t)) + align_up(2 * sizeof(int32_t));
+}
+
+// ------------------------------------------------------------------ fused layer geometry
+
+struct FusedGeom {
+    int NT, TPD, NA, NB, ND, slabs, C, NE;
+    size_t ctl, z, tword, ghead, ent, part;   // region sizes (aligned); tword also sizes pword
+};
+
+FusedGeom fused_geom(const pi_predictor *p, const pi_ffn *fn, int B) {
+    FusedGeom g;
+    const int f = p->d_ffn, d = p->d_model, r = p->rank;
+    g.NT = r <= 512 ? 1 : (r <= 1024 ? 2 : 4);
+    g.TPD = std::min(4, std::max(1, (f + 8192) / 16384));
+    g.NA = ceil_div(r, 4);
+    g.NB = ceil_div(f, kTile);
+    g.ND = ceil_div(g.NB, g.TPD);
+    g.slabs = down_slabs(d);
+    g.C = std::min(kFusedMaxChunks, std::max(1, std::min(g.ND, ceil_div(kDownTargetTiles, g.slabs))));
+    g.NE = g.slabs * g.C;
+    g.ctl = ctl_bytes(d);
+    g.z = align_up((size_t)B * r * sizeof(uint64_t));
+    g.tword = align_up((size_t)g.NB * sizeof(uint64_t));
+    g.ghead = align_up((size_t)g.ND * sizeof(uint64_t));
+    g.ent = align_up((size_t)g.ND * kTile * g.TPD * (1 + B) * sizeof(uint64_t));
+    g.part = align_up((size_t)g.C * B * d * sizeof(uint64_t));
+    (void)fn;
+    return g;
+}
+
+size_t fused_ws(const FusedGeom &g) { return g.ctl + g.z + 2 * g.tword + g.ghead + g.ent + g.part; }
+
+bool fused_eligible(const pi_predictor *p, const pi_ffn *fn, int B) {
+    (void)p;
+    return persistent_fits(fn->d_model, B);
 }
 
 int launch_status() { return hipGetLastError() == hipSuccess ? PI_OK : PI_ERR_HIP; }
@@ -167,7 +246,7 @@ int enqueue_sparse_bt(const pi_ffn *fn, const uint16_t *x, const int32_t *idx, c
     return enqueue_sparse_b<B, false, WT_F16>(fn, x, idx, counts, y, sc, st);
 }
 
-int enqueue_sparse(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y,
+int enqueue_sparse_legacy(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y,
                    const FfnScratch &sc, hipStream_t st) {
     const uint16_t *xx = static_cast<const uint16_t *>(x);
     switch (B) {
@@ -183,6 +262,102 @@ int enqueue_sparse(const pi_ffn *fn, const void *x, int B, const int32_t *idx, c
     return PI_ERR_BATCH;
 }
 
+// The persistent sparse-FFN kernel; ctl is the control block (shared with the fused layer kernel
+// inside a layer workspace), data the group headers, entries and partials.
+int enqueue_sparse_persistent(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts,
+                              float *y, int32_t *ctl, char *data, hipStream_t st, uint64_t *trace = nullptr) {
+    const SparseGeom g = sparse_geom(fn, B);
+    FusedArgs a{};
+    a.d = fn->d_model; a.f = fn->d_ffn; a.n_slots = fn->n_slots;
+    a.slabs = g.slabs; a.C = g.C; a.NE = g.NE; a.ND = g.NDmax; a.cap = 4;
+    a.row_bytes = row_bytes_of(fn);
+    a.w_in = static_cast<const uint8_t *>(fn->w_in); a.w_dn = static_cast<const uint8_t *>(fn->w_down_t);
+    a.b_up = static_cast<const uint16_t *>(fn->b_up); a.b_down = static_cast<const uint16_t *>(fn->b_down);
+    a.slot_of = fn->slot_of;
+    a.x = static_cast<const uint16_t *>(x); a.y = y;
+    a.idx_in = idx; a.counts_in = counts;
+    a.ctl = ctl;
+    a.ghead = reinterpret_cast<uint64_t *>(data); data += g.ghead;
+    a.ent = reinterpret_cast<uint64_t *>(data); data += g.ent;
+    a.part = reinterpret_cast<uint64_t *>(data);
+#ifdef PIK_TRACE
+    a.trace = trace;
+#else
+    (void)trace;
+#endif
+    const int wt = fn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16;
+    int rc;
+    switch (B) {
+        case 1: rc = launch_sparse_batch<1>(a, wt, fn->gated, st); break;
+        case 2: rc = launch_sparse_batch<2>(a, wt, fn->gated, st); break;
+        case 3: rc = launch_sparse_batch<3>(a, wt, fn->gated, st); break;
+        case 4: rc = launch_sparse_batch<4>(a, wt, fn->gated, st); break;
+        case 5: rc = launch_sparse_batch<5>(a, wt, fn->gated, st); break;
+        case 6: rc = launch_sparse_batch<6>(a, wt, fn->gated, st); break;
+        case 7: rc = launch_sparse_batch<7>(a, wt, fn->gated, st); break;
+        case 8: rc = launch_sparse_batch<8>(a, wt, fn->gated, st); break;
+        default: return PI_ERR_BATCH;
+    }
+    return rc == 0 ? PI_OK : PI_ERR_HIP;
+}
+
+// pi_sparse_ffn's work on a workspace laid out by ffn_ws (ctl: the control block to use).
+int enqueue_sparse(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y,
+                   void *ws, int32_t *ctl, hipStream_t st) {
+    if (sparse_persistent(fn, B)) {
+        char *w = static_cast<char *>(ws);
+        return enqueue_sparse_persistent(fn, x, B, idx, counts, y, ctl ? ctl : reinterpret_cast<int32_t *>(w),
+                                         w + sparse_geom(fn, B).ctl, st);
+    }
+    return enqueue_sparse_legacy(fn, x, B, idx, counts, y, ffn_scratch(fn, B, ws), st);
+}
+
+int enqueue_fused(const pi_predictor *p, const pi_ffn *fn, const void *x, int B, float *y, uint8_t *mask_out,
+                  int32_t *idx_out, int32_t *counts_out, void *ws, hipStream_t st, uint64_t *trace = nullptr) {
+    const FusedGeom g = fused_geom(p, fn, B);
+    char *w = static_cast<char *>(ws);
+    FusedArgs a{};
+    a.d = p->d_model; a.f = p->d_ffn; a.r = p->rank; a.n_slots = fn->n_slots;
+    a.slabs = g.slabs; a.C = g.C; a.TPD = g.TPD; a.NA = g.NA; a.NB = g.NB; a.ND = g.ND; a.NE = g.NE;
+    a.cap = kTile * g.TPD;
+    a.want_x = (idx_out != nullptr || counts_out != nullptr) ? 1 : 0;
+    a.tasks = g.NA + g.NB + g.ND + g.NE + a.want_x;
+    a.row_bytes = row_bytes_of(fn);
+    a.p1 = static_cast<const uint16_t *>(p->p1); a.p2 = static_cast<const uint16_t *>(p->p2);
+    a.c = static_cast<const uint16_t *>(p->c);
+    a.w_in = static_cast<const uint8_t *>(fn->w_in); a.w_dn = static_cast<const uint8_t *>(fn->w_down_t);
+    a.b_up = static_cast<const uint16_t *>(fn->b_up); a.b_down = static_cast<const uint16_t *>(fn->b_down);
+    a.slot_of = fn->slot_of;
+    a.x = static_cast<const uint16_t *>(x); a.y = y;
+    a.mask_out = mask_out; a.idx_out = idx_out; a.counts_out = counts_out;
+    a.ctl = reinterpret_cast<int32_t *>(w); w += g.ctl;
+    a.z = reinterpret_cast<uint64_t *>(w); w += g.z;
+    a.tword = reinterpret_cast<uint64_t *>(w); w += g.tword;
+    a.pword = reinterpret_cast<uint64_t *>(w); w += g.tword;
+    a.ghead = reinterpret_cast<uint64_t *>(w); w += g.ghead;
+    a.ent = reinterpret_cast<uint64_t *>(w); w += g.ent;
+    a.part = reinterpret_cast<uint64_t *>(w);
+#ifdef PIK_TRACE
+    a.trace = trace;
+#else
+    (void)trace;
+#endif
+    const int wt = fn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16;
+    int rc;
+    switch (B) {
+        case 1: rc = launch_fused_batch<1>(a, wt, fn->gated, g.NT, st); break;
+        case 2: rc = launch_fused_batch<2>(a, wt, fn->gated, g.NT, st); break;
+        case 3: rc = launch_fused_batch<3>(a, wt, fn->gated, g.NT, st); break;
+        case 4: rc = launch_fused_batch<4>(a, wt, fn->gated, g.NT, st); break;
+        case 5: rc = launch_fused_batch<5>(a, wt, fn->gated, g.NT, st); break;
+        case 6: rc = launch_fused_batch<6>(a, wt, fn->gated, g.NT, st); break;
+        case 7: rc = launch_fused_batch<7>(a, wt, fn->gated, g.NT, st); break;
+        case 8: rc = launch_fused_batch<8>(a, wt, fn->gated, g.NT, st); break;
+        default: return PI_ERR_BATCH;
+    }
+    return rc == 0 ? PI_OK : PI_ERR_HIP;
+}
+
 }  // namespace
 
 // ==================================================================== C ABI
@@ -195,7 +370,8 @@ size_t pi_workspace_bytes(const pi_predictor *pred, const pi_ffn *ffn, int32_t b
     if (ffn && check_ffn(ffn) != PI_OK) return 0;
     if (pred && ffn) {
         if (pred->d_model != ffn->d_model || pred->d_ffn != ffn->d_ffn) return 0;
-        return pred_ws(pred, batch) + layer_extra_ws(pred->d_ffn) + ffn_ws(ffn, batch);
+        return fused_ws(fused_geom(pred, ffn, batch)) + pred_ws(pred, batch) + layer_extra_ws(pred->d_ffn) +
+               ffn_ws(ffn, batch);
     }
     return pred ? pred_ws(pred, batch) : ffn_ws(ffn, batch);
 }
@@ -228,7 +404,7 @@ int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t
     if (!aligned16(x)) return PI_ERR_ALIGN;
     if (!ws || ws_bytes < ffn_ws(ffn, batch)) return PI_ERR_WORKSPACE;
     if (!aligned16(ws)) return PI_ERR_ALIGN;
-    return enqueue_sparse(ffn, x, batch, idx, counts, y, ffn_scratch(ffn, batch, ws), static_cast<hipStream_t>(stream));
+    return enqueue_sparse(ffn, x, batch, idx, counts, y, ws, nullptr, static_cast<hipStream_t>(stream));
 }
 
 int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y,
@@ -245,7 +421,8 @@ int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int
     if (!ws || ws_bytes < need) return PI_ERR_WORKSPACE;
     if (!aligned16(ws)) return PI_ERR_ALIGN;
     const int f = pred->d_ffn;
-    char *p = static_cast<char *>(ws);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *p = static_cast<char *>(ws) + fused_ws(fused_geom(pred, ffn, batch));
     float *z = reinterpret_cast<float *>(p);
     p += pred_ws(pred, batch);
     uint8_t *mask = reinterpret_cast<uint8_t *>(p);
@@ -254,14 +431,41 @@ int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int
     p += align_up((size_t)f * sizeof(int32_t));
     int32_t *counts = reinterpret_cast<int32_t *>(p);
     p += align_up(2 * sizeof(int32_t));
-    const FfnScratch sc = ffn_scratch(ffn, batch, p);
     if (mask_out) mask = mask_out;
     if (idx_out) idx = idx_out;
     if (counts_out) counts = counts_out;
-    hipStream_t st = static_cast<hipStream_t>(stream);
     if ((rc = enqueue_predict(pred, x, batch, mask, nullptr, z, st))) return rc;
     if ((rc = enqueue_compact(mask, f, ffn->slot_of, idx, counts, st))) return rc;
-    return enqueue_sparse(ffn, x, batch, idx, counts, y, sc, st);
+    // the sparse kernel shares the control block at the start of the workspace
+    return enqueue_sparse(ffn, x, batch, idx, counts, y, p, static_cast<int32_t *>(ws), st);
+}
+
+int pi_ffn_layer_fused(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y,
+                       uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws, size_t ws_bytes,
+                       void *stream) {
+    int rc = check_pred(pred);
+    if (rc) return rc;
+    if ((rc = check_ffn(ffn))) return rc;
+    if ((rc = check_batch(batch))) return rc;
+    if (pred->d_model != ffn->d_model || pred->d_ffn != ffn->d_ffn) return PI_ERR_SHAPE;
+    if (!x || !y) return PI_ERR_NULL;
+    if (!aligned16(x)) return PI_ERR_ALIGN;
+    if (!fused_eligible(pred, ffn, batch)) return PI_ERR_SHAPE;
+    const size_t need = pi_workspace_bytes(pred, ffn, batch);
+    if (!ws || ws_bytes < need) return PI_ERR_WORKSPACE;
+    if (!aligned16(ws)) return PI_ERR_ALIGN;
+    return enqueue_fused(pred, ffn, x, batch, y, mask_out, idx_out, counts_out, ws, static_cast<hipStream_t>(stream));
+}
+
+size_t pi_sparse_ffn_h_offset(const pi_ffn *ffn, int32_t batch, int32_t *kind) {
+    if (check_ffn(ffn) != PI_OK || check_batch(batch) != PI_OK || !kind) return (size_t)-1;
+    if (sparse_persistent(ffn, batch)) {
+        const SparseGeom g = sparse_geom(ffn, batch);
+        *kind = 1;
+        return g.ctl + g.ghead;
+    }
+    *kind = 2;
+    return 0;
 }
 
 const char *pi_status_string(int status) {
@@ -279,5 +483,25 @@ const char *pi_status_string(int status) {
 }
 
 int pi_version(void) { return 100; }
+
+#ifdef PIK_TRACE
+// Diagnostic build only: pi_ffn_layer through the fused kernel with per-task timestamps.
+int pi_trace_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y, void *ws,
+                   uint64_t *trace, int32_t *tasks_out, void *stream) {
+    const FusedGeom g = fused_geom(pred, ffn, batch);
+    *tasks_out = g.NA + g.NB + g.ND + g.NE;
+    return enqueue_fused(pred, ffn, x, batch, y, nullptr, nullptr, nullptr, ws, static_cast<hipStream_t>(stream),
+                         trace);
+}
+
+int pi_trace_sparse(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx, const int32_t *counts,
+                    float *y, void *ws, uint64_t *trace, int32_t *ne_out, void *stream) {
+    if (!sparse_persistent(ffn, batch)) return PI_ERR_SHAPE;
+    *ne_out = sparse_geom(ffn, batch).NE;
+    char *w = static_cast<char *>(ws);
+    return enqueue_sparse_persistent(ffn, x, batch, idx, counts, y, reinterpret_cast<int32_t *>(w),
+                                     w + sparse_geom(ffn, batch).ctl, static_cast<hipStream_t>(stream), trace);
+}
+#endif
 
 }  // extern "C"

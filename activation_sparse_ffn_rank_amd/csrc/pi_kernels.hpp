@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void k_pred_l2(const uint16_t *__restrict__ p2
 // a register (re-reading only beyond that), and a single block prefix sum over the per-thread
 // counts gives every listed neuron its position -- so idx is ascending.  counts = {listed,
 // predicted}.
-__global__ __launch_bounds__(1024) void k_compact(const uint8_t *__restrict__ mask, int f,
+static __global__ __launch_bounds__(1024) void k_compact(const uint8_t *__restrict__ mask, int f,
                                                   const int32_t *__restrict__ slot_of, int32_t *__restrict__ idx,
                                                   int32_t *__restrict__ counts) {
     __shared__ int wsum[16], wpred[16];

@@ -52,7 +52,8 @@ class DeviceLayer:
         return int(self.w_in.shape[0])
 
     def workspace(self, batch: int, device="cuda") -> torch.Tensor:
+        """Zero-filled workspace for pi_ffn_layer (it must start zeroed; calls leave it ready)."""
         n = _abi.pi_workspace_bytes(self.pred, self.ffn, batch)
         if n == 0:
             raise ValueError("invalid layer for the C ABI")
-        return torch.empty(n, dtype=torch.uint8, device=device)
+        return torch.zeros(n, dtype=torch.uint8, device=device)

@@ -8,8 +8,9 @@ are resident in HBM before timing starts.  W warmup steps and K timed steps are 
 HIP graphs captured on one stream; the timed region is bracketed by device synchronizations.
 
 Printed: one JSON line with tokens/s, ms per step, per-layer microseconds, the roofline of the
-sparse-FFN kernels on the bytes they must read (HIP events on the launch stream, eager pass),
-and the CPU oracle's rate on a bounded sample of the same workload.
+sparse-FFN kernel on the bytes it must read (HIP events on the launch stream around a graph of its
+launches), and
+the CPU oracle's rate on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -35,7 +36,7 @@ def parse():
     ap.add_argument("--config", type=int, default=2, help="layer-stack configuration id (1-5)")
     ap.add_argument("--batch", type=int, default=1)
     ap.add_argument("--layers", type=int, default=0, help="use only the first N layers (0 = all)")
-    ap.add_argument("--roofline-steps", type=int, default=32, help="eager steps timed per kernel group")
+    ap.add_argument("--roofline-steps", type=int, default=16, help="tokens whose launches the roofline pass times")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph replay")
@@ -78,12 +79,11 @@ def main():
 
     ws = layers[0].workspace(B, device=dev)
     y = torch.empty((L, B, cfg.d), dtype=torch.float32, device=dev)
-    counts = torch.zeros((W + K, L, 2), dtype=torch.int32, device=dev)
 
     def step(t):
         for l in range(L):
             lay = layers[l]
-            _abi.pi_ffn_layer(lay.pred, lay.ffn, xd[t, l], B, y[l], None, None, counts[t, l], ws)
+            _abi.pi_ffn_layer(lay.pred, lay.ffn, xd[t, l], B, y[l], None, None, None, ws)
 
     # ------------------------------------------------------------------ graph capture + timing
     stream = torch.cuda.Stream(device=dev)
@@ -114,85 +114,105 @@ def main():
         ev1.record(stream)
         torch.cuda.synchronize()
         elapsed_ms = ev0.elapsed_time(ev1)
+    status = _abi.workspace_status(ws)
+    if status != 0:
+        raise RuntimeError(f"workspace status {status}: a cross-workgroup wait timed out; results invalid")
     log(f"timed {K} steps: {elapsed_ms:.3f} ms")
 
-    cnt = counts[W:].cpu().numpy()                              # [K][L][2]
-    n_act = cnt[..., 0].astype(np.float64)
-    n_pred = cnt[..., 1].astype(np.float64)
-
-    # ------------------------------------------------------------------ bytes per step
+    # ------------------------------------------------------------------ roofline pass (HIP events)
+    # The sparse FFN (gathered up/gate rows + active rows of W_down^T) is one kernel, pi_sparse_ffn.
+    # An eager pass runs pi_predict and pi_compact on R tokens x L layers, keeps every index list,
+    # runs pi_sparse_ffn once per list and counts from the h table it leaves in its workspace the
+    # listed neurons whose h is nonzero for some token: the rows of W_down^T the kernel must read.
+    # Then the R*L launches of each entry point are captured into a graph of their own and timed
+    # with HIP events on the launch stream around its replay: elapsed / launches is the average
+    # launch duration, back to back as in the decode step.
+    R = min(args.roofline_steps, K)
+    N = R * L
     rb = cfg.row_bytes()
     in_rows = 2 if cfg.gated else 1
     pred_bytes = 2 * (cfg.r * cfg.d + cfg.f * cfg.r + cfg.f)
-    act_bytes = n_act * (in_rows + 1) * rb                       # [K][L] predicted-active rows
-    step_bytes = (pred_bytes * L + act_bytes.sum(axis=1))        # per step
-
-    # ------------------------------------------------------------------ roofline pass (eager, HIP events)
-    R = min(args.roofline_steps, K)
-    seg = {"predict": 0.0, "compact": 0.0, "sparse_ffn": 0.0}
-    touched_down = 0.0
-    act_rows_rf = 0.0
-    mask = torch.empty(cfg.f, dtype=torch.uint8, device=dev)
-    idx = torch.empty(cfg.f, dtype=torch.int32, device=dev)
-    cnt1 = torch.empty(2, dtype=torch.int32, device=dev)
+    masks = torch.empty((N, cfg.f), dtype=torch.uint8, device=dev)
+    idx_all = torch.empty((N, cfg.f), dtype=torch.int32, device=dev)
+    cnt_all = torch.empty((N, 2), dtype=torch.int32, device=dev)
     ws_p = torch.empty(_abi.pi_workspace_bytes(layers[0].pred, None, B), dtype=torch.uint8, device=dev)
-    ws_f = torch.empty(_abi.pi_workspace_bytes(None, layers[0].ffn, B), dtype=torch.uint8, device=dev)
-    h_view = ws_f[: B * layers[0].n_slots * 4].view(torch.float32).view(B, layers[0].n_slots)
-    with torch.cuda.stream(stream):
-        evs = []
-        for t in range(W, W + R):
-            for l in range(L):
-                lay = layers[l]
-                e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-                e[0].record(stream)
-                _abi.pi_predict(lay.pred, xd[t, l], B, mask, None, ws_p)
-                e[1].record(stream)
-                _abi.pi_compact(mask, cfg.f, lay.slot_of, idx, cnt1)
-                e[2].record(stream)
-                _abi.pi_sparse_ffn(lay.ffn, xd[t, l], B, idx, cnt1, y[l], ws_f)
-                e[3].record(stream)
-                n = cnt1[0]
-                nz = (h_view[:, :].narrow(1, 0, lay.n_slots) != 0).any(dim=0)
-                k = torch.arange(lay.n_slots, device=dev) < n
-                evs.append((e, (nz & k).sum(), n))
-        torch.cuda.synchronize()
-    for e, nz, n in evs:
-        seg["predict"] += e[0].elapsed_time(e[1])
-        seg["compact"] += e[1].elapsed_time(e[2])
-        seg["sparse_ffn"] += e[2].elapsed_time(e[3])
-        touched_down += float(nz)
-        act_rows_rf += float(n)
-    launches = R * L
-    us = {k: v * 1000.0 / launches for k, v in seg.items()}     # per layer launch
-    ffn_alg_bytes = act_rows_rf * in_rows * rb + touched_down * rb   # bytes the FFN kernels must read
-    ffn_pred_bytes = act_rows_rf * (in_rows + 1) * rb
-    ffn_gbs = ffn_alg_bytes / launches / (us["sparse_ffn"] * 1e-6) / 1e9
-    pred_gbs = pred_bytes / (us["predict"] * 1e-6) / 1e9
+    ws_f = torch.zeros(_abi.pi_workspace_bytes(None, layers[0].ffn, B), dtype=torch.uint8, device=dev)
+    y_chk = torch.empty((B, cfg.d), dtype=torch.float32, device=dev)
+    ns = layers[0].n_slots
+    ar = torch.arange(ns, device=dev)
+    cases = [(W + i // L, i % L) for i in range(N)]             # (token, layer) of launch i
 
+    def run_predict():
+        for i, (t, l) in enumerate(cases):
+            _abi.pi_predict(layers[l].pred, xd[t, l], B, masks[i], None, ws_p)
+
+    def run_compact():
+        for i, (t, l) in enumerate(cases):
+            _abi.pi_compact(masks[i], cfg.f, layers[l].slot_of, idx_all[i], cnt_all[i])
+
+    def run_ffn():
+        for i, (t, l) in enumerate(cases):
+            _abi.pi_sparse_ffn(layers[l].ffn, xd[t, l], B, idx_all[i], cnt_all[i], y_chk, ws_f)
+
+    with torch.cuda.stream(stream):
+        run_predict()
+        run_compact()
+        live = []
+        for i, (t, l) in enumerate(cases):
+            _abi.pi_sparse_ffn(layers[l].ffn, xd[t, l], B, idx_all[i], cnt_all[i], y_chk, ws_f)
+            h, ok = _abi.sparse_ffn_h(layers[l].ffn, B, ws_f, ns)
+            live.append(((h != 0).any(dim=0) & ok & (ar < cnt_all[i, 0])).sum())
+        torch.cuda.synchronize()
+        n_live = torch.stack(live).cpu().numpy().astype(np.float64)
+        cnt_host = cnt_all.cpu().numpy().astype(np.float64)
+        leg_us = {}
+        for name, fn in (("predict", run_predict), ("compact", run_compact), ("sparse_ffn", run_ffn)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                fn()
+            g.replay()                                          # warm
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            leg_us[name] = e0.elapsed_time(e1) * 1000.0 / N
+            del g
+    if _abi.workspace_status(ws_f) != 0:
+        raise RuntimeError("sparse-FFN workspace status nonzero: a cross-workgroup wait timed out")
+    n_act, n_pred = cnt_host[:, 0], cnt_host[:, 1]
+    vec_bytes = B * cfg.d * (2 + 4) + 2 * cfg.d                  # x in, y out, b_down
+    ffn_touched = n_act * in_rows * rb + n_live * rb + 8 * n_act + vec_bytes   # + idx and slot lookups
+    ffn_predicted = n_act * (in_rows + 1) * rb + 8 * n_act + vec_bytes
+    ffn_us = leg_us["sparse_ffn"]
+    ffn_gbs = float(ffn_touched.mean()) / (ffn_us * 1e-6) / 1e9
+    step_bytes = (pred_bytes + float(ffn_touched.mean())) * L
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
         budget = args.cpu_seconds
-        done, spent, l = 0, 0.0, 0
-        while spent < budget and done < 4 * L:
-            host = synth.make_layer(cfg, l % L)
-            x = x_all[W, l % L]
-            s0 = time.perf_counter()
-            oracle.ffn_layer(host, x, want_logits=False)
-            spent += time.perf_counter() - s0
-            done += 1
-            l += 1
-            del host
+        n_lay = min(L, 4)
+        hosts = [synth.make_layer(cfg, l) for l in range(n_lay)]
+        done, spent, t = 0, 0.0, 0
+        while spent < budget:
+            for l in range(n_lay):
+                s0 = time.perf_counter()
+                oracle.ffn_layer(hosts[l], x_all[t % (W + K), l], want_logits=False)
+                spent += time.perf_counter() - s0
+                done += 1
+            t += 1
+        del hosts
         per_layer = spent / done
-        cpu = {"value": B / (per_layer * L), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-               "sample": f"{done} (layer, batch) evaluations of the full layer (predictor + mask + compaction + "
-                         f"sparse FFN) at batch {B}, first token, layers 0..{min(done, L) - 1}; "
-                         f"{spent:.1f}s, {per_layer * 1e3:.1f} ms per layer, scaled to a {L}-layer step"}
+        cpu = {"value": round(B / (per_layer * L), 3), "unit": "tokens/s", "cores": oracle.num_threads(),
+               "kind": "oracle",
+               "sample": f"{done} evaluations of the whole layer (predictor, mask, compaction, sparse FFN) at "
+                         f"batch {B}: layers 0..{n_lay - 1} of the same stack, tokens 0..{t - 1} of the seeded "
+                         f"inputs; {spent:.1f}s, {per_layer * 1e3:.2f} ms per layer, scaled to the {L}-layer step"}
 
     ms_per_step = elapsed_ms / K
     tokens_per_s = B * K / (elapsed_ms / 1e3)
-    step_gb = float(step_bytes.mean()) / 1e9
     out = {
         "metric": "sparse-FFN decode tokens/s (batch 1) + achieved HBM GB/s on active-row bytes",
         "value": round(tokens_per_s, 2),
@@ -216,26 +236,30 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "pi_sparse_ffn (k_sparse_up + k_sparse_down + k_reduce_y)",
+            "kernel": "k_sparse_fused (pi_sparse_ffn: gathered up/gate rows with ReLU/ReGLU + active rows of W_down^T)",
             "achieved": round(ffn_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(ffn_gbs / PEAK_HBM_GBS, 4),
             "traffic": None,
+            "bytes_per_launch": round(float(ffn_touched.mean())),
+            "launch_us": round(ffn_us, 3),
+            "launches": int(N),
         },
         "cpu_baseline": cpu,
         "detail": {
             "us_per_layer": round(ms_per_step * 1000.0 / L, 3),
-            "step_gb_algorithmic": round(step_gb, 4),
-            "step_gbs": round(step_gb / (ms_per_step / 1e3), 1),
+            "graph_us_predict": round(leg_us["predict"], 3),
+            "graph_us_compact": round(leg_us["compact"], 3),
+            "graph_us_sparse_ffn": round(ffn_us, 3),
+            "predictor_bytes": pred_bytes,
+            "ffn_bytes_predicted_rows": round(float(ffn_predicted.mean())),
+            "step_gb_touched": round(step_bytes / 1e9, 4),
+            "step_gbs": round(step_bytes / 1e9 / (ms_per_step / 1e3), 1),
             "active_density": round(float(n_act.mean()) / cfg.f, 4),
             "predicted_density": round(float(n_pred.mean()) / cfg.f, 4),
             "covered_share": round(float(n_act.sum() / max(n_pred.sum(), 1)), 4),
-            "eager_us_per_layer": {k: round(v, 3) for k, v in us.items()},
-            "predict_gbs": round(pred_gbs, 1),
-            "ffn_bytes_per_layer_touched": round(ffn_alg_bytes / launches),
-            "ffn_bytes_per_layer_predicted": round(ffn_pred_bytes / launches),
-            "down_rows_skipped_share": round(1.0 - touched_down / max(act_rows_rf, 1), 4),
+            "down_rows_skipped_share": round(1.0 - float(n_live.sum()) / max(float(n_act.sum()), 1.0), 4),
         },
     }
     print(json.dumps(out), flush=True)

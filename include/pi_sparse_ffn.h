@@ -110,16 +110,47 @@ int pi_compact(const uint8_t *mask, int32_t d_ffn, const int32_t *slot_of, int32
 /* Neuron-aware sparse FFN over idx[0..counts[0]) (method section: sparse operators that
  * compute only the active neurons).  idx and counts are device memory (as pi_compact writes
  * them); n is clamped to [0, n_slots] and entries whose neuron or slot is out of range are
- * skipped.  y [batch][d_model] fp32 is overwritten. */
+ * skipped.  y [batch][d_model] fp32 is overwritten.
+ * When batch * d_model <= 32768 this is ONE persistent kernel: workgroups computing h for groups
+ * of four listed neurons hand (slot, h) entries to the workgroups that accumulate the rows of
+ * W_down^T, through the workspace.  Then:
+ *  - the workspace must be zero-filled before the first call that uses it, and each call leaves
+ *    it ready for the next one (never clear or share it while a call is in flight);
+ *  - the int32 at byte offset 384 of the workspace is a sticky status word: nonzero means a
+ *    cross-workgroup wait ran out its time limit (20 ms) and the outputs of that call are invalid.
+ * Every wait inside the kernel is bounded.  Larger shapes run two kernels (h, then the rows of
+ * W_down^T) and need no zero fill. */
 int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx,
                   const int32_t *counts, float *y, void *ws, size_t ws_bytes, void *stream);
 
-/* Whole layer: pi_predict -> pi_compact -> pi_sparse_ffn.  pred and ffn must agree on
- * d_model and d_ffn.  mask_out [d_ffn], idx_out [d_ffn] and counts_out [2] receive the
- * intermediate results when non-NULL (otherwise they live in the workspace). */
+/* Whole layer: pi_predict -> pi_compact -> pi_sparse_ffn, stream-ordered.  pred and ffn must
+ * agree on d_model and d_ffn.  mask_out [d_ffn], idx_out [d_ffn] and counts_out [2] receive the
+ * intermediate results when non-NULL (otherwise they live in the workspace).  The workspace
+ * rules of pi_sparse_ffn apply (zero-filled before first use; status word at byte offset 384). */
 int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch,
                  float *y, uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws,
                  size_t ws_bytes, void *stream);
+
+/* The same layer as ONE persistent kernel whose workgroups hand work to each other through the
+ * workspace (same arguments and results as pi_ffn_layer).  Requires batch * d_model <= 32768 so
+ * that x and the kernel's own arrays fit one workgroup's LDS (PI_ERR_SHAPE otherwise).
+ *  - The workspace must be zero-filled before the first call that uses it, and each call leaves it
+ *    ready for the next one (never clear or share it while a call is in flight).
+ *  - The int32 at byte offset 384 of the workspace is a sticky status word: nonzero means a
+ *    cross-workgroup wait ran out its time limit (20 ms) and the outputs of that call are invalid.
+ * Every wait inside the kernel is bounded, so a failure cannot hang the device. */
+int pi_ffn_layer_fused(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch,
+                       float *y, uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws,
+                       size_t ws_bytes, void *stream);
+
+/* Diagnostics: where a pi_sparse_ffn call leaves h (list position k, token b) in its workspace,
+ * for callers that count the rows of W_down^T that had to be read (h != 0 for some token).
+ * Returns the byte offset of the table inside a pi_sparse_ffn workspace and sets *kind:
+ *  1 = persistent kernel: position k is (1 + batch) uint64 words at offset + 8*k*(1 + batch);
+ *      the low 32 bits of word 0 are the slot (-1 = skipped), those of word 1 + b the fp32 bits of h;
+ *  2 = two-kernel form: fp32 h at offset + 4*(b*max(n_slots, 1) + k).
+ * Positions k >= counts[0] hold stale values.  Returns (size_t)-1 on invalid arguments. */
+size_t pi_sparse_ffn_h_offset(const pi_ffn *ffn, int32_t batch, int32_t *kind);
 
 /* Human-readable name of a pi_status value (static storage). */
 const char *pi_status_string(int status);

@@ -67,7 +67,15 @@ def gpu_predict(dl: DeviceLayer, x: np.ndarray):
     return logits.cpu().numpy(), mask.cpu().numpy()
 
 
-def gpu_layer(dl: DeviceLayer, x: np.ndarray, ws: torch.Tensor | None = None):
+def fused_fits(d_model: int, batch: int) -> bool:
+    """pi_ffn_layer_fused takes batch * d_model <= 32768 (x must fit one workgroup's LDS)."""
+    return batch * d_model <= 32768
+
+
+LAYER_ENTRIES = {"layer": _abi.pi_ffn_layer, "fused": _abi.pi_ffn_layer_fused}
+
+
+def gpu_layer(dl: DeviceLayer, x: np.ndarray, ws: torch.Tensor | None = None, entry: str = "layer"):
     B = x.shape[0]
     xd = to_dev(x)
     y = torch.empty((B, dl.d_model), dtype=torch.float32, device="cuda")
@@ -75,25 +83,36 @@ def gpu_layer(dl: DeviceLayer, x: np.ndarray, ws: torch.Tensor | None = None):
     idx = torch.empty(dl.d_ffn, dtype=torch.int32, device="cuda")
     counts = torch.empty(2, dtype=torch.int32, device="cuda")
     ws = dl.workspace(B) if ws is None else ws
-    _abi.pi_ffn_layer(dl.pred, dl.ffn, xd, B, y, mask, idx, counts, ws)
+    LAYER_ENTRIES[entry](dl.pred, dl.ffn, xd, B, y, mask, idx, counts, ws)
     torch.cuda.synchronize()
+    assert _abi.workspace_status(ws) == 0, "a cross-workgroup wait timed out"
     n = int(counts[0])
     return dict(y=y.cpu().numpy(), mask=mask.cpu().numpy(), idx=idx[:n].cpu().numpy(), n=n,
                 n_pred=int(counts[1]))
 
 
-def check_layer_against_oracle(layer, dl: DeviceLayer, x: np.ndarray, what: str, b_down=None) -> dict:
+def check_layer_against_oracle(layer, dl: DeviceLayer, x: np.ndarray, what: str, b_down=None,
+                               entries=("layer", "fused")) -> dict:
     """End-to-end rule: masks agree outside the band; given the GPU's mask the oracle's index list
-    is identical; given that list the oracle's y agrees within tolerance."""
+    is identical; given that list the oracle's y agrees within tolerance.  Checked for every
+    layer entry point named in `entries` that takes this shape."""
     cfg = layer.cfg
-    got = gpu_layer(dl, x)
+    B = x.shape[0]
     logits_ref, _, _ = oracle.predict(layer.p1, layer.p2, layer.c, x)
-    dont_care = check_mask(got["mask"], logits_ref, what)
-    idx_ref, n_ref, npred_ref = oracle.compact(got["mask"], layer.slot_of)
-    assert np.array_equal(got["idx"], idx_ref) and got["n"] == n_ref and got["n_pred"] == npred_ref, what
     bd = layer.b_down if b_down is None else b_down
-    y_ref = oracle.sparse_ffn(cfg.d, cfg.f, cfg.gated, cfg.wtype, layer.w_in, layer.w_down_t, x, idx_ref,
-                              b_up=layer.b_up, b_down=bd, slot_of=layer.slot_of)
-    worst = check_y(got["y"], y_ref, cfg.wtype, what)
-    worst.update(n=got["n"], n_pred=got["n_pred"], dont_care=dont_care)
+    worst = None
+    for entry in entries:
+        if entry == "fused" and not fused_fits(cfg.d, B):
+            continue
+        tag = f"{what} [{entry}]"
+        got = gpu_layer(dl, x, entry=entry)
+        dont_care = check_mask(got["mask"], logits_ref, tag)
+        idx_ref, n_ref, npred_ref = oracle.compact(got["mask"], layer.slot_of)
+        assert np.array_equal(got["idx"], idx_ref) and got["n"] == n_ref and got["n_pred"] == npred_ref, tag
+        y_ref = oracle.sparse_ffn(cfg.d, cfg.f, cfg.gated, cfg.wtype, layer.w_in, layer.w_down_t, x, idx_ref,
+                                  b_up=layer.b_up, b_down=bd, slot_of=layer.slot_of)
+        w = check_y(got["y"], y_ref, cfg.wtype, tag)
+        w.update(n=got["n"], n_pred=got["n_pred"], dont_care=dont_care)
+        if worst is None:
+            worst = w
     return worst

@@ -15,7 +15,7 @@ import torch
 import oracle
 import synth
 from activation_sparse_ffn_rank_amd import DeviceLayer, _abi
-from gpu_util import (LOGIT_ATOL, announce, check_layer_against_oracle, check_mask, check_y, gpu_layer,
+from gpu_util import (LAYER_ENTRIES, LOGIT_ATOL, announce, check_layer_against_oracle, check_mask, check_y, gpu_layer,
                       gpu_predict, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -115,7 +115,7 @@ def test_sparse_ffn(d, f, gated, wtype, B, share):
                      b_down=b_down)
     guard = 64
     y = torch.full((B * d + guard,), 12345.0, dtype=torch.float32, device="cuda")
-    ws = torch.empty(_abi.pi_workspace_bytes(None, dl.ffn, B), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(_abi.pi_workspace_bytes(None, dl.ffn, B), dtype=torch.uint8, device="cuda")
     counts = to_dev(np.array([idx.size, idx.size], np.int32))
     idx_d = to_dev(idx) if idx.size else torch.zeros(1, dtype=torch.int32, device="cuda")
     _abi.pi_sparse_ffn(dl.ffn, to_dev(x), B, idx_d, counts, y, ws)
@@ -138,7 +138,7 @@ def test_sparse_ffn_skips_bad_index_entries():
     idx = np.array([5, -1, 17, 100000, 42], np.int32)
     dl = DeviceLayer(p1=np.zeros((8, d), np.uint16), p2=np.zeros((f, 8), np.uint16), c=np.zeros(f, np.uint16),
                      w_in=w_in, w_down_t=w_dn, d_model=d, d_ffn=f, gated=False, wtype=F16, b_up=b_up, b_down=b_down)
-    ws = torch.empty(_abi.pi_workspace_bytes(None, dl.ffn, 1), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(_abi.pi_workspace_bytes(None, dl.ffn, 1), dtype=torch.uint8, device="cuda")
     y = torch.empty(d, dtype=torch.float32, device="cuda")
     _abi.pi_sparse_ffn(dl.ffn, to_dev(x), 1, to_dev(idx), to_dev(np.array([5, 5], np.int32)), y, ws)
     torch.cuda.synchronize()
@@ -220,9 +220,11 @@ def test_layer_is_deterministic():
     assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["idx"], b["idx"])
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("entry", ["layer", "fused"])
+def test_graph_replay_matches_eager(entry):
     """The launch sequence captured into a HIP graph (as the benchmark runs it) gives, on every
     replay, exactly what eager calls give."""
+    run = LAYER_ENTRIES[entry]
     cfg = synth.custom_config(2048, 5000, 256, gated=False, bias_up=True, density=0.1, seed=9, layers=3)
     layers = [synth.make_layer(cfg, l) for l in range(3)]
     dls = [DeviceLayer.from_host(L) for L in layers]
@@ -232,13 +234,13 @@ def test_graph_replay_matches_eager():
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         for l in range(3):
-            _abi.pi_ffn_layer(dls[l].pred, dls[l].ffn, xs[l], 1, ys[l], None, None, None, ws)
+            run(dls[l].pred, dls[l].ffn, xs[l], 1, ys[l], None, None, None, ws)
         torch.cuda.synchronize()
         eager = [y.clone() for y in ys]
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
             for l in range(3):
-                _abi.pi_ffn_layer(dls[l].pred, dls[l].ffn, xs[l], 1, ys[l], None, None, None, ws)
+                run(dls[l].pred, dls[l].ffn, xs[l], 1, ys[l], None, None, None, ws)
     for rep in range(4):
         for y in ys:
             y.fill_(float("nan"))
@@ -247,5 +249,50 @@ def test_graph_replay_matches_eager():
         for l in range(3):
             assert torch.equal(ys[l], eager[l]), f"replay {rep} layer {l}"
         # eager work between replays
-        _abi.pi_ffn_layer(dls[0].pred, dls[0].ffn, xs[0], 1, ys[0], None, None, None, ws)
+        run(dls[0].pred, dls[0].ffn, xs[0], 1, ys[0], None, None, None, ws)
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("entry", ["layer", "fused"])
+def test_layer_outputs_are_optional(entry):
+    """mask/idx/counts outputs change nothing about y (bitwise)."""
+    run = LAYER_ENTRIES[entry]
+    cfg = synth.custom_config(2048, 6000, 512, gated=True, bias_up=False, density=0.1, seed=31)
+    layer = synth.make_layer(cfg, 0)
+    dl = DeviceLayer.from_host(layer)
+    x = to_dev(synth.make_x(cfg, 0, 0, 2))
+    ws = dl.workspace(2)
+    y1 = torch.empty((2, cfg.d), dtype=torch.float32, device="cuda")
+    y2 = torch.empty_like(y1)
+    run(dl.pred, dl.ffn, x, 2, y1, None, None, None, ws)
+    got = gpu_layer(dl, synth.make_x(cfg, 0, 0, 2), ws=ws, entry=entry)
+    run(dl.pred, dl.ffn, x, 2, y2, None, None, None, ws)
+    torch.cuda.synchronize()
+    assert _abi.workspace_status(ws) == 0
+    assert torch.equal(y1, y2) and np.array_equal(y1.cpu().numpy(), got["y"])
+
+
+@pytest.mark.parametrize("entry", ["layer", "fused"])
+def test_many_calls_share_one_workspace(entry):
+    """Back-to-back launches on one workspace (epochs advance, counters reset) stay exact."""
+    run = LAYER_ENTRIES[entry]
+    cfg = synth.custom_config(1024, 4096, 128, density=0.1, seed=41, layers=2)
+    layers = [synth.make_layer(cfg, l) for l in range(2)]
+    dls = [DeviceLayer.from_host(L) for L in layers]
+    ws = dls[0].workspace(1)
+    xs = [to_dev(synth.make_x(cfg, l, t, 1)) for t in range(5) for l in range(2)]
+    ref = []
+    for i, x in enumerate(xs):
+        y = torch.empty((1, cfg.d), dtype=torch.float32, device="cuda")
+        run(dls[i % 2].pred, dls[i % 2].ffn, x, 1, y, None, None, None, ws)
+        ref.append(y)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, x in enumerate(xs):
+            y = torch.empty((1, cfg.d), dtype=torch.float32, device="cuda")
+            run(dls[i % 2].pred, dls[i % 2].ffn, x, 1, y, None, None, None, ws)
+            torch.cuda.synchronize()
+            assert torch.equal(y, ref[i]), (rep, i)
+    assert _abi.workspace_status(ws) == 0
+    got = check_layer_against_oracle(layers[1], dls[1], synth.make_x(cfg, 1, 4, 1), "after many calls", entries=(entry,))
+    assert got["n"] > 0
