@@ -6,7 +6,7 @@
 // No C++ exception crosses the ABI.
 #include "pi_sparse_ffn.h"
 #include "pi_kernels.hpp"
-#include "pi_fused.hpp"
+#include "pi_tail.hpp"
 
 #include <algorithm>
 
@@ -93,38 +93,74 @@ bool persistent_fits(int d, int B) {
     return x <= (size_t)kLdsXBytes && x + fixed <= 160 * 1024;
 }
 
-// Geometry of the persistent sparse-FFN kernel: groups of 4 listed neurons (at most
-// ceil(n_slots / 4) of them), slab x chunk down tiles.  Scratch: the control block, one stamped
-// header per group, (1 + B) stamped words per entry, stamped chunk partials [C][B][d].
+// Scratch of the persistent sparse-FFN kernel: the control block, (1 + B) stamped words per list
+// position (slot, h per token), stamped chunk partials [kSparseMaxChunks][B][d].  The chunk count
+// itself is chosen at launch from the device's occupancy.
 struct SparseGeom {
-    int slabs, C, NE, NDmax;
-    size_t ctl, ghead, ent, part;
+    int slabs;
+    size_t ctl, ent, part;
 };
 
-size_t ctl_bytes(int d) { return align_up((size_t)(CTL_LAYER0 + ctl_layer_stride(down_slabs(d))) * sizeof(int32_t)); }
+// Control block of either persistent kernel: room for the tickets of the most column slabs
+// either one uses (256-column slabs).
+size_t ctl_bytes(int d) { return align_up((size_t)(CTL_LAYER0 + ctl_layer_stride(ceil_div(d, 256))) * sizeof(int32_t)); }
 
 SparseGeom sparse_geom(const pi_ffn *fn, int B) {
     SparseGeom g;
     const int d = fn->d_model;
-    g.NDmax = std::max(1, ceil_div(fn->n_slots, 4));
-    g.slabs = down_slabs(d);
-    g.C = std::min(kFusedMaxChunks, std::max(1, std::min(g.NDmax, ceil_div(kDownTargetTiles, g.slabs))));
-    g.NE = g.slabs * g.C;
+    g.slabs = sparse_slabs(d, fn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16);
     g.ctl = ctl_bytes(d);
-    g.ghead = align_up((size_t)g.NDmax * sizeof(uint64_t));
-    g.ent = align_up((size_t)g.NDmax * 4 * (1 + B) * sizeof(uint64_t));
-    g.part = align_up((size_t)g.C * B * d * sizeof(uint64_t));
+    g.ent = align_up((size_t)std::max(fn->n_slots, 1) * (1 + B) * sizeof(uint64_t));
+    g.part = align_up((size_t)kSparseMaxChunks * B * d * sizeof(uint64_t));
     return g;
 }
 
 bool sparse_persistent(const pi_ffn *fn, int B) { return persistent_fits(fn->d_model, B); }
+
+// The tail kernel (second predictor matrix + mask + sparse FFN) keeps x [B][d] fp16 and z [B][r]
+// fp32 in dynamic LDS next to its static arrays (wave partials of the down tiles, the list of a
+// down tile's neurons, a few words); all of it must fit one workgroup.  It is used while every
+// 32-neuron tile can have an up workgroup of its own (d_ffn <= 32 * kTailMaxTiles).
+bool tail_persistent(const pi_predictor *p, const pi_ffn *fn, int B) {
+    const size_t stat = (size_t)4 * B * kTailCPL * 64 * 4 + (size_t)B * kTailSlab * 4 + (size_t)kTailListMax * 4 + 512;
+    // the kernel reads through 32-bit buffer offsets: every matrix (and the partials) must stay
+    // below kBufMax bytes
+    const int64_t in_bytes = (int64_t)fn->n_slots * row_bytes_of(fn) * (fn->gated ? 2 : 1);
+    const int64_t p2_bytes = (int64_t)p->d_ffn * p->rank * 2;
+    const int64_t part_bytes = (int64_t)kSparseMaxChunks * B * fn->d_model * 8;
+    if (in_bytes >= (int64_t)kBufMax || p2_bytes >= (int64_t)kBufMax || part_bytes >= (int64_t)kBufMax) return false;
+    return ceil_div(fn->d_ffn, 32) <= kTailMaxTiles && (size_t)B * fn->d_model * 2 <= (size_t)kLdsXBytes &&
+           tail_dyn_lds(B, fn->d_model, p->rank) + stat <= 160 * 1024;
+}
+
+// Scratch of the tail kernel (after the shared control block): a stamped word per 32-neuron tile,
+// (1 + B) stamped words per neuron (slot, h per token), stamped chunk partials.
+struct TailGeom {
+    int slabs, NTL;
+    size_t tword, ent, part;
+};
+
+TailGeom tail_geom(const pi_ffn *fn, int B) {
+    TailGeom g;
+    g.slabs = ceil_div(fn->d_model, kTailSlab);
+    g.NTL = ceil_div(fn->d_ffn, 32);
+    g.tword = align_up((size_t)g.NTL * sizeof(uint64_t));
+    g.ent = align_up((size_t)fn->d_ffn * (1 + B) * sizeof(uint64_t));
+    g.part = align_up((size_t)kSparseMaxChunks * B * fn->d_model * sizeof(uint64_t));
+    return g;
+}
+
+size_t tail_ws(const pi_ffn *fn, int B) {
+    const TailGeom g = tail_geom(fn, B);
+    return g.tword + g.ent + g.part;
+}
 
 // Scratch of pi_sparse_ffn: the persistent kernel's regions (control block first, so that the
 // status word sits at a fixed offset), or the two-kernel path's when x does not fit LDS.
 size_t ffn_ws(const pi_ffn *f, int B) {
     if (sparse_persistent(f, B)) {
         const SparseGeom g = sparse_geom(f, B);
-        return g.ctl + g.ghead + g.ent + g.part;
+        return g.ctl + g.ent + g.part;
     }
     return ffn_legacy_ws(f, B);
 }
@@ -214,6 +250,67 @@ int enqueue_predict(const pi_predictor *p, const void *x, int B, uint8_t *mask, 
     return PI_ERR_BATCH;
 }
 
+template <int B>
+void enqueue_pred_l1_b(const pi_predictor *p, const uint16_t *x, float *z, hipStream_t st) {
+    hipLaunchKernelGGL(k_pred_l1<B>, dim3(p->rank), dim3(256), 0, st, static_cast<const uint16_t *>(p->p1), x, z,
+                       p->d_model, p->rank);
+}
+
+int enqueue_pred_l1(const pi_predictor *p, const void *x, int B, float *z, hipStream_t st) {
+    const uint16_t *xx = static_cast<const uint16_t *>(x);
+    switch (B) {
+        case 1: enqueue_pred_l1_b<1>(p, xx, z, st); break;
+        case 2: enqueue_pred_l1_b<2>(p, xx, z, st); break;
+        case 3: enqueue_pred_l1_b<3>(p, xx, z, st); break;
+        case 4: enqueue_pred_l1_b<4>(p, xx, z, st); break;
+        case 5: enqueue_pred_l1_b<5>(p, xx, z, st); break;
+        case 6: enqueue_pred_l1_b<6>(p, xx, z, st); break;
+        case 7: enqueue_pred_l1_b<7>(p, xx, z, st); break;
+        case 8: enqueue_pred_l1_b<8>(p, xx, z, st); break;
+        default: return PI_ERR_BATCH;
+    }
+    return launch_status();
+}
+
+// The tail kernel: z (from k_pred_l1) -> mask -> sparse FFN -> y; ctl is the shared control block,
+// data the tail scratch (tail_ws bytes); mask (optional) receives the fired flags.
+int enqueue_tail(const pi_predictor *p, const pi_ffn *fn, const void *x, int B, const float *z, float *y,
+                 uint8_t *mask, int32_t *ctl, char *data, hipStream_t st, uint64_t *trace = nullptr) {
+    const TailGeom g = tail_geom(fn, B);
+    TailArgs a{};
+    a.d = fn->d_model; a.f = fn->d_ffn; a.r = p->rank; a.n_slots = fn->n_slots; a.slabs = g.slabs; a.NTL = g.NTL;
+    a.row_bytes = row_bytes_of(fn);
+    a.p2 = static_cast<const uint16_t *>(p->p2); a.c = static_cast<const uint16_t *>(p->c); a.z = z;
+    a.w_in = static_cast<const uint8_t *>(fn->w_in); a.w_dn = static_cast<const uint8_t *>(fn->w_down_t);
+    a.b_up = static_cast<const uint16_t *>(fn->b_up); a.b_down = static_cast<const uint16_t *>(fn->b_down);
+    a.slot_of = fn->slot_of;
+    a.x = static_cast<const uint16_t *>(x); a.y = y; a.mask = mask;
+    a.ctl = ctl;
+    a.tword = reinterpret_cast<uint64_t *>(data); data += g.tword;
+    a.ent = reinterpret_cast<uint64_t *>(data); data += g.ent;
+    a.part = reinterpret_cast<uint64_t *>(data);
+#ifdef PIK_TRACE
+    a.trace = trace;
+#else
+    (void)trace;
+#endif
+    const int wt = fn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16;
+    const int NT = p->rank <= 512 ? 1 : (p->rank <= 1024 ? 2 : 4);
+    int rc;
+    switch (B) {
+        case 1: rc = launch_tail_batch<1>(a, wt, fn->gated, NT, st); break;
+        case 2: rc = launch_tail_batch<2>(a, wt, fn->gated, NT, st); break;
+        case 3: rc = launch_tail_batch<3>(a, wt, fn->gated, NT, st); break;
+        case 4: rc = launch_tail_batch<4>(a, wt, fn->gated, NT, st); break;
+        case 5: rc = launch_tail_batch<5>(a, wt, fn->gated, NT, st); break;
+        case 6: rc = launch_tail_batch<6>(a, wt, fn->gated, NT, st); break;
+        case 7: rc = launch_tail_batch<7>(a, wt, fn->gated, NT, st); break;
+        case 8: rc = launch_tail_batch<8>(a, wt, fn->gated, NT, st); break;
+        default: return PI_ERR_BATCH;
+    }
+    return rc == 0 ? PI_OK : PI_ERR_HIP;
+}
+
 int enqueue_compact(const uint8_t *mask, int f, const int32_t *slot_of, int32_t *idx, int32_t *counts,
                     hipStream_t st) {
     hipLaunchKernelGGL(k_compact, dim3(1), dim3(1024), 0, st, mask, f, slot_of, idx, counts);
@@ -263,21 +360,19 @@ int enqueue_sparse_legacy(const pi_ffn *fn, const void *x, int B, const int32_t 
 }
 
 // The persistent sparse-FFN kernel; ctl is the control block (shared with the fused layer kernel
-// inside a layer workspace), data the group headers, entries and partials.
+// inside a layer workspace), data the entry table and the partials.
 int enqueue_sparse_persistent(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts,
                               float *y, int32_t *ctl, char *data, hipStream_t st, uint64_t *trace = nullptr) {
     const SparseGeom g = sparse_geom(fn, B);
-    FusedArgs a{};
-    a.d = fn->d_model; a.f = fn->d_ffn; a.n_slots = fn->n_slots;
-    a.slabs = g.slabs; a.C = g.C; a.NE = g.NE; a.ND = g.NDmax; a.cap = 4;
+    SparseArgs a{};
+    a.d = fn->d_model; a.f = fn->d_ffn; a.n_slots = fn->n_slots; a.slabs = g.slabs;
     a.row_bytes = row_bytes_of(fn);
     a.w_in = static_cast<const uint8_t *>(fn->w_in); a.w_dn = static_cast<const uint8_t *>(fn->w_down_t);
     a.b_up = static_cast<const uint16_t *>(fn->b_up); a.b_down = static_cast<const uint16_t *>(fn->b_down);
     a.slot_of = fn->slot_of;
     a.x = static_cast<const uint16_t *>(x); a.y = y;
-    a.idx_in = idx; a.counts_in = counts;
+    a.idx = idx; a.counts = counts;
     a.ctl = ctl;
-    a.ghead = reinterpret_cast<uint64_t *>(data); data += g.ghead;
     a.ent = reinterpret_cast<uint64_t *>(data); data += g.ent;
     a.part = reinterpret_cast<uint64_t *>(data);
 #ifdef PIK_TRACE
@@ -371,7 +466,7 @@ size_t pi_workspace_bytes(const pi_predictor *pred, const pi_ffn *ffn, int32_t b
     if (pred && ffn) {
         if (pred->d_model != ffn->d_model || pred->d_ffn != ffn->d_ffn) return 0;
         return fused_ws(fused_geom(pred, ffn, batch)) + pred_ws(pred, batch) + layer_extra_ws(pred->d_ffn) +
-               ffn_ws(ffn, batch);
+               ffn_ws(ffn, batch) + tail_ws(ffn, batch);
     }
     return pred ? pred_ws(pred, batch) : ffn_ws(ffn, batch);
 }
@@ -431,13 +526,24 @@ int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int
     p += align_up((size_t)f * sizeof(int32_t));
     int32_t *counts = reinterpret_cast<int32_t *>(p);
     p += align_up(2 * sizeof(int32_t));
+    char *ffn_scr = p;
+    char *tail_scr = p + ffn_ws(ffn, batch);
     if (mask_out) mask = mask_out;
     if (idx_out) idx = idx_out;
     if (counts_out) counts = counts_out;
+    if (tail_persistent(pred, ffn, batch)) {
+        // z, then one kernel for the mask and the sparse FFN; the list only when it is asked for
+        const bool want_list = idx_out != nullptr || counts_out != nullptr;
+        if ((rc = enqueue_pred_l1(pred, x, batch, z, st))) return rc;
+        if ((rc = enqueue_tail(pred, ffn, x, batch, z, y, (mask_out || want_list) ? mask : nullptr,
+                               static_cast<int32_t *>(ws), tail_scr, st)))
+            return rc;
+        return want_list ? enqueue_compact(mask, f, ffn->slot_of, idx, counts, st) : PI_OK;
+    }
     if ((rc = enqueue_predict(pred, x, batch, mask, nullptr, z, st))) return rc;
     if ((rc = enqueue_compact(mask, f, ffn->slot_of, idx, counts, st))) return rc;
     // the sparse kernel shares the control block at the start of the workspace
-    return enqueue_sparse(ffn, x, batch, idx, counts, y, p, static_cast<int32_t *>(ws), st);
+    return enqueue_sparse(ffn, x, batch, idx, counts, y, ffn_scr, static_cast<int32_t *>(ws), st);
 }
 
 int pi_ffn_layer_fused(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y,
@@ -460,9 +566,8 @@ int pi_ffn_layer_fused(const pi_predictor *pred, const pi_ffn *ffn, const void *
 size_t pi_sparse_ffn_h_offset(const pi_ffn *ffn, int32_t batch, int32_t *kind) {
     if (check_ffn(ffn) != PI_OK || check_batch(batch) != PI_OK || !kind) return (size_t)-1;
     if (sparse_persistent(ffn, batch)) {
-        const SparseGeom g = sparse_geom(ffn, batch);
         *kind = 1;
-        return g.ctl + g.ghead;
+        return sparse_geom(ffn, batch).ctl;
     }
     *kind = 2;
     return 0;
@@ -494,10 +599,21 @@ int pi_trace_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, i
                          trace);
 }
 
+int pi_trace_tail(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y, void *ws,
+                  uint64_t *trace, void *stream) {
+    if (!tail_persistent(pred, ffn, batch)) return PI_ERR_SHAPE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *p = static_cast<char *>(ws) + fused_ws(fused_geom(pred, ffn, batch));
+    float *z = reinterpret_cast<float *>(p);
+    p += pred_ws(pred, batch) + layer_extra_ws(pred->d_ffn) + ffn_ws(ffn, batch);
+    int rc = enqueue_pred_l1(pred, x, batch, z, st);
+    if (rc) return rc;
+    return enqueue_tail(pred, ffn, x, batch, z, y, nullptr, static_cast<int32_t *>(ws), p, st, trace);
+}
+
 int pi_trace_sparse(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx, const int32_t *counts,
-                    float *y, void *ws, uint64_t *trace, int32_t *ne_out, void *stream) {
+                    float *y, void *ws, uint64_t *trace, void *stream) {
     if (!sparse_persistent(ffn, batch)) return PI_ERR_SHAPE;
-    *ne_out = sparse_geom(ffn, batch).NE;
     char *w = static_cast<char *>(ws);
     return enqueue_sparse_persistent(ffn, x, batch, idx, counts, y, reinterpret_cast<int32_t *>(w),
                                      w + sparse_geom(ffn, batch).ctl, static_cast<hipStream_t>(stream), trace);

@@ -61,7 +61,6 @@ struct FusedArgs {
     float *y;
     uint8_t *mask_out;
     int32_t *idx_out, *counts_out;
-    const int32_t *idx_in, *counts_in;   // sparse-only kernel: the listed neurons and their count
     // scratch (workspace); every uint64_t word is (value | stamp << 32)
     int32_t *ctl;        // control block
     uint64_t *z;         // [B][r]     z values
@@ -629,87 +628,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B <= 2 ? 3 
     }
 }
 
-// ------------------------------------------------------------------------------ sparse FFN alone
-
-// Up task of the sparse-only kernel: group g holds list positions 4g .. 4g+3, one per wave.
-template <int B, bool GATED, int WT>
-__device__ void task_Dpos(const FusedArgs &a, int g, int n, int lane, int wave, uint32_t stamp, const uint16_t *xs) {
-    const int k = g * 4 + wave;
-    if (k < n) {
-        const int s = slot_of_id(a.idx_in[k], a.slot_of, a.f, a.n_slots);
-        float ag[B], au[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) ag[b] = au[b] = 0.f;
-        const int64_t in_stride = GATED ? 2 * a.row_bytes : a.row_bytes;
-        if (s >= 0) neuron_dots<B, GATED, WT>(a.w_in + (int64_t)s * in_stride, a.row_bytes, a.d, xs, a.d, lane, ag, au);
-        const float bias = (!GATED && a.b_up != nullptr && s >= 0) ? half_to_float(a.b_up[s]) : 0.f;
-        uint64_t *e = a.ent + ((size_t)g * a.cap + wave) * (1 + B);
-#pragma unroll
-        for (int b = 0; b < B; ++b) {
-            const float u = wave_sum(au[b]);
-            float hv;
-            if (GATED) {
-                const float gv = wave_sum(ag[b]);
-                hv = fmaxf(gv, 0.f) * u;
-            } else {
-                hv = fmaxf(u + bias, 0.f);
-            }
-            if (lane == 0) store_c64(e + 1 + b, stamped_f(s >= 0 ? hv : 0.f, stamp));
-        }
-        if (lane == 0) store_c64(e, stamped((uint32_t)s, stamp));
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) store_c64(a.ghead + g, stamped((uint32_t)min(4, n - g * 4), stamp));
-}
-
-// pi_sparse_ffn as one persistent kernel: the up tasks (groups of 4 listed neurons) publish
-// stamped (slot, h) entries, the down tiles (512-column slab x chunk of groups) poll them and the
-// last chunk of each slab writes y.  The number of groups comes from the device-side count, so
-// no task is spent on unlisted positions.
-template <int B, bool GATED, int WT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B <= 2 ? 3 : 2))) void k_sparse_fused(FusedArgs a) {
-    extern __shared__ __align__(16) uint16_t xs[];              // x [B][d] (q4-paired for Q4_0)
-    __shared__ float s_red4[4 * B * 8 * kWave];
-    __shared__ int s_misc[4 * (kWave + 1) + 32 * 4 + 8];
-    __shared__ int s_last;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const uint32_t stamp = (uint32_t)load_coherent_i(a.ctl + CTL_EPOCH) + 1u;
-#ifdef PIK_TRACE
-    if (a.trace != nullptr && threadIdx.x == 0) a.trace[(size_t)(16384 + blockIdx.x) * 4 + 1] = wall_clock64();
-#endif
-    const int n = min(max(a.counts_in[0], 0), a.n_slots);
-    a.ND = (n + 3) / 4;
-    const int tasks = a.ND + a.NE;
-    stage_x<B, WT == WT_Q4_0>(xs, a.x, a.d, 0, a.d, a.d);
-    __syncthreads();
-    for (int g = blockIdx.x; g < tasks; g += a.P) {
-        PIK_TRACE_AT(g, 0);
-        PIK_TRACE_AT(g, 1);
-        PIK_TRACE_AT(g, 2);
-        if (g < a.ND)
-            task_Dpos<B, GATED, WT>(a, g, n, lane, wave, stamp, xs);
-        else
-            task_E<B, WT>(a, g - a.ND, lane, wave, stamp, s_red4, s_misc, &s_last, g);
-        PIK_TRACE_AT(g, 3);
-    }
-#ifdef PIK_TRACE
-    if (a.trace != nullptr && threadIdx.x == 0) {
-        a.trace[(size_t)(16384 + blockIdx.x) * 4 + 0] = n;
-        a.trace[(size_t)(16384 + blockIdx.x) * 4 + 2] = wall_clock64();
-    }
-#endif
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        if (atomicAdd(a.ctl + CTL_EXIT, 1) == a.P - 1) {
-            const int ls = ctl_layer_stride(a.slabs);
-            for (int i = 0; i < ls; i += 32) store_coherent_i(a.ctl + CTL_LAYER0 + i, 0);
-            store_coherent_i(a.ctl + CTL_ABORT, 0);
-            store_coherent_i(a.ctl + CTL_EXIT, 0);
-            store_coherent_i(a.ctl + CTL_EPOCH, (int32_t)stamp);
-        }
-    }
-}
-
 // Launch of the fused layer kernel for batch width B (one translation unit per B, so the
 // variants compile in parallel).  Picks the grid so that every workgroup is resident at once.
 // Returns 0 on success, nonzero on a HIP error.
@@ -724,16 +642,5 @@ template <> int launch_fused_batch<6>(FusedArgs &, int, int, int, hipStream_t);
 template <> int launch_fused_batch<7>(FusedArgs &, int, int, int, hipStream_t);
 template <> int launch_fused_batch<8>(FusedArgs &, int, int, int, hipStream_t);
 
-// Launch of the sparse-only persistent kernel (same per-B translation units).
-template <int B>
-int launch_sparse_batch(FusedArgs &a, int wtype, int gated, hipStream_t st);
-template <> int launch_sparse_batch<1>(FusedArgs &, int, int, hipStream_t);
-template <> int launch_sparse_batch<2>(FusedArgs &, int, int, hipStream_t);
-template <> int launch_sparse_batch<3>(FusedArgs &, int, int, hipStream_t);
-template <> int launch_sparse_batch<4>(FusedArgs &, int, int, hipStream_t);
-template <> int launch_sparse_batch<5>(FusedArgs &, int, int, hipStream_t);
-template <> int launch_sparse_batch<6>(FusedArgs &, int, int, hipStream_t);
-template <> int launch_sparse_batch<7>(FusedArgs &, int, int, hipStream_t);
-template <> int launch_sparse_batch<8>(FusedArgs &, int, int, hipStream_t);
 
 }  // namespace pik

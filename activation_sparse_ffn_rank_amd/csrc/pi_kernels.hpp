@@ -39,6 +39,29 @@ __device__ __forceinline__ uint4 ld16(const void *p) { return *reinterpret_cast<
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
 
+// Loads through a buffer resource (base, size in bytes): the hardware returns zeros for an offset
+// at or past the size and touches no memory, so a guarded load needs no branch -- pass kOOB as the
+// offset (or as one of two summed parts of it) of a load that must not happen.  Buffers must stay
+// below kBufMax bytes, so that a valid part plus kOOB, or kOOB plus kOOB, is still past the end
+// and does not wrap around 2^32.
+constexpr uint32_t kOOB = 0x40000000u;
+constexpr uint64_t kBufMax = 0x40000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ uint64_t bld8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+__device__ __forceinline__ uint16_t bld2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
 __device__ __forceinline__ float half_to_float(uint16_t b) { return (float)__builtin_bit_cast(f16, b); }
 
 // a.lo*b.lo + a.hi*b.hi + c with fp16 inputs and fp32 accumulation (v_dot2_f32_f16).
@@ -78,8 +101,12 @@ __device__ __forceinline__ float reduce_scatter(float (&v)[N], int lane) {
         const bool hi = (lane & m) != 0;
 #pragma unroll
         for (int i = 0; i < half; ++i) {
-            const float send = hi ? v[i] : v[i + half];
-            const float keep = hi ? v[i + half] : v[i];
+            // read both values into registers first: a select between two array loads would
+            // otherwise become a lane-dependent index into the array, which lives in scratch
+            float lo = v[i], up = v[i + half];
+            asm volatile("" : "+v"(lo), "+v"(up));
+            const float send = hi ? lo : up;
+            const float keep = hi ? up : lo;
             v[i] = keep + __shfl_xor(send, m, kWave);
         }
     }
@@ -401,6 +428,29 @@ struct RowPass {
                 const int q = p0 + lane + v * kWave;
                 wu[v] = q < nq ? ld16(row + (size_t)q * 16) : zero4();
                 sc[WT == WT_Q4_0 ? v : 0] = q < nq ? scales[q] : (uint16_t)0;
+            }
+        }
+    }
+
+    // The same loads through a buffer resource over the rows, the neuron's row(s) starting at byte
+    // `base`; no branches (columns past d read zeros).
+    __device__ __forceinline__ void issue_buf(__amdgpu_buffer_rsrc_t r, uint32_t base, int64_t row_bytes, int d,
+                                              int p0, int lane) {
+        if (WT == WT_F16) {
+            const uint32_t gb = base, ub = base + (GATED ? (uint32_t)row_bytes : 0u);
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int col = p0 + lane * 8 + v * 512;
+                wu[v] = bld16(r, col < d ? ub + (uint32_t)col * 2 : kOOB);
+                if (GATED) wg[GATED ? v : 0] = bld16(r, col < d ? gb + (uint32_t)col * 2 : kOOB);
+            }
+        } else {
+            const int nq = d / 32;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                const int q = p0 + lane + v * kWave;
+                wu[v] = bld16(r, q < nq ? base + (uint32_t)q * 16 : kOOB);
+                sc[WT == WT_Q4_0 ? v : 0] = bld2(r, q < nq ? base + (uint32_t)(d / 2) + (uint32_t)q * 2 : kOOB);
             }
         }
     }

@@ -123,7 +123,7 @@ def main():
     # The sparse FFN (gathered up/gate rows + active rows of W_down^T) is one kernel, pi_sparse_ffn.
     # An eager pass runs pi_predict and pi_compact on R tokens x L layers, keeps every index list,
     # runs pi_sparse_ffn once per list and counts from the h table it leaves in its workspace the
-    # listed neurons whose h is nonzero for some token: the rows of W_down^T the kernel must read.
+    # listed neurons whose h is nonzero for some token (the rows of W_down^T that contribute).
     # Then the R*L launches of each entry point are captured into a graph of their own and timed
     # with HIP events on the launch stream around its replay: elapsed / launches is the average
     # launch duration, back to back as in the decode step.
@@ -182,8 +182,12 @@ def main():
     if _abi.workspace_status(ws_f) != 0:
         raise RuntimeError("sparse-FFN workspace status nonzero: a cross-workgroup wait timed out")
     n_act, n_pred = cnt_host[:, 0], cnt_host[:, 1]
+    # the persistent kernel issues the down-row loads before h is known, so it reads every listed
+    # row; the two-kernel form (shapes whose x does not fit LDS) skips rows with h = 0
+    _, h_kind = _abi.pi_sparse_ffn_h_offset(layers[0].ffn, B)
+    n_read_down = n_act if h_kind == 1 else n_live
     vec_bytes = B * cfg.d * (2 + 4) + 2 * cfg.d                  # x in, y out, b_down
-    ffn_touched = n_act * in_rows * rb + n_live * rb + 8 * n_act + vec_bytes   # + idx and slot lookups
+    ffn_touched = n_act * in_rows * rb + n_read_down * rb + 8 * n_act + vec_bytes   # + idx and slot lookups
     ffn_predicted = n_act * (in_rows + 1) * rb + 8 * n_act + vec_bytes
     ffn_us = leg_us["sparse_ffn"]
     ffn_gbs = float(ffn_touched.mean()) / (ffn_us * 1e-6) / 1e9
@@ -259,7 +263,8 @@ def main():
             "active_density": round(float(n_act.mean()) / cfg.f, 4),
             "predicted_density": round(float(n_pred.mean()) / cfg.f, 4),
             "covered_share": round(float(n_act.sum() / max(n_pred.sum(), 1)), 4),
-            "down_rows_skipped_share": round(1.0 - float(n_live.sum()) / max(float(n_act.sum()), 1.0), 4),
+            "down_rows_zero_h_share": round(1.0 - float(n_live.sum()) / max(float(n_act.sum()), 1.0), 4),
+            "down_rows_read_share": round(float(n_read_down.sum()) / max(float(n_act.sum()), 1.0), 4),
         },
     }
     print(json.dumps(out), flush=True)
