@@ -21,7 +21,7 @@ PI_MAX_BATCH = 8
 
 # Every function the header declares; the CPU tests check that libpi.so exports them all.
 EXPORTS = ("pi_workspace_bytes", "pi_predict", "pi_compact", "pi_sparse_ffn", "pi_ffn_layer",
-           "pi_ffn_layer_fused", "pi_sparse_ffn_h_offset", "pi_status_string", "pi_version")
+           "pi_predict_hidden", "pi_ffn_layer_from_hidden", "pi_layer_path", "pi_ffn_layer_fused", "pi_sparse_ffn_h_offset", "pi_status_string", "pi_version")
 
 
 class pi_predictor(ctypes.Structure):
@@ -63,6 +63,12 @@ def lib() -> ctypes.CDLL:
         L.pi_sparse_ffn.argtypes = [P(pi_ffn), vp, i32, vp, vp, vp, vp, sz, vp]
         L.pi_ffn_layer.restype = ctypes.c_int
         L.pi_ffn_layer.argtypes = [P(pi_predictor), P(pi_ffn), vp, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.pi_predict_hidden.restype = ctypes.c_int
+        L.pi_predict_hidden.argtypes = [P(pi_predictor), vp, i32, vp, vp]
+        L.pi_ffn_layer_from_hidden.restype = ctypes.c_int
+        L.pi_ffn_layer_from_hidden.argtypes = [P(pi_predictor), P(pi_ffn), vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.pi_layer_path.restype = ctypes.c_int
+        L.pi_layer_path.argtypes = [P(pi_predictor), P(pi_ffn), i32]
         L.pi_ffn_layer_fused.restype = ctypes.c_int
         L.pi_ffn_layer_fused.argtypes = [P(pi_predictor), P(pi_ffn), vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.pi_sparse_ffn_h_offset.restype = sz
@@ -146,6 +152,22 @@ def pi_ffn_layer(pred, ffn, x, batch, y, mask_out, idx_out, counts_out, ws, stre
                                               _ptr(idx_out), _ptr(counts_out), _ptr(ws),
                                               _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0,
                                               _stream(stream)))
+
+
+def pi_predict_hidden(pred, x, batch, z, stream=None) -> None:
+    _check("pi_predict_hidden", lib().pi_predict_hidden(_byref(pred), _ptr(x), batch, _ptr(z), _stream(stream)))
+
+
+def pi_ffn_layer_from_hidden(pred, ffn, x, batch, z, y, mask_out, idx_out, counts_out, ws, stream=None) -> None:
+    _check("pi_ffn_layer_from_hidden", lib().pi_ffn_layer_from_hidden(
+        _byref(pred), _byref(ffn), _ptr(x), batch, _ptr(z), _ptr(y), _ptr(mask_out), _ptr(idx_out),
+        _ptr(counts_out), _ptr(ws), _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0,
+        _stream(stream)))
+
+
+def pi_layer_path(pred, ffn, batch) -> int:
+    """1: pi_ffn_layer_from_hidden is one persistent kernel; 2: separate kernels; 0: invalid."""
+    return int(lib().pi_layer_path(_byref(pred), _byref(ffn), batch))
 
 
 def pi_ffn_layer_fused(pred, ffn, x, batch, y, mask_out, idx_out, counts_out, ws, stream=None) -> None:

@@ -218,10 +218,8 @@ int launch_status() { return hipGetLastError() == hipSuccess ? PI_OK : PI_ERR_HI
 // ------------------------------------------------------------------ enqueue helpers
 
 template <int B>
-int enqueue_predict_b(const pi_predictor *p, const uint16_t *x, uint8_t *mask, float *logits, float *z,
-                      hipStream_t st) {
-    const int d = p->d_model, r = p->rank, f = p->d_ffn;
-    hipLaunchKernelGGL(k_pred_l1<B>, dim3(r), dim3(256), 0, st, static_cast<const uint16_t *>(p->p1), x, z, d, r);
+int enqueue_pred_l2_b(const pi_predictor *p, const float *z, uint8_t *mask, float *logits, hipStream_t st) {
+    const int r = p->rank, f = p->d_ffn;
     constexpr int R = 8;                               // predictor rows per wave
     const int groups = ceil_div(f, 4 * R);
     const uint16_t *p2 = static_cast<const uint16_t *>(p->p2), *c = static_cast<const uint16_t *>(p->c);
@@ -232,6 +230,29 @@ int enqueue_predict_b(const pi_predictor *p, const uint16_t *x, uint8_t *mask, f
     else
         hipLaunchKernelGGL((k_pred_l2<B, 4, R>), dim3(groups), dim3(256), 0, st, p2, c, z, r, f, logits, mask);
     return launch_status();
+}
+
+int enqueue_pred_l2(const pi_predictor *p, const float *z, int B, uint8_t *mask, float *logits, hipStream_t st) {
+    switch (B) {
+        case 1: return enqueue_pred_l2_b<1>(p, z, mask, logits, st);
+        case 2: return enqueue_pred_l2_b<2>(p, z, mask, logits, st);
+        case 3: return enqueue_pred_l2_b<3>(p, z, mask, logits, st);
+        case 4: return enqueue_pred_l2_b<4>(p, z, mask, logits, st);
+        case 5: return enqueue_pred_l2_b<5>(p, z, mask, logits, st);
+        case 6: return enqueue_pred_l2_b<6>(p, z, mask, logits, st);
+        case 7: return enqueue_pred_l2_b<7>(p, z, mask, logits, st);
+        case 8: return enqueue_pred_l2_b<8>(p, z, mask, logits, st);
+    }
+    return PI_ERR_BATCH;
+}
+
+template <int B>
+int enqueue_predict_b(const pi_predictor *p, const uint16_t *x, uint8_t *mask, float *logits, float *z,
+                      hipStream_t st) {
+    hipLaunchKernelGGL(k_pred_l1<B>, dim3(p->rank), dim3(256), 0, st, static_cast<const uint16_t *>(p->p1), x, z,
+                       p->d_model, p->rank);
+    if (launch_status() != PI_OK) return PI_ERR_HIP;
+    return enqueue_pred_l2_b<B>(p, z, mask, logits, st);
 }
 
 int enqueue_predict(const pi_predictor *p, const void *x, int B, uint8_t *mask, float *logits, float *z,
@@ -502,24 +523,22 @@ int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t
     return enqueue_sparse(ffn, x, batch, idx, counts, y, ws, nullptr, static_cast<hipStream_t>(stream));
 }
 
-int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y,
-                 uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws, size_t ws_bytes,
-                 void *stream) {
+int pi_predict_hidden(const pi_predictor *pred, const void *x, int32_t batch, float *z, void *stream) {
     int rc = check_pred(pred);
     if (rc) return rc;
-    if ((rc = check_ffn(ffn))) return rc;
     if ((rc = check_batch(batch))) return rc;
-    if (pred->d_model != ffn->d_model || pred->d_ffn != ffn->d_ffn) return PI_ERR_SHAPE;
-    if (!x || !y) return PI_ERR_NULL;
-    if (!aligned16(x)) return PI_ERR_ALIGN;
-    const size_t need = pi_workspace_bytes(pred, ffn, batch);
-    if (!ws || ws_bytes < need) return PI_ERR_WORKSPACE;
-    if (!aligned16(ws)) return PI_ERR_ALIGN;
+    if (!x || !z) return PI_ERR_NULL;
+    if (!aligned16(x) || !aligned16(z)) return PI_ERR_ALIGN;
+    return enqueue_pred_l1(pred, x, batch, z, static_cast<hipStream_t>(stream));
+}
+
+namespace {
+
+// The layer from z on (mask, placement restriction, sparse FFN) on a layer workspace.
+int layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, const float *z,
+                      float *y, uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws, hipStream_t st) {
     const int f = pred->d_ffn;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    char *p = static_cast<char *>(ws) + fused_ws(fused_geom(pred, ffn, batch));
-    float *z = reinterpret_cast<float *>(p);
-    p += pred_ws(pred, batch);
+    char *p = static_cast<char *>(ws) + fused_ws(fused_geom(pred, ffn, batch)) + pred_ws(pred, batch);
     uint8_t *mask = reinterpret_cast<uint8_t *>(p);
     p += align_up((size_t)f);
     int32_t *idx = reinterpret_cast<int32_t *>(p);
@@ -531,19 +550,63 @@ int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int
     if (mask_out) mask = mask_out;
     if (idx_out) idx = idx_out;
     if (counts_out) counts = counts_out;
+    int rc;
     if (tail_persistent(pred, ffn, batch)) {
-        // z, then one kernel for the mask and the sparse FFN; the list only when it is asked for
+        // one kernel for the mask and the sparse FFN; the list only when it is asked for
         const bool want_list = idx_out != nullptr || counts_out != nullptr;
-        if ((rc = enqueue_pred_l1(pred, x, batch, z, st))) return rc;
         if ((rc = enqueue_tail(pred, ffn, x, batch, z, y, (mask_out || want_list) ? mask : nullptr,
                                static_cast<int32_t *>(ws), tail_scr, st)))
             return rc;
         return want_list ? enqueue_compact(mask, f, ffn->slot_of, idx, counts, st) : PI_OK;
     }
-    if ((rc = enqueue_predict(pred, x, batch, mask, nullptr, z, st))) return rc;
+    if ((rc = enqueue_pred_l2(pred, z, batch, mask, nullptr, st))) return rc;
     if ((rc = enqueue_compact(mask, f, ffn->slot_of, idx, counts, st))) return rc;
     // the sparse kernel shares the control block at the start of the workspace
     return enqueue_sparse(ffn, x, batch, idx, counts, y, ffn_scr, static_cast<int32_t *>(ws), st);
+}
+
+int check_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, const float *y,
+                const void *ws, size_t ws_bytes) {
+    int rc = check_pred(pred);
+    if (rc) return rc;
+    if ((rc = check_ffn(ffn))) return rc;
+    if ((rc = check_batch(batch))) return rc;
+    if (pred->d_model != ffn->d_model || pred->d_ffn != ffn->d_ffn) return PI_ERR_SHAPE;
+    if (!x || !y) return PI_ERR_NULL;
+    if (!aligned16(x)) return PI_ERR_ALIGN;
+    if (!ws || ws_bytes < pi_workspace_bytes(pred, ffn, batch)) return PI_ERR_WORKSPACE;
+    if (!aligned16(ws)) return PI_ERR_ALIGN;
+    return PI_OK;
+}
+
+}  // namespace
+
+int pi_layer_path(const pi_predictor *pred, const pi_ffn *ffn, int32_t batch) {
+    if (check_pred(pred) != PI_OK || check_ffn(ffn) != PI_OK || check_batch(batch) != PI_OK) return 0;
+    if (pred->d_model != ffn->d_model || pred->d_ffn != ffn->d_ffn) return 0;
+    return tail_persistent(pred, ffn, batch) ? 1 : 2;
+}
+
+int pi_ffn_layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch,
+                             const float *z, float *y, uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out,
+                             void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_layer(pred, ffn, x, batch, y, ws, ws_bytes);
+    if (rc) return rc;
+    if (!z) return PI_ERR_NULL;
+    if (!aligned16(z)) return PI_ERR_ALIGN;
+    return layer_from_hidden(pred, ffn, x, batch, z, y, mask_out, idx_out, counts_out, ws,
+                             static_cast<hipStream_t>(stream));
+}
+
+int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y,
+                 uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws, size_t ws_bytes,
+                 void *stream) {
+    int rc = check_layer(pred, ffn, x, batch, y, ws, ws_bytes);
+    if (rc) return rc;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    float *z = reinterpret_cast<float *>(static_cast<char *>(ws) + fused_ws(fused_geom(pred, ffn, batch)));
+    if ((rc = enqueue_pred_l1(pred, x, batch, z, st))) return rc;
+    return layer_from_hidden(pred, ffn, x, batch, z, y, mask_out, idx_out, counts_out, ws, st);
 }
 
 int pi_ffn_layer_fused(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y,

@@ -8,8 +8,8 @@ are resident in HBM before timing starts.  W warmup steps and K timed steps are 
 HIP graphs captured on one stream; the timed region is bracketed by device synchronizations.
 
 Printed: one JSON line with tokens/s, ms per step, per-layer microseconds, the roofline of the
-sparse-FFN kernel on the bytes it must read (HIP events on the launch stream around a graph of its
-launches), and
+step's dominant kernel on the bytes it reads (HIP events on the launch stream around a graph of
+its launches), and
 the CPU oracle's rate on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -28,6 +28,35 @@ import numpy as np  # noqa: E402
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 
 
+def kernel_sources_sha256() -> str:
+    """Digest of the HIP sources; hardware byte counts taken on other sources are stale."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "activation_sparse_ffn_rank_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            with open(os.path.join(csrc, name), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel_prefix: str):
+    """HBM bytes per launch (read + written) of the kernel whose name starts with kernel_prefix, from the
+    counter summary in profiles/ for this workload -- None when there is none or the sources changed."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("sources_sha256") != kernel_sources_sha256():
+        return None
+    for name, v in rec.get("kernels", {}).items():
+        if name.startswith(kernel_prefix):
+            return int(v["read_bytes"]) + int(v["write_bytes"])
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -40,6 +69,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph replay")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after the measurement, run one device-to-device copy of this many MiB (a kernel of "
+                         "known traffic, for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -119,44 +151,48 @@ def main():
         raise RuntimeError(f"workspace status {status}: a cross-workgroup wait timed out; results invalid")
     log(f"timed {K} steps: {elapsed_ms:.3f} ms")
 
-    # ------------------------------------------------------------------ roofline pass (HIP events)
-    # The sparse FFN (gathered up/gate rows + active rows of W_down^T) is one kernel, pi_sparse_ffn.
-    # An eager pass runs pi_predict and pi_compact on R tokens x L layers, keeps every index list,
-    # runs pi_sparse_ffn once per list and counts from the h table it leaves in its workspace the
-    # listed neurons whose h is nonzero for some token (the rows of W_down^T that contribute).
-    # Then the R*L launches of each entry point are captured into a graph of their own and timed
-    # with HIP events on the launch stream around its replay: elapsed / launches is the average
-    # launch duration, back to back as in the decode step.
+    # ------------------------------------------------------------------ per-kernel legs (HIP events)
+    # pi_ffn_layer is pi_predict_hidden (z = ReLU(P1 x), one kernel) followed by
+    # pi_ffn_layer_from_hidden (logits, mask and the sparse FFN: one persistent kernel on path 1).
+    # An eager pass runs both on R tokens x L layers, keeping every z and every index list, and
+    # runs pi_sparse_ffn on each list (the sparse FFN alone, one kernel) to count the listed
+    # neurons whose h is nonzero for some token.  Then the R*L launches of each entry point are
+    # captured into a graph of their own and timed with HIP events on the launch stream around
+    # its replay: elapsed / launches is the average launch duration, back to back as in the step.
     R = min(args.roofline_steps, K)
     N = R * L
     rb = cfg.row_bytes()
     in_rows = 2 if cfg.gated else 1
     pred_bytes = 2 * (cfg.r * cfg.d + cfg.f * cfg.r + cfg.f)
+    path = _abi.pi_layer_path(layers[0].pred, layers[0].ffn, B)
+    z_all = torch.empty((N, B, cfg.r), dtype=torch.float32, device=dev)
     masks = torch.empty((N, cfg.f), dtype=torch.uint8, device=dev)
     idx_all = torch.empty((N, cfg.f), dtype=torch.int32, device=dev)
     cnt_all = torch.empty((N, 2), dtype=torch.int32, device=dev)
-    ws_p = torch.empty(_abi.pi_workspace_bytes(layers[0].pred, None, B), dtype=torch.uint8, device=dev)
     ws_f = torch.zeros(_abi.pi_workspace_bytes(None, layers[0].ffn, B), dtype=torch.uint8, device=dev)
     y_chk = torch.empty((B, cfg.d), dtype=torch.float32, device=dev)
     ns = layers[0].n_slots
     ar = torch.arange(ns, device=dev)
     cases = [(W + i // L, i % L) for i in range(N)]             # (token, layer) of launch i
 
-    def run_predict():
+    def run_hidden():
         for i, (t, l) in enumerate(cases):
-            _abi.pi_predict(layers[l].pred, xd[t, l], B, masks[i], None, ws_p)
+            _abi.pi_predict_hidden(layers[l].pred, xd[t, l], B, z_all[i])
 
-    def run_compact():
+    def run_rest():
         for i, (t, l) in enumerate(cases):
-            _abi.pi_compact(masks[i], cfg.f, layers[l].slot_of, idx_all[i], cnt_all[i])
+            _abi.pi_ffn_layer_from_hidden(layers[l].pred, layers[l].ffn, xd[t, l], B, z_all[i], y_chk, None, None,
+                                          None, ws)
 
-    def run_ffn():
+    def run_sparse():
         for i, (t, l) in enumerate(cases):
             _abi.pi_sparse_ffn(layers[l].ffn, xd[t, l], B, idx_all[i], cnt_all[i], y_chk, ws_f)
 
     with torch.cuda.stream(stream):
-        run_predict()
-        run_compact()
+        run_hidden()
+        for i, (t, l) in enumerate(cases):
+            _abi.pi_ffn_layer_from_hidden(layers[l].pred, layers[l].ffn, xd[t, l], B, z_all[i], y_chk, masks[i],
+                                          idx_all[i], cnt_all[i], ws)
         live = []
         for i, (t, l) in enumerate(cases):
             _abi.pi_sparse_ffn(layers[l].ffn, xd[t, l], B, idx_all[i], cnt_all[i], y_chk, ws_f)
@@ -166,7 +202,7 @@ def main():
         n_live = torch.stack(live).cpu().numpy().astype(np.float64)
         cnt_host = cnt_all.cpu().numpy().astype(np.float64)
         leg_us = {}
-        for name, fn in (("predict", run_predict), ("compact", run_compact), ("sparse_ffn", run_ffn)):
+        for name, fn in (("hidden", run_hidden), ("rest", run_rest), ("sparse_ffn", run_sparse)):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
                 fn()
@@ -179,18 +215,35 @@ def main():
             torch.cuda.synchronize()
             leg_us[name] = e0.elapsed_time(e1) * 1000.0 / N
             del g
-    if _abi.workspace_status(ws_f) != 0:
-        raise RuntimeError("sparse-FFN workspace status nonzero: a cross-workgroup wait timed out")
+    for w in (ws, ws_f):
+        if _abi.workspace_status(w) != 0:
+            raise RuntimeError("workspace status nonzero: a cross-workgroup wait timed out")
     n_act, n_pred = cnt_host[:, 0], cnt_host[:, 1]
-    # the persistent kernel issues the down-row loads before h is known, so it reads every listed
-    # row; the two-kernel form (shapes whose x does not fit LDS) skips rows with h = 0
+    vec_bytes = B * cfg.d * (2 + 4) + 2 * cfg.d                  # x in, y out, b_down
+    slot_bytes = 4 * cfg.f if layers[0].slot_of is not None else 0
+    # sparse FFN alone: the persistent kernel reads every listed row (its down-row loads go out
+    # before h is known); the two-kernel form skips down rows whose h is zero for every token
     _, h_kind = _abi.pi_sparse_ffn_h_offset(layers[0].ffn, B)
     n_read_down = n_act if h_kind == 1 else n_live
-    vec_bytes = B * cfg.d * (2 + 4) + 2 * cfg.d                  # x in, y out, b_down
-    ffn_touched = n_act * in_rows * rb + n_read_down * rb + 8 * n_act + vec_bytes   # + idx and slot lookups
+    ffn_touched = n_act * in_rows * rb + n_read_down * rb + 8 * n_act + vec_bytes
     ffn_predicted = n_act * (in_rows + 1) * rb + 8 * n_act + vec_bytes
-    ffn_us = leg_us["sparse_ffn"]
-    ffn_gbs = float(ffn_touched.mean()) / (ffn_us * 1e-6) / 1e9
+    # the rest of the layer on path 1 (one kernel): P2 and c, z, every listed row in and down
+    rest_bytes = 2 * cfg.f * cfg.r + 2 * cfg.f + 4 * B * cfg.r + slot_bytes + n_act * (in_rows + 1) * rb + vec_bytes
+    hidden_bytes = 2 * cfg.r * cfg.d + 2 * B * cfg.d + 4 * B * cfg.r
+    gname = "true" if cfg.gated else "false"
+    wname = 1 if cfg.wtype == synth.F16 else 2
+    if path == 1:
+        roof_kernel = ("k_layer_tail (pi_ffn_layer_from_hidden: predictor logits and mask, gathered up/gate rows "
+                       "with ReLU/ReGLU, active rows of W_down^T)")
+        roof_bytes, roof_us = float(rest_bytes.mean()), leg_us["rest"]
+        roof_prefix = f"void pik::k_layer_tail<{B}, {gname}, {wname},"
+    else:
+        roof_kernel = "k_sparse_ffn (pi_sparse_ffn: gathered up/gate rows with ReLU/ReGLU + active rows of W_down^T)"
+        roof_bytes, roof_us = float(ffn_touched.mean()), leg_us["sparse_ffn"]
+        roof_prefix = f"void pik::k_sparse_ffn<{B}, {gname}, {wname}>"
+    workload_tag = f"{cfg.name}_b{B}"
+    roof_traffic = measured_traffic(workload_tag, roof_prefix) if L == cfg.layers else None
+    roof_gbs = roof_bytes / (roof_us * 1e-6) / 1e9
     step_bytes = (pred_bytes + float(ffn_touched.mean())) * L
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
@@ -240,34 +293,46 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "k_sparse_fused (pi_sparse_ffn: gathered up/gate rows with ReLU/ReGLU + active rows of W_down^T)",
-            "achieved": round(ffn_gbs, 1),
+            "kernel": roof_kernel,
+            "achieved": round(roof_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
-            "frac": round(ffn_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
-            "bytes_per_launch": round(float(ffn_touched.mean())),
-            "launch_us": round(ffn_us, 3),
+            "frac": round(roof_gbs / PEAK_HBM_GBS, 4),
+            "traffic": roof_traffic,
+            "bytes_per_launch": round(roof_bytes),
+            "launch_us": round(roof_us, 3),
             "launches": int(N),
         },
         "cpu_baseline": cpu,
         "detail": {
             "us_per_layer": round(ms_per_step * 1000.0 / L, 3),
-            "graph_us_predict": round(leg_us["predict"], 3),
-            "graph_us_compact": round(leg_us["compact"], 3),
-            "graph_us_sparse_ffn": round(ffn_us, 3),
+            "layer_path": path,
+            "graph_us_predict_hidden": round(leg_us["hidden"], 3),
+            "graph_us_layer_from_hidden": round(leg_us["rest"], 3),
+            "graph_us_sparse_ffn": round(leg_us["sparse_ffn"], 3),
+            "bytes_predict_hidden": hidden_bytes,
+            "bytes_layer_from_hidden": round(float(rest_bytes.mean())),
+            "bytes_sparse_ffn_read": round(float(ffn_touched.mean())),
+            "bytes_sparse_ffn_predicted_rows": round(float(ffn_predicted.mean())),
+            "gbs_sparse_ffn": round(float(ffn_touched.mean()) / (leg_us["sparse_ffn"] * 1e-6) / 1e9, 1),
             "predictor_bytes": pred_bytes,
-            "ffn_bytes_predicted_rows": round(float(ffn_predicted.mean())),
-            "step_gb_touched": round(step_bytes / 1e9, 4),
+            "step_gb_algorithmic": round(step_bytes / 1e9, 4),
             "step_gbs": round(step_bytes / 1e9 / (ms_per_step / 1e3), 1),
             "active_density": round(float(n_act.mean()) / cfg.f, 4),
             "predicted_density": round(float(n_pred.mean()) / cfg.f, 4),
             "covered_share": round(float(n_act.sum() / max(n_pred.sum(), 1)), 4),
             "down_rows_zero_h_share": round(1.0 - float(n_live.sum()) / max(float(n_act.sum()), 1.0), 4),
-            "down_rows_read_share": round(float(n_read_down.sum()) / max(float(n_act.sum()), 1.0), 4),
         },
     }
     print(json.dumps(out), flush=True)
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe_mib} MiB read and written")
 
 
 if __name__ == "__main__":

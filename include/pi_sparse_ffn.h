@@ -131,6 +131,23 @@ int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int
                  float *y, uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws,
                  size_t ws_bytes, void *stream);
 
+/* The layer in two steps, split where pi_ffn_layer's first kernel ends (for callers that time or
+ * schedule the steps separately).  pi_predict_hidden writes z = max(0, P1 x_b) as fp32
+ * [batch][rank] to z (device, 16-byte aligned, caller-owned; no workspace).
+ * pi_ffn_layer_from_hidden then runs the rest of the layer from that z: logits, mask, placement
+ * restriction and the sparse FFN, with the arguments, workspace rules and results of pi_ffn_layer.
+ * pi_ffn_layer(...) is exactly pi_predict_hidden followed by pi_ffn_layer_from_hidden. */
+int pi_predict_hidden(const pi_predictor *pred, const void *x, int32_t batch, float *z, void *stream);
+int pi_ffn_layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch,
+                             const float *z, float *y, uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out,
+                             void *ws, size_t ws_bytes, void *stream);
+
+/* Which launches pi_ffn_layer_from_hidden makes for this layer and batch: 1 = one persistent kernel
+ * (logits, mask and sparse FFN together; x, z and the kernel's arrays fit one workgroup's LDS and
+ * d_ffn <= 12288), 2 = separate kernels (logits and mask, compaction, sparse FFN).  0 on invalid
+ * arguments. */
+int pi_layer_path(const pi_predictor *pred, const pi_ffn *ffn, int32_t batch);
+
 /* The same layer as ONE persistent kernel whose workgroups hand work to each other through the
  * workspace (same arguments and results as pi_ffn_layer).  Requires batch * d_model <= 32768 so
  * that x and the kernel's own arrays fit one workgroup's LDS (PI_ERR_SHAPE otherwise).

@@ -72,7 +72,14 @@ def fused_fits(d_model: int, batch: int) -> bool:
     return batch * d_model <= 32768
 
 
-LAYER_ENTRIES = {"layer": _abi.pi_ffn_layer, "fused": _abi.pi_ffn_layer_fused}
+def _layer_split(pred, ffn, x, batch, y, mask_out, idx_out, counts_out, ws, stream=None):
+    """pi_ffn_layer as its two published steps: pi_predict_hidden, then pi_ffn_layer_from_hidden."""
+    z = torch.empty((batch, pred.rank), dtype=torch.float32, device="cuda")
+    _abi.pi_predict_hidden(pred, x, batch, z, stream)
+    _abi.pi_ffn_layer_from_hidden(pred, ffn, x, batch, z, y, mask_out, idx_out, counts_out, ws, stream)
+
+
+LAYER_ENTRIES = {"layer": _abi.pi_ffn_layer, "fused": _abi.pi_ffn_layer_fused, "split": _layer_split}
 
 
 def gpu_layer(dl: DeviceLayer, x: np.ndarray, ws: torch.Tensor | None = None, entry: str = "layer"):

@@ -296,3 +296,24 @@ def test_many_calls_share_one_workspace(entry):
     assert _abi.workspace_status(ws) == 0
     got = check_layer_against_oracle(layers[1], dls[1], synth.make_x(cfg, 1, 4, 1), "after many calls", entries=(entry,))
     assert got["n"] > 0
+
+
+def test_split_layer_matches_whole_layer():
+    """pi_predict_hidden + pi_ffn_layer_from_hidden is bitwise pi_ffn_layer, and z = ReLU(P1 x) >= 0."""
+    for case in (dict(d=2048, f=5503, r=256, gated=True, wtype=F16, bias_up=False, density=0.12),
+                 dict(d=1536, f=6001, r=512, gated=False, wtype=F16, bias_up=True, density=0.06, hot_frac=0.26),
+                 dict(d=2048, f=4100, r=1024, gated=False, wtype=Q4, bias_up=True, density=0.05)):
+        cfg = synth.custom_config(**case, seed=71)
+        layer = synth.make_layer(cfg, 0, bias_scale=1.0, b_down=True)
+        dl = DeviceLayer.from_host(layer)
+        for B in (1, 3):
+            announce(f"split layer {case} B={B}")
+            x = synth.make_x(cfg, 0, 1, B)
+            whole = gpu_layer(dl, x, entry="layer")
+            split = gpu_layer(dl, x, entry="split")
+            assert np.array_equal(whole["y"], split["y"]) and np.array_equal(whole["idx"], split["idx"])
+            z = torch.empty((B, cfg.r), dtype=torch.float32, device="cuda")
+            _abi.pi_predict_hidden(dl.pred, to_dev(x), B, z)
+            torch.cuda.synchronize()
+            assert bool((z >= 0).all()) and bool(torch.isfinite(z).all())
+            check_layer_against_oracle(layer, dl, x, f"split B={B}", entries=("split",))
