@@ -127,6 +127,20 @@ __device__ bool poll_give_up(uint64_t t0, int32_t *ctl, int lane, int code) {
     return false;
 }
 
+// The same decision for a poll loop that has just re-issued its loads: `ab` is the abort word
+// loaded together with them (so a poll costs one round trip, not two).
+__device__ __forceinline__ bool poll_stop(int ab, uint64_t t0, int32_t *ctl, int lane, int code) {
+    if (__shfl(ab, 0, kWave)) return true;
+    if (wall_clock64() - t0 > kSpinTicks) {
+        if (lane == 0) {
+            store_coherent_i(ctl + CTL_ABORT, 1);
+            atomicOr(ctl + CTL_STATUS, code);
+        }
+        return true;
+    }
+    return false;
+}
+
 // Bounded wait by one thread until *p == stamp.  false = aborted.
 __device__ bool wait_stamp(const uint32_t *p, uint32_t stamp, int32_t *ctl) {
     const uint64_t t0 = wall_clock64();
@@ -148,8 +162,9 @@ __device__ __forceinline__ uint64_t poll_word(const uint64_t *p, uint32_t stamp,
     uint64_t w = p ? load_c64(p) : stamped(0u, stamp);
     const uint64_t t0 = wall_clock64();
     while (__ballot(!fresh(w, stamp)) != 0) {
-        if (poll_give_up(t0, ctl, lane, code)) break;
+        const int ab = lane == 0 ? load_coherent_i(ctl + CTL_ABORT) : 0;   // with the re-read
         if (!fresh(w, stamp)) w = load_c64(p);
+        if (poll_stop(ab, t0, ctl, lane, code)) break;
     }
     return w;
 }

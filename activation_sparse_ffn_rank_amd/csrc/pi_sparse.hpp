@@ -73,10 +73,12 @@ __device__ __forceinline__ void poll_words(const uint64_t *p, uint32_t stamp, in
 #pragma unroll
         for (int i = 0; i < W; ++i) stale |= !fresh(w[i], stamp);
         if (__ballot(stale) == 0) break;
-        if (poll_give_up(t0, ctl, lane, code)) break;
+        // the abort word and the stale words go out together: one round trip per poll
+        const int ab = lane == 0 ? load_coherent_i(ctl + CTL_ABORT) : 0;
 #pragma unroll
         for (int i = 0; i < W; ++i)
             if (!fresh(w[i], stamp)) w[i] = load_c64(p + i);
+        if (poll_stop(ab, t0, ctl, lane, code)) break;
     }
 }
 

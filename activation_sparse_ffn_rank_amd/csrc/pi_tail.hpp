@@ -18,8 +18,8 @@
 //   down  (NE = slabs * C) tile (column slab, chunk of consecutive neuron tiles): it polls the
 //                          chunk's tile words, lists the listed neurons in ascending order, issues
 //                          the loads of their W_down^T rows (its columns only) before h is known,
-//                          then polls h, accumulates, and hands its partial to the slab reduction
-//                          (the last chunk sums the C partials in chunk order, adds b_down, writes y).
+//                          then polls h, accumulates, and stores a partial; then each tile finishes
+//                          its share of the slab's columns: the C partials in chunk order + b_down.
 // No compaction pass is needed: a chunk's neurons are found from its own tile words, and every
 // sum runs in an order fixed by the mask alone, so results do not depend on timing.
 //
@@ -221,7 +221,7 @@ __device__ __forceinline__ void tail_up(const TailArgs &a, uint32_t stamp, int l
 
 template <int B, int WT>
 __device__ __forceinline__ void tail_down(const TailArgs &a, uint32_t stamp, int lane, int wave, int e, float *s_red, int *s_list,
-                          int *s_cnt, int *s_last, float *s_own) {
+                          int *s_cnt, float *s_own) {
     constexpr int CPL = kTailCPL, SLAB = kTailSlab;
     constexpr int U = 32;                               // rows in flight per wave
     constexpr int TPR = kTailListMax / 32;              // neuron tiles per round (one per lane)
@@ -340,7 +340,10 @@ __device__ __forceinline__ void tail_down(const TailArgs &a, uint32_t stamp, int
         __syncthreads();                                // s_list / s_cnt are rewritten next round
     }
 
-    // waves -> LDS -> stamped chunk partial -> slab ticket; the last chunk sums in chunk order
+    // Reduction, scattered over the slab's tiles: the 4 waves meet in LDS, the tile stores its
+    // stamped chunk partial, then tile ck finishes columns [ck*W, (ck+1)*W) of the slab: it polls
+    // those columns' partials of every chunk, sums them in chunk order (its own from LDS), adds
+    // b_down and writes y.  No ticket and no single workgroup reading the whole slab.
 #pragma unroll
     for (int b = 0; b < B; ++b)
 #pragma unroll
@@ -355,86 +358,54 @@ __device__ __forceinline__ void tail_down(const TailArgs &a, uint32_t stamp, int
         float sum = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) sum += s_red[((w * B + b) * CPL + t) * kWave + ln];
-        s_own[o] = sum;                                 // kept for this tile's own reduction
+        s_own[o] = sum;
         if (gcol < a.d) store_c64(a.part + (size_t)ck * Bd + (size_t)b * a.d + gcol, stamped_f(sum, stamp));
     }
     __syncthreads();
-    int32_t *ticket = a.ctl + CTL_LAYER0 + CTL_TICKET0 + 32 * slab;
-    if (threadIdx.x == 0) *s_last = (atomicAdd(ticket, 1) == a.C - 1);
-    __syncthreads();
     TAIL_TRACE(6, wall_clock64());
-    TAIL_TRACE(10, *s_last);
-    if (!*s_last) return;
-    // the last chunk to arrive: every other chunk's partial (already stored before its ticket, so
-    // normally current) for two outputs per thread at a time, then the sums in chunk order
-    // Every other chunk's partial through a buffer resource (coalesced loads; the lines were
-    // written through to memory by agent-coherent stores).  A copy this L2 might still hold carries
-    // an older stamp: then that output takes the slow path, which re-reads each word with
-    // agent-coherent loads.  Sums run in chunk order, this tile's own partial coming from LDS.
-    const __amdgpu_buffer_rsrc_t rp = buf_rsrc(a.part, (uint32_t)((size_t)a.C * Bd * 8));
-    constexpr int OPT = 2;
-    for (int o0 = threadIdx.x; o0 < B * SLAB; o0 += OPT * blockDim.x) {
-        uint64_t v[OPT][kSparseMaxChunks];
-        uint32_t off[OPT];
-        bool ok[OPT], stale[OPT];
-        float bd[OPT];
+    const int W = (SLAB + a.C - 1) / a.C;              // columns this tile finishes
+    const int c0 = ck * W, nc = max(0, min(W, SLAB - c0));
+    const int nout = B * nc;
+    for (int o0 = 0; o0 < nout; o0 += blockDim.x) {    // one output (token, column) per thread
+        const int o = o0 + threadIdx.x;
+        const int b = o / nc, cc = c0 + (o - b * nc);
+        const int gcol = slab * SLAB + cc;
+        const bool ok = o < nout && gcol < a.d;
+        const size_t off = (size_t)b * a.d + (ok ? gcol : 0);
+        const float bd = (ok && a.b_down != nullptr) ? half_to_float(a.b_down[gcol]) : 0.f;
+        uint64_t v[kSparseMaxChunks];
 #pragma unroll
-        for (int q = 0; q < OPT; ++q) {
-            const int o = o0 + q * blockDim.x;
-            const int b = o / SLAB, cc = o - b * SLAB;
-            const int gcol = slab * SLAB + cc;
-            ok[q] = o < B * SLAB && gcol < a.d;
-            off[q] = (uint32_t)(b * a.d + (ok[q] ? gcol : 0));
-            bd[q] = (ok[q] && a.b_down != nullptr) ? half_to_float(a.b_down[gcol]) : 0.f;
+        for (int c = 0; c < kSparseMaxChunks; ++c)
+            v[c] = (ok && c < a.C && c != ck) ? load_c64(a.part + (size_t)c * Bd + off) : stamped(0u, stamp);
+        float bdv = bd;
+        asm volatile("" : "+v"(bdv));                  // b_down arrives with the first partials
+        const uint64_t t0 = wall_clock64();
+        for (;;) {
+            bool stale = false;
 #pragma unroll
-            for (int c = 0; c < kSparseMaxChunks; ++c) {
-                const bool want = ok[q] && c < a.C && c != ck;
-                v[q][c] = bld8(rp, want ? ((uint32_t)c * (uint32_t)Bd + off[q]) * 8u : kOOB);
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < OPT; ++q) {
-            stale[q] = false;
+            for (int c = 0; c < kSparseMaxChunks; ++c) stale |= !fresh(v[c], stamp);
+            if (__syncthreads_or(stale) == 0) break;
+            // the abort word and the stale partials go out together: one round trip per poll
+            const int ab = threadIdx.x == 0 ? load_coherent_i(a.ctl + CTL_ABORT) : 0;
 #pragma unroll
             for (int c = 0; c < kSparseMaxChunks; ++c)
-                stale[q] |= ok[q] && c < a.C && c != ck && !fresh(v[q][c], stamp);
-        }
-        if (o0 == (int)threadIdx.x) TAIL_TRACE(7, wall_clock64());
-#ifdef PIK_TRACE
-        if (a.trace != nullptr && (stale[0] || stale[OPT - 1])) atomicAdd((unsigned long long *)&a.trace[(size_t)blockIdx.x * 16 + 11], 1ull);
-#endif
-#pragma unroll
-        for (int q = 0; q < OPT; ++q) {
-            const int o = o0 + q * blockDim.x;
-            if (!ok[q]) continue;
-            float sum = 0.f;
-            if (!stale[q]) {
-#pragma unroll
-                for (int c = 0; c < kSparseMaxChunks; ++c)
-                    if (c < a.C) sum += c == ck ? s_own[o] : word_f(v[q][c]);
-            } else {
-#pragma unroll 1
-                for (int c = 0; c < a.C; ++c) {
-                    if (c == ck) {
-                        sum += s_own[o];
-                        continue;
-                    }
-                    const uint64_t *pw = a.part + (size_t)c * Bd + off[q];
-                    uint64_t w = load_c64(pw);
-                    const uint64_t t0 = wall_clock64();
-                    while (!fresh(w, stamp) && !load_coherent_i(a.ctl + CTL_ABORT)) {
-                        if (wall_clock64() - t0 > kSpinTicks) {
-                            store_coherent_i(a.ctl + CTL_ABORT, 1);
-                            atomicOr(a.ctl + CTL_STATUS, 4);
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(2);
-                        w = load_c64(pw);
-                    }
-                    sum += word_f(w);
+                if (!fresh(v[c], stamp)) v[c] = load_c64(a.part + (size_t)c * Bd + off);
+            if (__syncthreads_or(ab)) break;
+            if (wall_clock64() - t0 > kSpinTicks) {
+                if (threadIdx.x == 0) {
+                    store_coherent_i(a.ctl + CTL_ABORT, 1);
+                    atomicOr(a.ctl + CTL_STATUS, 4);
                 }
+                break;
             }
-            a.y[off[q]] = sum + bd[q];
+        }
+        if (o0 == 0) TAIL_TRACE(7, wall_clock64());
+        if (ok) {
+            float sum = 0.f;
+#pragma unroll
+            for (int c = 0; c < kSparseMaxChunks; ++c)
+                if (c < a.C) sum += c == ck ? s_own[b * SLAB + cc] : word_f(v[c]);
+            a.y[off] = sum + bdv;
         }
     }
     TAIL_TRACE(8, wall_clock64());
@@ -450,7 +421,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __shared__ int s_list[kTailListMax];
     __shared__ uint32_t s_words[4];
     __shared__ int s_slot[32];
-    __shared__ int s_cnt, s_last;
+    __shared__ int s_cnt;
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     TAIL_TRACE(1, wall_clock64());
     const uint32_t stamp = (uint32_t)load_coherent_i(a.ctl + CTL_EPOCH) + 1u;
@@ -467,7 +438,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         TAIL_TRACE(2, wall_clock64());
         tail_up<B, GATED, WT, NT>(a, stamp, lane, wave, xs, zs, s_words, s_slot, pt);
     } else {
-        tail_down<B, WT>(a, stamp, lane, wave, blockIdx.x - a.PU, s_red, s_list, &s_cnt, &s_last, s_own);
+        tail_down<B, WT>(a, stamp, lane, wave, blockIdx.x - a.PU, s_red, s_list, &s_cnt, s_own);
     }
     TAIL_TRACE(0, up ? 1 : 2);
     TAIL_TRACE(9, wall_clock64());

@@ -265,8 +265,9 @@ def main():
         cpu = {"value": round(B / (per_layer * L), 3), "unit": "tokens/s", "cores": oracle.num_threads(),
                "kind": "oracle",
                "sample": f"{done} evaluations of the whole layer (predictor, mask, compaction, sparse FFN) at "
-                         f"batch {B}: layers 0..{n_lay - 1} of the same stack, tokens 0..{t - 1} of the seeded "
-                         f"inputs; {spent:.1f}s, {per_layer * 1e3:.2f} ms per layer, scaled to the {L}-layer step"}
+                         f"batch {B}: layers 0..{n_lay - 1} of the same stack, {t} token steps cycling over the "
+                         f"{W + K} seeded inputs; {spent:.1f}s, {per_layer * 1e3:.2f} ms per layer, scaled to the "
+                         f"{L}-layer step"}
 
     ms_per_step = elapsed_ms / K
     tokens_per_s = B * K / (elapsed_ms / 1e3)
