@@ -113,3 +113,49 @@ def test_status_strings(L):
         s = _abi.pi_status_string(code)
         assert s and s != "unknown status"
     assert _abi.pi_status_string(5) == "unknown status"
+
+
+def test_split_and_fused_layer_reject(L):
+    p, f = pred(), ffn()
+    big = ws_for(L, p, f, 2)
+    hid = lambda pp, x=A, B=2, z=A: L.pi_predict_hidden(pp, x, B, z, None)
+    assert hid(None) == _abi.PI_ERR_NULL
+    assert hid(ctypes.byref(p), z=0) == _abi.PI_ERR_NULL
+    assert hid(ctypes.byref(p), x=U) == _abi.PI_ERR_ALIGN
+    assert hid(ctypes.byref(p), z=U) == _abi.PI_ERR_ALIGN
+    assert hid(ctypes.byref(p), B=9) == _abi.PI_ERR_BATCH
+    rest = lambda pp, ff, B=2, z=A, n=big: L.pi_ffn_layer_from_hidden(pp, ff, A, B, z, A, None, None, None, A, n, None)
+    assert rest(ctypes.byref(p), ctypes.byref(f), z=0) == _abi.PI_ERR_NULL
+    assert rest(ctypes.byref(p), ctypes.byref(f), z=U) == _abi.PI_ERR_ALIGN
+    assert rest(ctypes.byref(p), ctypes.byref(f), n=big - 1) == _abi.PI_ERR_WORKSPACE
+    assert rest(ctypes.byref(pred(d=512)), ctypes.byref(f)) == _abi.PI_ERR_SHAPE
+    fused = lambda pp, ff, B=2, n=big: L.pi_ffn_layer_fused(pp, ff, A, B, A, None, None, None, A, n, None)
+    assert fused(ctypes.byref(p), ctypes.byref(f), n=big - 1) == _abi.PI_ERR_WORKSPACE
+    # x [B][d] fp16 must fit one workgroup's LDS (B * d <= 32768)
+    pb, fb = pred(d=8192, f=4096), ffn(d=8192, f=4096)
+    assert fused(ctypes.byref(pb), ctypes.byref(fb), B=8, n=ws_for(L, pb, fb, 8)) == _abi.PI_ERR_SHAPE
+
+
+def test_layer_path(L):
+    path = lambda pp, ff, B: L.pi_layer_path(ctypes.byref(pp) if pp else None, ctypes.byref(ff) if ff else None, B)
+    # one persistent kernel: d_ffn <= 12288 and x, z fit LDS
+    assert path(pred(d=4096, f=11008, r=1024), ffn(d=4096, f=11008, gated=1), 1) == 1
+    assert path(pred(d=1024, f=4096, r=128), ffn(d=1024, f=4096), 8) == 1
+    # separate kernels: too many neurons, or x too large for LDS
+    assert path(pred(d=8192, f=32768, r=1024), ffn(d=8192, f=32768), 1) == 2
+    assert path(pred(d=12288, f=12288, r=1024), ffn(d=12288, f=12288), 8) == 2
+    # invalid
+    assert path(pred(), ffn(), 0) == 0
+    assert path(pred(d=512), ffn(), 1) == 0
+    assert path(None, ffn(), 1) == 0
+
+
+def test_h_offset(L):
+    kind = ctypes.c_int32(0)
+    small, large = ffn(d=1024, f=4096), ffn(d=12288, f=4096)
+    off = L.pi_sparse_ffn_h_offset(ctypes.byref(small), 1, ctypes.byref(kind))
+    assert kind.value == 1 and 0 < off < ws_for(L, None, small, 1)
+    off = L.pi_sparse_ffn_h_offset(ctypes.byref(large), 8, ctypes.byref(kind))
+    assert kind.value == 2 and off == 0                       # x [8][12288] does not fit LDS: two kernels
+    assert L.pi_sparse_ffn_h_offset(ctypes.byref(small), 9, ctypes.byref(kind)) == 2**64 - 1
+    assert L.pi_sparse_ffn_h_offset(ctypes.byref(small), 1, None) == 2**64 - 1
