@@ -76,10 +76,26 @@ __device__ __forceinline__ float dot8(const uint4 &a, const uint4 &b, float c) {
     return fdot2(a.w, b.w, c);
 }
 
+// DPP lane permutation of v (gfx9 encodings: quad_perm, row_half_mirror, row_mirror).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the wave, returned in every lane.  Within each 16-lane row the sum is formed with DPP
+// moves (swap neighbours, swap pairs, mirror halves, mirror the row: every lane then holds its
+// row's sum), and the four row sums are added from scalar reads -- no LDS round trips, and a
+// fixed order, so the result does not depend on timing.
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-    return v;
+    v += dpp_f<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_f<0x141>(v);   // row_half_mirror
+    v += dpp_f<0x140>(v);   // row_mirror
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
 }
 
 // Broadcast lane j's value (j wave-uniform) through a scalar register.
