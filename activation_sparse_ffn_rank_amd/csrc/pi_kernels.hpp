@@ -82,6 +82,25 @@ __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
 
+template <int CTRL, int ROW_MASK, int BANK_MASK>
+__device__ __forceinline__ int dpp_i(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, BANK_MASK, false);
+}
+
+// Inclusive prefix sum over the wave: shifts by 1, 2, 3 within each 16-lane row, then by 4 and 8
+// (lanes that have them), then row 0's total into row 1 and row 2's into row 3, then rows 0-1's
+// total into rows 2-3.  Lanes a move does not reach add 0.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    int s = x + dpp_i<0x111, 0xF, 0xF>(x);   // row_shr:1
+    s += dpp_i<0x112, 0xF, 0xF>(x);           // row_shr:2
+    s += dpp_i<0x113, 0xF, 0xF>(x);           // row_shr:3
+    s += dpp_i<0x114, 0xF, 0xE>(s);           // row_shr:4, banks 1-3
+    s += dpp_i<0x118, 0xF, 0xC>(s);           // row_shr:8, banks 2-3
+    s += dpp_i<0x142, 0xA, 0xF>(s);           // row_bcast:15 into rows 1 and 3
+    s += dpp_i<0x143, 0xC, 0xF>(s);           // row_bcast:31 into rows 2 and 3
+    return s;
+}
+
 // Sum over the wave, returned in every lane.  Within each 16-lane row the sum is formed with DPP
 // moves (swap neighbours, swap pairs, mirror halves, mirror the row: every lane then holds its
 // row's sum), and the four row sums are added from scalar reads -- no LDS round trips, and a

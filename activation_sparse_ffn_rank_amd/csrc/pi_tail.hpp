@@ -73,8 +73,8 @@ __host__ __device__ inline size_t tail_dyn_lds(int B, int d, int r) {
 
 // ------------------------------------------------------------------------------ up workgroups
 
-// The P2 rows of one 32-neuron tile (wave w: rows 8w .. 8w+7), plus the offset and slot of the row
-// that lane (8i) owns after the reduce-scatter -- all loads issued together.
+// The P2 rows of one 32-neuron tile (wave w: rows 8w .. 8w+7), plus the offset and slot of row i in
+// lane i -- all loads issued together.
 template <int B, int NT>
 struct P2Tile {
     static constexpr int R = 8;
@@ -91,10 +91,10 @@ struct P2Tile {
                 const int row = row0 + i, col = lane * 8 + q * 512;
                 w[i][q] = bld16(rs, (row < a.f && col < a.r) ? ((uint32_t)row * a.r + col) * 2 : kOOB);
             }
-        const int row = row0 + lane / (kWave / R);
-        const bool owner = (lane % (kWave / R)) == 0 && row < a.f;
-        c = owner ? a.c[row] : (uint16_t)0;
-        slot = owner ? (a.slot_of ? a.slot_of[row] : row) : -1;
+        const int row = row0 + lane;                 // lane i < R: offset and slot of row i
+        const bool mine = lane < R && row < a.f;
+        c = mine ? a.c[row] : (uint16_t)0;
+        slot = mine ? (a.slot_of ? a.slot_of[row] : row) : -1;
     }
 };
 
@@ -122,19 +122,16 @@ __device__ __forceinline__ void tail_publish(const TailArgs &a, int id, int s, f
 template <int B, bool GATED, int WT, int NT>
 __device__ __forceinline__ void tail_up(const TailArgs &a, uint32_t stamp, int lane, int wave, const uint16_t *xs, const float *zs,
                         uint32_t *s_words, int *s_slot, P2Tile<B, NT> &pt) {
-    constexpr int R = P2Tile<B, NT>::R, G = kWave / R;
+    constexpr int R = P2Tile<B, NT>::R;
     const int64_t in_stride = GATED ? 2 * a.row_bytes : a.row_bytes;
     const __amdgpu_buffer_rsrc_t rin = buf_rsrc(a.w_in, (uint32_t)(a.n_slots * in_stride));
     bool first = true;
     for (int t = blockIdx.x; t < a.NTL; t += a.PU) {
         if (!first) pt.issue(a, t, wave, lane);
         first = false;
-        const int ri = lane / G;
-        const int row = t * 32 + wave * R + ri;
-        const bool owner = (lane % G) == 0 && row < a.f;
+        const int row0 = t * 32 + wave * R;
         const float ci = half_to_float(pt.c);
-        const int slot = pt.slot;
-        uint8_t m = 0;
+        uint32_t mb = 0;                            // fired bits of the wave's rows (uniform)
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             float v[R];
@@ -159,17 +156,19 @@ __device__ __forceinline__ void tail_up(const TailArgs &a, uint32_t stamp, int l
                     }
                 }
             }
-            const float l = reduce_scatter<R>(v, lane) + ci;
-            if (owner) m |= (uint8_t)(l > 0.f);
-        }
-        if (owner && a.mask != nullptr) a.mask[row] = m;
-        const bool resident = slot >= 0 && slot < a.n_slots;
-        if (owner) s_slot[wave * R + ri] = resident ? slot : -1;
-        // the tile's listed bits: wave w's rows are tile rows 8w .. 8w+7, owned by lanes 0, 8, ..., 56
-        const uint64_t lb = __ballot(owner && m && resident);
-        uint32_t byte = 0;
 #pragma unroll
-        for (int i = 0; i < R; ++i) byte |= (uint32_t)((lb >> (i * G)) & 1u) << i;
+            for (int i = 0; i < R; ++i) {
+                const float l = wave_sum(v[i]) + bcastf(ci, i);
+                mb |= (uint32_t)(l > 0.f) << i;
+            }
+        }
+        const int row = row0 + lane;
+        const bool mine = lane < R && row < a.f;
+        if (mine && a.mask != nullptr) a.mask[row] = (uint8_t)((mb >> lane) & 1u);
+        const bool resident = pt.slot >= 0 && pt.slot < a.n_slots;
+        if (lane < R) s_slot[wave * R + lane] = resident ? pt.slot : -1;
+        // the tile's listed bits: wave w's rows are tile rows 8w .. 8w+7
+        const uint32_t byte = mb & (uint32_t)__ballot(mine && resident);
         if (lane == 0) s_words[wave] = byte;
         if (t == (int)blockIdx.x) TAIL_TRACE(3, wall_clock64());
         __syncthreads();
@@ -248,14 +247,9 @@ __device__ __forceinline__ void tail_down(const TailArgs &a, uint32_t stamp, int
             const int valid = mine ? min(32, a.f - tt * 32) : 0;
             const uint32_t word = mine ? (uint32_t)w1[0] & (valid >= 32 ? 0xFFFFFFFFu : ((1u << valid) - 1u)) : 0u;
             const int c = __builtin_popcount(word);
-            int incl = c;
-#pragma unroll
-            for (int o = 1; o < kWave; o <<= 1) {
-                const int v = __shfl_up(incl, o, kWave);
-                if (lane >= o) incl += v;
-            }
+            const int incl = wave_incl_scan(c);
             int pos = incl - c;
-            for (uint32_t bits = word; bits; bits &= bits - 1) s_list[pos++] = tt * 32 + __builtin_ctz(bits);
+            for (uint32_t bits = word; bits && pos < kTailListMax; bits &= bits - 1) s_list[pos++] = tt * 32 + __builtin_ctz(bits);
             if (lane == kWave - 1) *s_cnt = incl;
             if (tb == T0) TAIL_TRACE(2, wall_clock64());
         }
