@@ -115,12 +115,16 @@ SparseGeom sparse_geom(const pi_ffn *fn, int B) {
     return g;
 }
 
-bool sparse_persistent(const pi_ffn *fn, int B) { return persistent_fits(fn->d_model, B); }
+// The persistent form needs every workgroup resident; at batch > 2 its x copy and partial arrays
+// leave too few resident workgroups per CU, and the two-kernel form is faster (measured).
+bool sparse_persistent(const pi_ffn *fn, int B) { return B <= 2 && persistent_fits(fn->d_model, B); }
 
 // The tail kernel (second predictor matrix + mask + sparse FFN) keeps x [B][d] fp16 and z [B][r]
 // fp32 in dynamic LDS next to its static arrays (wave partials of the down tiles, the list of a
 // down tile's neurons, a few words); all of it must fit one workgroup.  It is used while every
-// 32-neuron tile can have an up workgroup of its own (d_ffn <= 32 * kTailMaxTiles).
+// 32-neuron tile can have an up workgroup of its own (d_ffn <= 32 * kTailMaxTiles), and at batch
+// <= 2 up to d_ffn = 32 * kTailMaxTilesB2 (up workgroups then take several tiles each; measured
+// faster than separate kernels there, slower at larger batch).
 bool tail_persistent(const pi_predictor *p, const pi_ffn *fn, int B) {
     const size_t stat = (size_t)4 * B * kTailCPL * 64 * 4 + (size_t)B * kTailSlab * 4 + (size_t)kTailListMax * 4 + 512;
     // the kernel reads through 32-bit buffer offsets: every matrix (and the partials) must stay
@@ -129,7 +133,9 @@ bool tail_persistent(const pi_predictor *p, const pi_ffn *fn, int B) {
     const int64_t p2_bytes = (int64_t)p->d_ffn * p->rank * 2;
     const int64_t part_bytes = (int64_t)kSparseMaxChunks * B * fn->d_model * 8;
     if (in_bytes >= (int64_t)kBufMax || p2_bytes >= (int64_t)kBufMax || part_bytes >= (int64_t)kBufMax) return false;
-    return ceil_div(fn->d_ffn, 32) <= kTailMaxTiles && (size_t)B * fn->d_model * 2 <= (size_t)kLdsXBytes &&
+    const int tiles = ceil_div(fn->d_ffn, 32);
+    if (tiles > (B <= 2 ? kTailMaxTilesB2 : kTailMaxTiles)) return false;
+    return (size_t)B * fn->d_model * 2 <= (size_t)kLdsXBytes &&
            tail_dyn_lds(B, fn->d_model, p->rank) + stat <= 160 * 1024;
 }
 

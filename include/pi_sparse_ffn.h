@@ -111,8 +111,9 @@ int pi_compact(const uint8_t *mask, int32_t d_ffn, const int32_t *slot_of, int32
  * compute only the active neurons).  idx and counts are device memory (as pi_compact writes
  * them); n is clamped to [0, n_slots] and entries whose neuron or slot is out of range are
  * skipped.  y [batch][d_model] fp32 is overwritten.
- * When batch * d_model <= 32768 this is ONE persistent kernel: workgroups computing h for groups
- * of four listed neurons hand (slot, h) entries to the workgroups that accumulate the rows of
+ * When batch <= 2 and batch * d_model <= 32768 this is ONE persistent kernel: workgroups
+ * computing h for groups of four listed neurons hand (slot, h) entries to the workgroups that
+ * accumulate the rows of
  * W_down^T, through the workspace.  Then:
  *  - the workspace must be zero-filled before the first call that uses it, and each call leaves
  *    it ready for the next one (never clear or share it while a call is in flight);
@@ -144,8 +145,8 @@ int pi_ffn_layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const 
 
 /* Which launches pi_ffn_layer_from_hidden makes for this layer and batch: 1 = one persistent kernel
  * (logits, mask and sparse FFN together; x, z and the kernel's arrays fit one workgroup's LDS and
- * d_ffn <= 12288), 2 = separate kernels (logits and mask, compaction, sparse FFN).  0 on invalid
- * arguments. */
+ * d_ffn <= 12288, or d_ffn <= 32768 at batch <= 2), 2 = separate kernels (logits and mask,
+ * compaction, sparse FFN).  0 on invalid arguments. */
 int pi_layer_path(const pi_predictor *pred, const pi_ffn *ffn, int32_t batch);
 
 /* The same layer as ONE persistent kernel whose workgroups hand work to each other through the

@@ -141,8 +141,10 @@ def test_layer_path(L):
     # one persistent kernel: d_ffn <= 12288 and x, z fit LDS
     assert path(pred(d=4096, f=11008, r=1024), ffn(d=4096, f=11008, gated=1), 1) == 1
     assert path(pred(d=1024, f=4096, r=128), ffn(d=1024, f=4096), 8) == 1
-    # separate kernels: too many neurons, or x too large for LDS
-    assert path(pred(d=8192, f=32768, r=1024), ffn(d=8192, f=32768), 1) == 2
+    assert path(pred(d=8192, f=32768, r=1024), ffn(d=8192, f=32768), 1) == 1    # several tiles per workgroup
+    # separate kernels: too many neurons for the batch, or x too large for LDS
+    assert path(pred(d=8192, f=32768, r=1024), ffn(d=8192, f=32768), 4) == 2
+    assert path(pred(d=12288, f=49152, r=1024), ffn(d=12288, f=49152), 1) == 2
     assert path(pred(d=12288, f=12288, r=1024), ffn(d=12288, f=12288), 8) == 2
     # invalid
     assert path(pred(), ffn(), 0) == 0
@@ -157,5 +159,7 @@ def test_h_offset(L):
     assert kind.value == 1 and 0 < off < ws_for(L, None, small, 1)
     off = L.pi_sparse_ffn_h_offset(ctypes.byref(large), 8, ctypes.byref(kind))
     assert kind.value == 2 and off == 0                       # x [8][12288] does not fit LDS: two kernels
+    L.pi_sparse_ffn_h_offset(ctypes.byref(small), 4, ctypes.byref(kind))
+    assert kind.value == 2                                    # batch > 2: two kernels
     assert L.pi_sparse_ffn_h_offset(ctypes.byref(small), 9, ctypes.byref(kind)) == 2**64 - 1
     assert L.pi_sparse_ffn_h_offset(ctypes.byref(small), 1, None) == 2**64 - 1
