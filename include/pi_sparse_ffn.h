@@ -112,15 +112,14 @@ int pi_compact(const uint8_t *mask, int32_t d_ffn, const int32_t *slot_of, int32
  * them); n is clamped to [0, n_slots] and entries whose neuron or slot is out of range are
  * skipped.  y [batch][d_model] fp32 is overwritten.
  * When batch <= 2 and batch * d_model <= 32768 this is ONE persistent kernel: workgroups
- * computing h for groups of four listed neurons hand (slot, h) entries to the workgroups that
- * accumulate the rows of
- * W_down^T, through the workspace.  Then:
+ * computing h for groups of four listed neurons hand (slot, h) entries, through the workspace, to
+ * the workgroups that accumulate the rows of W_down^T.  Then:
  *  - the workspace must be zero-filled before the first call that uses it, and each call leaves
  *    it ready for the next one (never clear or share it while a call is in flight);
  *  - the int32 at byte offset 384 of the workspace is a sticky status word: nonzero means a
  *    cross-workgroup wait ran out its time limit (20 ms) and the outputs of that call are invalid.
- * Every wait inside the kernel is bounded.  Larger shapes run two kernels (h, then the rows of
- * W_down^T) and need no zero fill. */
+ * Every wait inside the kernel is bounded.  Other shapes and batches run two kernels (h, then the
+ * rows of W_down^T) and need no zero fill. */
 int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx,
                   const int32_t *counts, float *y, void *ws, size_t ws_bytes, void *stream);
 
