@@ -465,18 +465,22 @@ __device__ void task_E(const FusedArgs &a, int e, int lane, int wave, uint32_t s
                 } else {
                     uint32_t cw[U];
                     uint16_t sc[U];
+                    bool okv[U];
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
+                        // unconditional loads (row 0, column 0 stand in for an absent row or
+                        // column), so that all U rows are in flight before the first conversion
                         const int s = js[u] >= 0 ? bcast(sl, js[u]) : -1;
-                        const bool ok = s >= 0 && colok;
-                        const uint8_t *row = a.w_dn + (int64_t)(ok ? s : 0) * a.row_bytes;
-                        cw[u] = ok ? *reinterpret_cast<const uint32_t *>(row + col / 2) : 0u;
-                        sc[u] = ok ? *reinterpret_cast<const uint16_t *>(row + a.d / 2 + (col / 32) * 2) : (uint16_t)0;
+                        okv[u] = s >= 0 && colok;
+                        const uint8_t *row = a.w_dn + (int64_t)(okv[u] ? s : 0) * a.row_bytes;
+                        const int cc = colok ? col : 0;
+                        cw[u] = *reinterpret_cast<const uint32_t *>(row + cc / 2);
+                        sc[u] = *reinterpret_cast<const uint16_t *>(row + a.d / 2 + (cc / 32) * 2);
                     }
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         if (js[u] < 0) continue;
-                        const float scf = half_to_float(sc[u]);
+                        const float scf = okv[u] ? half_to_float(sc[u]) : 0.f;
 #pragma unroll
                         for (int p = 0; p < 4; ++p) {
                             const h2 pr = __builtin_bit_cast(h2, q4pair(cw[u], 4 * p));
@@ -608,7 +612,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B <= 2 ? 3 
     __shared__ int s_misc[4 * (kWave + 1) + 32 * 4 + 8];        // E prefix / D ids / X scan
     __shared__ uint32_t s_words[8];
     __shared__ int s_last;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const uint32_t stamp = (uint32_t)load_coherent_i(a.ctl + CTL_EPOCH) + 1u;
     stage_x<B, WT == WT_Q4_0>(xs, a.x, a.d, 0, a.d, a.d);
     __syncthreads();

@@ -229,7 +229,7 @@ __global__ __launch_bounds__(256) void k_pred_l1(const uint16_t *__restrict__ p1
                                                  float *__restrict__ z, int d, int r) {
     constexpr int U = 8;                      // 16-byte loads per thread per pass (16384 columns)
     __shared__ float red[4][B];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int j = blockIdx.x;
     const uint16_t *row = p1 + (size_t)j * d;
     float acc[B];
@@ -267,7 +267,7 @@ template <int B, int NT, int R>
 __global__ __launch_bounds__(256) void k_pred_l2(const uint16_t *__restrict__ p2, const uint16_t *__restrict__ c,
                                                  const float *__restrict__ z, int r, int f,
                                                  float *__restrict__ logits, uint8_t *__restrict__ mask) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int row0 = (blockIdx.x * 4 + wave) * R;
     if (row0 >= f) return;
     uint4 w[R][NT];
@@ -334,7 +334,7 @@ static __global__ __launch_bounds__(1024) void k_compact(const uint8_t *__restri
                                                   const int32_t *__restrict__ slot_of, int32_t *__restrict__ idx,
                                                   int32_t *__restrict__ counts) {
     __shared__ int wsum[16], wpred[16];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int seg = (((f + 1023) / 1024) + 15) & ~15;
     const int i0 = tid * seg;
     const int i1 = min(i0 + seg, f);
@@ -456,13 +456,16 @@ struct RowPass {
                 if (GATED) wg[GATED ? v : 0] = col < d ? ld16(gr + col) : zero4();
             }
         } else {
+            // Unconditional loads from a clamped block (consume() skips blocks past the row):
+            // a guarded load would let the compiler pull the scale conversion into the guard and
+            // wait for each block's load before issuing the next.
             const uint16_t *scales = reinterpret_cast<const uint16_t *>(row + d / 2);
             const int nq = d / 32;
 #pragma unroll
             for (int v = 0; v < V; ++v) {
-                const int q = p0 + lane + v * kWave;
-                wu[v] = q < nq ? ld16(row + (size_t)q * 16) : zero4();
-                sc[WT == WT_Q4_0 ? v : 0] = q < nq ? scales[q] : (uint16_t)0;
+                const int q = min(p0 + lane + v * kWave, nq - 1);
+                wu[v] = ld16(row + (size_t)q * 16);
+                sc[WT == WT_Q4_0 ? v : 0] = scales[q];
             }
         }
     }
@@ -566,7 +569,7 @@ __global__ __launch_bounds__(256) void k_sparse_up(const uint8_t *__restrict__ w
                                                    float *__restrict__ h, int h_stride, int xch,
                                                    int32_t *__restrict__ zero_ptr, int nzero) {
     extern __shared__ __align__(16) uint16_t xs[];
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (blockIdx.x == 0)
         for (int t = threadIdx.x; t < nzero; t += blockDim.x) zero_ptr[t] = 0;
     const int G = gridDim.x;
@@ -670,7 +673,7 @@ __global__ __launch_bounds__(256) void k_sparse_down(const uint8_t *__restrict__
     constexpr int U = 8;
     __shared__ float red[4][B][8][kWave];
     __shared__ int s_last;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int slab = blockIdx.x, ck = blockIdx.y;
     const int n = min(max(counts[0], 0), n_slots);
     const int k0 = (int)((int64_t)n * ck / C), k1 = (int)((int64_t)n * (ck + 1) / C);
@@ -727,18 +730,22 @@ __global__ __launch_bounds__(256) void k_sparse_down(const uint8_t *__restrict__
             } else {
                 uint32_t cw[U];
                 uint16_t sc[U];
+                bool okv[U];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
+                    // unconditional loads (row 0, column 0 stand in for an absent row or column),
+                    // so that all U rows are in flight before the first scale is converted
                     const int s = js[u] >= 0 ? bcast(sl, js[u]) : -1;
-                    const bool ok = s >= 0 && colok;
-                    const uint8_t *row = w_dn + (int64_t)(ok ? s : 0) * row_bytes;
-                    cw[u] = ok ? *reinterpret_cast<const uint32_t *>(row + col / 2) : 0u;
-                    sc[u] = ok ? *reinterpret_cast<const uint16_t *>(row + d / 2 + (col / 32) * 2) : (uint16_t)0;
+                    okv[u] = s >= 0 && colok;
+                    const uint8_t *row = w_dn + (int64_t)(okv[u] ? s : 0) * row_bytes;
+                    const int cc = colok ? col : 0;
+                    cw[u] = *reinterpret_cast<const uint32_t *>(row + cc / 2);
+                    sc[u] = *reinterpret_cast<const uint16_t *>(row + d / 2 + (cc / 32) * 2);
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     if (js[u] < 0) continue;
-                    const float scf = half_to_float(sc[u]);
+                    const float scf = okv[u] ? half_to_float(sc[u]) : 0.f;
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
                         // q4pair(w, 4p) = (code_p - 8, code_{p+4} - 8): columns p and p+4.

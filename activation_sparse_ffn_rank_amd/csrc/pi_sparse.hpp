@@ -13,9 +13,10 @@
 //   down  (NE = slabs * C) tile (column slab, chunk of the list): it looks up its positions' slots
 //                          and issues the loads of their W_down^T rows, restricted to its columns,
 //                          BEFORE h is known -- so the down rows stream while the up rows do --
-//                          then polls h, accumulates, and hands its partial to the slab's
-//                          reduction: the last chunk to arrive sums the C partials in chunk order,
-//                          adds b_down and writes y.  Every result is independent of timing.
+//                          then polls h, accumulates, and stores its stamped chunk partial; each
+//                          tile of a slab then finishes 1/C of the slab's columns, summing the C
+//                          partials in chunk order, adding b_down and writing y.  Every result
+//                          is independent of timing.
 // Reading the down rows before h is known means rows whose h is zero for every token are read
 // too (their products are skipped); it removes a dependent HBM round trip from the critical path.
 //
@@ -52,7 +53,7 @@ struct SparseArgs {
     const uint16_t *x;
     float *y;
     const int32_t *idx, *counts;
-    int32_t *ctl;        // control block (epoch, exit count, abort, status, slab tickets)
+    int32_t *ctl;        // control block (epoch, exit count, abort, status)
     uint64_t *ent;       // [n_slots][1 + B]: slot, then h per token, stamped
     uint64_t *part;      // [C][B][d] chunk partials, stamped
 #ifdef PIK_TRACE
@@ -122,8 +123,7 @@ __device__ void sparse_up(const SparseArgs &a, int n, uint32_t stamp, int lane, 
 // ------------------------------------------------------------------------------ down tiles
 
 template <int B, int WT>
-__device__ void sparse_down(const SparseArgs &a, int n, uint32_t stamp, int lane, int wave, int e, float *s_red,
-                            int *s_last) {
+__device__ void sparse_down(const SparseArgs &a, int n, uint32_t stamp, int lane, int wave, int e, float *s_red) {
     using DC = DownCols<WT>;
     constexpr int CPL = DC::CPL, SLAB = DC::SLAB;
     constexpr int U = 32;                               // rows in flight per wave
@@ -131,6 +131,11 @@ __device__ void sparse_down(const SparseArgs &a, int n, uint32_t stamp, int lane
     const int p0 = (int)((int64_t)n * ck / a.C), p1 = (int)((int64_t)n * (ck + 1) / a.C);
     const int col = slab * SLAB + lane * CPL;
     const bool colok = col < a.d;
+    // This lane's bytes of any row (a lane past d reads column 0 and never stores it): the loads
+    // below are unconditional, so that the compiler issues all U of them before the first use.
+    const int cc = colok ? col : 0;
+    const uint8_t *wcol = a.w_dn + (WT == WT_F16 ? (int64_t)cc * 2 : (int64_t)cc / 2);
+    const uint8_t *wsc = a.w_dn + a.d / 2 + (cc / 32) * 2;
     float acc[B][CPL];
 #pragma unroll
     for (int b = 0; b < B; ++b)
@@ -142,6 +147,7 @@ __device__ void sparse_down(const SparseArgs &a, int n, uint32_t stamp, int lane
         const int m = min(kWave, (p1 - base + 3) / 4);  // lanes 0..m-1 hold a position
         const int k = base + 4 * lane;
         const int s = lane < m ? slot_of_id(a.idx[k], a.slot_of, a.f, a.n_slots) : -1;
+        const int sr = s >= 0 ? s : 0;                  // an absent row reads row 0; its h is 0
         float hv[B];
         for (int j0 = 0; j0 < m; j0 += U) {
             // loads of the next U rows (restricted to this tile's columns) go out first
@@ -150,16 +156,12 @@ __device__ void sparse_down(const SparseArgs &a, int n, uint32_t stamp, int lane
             uint16_t sq[WT == WT_Q4_0 ? U : 1];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                const int j = j0 + u;
-                const int sj = j < m ? bcast(s, j) : -1;
-                const bool ok = sj >= 0 && colok;
-                const uint8_t *row = a.w_dn + (int64_t)(ok ? sj : 0) * a.row_bytes;
+                const int64_t ro = (int64_t)__builtin_amdgcn_readlane(sr, j0 + u) * a.row_bytes;
                 if (WT == WT_F16) {
-                    wf[WT == WT_F16 ? u : 0] = ok ? *reinterpret_cast<const uint2 *>(row + (int64_t)col * 2) : uint2{0u, 0u};
+                    wf[WT == WT_F16 ? u : 0] = *reinterpret_cast<const uint2 *>(wcol + ro);
                 } else {
-                    wq[WT == WT_Q4_0 ? u : 0] = ok ? *reinterpret_cast<const uint32_t *>(row + col / 2) : 0u;
-                    sq[WT == WT_Q4_0 ? u : 0] =
-                        ok ? *reinterpret_cast<const uint16_t *>(row + a.d / 2 + (col / 32) * 2) : (uint16_t)0;
+                    wq[WT == WT_Q4_0 ? u : 0] = *reinterpret_cast<const uint32_t *>(wcol + ro);
+                    sq[WT == WT_Q4_0 ? u : 0] = *reinterpret_cast<const uint16_t *>(wsc + ro);
                 }
             }
             if (j0 == 0) {
@@ -210,8 +212,15 @@ __device__ void sparse_down(const SparseArgs &a, int n, uint32_t stamp, int lane
             }
         }
     }
+#ifdef PIK_TRACE
+    if (a.trace != nullptr && threadIdx.x == 0) a.trace[(size_t)blockIdx.x * 8 + 4] = wall_clock64() + (acc[0][0] == 1e30f ? 1 : 0);
+#endif
 
-    // waves -> LDS -> stamped chunk partial -> slab ticket; the last chunk sums in chunk order
+    // Reduction, scattered over the slab's tiles: the 4 waves meet in LDS, the tile stores its
+    // stamped chunk partial, then tile ck finishes columns [ck*W, (ck+1)*W) of the slab: it polls
+    // those columns' partials of every other chunk, sums all C in chunk order (its own from LDS),
+    // adds b_down and writes y.  The tile's own partial of (token b, column ln*CPL + t) is kept
+    // in wave 0's LDS entry for it, which only the thread that sums that entry touches.
 #pragma unroll
     for (int b = 0; b < B; ++b)
 #pragma unroll
@@ -219,53 +228,65 @@ __device__ void sparse_down(const SparseArgs &a, int n, uint32_t stamp, int lane
     __syncthreads();
     const int Bd = B * a.d;
     for (int o = threadIdx.x; o < B * SLAB; o += blockDim.x) {
-        const int b = o / SLAB, cc = o - b * SLAB;
-        const int ln = cc / CPL, t = cc - ln * CPL;
-        const int gcol = slab * SLAB + cc;
-        if (gcol < a.d) {
-            float sum = 0.f;
+        const int b = o / SLAB, c = o - b * SLAB;
+        const int ln = c / CPL, t = c - ln * CPL;
+        const int gcol = slab * SLAB + c;
+        float sum = 0.f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) sum += s_red[((w * B + b) * CPL + t) * kWave + ln];
-            store_c64(a.part + (size_t)ck * Bd + (size_t)b * a.d + gcol, stamped_f(sum, stamp));
-        }
+        for (int w = 0; w < 4; ++w) sum += s_red[((w * B + b) * CPL + t) * kWave + ln];
+        s_red[(b * CPL + t) * kWave + ln] = sum;
+        if (gcol < a.d) store_c64(a.part + (size_t)ck * Bd + (size_t)b * a.d + gcol, stamped_f(sum, stamp));
     }
     __syncthreads();
-    int32_t *ticket = a.ctl + CTL_LAYER0 + CTL_TICKET0 + 32 * slab;
-    if (threadIdx.x == 0) *s_last = (atomicAdd(ticket, 1) == a.C - 1);
-    __syncthreads();
-    if (!*s_last) return;
-    for (int o = threadIdx.x; o < B * SLAB; o += blockDim.x) {
-        const int b = o / SLAB, cc = o - b * SLAB;
-        const int gcol = slab * SLAB + cc;
-        const bool ok = gcol < a.d;
+#ifdef PIK_TRACE
+    if (a.trace != nullptr && threadIdx.x == 0) a.trace[(size_t)blockIdx.x * 8 + 5] = wall_clock64();
+#endif
+    const int W = (SLAB + a.C - 1) / a.C;              // columns this tile finishes
+    const int c0 = ck * W, nc = max(0, min(W, SLAB - c0));
+    const int nout = B * nc;
+    for (int o0 = 0; o0 < nout; o0 += blockDim.x) {    // one output (token, column) per thread
+        const int o = o0 + threadIdx.x;
+        const int b = o / max(nc, 1), c = c0 + (o - b * nc);
+        const int gcol = slab * SLAB + c;
+        const bool ok = o < nout && gcol < a.d;
         const size_t off = (size_t)b * a.d + (ok ? gcol : 0);
+        const float bd = (ok && a.b_down != nullptr) ? half_to_float(a.b_down[gcol]) : 0.f;
         uint64_t v[kSparseMaxChunks];
 #pragma unroll
-        for (int c = 0; c < kSparseMaxChunks; ++c)
-            v[c] = (ok && c < a.C) ? load_c64(a.part + (size_t)c * Bd + off) : stamped(0u, stamp);
-        // a chunk's partial store may still be in flight: re-read the stale ones (bounded)
+        for (int q = 0; q < kSparseMaxChunks; ++q)
+            v[q] = (ok && q < a.C && q != ck) ? load_c64(a.part + (size_t)q * Bd + off) : stamped(0u, stamp);
+        float bdv = bd;
+        asm volatile("" : "+v"(bdv));                  // b_down arrives with the first partials
         const uint64_t t0 = wall_clock64();
         for (;;) {
             bool stale = false;
 #pragma unroll
-            for (int c = 0; c < kSparseMaxChunks; ++c) stale |= !fresh(v[c], stamp);
-            if (!stale || load_coherent_i(a.ctl + CTL_ABORT)) break;
+            for (int q = 0; q < kSparseMaxChunks; ++q) stale |= !fresh(v[q], stamp);
+            if (__syncthreads_or(stale) == 0) break;
+            // the abort word and the stale partials go out together: one round trip per poll
+            const int ab = threadIdx.x == 0 ? load_coherent_i(a.ctl + CTL_ABORT) : 0;
+#pragma unroll
+            for (int q = 0; q < kSparseMaxChunks; ++q)
+                if (!fresh(v[q], stamp)) v[q] = load_c64(a.part + (size_t)q * Bd + off);
+            if (__syncthreads_or(ab)) break;
             if (wall_clock64() - t0 > kSpinTicks) {
-                store_coherent_i(a.ctl + CTL_ABORT, 1);
-                atomicOr(a.ctl + CTL_STATUS, 4);
+                if (threadIdx.x == 0) {
+                    store_coherent_i(a.ctl + CTL_ABORT, 1);
+                    atomicOr(a.ctl + CTL_STATUS, 4);
+                }
                 break;
             }
-#pragma unroll
-            for (int c = 0; c < kSparseMaxChunks; ++c)
-                if (!fresh(v[c], stamp)) v[c] = load_c64(a.part + (size_t)c * Bd + off);
         }
-        float sum = 0.f;
-#pragma unroll
-        for (int c = 0; c < kSparseMaxChunks; ++c)
-            if (c < a.C) sum += word_f(v[c]);
+#ifdef PIK_TRACE
+        if (a.trace != nullptr && threadIdx.x == 0 && o0 == 0) a.trace[(size_t)blockIdx.x * 8 + 6] = wall_clock64();
+#endif
         if (ok) {
-            if (a.b_down != nullptr) sum += half_to_float(a.b_down[gcol]);
-            a.y[off] = sum;
+            const int ln = c / CPL, t = c - ln * CPL;
+            float sum = 0.f;
+#pragma unroll
+            for (int q = 0; q < kSparseMaxChunks; ++q)
+                if (q < a.C) sum += q == ck ? s_red[(b * CPL + t) * kWave + ln] : word_f(v[q]);
+            a.y[off] = sum + bdv;
         }
     }
 }
@@ -276,13 +297,12 @@ template <int B, bool GATED, int WT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B <= 2 ? 3 : 2))) void k_sparse_ffn(SparseArgs a) {
     extern __shared__ __align__(16) uint16_t xs[];              // x [B][d] (q4-paired for Q4_0), up only
     __shared__ float s_red[4 * B * DownCols<WT>::CPL * kWave];
-    __shared__ int s_last;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
 #ifdef PIK_TRACE
     if (a.trace != nullptr && threadIdx.x == 0) a.trace[(size_t)blockIdx.x * 8 + 1] = wall_clock64();
 #endif
     const uint32_t stamp = (uint32_t)load_coherent_i(a.ctl + CTL_EPOCH) + 1u;
-    const int n = min(max(a.counts[0], 0), a.n_slots);
+    const int n = __builtin_amdgcn_readfirstlane(min(max(a.counts[0], 0), a.n_slots));
     const bool up = (int)blockIdx.x < a.PD;
     if (up) {
         stage_x<B, WT == WT_Q4_0>(xs, a.x, a.d, 0, a.d, a.d);
@@ -292,7 +312,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B <= 2 ? 3 
 #endif
         sparse_up<B, GATED, WT>(a, n, stamp, lane, wave, xs);
     } else {
-        sparse_down<B, WT>(a, n, stamp, lane, wave, blockIdx.x - a.PD, s_red, &s_last);
+        sparse_down<B, WT>(a, n, stamp, lane, wave, blockIdx.x - a.PD, s_red);
     }
 #ifdef PIK_TRACE
     if (a.trace != nullptr && threadIdx.x == 0) {
@@ -300,12 +320,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(B <= 2 ? 3 
         a.trace[(size_t)blockIdx.x * 8 + 3] = wall_clock64();
     }
 #endif
-    // leave: the last workgroup out resets the slab tickets and advances the epoch
+    // leave: the last workgroup out advances the epoch
     __syncthreads();
     if (threadIdx.x == 0) {
         if (atomicAdd(a.ctl + CTL_EXIT, 1) == a.PD + a.NE - 1) {
-            const int ls = ctl_layer_stride(a.slabs);
-            for (int i = 0; i < ls; i += 32) store_coherent_i(a.ctl + CTL_LAYER0 + i, 0);
             store_coherent_i(a.ctl + CTL_ABORT, 0);
             store_coherent_i(a.ctl + CTL_EXIT, 0);
             store_coherent_i(a.ctl + CTL_EPOCH, (int32_t)stamp);

@@ -256,7 +256,7 @@ __device__ __forceinline__ void tail_down(const TailArgs &a, uint32_t stamp, int
             if (tb == T0) TAIL_TRACE(2, wall_clock64());
         }
         __syncthreads();
-        const int L = *s_cnt;
+        const int L = __builtin_amdgcn_readfirstlane(*s_cnt);
         // wave w takes list entries w, w + 4, ...: lane j of a round holds entry base + 4j
         for (int base = wave; base < L; base += 4 * kWave) {
             const int m = min(kWave, (L - base + 3) / 4);
@@ -418,7 +418,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __shared__ uint32_t s_words[4];
     __shared__ int s_slot[32];
     __shared__ int s_cnt;
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     TAIL_TRACE(1, wall_clock64());
     const uint32_t stamp = (uint32_t)load_coherent_i(a.ctl + CTL_EPOCH) + 1u;
     const bool up = (int)blockIdx.x < a.PU;
