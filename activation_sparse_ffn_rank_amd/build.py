@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libpi.so")
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "pi_abi.hip"), os.path.join(CSRC, "pi_fused_b.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, "pi_kernels.hpp"), os.path.join(CSRC, "pi_fused.hpp"),
+DEPENDS = SOURCES + [os.path.join(CSRC, n) for n in ("pi_kernels.hpp", "pi_fused.hpp", "pi_tail.hpp", "pi_sparse.hpp")] + [
                      os.path.join(ROOT, "include", "pi_sparse_ffn.h")]
 OBJDIR = os.path.join(ROOT, "_build")
 

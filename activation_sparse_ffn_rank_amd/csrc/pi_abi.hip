@@ -30,8 +30,8 @@ int check_batch(int32_t B) { return (B >= 1 && B <= PI_MAX_BATCH) ? PI_OK : PI_E
 int check_pred(const pi_predictor *p) {
     if (!p) return PI_ERR_NULL;
     if (!p->p1 || !p->p2 || !p->c) return PI_ERR_NULL;
-    if (p->d_model < 8 || p->d_model % 8 != 0 || p->d_ffn < 1 || p->rank < 8 || p->rank % 8 != 0 ||
-        p->rank > PI_MAX_RANK)
+    if (p->d_model < 8 || p->d_model % 8 != 0 || p->d_model > PI_MAX_D_MODEL || p->d_ffn < 1 || p->rank < 8 ||
+        p->rank % 8 != 0 || p->rank > PI_MAX_RANK)
         return PI_ERR_SHAPE;
     if (!aligned16(p->p1) || !aligned16(p->p2)) return PI_ERR_ALIGN;
     return PI_OK;
@@ -50,6 +50,7 @@ int check_ffn(const pi_ffn *f) {
     if (f->gated && f->b_up) return PI_ERR_DTYPE;                  // the gated form has no up bias
     if (f->d_ffn < 1 || f->n_slots < 0 || f->n_slots > f->d_ffn) return PI_ERR_SHAPE;
     if (!f->slot_of && f->n_slots != f->d_ffn) return PI_ERR_SHAPE;
+    if (f->d_model > PI_MAX_D_MODEL) return PI_ERR_SHAPE;
     if (f->wtype == PI_F16 && (f->d_model < 8 || f->d_model % 8 != 0)) return PI_ERR_SHAPE;
     if (f->wtype == PI_Q4_0 && (f->d_model < 256 || f->d_model % 256 != 0)) return PI_ERR_SHAPE;
     if (!aligned16(f->w_in) || !aligned16(f->w_down_t)) return PI_ERR_ALIGN;
@@ -161,14 +162,15 @@ size_t tail_ws(const pi_ffn *fn, int B) {
     return g.tword + g.ent + g.part;
 }
 
-// Scratch of pi_sparse_ffn: the persistent kernel's regions (control block first, so that the
-// status word sits at a fixed offset), or the two-kernel path's when x does not fit LDS.
+// Scratch of pi_sparse_ffn: a control block first on every path, so that the status word sits at
+// a fixed offset (the two-kernel form never waits and leaves it as it found it), then the
+// persistent kernel's regions, or the two-kernel form's (batch > 2, or x does not fit LDS).
 size_t ffn_ws(const pi_ffn *f, int B) {
     if (sparse_persistent(f, B)) {
         const SparseGeom g = sparse_geom(f, B);
         return g.ctl + g.ent + g.part;
     }
-    return ffn_legacy_ws(f, B);
+    return ctl_bytes(f->d_model) + ffn_legacy_ws(f, B);
 }
 
 FfnScratch ffn_scratch(const pi_ffn *f, int B, void *base) {
@@ -229,12 +231,13 @@ int enqueue_pred_l2_b(const pi_predictor *p, const float *z, uint8_t *mask, floa
     constexpr int R = 8;                               // predictor rows per wave
     const int groups = ceil_div(f, 4 * R);
     const uint16_t *p2 = static_cast<const uint16_t *>(p->p2), *c = static_cast<const uint16_t *>(p->c);
+    const size_t zb = (size_t)B * r * sizeof(float);       // z staged in LDS (<= 64 KB)
     if (r <= 512)
-        hipLaunchKernelGGL((k_pred_l2<B, 1, R>), dim3(groups), dim3(256), 0, st, p2, c, z, r, f, logits, mask);
+        hipLaunchKernelGGL((k_pred_l2<B, 1, R>), dim3(groups), dim3(256), zb, st, p2, c, z, r, f, logits, mask);
     else if (r <= 1024)
-        hipLaunchKernelGGL((k_pred_l2<B, 2, R>), dim3(groups), dim3(256), 0, st, p2, c, z, r, f, logits, mask);
+        hipLaunchKernelGGL((k_pred_l2<B, 2, R>), dim3(groups), dim3(256), zb, st, p2, c, z, r, f, logits, mask);
     else
-        hipLaunchKernelGGL((k_pred_l2<B, 4, R>), dim3(groups), dim3(256), 0, st, p2, c, z, r, f, logits, mask);
+        hipLaunchKernelGGL((k_pred_l2<B, 4, R>), dim3(groups), dim3(256), zb, st, p2, c, z, r, f, logits, mask);
     return launch_status();
 }
 
@@ -252,11 +255,29 @@ int enqueue_pred_l2(const pi_predictor *p, const float *z, int B, uint8_t *mask,
     return PI_ERR_BATCH;
 }
 
+template <int B, int U>
+void enqueue_pred_l1_bu(const pi_predictor *p, const uint16_t *x, float *z, hipStream_t st) {
+    constexpr int RW = pred_l1_rows(B);
+    hipLaunchKernelGGL((k_pred_l1<B, RW, U>), dim3(ceil_div(p->rank, RW)), dim3(256), 0, st,
+                       static_cast<const uint16_t *>(p->p1), x, z, p->d_model, p->rank);
+}
+
+// One pass of k_pred_l1 covers U*2048 columns: as many as d needs (loads past d touch no memory
+// but take issue slots), at most 8/RW loads per thread per row.
+template <int B>
+void enqueue_pred_l1_b(const pi_predictor *p, const uint16_t *x, float *z, hipStream_t st) {
+    constexpr int UMAX = 8 / pred_l1_rows(B);
+    const int need = ceil_div(p->d_model, 2048);
+    if (need <= 1 || UMAX == 1) enqueue_pred_l1_bu<B, 1>(p, x, z, st);
+    else if (need <= 2 || UMAX == 2) enqueue_pred_l1_bu<B, 2>(p, x, z, st);
+    else if (need <= 4 || UMAX == 4) enqueue_pred_l1_bu<B, (UMAX >= 4 ? 4 : 2)>(p, x, z, st);
+    else enqueue_pred_l1_bu<B, UMAX>(p, x, z, st);
+}
+
 template <int B>
 int enqueue_predict_b(const pi_predictor *p, const uint16_t *x, uint8_t *mask, float *logits, float *z,
                       hipStream_t st) {
-    hipLaunchKernelGGL(k_pred_l1<B>, dim3(p->rank), dim3(256), 0, st, static_cast<const uint16_t *>(p->p1), x, z,
-                       p->d_model, p->rank);
+    enqueue_pred_l1_b<B>(p, x, z, st);
     if (launch_status() != PI_OK) return PI_ERR_HIP;
     return enqueue_pred_l2_b<B>(p, z, mask, logits, st);
 }
@@ -277,11 +298,6 @@ int enqueue_predict(const pi_predictor *p, const void *x, int B, uint8_t *mask, 
     return PI_ERR_BATCH;
 }
 
-template <int B>
-void enqueue_pred_l1_b(const pi_predictor *p, const uint16_t *x, float *z, hipStream_t st) {
-    hipLaunchKernelGGL(k_pred_l1<B>, dim3(p->rank), dim3(256), 0, st, static_cast<const uint16_t *>(p->p1), x, z,
-                       p->d_model, p->rank);
-}
 
 int enqueue_pred_l1(const pi_predictor *p, const void *x, int B, float *z, hipStream_t st) {
     const uint16_t *xx = static_cast<const uint16_t *>(x);
@@ -350,7 +366,7 @@ int enqueue_sparse_b(const pi_ffn *fn, const uint16_t *x, const int32_t *idx, co
     const int d = fn->d_model, f = fn->d_ffn, ns = fn->n_slots;
     const int64_t rb = row_bytes_of(fn);
     const int xch = x_chunk(d, B);
-    const int G = std::max(1, std::min(kUpMaxGroups, ceil_div(ns, 8)));
+    const int G = std::max(1, std::min(kUpMaxGroups, ceil_div(ns, 4 * UpStep<GATED, WT>::R)));
     const int h_stride = std::max(ns, 1);
     const int slabs = down_slabs(d), C = down_chunks(d);
     hipLaunchKernelGGL((k_sparse_up<B, GATED, WT>), dim3(G), dim3(256), (size_t)B * xch * 2, st,
@@ -431,7 +447,8 @@ int enqueue_sparse(const pi_ffn *fn, const void *x, int B, const int32_t *idx, c
         return enqueue_sparse_persistent(fn, x, B, idx, counts, y, ctl ? ctl : reinterpret_cast<int32_t *>(w),
                                          w + sparse_geom(fn, B).ctl, st);
     }
-    return enqueue_sparse_legacy(fn, x, B, idx, counts, y, ffn_scratch(fn, B, ws), st);
+    return enqueue_sparse_legacy(fn, x, B, idx, counts, y,
+                                 ffn_scratch(fn, B, static_cast<char *>(ws) + ctl_bytes(fn->d_model)), st);
 }
 
 int enqueue_fused(const pi_predictor *p, const pi_ffn *fn, const void *x, int B, float *y, uint8_t *mask_out,
@@ -639,7 +656,7 @@ size_t pi_sparse_ffn_h_offset(const pi_ffn *ffn, int32_t batch, int32_t *kind) {
         return sparse_geom(ffn, batch).ctl;
     }
     *kind = 2;
-    return 0;
+    return ctl_bytes(ffn->d_model);
 }
 
 const char *pi_status_string(int status) {

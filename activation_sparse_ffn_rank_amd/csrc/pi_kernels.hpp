@@ -12,7 +12,7 @@
 // contraction to feed it at batch <= 8.
 //
 // Kernels (all stream-ordered; none needs a host sync):
-//   k_pred_l1     z = max(0, P1 x)                   one workgroup per row of P1
+//   k_pred_l1     z = max(0, P1 x)                   one workgroup per row of P1 (4 rows at batch >= 4)
 //   k_pred_l2     l = P2 z + c, mask = OR_b [l > 0]  R rows per wave, reduce-scatter sums
 //   k_compact     idx = ascending {i : mask_i, slot_of_i >= 0}, counts = {n, n_pred}
 //   k_sparse_up   h = ReLU(W_in[s] x + b) or ReLU(W_g x)(W_u x) over the listed neurons
@@ -186,16 +186,50 @@ __device__ __forceinline__ float q4_block_dot(const uint4 &codes, const uint16_t
     return fmaf(scale, s, acc);
 }
 
-// Stage columns [c0, c0+cw) of x [B][d] (fp16) into LDS xs [B][xch]; cw % 8 == 0.
+// Stage columns [c0, c0+cw) of x [B][d] (fp16) into LDS xs [B][xch]; cw % 8 == 0, B*d*2 <
+// kBufMax.  Each thread issues up to 8 loads (through a buffer resource: no branch, so the compiler
+// issues them together) before its first LDS store, so staging costs one memory round trip per 8
+// vectors a thread copies, not one per vector -- and does not drain the caller's loads in flight
+// once per vector.
 template <int B, bool Q4ORDER>
 __device__ __forceinline__ void stage_x(uint16_t *xs, const uint16_t *__restrict__ x, int d, int c0, int cw,
                                         int xch) {
-    const int vecs = cw >> 3;
-    for (int t = threadIdx.x; t < B * vecs; t += blockDim.x) {
-        const int b = t / vecs, v = t - b * vecs;
-        uint4 val = ld16(x + (size_t)b * d + c0 + v * 8);
-        if (Q4ORDER) val = pair_for_q4(val);
-        *reinterpret_cast<uint4 *>(xs + b * xch + v * 8) = val;
+    constexpr int K = 8;
+    const int vecs = cw >> 3, total = B * vecs;
+    const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x, (uint32_t)(B * d) * 2);
+    for (int t0 = threadIdx.x; t0 < total; t0 += K * blockDim.x) {
+        uint4 v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int t = t0 + k * blockDim.x, b = t / vecs, vv = t - b * vecs;
+            v[k] = bld16(rx, t < total ? (uint32_t)(b * d + c0 + vv * 8) * 2 : kOOB);
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int t = t0 + k * blockDim.x, b = t / vecs, vv = t - b * vecs;
+            if (t < total) *reinterpret_cast<uint4 *>(xs + b * xch + vv * 8) = Q4ORDER ? pair_for_q4(v[k]) : v[k];
+        }
+    }
+}
+
+// Copy n 16-byte vectors from global src to LDS dst (16-byte aligned, n*16 < kBufMax), up to 8
+// loads per thread in flight before the first store.
+__device__ __forceinline__ void stage_vec16(void *dst, const void *__restrict__ src, int n) {
+    constexpr int K = 8;
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(src, (uint32_t)n * 16);
+    uint4 *d4 = static_cast<uint4 *>(dst);
+    for (int t0 = threadIdx.x; t0 < n; t0 += K * blockDim.x) {
+        uint4 v[K];
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int t = t0 + k * blockDim.x;
+            v[k] = bld16(rs, t < n ? (uint32_t)t * 16 : kOOB);
+        }
+#pragma unroll
+        for (int k = 0; k < K; ++k) {
+            const int t = t0 + k * blockDim.x;
+            if (t < n) d4[t] = v[k];
+        }
     }
 }
 
@@ -221,63 +255,97 @@ __device__ __forceinline__ int slot_of_id(int i, const int32_t *__restrict__ slo
 
 // ------------------------------------------------------------------------------ predictor
 
-// z[b][j] = max(0, P1[j] . x_b).  One 256-thread workgroup per row j: every thread issues its
-// row loads first (they do not depend on x), then reads x through L2, then the four wave sums
-// meet in LDS.
-template <int B>
+// z[b][j] = max(0, P1[j] . x_b).  One 256-thread workgroup per RW consecutive rows: every
+// thread issues its loads of all RW rows and of the matching x vectors of every token before the
+// first product (each x vector read through L2 once serves all RW rows), then the four wave sums
+// of each (row, token) meet in LDS.  Loads go through buffer resources, so columns past d and rows
+// past r read zeros without a branch -- a guarded load would make the compiler wait for each x
+// load in turn.  RW > 1 pays at larger batches, where re-reading x for every row would cost more
+// L2 traffic than the rows themselves.  Requires B*d*2 < kBufMax.
+constexpr int pred_l1_rows(int B) { return B >= 4 ? 4 : 1; }
+
+// U: 16-byte loads per thread per row per pass (a pass covers U*2048 columns), chosen on the host
+// so that a pass is not mostly past d.
+template <int B, int RW, int U>
 __global__ __launch_bounds__(256) void k_pred_l1(const uint16_t *__restrict__ p1, const uint16_t *__restrict__ x,
                                                  float *__restrict__ z, int d, int r) {
-    constexpr int U = 8;                      // 16-byte loads per thread per pass (16384 columns)
-    __shared__ float red[4][B];
+    __shared__ float red[4][RW][B];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int j = blockIdx.x;
-    const uint16_t *row = p1 + (size_t)j * d;
-    float acc[B];
+    const int j0 = blockIdx.x * RW;
+    __amdgpu_buffer_rsrc_t rrow[RW];
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    for (int i = 0; i < RW; ++i)
+        rrow[i] = buf_rsrc(p1 + (size_t)min(j0 + i, r - 1) * d, j0 + i < r ? (uint32_t)d * 2 : 0u);
+    const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x, (uint32_t)(B * d) * 2);
+    float acc[RW][B];
+#pragma unroll
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[i][b] = 0.f;
     for (int c0 = 0; c0 < d; c0 += U * 2048) {
-        uint4 w[U];
+        uint4 w[RW][U], xv[B][U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int col = c0 + tid * 8 + u * 2048;
-            w[u] = col < d ? ld16(row + col) : zero4();
+            const uint32_t off = col < d ? (uint32_t)col * 2 : kOOB;
+#pragma unroll
+            for (int i = 0; i < RW; ++i) w[i][u] = bld16(rrow[i], off);
         }
 #pragma unroll
         for (int b = 0; b < B; ++b)
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int col = c0 + tid * 8 + u * 2048;
-                if (col < d) acc[b] = dot8(w[u], ld16(x + (size_t)b * d + col), acc[b]);
+                xv[b][u] = bld16(rx, col < d ? (uint32_t)(b * d + col) * 2 : kOOB);
             }
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int i = 0; i < RW; ++i) acc[i][b] = dot8(w[i][u], xv[b][u], acc[i][b]);
     }
 #pragma unroll
-    for (int b = 0; b < B; ++b) {
-        const float s = wave_sum(acc[b]);
-        if (lane == 0) red[wave][b] = s;
-    }
+    for (int i = 0; i < RW; ++i)
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            const float s = wave_sum(acc[i][b]);
+            if (lane == 0) red[wave][i][b] = s;
+        }
     __syncthreads();
-    if (tid < B) z[tid * r + j] = fmaxf(red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid], 0.f);
+    if (tid < RW * B) {
+        const int i = tid / B, b = tid - i * B;
+        if (j0 + i < r) z[b * r + j0 + i] = fmaxf(red[0][i][b] + red[1][i][b] + red[2][i][b] + red[3][i][b], 0.f);
+    }
 }
 
 // l[b][i] = P2[i] . z_b + c[i];  mask[i] = OR_b [l > 0].  Each wave owns R consecutive rows and
 // issues all R*NT row loads at once; lane L covers columns L*8 + 512t (t < NT, r <= 512*NT), whose
-// z values it reads once per token and reuses for all R rows; the R sums are finished with one
-// reduce-scatter, after which lane (64/R)*i owns row i.
+// z values it reads from the workgroup's LDS copy of z once per token and reuses for all R rows;
+// the R sums are finished with one reduce-scatter, after which lane (64/R)*i owns row i.
 template <int B, int NT, int R>
 __global__ __launch_bounds__(256) void k_pred_l2(const uint16_t *__restrict__ p2, const uint16_t *__restrict__ c,
                                                  const float *__restrict__ z, int r, int f,
                                                  float *__restrict__ logits, uint8_t *__restrict__ mask) {
+    extern __shared__ __align__(16) float zs[];                // z [B][r], staged once per workgroup
     const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int row0 = (blockIdx.x * 4 + wave) * R;
-    if (row0 >= f) return;
+    const int row0 = min((blockIdx.x * 4 + wave) * R, f);        // f: this wave has no rows
+    // the wave's rows (fewer at the end of P2) through a buffer resource: columns past r and rows
+    // past f read zeros without a branch, so every load is issued before the first product
+    const __amdgpu_buffer_rsrc_t rp = buf_rsrc(p2 + (size_t)row0 * r, (uint32_t)(min(R, f - row0) * r) * 2);
     uint4 w[R][NT];
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const int row = row0 + i, col = lane * 8 + t * 512;
-            w[i][t] = (row < f && col < r) ? ld16(p2 + (size_t)row * r + col) : zero4();
+            const int col = lane * 8 + t * 512;
+            w[i][t] = bld16(rp, col < r ? (uint32_t)(i * r + col) * 2 : kOOB);
         }
+    // z goes to LDS in one round trip (the rows' loads are already in flight), so no token waits
+    // on a load of its own
+    stage_vec16(zs, z, B * r / 4);
+    __syncthreads();
+    if (row0 >= f) return;
     const float c_lane = (lane < R && row0 + lane < f) ? half_to_float(c[row0 + lane]) : 0.f;
     constexpr int G = kWave / R;
     const int ri = lane / G;                                  // row owned after the reduce-scatter
@@ -289,12 +357,10 @@ __global__ __launch_bounds__(256) void k_pred_l2(const uint16_t *__restrict__ p2
         float zr[NT][8];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
-            const int col = lane * 8 + t * 512;
-            float4 za = make_float4(0.f, 0.f, 0.f, 0.f), zb = za;
-            if (col < r) {
-                za = *reinterpret_cast<const float4 *>(z + (size_t)b * r + col);
-                zb = *reinterpret_cast<const float4 *>(z + (size_t)b * r + col + 4);
-            }
+            // a lane past r reads column 0 (its weights are zero)
+            const int col = lane * 8 + t * 512 < r ? lane * 8 + t * 512 : 0;
+            const float4 za = *reinterpret_cast<const float4 *>(zs + b * r + col);
+            const float4 zb = *reinterpret_cast<const float4 *>(zs + b * r + col + 4);
             zr[t][0] = za.x; zr[t][1] = za.y; zr[t][2] = za.z; zr[t][3] = za.w;
             zr[t][4] = zb.x; zr[t][5] = zb.y; zr[t][6] = zb.z; zr[t][7] = zb.w;
         }
@@ -555,12 +621,26 @@ __device__ __forceinline__ void neuron_store(float (&ag)[B], float (&au)[B], int
     }
 }
 
-// h[b][k] for the listed neurons.  Neuron k goes to wave (k / G) % 4 of workgroup k % G in round
-// k / (4G), which spreads the listed neurons over every workgroup (and so every CU) first.
-// When B*d fp16 values fit the LDS budget (xch >= d), x is staged once per workgroup and its
-// global loads overlap the row loads of round 0; otherwise x is staged in column chunks and each
-// round walks the chunks.  Workgroup 0 also clears `zero_ptr[0..nzero)` (the down kernel's
-// slab tickets) -- the down kernel always runs after this one on the same stream.
+// Shape of one step of k_sparse_up: each lane holds U vectors of each of the wave's R neurons
+// (fp16: 8 columns per 16-byte vector; Q4_0: one 32-weight block), so a step covers STEP columns.
+template <bool GATED, int WT>
+struct UpStep {
+    static constexpr int R = 4;                                        // neurons per wave at once
+    static constexpr int U = WT == WT_F16 ? (GATED ? 2 : 4) : 2;       // vectors per lane per neuron
+    static constexpr int VC = WT == WT_F16 ? 8 : 32;                   // columns per vector
+    static constexpr int STEP = U * kWave * VC;
+};
+
+// h[b][k] for the listed neurons, R neurons per wave at a time.  In pass p, wave w of workgroup g
+// holds positions p*R*4G + j*4G + w*G + g (j < R), which spreads the listed neurons over every
+// workgroup (and so every CU) first.  x is staged in LDS in column chunks of xch columns (all of
+// it when B*d fp16 fit the LDS budget).  For each step of a chunk the loads of all R neurons' row
+// pieces go out first (for the chunk's first step, before the chunk is staged, so the two
+// latencies overlap), and every x vector read from LDS serves all R neurons.  Each neuron's row
+// is read through a buffer resource of its own: a position past n, or a neuron without a slot,
+// reads zeros and touches no memory, so no load needs a branch.  Workgroup 0 also clears
+// `zero_ptr[0..nzero)` (the down kernel's slab tickets) -- the down kernel always runs after this
+// one on the same stream.
 template <int B, bool GATED, int WT>
 __global__ __launch_bounds__(256) void k_sparse_up(const uint8_t *__restrict__ w_in, int64_t row_bytes, int d,
                                                    const uint16_t *__restrict__ b_up, const uint16_t *__restrict__ x,
@@ -568,100 +648,141 @@ __global__ __launch_bounds__(256) void k_sparse_up(const uint8_t *__restrict__ w
                                                    const int32_t *__restrict__ slot_of, int f, int n_slots,
                                                    float *__restrict__ h, int h_stride, int xch,
                                                    int32_t *__restrict__ zero_ptr, int nzero) {
+    using S = UpStep<GATED, WT>;
+    constexpr int R = S::R, U = S::U, VC = S::VC, STEP = S::STEP;
+    constexpr int RG = GATED ? R : 1;
     extern __shared__ __align__(16) uint16_t xs[];
     const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (blockIdx.x == 0)
         for (int t = threadIdx.x; t < nzero; t += blockDim.x) zero_ptr[t] = 0;
     const int G = gridDim.x;
     const int n = min(max(counts[0], 0), n_slots);
-    if ((int)blockIdx.x >= n) return;                           // no neuron for this workgroup
-    const int per_round = 4 * G;
-    const int rounds = (n + per_round - 1) / per_round;
     const int64_t in_stride = GATED ? 2 * row_bytes : row_bytes;
-
-    if (xch >= d) {
-        // x fits.  Round 0 overlaps its three latencies: the neuron's slot lookup, the first pass
-        // of its row loads, and the global loads of x for the LDS stage.
-        using P = RowPass<B, GATED, WT>;
-        {
-            const int k = __builtin_amdgcn_readfirstlane(wave * G + (int)blockIdx.x);
-            const int s = (k < n) ? slot_of_id(idx[k], slot_of, f, n_slots) : -1;
-            const uint8_t *row = w_in + (int64_t)(s >= 0 ? s : 0) * in_stride;
-            P pass;
-            if (s >= 0) pass.issue(row, row_bytes, d, 0, lane);
-            stage_x<B, WT == WT_Q4_0>(xs, x, d, 0, d, d);
-            __syncthreads();
-            if (k < n) {
-                float ag[B], au[B];
-#pragma unroll
-                for (int b = 0; b < B; ++b) ag[b] = au[b] = 0.f;
-                if (s >= 0) {
-                    pass.consume(xs, d, d, 0, lane, ag, au);
-                    for (int p0 = P::STEP; p0 < P::extent(d); p0 += P::STEP) {
-                        P nxt;
-                        nxt.issue(row, row_bytes, d, p0, lane);
-                        nxt.consume(xs, d, d, p0, lane, ag, au);
-                    }
-                }
-                neuron_store<B, GATED>(ag, au, s, k, b_up, h, h_stride, lane);
-            }
-        }
-        for (int rd = 1; rd < rounds; ++rd) {
-            const int k = __builtin_amdgcn_readfirstlane(rd * per_round + wave * G + (int)blockIdx.x);
-            if (k >= n) break;                                  // wave-uniform
-            const int s = slot_of_id(idx[k], slot_of, f, n_slots);
-            float ag[B], au[B];
-#pragma unroll
-            for (int b = 0; b < B; ++b) ag[b] = au[b] = 0.f;
-            if (s >= 0) neuron_dots<B, GATED, WT>(w_in + (int64_t)s * in_stride, row_bytes, d, xs, d, lane, ag, au);
-            neuron_store<B, GATED>(ag, au, s, k, b_up, h, h_stride, lane);
-        }
-        return;
-    }
-    // Chunked x: all waves of the workgroup walk the same chunks in lock-step.
+    const uint32_t up_off = GATED ? (uint32_t)row_bytes : 0u;           // the up row follows the gate row
     const int nchunks = (d + xch - 1) / xch;
-    for (int rd = 0; rd < rounds; ++rd) {
-        if (rd * per_round + (int)blockIdx.x >= n) break;       // workgroup-uniform
-        const int k = rd * per_round + wave * G + blockIdx.x;
-        const int s = (k < n) ? slot_of_id(idx[k], slot_of, f, n_slots) : -1;
-        float ag[B], au[B];
+
+    for (int p0 = 0; p0 < n; p0 += R * 4 * G) {
+        if (p0 + (int)blockIdx.x >= n) break;                           // workgroup-uniform
+        int kj[R], sj[R];
+        __amdgpu_buffer_rsrc_t rs[R];
 #pragma unroll
-        for (int b = 0; b < B; ++b) ag[b] = au[b] = 0.f;
+        for (int j = 0; j < R; ++j) {
+            kj[j] = p0 + j * 4 * G + wave * G + (int)blockIdx.x;
+            const int s = kj[j] < n ? slot_of_id(idx[kj[j]], slot_of, f, n_slots) : -1;
+            sj[j] = __builtin_amdgcn_readfirstlane(s);
+            rs[j] = buf_rsrc(w_in + (int64_t)(sj[j] >= 0 ? sj[j] : 0) * in_stride, sj[j] >= 0 ? (uint32_t)in_stride : 0u);
+        }
+        float au[R][B], ag[RG][B];
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                au[j][b] = 0.f;
+                if (GATED) ag[GATED ? j : 0][b] = 0.f;
+            }
         for (int ch = 0; ch < nchunks; ++ch) {
             const int c0 = ch * xch, cw = min(xch, d - c0);
-            __syncthreads();
-            stage_x<B, WT == WT_Q4_0>(xs, x, d, c0, cw, xch);
-            __syncthreads();
-            if (s >= 0) {
-                // the chunk [c0, c0+cw) of the row(s): cw is a multiple of 512, c0 of 32 (Q4_0 blocks)
-                const uint8_t *row = w_in + (int64_t)s * in_stride;
-                if (WT == WT_F16) {
-                    const int64_t off = (int64_t)c0 * 2;
-                    neuron_dots<B, GATED, WT>(row + off, row_bytes, cw, xs, xch, lane, ag, au);
-                } else {
-                    // Q4_0 chunk: blocks c0/32 .. (c0+cw)/32 of this row
-                    const uint16_t *scales = reinterpret_cast<const uint16_t *>(row + d / 2);
-                    const int qa = c0 / 32, nq = cw / 32;
-                    for (int qq = lane; qq < nq; qq += kWave) {
-                        const uint4 cwv = ld16(row + (size_t)(qa + qq) * 16);
-                        const float sc = half_to_float(scales[qa + qq]);
+            for (int st = 0; st < cw; st += STEP) {
+                uint4 wu[R][U], wg[RG][U];
+                uint16_t sc[R][WT == WT_Q4_0 ? U : 1];
 #pragma unroll
-                        for (int b = 0; b < B; ++b) au[b] = q4_block_dot(cwv, xs + b * xch + qq * 32, au[b], sc);
+                for (int u = 0; u < U; ++u) {
+                    const int lc = st + (u * kWave + lane) * VC;            // column inside the chunk
+                    const bool ok = lc < cw;
+#pragma unroll
+                    for (int j = 0; j < R; ++j) {
+                        if (WT == WT_F16) {
+                            const uint32_t off = ok ? (uint32_t)(c0 + lc) * 2 : kOOB;
+                            wu[j][u] = bld16(rs[j], off + up_off);
+                            if (GATED) wg[GATED ? j : 0][u] = bld16(rs[j], off);
+                        } else {
+                            const uint32_t q = (uint32_t)(c0 + lc) / 32;
+                            wu[j][u] = bld16(rs[j], ok ? q * 16 : kOOB);
+                            sc[j][WT == WT_Q4_0 ? u : 0] = bld2(rs[j], ok ? (uint32_t)(d / 2) + q * 2 : kOOB);
+                        }
+                    }
+                }
+                if (st == 0) {
+                    __syncthreads();                                    // the previous chunk is consumed
+                    stage_x<B, WT == WT_Q4_0>(xs, x, d, c0, cw, xch);
+                    __syncthreads();
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    // a lane past the chunk reads x at column 0 of it; its weights (and, for Q4_0,
+                    // its scales) were read as zeros, so it adds nothing, and no LDS read waits on
+                    // a branch
+                    const int lc = st + (u * kWave + lane) * VC < cw ? st + (u * kWave + lane) * VC : 0;
+                    if (WT == WT_F16) {
+#pragma unroll
+                        for (int b = 0; b < B; ++b) {
+                            const uint4 xv = *reinterpret_cast<const uint4 *>(xs + b * xch + lc);
+#pragma unroll
+                            for (int j = 0; j < R; ++j) {
+                                au[j][b] = dot8(wu[j][u], xv, au[j][b]);
+                                if (GATED) ag[GATED ? j : 0][b] = dot8(wg[GATED ? j : 0][u], xv, ag[GATED ? j : 0][b]);
+                            }
+                        }
+                    } else {
+                        float t[R][B];
+#pragma unroll
+                        for (int j = 0; j < R; ++j)
+#pragma unroll
+                            for (int b = 0; b < B; ++b) t[j][b] = 0.f;
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            uint32_t pr[R][4];
+#pragma unroll
+                            for (int j = 0; j < R; ++j) {
+                                const uint32_t cwd = g == 0 ? wu[j][u].x : g == 1 ? wu[j][u].y : g == 2 ? wu[j][u].z : wu[j][u].w;
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) pr[j][e] = q4pair(cwd, 4 * e);
+                            }
+#pragma unroll
+                            for (int b = 0; b < B; ++b) {
+                                const uint4 xv = *reinterpret_cast<const uint4 *>(xs + b * xch + lc + g * 8);
+#pragma unroll
+                                for (int j = 0; j < R; ++j) {
+                                    float s = t[j][b];
+                                    s = fdot2(pr[j][0], xv.x, s);
+                                    s = fdot2(pr[j][1], xv.y, s);
+                                    s = fdot2(pr[j][2], xv.z, s);
+                                    s = fdot2(pr[j][3], xv.w, s);
+                                    t[j][b] = s;
+                                }
+                            }
+                        }
+#pragma unroll
+                        for (int j = 0; j < R; ++j) {
+                            const float scf = half_to_float(sc[j][WT == WT_Q4_0 ? u : 0]);
+#pragma unroll
+                            for (int b = 0; b < B; ++b) au[j][b] = fmaf(scf, t[j][b], au[j][b]);
+                        }
                     }
                 }
             }
         }
-        if (k < n) neuron_store<B, GATED>(ag, au, s, k, b_up, h, h_stride, lane);
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            if (kj[j] >= n) continue;                                   // wave-uniform
+            float gj[B], uj[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                uj[b] = au[j][b];
+                gj[b] = GATED ? ag[GATED ? j : 0][b] : 0.f;
+            }
+            neuron_store<B, GATED>(gj, uj, sj[j], kj[j], b_up, h, h_stride, lane);
+        }
     }
 }
 
 // y over (512-column slab, neuron chunk) tiles.  Lane L owns columns slab*512 + 8L .. +8.  The
 // chunk's neurons are dealt round-robin to the 4 waves; a wave fetches the metadata (index, h,
 // slot) of up to 64 of its neurons at once, one lane per neuron, drops neurons whose h is zero
-// for every token (an exact zero contribution), and walks the rest 8 at a time with all 8 row
-// reads in flight.  The waves' partials meet in LDS; each chunk's partial goes to `part`, and
-// the last workgroup to finish a slab (slab ticket) sums the chunk partials in chunk order and
-// adds b_down, so y is deterministic.  Tickets must be zero on entry (k_sparse_up clears them)
+// for every token (an exact zero contribution), and walks the rest U at a time (16 fp16 or 32
+// Q4_0 rows) with all U row reads in flight.  The waves' partials meet in LDS; each chunk's
+// partial goes to `part`, and the last workgroup to finish a slab (slab ticket) sums the chunk
+// partials in chunk order and adds b_down, so y is deterministic.  Tickets must be zero on entry (k_sparse_up clears them)
 // and are left zero.
 template <int B, int WT>
 __global__ __launch_bounds__(256) void k_sparse_down(const uint8_t *__restrict__ w_dn, int64_t row_bytes, int d,
@@ -670,7 +791,7 @@ __global__ __launch_bounds__(256) void k_sparse_down(const uint8_t *__restrict__
                                                      const float *__restrict__ h, int h_stride,
                                                      float *__restrict__ part, int C, int32_t *__restrict__ tickets,
                                                      const uint16_t *__restrict__ b_down, float *__restrict__ y) {
-    constexpr int U = 8;
+    constexpr int U = WT == WT_F16 ? 16 : 32;                    // rows in flight per wave
     __shared__ float red[4][B][8][kWave];
     __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);

@@ -428,8 +428,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         uint16_t *xs = dyn;
         float *zs = reinterpret_cast<float *>(dyn + ((size_t)B * a.d + 7) / 8 * 8);
         stage_x<B, WT == WT_Q4_0>(xs, a.x, a.d, 0, a.d, a.d);
-        for (int i = threadIdx.x; i < B * a.r / 4; i += blockDim.x)
-            reinterpret_cast<float4 *>(zs)[i] = reinterpret_cast<const float4 *>(a.z)[i];
+        stage_vec16(zs, a.z, B * a.r / 4);
         __syncthreads();
         TAIL_TRACE(2, wall_clock64());
         tail_up<B, GATED, WT, NT>(a, stamp, lane, wave, xs, zs, s_words, s_slot, pt);

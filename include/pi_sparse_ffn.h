@@ -39,8 +39,8 @@
  *    (byte j: weight 2j in the low nibble, weight 2j+1 in the high nibble; weight value
  *    scale*(code-8)) followed by d/32 fp16 scales: 9d/16 bytes per row.
  *  - Alignment: p1, p2, x, w_in, w_down_t must be 16-byte aligned.  Shapes: 1 <= batch <= 8,
- *    d_model % 8 == 0 (fp16) or d_model % 256 == 0 (Q4_0), rank % 8 == 0 and rank <= 2048,
- *    d_ffn >= 1, 0 <= n_slots <= d_ffn.
+ *    d_model % 8 == 0 (fp16) or d_model % 256 == 0 (Q4_0), d_model <= 2^24, rank % 8 == 0 and
+ *    rank <= 2048, d_ffn >= 1, 0 <= n_slots <= d_ffn.
  */
 #ifndef PI_SPARSE_FFN_H
 #define PI_SPARSE_FFN_H
@@ -67,6 +67,7 @@ typedef enum { PI_F16 = 1, PI_Q4_0 = 2 } pi_wtype;
 
 #define PI_MAX_BATCH 8
 #define PI_MAX_RANK 2048
+#define PI_MAX_D_MODEL (1 << 24)  /* kernels address one token vector or row with 32-bit offsets */
 
 /* Low-rank predictor of one layer (the "adaptive predictor" of the method section; its shape
  * -- a rank-r ReLU MLP with a per-neuron offset on the logits -- is this library's reading). */
@@ -119,7 +120,9 @@ int pi_compact(const uint8_t *mask, int32_t d_ffn, const int32_t *slot_of, int32
  *  - the int32 at byte offset 384 of the workspace is a sticky status word: nonzero means a
  *    cross-workgroup wait ran out its time limit (20 ms) and the outputs of that call are invalid.
  * Every wait inside the kernel is bounded.  Other shapes and batches run two kernels (h, then the
- * rows of W_down^T) and need no zero fill. */
+ * rows of W_down^T), which never wait and need no zero fill; their workspace starts with the same
+ * control block, which they leave untouched, so a zero-filled workspace reads status 0 on every
+ * form. */
 int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx,
                   const int32_t *counts, float *y, void *ws, size_t ws_bytes, void *stream);
 

@@ -83,6 +83,8 @@ FFN_CASES = [  # (d, f, gated, wtype, B, active share)
     (768, 2049, False, F16, 3, 1.0), (512, 700, False, Q4, 1, 0.2), (1024, 1500, False, Q4, 4, 0.1),
     (2048, 999, False, Q4, 8, 0.15), (1024, 800, True, F16, 8, 0.2), (12288, 1200, False, Q4, 8, 0.1),
     (8192, 600, False, F16, 5, 0.2), (256, 64, False, F16, 1, 0.0), (7168, 513, False, F16, 4, 0.5),
+    # gated with x in column chunks; every neuron listed over several passes of the up kernel
+    (8192, 301, True, F16, 6, 0.3), (256, 12000, False, Q4, 3, 0.8),
 ]
 
 
@@ -128,6 +130,8 @@ def test_sparse_ffn(d, f, gated, wtype, B, share):
     _abi.pi_sparse_ffn(dl.ffn, to_dev(x), B, idx_d, counts, y2, ws)
     torch.cuda.synchronize()
     assert np.array_equal(y2.cpu().numpy(), yh[: B * d])
+    # every form keeps the status word at its fixed offset: 0 after two good calls
+    assert _abi.workspace_status(ws) == 0
 
 
 def test_sparse_ffn_skips_bad_index_entries():
