@@ -30,7 +30,8 @@ int check_batch(int32_t B) { return (B >= 1 && B <= PI_MAX_BATCH) ? PI_OK : PI_E
 int check_pred(const pi_predictor *p) {
     if (!p) return PI_ERR_NULL;
     if (!p->p1 || !p->p2 || !p->c) return PI_ERR_NULL;
-    if (p->d_model < 8 || p->d_model % 8 != 0 || p->d_model > PI_MAX_D_MODEL || p->d_ffn < 1 || p->rank < 8 ||
+    if (p->d_model < 8 || p->d_model % 8 != 0 || p->d_model > PI_MAX_D_MODEL || p->d_ffn < 1 ||
+        p->d_ffn > PI_MAX_D_FFN || p->rank < 8 ||
         p->rank % 8 != 0 || p->rank > PI_MAX_RANK)
         return PI_ERR_SHAPE;
     if (!aligned16(p->p1) || !aligned16(p->p2)) return PI_ERR_ALIGN;
@@ -48,7 +49,7 @@ int check_ffn(const pi_ffn *f) {
     if (f->gated != 0 && f->gated != 1) return PI_ERR_DTYPE;
     if (f->gated && f->wtype == PI_Q4_0) return PI_ERR_DTYPE;      // not a configuration of this library
     if (f->gated && f->b_up) return PI_ERR_DTYPE;                  // the gated form has no up bias
-    if (f->d_ffn < 1 || f->n_slots < 0 || f->n_slots > f->d_ffn) return PI_ERR_SHAPE;
+    if (f->d_ffn < 1 || f->d_ffn > PI_MAX_D_FFN || f->n_slots < 0 || f->n_slots > f->d_ffn) return PI_ERR_SHAPE;
     if (!f->slot_of && f->n_slots != f->d_ffn) return PI_ERR_SHAPE;
     if (f->d_model > PI_MAX_D_MODEL) return PI_ERR_SHAPE;
     if (f->wtype == PI_F16 && (f->d_model < 8 || f->d_model % 8 != 0)) return PI_ERR_SHAPE;
@@ -530,7 +531,7 @@ int pi_predict(const pi_predictor *pred, const void *x, int32_t batch, uint8_t *
 int pi_compact(const uint8_t *mask, int32_t d_ffn, const int32_t *slot_of, int32_t *idx, int32_t *counts,
                void *stream) {
     if (!mask || !idx || !counts) return PI_ERR_NULL;
-    if (d_ffn < 1) return PI_ERR_SHAPE;
+    if (d_ffn < 1 || d_ffn > PI_MAX_D_FFN) return PI_ERR_SHAPE;
     return enqueue_compact(mask, d_ffn, slot_of, idx, counts, static_cast<hipStream_t>(stream));
 }
 

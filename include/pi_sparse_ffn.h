@@ -40,7 +40,7 @@
  *    scale*(code-8)) followed by d/32 fp16 scales: 9d/16 bytes per row.
  *  - Alignment: p1, p2, x, w_in, w_down_t must be 16-byte aligned.  Shapes: 1 <= batch <= 8,
  *    d_model % 8 == 0 (fp16) or d_model % 256 == 0 (Q4_0), d_model <= 2^24, rank % 8 == 0 and
- *    rank <= 2048, d_ffn >= 1, 0 <= n_slots <= d_ffn.
+ *    rank <= 2048, 1 <= d_ffn <= 2^26, 0 <= n_slots <= d_ffn.
  */
 #ifndef PI_SPARSE_FFN_H
 #define PI_SPARSE_FFN_H
@@ -68,6 +68,7 @@ typedef enum { PI_F16 = 1, PI_Q4_0 = 2 } pi_wtype;
 #define PI_MAX_BATCH 8
 #define PI_MAX_RANK 2048
 #define PI_MAX_D_MODEL (1 << 24)  /* kernels address one token vector or row with 32-bit offsets */
+#define PI_MAX_D_FFN (1 << 26)    /* ... and the mask with 32-bit offsets */
 
 /* Low-rank predictor of one layer (the "adaptive predictor" of the method section; its shape
  * -- a rank-r ReLU MLP with a per-neuron offset on the logits -- is this library's reading). */

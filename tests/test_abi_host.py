@@ -69,6 +69,8 @@ def test_predict_rejects(L):
     assert call(ctypes.byref(pred(r=100))) == _abi.PI_ERR_SHAPE       # rank % 8
     assert call(ctypes.byref(pred(r=4096))) == _abi.PI_ERR_SHAPE      # rank > 2048
     assert call(ctypes.byref(pred(d=1020))) == _abi.PI_ERR_SHAPE
+    assert call(ctypes.byref(pred(d=(1 << 24) + 8))) == _abi.PI_ERR_SHAPE     # d_model > 2^24
+    assert call(ctypes.byref(pred(f=(1 << 26) + 1))) == _abi.PI_ERR_SHAPE     # d_ffn > 2^26
     assert call(ctypes.byref(pred(p1=U))) == _abi.PI_ERR_ALIGN
     assert call(ctypes.byref(p), x=U) == _abi.PI_ERR_ALIGN
     assert call(ctypes.byref(p), ws=0) == _abi.PI_ERR_WORKSPACE
@@ -79,6 +81,7 @@ def test_compact_rejects(L):
     assert L.pi_compact(None, 10, None, A, A, None) == _abi.PI_ERR_NULL
     assert L.pi_compact(A, 10, None, None, A, None) == _abi.PI_ERR_NULL
     assert L.pi_compact(A, 0, None, A, A, None) == _abi.PI_ERR_SHAPE
+    assert L.pi_compact(A, (1 << 26) + 1, None, A, A, None) == _abi.PI_ERR_SHAPE
 
 
 def test_sparse_ffn_rejects(L):
@@ -91,6 +94,7 @@ def test_sparse_ffn_rejects(L):
     assert call(ctypes.byref(ffn(gated=1, wtype=_abi.PI_Q4_0))) == _abi.PI_ERR_DTYPE
     assert call(ctypes.byref(ffn(gated=1, b_up=A))) == _abi.PI_ERR_DTYPE
     assert call(ctypes.byref(ffn(d=1000, wtype=_abi.PI_Q4_0))) == _abi.PI_ERR_SHAPE   # Q4_0 needs d % 256
+    assert call(ctypes.byref(ffn(d=(1 << 24) + 256))) == _abi.PI_ERR_SHAPE             # d_model > 2^24
     assert call(ctypes.byref(ffn(n_slots=100))) == _abi.PI_ERR_SHAPE                  # slot_of NULL: n_slots == f
     assert call(ctypes.byref(ffn(n_slots=5000, slot_of=A))) == _abi.PI_ERR_SHAPE      # n_slots > f
     assert call(ctypes.byref(ffn(w_dn=U))) == _abi.PI_ERR_ALIGN
