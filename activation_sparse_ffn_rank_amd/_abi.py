@@ -21,7 +21,8 @@ PI_MAX_BATCH = 8
 
 # Every function the header declares; the CPU tests check that libpi.so exports them all.
 EXPORTS = ("pi_workspace_bytes", "pi_predict", "pi_compact", "pi_sparse_ffn", "pi_ffn_layer",
-           "pi_predict_hidden", "pi_ffn_layer_from_hidden", "pi_layer_path", "pi_ffn_layer_fused", "pi_sparse_ffn_h_offset", "pi_status_string", "pi_version")
+           "pi_predict_hidden", "pi_ffn_layer_from_hidden", "pi_layer_path", "pi_ffn_layer_fused", "pi_sparse_ffn_h_offset",
+           "pi_cold_workspace_bytes", "pi_cold_ffn_host", "pi_status_string", "pi_version")
 
 
 class pi_predictor(ctypes.Structure):
@@ -73,6 +74,10 @@ def lib() -> ctypes.CDLL:
         L.pi_ffn_layer_fused.argtypes = [P(pi_predictor), P(pi_ffn), vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.pi_sparse_ffn_h_offset.restype = sz
         L.pi_sparse_ffn_h_offset.argtypes = [P(pi_ffn), i32, P(i32)]
+        L.pi_cold_workspace_bytes.restype = sz
+        L.pi_cold_workspace_bytes.argtypes = [P(pi_ffn), i32]
+        L.pi_cold_ffn_host.restype = ctypes.c_int
+        L.pi_cold_ffn_host.argtypes = [P(pi_ffn), vp, i32, vp, vp, P(i32), vp, sz, i32]
         L.pi_status_string.restype = ctypes.c_char_p
         L.pi_status_string.argtypes = [ctypes.c_int]
         L.pi_version.restype = ctypes.c_int
@@ -205,6 +210,40 @@ def sparse_ffn_h(ffn, batch: int, ws: torch.Tensor, n: int) -> tuple[torch.Tenso
     stride = max(int(ffn.n_slots), 1)
     h = ws[off: off + 4 * batch * stride].view(torch.float32).view(batch, stride)[:, :n]
     return h, torch.ones(n, dtype=torch.bool, device=ws.device)
+
+
+class HostFFN:
+    """Descriptor of FFN rows held in HOST memory (numpy arrays, kept alive here) for
+    pi_cold_ffn_host: neuron-major rows of the neurons held on the host, slot_of [d_ffn] (-1 = not
+    held here) or None (all neurons, identity)."""
+
+    def __init__(self, w_in, w_down_t, *, d_model: int, d_ffn: int, gated: bool, wtype: int, slot_of=None,
+                 b_up=None):
+        import numpy as np
+        self._keep = [np.ascontiguousarray(a) if a is not None else None for a in (w_in, w_down_t, slot_of, b_up)]
+        w_in, w_down_t, slot_of, b_up = self._keep
+        hp = lambda a: None if a is None else a.ctypes.data
+        self.ffn = pi_ffn(d_model, d_ffn, int(gated), wtype, int(w_in.shape[0]), hp(slot_of), hp(w_in),
+                          hp(w_down_t), hp(b_up), None)
+
+
+def pi_cold_workspace_bytes(host: HostFFN, batch: int) -> int:
+    return int(lib().pi_cold_workspace_bytes(ctypes.byref(host.ffn), batch))
+
+
+def pi_cold_ffn_host(host: HostFFN, x, batch: int, mask, y, ws, n_threads: int = 0) -> int:
+    """Host half of the hybrid split: y [batch][d] (numpy fp32, overwritten) = the contribution of
+    the predicted neurons held on the host; returns how many were computed.  x [batch][d] fp16
+    bits and mask [d_ffn] u8 are numpy arrays; ws a numpy byte array of pi_cold_workspace_bytes."""
+    import numpy as np
+    for a in (x, mask, y, ws):
+        assert isinstance(a, np.ndarray) and a.flags["C_CONTIGUOUS"], "host arrays must be contiguous numpy arrays"
+    assert y.dtype == np.float32 and mask.dtype == np.uint8 and x.dtype.itemsize == 2
+    n = ctypes.c_int32(0)
+    _check("pi_cold_ffn_host", lib().pi_cold_ffn_host(ctypes.byref(host.ffn), x.ctypes.data, batch, mask.ctypes.data,
+                                                       y.ctypes.data, ctypes.byref(n), ws.ctypes.data, ws.nbytes,
+                                                       n_threads))
+    return int(n.value)
 
 
 def pi_status_string(code: int) -> str:

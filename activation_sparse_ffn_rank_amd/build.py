@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libpi.so")
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "pi_abi.hip"), os.path.join(CSRC, "pi_fused_b.hip")]
-DEPENDS = SOURCES + [os.path.join(CSRC, n) for n in ("pi_kernels.hpp", "pi_fused.hpp", "pi_tail.hpp", "pi_sparse.hpp")] + [
+HOST_SOURCE = os.path.join(CSRC, "pi_cold.cpp")     # host half of the hybrid split (g++, OpenMP)
+DEPENDS = SOURCES + [HOST_SOURCE] + [os.path.join(CSRC, n) for n in ("pi_kernels.hpp", "pi_fused.hpp", "pi_tail.hpp", "pi_sparse.hpp")] + [
                      os.path.join(ROOT, "include", "pi_sparse_ffn.h")]
 OBJDIR = os.path.join(ROOT, "_build")
 
@@ -26,12 +27,23 @@ FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
 NOISE = "is not a recognized feature for this target"
 
 
+CXX = os.environ.get("CXX", "g++")
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-mavx2", "-mfma", "-mf16c", "-fopenmp"]
+HOST_OBJ = os.path.join(OBJDIR, "pi_cold.o")
+
+
 def _units():
     """(source, object, extra flags): the ABI unit plus one fused-kernel unit per batch width."""
     units = [(SOURCES[0], os.path.join(OBJDIR, "pi_abi.o"), [])]
     for b in range(1, 9):
         units.append((SOURCES[1], os.path.join(OBJDIR, f"pi_fused_b{b}.o"), [f"-DPIK_B={b}"]))
     return units
+
+
+def _gomp() -> str:
+    """libgomp of the host compiler (the OpenMP runtime torch loads too)."""
+    out = subprocess.run([CXX, "-print-file-name=libgomp.so"], capture_output=True, text=True).stdout.strip()
+    return out if os.path.isabs(out) else "-lgomp"
 
 
 def _clean(stderr: str) -> str:
@@ -44,6 +56,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     jobs = jobs or min(8, os.cpu_count() or 4)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     pending = [[HIPCC, *FLAGS, *inc, *extra, "-c", src, "-o", obj] for src, obj, extra in _units()]
+    pending.append([CXX, *HOST_FLAGS, *inc, "-c", HOST_SOURCE, "-o", HOST_OBJ])
     running = []
     while pending or running:
         while pending and len(running) < jobs:
@@ -56,9 +69,10 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         if proc.returncode != 0:
             for _, p in running:
                 p.wait()
-            raise RuntimeError(f"hipcc failed ({proc.returncode}) on {cmd[-3]}:\n{_clean(err)}")
+            raise RuntimeError(f"{cmd[0]} failed ({proc.returncode}) on {cmd[-3]}:\n{_clean(err)}")
     tmp = LIB + ".tmp"
-    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp] + [obj for _, obj, _ in _units()]
+    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp] + [obj for _, obj, _ in _units()] + [
+        HOST_OBJ, _gomp()]
     if verbose:
         print(" ".join(link), flush=True)
     res = subprocess.run(link, capture_output=True, text=True)

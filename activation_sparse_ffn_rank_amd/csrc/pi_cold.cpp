@@ -1,0 +1,223 @@
+// pi_cold.cpp -- the host half of the hybrid neuron split (PowerInfer, arXiv 2312.12456, method
+// section and abstract: hot neurons are preloaded on the GPU, the cold ones are computed on the
+// CPU, and the two partial results are combined).  The neurons that are predicted to fire but are
+// not resident on the device are computed here, on the host's cores, over the same neuron-major
+// rows the device kernels read; the caller adds the returned y to the device's y.
+//
+// For the listed neurons i (mask[i] != 0 and held here, ascending), slot s:
+//   h[b] = max(0, W_up[s] x_b + b_up[s])   or   max(0, W_gate[s] x_b) * (W_up[s] x_b)
+//   y[b] = sum over listed i of h[b] W_down^T[s]      (no b_down: the device half adds it once)
+//
+// The list is cut into kChunks fixed chunks; each chunk's partial y is summed in ascending order
+// by whichever thread takes it, and the chunk partials are added in chunk order, so y does not
+// depend on the number of threads.  fp16 rows are widened with F16C and accumulated in fp32 with
+// FMA; Q4_0 codes are decoded exactly (scale * (code - 8)).  Host code only: no HIP call.
+#include <immintrin.h>
+#include <omp.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "pi_sparse_ffn.h"
+
+namespace {
+
+constexpr int kChunks = 64;
+
+size_t align64(size_t x) { return (x + 63) / 64 * 64; }
+
+float hsum(__m256 v) {
+    __m128 s = _mm_add_ps(_mm256_castps256_ps128(v), _mm256_extractf128_ps(v, 1));
+    s = _mm_add_ps(s, _mm_movehl_ps(s, s));
+    s = _mm_add_ss(s, _mm_shuffle_ps(s, s, 1));
+    return _mm_cvtss_f32(s);
+}
+
+__m256 load_f16x8(const uint16_t *p) { return _mm256_cvtph_ps(_mm_loadu_si128(reinterpret_cast<const __m128i *>(p))); }
+
+float half_to_float(uint16_t h) { return _cvtsh_ss(h); }
+
+// dot of an fp16 row with fp32 x (d % 8 == 0)
+float dot_f16(const uint16_t *w, const float *x, int d) {
+    __m256 a0 = _mm256_setzero_ps(), a1 = a0, a2 = a0, a3 = a0;
+    int j = 0;
+    for (; j + 32 <= d; j += 32) {
+        a0 = _mm256_fmadd_ps(load_f16x8(w + j), _mm256_loadu_ps(x + j), a0);
+        a1 = _mm256_fmadd_ps(load_f16x8(w + j + 8), _mm256_loadu_ps(x + j + 8), a1);
+        a2 = _mm256_fmadd_ps(load_f16x8(w + j + 16), _mm256_loadu_ps(x + j + 16), a2);
+        a3 = _mm256_fmadd_ps(load_f16x8(w + j + 24), _mm256_loadu_ps(x + j + 24), a3);
+    }
+    for (; j < d; j += 8) a0 = _mm256_fmadd_ps(load_f16x8(w + j), _mm256_loadu_ps(x + j), a0);
+    return hsum(_mm256_add_ps(_mm256_add_ps(a0, a1), _mm256_add_ps(a2, a3)));
+}
+
+// y += h * row (fp16 row, d % 8 == 0)
+void axpy_f16(float h, const uint16_t *w, float *y, int d) {
+    const __m256 hv = _mm256_set1_ps(h);
+    for (int j = 0; j < d; j += 8) _mm256_storeu_ps(y + j, _mm256_fmadd_ps(hv, load_f16x8(w + j), _mm256_loadu_ps(y + j)));
+}
+
+// The 32 weights of Q4_0 block q of a row (d/2 code bytes, then d/32 fp16 scales), as
+// (code - 8) in four vectors of 8 consecutive weights, and the block's scale.
+void q4_block(const uint8_t *row, int d, int q, __m256 (&v)[4], float &scale) {
+    const __m128i c = _mm_loadu_si128(reinterpret_cast<const __m128i *>(row + (size_t)q * 16));
+    const __m128i lo = _mm_and_si128(c, _mm_set1_epi8(0x0F));                    // weights 2j
+    const __m128i hi = _mm_and_si128(_mm_srli_epi16(c, 4), _mm_set1_epi8(0x0F));  // weights 2j+1
+    const __m128i w0 = _mm_unpacklo_epi8(lo, hi), w1 = _mm_unpackhi_epi8(lo, hi); // weights 0..15, 16..31
+    const __m256 eight = _mm256_set1_ps(8.f);
+    v[0] = _mm256_sub_ps(_mm256_cvtepi32_ps(_mm256_cvtepu8_epi32(w0)), eight);
+    v[1] = _mm256_sub_ps(_mm256_cvtepi32_ps(_mm256_cvtepu8_epi32(_mm_srli_si128(w0, 8))), eight);
+    v[2] = _mm256_sub_ps(_mm256_cvtepi32_ps(_mm256_cvtepu8_epi32(w1)), eight);
+    v[3] = _mm256_sub_ps(_mm256_cvtepi32_ps(_mm256_cvtepu8_epi32(_mm_srli_si128(w1, 8))), eight);
+    uint16_t s;
+    memcpy(&s, row + (size_t)d / 2 + (size_t)q * 2, 2);
+    scale = half_to_float(s);
+}
+
+float dot_q4(const uint8_t *row, const float *x, int d) {
+    float acc = 0.f;
+    for (int q = 0; q < d / 32; ++q) {
+        __m256 v[4];
+        float sc;
+        q4_block(row, d, q, v, sc);
+        const float *xq = x + (size_t)q * 32;
+        __m256 s = _mm256_mul_ps(v[0], _mm256_loadu_ps(xq));
+        s = _mm256_fmadd_ps(v[1], _mm256_loadu_ps(xq + 8), s);
+        s = _mm256_fmadd_ps(v[2], _mm256_loadu_ps(xq + 16), s);
+        s = _mm256_fmadd_ps(v[3], _mm256_loadu_ps(xq + 24), s);
+        acc += sc * hsum(s);
+    }
+    return acc;
+}
+
+void axpy_q4(float h, const uint8_t *row, float *y, int d) {
+    for (int q = 0; q < d / 32; ++q) {
+        __m256 v[4];
+        float sc;
+        q4_block(row, d, q, v, sc);
+        const __m256 hs = _mm256_set1_ps(h * sc);
+        float *yq = y + (size_t)q * 32;
+        for (int k = 0; k < 4; ++k) _mm256_storeu_ps(yq + 8 * k, _mm256_fmadd_ps(hs, v[k], _mm256_loadu_ps(yq + 8 * k)));
+    }
+}
+
+int check_host_ffn(const pi_ffn *f) {
+    if (!f) return PI_ERR_NULL;
+    if (!f->w_in || !f->w_down_t) return PI_ERR_NULL;
+    if (f->wtype != PI_F16 && f->wtype != PI_Q4_0) return PI_ERR_DTYPE;
+    if (f->gated != 0 && f->gated != 1) return PI_ERR_DTYPE;
+    if (f->gated && f->wtype == PI_Q4_0) return PI_ERR_DTYPE;
+    if (f->gated && f->b_up) return PI_ERR_DTYPE;
+    if (f->b_down) return PI_ERR_DTYPE;                           // the device half adds b_down
+    if (f->d_ffn < 1 || f->d_ffn > PI_MAX_D_FFN || f->n_slots < 0 || f->n_slots > f->d_ffn) return PI_ERR_SHAPE;
+    if (!f->slot_of && f->n_slots != f->d_ffn) return PI_ERR_SHAPE;
+    if (f->d_model > PI_MAX_D_MODEL) return PI_ERR_SHAPE;
+    if (f->wtype == PI_F16 && (f->d_model < 8 || f->d_model % 8 != 0)) return PI_ERR_SHAPE;
+    if (f->wtype == PI_Q4_0 && (f->d_model < 256 || f->d_model % 256 != 0)) return PI_ERR_SHAPE;
+    return PI_OK;
+}
+
+struct ColdScratch {
+    float *xf;       // [B][d] x widened to fp32
+    float *part;     // [kChunks][B][d] chunk partials
+    int32_t *list;   // [d_ffn] listed neuron ids, ascending
+};
+
+ColdScratch cold_scratch(const pi_ffn *f, int B, void *ws) {
+    char *p = static_cast<char *>(ws);
+    const size_t bd = (size_t)B * f->d_model * sizeof(float);
+    ColdScratch s;
+    s.xf = reinterpret_cast<float *>(p);
+    s.part = reinterpret_cast<float *>(p + align64(bd));
+    s.list = reinterpret_cast<int32_t *>(p + align64(bd) + align64(kChunks * bd));
+    return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pi_cold_workspace_bytes(const pi_ffn *ffn, int32_t batch) {
+    if (check_host_ffn(ffn) != PI_OK || batch < 1 || batch > PI_MAX_BATCH) return 0;
+    const size_t bd = (size_t)batch * ffn->d_model * sizeof(float);
+    return align64(bd) + align64(kChunks * bd) + align64((size_t)ffn->d_ffn * sizeof(int32_t));
+}
+
+int pi_cold_ffn_host(const pi_ffn *ffn, const void *x, int32_t batch, const uint8_t *mask, float *y,
+                     int32_t *n_computed, void *ws, size_t ws_bytes, int32_t n_threads) {
+    int rc = check_host_ffn(ffn);
+    if (rc) return rc;
+    if (batch < 1 || batch > PI_MAX_BATCH) return PI_ERR_BATCH;
+    if (!x || !mask || !y) return PI_ERR_NULL;
+    if (n_threads < 0) return PI_ERR_SHAPE;
+    if (!ws || ws_bytes < pi_cold_workspace_bytes(ffn, batch)) return PI_ERR_WORKSPACE;
+    const int B = batch, d = ffn->d_model, f = ffn->d_ffn, ns = ffn->n_slots;
+    const bool q4 = ffn->wtype == PI_Q4_0, gated = ffn->gated != 0;
+    const size_t rb = q4 ? (size_t)d * 9 / 16 : (size_t)d * 2;
+    const size_t in_stride = gated ? 2 * rb : rb;
+    const uint8_t *w_in = static_cast<const uint8_t *>(ffn->w_in), *w_dn = static_cast<const uint8_t *>(ffn->w_down_t);
+    const uint16_t *b_up = static_cast<const uint16_t *>(ffn->b_up);
+    const ColdScratch sc = cold_scratch(ffn, B, ws);
+
+    // the listed neurons, ascending: predicted and held here
+    int n = 0;
+    for (int i = 0; i < f; ++i) {
+        if (!mask[i]) continue;
+        const int s = ffn->slot_of ? ffn->slot_of[i] : i;
+        if (s >= 0 && s < ns) sc.list[n++] = i;
+    }
+    if (n_computed) *n_computed = n;
+    const uint16_t *xh = static_cast<const uint16_t *>(x);
+    for (size_t j = 0; j < (size_t)B * d; j += 8) _mm256_storeu_ps(sc.xf + j, load_f16x8(xh + j));
+    const int nthr = n_threads > 0 ? n_threads : omp_get_max_threads();
+    const size_t bd = (size_t)B * d;
+
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthr)
+    for (int c = 0; c < kChunks; ++c) {
+        float *yc = sc.part + (size_t)c * bd;
+        memset(yc, 0, bd * sizeof(float));
+        const int k0 = (int)((int64_t)n * c / kChunks), k1 = (int)((int64_t)n * (c + 1) / kChunks);
+        for (int k = k0; k < k1; ++k) {
+            const int i = sc.list[k];
+            const int s = ffn->slot_of ? ffn->slot_of[i] : i;
+            const uint8_t *row = w_in + (size_t)s * in_stride;
+            float h[PI_MAX_BATCH];
+            bool any = false;
+            for (int b = 0; b < B; ++b) {
+                const float *xb = sc.xf + (size_t)b * d;
+                float hv;
+                if (q4) {
+                    const float u = dot_q4(row, xb, d) + (b_up ? half_to_float(b_up[s]) : 0.f);
+                    hv = u > 0.f ? u : 0.f;
+                } else if (gated) {
+                    const float g = dot_f16(reinterpret_cast<const uint16_t *>(row), xb, d);
+                    const float u = dot_f16(reinterpret_cast<const uint16_t *>(row + rb), xb, d);
+                    hv = (g > 0.f ? g : 0.f) * u;
+                } else {
+                    const float u = dot_f16(reinterpret_cast<const uint16_t *>(row), xb, d) +
+                                    (b_up ? half_to_float(b_up[s]) : 0.f);
+                    hv = u > 0.f ? u : 0.f;
+                }
+                h[b] = hv;
+                any |= hv != 0.f;
+            }
+            if (!any) continue;                                  // adds exact zeros
+            const uint8_t *dn = w_dn + (size_t)s * rb;
+            for (int b = 0; b < B; ++b) {
+                if (h[b] == 0.f) continue;
+                if (q4) axpy_q4(h[b], dn, yc + (size_t)b * d, d);
+                else axpy_f16(h[b], reinterpret_cast<const uint16_t *>(dn), yc + (size_t)b * d, d);
+            }
+        }
+    }
+    // chunk partials in chunk order
+#pragma omp parallel for schedule(static) num_threads(nthr)
+    for (size_t j = 0; j < bd; j += 8) {
+        __m256 s = _mm256_loadu_ps(sc.part + j);
+        for (int c = 1; c < kChunks; ++c) s = _mm256_add_ps(s, _mm256_loadu_ps(sc.part + (size_t)c * bd + j));
+        _mm256_storeu_ps(y + j, s);
+    }
+    return PI_OK;
+}
+
+}  // extern "C"

@@ -245,6 +245,40 @@ def main():
     roof_traffic = measured_traffic(workload_tag, roof_prefix) if L == cfg.layers else None
     roof_gbs = roof_bytes / (roof_us * 1e-6) / 1e9
     step_bytes = (pred_bytes + float(ffn_touched.mean())) * L
+    # ------------------------------------------------------------------ host half (placement stacks)
+    # With a placement, the predicted neurons that are not resident are the host's share of the
+    # hybrid split (pi_cold_ffn_host over the cold rows in host memory).  Timed here on the masks
+    # the device produced, for the first layers of the stack.
+    cold = None
+    if layers[0].slot_of is not None:
+        import synth as _s
+        n_lay = min(L, 2)
+        masks_h = masks.cpu().numpy()
+        hosts = []
+        for l in range(n_lay):
+            _, _, _, freq = _s.make_predictor(cfg, l)
+            cold_ids = np.setdiff1d(np.arange(cfg.f, dtype=np.int32), _s.hot_set(freq, cfg.n_hot()))
+            w_in_c, w_dn_c, b_up_c, _ = _s.make_ffn(cfg, l, cold_ids)
+            slot_c = np.full(cfg.f, -1, np.int32)
+            slot_c[cold_ids] = np.arange(cold_ids.size, dtype=np.int32)
+            hosts.append(_abi.HostFFN(w_in_c, w_dn_c, d_model=cfg.d, d_ffn=cfg.f, gated=cfg.gated, wtype=cfg.wtype,
+                                      slot_of=slot_c, b_up=b_up_c))
+        ws_h = np.zeros(_abi.pi_cold_workspace_bytes(hosts[0], B), np.uint8)
+        y_h = np.empty((B, cfg.d), np.float32)
+        times, counts_c = [], []
+        for i, (t, l) in enumerate(cases):
+            if l >= n_lay:
+                continue
+            x_h = np.ascontiguousarray(x_all[t, l])
+            s0 = time.perf_counter()
+            counts_c.append(_abi.pi_cold_ffn_host(hosts[l], x_h, B, masks_h[i], y_h, ws_h))
+            times.append(time.perf_counter() - s0)
+        del hosts
+        cold_us = 1e6 * float(np.median(times))
+        cold = {"host_us_per_layer": round(cold_us, 2), "neurons_per_layer": round(float(np.mean(counts_c)), 1),
+                "rows_mb_per_layer": round(float(np.mean(counts_c)) * (in_rows + 1) * rb / 1e6, 3),
+                "threads": _s.num_threads(), "calls": len(times),
+                "overlapped_layer_us_lower_bound": round(max(cold_us, elapsed_ms * 1000.0 / (K * L)), 2)}
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -323,6 +357,7 @@ def main():
             "predicted_density": round(float(n_pred.mean()) / cfg.f, 4),
             "covered_share": round(float(n_act.sum() / max(n_pred.sum(), 1)), 4),
             "down_rows_zero_h_share": round(1.0 - float(n_live.sum()) / max(float(n_act.sum()), 1.0), 4),
+            "cold_host": cold,
         },
     }
     print(json.dumps(out), flush=True)

@@ -173,6 +173,25 @@ int pi_ffn_layer_fused(const pi_predictor *pred, const pi_ffn *ffn, const void *
  * Positions k >= counts[0] hold stale values.  Returns (size_t)-1 on invalid arguments. */
 size_t pi_sparse_ffn_h_offset(const pi_ffn *ffn, int32_t batch, int32_t *kind);
 
+/* ---- host half of the hybrid split (method section and abstract: hot neurons are preloaded on
+ * the GPU, cold ones are computed on the CPU, and the partial results are combined) ----
+ *
+ * pi_cold_ffn_host computes, on the host's cores, the neurons that are predicted (mask[i] != 0)
+ * and held in host memory (ffn->slot_of[i] >= 0, or every neuron when slot_of is NULL), in
+ * ascending id order:  y[b] = sum_i h[b][i] W_down^T[slot_i],  h as in pi_sparse_ffn.  No b_down:
+ * the device half (pi_ffn_layer over the resident neurons) adds it, and the caller adds the two
+ * y's.  Every pointer is HOST memory owned by the caller (ffn's rows and slot_of too, in the
+ * layouts above; no alignment needed); x is [batch][d_model] fp16, mask [d_ffn] u8 (e.g. the
+ * device's mask_out, copied back), y [batch][d_model] fp32 (overwritten).  *n_computed (if
+ * non-NULL) receives the number of neurons computed.  ffn->b_down must be NULL (PI_ERR_DTYPE).
+ * ws is a host workspace of pi_cold_workspace_bytes(ffn, batch) bytes (no zero fill needed).
+ * n_threads = 0 uses the OpenMP default; the result does not depend on it (the neuron list is cut
+ * into 64 fixed chunks, added in chunk order).  Synchronous; returns a pi_status, and nothing is
+ * written on an error.  Needs an x86-64 host with AVX2, FMA and F16C. */
+size_t pi_cold_workspace_bytes(const pi_ffn *ffn, int32_t batch);   /* 0 on invalid arguments */
+int pi_cold_ffn_host(const pi_ffn *ffn, const void *x, int32_t batch, const uint8_t *mask, float *y,
+                     int32_t *n_computed, void *ws, size_t ws_bytes, int32_t n_threads);
+
 /* Human-readable name of a pi_status value (static storage). */
 const char *pi_status_string(int status);
 
