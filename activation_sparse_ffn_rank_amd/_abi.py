@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libpi.so")
 PI_OK, PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_DTYPE, PI_ERR_BATCH, PI_ERR_WORKSPACE, PI_ERR_ALIGN, PI_ERR_HIP = (
     0, -1, -2, -3, -4, -5, -6, -7)
 PI_F16, PI_Q4_0 = 1, 2
+PI_ACT_RELU, PI_ACT_SQUARED_RELU = 0, 1
 PI_MAX_BATCH = 8
 
 # Every function the header declares; the CPU tests check that libpi.so exports them all.
@@ -34,7 +35,7 @@ class pi_ffn(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("d_ffn", ctypes.c_int32), ("gated", ctypes.c_int32),
                 ("wtype", ctypes.c_int32), ("n_slots", ctypes.c_int32), ("slot_of", ctypes.c_void_p),
                 ("w_in", ctypes.c_void_p), ("w_down_t", ctypes.c_void_p), ("b_up", ctypes.c_void_p),
-                ("b_down", ctypes.c_void_p)]
+                ("b_down", ctypes.c_void_p), ("act", ctypes.c_int32)]
 
 
 class PiError(RuntimeError):
@@ -125,10 +126,10 @@ def make_predictor(p1: torch.Tensor, p2: torch.Tensor, c: torch.Tensor) -> pi_pr
 
 def make_ffn(w_in: torch.Tensor, w_down_t: torch.Tensor, *, d_model: int, d_ffn: int, gated: bool, wtype: int,
              slot_of: torch.Tensor | None = None, b_up: torch.Tensor | None = None,
-             b_down: torch.Tensor | None = None) -> pi_ffn:
+             b_down: torch.Tensor | None = None, act: int = PI_ACT_RELU) -> pi_ffn:
     """Descriptor of resident FFN weights (neuron-major rows, see the header)."""
     return pi_ffn(d_model, d_ffn, int(gated), wtype, int(w_in.shape[0]), _ptr(slot_of), _ptr(w_in), _ptr(w_down_t),
-                  _ptr(b_up), _ptr(b_down))
+                  _ptr(b_up), _ptr(b_down), act)
 
 
 def pi_workspace_bytes(pred: pi_predictor | None, ffn: pi_ffn | None, batch: int) -> int:
@@ -218,13 +219,13 @@ class HostFFN:
     held here) or None (all neurons, identity)."""
 
     def __init__(self, w_in, w_down_t, *, d_model: int, d_ffn: int, gated: bool, wtype: int, slot_of=None,
-                 b_up=None):
+                 b_up=None, act: int = PI_ACT_RELU):
         import numpy as np
         self._keep = [np.ascontiguousarray(a) if a is not None else None for a in (w_in, w_down_t, slot_of, b_up)]
         w_in, w_down_t, slot_of, b_up = self._keep
         hp = lambda a: None if a is None else a.ctypes.data
         self.ffn = pi_ffn(d_model, d_ffn, int(gated), wtype, int(w_in.shape[0]), hp(slot_of), hp(w_in),
-                          hp(w_down_t), hp(b_up), None)
+                          hp(w_down_t), hp(b_up), None, act)
 
 
 def pi_cold_workspace_bytes(host: HostFFN, batch: int) -> int:

@@ -49,6 +49,8 @@ int check_ffn(const pi_ffn *f) {
     if (f->gated != 0 && f->gated != 1) return PI_ERR_DTYPE;
     if (f->gated && f->wtype == PI_Q4_0) return PI_ERR_DTYPE;      // not a configuration of this library
     if (f->gated && f->b_up) return PI_ERR_DTYPE;                  // the gated form has no up bias
+    if (f->act != PI_ACT_RELU && f->act != PI_ACT_SQUARED_RELU) return PI_ERR_DTYPE;
+    if (f->gated && f->act != PI_ACT_RELU) return PI_ERR_DTYPE;     // ReGLU has its own form
     if (f->d_ffn < 1 || f->d_ffn > PI_MAX_D_FFN || f->n_slots < 0 || f->n_slots > f->d_ffn) return PI_ERR_SHAPE;
     if (!f->slot_of && f->n_slots != f->d_ffn) return PI_ERR_SHAPE;
     if (f->d_model > PI_MAX_D_MODEL) return PI_ERR_SHAPE;
@@ -324,6 +326,7 @@ int enqueue_tail(const pi_predictor *p, const pi_ffn *fn, const void *x, int B, 
     TailArgs a{};
     a.d = fn->d_model; a.f = fn->d_ffn; a.r = p->rank; a.n_slots = fn->n_slots; a.slabs = g.slabs; a.NTL = g.NTL;
     a.row_bytes = row_bytes_of(fn);
+    a.act = fn->act;
     a.p2 = static_cast<const uint16_t *>(p->p2); a.c = static_cast<const uint16_t *>(p->c); a.z = z;
     a.w_in = static_cast<const uint8_t *>(fn->w_in); a.w_dn = static_cast<const uint8_t *>(fn->w_down_t);
     a.b_up = static_cast<const uint16_t *>(fn->b_up); a.b_down = static_cast<const uint16_t *>(fn->b_down);
@@ -372,7 +375,7 @@ int enqueue_sparse_b(const pi_ffn *fn, const uint16_t *x, const int32_t *idx, co
     const int slabs = down_slabs(d), C = down_chunks(d);
     hipLaunchKernelGGL((k_sparse_up<B, GATED, WT>), dim3(G), dim3(256), (size_t)B * xch * 2, st,
                        static_cast<const uint8_t *>(fn->w_in), rb, d, static_cast<const uint16_t *>(fn->b_up), x,
-                       idx, counts, fn->slot_of, f, ns, sc.h, h_stride, xch, sc.tickets, slabs);
+                       idx, counts, fn->slot_of, f, ns, sc.h, h_stride, xch, sc.tickets, slabs, fn->act);
     hipLaunchKernelGGL((k_sparse_down<B, WT>), dim3(slabs, C), dim3(256), 0, st,
                        static_cast<const uint8_t *>(fn->w_down_t), rb, d, idx, counts, fn->slot_of, f, ns, sc.h,
                        h_stride, sc.part, C, sc.tickets, static_cast<const uint16_t *>(fn->b_down), y);
@@ -411,6 +414,7 @@ int enqueue_sparse_persistent(const pi_ffn *fn, const void *x, int B, const int3
     SparseArgs a{};
     a.d = fn->d_model; a.f = fn->d_ffn; a.n_slots = fn->n_slots; a.slabs = g.slabs;
     a.row_bytes = row_bytes_of(fn);
+    a.act = fn->act;
     a.w_in = static_cast<const uint8_t *>(fn->w_in); a.w_dn = static_cast<const uint8_t *>(fn->w_down_t);
     a.b_up = static_cast<const uint16_t *>(fn->b_up); a.b_down = static_cast<const uint16_t *>(fn->b_down);
     a.slot_of = fn->slot_of;
@@ -463,6 +467,7 @@ int enqueue_fused(const pi_predictor *p, const pi_ffn *fn, const void *x, int B,
     a.want_x = (idx_out != nullptr || counts_out != nullptr) ? 1 : 0;
     a.tasks = g.NA + g.NB + g.ND + g.NE + a.want_x;
     a.row_bytes = row_bytes_of(fn);
+    a.act = fn->act;
     a.p1 = static_cast<const uint16_t *>(p->p1); a.p2 = static_cast<const uint16_t *>(p->p2);
     a.c = static_cast<const uint16_t *>(p->c);
     a.w_in = static_cast<const uint8_t *>(fn->w_in); a.w_dn = static_cast<const uint8_t *>(fn->w_down_t);

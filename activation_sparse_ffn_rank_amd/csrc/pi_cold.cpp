@@ -5,7 +5,7 @@
 // rows the device kernels read; the caller adds the returned y to the device's y.
 //
 // For the listed neurons i (mask[i] != 0 and held here, ascending), slot s:
-//   h[b] = max(0, W_up[s] x_b + b_up[s])   or   max(0, W_gate[s] x_b) * (W_up[s] x_b)
+//   h[b] = max(0, W_up[s] x_b + b_up[s])  (squared for squared ReLU)  or  max(0, W_gate[s] x_b) * (W_up[s] x_b)
 //   y[b] = sum over listed i of h[b] W_down^T[s]      (no b_down: the device half adds it once)
 //
 // The list is cut into kChunks fixed chunks; each chunk's partial y is summed in ascending order
@@ -108,6 +108,8 @@ int check_host_ffn(const pi_ffn *f) {
     if (f->gated != 0 && f->gated != 1) return PI_ERR_DTYPE;
     if (f->gated && f->wtype == PI_Q4_0) return PI_ERR_DTYPE;
     if (f->gated && f->b_up) return PI_ERR_DTYPE;
+    if (f->act != PI_ACT_RELU && f->act != PI_ACT_SQUARED_RELU) return PI_ERR_DTYPE;
+    if (f->gated && f->act != PI_ACT_RELU) return PI_ERR_DTYPE;
     if (f->b_down) return PI_ERR_DTYPE;                           // the device half adds b_down
     if (f->d_ffn < 1 || f->d_ffn > PI_MAX_D_FFN || f->n_slots < 0 || f->n_slots > f->d_ffn) return PI_ERR_SHAPE;
     if (!f->slot_of && f->n_slots != f->d_ffn) return PI_ERR_SHAPE;
@@ -152,7 +154,7 @@ int pi_cold_ffn_host(const pi_ffn *ffn, const void *x, int32_t batch, const uint
     if (n_threads < 0) return PI_ERR_SHAPE;
     if (!ws || ws_bytes < pi_cold_workspace_bytes(ffn, batch)) return PI_ERR_WORKSPACE;
     const int B = batch, d = ffn->d_model, f = ffn->d_ffn, ns = ffn->n_slots;
-    const bool q4 = ffn->wtype == PI_Q4_0, gated = ffn->gated != 0;
+    const bool q4 = ffn->wtype == PI_Q4_0, gated = ffn->gated != 0, sq = ffn->act == PI_ACT_SQUARED_RELU;
     const size_t rb = q4 ? (size_t)d * 9 / 16 : (size_t)d * 2;
     const size_t in_stride = gated ? 2 * rb : rb;
     const uint8_t *w_in = static_cast<const uint8_t *>(ffn->w_in), *w_dn = static_cast<const uint8_t *>(ffn->w_down_t);
@@ -189,6 +191,7 @@ int pi_cold_ffn_host(const pi_ffn *ffn, const void *x, int32_t batch, const uint
                 if (q4) {
                     const float u = dot_q4(row, xb, d) + (b_up ? half_to_float(b_up[s]) : 0.f);
                     hv = u > 0.f ? u : 0.f;
+                    if (sq) hv *= hv;
                 } else if (gated) {
                     const float g = dot_f16(reinterpret_cast<const uint16_t *>(row), xb, d);
                     const float u = dot_f16(reinterpret_cast<const uint16_t *>(row + rb), xb, d);
@@ -197,6 +200,7 @@ int pi_cold_ffn_host(const pi_ffn *ffn, const void *x, int32_t batch, const uint
                     const float u = dot_f16(reinterpret_cast<const uint16_t *>(row), xb, d) +
                                     (b_up ? half_to_float(b_up[s]) : 0.f);
                     hv = u > 0.f ? u : 0.f;
+                    if (sq) hv *= hv;
                 }
                 h[b] = hv;
                 any |= hv != 0.f;

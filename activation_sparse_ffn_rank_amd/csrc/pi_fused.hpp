@@ -51,6 +51,7 @@ __host__ __device__ inline int ctl_layer_stride(int slabs) { return CTL_TICKET0 
 struct FusedArgs {
     // shapes (cap = entries per D group)
     int d, f, r, n_slots, slabs, C, TPD, NA, NB, ND, NE, tasks, P, want_x, cap;
+    int act;                                       // 1: squared ReLU (non-gated)
     int64_t row_bytes;
     // tensors
     const uint16_t *p1, *p2, *c;
@@ -363,6 +364,7 @@ __device__ void task_D(const FusedArgs &a, int g, int lane, int wave, uint32_t s
                 hv = fmaxf(gv, 0.f) * u;
             } else {
                 hv = fmaxf(u + bias, 0.f);
+                if (a.act) hv *= hv;                    // squared ReLU
             }
             if (lane == 0) store_c64(e + 1 + b, stamped_f(s >= 0 ? hv : 0.f, stamp));
         }

@@ -605,7 +605,7 @@ __device__ __forceinline__ void neuron_dots(const uint8_t *__restrict__ row, int
 // Epilogue of one neuron: finish the wave sums and apply bias + ReLU (or the ReGLU product).
 template <int B, bool GATED>
 __device__ __forceinline__ void neuron_store(float (&ag)[B], float (&au)[B], int s, int k, const uint16_t *b_up,
-                                             float *__restrict__ h, int h_stride, int lane) {
+                                             float *__restrict__ h, int h_stride, int lane, int act) {
     const float bias = (!GATED && b_up != nullptr && s >= 0) ? half_to_float(b_up[s]) : 0.f;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
@@ -616,6 +616,7 @@ __device__ __forceinline__ void neuron_store(float (&ag)[B], float (&au)[B], int
             hv = fmaxf(g, 0.f) * u;
         } else {
             hv = fmaxf(u + bias, 0.f);
+            if (act) hv *= hv;                          // squared ReLU
         }
         if (lane == 0) h[(size_t)b * h_stride + k] = (s >= 0) ? hv : 0.f;
     }
@@ -647,7 +648,7 @@ __global__ __launch_bounds__(256) void k_sparse_up(const uint8_t *__restrict__ w
                                                    const int32_t *__restrict__ idx, const int32_t *__restrict__ counts,
                                                    const int32_t *__restrict__ slot_of, int f, int n_slots,
                                                    float *__restrict__ h, int h_stride, int xch,
-                                                   int32_t *__restrict__ zero_ptr, int nzero) {
+                                                   int32_t *__restrict__ zero_ptr, int nzero, int act) {
     using S = UpStep<GATED, WT>;
     constexpr int R = S::R, U = S::U, VC = S::VC, STEP = S::STEP;
     constexpr int RG = GATED ? R : 1;
@@ -771,7 +772,7 @@ __global__ __launch_bounds__(256) void k_sparse_up(const uint8_t *__restrict__ w
                 uj[b] = au[j][b];
                 gj[b] = GATED ? ag[GATED ? j : 0][b] : 0.f;
             }
-            neuron_store<B, GATED>(gj, uj, sj[j], kj[j], b_up, h, h_stride, lane);
+            neuron_store<B, GATED>(gj, uj, sj[j], kj[j], b_up, h, h_stride, lane, act);
         }
     }
 }

@@ -46,6 +46,7 @@ __host__ __device__ inline int sparse_slabs(int d, int wt) { return (d + sparse_
 
 struct SparseArgs {
     int d, f, n_slots, slabs, C, PD, NE;
+    int act;             // 1: squared ReLU (non-gated)
     int64_t row_bytes;
     const uint8_t *w_in, *w_dn;
     const uint16_t *b_up, *b_down;
@@ -113,6 +114,7 @@ __device__ void sparse_up(const SparseArgs &a, int n, uint32_t stamp, int lane, 
                 hv = fmaxf(gv, 0.f) * u;
             } else {
                 hv = fmaxf(u + bias, 0.f);
+                if (a.act) hv *= hv;                    // squared ReLU
             }
             if (lane == 0) store_c64(e + 1 + b, stamped_f(s >= 0 ? hv : 0.f, stamp));
         }

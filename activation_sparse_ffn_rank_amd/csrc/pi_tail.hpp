@@ -41,6 +41,7 @@ constexpr int kTailSlab = kTailCPL * kWave;    // columns of a down tile
 
 struct TailArgs {
     int d, f, r, n_slots, slabs, C, PU, NE, NTL;   // NTL: number of 32-neuron tiles
+    int act;                                       // 1: squared ReLU (non-gated)
     int64_t row_bytes;
     const uint16_t *p2, *c;
     const float *z;                                // [B][r]
@@ -115,6 +116,7 @@ __device__ __forceinline__ void tail_publish(const TailArgs &a, int id, int s, f
             hv = fmaxf(gv, 0.f) * u;
         } else {
             hv = fmaxf(u + bias, 0.f);
+            if (a.act) hv *= hv;                        // squared ReLU
         }
         if (lane == 0) store_c64(e + 1 + b, stamped_f(hv, stamp));
     }

@@ -28,7 +28,7 @@ class DeviceLayer:
     """
 
     def __init__(self, *, p1, p2, c, w_in, w_down_t, d_model, d_ffn, gated, wtype, slot_of=None, b_up=None,
-                 b_down=None, device="cuda"):
+                 b_down=None, act=0, device="cuda"):
         self.d_model, self.d_ffn, self.gated, self.wtype = d_model, d_ffn, bool(gated), wtype
         self.p1, self.p2, self.c = _dev(p1, device), _dev(p2, device), _dev(c, device)
         self.w_in = _dev(np.ascontiguousarray(w_in).reshape(w_in.shape[0], -1), device)
@@ -37,7 +37,7 @@ class DeviceLayer:
         self.b_up, self.b_down = _dev(b_up, device), _dev(b_down, device)
         self.pred = _abi.make_predictor(self.p1, self.p2, self.c)
         self.ffn = _abi.make_ffn(self.w_in, self.w_down_t, d_model=d_model, d_ffn=d_ffn, gated=self.gated,
-                                 wtype=wtype, slot_of=self.slot_of, b_up=self.b_up, b_down=self.b_down)
+                                 wtype=wtype, slot_of=self.slot_of, b_up=self.b_up, b_down=self.b_down, act=act)
 
     @classmethod
     def from_host(cls, layer, device="cuda", b_down=None):
@@ -45,7 +45,7 @@ class DeviceLayer:
         cfg = layer.cfg
         return cls(p1=layer.p1, p2=layer.p2, c=layer.c, w_in=layer.w_in, w_down_t=layer.w_down_t, d_model=cfg.d,
                    d_ffn=cfg.f, gated=cfg.gated, wtype=cfg.wtype, slot_of=layer.slot_of, b_up=layer.b_up,
-                   b_down=layer.b_down if b_down is None else b_down, device=device)
+                   b_down=layer.b_down if b_down is None else b_down, act=getattr(cfg, "act", 0), device=device)
 
     @property
     def n_slots(self) -> int:

@@ -64,6 +64,9 @@ typedef enum {
 } pi_status;
 
 typedef enum { PI_F16 = 1, PI_Q4_0 = 2 } pi_wtype;
+/* Activation of a non-gated layer (README FAQ: the supported activations are ReLU, ReGLU and
+ * squared ReLU). */
+typedef enum { PI_ACT_RELU = 0, PI_ACT_SQUARED_RELU = 1 } pi_act;
 
 #define PI_MAX_BATCH 8
 #define PI_MAX_RANK 2048
@@ -90,6 +93,8 @@ typedef struct pi_ffn {
     const void *w_down_t;      /* [n_slots][row] */
     const void *b_up;          /* [n_slots] fp16, or NULL; must be NULL when gated */
     const void *b_down;        /* [d_model] fp16, or NULL */
+    int32_t act;               /* pi_act: PI_ACT_SQUARED_RELU makes h = max(0, W_up x + b_up)^2;
+                                  must be PI_ACT_RELU when gated.  A neuron is active iff h != 0. */
 } pi_ffn;
 
 /* Bytes of workspace the calls below need for this layer and batch (either descriptor may be

@@ -124,9 +124,19 @@ def compact(mask, slot_of=None):
     return idx[: counts[0]].copy(), int(counts[0]), int(counts[1])
 
 
+RELU, REGLU, SQUARED_RELU = 0, 1, 2     # FFN kinds of the C oracle (its `gated` argument)
+
+
+def _kind(gated, act) -> int:
+    """ReGLU when gated; otherwise ReLU, or squared ReLU when act == 1 (the C ABI's pi_act)."""
+    if gated and act:
+        raise ValueError("squared ReLU is a non-gated form")
+    return REGLU if gated else (SQUARED_RELU if act else RELU)
+
+
 def sparse_ffn(d, f, gated, wtype, w_in, w_down_t, x, idx, b_up=None, b_down=None, slot_of=None,
-               want_h=False):
-    """y [B][d] float64 (caller rounds to fp32); optionally h [B][n] float64."""
+               want_h=False, act=0):
+    """y [B][d] float64 (caller rounds to fp32); optionally h [B][n] float64.  act=1: squared ReLU."""
     w_in, w_down_t = np.ascontiguousarray(w_in), np.ascontiguousarray(w_down_t)
     x = _c(np.atleast_2d(x), np.uint16)
     idx = _c(idx, np.int32)
@@ -135,21 +145,21 @@ def sparse_ffn(d, f, gated, wtype, w_in, w_down_t, x, idx, b_up=None, b_down=Non
     n_slots = w_in.shape[0]
     y = np.empty((B, d), dtype=np.float64)
     h = np.empty((B, max(n, 1)), dtype=np.float64) if want_h else None
-    rc = lib().pio_sparse_ffn(d, f, int(gated), wtype, n_slots, _p(_c(slot_of, np.int32)), _p(w_in), _p(w_down_t),
+    rc = lib().pio_sparse_ffn(d, f, _kind(gated, act), wtype, n_slots, _p(_c(slot_of, np.int32)), _p(w_in), _p(w_down_t),
                               _p(_c(b_up, np.uint16)), _p(_c(b_down, np.uint16)), _p(x), B,
                               _p(idx) if n else None, n, _p(h), _p(y))
     _check(rc, "sparse_ffn")
     return (y, h[:, :n]) if want_h else y
 
 
-def dense_ffn(d, f, gated, wtype, w_in, w_down_t, x, b_up=None, b_down=None):
+def dense_ffn(d, f, gated, wtype, w_in, w_down_t, x, b_up=None, b_down=None, act=0):
     """Dense FFN over all f neurons: (y [B][d] f64, true mask [B][f] u8)."""
     w_in, w_down_t = np.ascontiguousarray(w_in), np.ascontiguousarray(w_down_t)
     x = _c(np.atleast_2d(x), np.uint16)
     B = x.shape[0]
     y = np.empty((B, d), dtype=np.float64)
     tm = np.empty((B, f), dtype=np.uint8)
-    rc = lib().pio_dense_ffn(d, f, int(gated), wtype, _p(w_in), _p(w_down_t), _p(_c(b_up, np.uint16)),
+    rc = lib().pio_dense_ffn(d, f, _kind(gated, act), wtype, _p(w_in), _p(w_down_t), _p(_c(b_up, np.uint16)),
                              _p(_c(b_down, np.uint16)), _p(x), B, _p(tm), _p(y))
     _check(rc, "dense_ffn")
     return y, tm
@@ -167,7 +177,8 @@ def ffn_layer(layer, x, want_logits=True, b_down=None):
     counts = np.zeros(2, dtype=np.int32)
     y = np.empty((B, d), dtype=np.float64)
     bd = layer.b_down if b_down is None else b_down
-    rc = lib().pio_ffn_layer(d, f, r, _p(layer.p1), _p(layer.p2), _p(layer.c), int(cfg.gated), cfg.wtype,
+    rc = lib().pio_ffn_layer(d, f, r, _p(layer.p1), _p(layer.p2), _p(layer.c), _kind(cfg.gated, getattr(cfg, "act", 0)),
+                             cfg.wtype,
                              layer.n_slots, _p(_c(layer.slot_of, np.int32)), _p(layer.w_in), _p(layer.w_down_t),
                              _p(_c(layer.b_up, np.uint16)), _p(_c(bd, np.uint16)), _p(x), B, _p(logits),
                              _p(mask), _p(idx), _p(counts), _p(y))

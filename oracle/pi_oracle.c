@@ -164,10 +164,11 @@ int pio_sparse_ffn(int64_t d, int64_t f, int gated, int wtype, int64_t n_slots,
     if (n > 0 && !idx) return -1;
     if (wtype != PIO_F16 && wtype != PIO_Q4_0) return -3;
     if (wtype == PIO_Q4_0 && d % 32 != 0) return -3;
-    if (gated && b_up) return -3;                    /* the gated form has no up bias */
+    if (gated < 0 || gated > PIO_SQUARED_RELU) return -3;
+    if (gated == PIO_REGLU && b_up) return -3;       /* the gated form has no up bias */
     pio_init();
     const int64_t rb = pio_row_bytes(wtype, d);
-    const int64_t in_rows = gated ? 2 : 1;
+    const int64_t in_rows = gated == PIO_REGLU ? 2 : 1;
     const uint8_t *win = (const uint8_t *)w_in;
     const uint8_t *wdn = (const uint8_t *)w_down_t;
 
@@ -188,7 +189,7 @@ int pio_sparse_ffn(int64_t d, int64_t f, int gated, int wtype, int64_t n_slots,
         for (int64_t b = 0; b < B; ++b) {
             const uint16_t *xb = x + b * d;
             double hv;
-            if (gated) {
+            if (gated == PIO_REGLU) {
                 double g = pio_dot_row(row, wtype, d, xb);        /* gate row first */
                 double u = pio_dot_row(row + rb, wtype, d, xb);   /* then the up row */
                 hv = (g > 0.0 ? g : 0.0) * u;
@@ -196,6 +197,7 @@ int pio_sparse_ffn(int64_t d, int64_t f, int gated, int wtype, int64_t n_slots,
                 double u = pio_dot_row(row, wtype, d, xb);
                 if (b_up) u += g_half[b_up[slot[k]]];
                 hv = u > 0.0 ? u : 0.0;
+                if (gated == PIO_SQUARED_RELU) hv = hv * hv;     /* squared ReLU: ReLU(u)^2 */
             }
             h[b * n + k] = hv;
         }

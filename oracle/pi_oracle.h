@@ -17,6 +17,9 @@ extern "C" {
 #endif
 
 enum { PIO_F16 = 1, PIO_Q4_0 = 2 };
+/* FFN kinds (the `gated` argument below): ReLU(W_up x + b_up), ReGLU ReLU(W_gate x) (W_up x), and
+ * squared ReLU ReLU(W_up x + b_up)^2 (README FAQ: the activations the method supports). */
+enum { PIO_RELU = 0, PIO_REGLU = 1, PIO_SQUARED_RELU = 2 };
 
 /* IEEE 754 binary16 bit pattern -> double (exact). */
 double pio_half(uint16_t h);
@@ -37,8 +40,9 @@ int pio_predict(int64_t d, int64_t f, int64_t r, const uint16_t *p1, const uint1
 int pio_compact(const uint8_t *mask, int64_t f, const int32_t *slot_of, int32_t *idx,
                 int32_t *counts);
 
-/* Sparse FFN over neuron ids idx[0..n).  Weight rows are neuron-major and indexed by slot
- * (slot_of[i], or i when slot_of is NULL): w_in row = gate row then up row when gated.
+/* Sparse FFN over neuron ids idx[0..n).  gated: the FFN kind (PIO_RELU, PIO_REGLU or
+ * PIO_SQUARED_RELU).  Weight rows are neuron-major and indexed by slot (slot_of[i], or i when
+ * slot_of is NULL): w_in row = gate row then up row for ReGLU.
  * h_out [B][n] (nullable) receives the activations; y [B][d] receives the output. */
 int pio_sparse_ffn(int64_t d, int64_t f, int gated, int wtype, int64_t n_slots,
                    const int32_t *slot_of, const void *w_in, const void *w_down_t,

@@ -96,6 +96,7 @@ class Config:
     batches: tuple
     hot_frac: float | None = None     # placement: keep this share of neurons resident
     seed: int = 0
+    act: int = 0                      # 1: squared ReLU (non-gated)
 
     def row_bytes(self) -> int:
         return self.d * 2 if self.wtype == F16 else self.d * 9 // 16
@@ -117,8 +118,8 @@ TOP_FRAC, TOP_SHARE, P_CAP = 0.26, 0.80, 0.99
 
 
 def custom_config(d, f, r, *, gated=False, wtype=F16, bias_up=True, density=0.1, hot_frac=None,
-                  seed=1234, layers=1, tokens=4, name="custom") -> Config:
-    return Config(0, name, layers, d, f, r, gated, wtype, bias_up, density, tokens, (1,), hot_frac, seed)
+                  seed=1234, layers=1, tokens=4, name="custom", act=0) -> Config:
+    return Config(0, name, layers, d, f, r, gated, wtype, bias_up, density, tokens, (1,), hot_frac, seed, act)
 
 
 # ----------------------------------------------------------------------------- primitives

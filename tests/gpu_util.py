@@ -117,7 +117,7 @@ def check_layer_against_oracle(layer, dl: DeviceLayer, x: np.ndarray, what: str,
         idx_ref, n_ref, npred_ref = oracle.compact(got["mask"], layer.slot_of)
         assert np.array_equal(got["idx"], idx_ref) and got["n"] == n_ref and got["n_pred"] == npred_ref, tag
         y_ref = oracle.sparse_ffn(cfg.d, cfg.f, cfg.gated, cfg.wtype, layer.w_in, layer.w_down_t, x, idx_ref,
-                                  b_up=layer.b_up, b_down=bd, slot_of=layer.slot_of)
+                                  b_up=layer.b_up, b_down=bd, slot_of=layer.slot_of, act=cfg.act)
         w = check_y(got["y"], y_ref, cfg.wtype, tag)
         w.update(n=got["n"], n_pred=got["n_pred"], dont_care=dont_care)
         if worst is None:

@@ -39,8 +39,9 @@ def pred(d=1024, f=4096, r=128, p1=A, p2=A, c=A):
     return _abi.pi_predictor(d, f, r, p1, p2, c)
 
 
-def ffn(d=1024, f=4096, gated=0, wtype=_abi.PI_F16, n_slots=None, slot_of=None, w_in=A, w_dn=A, b_up=None, b_down=None):
-    return _abi.pi_ffn(d, f, gated, wtype, f if n_slots is None else n_slots, slot_of, w_in, w_dn, b_up, b_down)
+def ffn(d=1024, f=4096, gated=0, wtype=_abi.PI_F16, n_slots=None, slot_of=None, w_in=A, w_dn=A, b_up=None, b_down=None,
+        act=0):
+    return _abi.pi_ffn(d, f, gated, wtype, f if n_slots is None else n_slots, slot_of, w_in, w_dn, b_up, b_down, act)
 
 
 def ws_for(L, p, f, B):
@@ -93,6 +94,8 @@ def test_sparse_ffn_rejects(L):
     assert call(ctypes.byref(ffn(wtype=3))) == _abi.PI_ERR_DTYPE
     assert call(ctypes.byref(ffn(gated=1, wtype=_abi.PI_Q4_0))) == _abi.PI_ERR_DTYPE
     assert call(ctypes.byref(ffn(gated=1, b_up=A))) == _abi.PI_ERR_DTYPE
+    assert call(ctypes.byref(ffn(act=2))) == _abi.PI_ERR_DTYPE                         # no such activation
+    assert call(ctypes.byref(ffn(gated=1, act=_abi.PI_ACT_SQUARED_RELU))) == _abi.PI_ERR_DTYPE
     assert call(ctypes.byref(ffn(d=1000, wtype=_abi.PI_Q4_0))) == _abi.PI_ERR_SHAPE   # Q4_0 needs d % 256
     assert call(ctypes.byref(ffn(d=(1 << 24) + 256))) == _abi.PI_ERR_SHAPE             # d_model > 2^24
     assert call(ctypes.byref(ffn(n_slots=100))) == _abi.PI_ERR_SHAPE                  # slot_of NULL: n_slots == f

@@ -82,6 +82,24 @@ def test_cold_matches_oracle(d, f, gated, wtype, B, pshare, hshare):
     _check(y, y_ref, wtype)
 
 
+@pytest.mark.parametrize("wtype,B", [(F16, 1), (Q4, 3)])
+def test_cold_squared_relu(wtype, B):
+    cfg = synth.custom_config(512, 900, 8, gated=False, wtype=wtype, bias_up=True, seed=21, act=1)
+    w_in, w_dn, b_up, _ = synth.make_ffn(cfg, 0, None, bias_scale=1.0)
+    rng = np.random.default_rng(B)
+    mask = (rng.random(cfg.f) < 0.3).astype(np.uint8)
+    hot, cold = _split(cfg.f, rng, 0.26)
+    slot_of = np.full(cfg.f, -1, np.int32)
+    slot_of[cold] = np.arange(cold.size, dtype=np.int32)
+    host = _abi.HostFFN(w_in[cold], w_dn[cold], d_model=cfg.d, d_ffn=cfg.f, gated=False, wtype=wtype,
+                        slot_of=slot_of, b_up=b_up[cold], act=1)
+    x = synth.normal_f16(cfg.seed, 0, synth.T_X, B, cfg.d, 1.0)
+    y, n = _run(host, x, mask)
+    idx = cold[mask[cold] != 0]
+    assert n == idx.size
+    _check(y, oracle.sparse_ffn(cfg.d, cfg.f, False, wtype, w_in, w_dn, x, idx, b_up=b_up, act=1), wtype)
+
+
 def test_hot_plus_cold_is_the_whole_predicted_set():
     """The merge: y(M and H) with b_down + y(M minus H) = y(M) with b_down (the oracle's additivity)."""
     cfg, w_in, w_dn, b_up = _layer(1024, 3000, False, F16, seed=11)
@@ -144,3 +162,7 @@ def test_cold_rejects():
     bad = _abi.pi_ffn(500, 600, 0, F16, 600, None, w_in.ctypes.data, w_dn.ctypes.data, None, None)
     assert call(f=ctypes.byref(bad)) == _abi.PI_ERR_SHAPE              # d_model % 8
     assert L.pi_cold_workspace_bytes(ctypes.byref(bad), 1) == 0
+    bad = _abi.pi_ffn(512, 600, 0, F16, 600, None, w_in.ctypes.data, w_dn.ctypes.data, None, None, 2)
+    assert call(f=ctypes.byref(bad)) == _abi.PI_ERR_DTYPE              # no such activation
+    bad = _abi.pi_ffn(512, 600, 1, F16, 600, None, w_in.ctypes.data, w_dn.ctypes.data, None, None, 1)
+    assert call(f=ctypes.byref(bad)) == _abi.PI_ERR_DTYPE              # squared ReLU is non-gated

@@ -134,6 +134,28 @@ def test_sparse_ffn(d, f, gated, wtype, B, share):
     assert _abi.workspace_status(ws) == 0
 
 
+@pytest.mark.parametrize("d,f,wtype,B", [(1024, 3000, F16, 1), (1024, 3000, F16, 2), (2048, 999, Q4, 1),
+                                         (768, 2049, F16, 5), (12288, 700, Q4, 8)])
+def test_sparse_ffn_squared_relu(d, f, wtype, B):
+    """Squared ReLU h = max(0, W_up x + b_up)^2 through the persistent form (batch <= 2) and the
+    two-kernel form (batch > 2, or x in LDS column chunks)."""
+    announce(f"sparse_ffn squared ReLU d={d} f={f} wtype={wtype} B={B}")
+    cfg, w_in, w_dn, b_up, b_down = _ffn_layer(d, f, False, wtype, seed=d + 5 * f)
+    rng = np.random.default_rng(d + f + B)
+    idx = np.sort(rng.choice(f, f // 4, replace=False)).astype(np.int32)
+    x = synth.normal_f16(cfg.seed, 0, synth.T_X, B, d, 1.0)
+    y_ref = oracle.sparse_ffn(d, f, False, wtype, w_in, w_dn, x, idx, b_up=b_up, b_down=b_down, act=1)
+    dl = DeviceLayer(p1=np.zeros((8, d), np.uint16), p2=np.zeros((f, 8), np.uint16), c=np.zeros(f, np.uint16),
+                     w_in=w_in, w_down_t=w_dn, d_model=d, d_ffn=f, gated=False, wtype=wtype, b_up=b_up,
+                     b_down=b_down, act=1)
+    y = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(_abi.pi_workspace_bytes(None, dl.ffn, B), dtype=torch.uint8, device="cuda")
+    _abi.pi_sparse_ffn(dl.ffn, to_dev(x), B, to_dev(idx), to_dev(np.array([idx.size, idx.size], np.int32)), y, ws)
+    torch.cuda.synchronize()
+    assert _abi.workspace_status(ws) == 0
+    check_y(y.cpu().numpy(), y_ref, wtype, "sparse_ffn squared ReLU")
+
+
 def test_sparse_ffn_skips_bad_index_entries():
     """Out-of-range ids or non-resident slots are skipped, and counts beyond n_slots are clamped."""
     d, f = 512, 300
@@ -158,10 +180,14 @@ LAYER_CASES = [  # small layers spanning several tiles, ragged f, placement, all
     dict(d=2048, f=5503, r=256, gated=True, wtype=F16, bias_up=False, density=0.12),
     dict(d=1536, f=6001, r=512, gated=False, wtype=F16, bias_up=True, density=0.06, hot_frac=0.26),
     dict(d=2048, f=4100, r=1024, gated=False, wtype=Q4, bias_up=True, density=0.05),
+    # squared ReLU: the tail kernel (small f) and separate kernels (large f), fp16 and Q4_0
+    dict(d=1024, f=4096, r=128, gated=False, wtype=F16, bias_up=True, density=0.1, act=1),
+    dict(d=1024, f=40000, r=128, gated=False, wtype=Q4, bias_up=True, density=0.05, act=1),
 ]
 
 
-@pytest.mark.parametrize("case", LAYER_CASES, ids=["relu", "reglu", "placement", "q4_0"])
+@pytest.mark.parametrize("case", LAYER_CASES, ids=["relu", "reglu", "placement", "q4_0", "squared_relu",
+                                                  "squared_relu_q4_0_large_f"])
 @pytest.mark.parametrize("B", [1, 4, 8])
 def test_ffn_layer(case, B):
     announce(f"ffn_layer {case} B={B}")

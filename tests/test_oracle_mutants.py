@@ -38,6 +38,9 @@ MUTANTS = {
     "P1 transposed": ("g_half[p1[j * d + k]]", "g_half[p1[k * r + j]]"),
     "P2 transposed": ("g_half[p2[i * r + j]]", "g_half[p2[j * f + i]]"),
     "output ReLU dropped": ("hv = u > 0.0 ? u : 0.0;", "hv = u;"),
+    "squared ReLU not squared": ("if (gated == PIO_SQUARED_RELU) hv = hv * hv;", ";"),
+    "squared ReLU squares before the ReLU": ("hv = u > 0.0 ? u : 0.0;\n                if (gated == PIO_SQUARED_RELU) hv = hv * hv;",
+                                             "hv = u > 0.0 ? u : 0.0;\n                if (gated == PIO_SQUARED_RELU) hv = u * u;"),
 }
 
 
@@ -65,6 +68,8 @@ def _pin_suite(golden):
         lambda: pins.test_brute_force_all_masks_tiny(True),
         lambda: pins.test_dense_equals_sparse_invariants(pins.LAYER_CASES[0]),
         lambda: pins.test_dense_equals_sparse_invariants(pins.LAYER_CASES[2]),
+        lambda: pins.test_dense_equals_sparse_invariants(pins.LAYER_CASES[3]),
+        lambda: pins.test_squared_relu_by_hand(),
         lambda: pins.test_placement_slots_are_an_indirection(),
         lambda: pins.test_empty_active_set_gives_down_bias(),
     ]

@@ -287,6 +287,8 @@ def _numpy_dense(layer, x):
         if layer.b_up is not None:
             pre = pre + layer.b_up.view(np.float16).astype(np.float64)
         H = np.maximum(pre, 0.0)
+        if getattr(cfg, "act", 0):
+            H = H * H                                   # squared ReLU
     Y = H @ _np_decode(layer.w_down_t, cfg.wtype, d)
     if layer.b_down is not None:
         Y = Y + layer.b_down.view(np.float16).astype(np.float64)
@@ -297,10 +299,12 @@ LAYER_CASES = [
     dict(d=256, f=700, r=32, gated=False, wtype=F16, bias_up=True),
     dict(d=256, f=513, r=32, gated=True, wtype=F16, bias_up=False),
     dict(d=320, f=300, r=16, gated=False, wtype=Q4, bias_up=True),
+    dict(d=256, f=400, r=32, gated=False, wtype=F16, bias_up=True, act=1),
+    dict(d=256, f=300, r=16, gated=False, wtype=Q4, bias_up=True, act=1),
 ]
 
 
-@pytest.mark.parametrize("case", LAYER_CASES, ids=["relu", "reglu", "q4_0"])
+@pytest.mark.parametrize("case", LAYER_CASES, ids=["relu", "reglu", "q4_0", "squared_relu", "squared_relu_q4_0"])
 def test_dense_equals_sparse_invariants(case):
     """I1 (all neurons = dense MLP), I2 (true mask = dense, bit-exact), I3 (NaN rows outside
     the set change nothing), I4 (disjoint sets add), I8 (batch rows equal single tokens)."""
@@ -310,7 +314,7 @@ def test_dense_equals_sparse_invariants(case):
     x = np.concatenate([synth.make_x(cfg, 0, t, 1) for t in range(3)])
     yref, H = _numpy_dense(layer, x)
     args = (d, f, cfg.gated, cfg.wtype, layer.w_in, layer.w_down_t)
-    kw = dict(b_up=layer.b_up, b_down=layer.b_down)
+    kw = dict(b_up=layer.b_up, b_down=layer.b_down, act=cfg.act)
     # I1
     y_all = oracle.sparse_ffn(*args, x, np.arange(f), **kw)
     np.testing.assert_allclose(y_all, yref, rtol=1e-10, atol=1e-10)
@@ -399,3 +403,17 @@ def test_rejects_bad_arguments():
     with pytest.raises(ValueError):
         oracle.sparse_ffn(32, 10, False, F16, np.zeros((4, 32), np.uint16), np.zeros((4, 32), np.uint16),
                           np.zeros((1, 32), np.uint16), np.array([5], np.int32))   # slot 5 >= n_slots
+
+
+def test_squared_relu_by_hand():
+    """Squared ReLU (README FAQ lists it beside ReLU and ReGLU), one neuron worked by hand, every
+    value exact in fp16: x = (1, 2); W_up = (3, -1), b_up = 0.5 -> u = 1.5, h = 2.25;
+    W_down^T = (2, -4) -> y = (4.5, -9).  With W_up = (-3, 1): u = -0.5 -> h = 0 -> y = 0
+    (the square comes after the ReLU)."""
+    h16 = lambda *v: np.array(v, np.float16).view(np.uint16)
+    x = h16(1, 2).reshape(1, 2)
+    for w_up, y_exp, h_exp in (((3, -1), (4.5, -9.0), 2.25), ((-3, 1), (0.0, 0.0), 0.0)):
+        y, h = oracle.sparse_ffn(8, 1, False, F16, np.pad(h16(*w_up), (0, 6)).reshape(1, 8),
+                                 np.pad(h16(2, -4), (0, 6)).reshape(1, 8), np.pad(x, ((0, 0), (0, 6))),
+                                 np.array([0], np.int32), b_up=h16(0.5), want_h=True, act=1)
+        assert h[0, 0] == h_exp and np.array_equal(y[0, :2], np.array(y_exp)) and np.all(y[0, 2:] == 0)
