@@ -23,7 +23,7 @@ PI_MAX_BATCH = 8
 # Every function the header declares; the CPU tests check that libpi.so exports them all.
 EXPORTS = ("pi_workspace_bytes", "pi_predict", "pi_compact", "pi_sparse_ffn", "pi_ffn_layer",
            "pi_predict_hidden", "pi_ffn_layer_from_hidden", "pi_layer_path", "pi_ffn_layer_fused", "pi_sparse_ffn_h_offset",
-           "pi_cold_workspace_bytes", "pi_cold_ffn_host", "pi_status_string", "pi_version")
+           "pi_cold_workspace_bytes", "pi_cold_ffn_host", "pi_place", "pi_status_string", "pi_version")
 
 
 class pi_predictor(ctypes.Structure):
@@ -79,6 +79,9 @@ def lib() -> ctypes.CDLL:
         L.pi_cold_workspace_bytes.argtypes = [P(pi_ffn), i32]
         L.pi_cold_ffn_host.restype = ctypes.c_int
         L.pi_cold_ffn_host.argtypes = [P(pi_ffn), vp, i32, vp, vp, P(i32), vp, sz, i32]
+        L.pi_place.restype = ctypes.c_int
+        L.pi_place.argtypes = [i32, vp, vp, vp, ctypes.c_int64, ctypes.c_double, ctypes.c_double, vp, vp,
+                               P(ctypes.c_double)]
         L.pi_status_string.restype = ctypes.c_char_p
         L.pi_status_string.argtypes = [ctypes.c_int]
         L.pi_version.restype = ctypes.c_int
@@ -245,6 +248,22 @@ def pi_cold_ffn_host(host: HostFFN, x, batch: int, mask, y, ws, n_threads: int =
                                                        y.ctypes.data, ctypes.byref(n), ws.ctypes.data, ws.nbytes,
                                                        n_threads))
     return int(n.value)
+
+
+def pi_place(d_ffn, neuron_bytes, freq, budget_bytes: int, gpu_bytes_per_s: float, host_bytes_per_s: float):
+    """Offline placement (host): returns (slot_of list of int32 arrays per layer, n_placed array,
+    expected seconds per token).  d_ffn, neuron_bytes: per layer; freq: per-layer float arrays."""
+    import numpy as np
+    d = np.ascontiguousarray(d_ffn, dtype=np.int32)
+    nb = np.ascontiguousarray(neuron_bytes, dtype=np.int64)
+    fr = np.ascontiguousarray(np.concatenate([np.asarray(p, np.float32) for p in freq]), dtype=np.float32)
+    so = np.empty(int(d.sum()), np.int32)
+    npl = np.empty(d.size, np.int32)
+    t = ctypes.c_double(0.0)
+    _check("pi_place", lib().pi_place(d.size, d.ctypes.data, nb.ctypes.data, fr.ctypes.data, int(budget_bytes),
+                                      float(gpu_bytes_per_s), float(host_bytes_per_s), so.ctypes.data,
+                                      npl.ctypes.data, ctypes.byref(t)))
+    return np.split(so, np.cumsum(d)[:-1]), npl, float(t.value)
 
 
 def pi_status_string(code: int) -> str:

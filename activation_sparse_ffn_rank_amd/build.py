@@ -15,8 +15,9 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libpi.so")
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "pi_abi.hip"), os.path.join(CSRC, "pi_fused_b.hip")]
-HOST_SOURCE = os.path.join(CSRC, "pi_cold.cpp")     # host half of the hybrid split (g++, OpenMP)
-DEPENDS = SOURCES + [HOST_SOURCE] + [os.path.join(CSRC, n) for n in ("pi_kernels.hpp", "pi_fused.hpp", "pi_tail.hpp", "pi_sparse.hpp")] + [
+HOST_SOURCES = [os.path.join(CSRC, "pi_cold.cpp"),   # host half of the hybrid split (g++, OpenMP)
+                os.path.join(CSRC, "pi_place.cpp")]  # offline placement under a memory budget
+DEPENDS = SOURCES + HOST_SOURCES + [os.path.join(CSRC, n) for n in ("pi_kernels.hpp", "pi_fused.hpp", "pi_tail.hpp", "pi_sparse.hpp")] + [
                      os.path.join(ROOT, "include", "pi_sparse_ffn.h")]
 OBJDIR = os.path.join(ROOT, "_build")
 
@@ -29,7 +30,7 @@ NOISE = "is not a recognized feature for this target"
 
 CXX = os.environ.get("CXX", "g++")
 HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-mavx2", "-mfma", "-mf16c", "-fopenmp"]
-HOST_OBJ = os.path.join(OBJDIR, "pi_cold.o")
+HOST_OBJS = [os.path.join(OBJDIR, os.path.basename(p).replace(".cpp", ".o")) for p in HOST_SOURCES]
 
 
 def _units():
@@ -56,7 +57,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     jobs = jobs or min(8, os.cpu_count() or 4)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
     pending = [[HIPCC, *FLAGS, *inc, *extra, "-c", src, "-o", obj] for src, obj, extra in _units()]
-    pending.append([CXX, *HOST_FLAGS, *inc, "-c", HOST_SOURCE, "-o", HOST_OBJ])
+    for src, obj in zip(HOST_SOURCES, HOST_OBJS):
+        pending.append([CXX, *HOST_FLAGS, *inc, "-c", src, "-o", obj])
     running = []
     while pending or running:
         while pending and len(running) < jobs:
@@ -72,7 +74,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
             raise RuntimeError(f"{cmd[0]} failed ({proc.returncode}) on {cmd[-3]}:\n{_clean(err)}")
     tmp = LIB + ".tmp"
     link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp] + [obj for _, obj, _ in _units()] + [
-        HOST_OBJ, _gomp()]
+        *HOST_OBJS, _gomp()]
     if verbose:
         print(" ".join(link), flush=True)
     res = subprocess.run(link, capture_output=True, text=True)

@@ -197,6 +197,27 @@ size_t pi_cold_workspace_bytes(const pi_ffn *ffn, int32_t batch);   /* 0 on inva
 int pi_cold_ffn_host(const pi_ffn *ffn, const void *x, int32_t batch, const uint8_t *mask, float *y,
                      int32_t *n_computed, void *ws, size_t ws_bytes, int32_t n_threads);
 
+/* ---- offline placement (method section: an offline policy, an integer linear program over
+ * activation frequency and hardware bandwidth, chooses the neurons preloaded on the GPU; README:
+ * the result is the GPU index, sized by a VRAM budget) ----
+ *
+ * pi_place chooses, for n_layers layers of d_ffn[l] neurons of neuron_bytes[l] bytes each (all of
+ * a neuron's rows in that layer's format) with firing frequencies freq (concatenated per layer,
+ * each in [0, 1]), the neurons to keep on the device so that the expected time of a token,
+ * sum_l max(device bytes_l / gpu_bytes_per_s, host bytes_l / host_bytes_per_s) with the bytes of
+ * a neuron counted at its firing frequency, is smallest under sum_l neuron_bytes[l] * placed_l <=
+ * budget_bytes.  Output: slot_of (concatenated per layer, [d_ffn[l]] each: the neuron's slot, in
+ * ascending id order among the placed ones, or -1) -- the layer's pi_ffn.slot_of -- n_placed
+ * [n_layers], and *expected_s (if non-NULL) the model's expected seconds per token.  Greedy by
+ * marginal gain per byte over the most frequent remaining neuron of each layer.  Among placements
+ * that keep each layer's most frequent neurons it is exact when all neurons have the same size
+ * (within one neuron's time otherwise); those include the optimum while the host side of every
+ * layer dominates, and are within one neuron's time per layer of it in general.  Host memory,
+ * synchronous; returns a pi_status. */
+int pi_place(int32_t n_layers, const int32_t *d_ffn, const int64_t *neuron_bytes, const float *freq,
+             int64_t budget_bytes, double gpu_bytes_per_s, double host_bytes_per_s, int32_t *slot_of,
+             int32_t *n_placed, double *expected_s);
+
 /* Human-readable name of a pi_status value (static storage). */
 const char *pi_status_string(int status);
 

@@ -193,3 +193,58 @@ def num_threads() -> int:
 
 def set_num_threads(n: int) -> None:
     lib().pio_set_num_threads(n)
+
+
+# ------------------------------------------------------------------ offline placement (tiny cases)
+# The model the placement solves (the pages name an integer linear program over activation
+# frequency and hardware bandwidth, without a formulation): layer l keeps the set H_l on the
+# device; a token streams c_l * sum_{i in H_l} p_{l,i} bytes there and c_l * sum_{i not in H_l}
+# p_{l,i} bytes on the host, in parallel, so the layer takes the larger of the two times.
+
+def place_objective(neuron_bytes, freq, placed, bw_gpu, bw_host):
+    """Expected seconds per token of a placement: sum over layers of
+    max(c * (sum of p over placed) / bw_gpu, c * (sum of p over the rest) / bw_host)."""
+    t = 0.0
+    for c, p, h in zip(neuron_bytes, freq, placed):
+        p = np.asarray(p, np.float64)
+        on = float(p[np.asarray(h, bool)].sum())
+        t += max(c * on / bw_gpu, c * (float(p.sum()) - on) / bw_host)
+    return t
+
+
+def place_exact(neuron_bytes, freq, budget, bw_gpu, bw_host):
+    """The optimum by brute force over every subset of all neurons (pure Python: tiny cases only).
+    Returns (objective, placement as per-layer boolean arrays)."""
+    import itertools
+    sizes = [len(p) for p in freq]
+    cost = np.concatenate([np.full(n, c, np.int64) for n, c in zip(sizes, neuron_bytes)])
+    best, arg = None, None
+    for bits in itertools.product((False, True), repeat=int(sum(sizes))):
+        sel = np.array(bits, bool)
+        if int(cost[sel].sum()) > budget:
+            continue
+        placed = np.split(sel, np.cumsum(sizes)[:-1])
+        t = place_objective(neuron_bytes, freq, placed, bw_gpu, bw_host)
+        if best is None or t < best:
+            best, arg = t, placed
+    return best, arg
+
+
+def place_exact_prefix(neuron_bytes, freq, budget, bw_gpu, bw_host):
+    """The optimum over placements that keep, in every layer, its n_l most frequent neurons (ties:
+    lower id), by enumerating every (n_0, n_1, ...) under the budget.  Returns the objective."""
+    import itertools
+    orders = [np.argsort(-np.asarray(p, np.float64), kind="stable") for p in freq]
+    best = None
+    for ns in itertools.product(*[range(len(p) + 1) for p in freq]):
+        if sum(n * c for n, c in zip(ns, neuron_bytes)) > budget:
+            continue
+        placed = []
+        for n, order, p in zip(ns, orders, freq):
+            h = np.zeros(len(p), bool)
+            h[order[:n]] = True
+            placed.append(h)
+        t = place_objective(neuron_bytes, freq, placed, bw_gpu, bw_host)
+        if best is None or t < best:
+            best = t
+    return best
