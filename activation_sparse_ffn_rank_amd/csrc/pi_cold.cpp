@@ -37,26 +37,6 @@ __m256 load_f16x8(const uint16_t *p) { return _mm256_cvtph_ps(_mm_loadu_si128(re
 
 float half_to_float(uint16_t h) { return _cvtsh_ss(h); }
 
-// dot of an fp16 row with fp32 x (d % 8 == 0)
-float dot_f16(const uint16_t *w, const float *x, int d) {
-    __m256 a0 = _mm256_setzero_ps(), a1 = a0, a2 = a0, a3 = a0;
-    int j = 0;
-    for (; j + 32 <= d; j += 32) {
-        a0 = _mm256_fmadd_ps(load_f16x8(w + j), _mm256_loadu_ps(x + j), a0);
-        a1 = _mm256_fmadd_ps(load_f16x8(w + j + 8), _mm256_loadu_ps(x + j + 8), a1);
-        a2 = _mm256_fmadd_ps(load_f16x8(w + j + 16), _mm256_loadu_ps(x + j + 16), a2);
-        a3 = _mm256_fmadd_ps(load_f16x8(w + j + 24), _mm256_loadu_ps(x + j + 24), a3);
-    }
-    for (; j < d; j += 8) a0 = _mm256_fmadd_ps(load_f16x8(w + j), _mm256_loadu_ps(x + j), a0);
-    return hsum(_mm256_add_ps(_mm256_add_ps(a0, a1), _mm256_add_ps(a2, a3)));
-}
-
-// y += h * row (fp16 row, d % 8 == 0)
-void axpy_f16(float h, const uint16_t *w, float *y, int d) {
-    const __m256 hv = _mm256_set1_ps(h);
-    for (int j = 0; j < d; j += 8) _mm256_storeu_ps(y + j, _mm256_fmadd_ps(hv, load_f16x8(w + j), _mm256_loadu_ps(y + j)));
-}
-
 // The 32 weights of Q4_0 block q of a row (d/2 code bytes, then d/32 fp16 scales), as
 // (code - 8) in four vectors of 8 consecutive weights, and the block's scale.
 void q4_block(const uint8_t *row, int d, int q, __m256 (&v)[4], float &scale) {
@@ -74,30 +54,73 @@ void q4_block(const uint8_t *row, int d, int q, __m256 (&v)[4], float &scale) {
     scale = half_to_float(s);
 }
 
-float dot_q4(const uint8_t *row, const float *x, int d) {
-    float acc = 0.f;
-    for (int q = 0; q < d / 32; ++q) {
-        __m256 v[4];
-        float sc;
-        q4_block(row, d, q, v, sc);
-        const float *xq = x + (size_t)q * 32;
-        __m256 s = _mm256_mul_ps(v[0], _mm256_loadu_ps(xq));
-        s = _mm256_fmadd_ps(v[1], _mm256_loadu_ps(xq + 8), s);
-        s = _mm256_fmadd_ps(v[2], _mm256_loadu_ps(xq + 16), s);
-        s = _mm256_fmadd_ps(v[3], _mm256_loadu_ps(xq + 24), s);
-        acc += sc * hsum(s);
+// Four rows at a time: the dots of four fp16 rows with one x (each x vector loaded once for all
+// four), and y += sum_r h[r] * row_r (y loaded and stored once per four rows).  A missing row is
+// passed as a copy of row 0 with h = 0, which adds exact zeros.
+void dot4_f16(const uint16_t *const (&w)[4], const float *x, int d, float (&out)[4]) {
+    __m256 a[4][2];
+    for (int r = 0; r < 4; ++r) a[r][0] = a[r][1] = _mm256_setzero_ps();
+    int j = 0;
+    for (; j + 16 <= d; j += 16) {
+        const __m256 x0 = _mm256_loadu_ps(x + j), x1 = _mm256_loadu_ps(x + j + 8);
+        for (int r = 0; r < 4; ++r) {
+            a[r][0] = _mm256_fmadd_ps(load_f16x8(w[r] + j), x0, a[r][0]);
+            a[r][1] = _mm256_fmadd_ps(load_f16x8(w[r] + j + 8), x1, a[r][1]);
+        }
     }
-    return acc;
+    if (j < d) {                                                  // d % 16 == 8
+        const __m256 x0 = _mm256_loadu_ps(x + j);
+        for (int r = 0; r < 4; ++r) a[r][0] = _mm256_fmadd_ps(load_f16x8(w[r] + j), x0, a[r][0]);
+    }
+    for (int r = 0; r < 4; ++r) out[r] = hsum(_mm256_add_ps(a[r][0], a[r][1]));
 }
 
-void axpy_q4(float h, const uint8_t *row, float *y, int d) {
+void axpy4_f16(const float (&h)[4], const uint16_t *const (&w)[4], float *y, int d) {
+    const __m256 h0 = _mm256_set1_ps(h[0]), h1 = _mm256_set1_ps(h[1]), h2 = _mm256_set1_ps(h[2]),
+                 h3 = _mm256_set1_ps(h[3]);
+    for (int j = 0; j < d; j += 8) {
+        __m256 acc = _mm256_loadu_ps(y + j);
+        acc = _mm256_fmadd_ps(h0, load_f16x8(w[0] + j), acc);
+        acc = _mm256_fmadd_ps(h1, load_f16x8(w[1] + j), acc);
+        acc = _mm256_fmadd_ps(h2, load_f16x8(w[2] + j), acc);
+        acc = _mm256_fmadd_ps(h3, load_f16x8(w[3] + j), acc);
+        _mm256_storeu_ps(y + j, acc);
+    }
+}
+
+void dot4_q4(const uint8_t *const (&w)[4], const float *x, int d, float (&out)[4]) {
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int q = 0; q < d / 32; ++q) {
-        __m256 v[4];
-        float sc;
-        q4_block(row, d, q, v, sc);
-        const __m256 hs = _mm256_set1_ps(h * sc);
+        const float *xq = x + (size_t)q * 32;
+        const __m256 x0 = _mm256_loadu_ps(xq), x1 = _mm256_loadu_ps(xq + 8), x2 = _mm256_loadu_ps(xq + 16),
+                     x3 = _mm256_loadu_ps(xq + 24);
+        for (int r = 0; r < 4; ++r) {
+            __m256 v[4];
+            float sc;
+            q4_block(w[r], d, q, v, sc);
+            __m256 t = _mm256_mul_ps(v[0], x0);
+            t = _mm256_fmadd_ps(v[1], x1, t);
+            t = _mm256_fmadd_ps(v[2], x2, t);
+            t = _mm256_fmadd_ps(v[3], x3, t);
+            acc[r] += sc * hsum(t);
+        }
+    }
+    for (int r = 0; r < 4; ++r) out[r] = acc[r];
+}
+
+void axpy4_q4(const float (&h)[4], const uint8_t *const (&w)[4], float *y, int d) {
+    for (int q = 0; q < d / 32; ++q) {
         float *yq = y + (size_t)q * 32;
-        for (int k = 0; k < 4; ++k) _mm256_storeu_ps(yq + 8 * k, _mm256_fmadd_ps(hs, v[k], _mm256_loadu_ps(yq + 8 * k)));
+        __m256 acc[4];
+        for (int k = 0; k < 4; ++k) acc[k] = _mm256_loadu_ps(yq + 8 * k);
+        for (int r = 0; r < 4; ++r) {
+            __m256 v[4];
+            float sc;
+            q4_block(w[r], d, q, v, sc);
+            const __m256 hs = _mm256_set1_ps(h[r] * sc);
+            for (int k = 0; k < 4; ++k) acc[k] = _mm256_fmadd_ps(hs, v[k], acc[k]);
+        }
+        for (int k = 0; k < 4; ++k) _mm256_storeu_ps(yq + 8 * k, acc[k]);
     }
 }
 
@@ -179,38 +202,72 @@ int pi_cold_ffn_host(const pi_ffn *ffn, const void *x, int32_t batch, const uint
         float *yc = sc.part + (size_t)c * bd;
         memset(yc, 0, bd * sizeof(float));
         const int k0 = (int)((int64_t)n * c / kChunks), k1 = (int)((int64_t)n * (c + 1) / kChunks);
-        for (int k = k0; k < k1; ++k) {
-            const int i = sc.list[k];
-            const int s = ffn->slot_of ? ffn->slot_of[i] : i;
-            const uint8_t *row = w_in + (size_t)s * in_stride;
-            float h[PI_MAX_BATCH];
+        // neurons four at a time (gated: two, as four rows); a missing neuron repeats the first
+        // with h = 0
+        const int G = gated ? 2 : 4;
+        for (int k = k0; k < k1; k += G) {
+            const int m = k1 - k < G ? k1 - k : G;
+            int sl[4];
+            for (int i = 0; i < 4; ++i) {
+                const int id = sc.list[k + (i < m ? i : 0)];
+                sl[i] = ffn->slot_of ? ffn->slot_of[id] : id;
+            }
+            float h[PI_MAX_BATCH][4];
             bool any = false;
             for (int b = 0; b < B; ++b) {
                 const float *xb = sc.xf + (size_t)b * d;
-                float hv;
+                float u[4], g[4];
                 if (q4) {
-                    const float u = dot_q4(row, xb, d) + (b_up ? half_to_float(b_up[s]) : 0.f);
-                    hv = u > 0.f ? u : 0.f;
-                    if (sq) hv *= hv;
+                    const uint8_t *const rows[4] = {w_in + (size_t)sl[0] * in_stride, w_in + (size_t)sl[1] * in_stride,
+                                                    w_in + (size_t)sl[2] * in_stride, w_in + (size_t)sl[3] * in_stride};
+                    dot4_q4(rows, xb, d, u);
                 } else if (gated) {
-                    const float g = dot_f16(reinterpret_cast<const uint16_t *>(row), xb, d);
-                    const float u = dot_f16(reinterpret_cast<const uint16_t *>(row + rb), xb, d);
-                    hv = (g > 0.f ? g : 0.f) * u;
+                    // rows: gate and up of neurons 0 and 1
+                    const uint16_t *const rows[4] = {
+                        reinterpret_cast<const uint16_t *>(w_in + (size_t)sl[0] * in_stride),
+                        reinterpret_cast<const uint16_t *>(w_in + (size_t)sl[0] * in_stride + rb),
+                        reinterpret_cast<const uint16_t *>(w_in + (size_t)sl[1] * in_stride),
+                        reinterpret_cast<const uint16_t *>(w_in + (size_t)sl[1] * in_stride + rb)};
+                    float gu[4];
+                    dot4_f16(rows, xb, d, gu);
+                    g[0] = gu[0]; u[0] = gu[1]; g[1] = gu[2]; u[1] = gu[3];
                 } else {
-                    const float u = dot_f16(reinterpret_cast<const uint16_t *>(row), xb, d) +
-                                    (b_up ? half_to_float(b_up[s]) : 0.f);
-                    hv = u > 0.f ? u : 0.f;
-                    if (sq) hv *= hv;
+                    const uint16_t *const rows[4] = {reinterpret_cast<const uint16_t *>(w_in + (size_t)sl[0] * in_stride),
+                                                     reinterpret_cast<const uint16_t *>(w_in + (size_t)sl[1] * in_stride),
+                                                     reinterpret_cast<const uint16_t *>(w_in + (size_t)sl[2] * in_stride),
+                                                     reinterpret_cast<const uint16_t *>(w_in + (size_t)sl[3] * in_stride)};
+                    dot4_f16(rows, xb, d, u);
                 }
-                h[b] = hv;
-                any |= hv != 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    float hv = 0.f;
+                    if (i < m) {
+                        if (gated) {
+                            hv = (g[i] > 0.f ? g[i] : 0.f) * u[i];
+                        } else {
+                            const float v = u[i] + (b_up ? half_to_float(b_up[sl[i]]) : 0.f);
+                            hv = v > 0.f ? v : 0.f;
+                            if (sq) hv *= hv;
+                        }
+                    }
+                    h[b][i] = hv;
+                    any |= hv != 0.f;
+                }
             }
             if (!any) continue;                                  // adds exact zeros
-            const uint8_t *dn = w_dn + (size_t)s * rb;
             for (int b = 0; b < B; ++b) {
-                if (h[b] == 0.f) continue;
-                if (q4) axpy_q4(h[b], dn, yc + (size_t)b * d, d);
-                else axpy_f16(h[b], reinterpret_cast<const uint16_t *>(dn), yc + (size_t)b * d, d);
+                float *yb = yc + (size_t)b * d;
+                const float hb[4] = {h[b][0], h[b][1], h[b][2], h[b][3]};
+                if (q4) {
+                    const uint8_t *const rows[4] = {w_dn + (size_t)sl[0] * rb, w_dn + (size_t)sl[1] * rb,
+                                                    w_dn + (size_t)sl[2] * rb, w_dn + (size_t)sl[3] * rb};
+                    axpy4_q4(hb, rows, yb, d);
+                } else {
+                    const uint16_t *const rows[4] = {reinterpret_cast<const uint16_t *>(w_dn + (size_t)sl[0] * rb),
+                                                     reinterpret_cast<const uint16_t *>(w_dn + (size_t)sl[1] * rb),
+                                                     reinterpret_cast<const uint16_t *>(w_dn + (size_t)sl[2] * rb),
+                                                     reinterpret_cast<const uint16_t *>(w_dn + (size_t)sl[3] * rb)};
+                    axpy4_f16(hb, rows, yb, d);
+                }
             }
         }
     }
