@@ -265,20 +265,56 @@ def main():
                                       slot_of=slot_c, b_up=b_up_c))
         ws_h = np.zeros(_abi.pi_cold_workspace_bytes(hosts[0], B), np.uint8)
         y_h = np.empty((B, cfg.d), np.float32)
-        times, counts_c = [], []
-        for i, (t, l) in enumerate(cases):
-            if l >= n_lay:
-                continue
-            x_h = np.ascontiguousarray(x_all[t, l])
-            s0 = time.perf_counter()
-            counts_c.append(_abi.pi_cold_ffn_host(hosts[l], x_h, B, masks_h[i], y_h, ws_h))
-            times.append(time.perf_counter() - s0)
+        # every host thread, and half of them (hosts that expose two threads per core often run this
+        # memory-bound loop faster on one per core); the faster is reported, with its count
+        best = None
+        for nthr in sorted({_s.num_threads(), max(1, _s.num_threads() // 2)}):
+            times, counts_c = [], []
+            for i, (t, l) in enumerate(cases):
+                if l >= n_lay:
+                    continue
+                x_h = np.ascontiguousarray(x_all[t, l])
+                s0 = time.perf_counter()
+                counts_c.append(_abi.pi_cold_ffn_host(hosts[l], x_h, B, masks_h[i], y_h, ws_h, nthr))
+                times.append(time.perf_counter() - s0)
+            med = float(np.median(times))
+            if best is None or med < best[0]:
+                best = (med, nthr, counts_c, len(times))
+        # the hybrid layer end to end, as the method runs it (device over the resident neurons,
+        # host over the rest, y's added), with the layer's dependencies kept in order: device
+        # layer -> mask to pinned host memory -> host half -> host y to the device -> added to y
+        nthr = best[1]
+        mask_pin = torch.empty(cfg.f, dtype=torch.uint8, pin_memory=True)
+        ycold_pin = torch.empty((B, cfg.d), dtype=torch.float32, pin_memory=True)
+        y_dev = torch.empty((B, cfg.d), dtype=torch.float32, device=dev)
+        m_dev = torch.empty(cfg.f, dtype=torch.uint8, device=dev)
+        yc_dev = torch.empty((B, cfg.d), dtype=torch.float32, device=dev)
+        hyb = []
+        with torch.cuda.stream(stream):
+            for rep in range(2):
+                for i, (t, l) in enumerate(cases):
+                    if l >= n_lay:
+                        continue
+                    torch.cuda.synchronize()
+                    s0 = time.perf_counter()
+                    _abi.pi_ffn_layer(layers[l].pred, layers[l].ffn, xd[t, l], B, y_dev, m_dev, None, None, ws)
+                    mask_pin.copy_(m_dev, non_blocking=True)
+                    stream.synchronize()
+                    _abi.pi_cold_ffn_host(hosts[l], np.ascontiguousarray(x_all[t, l]), B, mask_pin.numpy(),
+                                          ycold_pin.numpy(), ws_h, nthr)
+                    yc_dev.copy_(ycold_pin, non_blocking=True)
+                    y_dev.add_(yc_dev)
+                    stream.synchronize()
+                    if rep == 1:
+                        hyb.append(time.perf_counter() - s0)
         del hosts
-        cold_us = 1e6 * float(np.median(times))
+        cold_us = 1e6 * best[0]
+        counts_c = best[2]
         cold = {"host_us_per_layer": round(cold_us, 2), "neurons_per_layer": round(float(np.mean(counts_c)), 1),
                 "rows_mb_per_layer": round(float(np.mean(counts_c)) * (in_rows + 1) * rb / 1e6, 3),
-                "threads": _s.num_threads(), "calls": len(times),
-                "overlapped_layer_us_lower_bound": round(max(cold_us, elapsed_ms * 1000.0 / (K * L)), 2)}
+                "threads": best[1], "calls": best[3],
+                "hybrid_layer_us": round(1e6 * float(np.median(hyb)), 2),
+                "device_only_layer_us": round(elapsed_ms * 1000.0 / (K * L), 2)}
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
