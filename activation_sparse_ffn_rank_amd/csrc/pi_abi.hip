@@ -17,7 +17,7 @@ using namespace pik;
 constexpr size_t kAlign = 256;
 constexpr int kLdsXBytes = 64 * 1024;   // per-workgroup LDS budget for staged token vectors
 constexpr int kUpMaxGroups = 512;       // workgroups of k_sparse_up
-constexpr int kDownTargetTiles = 384;   // (slab, chunk) tiles of k_sparse_down
+constexpr int kDownTargetTiles = 768;   // (slab, chunk) tiles of k_sparse_down
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 

@@ -793,7 +793,9 @@ __global__ __launch_bounds__(256) void k_sparse_down(const uint8_t *__restrict__
                                                      float *__restrict__ part, int C, int32_t *__restrict__ tickets,
                                                      const uint16_t *__restrict__ b_down, float *__restrict__ y) {
     constexpr int U = WT == WT_F16 ? 16 : 32;                    // rows in flight per wave
+    constexpr int HB = (B + 3) / 4 * 4;
     __shared__ float red[4][B][8][kWave];
+    __shared__ __align__(16) float s_h[4][kWave][HB];           // h of the wave's 64 positions
     __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int slab = blockIdx.x, ck = blockIdx.y;
@@ -820,6 +822,20 @@ __global__ __launch_bounds__(256) void k_sparse_down(const uint8_t *__restrict__
         }
         const int sl = (in && any) ? slot_of_id(id, slot_of, f, n_slots) : -1;
         uint64_t live = __ballot(sl >= 0);
+        // every lane's h goes to the wave's LDS rows, so that a row's B values are read back with
+        // B/4 broadcast loads instead of B cross-lane reads (no other wave touches these rows)
+#pragma unroll
+        for (int b = 0; b < B; ++b) s_h[wave][lane][b] = hv[b];
+        auto h_of = [&](int j, float (&hb)[B]) {
+#pragma unroll
+            for (int q = 0; q < HB / 4; ++q) {
+                const float4 v = *reinterpret_cast<const float4 *>(&s_h[wave][j][4 * q]);
+                const float e[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (4 * q + k < B) hb[4 * q + k] = e[k];
+            }
+        };
         while (live) {                                           // wave-uniform
             int js[U];
 #pragma unroll
@@ -838,14 +854,15 @@ __global__ __launch_bounds__(256) void k_sparse_down(const uint8_t *__restrict__
                 for (int u = 0; u < U; ++u) {
                     if (js[u] < 0) continue;                     // wave-uniform
                     const uint32_t wq[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+                    float hb[B];
+                    h_of(js[u], hb);
 #pragma unroll
                     for (int b = 0; b < B; ++b) {
-                        const float hb = bcastf(hv[b], js[u]);
 #pragma unroll
                         for (int p = 0; p < 4; ++p) {
                             const h2 pr = __builtin_bit_cast(h2, wq[p]);
-                            acc[b][2 * p] = fmaf(hb, (float)pr.x, acc[b][2 * p]);
-                            acc[b][2 * p + 1] = fmaf(hb, (float)pr.y, acc[b][2 * p + 1]);
+                            acc[b][2 * p] = fmaf(hb[b], (float)pr.x, acc[b][2 * p]);
+                            acc[b][2 * p + 1] = fmaf(hb[b], (float)pr.y, acc[b][2 * p + 1]);
                         }
                     }
                 }
@@ -868,6 +885,10 @@ __global__ __launch_bounds__(256) void k_sparse_down(const uint8_t *__restrict__
                 for (int u = 0; u < U; ++u) {
                     if (js[u] < 0) continue;
                     const float scf = okv[u] ? half_to_float(sc[u]) : 0.f;
+                    float cf[B];
+                    h_of(js[u], cf);
+#pragma unroll
+                    for (int b = 0; b < B; ++b) cf[b] *= scf;
 #pragma unroll
                     for (int p = 0; p < 4; ++p) {
                         // q4pair(w, 4p) = (code_p - 8, code_{p+4} - 8): columns p and p+4.
@@ -875,9 +896,8 @@ __global__ __launch_bounds__(256) void k_sparse_down(const uint8_t *__restrict__
                         const float lo = (float)pr.x, hi = (float)pr.y;
 #pragma unroll
                         for (int b = 0; b < B; ++b) {
-                            const float cf = bcastf(hv[b], js[u]) * scf;
-                            acc[b][p] = fmaf(cf, lo, acc[b][p]);
-                            acc[b][p + 4] = fmaf(cf, hi, acc[b][p + 4]);
+                            acc[b][p] = fmaf(cf[b], lo, acc[b][p]);
+                            acc[b][p + 4] = fmaf(cf[b], hi, acc[b][p + 4]);
                         }
                     }
                 }
