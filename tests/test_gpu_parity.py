@@ -85,6 +85,8 @@ FFN_CASES = [  # (d, f, gated, wtype, B, active share)
     (8192, 600, False, F16, 5, 0.2), (256, 64, False, F16, 1, 0.0), (7168, 513, False, F16, 4, 0.5),
     # gated with x in column chunks; every neuron listed over several passes of the up kernel
     (8192, 301, True, F16, 6, 0.3), (256, 12000, False, Q4, 3, 0.8),
+    # edges of the batch > 2 form: the smallest d_model, a single neuron, an empty list
+    (8, 40, False, F16, 3, 0.5), (8, 33, True, F16, 8, 1.0), (256, 1, False, Q4, 4, 1.0), (512, 300, False, Q4, 5, 0.0),
 ]
 
 
