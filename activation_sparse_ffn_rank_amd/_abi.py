@@ -19,9 +19,11 @@ PI_OK, PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_DTYPE, PI_ERR_BATCH, PI_ERR_WORKSPACE, 
 PI_F16, PI_Q4_0 = 1, 2
 PI_ACT_RELU, PI_ACT_SQUARED_RELU = 0, 1
 PI_MAX_BATCH = 8
+PI_MAX_WIDE_BATCH = 16
 
 # Every function the header declares; the CPU tests check that libpi.so exports them all.
-EXPORTS = ("pi_workspace_bytes", "pi_predict", "pi_compact", "pi_sparse_ffn", "pi_ffn_layer",
+EXPORTS = ("pi_workspace_bytes", "pi_predict", "pi_compact", "pi_sparse_ffn", "pi_sparse_ffn_wide_workspace_bytes", "pi_sparse_ffn_wide",
+           "pi_ffn_layer",
            "pi_predict_hidden", "pi_ffn_layer_from_hidden", "pi_layer_path", "pi_ffn_layer_fused", "pi_sparse_ffn_h_offset",
            "pi_cold_workspace_bytes", "pi_cold_ffn_host", "pi_place", "pi_status_string", "pi_version")
 
@@ -63,6 +65,10 @@ def lib() -> ctypes.CDLL:
         L.pi_compact.argtypes = [vp, i32, vp, vp, vp, vp]
         L.pi_sparse_ffn.restype = ctypes.c_int
         L.pi_sparse_ffn.argtypes = [P(pi_ffn), vp, i32, vp, vp, vp, vp, sz, vp]
+        L.pi_sparse_ffn_wide_workspace_bytes.restype = sz
+        L.pi_sparse_ffn_wide_workspace_bytes.argtypes = [P(pi_ffn), i32]
+        L.pi_sparse_ffn_wide.restype = ctypes.c_int
+        L.pi_sparse_ffn_wide.argtypes = [P(pi_ffn), vp, i32, vp, vp, vp, vp, sz, vp]
         L.pi_ffn_layer.restype = ctypes.c_int
         L.pi_ffn_layer.argtypes = [P(pi_predictor), P(pi_ffn), vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.pi_predict_hidden.restype = ctypes.c_int
@@ -154,6 +160,16 @@ def pi_sparse_ffn(ffn, x, batch, idx, counts, y, ws, stream=None) -> None:
     _check("pi_sparse_ffn", lib().pi_sparse_ffn(_byref(ffn), _ptr(x), batch, _ptr(idx), _ptr(counts), _ptr(y),
                                                 _ptr(ws), _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0,
                                                 _stream(stream)))
+
+
+def pi_sparse_ffn_wide_workspace_bytes(ffn, batch: int) -> int:
+    return int(lib().pi_sparse_ffn_wide_workspace_bytes(_byref(ffn), batch))
+
+
+def pi_sparse_ffn_wide(ffn, x, batch, idx, counts, y, ws, stream=None) -> None:
+    _check("pi_sparse_ffn_wide", lib().pi_sparse_ffn_wide(
+        _byref(ffn), _ptr(x), batch, _ptr(idx), _ptr(counts), _ptr(y), _ptr(ws),
+        _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0, _stream(stream)))
 
 
 def pi_ffn_layer(pred, ffn, x, batch, y, mask_out, idx_out, counts_out, ws, stream=None) -> None:

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "pi_abi.hip"), os.path.join(CSRC, "pi_fused_b.hip")]
 HOST_SOURCES = [os.path.join(CSRC, "pi_cold.cpp"),   # host half of the hybrid split (g++, OpenMP)
                 os.path.join(CSRC, "pi_place.cpp")]  # offline placement under a memory budget
-DEPENDS = SOURCES + HOST_SOURCES + [os.path.join(CSRC, n) for n in ("pi_kernels.hpp", "pi_fused.hpp", "pi_tail.hpp", "pi_sparse.hpp")] + [
+DEPENDS = SOURCES + HOST_SOURCES + [os.path.join(CSRC, n) for n in ("pi_kernels.hpp", "pi_fused.hpp", "pi_tail.hpp", "pi_sparse.hpp", "pi_wide.hpp")] + [
                      os.path.join(ROOT, "include", "pi_sparse_ffn.h")]
 OBJDIR = os.path.join(ROOT, "_build")
 

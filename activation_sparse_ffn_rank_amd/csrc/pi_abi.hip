@@ -7,6 +7,7 @@
 #include "pi_sparse_ffn.h"
 #include "pi_kernels.hpp"
 #include "pi_tail.hpp"
+#include "pi_wide.hpp"
 
 #include <algorithm>
 
@@ -68,6 +69,27 @@ int x_chunk(int d, int B) {
 }
 
 int down_slabs(int d) { return ceil_div(d, 512); }
+
+// Workspace of pi_sparse_ffn_wide: slab tickets, h as fp16 hi and lo parts [16][hs], and the
+// chunk partials [C][B][d] fp32.
+constexpr int kWideTargetGroups = 512;   // (slab, chunk) workgroups of k_wide_down
+struct WideGeom {
+    int S, C, hs;
+    size_t hi, lo, part, total;
+};
+WideGeom wide_geom(const pi_ffn *fn, int B) {
+    WideGeom g{};
+    const int d = fn->d_model;
+    g.S = ceil_div(d, kWideDownCols);
+    g.C = std::min(kWideMaxChunks, std::max(1, ceil_div(kWideTargetGroups, g.S)));
+    g.hs = ceil_div(std::max(fn->n_slots, 1), 16) * 16;
+    g.hi = align_up((size_t)g.S * 4);
+    g.lo = g.hi + align_up((size_t)kWideB * g.hs * 2);
+    g.part = g.lo + align_up((size_t)kWideB * g.hs * 2);
+    g.total = g.part + align_up((size_t)g.C * B * d * 4);
+    return g;
+}
+int check_wide_batch(int32_t B) { return (B >= 1 && B <= PI_MAX_WIDE_BATCH) ? PI_OK : PI_ERR_BATCH; }
 
 int down_chunks(int d) {
     return std::min(kDownMaxChunks, std::max(1, ceil_div(kDownTargetTiles, down_slabs(d))));
@@ -552,6 +574,44 @@ int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t
     return enqueue_sparse(ffn, x, batch, idx, counts, y, ws, nullptr, static_cast<hipStream_t>(stream));
 }
 
+size_t pi_sparse_ffn_wide_workspace_bytes(const pi_ffn *ffn, int32_t batch) {
+    if (check_ffn(ffn) != PI_OK || check_wide_batch(batch) != PI_OK || ffn->wtype != PI_F16) return 0;
+    return wide_geom(ffn, batch).total;
+}
+
+int pi_sparse_ffn_wide(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx, const int32_t *counts,
+                       float *y, void *ws, size_t ws_bytes, void *stream) {
+    int rc = check_ffn(ffn);
+    if (rc) return rc;
+    if ((rc = check_wide_batch(batch))) return rc;
+    if (ffn->wtype != PI_F16) return PI_ERR_DTYPE;
+    if (!x || !idx || !counts || !y) return PI_ERR_NULL;
+    if (!aligned16(x)) return PI_ERR_ALIGN;
+    const WideGeom g = wide_geom(ffn, batch);
+    if (!ws || ws_bytes < g.total) return PI_ERR_WORKSPACE;
+    if (!aligned16(ws)) return PI_ERR_ALIGN;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char *w = static_cast<char *>(ws);
+    int32_t *tickets = reinterpret_cast<int32_t *>(w);
+    uint16_t *h_hi = reinterpret_cast<uint16_t *>(w + g.hi), *h_lo = reinterpret_cast<uint16_t *>(w + g.lo);
+    float *part = reinterpret_cast<float *>(w + g.part);
+    const int d = ffn->d_model, f = ffn->d_ffn, ns = ffn->n_slots;
+    const int64_t rb = row_bytes_of(ffn);
+    const uint8_t *w_in = static_cast<const uint8_t *>(ffn->w_in);
+    const uint16_t *xx = static_cast<const uint16_t *>(x), *b_up = static_cast<const uint16_t *>(ffn->b_up);
+    const dim3 up_grid(std::max(1, ceil_div(ns, 16)));
+    if (ffn->gated)
+        hipLaunchKernelGGL(k_wide_up<true>, up_grid, dim3(256), 0, st, w_in, rb, d, b_up, xx, batch, idx, counts,
+                           ffn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, ffn->act);
+    else
+        hipLaunchKernelGGL(k_wide_up<false>, up_grid, dim3(256), 0, st, w_in, rb, d, b_up, xx, batch, idx, counts,
+                           ffn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, ffn->act);
+    hipLaunchKernelGGL(k_wide_down, dim3(g.S, g.C), dim3(256), 0, st, static_cast<const uint8_t *>(ffn->w_down_t), rb,
+                       d, batch, idx, counts, ffn->slot_of, f, ns, h_hi, h_lo, g.hs, part, g.C, tickets,
+                       static_cast<const uint16_t *>(ffn->b_down), y);
+    return launch_status();
+}
+
 int pi_predict_hidden(const pi_predictor *pred, const void *x, int32_t batch, float *z, void *stream) {
     int rc = check_pred(pred);
     if (rc) return rc;
@@ -671,7 +731,7 @@ const char *pi_status_string(int status) {
         case PI_ERR_NULL: return "a required pointer is NULL";
         case PI_ERR_SHAPE: return "a size is out of range or inconsistent";
         case PI_ERR_DTYPE: return "unsupported weight kind or gating combination";
-        case PI_ERR_BATCH: return "batch outside [1, 8]";
+        case PI_ERR_BATCH: return "batch outside [1, 8] ([1, 16] for pi_sparse_ffn_wide)";
         case PI_ERR_WORKSPACE: return "workspace missing or too small";
         case PI_ERR_ALIGN: return "pointer or row not 16-byte aligned";
         case PI_ERR_HIP: return "HIP kernel launch failed";

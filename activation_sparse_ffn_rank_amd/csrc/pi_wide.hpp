@@ -1,0 +1,245 @@
+// pi_wide.hpp -- the neuron-aware sparse FFN at batches of 9 to 16 tokens, on MFMA.
+//
+// The sparse operator of the method (PowerInfer, arXiv 2312.12456, method section: only the
+// predicted neurons' rows are read and computed) is, at a batch of B tokens, a contraction over
+// the gathered rows: H = act(X W_in[idx]^T + b) is [B x n], Y = H W_down^T[idx] is [B x d].  At
+// B <= 8 the GEMV kernels of pi_kernels.hpp keep the vector ALU below the HBM rate; at B = 16
+// the down step alone needs 16 FMAs per fp16 weight (64 T FMA/s at 8 TB/s, most of the vector
+// ALU's 78.6 T), so here both steps run on v_mfma_f32_16x16x16_f16 tiles with the batch padded
+// to 16 (tokens >= B read as zero and are never stored).
+//
+// Operand layout of a 16x16x16 f16 MFMA (wave64): lane l supplies A[m = l%16][k = 4(l/16)+v] and
+// B[k = 4(l/16)+v][n = l%16] for v < 4, and receives D[m = 4(l/16)+v][n = l%16].  A contraction
+// may assign its k indices to (lane group, v) slots in any order as long as A and B agree, which
+// the kernels use to make every lane's loads contiguous.
+//
+// Kernels (stream-ordered):
+//   k_wide_up    one workgroup per 16 listed neurons: H tile [16 tokens x 16 neurons] over all d,
+//                the four waves taking interleaved 256-column blocks, summed in LDS; writes h
+//                as fp16 hi + fp16 lo parts (h = hi + lo to ~2^-22 relative), so that feeding h to
+//                the f16 MFMA of the down step costs no accuracy.
+//   k_wide_down  (128-column slab, neuron chunk) tiles: Y tile [16 tokens x 128 columns] over the
+//                chunk's neurons, waves summed in LDS, chunk partials summed in chunk order by the
+//                last workgroup of each slab (deterministic), plus b_down.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pi_kernels.hpp"
+
+namespace pik {
+
+constexpr int kWideB = 16;            // the padded batch: one MFMA M (or N) dimension
+constexpr int kWideUpCols = 256;      // columns per k_wide_up block (8 column groups of 32)
+constexpr int kWideDownCols = 128;    // columns per k_wide_down slab (16 lanes x 8 columns)
+constexpr int kWideMaxChunks = 32;    // chunk partials per slab summed by the last workgroup
+
+typedef f16 h4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f4 mfma16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f4 c) {
+    const h4 a = __builtin_bit_cast(h4, make_uint2(a0, a1));
+    const h4 b = __builtin_bit_cast(h4, make_uint2(b0, b1));
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// h[b][k] for the listed neurons, as fp16 hi and lo parts in [16][hs] arrays.  Workgroup t holds
+// list positions 16t .. 16t+15; lane l of every wave works on position 16t + l%16 and token l%16
+// (the MFMA's n and m) and columns blk + 32j + 8(l/16) .. +8 of block blk (j < 8), so each of a
+// row's 16-byte loads is contiguous with the next lane group's.  Row loads are unconditional (slot
+// 0, column 0 stand in for an absent neuron or a column past d, and the value is zeroed), so all
+// of a block's loads are in flight together; x is read through a buffer resource (a token >= B or
+// a column past d reads zero).  Workgroup 0 also clears `zero_ptr[0..nzero)` (the down kernel's
+// slab tickets); the down kernel always runs after this one on the same stream.
+template <bool GATED>
+__global__ __launch_bounds__(256) void k_wide_up(const uint8_t *__restrict__ w_in, int64_t row_bytes, int d,
+                                                 const uint16_t *__restrict__ b_up, const uint16_t *__restrict__ x,
+                                                 int B, const int32_t *__restrict__ idx,
+                                                 const int32_t *__restrict__ counts,
+                                                 const int32_t *__restrict__ slot_of, int f, int n_slots,
+                                                 uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int hs,
+                                                 int32_t *__restrict__ zero_ptr, int nzero, int act) {
+    __shared__ f4 red[GATED ? 2 : 1][4][kWave];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    if (blockIdx.x == 0)
+        for (int t = tid; t < nzero; t += blockDim.x) zero_ptr[t] = 0;
+    const int n = min(max(counts[0], 0), n_slots);
+    const int t0 = blockIdx.x * 16;
+    if (t0 >= n) return;                                         // workgroup-uniform
+    const int r = lane & 15, g = lane >> 4;
+    const int pos = t0 + r;
+    const int s = pos < n ? slot_of_id(idx[pos], slot_of, f, n_slots) : -1;
+    const int64_t stride = row_bytes * (GATED ? 2 : 1);
+    const uint8_t *row = w_in + (int64_t)(s >= 0 ? s : 0) * stride;
+    const __amdgpu_buffer_rsrc_t xr = buf_rsrc(x, (uint32_t)B * (uint32_t)d * 2u);
+    const uint32_t xrow = r < B ? (uint32_t)r * (uint32_t)d * 2u : kOOB;
+    f4 au = {0.f, 0.f, 0.f, 0.f}, ag = {0.f, 0.f, 0.f, 0.f};
+    for (int blk = wave * kWideUpCols; blk < d; blk += 4 * kWideUpCols) {
+        uint4 wu[8], wg[8], xv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int col = blk + 32 * j + 8 * g;
+            const bool ok = col < d;                             // d % 8 == 0: a vector is all in or all out
+            const int64_t off = (int64_t)(ok ? col : 0) * 2;
+            if (GATED) {
+                wg[j] = ld16(row + off);
+                wu[j] = ld16(row + row_bytes + off);
+            } else {
+                wu[j] = ld16(row + off);
+            }
+            xv[j] = bld16(xr, xrow + (ok ? (uint32_t)col * 2u : kOOB));
+        }
+        const bool live = s >= 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool ok = live && blk + 32 * j + 8 * g < d;
+            const uint4 u = ok ? wu[j] : zero4();
+            au = mfma16(xv[j].x, xv[j].y, u.x, u.y, au);
+            au = mfma16(xv[j].z, xv[j].w, u.z, u.w, au);
+            if (GATED) {
+                const uint4 q = ok ? wg[j] : zero4();
+                ag = mfma16(xv[j].x, xv[j].y, q.x, q.y, ag);
+                ag = mfma16(xv[j].z, xv[j].w, q.z, q.w, ag);
+            }
+        }
+    }
+    red[0][wave][lane] = au;
+    if (GATED) red[GATED ? 1 : 0][wave][lane] = ag;
+    __syncthreads();
+    // thread (v, l): D element v of lane l = token 4(l/16) + v, position t0 + l%16 -- the position
+    // whose slot this thread looked up itself (s)
+    const int v = tid / kWave, l = lane;
+    const int b = 4 * (l >> 4) + v;
+    float u = red[0][0][l][v] + red[0][1][l][v] + red[0][2][l][v] + red[0][3][l][v];
+    float hv;
+    if (GATED) {
+        const float gg = red[GATED ? 1 : 0][0][l][v] + red[GATED ? 1 : 0][1][l][v] + red[GATED ? 1 : 0][2][l][v] +
+                         red[GATED ? 1 : 0][3][l][v];
+        hv = fmaxf(gg, 0.f) * u;
+    } else {
+        const float bias = (b_up != nullptr && s >= 0) ? half_to_float(b_up[s]) : 0.f;
+        hv = fmaxf(u + bias, 0.f);
+        if (act) hv *= hv;                                       // squared ReLU
+    }
+    if (s < 0 || b >= B) hv = 0.f;
+    const f16 hi = (f16)hv;
+    const f16 lo = (f16)(hv - (float)hi);
+    h_hi[(size_t)b * hs + pos] = __builtin_bit_cast(uint16_t, hi);
+    h_lo[(size_t)b * hs + pos] = __builtin_bit_cast(uint16_t, lo);
+}
+
+// y over (128-column slab, neuron chunk) tiles.  The chunk's 16-position steps are split into four
+// contiguous runs, one per wave.  In a step, lane l reads columns c0 + 8(l%16) .. +8 of the rows of
+// positions 4(l/16) + v (v < 4; 16 lanes cover 256 contiguous bytes of a row) and h of token l%16
+// at the same four positions; MFMA e (e < 8) then takes half e of each of the four row vectors as
+// its B operand, so its D holds columns c0 + 8(l%16) + e.  Slots are looked up 64 positions at a
+// time, one lane per position, and handed to the lanes that need them by ds_bpermute.  The waves'
+// tiles meet in LDS, each chunk's partial goes to `part` ([C][B][d] fp32), and the last workgroup
+// to finish a slab (slab ticket) sums the partials in chunk order and adds b_down.  Tickets must
+// be zero on entry (k_wide_up clears them) and are left zero.
+__global__ __launch_bounds__(256) void k_wide_down(const uint8_t *__restrict__ w_dn, int64_t row_bytes, int d, int B,
+                                                   const int32_t *__restrict__ idx, const int32_t *__restrict__ counts,
+                                                   const int32_t *__restrict__ slot_of, int f, int n_slots,
+                                                   const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
+                                                   int hs, float *__restrict__ part, int C,
+                                                   int32_t *__restrict__ tickets, const uint16_t *__restrict__ b_down,
+                                                   float *__restrict__ y) {
+    __shared__ f4 red[4][8][kWave];
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int slab = blockIdx.x, ck = blockIdx.y;
+    const int n = min(max(counts[0], 0), n_slots);
+    const int T = (n + 15) / 16;                                 // 16-position steps
+    const int c_lo = (int)((int64_t)T * ck / C), c_hi = (int)((int64_t)T * (ck + 1) / C);
+    const int w_lo = c_lo + (c_hi - c_lo) * wave / 4, w_hi = c_lo + (c_hi - c_lo) * (wave + 1) / 4;
+    const int r = lane & 15, g = lane >> 4;
+    const int col = slab * kWideDownCols + 8 * r;
+    const bool colok = col < d;
+    const int64_t coff = (int64_t)(colok ? col : 0) * 2;
+    f4 acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = f4{0.f, 0.f, 0.f, 0.f};
+
+    for (int st0 = w_lo; st0 < w_hi; st0 += 4) {                 // four steps per slot lookup
+        const int p = st0 * 16 + lane;                           // this lane's lookup position
+        const int sl = (p < w_hi * 16 && p < n) ? slot_of_id(idx[p], slot_of, f, n_slots) : -1;
+        // every load of the four steps goes out before the first MFMA; a step past the wave's run
+        // (its positions looked up as -1) reads slot 0 and the last valid step's h, and is zeroed
+        int sv[4][4];
+        uint4 wv[4][4];
+        uint2 ahi[4], alo[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int sq = min(st0 + q, w_hi - 1);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                sv[q][v] = __shfl(sl, q * 16 + 4 * g + v);
+                wv[q][v] = ld16(w_dn + (int64_t)(sv[q][v] >= 0 ? sv[q][v] : 0) * row_bytes + coff);
+            }
+            const size_t ho = (size_t)r * hs + (size_t)sq * 16 + 4 * g;
+            ahi[q] = *reinterpret_cast<const uint2 *>(h_hi + ho);
+            alo[q] = *reinterpret_cast<const uint2 *>(h_lo + ho);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (st0 + q >= w_hi) {                               // wave-uniform
+                ahi[q] = make_uint2(0u, 0u);
+                alo[q] = make_uint2(0u, 0u);
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                if (sv[q][v] < 0 || !colok) wv[q][v] = zero4();
+            const uint32_t wq[4][4] = {{wv[q][0].x, wv[q][0].y, wv[q][0].z, wv[q][0].w},
+                                       {wv[q][1].x, wv[q][1].y, wv[q][1].z, wv[q][1].w},
+                                       {wv[q][2].x, wv[q][2].y, wv[q][2].z, wv[q][2].w},
+                                       {wv[q][3].x, wv[q][3].y, wv[q][3].z, wv[q][3].w}};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                // halves 2c (low) and 2c+1 (high) of the four rows, packed as k = 0..3
+                const uint32_t e0 = (wq[0][c] & 0xffffu) | (wq[1][c] << 16);
+                const uint32_t e1 = (wq[2][c] & 0xffffu) | (wq[3][c] << 16);
+                const uint32_t o0 = (wq[0][c] >> 16) | (wq[1][c] & 0xffff0000u);
+                const uint32_t o1 = (wq[2][c] >> 16) | (wq[3][c] & 0xffff0000u);
+                acc[2 * c] = mfma16(ahi[q].x, ahi[q].y, e0, e1, acc[2 * c]);
+                acc[2 * c] = mfma16(alo[q].x, alo[q].y, e0, e1, acc[2 * c]);
+                acc[2 * c + 1] = mfma16(ahi[q].x, ahi[q].y, o0, o1, acc[2 * c + 1]);
+                acc[2 * c + 1] = mfma16(alo[q].x, alo[q].y, o0, o1, acc[2 * c + 1]);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave][e][lane] = acc[e];
+    __syncthreads();
+    // output (token b, column cc of the slab): lane 16(b/4) + cc/8, MFMA e = cc%8, element b%4
+    const int Bd = B * d;
+    for (int o = tid; o < B * kWideDownCols; o += blockDim.x) {
+        const int b = o / kWideDownCols, cc = o - b * kWideDownCols;
+        const int ln = 16 * (b >> 2) + (cc >> 3), e = cc & 7, v = b & 3;
+        const int gcol = slab * kWideDownCols + cc;
+        if (gcol < d)
+            store_coherent(part + (size_t)ck * Bd + (size_t)b * d + gcol,
+                           red[0][e][ln][v] + red[1][e][ln][v] + red[2][e][ln][v] + red[3][e][ln][v]);
+    }
+    wait_stores_done();                                          // this thread's partials are out
+    __syncthreads();                                             // ... and so are everyone's
+    if (tid == 0) s_last = (atomicAdd(&tickets[slab], 1) == C - 1);
+    __syncthreads();
+    if (!s_last) return;
+    for (int o = tid; o < B * kWideDownCols; o += blockDim.x) {
+        const int b = o / kWideDownCols, cc = o - b * kWideDownCols;
+        const int gcol = slab * kWideDownCols + cc;
+        const bool ok = gcol < d;
+        const size_t off = (size_t)b * d + (ok ? gcol : 0);
+        float pv[kWideMaxChunks];
+#pragma unroll
+        for (int c = 0; c < kWideMaxChunks; ++c) pv[c] = (ok && c < C) ? load_coherent(part + (size_t)c * Bd + off) : 0.f;
+        float sum = (ok && b_down) ? half_to_float(b_down[gcol]) : 0.f;
+#pragma unroll
+        for (int c = 0; c < kWideMaxChunks; ++c) sum += pv[c];
+        if (ok) y[off] = sum;
+    }
+    if (tid == 0) tickets[slab] = 0;
+}
+
+}  // namespace pik

@@ -69,6 +69,7 @@ typedef enum { PI_F16 = 1, PI_Q4_0 = 2 } pi_wtype;
 typedef enum { PI_ACT_RELU = 0, PI_ACT_SQUARED_RELU = 1 } pi_act;
 
 #define PI_MAX_BATCH 8
+#define PI_MAX_WIDE_BATCH 16      /* pi_sparse_ffn_wide */
 #define PI_MAX_RANK 2048
 #define PI_MAX_D_MODEL (1 << 24)  /* kernels address one token vector or row with 32-bit offsets */
 #define PI_MAX_D_FFN (1 << 26)    /* ... and the mask with 32-bit offsets */
@@ -131,6 +132,20 @@ int pi_compact(const uint8_t *mask, int32_t d_ffn, const int32_t *slot_of, int32
  * form. */
 int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx,
                   const int32_t *counts, float *y, void *ws, size_t ws_bytes, void *stream);
+
+/* The same sparse FFN at batches of up to 16 tokens on MFMA (matrix-core) tiles, for prefill-like
+ * batches where the per-token GEMV form would be bound by the vector ALU (the method's sparse
+ * operator over the predicted neurons, method section, computed as [16 x n] and [16 x d]
+ * products over the gathered rows with the batch padded to 16).  Arguments, idx/counts rules and
+ * y as in pi_sparse_ffn, with 1 <= batch <= PI_MAX_WIDE_BATCH (PI_ERR_BATCH otherwise) and fp16
+ * weights only (PI_ERR_DTYPE for Q4_0).  Two kernels; the workspace of
+ * pi_sparse_ffn_wide_workspace_bytes(ffn, batch) bytes (16-byte aligned) needs no zero fill, holds
+ * no status word, and must not be shared by calls in flight at the same time.  h passes between
+ * the kernels as an fp16 pair (h = hi + lo), so |h| must stay below 65504.  y is deterministic
+ * (fixed summation order).  The workspace-size call returns 0 on invalid arguments. */
+size_t pi_sparse_ffn_wide_workspace_bytes(const pi_ffn *ffn, int32_t batch);
+int pi_sparse_ffn_wide(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx,
+                       const int32_t *counts, float *y, void *ws, size_t ws_bytes, void *stream);
 
 /* Whole layer: pi_predict -> pi_compact -> pi_sparse_ffn, stream-ordered.  pred and ffn must
  * agree on d_model and d_ffn.  mask_out [d_ffn], idx_out [d_ffn] and counts_out [2] receive the
