@@ -72,7 +72,7 @@ int down_slabs(int d) { return ceil_div(d, 512); }
 
 // Workspace of pi_sparse_ffn_wide: slab tickets, h as fp16 hi and lo parts [16][hs], and the
 // chunk partials [C][B][d] fp32.
-constexpr int kWideTargetGroups = 512;   // (slab, chunk) workgroups of k_wide_down
+constexpr int kWideTargetGroups = 256;   // (slab, chunk) workgroups of k_wide_down (8 waves each)
 struct WideGeom {
     int S, C, hs;
     size_t hi, lo, part, total;
@@ -601,12 +601,12 @@ int pi_sparse_ffn_wide(const pi_ffn *ffn, const void *x, int32_t batch, const in
     const uint16_t *xx = static_cast<const uint16_t *>(x), *b_up = static_cast<const uint16_t *>(ffn->b_up);
     const dim3 up_grid(std::max(1, ceil_div(ns, 16)));
     if (ffn->gated)
-        hipLaunchKernelGGL(k_wide_up<true>, up_grid, dim3(256), 0, st, w_in, rb, d, b_up, xx, batch, idx, counts,
+        hipLaunchKernelGGL(k_wide_up<true>, up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx, batch, idx, counts,
                            ffn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, ffn->act);
     else
-        hipLaunchKernelGGL(k_wide_up<false>, up_grid, dim3(256), 0, st, w_in, rb, d, b_up, xx, batch, idx, counts,
+        hipLaunchKernelGGL(k_wide_up<false>, up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx, batch, idx, counts,
                            ffn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, ffn->act);
-    hipLaunchKernelGGL(k_wide_down, dim3(g.S, g.C), dim3(256), 0, st, static_cast<const uint8_t *>(ffn->w_down_t), rb,
+    hipLaunchKernelGGL(k_wide_down, dim3(g.S, g.C), dim3(kWideThreads), 0, st, static_cast<const uint8_t *>(ffn->w_down_t), rb,
                        d, batch, idx, counts, ffn->slot_of, f, ns, h_hi, h_lo, g.hs, part, g.C, tickets,
                        static_cast<const uint16_t *>(ffn->b_down), y);
     return launch_status();

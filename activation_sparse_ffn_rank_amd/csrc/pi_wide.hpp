@@ -15,7 +15,7 @@
 //
 // Kernels (stream-ordered):
 //   k_wide_up    one workgroup per 16 listed neurons: H tile [16 tokens x 16 neurons] over all d,
-//                the four waves taking interleaved 256-column blocks, summed in LDS; writes h
+//                the eight waves taking interleaved 256-column blocks, summed in LDS; writes h
 //                as fp16 hi + fp16 lo parts (h = hi + lo to ~2^-22 relative), so that feeding h to
 //                the f16 MFMA of the down step costs no accuracy.
 //   k_wide_down  (128-column slab, neuron chunk) tiles: Y tile [16 tokens x 128 columns] over the
@@ -33,7 +33,9 @@ namespace pik {
 constexpr int kWideB = 16;            // the padded batch: one MFMA M (or N) dimension
 constexpr int kWideUpCols = 256;      // columns per k_wide_up block (8 column groups of 32)
 constexpr int kWideDownCols = 128;    // columns per k_wide_down slab (16 lanes x 8 columns)
-constexpr int kWideMaxChunks = 32;    // chunk partials per slab summed by the last workgroup
+constexpr int kWideMaxChunks = 16;    // chunk partials per slab summed by the last workgroup
+constexpr int kWideWaves = 8;         // waves per workgroup in both kernels
+constexpr int kWideThreads = kWideWaves * kWave;
 
 typedef f16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -53,14 +55,14 @@ __device__ __forceinline__ f4 mfma16(uint32_t a0, uint32_t a1, uint32_t b0, uint
 // a column past d reads zero).  Workgroup 0 also clears `zero_ptr[0..nzero)` (the down kernel's
 // slab tickets); the down kernel always runs after this one on the same stream.
 template <bool GATED>
-__global__ __launch_bounds__(256) void k_wide_up(const uint8_t *__restrict__ w_in, int64_t row_bytes, int d,
+__global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restrict__ w_in, int64_t row_bytes, int d,
                                                  const uint16_t *__restrict__ b_up, const uint16_t *__restrict__ x,
                                                  int B, const int32_t *__restrict__ idx,
                                                  const int32_t *__restrict__ counts,
                                                  const int32_t *__restrict__ slot_of, int f, int n_slots,
                                                  uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int hs,
                                                  int32_t *__restrict__ zero_ptr, int nzero, int act) {
-    __shared__ f4 red[GATED ? 2 : 1][4][kWave];
+    __shared__ f4 red[GATED ? 2 : 1][kWideWaves][kWave];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     if (blockIdx.x == 0)
         for (int t = tid; t < nzero; t += blockDim.x) zero_ptr[t] = 0;
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(256) void k_wide_up(const uint8_t *__restrict__ w_i
     const __amdgpu_buffer_rsrc_t xr = buf_rsrc(x, (uint32_t)B * (uint32_t)d * 2u);
     const uint32_t xrow = r < B ? (uint32_t)r * (uint32_t)d * 2u : kOOB;
     f4 au = {0.f, 0.f, 0.f, 0.f}, ag = {0.f, 0.f, 0.f, 0.f};
-    for (int blk = wave * kWideUpCols; blk < d; blk += 4 * kWideUpCols) {
+    for (int blk = wave * kWideUpCols; blk < d; blk += kWideWaves * kWideUpCols) {
         uint4 wu[8], wg[8], xv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -107,15 +109,19 @@ __global__ __launch_bounds__(256) void k_wide_up(const uint8_t *__restrict__ w_i
     red[0][wave][lane] = au;
     if (GATED) red[GATED ? 1 : 0][wave][lane] = ag;
     __syncthreads();
-    // thread (v, l): D element v of lane l = token 4(l/16) + v, position t0 + l%16 -- the position
-    // whose slot this thread looked up itself (s)
+    // thread (v, l) of the first four waves: D element v of lane l = token 4(l/16) + v, position
+    // t0 + l%16 -- the position whose slot this thread looked up itself (s)
+    if (tid >= 4 * kWave) return;
     const int v = tid / kWave, l = lane;
     const int b = 4 * (l >> 4) + v;
-    float u = red[0][0][l][v] + red[0][1][l][v] + red[0][2][l][v] + red[0][3][l][v];
+    float u = 0.f, gg = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWideWaves; ++w) {
+        u += red[0][w][l][v];
+        if (GATED) gg += red[GATED ? 1 : 0][w][l][v];
+    }
     float hv;
     if (GATED) {
-        const float gg = red[GATED ? 1 : 0][0][l][v] + red[GATED ? 1 : 0][1][l][v] + red[GATED ? 1 : 0][2][l][v] +
-                         red[GATED ? 1 : 0][3][l][v];
         hv = fmaxf(gg, 0.f) * u;
     } else {
         const float bias = (b_up != nullptr && s >= 0) ? half_to_float(b_up[s]) : 0.f;
@@ -129,22 +135,26 @@ __global__ __launch_bounds__(256) void k_wide_up(const uint8_t *__restrict__ w_i
     h_lo[(size_t)b * hs + pos] = __builtin_bit_cast(uint16_t, lo);
 }
 
-// y over (128-column slab, neuron chunk) tiles.  The chunk's 16-position steps are split into four
+// y over (128-column slab, neuron chunk) tiles.  The chunk's 16-position steps are split into eight
 // contiguous runs, one per wave.  In a step, lane l reads columns c0 + 8(l%16) .. +8 of the rows of
 // positions 4(l/16) + v (v < 4; 16 lanes cover 256 contiguous bytes of a row) and h of token l%16
 // at the same four positions; MFMA e (e < 8) then takes half e of each of the four row vectors as
 // its B operand, so its D holds columns c0 + 8(l%16) + e.  Slots are looked up 64 positions at a
 // time, one lane per position, and handed to the lanes that need them by ds_bpermute.  The waves'
 // tiles meet in LDS, each chunk's partial goes to `part` ([C][B][d] fp32), and the last workgroup
-// to finish a slab (slab ticket) sums the partials in chunk order and adds b_down.  Tickets must
-// be zero on entry (k_wide_up clears them) and are left zero.
-__global__ __launch_bounds__(256) void k_wide_down(const uint8_t *__restrict__ w_dn, int64_t row_bytes, int d, int B,
-                                                   const int32_t *__restrict__ idx, const int32_t *__restrict__ counts,
-                                                   const int32_t *__restrict__ slot_of, int f, int n_slots,
-                                                   const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
-                                                   int hs, float *__restrict__ part, int C,
-                                                   int32_t *__restrict__ tickets, const uint16_t *__restrict__ b_down,
-                                                   float *__restrict__ y) {
+// to finish a slab (slab ticket) sums the partials in chunk order and adds b_down, every thread
+// issuing all of its loads before the first add.  Tickets must be zero on entry (k_wide_up clears
+// them) and are left zero.
+__global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__restrict__ w_dn, int64_t row_bytes,
+                                                            int d, int B, const int32_t *__restrict__ idx,
+                                                            const int32_t *__restrict__ counts,
+                                                            const int32_t *__restrict__ slot_of, int f, int n_slots,
+                                                            const uint16_t *__restrict__ h_hi,
+                                                            const uint16_t *__restrict__ h_lo, int hs,
+                                                            float *__restrict__ part, int C,
+                                                            int32_t *__restrict__ tickets,
+                                                            const uint16_t *__restrict__ b_down,
+                                                            float *__restrict__ y) {
     __shared__ f4 red[4][8][kWave];
     __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -152,7 +162,7 @@ __global__ __launch_bounds__(256) void k_wide_down(const uint8_t *__restrict__ w
     const int n = min(max(counts[0], 0), n_slots);
     const int T = (n + 15) / 16;                                 // 16-position steps
     const int c_lo = (int)((int64_t)T * ck / C), c_hi = (int)((int64_t)T * (ck + 1) / C);
-    const int w_lo = c_lo + (c_hi - c_lo) * wave / 4, w_hi = c_lo + (c_hi - c_lo) * (wave + 1) / 4;
+    const int w_lo = c_lo + (c_hi - c_lo) * wave / kWideWaves, w_hi = c_lo + (c_hi - c_lo) * (wave + 1) / kWideWaves;
     const int r = lane & 15, g = lane >> 4;
     const int col = slab * kWideDownCols + 8 * r;
     const bool colok = col < d;
@@ -208,8 +218,16 @@ __global__ __launch_bounds__(256) void k_wide_down(const uint8_t *__restrict__ w
             }
         }
     }
+    // waves 4..7 hand their tiles to waves 0..3, which then hold pairwise sums
+    if (wave >= 4) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) red[wave][e][lane] = acc[e];
+        for (int e = 0; e < 8; ++e) red[wave - 4][e][lane] = acc[e];
+    }
+    __syncthreads();
+    if (wave < 4) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) red[wave][e][lane] = acc[e] + red[wave][e][lane];
+    }
     __syncthreads();
     // output (token b, column cc of the slab): lane 16(b/4) + cc/8, MFMA e = cc%8, element b%4
     const int Bd = B * d;
@@ -226,18 +244,29 @@ __global__ __launch_bounds__(256) void k_wide_down(const uint8_t *__restrict__ w
     if (tid == 0) s_last = (atomicAdd(&tickets[slab], 1) == C - 1);
     __syncthreads();
     if (!s_last) return;
-    for (int o = tid; o < B * kWideDownCols; o += blockDim.x) {
+    constexpr int OPT = kWideB * kWideDownCols / kWideThreads;   // outputs per thread
+    float pv[OPT][kWideMaxChunks];
+#pragma unroll
+    for (int k = 0; k < OPT; ++k) {
+        const int o = tid + k * kWideThreads;
         const int b = o / kWideDownCols, cc = o - b * kWideDownCols;
         const int gcol = slab * kWideDownCols + cc;
-        const bool ok = gcol < d;
-        const size_t off = (size_t)b * d + (ok ? gcol : 0);
-        float pv[kWideMaxChunks];
+        const bool ok = b < B && gcol < d;
+        const size_t off = ok ? (size_t)b * d + gcol : 0;
 #pragma unroll
-        for (int c = 0; c < kWideMaxChunks; ++c) pv[c] = (ok && c < C) ? load_coherent(part + (size_t)c * Bd + off) : 0.f;
-        float sum = (ok && b_down) ? half_to_float(b_down[gcol]) : 0.f;
+        for (int c = 0; c < kWideMaxChunks; ++c)
+            pv[k][c] = (ok && c < C) ? load_coherent(part + (size_t)c * Bd + off) : 0.f;
+    }
 #pragma unroll
-        for (int c = 0; c < kWideMaxChunks; ++c) sum += pv[c];
-        if (ok) y[off] = sum;
+    for (int k = 0; k < OPT; ++k) {
+        const int o = tid + k * kWideThreads;
+        const int b = o / kWideDownCols, cc = o - b * kWideDownCols;
+        const int gcol = slab * kWideDownCols + cc;
+        if (b >= B || gcol >= d) continue;
+        float sum = b_down ? half_to_float(b_down[gcol]) : 0.f;
+#pragma unroll
+        for (int c = 0; c < kWideMaxChunks; ++c) sum += pv[k][c];
+        y[(size_t)b * d + gcol] = sum;
     }
     if (tid == 0) tickets[slab] = 0;
 }

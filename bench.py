@@ -315,6 +315,50 @@ def main():
                 "threads": best[1], "calls": best[3],
                 "hybrid_layer_us": round(1e6 * float(np.median(hyb)), 2),
                 "device_only_layer_us": round(elapsed_ms * 1000.0 / (K * L), 2)}
+    # ------------------------------------------------------------------ 16-token batches on MFMA
+    # pi_sparse_ffn_wide over each layer's union of 16 tokens' predicted lists (the masks of the
+    # eager pass above, ORed and compacted outside the timed region), x of those 16 tokens; one
+    # graph of L launches, timed with HIP events on the launch stream.
+    wide = None
+    if B == 1 and R >= 16 and cfg.wtype == synth.F16 and layers[0].slot_of is None:
+        with torch.cuda.stream(stream):
+            idx_w = torch.empty((L, cfg.f), dtype=torch.int32, device=dev)
+            cnt_w = torch.empty((L, 2), dtype=torch.int32, device=dev)
+            x_w = torch.empty((L, 16, cfg.d), dtype=torch.int16, device=dev)
+            for l in range(L):
+                sel = [i for i, (t, ll) in enumerate(cases) if ll == l][:16]
+                union = masks[sel].amax(dim=0).contiguous()
+                _abi.pi_compact(union, cfg.f, None, idx_w[l], cnt_w[l])
+                x_w[l] = xd[[cases[i][0] for i in sel], l, 0]
+            ws_w = torch.empty(_abi.pi_sparse_ffn_wide_workspace_bytes(layers[0].ffn, 16), dtype=torch.uint8,
+                               device=dev)
+            y_w = torch.empty((16, cfg.d), dtype=torch.float32, device=dev)
+
+            def run_wide():
+                for l in range(L):
+                    _abi.pi_sparse_ffn_wide(layers[l].ffn, x_w[l], 16, idx_w[l], cnt_w[l], y_w, ws_w)
+
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                run_wide()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wide_us = e0.elapsed_time(e1) * 1000.0 / L
+            del g
+        n_w = cnt_w[:, 0].cpu().numpy().astype(np.float64)
+        wide_bytes = float((n_w * (in_rows + 1) * rb + 4 * n_w).mean()) + 16 * cfg.d * (2 + 4) + 2 * cfg.d
+        wide = {"batch": 16, "us_per_layer": round(wide_us, 3), "neurons_per_layer": round(float(n_w.mean()), 1),
+                "algorithmic_bytes_per_layer": int(wide_bytes),
+                "gb_per_s": round(wide_bytes / (wide_us * 1e-6) / 1e9, 1),
+                "hbm_frac": round(wide_bytes / (wide_us * 1e-6) / 8e12, 4),
+                "kernels": "k_wide_up + k_wide_down (pi_sparse_ffn_wide, MFMA 16x16x16 f16)"}
+        log(f"16-token sparse FFN (MFMA): {wide_us:.1f} us/layer over {n_w.mean():.0f} neurons")
+
     # ------------------------------------------------------------------ CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -394,6 +438,7 @@ def main():
             "covered_share": round(float(n_act.sum() / max(n_pred.sum(), 1)), 4),
             "down_rows_zero_h_share": round(1.0 - float(n_live.sum()) / max(float(n_act.sum()), 1.0), 4),
             "cold_host": cold,
+            "wide_b16": wide,
         },
     }
     print(json.dumps(out), flush=True)
