@@ -82,7 +82,7 @@ WideGeom wide_geom(const pi_ffn *fn, int B) {
     const int d = fn->d_model;
     g.S = ceil_div(d, kWideDownCols);
     g.C = std::min(kWideMaxChunks, std::max(1, ceil_div(kWideTargetGroups, g.S)));
-    g.hs = ceil_div(std::max(fn->n_slots, 1), 16) * 16;
+    g.hs = ceil_div(std::max(fn->n_slots, 1), 32) * 32;    // k_wide_up writes whole 32-position groups
     g.hi = align_up((size_t)g.S * 4);
     g.lo = g.hi + align_up((size_t)kWideB * g.hs * 2);
     g.part = g.lo + align_up((size_t)kWideB * g.hs * 2);
@@ -575,7 +575,7 @@ int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t
 }
 
 size_t pi_sparse_ffn_wide_workspace_bytes(const pi_ffn *ffn, int32_t batch) {
-    if (check_ffn(ffn) != PI_OK || check_wide_batch(batch) != PI_OK || ffn->wtype != PI_F16) return 0;
+    if (check_ffn(ffn) != PI_OK || check_wide_batch(batch) != PI_OK) return 0;
     return wide_geom(ffn, batch).total;
 }
 
@@ -584,7 +584,6 @@ int pi_sparse_ffn_wide(const pi_ffn *ffn, const void *x, int32_t batch, const in
     int rc = check_ffn(ffn);
     if (rc) return rc;
     if ((rc = check_wide_batch(batch))) return rc;
-    if (ffn->wtype != PI_F16) return PI_ERR_DTYPE;
     if (!x || !idx || !counts || !y) return PI_ERR_NULL;
     if (!aligned16(x)) return PI_ERR_ALIGN;
     const WideGeom g = wide_geom(ffn, batch);
@@ -600,15 +599,23 @@ int pi_sparse_ffn_wide(const pi_ffn *ffn, const void *x, int32_t batch, const in
     const uint8_t *w_in = static_cast<const uint8_t *>(ffn->w_in);
     const uint16_t *xx = static_cast<const uint16_t *>(x), *b_up = static_cast<const uint16_t *>(ffn->b_up);
     const dim3 up_grid(std::max(1, ceil_div(ns, 16)));
-    if (ffn->gated)
-        hipLaunchKernelGGL(k_wide_up<true>, up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx, batch, idx, counts,
-                           ffn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, ffn->act);
+    if (ffn->wtype == PI_Q4_0)
+        hipLaunchKernelGGL((k_wide_up<false, WT_Q4_0, 2>), dim3(std::max(1, ceil_div(ns, 32))), dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
+                           batch, idx, counts, ffn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, ffn->act);
+    else if (ffn->gated)
+        hipLaunchKernelGGL((k_wide_up<true, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
+                           batch, idx, counts, ffn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, ffn->act);
     else
-        hipLaunchKernelGGL(k_wide_up<false>, up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx, batch, idx, counts,
-                           ffn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, ffn->act);
-    hipLaunchKernelGGL(k_wide_down, dim3(g.S, g.C), dim3(kWideThreads), 0, st, static_cast<const uint8_t *>(ffn->w_down_t), rb,
-                       d, batch, idx, counts, ffn->slot_of, f, ns, h_hi, h_lo, g.hs, part, g.C, tickets,
-                       static_cast<const uint16_t *>(ffn->b_down), y);
+        hipLaunchKernelGGL((k_wide_up<false, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
+                           batch, idx, counts, ffn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, ffn->act);
+    const uint8_t *w_dn = static_cast<const uint8_t *>(ffn->w_down_t);
+    const uint16_t *b_dn = static_cast<const uint16_t *>(ffn->b_down);
+    if (ffn->wtype == PI_Q4_0)
+        hipLaunchKernelGGL(k_wide_down<WT_Q4_0>, dim3(g.S, g.C), dim3(kWideThreads), 0, st, w_dn, rb, d, batch, idx,
+                           counts, ffn->slot_of, f, ns, h_hi, h_lo, g.hs, part, g.C, tickets, b_dn, y);
+    else
+        hipLaunchKernelGGL(k_wide_down<WT_F16>, dim3(g.S, g.C), dim3(kWideThreads), 0, st, w_dn, rb, d, batch, idx,
+                           counts, ffn->slot_of, f, ns, h_hi, h_lo, g.hs, part, g.C, tickets, b_dn, y);
     return launch_status();
 }
 

@@ -1,4 +1,4 @@
-// pi_wide.hpp -- the neuron-aware sparse FFN at batches of 9 to 16 tokens, on MFMA.
+// pi_wide.hpp -- the neuron-aware sparse FFN at batches of up to 16 tokens, on MFMA.
 //
 // The sparse operator of the method (PowerInfer, arXiv 2312.12456, method section: only the
 // predicted neurons' rows are read and computed) is, at a batch of B tokens, a contraction over
@@ -54,7 +54,7 @@ __device__ __forceinline__ f4 mfma16(uint32_t a0, uint32_t a1, uint32_t b0, uint
 // of a block's loads are in flight together; x is read through a buffer resource (a token >= B or
 // a column past d reads zero).  Workgroup 0 also clears `zero_ptr[0..nzero)` (the down kernel's
 // slab tickets); the down kernel always runs after this one on the same stream.
-template <bool GATED>
+template <bool GATED, int WT, int NT>
 __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restrict__ w_in, int64_t row_bytes, int d,
                                                  const uint16_t *__restrict__ b_up, const uint16_t *__restrict__ x,
                                                  int B, const int32_t *__restrict__ idx,
@@ -62,22 +62,71 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
                                                  const int32_t *__restrict__ slot_of, int f, int n_slots,
                                                  uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int hs,
                                                  int32_t *__restrict__ zero_ptr, int nzero, int act) {
-    __shared__ f4 red[GATED ? 2 : 1][kWideWaves][kWave];
+    __shared__ f4 red[GATED ? 2 : NT][kWideWaves][kWave];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     if (blockIdx.x == 0)
         for (int t = tid; t < nzero; t += blockDim.x) zero_ptr[t] = 0;
     const int n = min(max(counts[0], 0), n_slots);
-    const int t0 = blockIdx.x * 16;
+    const int t0 = blockIdx.x * 16 * NT;
     if (t0 >= n) return;                                         // workgroup-uniform
     const int r = lane & 15, g = lane >> 4;
+    int sl[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        const int pu = t0 + 16 * u + r;
+        sl[u] = pu < n ? slot_of_id(idx[pu], slot_of, f, n_slots) : -1;
+    }
+    const int s = sl[0];
     const int pos = t0 + r;
-    const int s = pos < n ? slot_of_id(idx[pos], slot_of, f, n_slots) : -1;
     const int64_t stride = row_bytes * (GATED ? 2 : 1);
     const uint8_t *row = w_in + (int64_t)(s >= 0 ? s : 0) * stride;
     const __amdgpu_buffer_rsrc_t xr = buf_rsrc(x, (uint32_t)B * (uint32_t)d * 2u);
     const uint32_t xrow = r < B ? (uint32_t)r * (uint32_t)d * 2u : kOOB;
     f4 au = {0.f, 0.f, 0.f, 0.f}, ag = {0.f, 0.f, 0.f, 0.f};
-    for (int blk = wave * kWideUpCols; blk < d; blk += kWideWaves * kWideUpCols) {
+    f4 aq[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) aq[u] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int blk = wave * kWideUpCols; WT == WT_Q4_0 && blk < d; blk += kWideWaves * kWideUpCols) {
+        // Q4_0 (d % 256 == 0, so every block of the 256 columns exists): lane group g takes the
+        // 32-weight blocks blk/32 + g + 4j (j < 2) of each of its NT rows, one 16-byte code load and
+        // one scale each; the codes become exact fp16 (code - 8) pairs, times the block's scale (one
+        // fp16 rounding), and x -- read once for the NT rows -- is re-paired to the codes' order, so
+        // each code word feeds two MFMAs
+        uint4 cw[NT][2], xq[2][4];
+        uint32_t sc[NT][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int kb = blk / 32 + g + 4 * j;
+#pragma unroll
+            for (int u = 0; u < NT; ++u) {
+                const uint8_t *ru = w_in + (int64_t)(sl[u] >= 0 ? sl[u] : 0) * stride;
+                cw[u][j] = ld16(ru + (int64_t)kb * 16);
+                sc[u][j] = *reinterpret_cast<const uint16_t *>(ru + d / 2 + (int64_t)kb * 2);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xq[j][i] = bld16(xr, xrow + (uint32_t)(kb * 32 + 8 * i) * 2u);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 xp = pair_for_q4(xq[j][q]);
+#pragma unroll
+                for (int u = 0; u < NT; ++u) {
+                    const h2 s2 = __builtin_bit_cast(h2, sl[u] >= 0 ? (sc[u][j] | (sc[u][j] << 16)) : 0u);
+                    const uint32_t wd = q == 0 ? cw[u][j].x : q == 1 ? cw[u][j].y : q == 2 ? cw[u][j].z : cw[u][j].w;
+                    uint32_t w[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        w[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, q4pair(wd, 4 * p)) * s2);
+                    aq[u] = mfma16(xp.x, xp.y, w[0], w[1], aq[u]);
+                    aq[u] = mfma16(xp.z, xp.w, w[2], w[3], aq[u]);
+                }
+            }
+        }
+    }
+    if (WT == WT_Q4_0) au = aq[0];
+    for (int blk = wave * kWideUpCols; WT == WT_F16 && blk < d; blk += kWideWaves * kWideUpCols) {
         uint4 wu[8], wg[8], xv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -108,31 +157,37 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
     }
     red[0][wave][lane] = au;
     if (GATED) red[GATED ? 1 : 0][wave][lane] = ag;
+#pragma unroll
+    for (int u = 1; u < NT; ++u) red[GATED ? 0 : u][wave][lane] = aq[u];
     __syncthreads();
-    // thread (v, l) of the first four waves: D element v of lane l = token 4(l/16) + v, position
-    // t0 + l%16 -- the position whose slot this thread looked up itself (s)
-    if (tid >= 4 * kWave) return;
-    const int v = tid / kWave, l = lane;
+    // thread (tile, v, l) of the first 4*NT waves: D element v of lane l of that tile = token
+    // 4(l/16) + v, position t0 + 16*tile + l%16 -- a position whose slot this thread looked up
+    // itself (sl[tile])
+    if (tid >= 4 * NT * kWave) return;
+    const int tile = tid / (4 * kWave), v = (tid / kWave) & 3, l = lane;
     const int b = 4 * (l >> 4) + v;
     float u = 0.f, gg = 0.f;
 #pragma unroll
     for (int w = 0; w < kWideWaves; ++w) {
-        u += red[0][w][l][v];
+        u += red[GATED ? 0 : tile][w][l][v];
         if (GATED) gg += red[GATED ? 1 : 0][w][l][v];
     }
     float hv;
     if (GATED) {
         hv = fmaxf(gg, 0.f) * u;
     } else {
-        const float bias = (b_up != nullptr && s >= 0) ? half_to_float(b_up[s]) : 0.f;
+        const int st = tile == 0 ? sl[0] : sl[NT - 1];
+        const float bias = (b_up != nullptr && st >= 0) ? half_to_float(b_up[st]) : 0.f;
         hv = fmaxf(u + bias, 0.f);
         if (act) hv *= hv;                                       // squared ReLU
     }
-    if (s < 0 || b >= B) hv = 0.f;
+    const int st = tile == 0 ? sl[0] : sl[NT - 1];
+    if (st < 0 || b >= B) hv = 0.f;
+    const int pt = pos + 16 * tile;
     const f16 hi = (f16)hv;
     const f16 lo = (f16)(hv - (float)hi);
-    h_hi[(size_t)b * hs + pos] = __builtin_bit_cast(uint16_t, hi);
-    h_lo[(size_t)b * hs + pos] = __builtin_bit_cast(uint16_t, lo);
+    h_hi[(size_t)b * hs + pt] = __builtin_bit_cast(uint16_t, hi);
+    h_lo[(size_t)b * hs + pt] = __builtin_bit_cast(uint16_t, lo);
 }
 
 // y over (128-column slab, neuron chunk) tiles.  The chunk's 16-position steps are split into eight
@@ -145,6 +200,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
 // to finish a slab (slab ticket) sums the partials in chunk order and adds b_down, every thread
 // issuing all of its loads before the first add.  Tickets must be zero on entry (k_wide_up clears
 // them) and are left zero.
+template <int WT>
 __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__restrict__ w_dn, int64_t row_bytes,
                                                             int d, int B, const int32_t *__restrict__ idx,
                                                             const int32_t *__restrict__ counts,
@@ -178,6 +234,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
         // (its positions looked up as -1) reads slot 0 and the last valid step's h, and is zeroed
         int sv[4][4];
         uint4 wv[4][4];
+        uint32_t qc[4][4], qs[4][4];                             // Q4_0: code word and scale
         uint2 ahi[4], alo[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -185,7 +242,14 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 sv[q][v] = __shfl(sl, q * 16 + 4 * g + v);
-                wv[q][v] = ld16(w_dn + (int64_t)(sv[q][v] >= 0 ? sv[q][v] : 0) * row_bytes + coff);
+                const uint8_t *rw = w_dn + (int64_t)(sv[q][v] >= 0 ? sv[q][v] : 0) * row_bytes;
+                if (WT == WT_F16) {
+                    wv[q][v] = ld16(rw + coff);
+                } else {
+                    const int cq = colok ? col : 0;
+                    qc[q][v] = *reinterpret_cast<const uint32_t *>(rw + cq / 2);
+                    qs[q][v] = *reinterpret_cast<const uint16_t *>(rw + d / 2 + (cq / 32) * 2);
+                }
             }
             const size_t ho = (size_t)r * hs + (size_t)sq * 16 + 4 * g;
             ahi[q] = *reinterpret_cast<const uint2 *>(h_hi + ho);
@@ -198,8 +262,21 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
                 alo[q] = make_uint2(0u, 0u);
             }
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-                if (sv[q][v] < 0 || !colok) wv[q][v] = zero4();
+            for (int v = 0; v < 4; ++v) {
+                const bool okv = sv[q][v] >= 0 && colok;
+                if (WT == WT_F16) {
+                    if (!okv) wv[q][v] = zero4();
+                } else {
+                    // exact (code - 8) pairs times the row's block scale: halves in the order
+                    // (w0, w4, w1, w5, w2, w6, w3, w7) of the 8 columns
+                    const h2 s2 = __builtin_bit_cast(h2, okv ? (qs[q][v] | (qs[q][v] << 16)) : 0u);
+                    uint32_t w[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        w[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, q4pair(qc[q][v], 4 * p)) * s2);
+                    wv[q][v] = make_uint4(w[0], w[1], w[2], w[3]);
+                }
+            }
             const uint32_t wq[4][4] = {{wv[q][0].x, wv[q][0].y, wv[q][0].z, wv[q][0].w},
                                        {wv[q][1].x, wv[q][1].y, wv[q][1].z, wv[q][1].w},
                                        {wv[q][2].x, wv[q][2].y, wv[q][2].z, wv[q][2].w},
@@ -229,11 +306,14 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
         for (int e = 0; e < 8; ++e) red[wave][e][lane] = acc[e] + red[wave][e][lane];
     }
     __syncthreads();
-    // output (token b, column cc of the slab): lane 16(b/4) + cc/8, MFMA e = cc%8, element b%4
+    // output (token b, column cc of the slab): lane 16(b/4) + cc/8, element b%4 of MFMA e, where
+    // e = cc%8 for fp16 rows and the position of column cc%8 in the Q4_0 half order
     const int Bd = B * d;
     for (int o = tid; o < B * kWideDownCols; o += blockDim.x) {
         const int b = o / kWideDownCols, cc = o - b * kWideDownCols;
-        const int ln = 16 * (b >> 2) + (cc >> 3), e = cc & 7, v = b & 3;
+        const int c8 = cc & 7;
+        const int e = WT == WT_F16 ? c8 : (((c8 & 3) << 1) | (c8 >> 2));
+        const int ln = 16 * (b >> 2) + (cc >> 3), v = b & 3;
         const int gcol = slab * kWideDownCols + cc;
         if (gcol < d)
             store_coherent(part + (size_t)ck * Bd + (size_t)b * d + gcol,

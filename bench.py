@@ -320,7 +320,7 @@ def main():
     # eager pass above, ORed and compacted outside the timed region), x of those 16 tokens; one
     # graph of L launches, timed with HIP events on the launch stream.
     wide = None
-    if B == 1 and R >= 16 and cfg.wtype == synth.F16 and layers[0].slot_of is None:
+    if B == 1 and R >= 16 and layers[0].slot_of is None:
         with torch.cuda.stream(stream):
             idx_w = torch.empty((L, cfg.f), dtype=torch.int32, device=dev)
             cnt_w = torch.empty((L, 2), dtype=torch.int32, device=dev)

@@ -137,8 +137,9 @@ int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t
  * batches where the per-token GEMV form would be bound by the vector ALU (the method's sparse
  * operator over the predicted neurons, method section, computed as [16 x n] and [16 x d]
  * products over the gathered rows with the batch padded to 16).  Arguments, idx/counts rules and
- * y as in pi_sparse_ffn, with 1 <= batch <= PI_MAX_WIDE_BATCH (PI_ERR_BATCH otherwise) and fp16
- * weights only (PI_ERR_DTYPE for Q4_0).  Two kernels; the workspace of
+ * y as in pi_sparse_ffn, with 1 <= batch <= PI_MAX_WIDE_BATCH (PI_ERR_BATCH otherwise); fp16 and
+ * Q4_0 rows (Q4_0 weights enter the MFMA as fp16 scale * (code - 8), rounded once to fp16).
+ * Two kernels; the workspace of
  * pi_sparse_ffn_wide_workspace_bytes(ffn, batch) bytes (16-byte aligned) needs no zero fill, holds
  * no status word, and must not be shared by calls in flight at the same time.  h passes between
  * the kernels as an fp16 pair (h = hi + lo), so |h| must stay below 65504.  y is deterministic

@@ -111,11 +111,13 @@ def test_sparse_ffn_wide_rejects(L):
     big = wsz(ctypes.byref(f), 16)
     assert big > 0 and wsz(ctypes.byref(f), 1) < big                                  # partials scale with batch
     assert wsz(ctypes.byref(f), 17) == 0 and wsz(ctypes.byref(f), 0) == 0
-    assert wsz(ctypes.byref(ffn(d=1024, wtype=_abi.PI_Q4_0)), 16) == 0                # fp16 weights only
+    assert wsz(ctypes.byref(ffn(d=1024, wtype=_abi.PI_Q4_0)), 16) > 0
+    assert wsz(ctypes.byref(ffn(d=1000, wtype=_abi.PI_Q4_0)), 16) == 0               # Q4_0 needs d % 256
     call = lambda ff, x=A, B=16, ws=A, n=big: L.pi_sparse_ffn_wide(ff, x, B, A, A, A, ws, n, None)
     assert call(None) == _abi.PI_ERR_NULL
     assert call(ctypes.byref(ffn(w_dn=0))) == _abi.PI_ERR_NULL
-    assert call(ctypes.byref(ffn(wtype=_abi.PI_Q4_0))) == _abi.PI_ERR_DTYPE
+    assert call(ctypes.byref(ffn(wtype=3))) == _abi.PI_ERR_DTYPE
+    assert call(ctypes.byref(ffn(gated=1, wtype=_abi.PI_Q4_0))) == _abi.PI_ERR_DTYPE
     assert call(ctypes.byref(ffn(gated=1, act=_abi.PI_ACT_SQUARED_RELU))) == _abi.PI_ERR_DTYPE
     assert call(ctypes.byref(ffn(d=1001))) == _abi.PI_ERR_SHAPE
     assert call(ctypes.byref(f), B=17) == _abi.PI_ERR_BATCH and call(ctypes.byref(f), B=0) == _abi.PI_ERR_BATCH

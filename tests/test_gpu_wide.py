@@ -1,4 +1,5 @@
-"""pi_sparse_ffn_wide (the sparse FFN at up to 16 tokens on MFMA tiles) against the oracle -- MI355X.
+"""pi_sparse_ffn_wide (the sparse FFN at up to 16 tokens on MFMA tiles; fp16 and Q4_0 rows) against
+the oracle -- MI355X.
 
 The operation is the method's sparse operator over the listed neurons (PowerInfer, method
 section), exactly as pi_sparse_ffn computes it; only the batch range (1..16) and the kernels differ.
@@ -18,7 +19,7 @@ from gpu_util import announce, check_y, to_dev
 
 pytestmark = pytest.mark.gpu
 
-F16 = synth.F16
+F16, Q4 = synth.F16, synth.Q4_0
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -28,19 +29,23 @@ def _gpu():
     _abi.lib()
 
 
-WIDE_CASES = [  # (d, f, gated, act, B, active share)
-    (1024, 4096, False, 0, 16, 0.3), (4096, 3001, True, 0, 16, 0.2), (2048, 2500, False, 1, 16, 0.25),
-    (1024, 1000, False, 0, 9, 0.5), (1000, 777, True, 0, 12, 0.4), (768, 2049, False, 0, 13, 1.0),
-    (8192, 600, False, 0, 16, 0.2), (4096, 11008, True, 0, 16, 0.1), (1024, 1500, False, 0, 1, 0.1),
-    (512, 700, True, 0, 8, 0.3), (2048, 4000, False, 1, 4, 0.2),
+WIDE_CASES = [  # (d, f, gated, wtype, act, B, active share)
+    (1024, 4096, False, F16, 0, 16, 0.3), (4096, 3001, True, F16, 0, 16, 0.2), (2048, 2500, False, F16, 1, 16, 0.25),
+    (1024, 1000, False, F16, 0, 9, 0.5), (1000, 777, True, F16, 0, 12, 0.4), (768, 2049, False, F16, 0, 13, 1.0),
+    (8192, 600, False, F16, 0, 16, 0.2), (4096, 11008, True, F16, 0, 16, 0.1), (1024, 1500, False, F16, 0, 1, 0.1),
+    (512, 700, True, F16, 0, 8, 0.3), (2048, 4000, False, F16, 1, 4, 0.2),
+    # Q4_0 rows (32-weight blocks with an fp16 scale)
+    (1024, 1500, False, Q4, 0, 16, 0.3), (12288, 700, False, Q4, 0, 16, 0.2), (256, 3000, False, Q4, 1, 10, 0.5),
+    (2048, 999, False, Q4, 0, 8, 0.15), (768, 400, False, Q4, 0, 1, 1.0),
     # edges: the smallest d_model, d past a 256-column block, a single neuron, an empty list
-    (8, 40, False, 0, 16, 0.5), (8, 33, True, 0, 16, 1.0), (264, 100, False, 0, 11, 0.6), (256, 1, False, 0, 16, 1.0),
-    (512, 300, False, 0, 16, 0.0),
+    (8, 40, False, F16, 0, 16, 0.5), (8, 33, True, F16, 0, 16, 1.0), (264, 100, False, F16, 0, 11, 0.6),
+    (256, 1, False, F16, 0, 16, 1.0), (512, 300, False, F16, 0, 16, 0.0), (256, 1, False, Q4, 0, 16, 1.0),
+    (512, 300, False, Q4, 0, 16, 0.0),
 ]
 
 
-def _layer(d, f, gated, act, seed):
-    cfg = synth.custom_config(d, f, 8, gated=gated, wtype=F16, bias_up=not gated, seed=seed, act=act)
+def _layer(d, f, gated, act, seed, wtype=F16):
+    cfg = synth.custom_config(d, f, 8, gated=gated, wtype=wtype, bias_up=not gated, seed=seed, act=act)
     w_in, w_dn, b_up, _ = synth.make_ffn(cfg, 0, None, bias_scale=1.0)
     b_down = synth.normal_f16(seed, 0, synth.T_BDOWN, 1, d, 1.0)[0]
     return cfg, w_in, w_dn, b_up, b_down
@@ -61,23 +66,28 @@ def _run_wide(dl, x, B, idx, n_listed=None):
     return yh[: B * d].reshape(B, d), (x, idx_d, counts, ws)
 
 
-@pytest.mark.parametrize("d,f,gated,act,B,share", WIDE_CASES)
-def test_sparse_ffn_wide(d, f, gated, act, B, share):
-    announce(f"sparse_ffn_wide d={d} f={f} gated={gated} act={act} B={B} share={share}")
-    cfg, w_in, w_dn, b_up, b_down = _layer(d, f, gated, act, seed=d * 5 + f)
+@pytest.mark.parametrize("d,f,gated,wtype,act,B,share", WIDE_CASES)
+def test_sparse_ffn_wide(d, f, gated, wtype, act, B, share):
+    announce(f"sparse_ffn_wide d={d} f={f} gated={gated} wtype={wtype} act={act} B={B} share={share}")
+    cfg, w_in, w_dn, b_up, b_down = _layer(d, f, gated, act, seed=d * 5 + f, wtype=wtype)
     rng = np.random.default_rng(d + f + B)
     idx = np.sort(rng.choice(f, int(round(share * f)), replace=False)).astype(np.int32)
     x = synth.normal_f16(cfg.seed, 0, synth.T_X, B, d, 1.0)
-    y_ref = oracle.sparse_ffn(d, f, gated, F16, w_in, w_dn, x, idx, b_up=b_up, b_down=b_down, act=act)
+    y_ref = oracle.sparse_ffn(d, f, gated, wtype, w_in, w_dn, x, idx, b_up=b_up, b_down=b_down, act=act)
+    # poison every row that is not listed (fp16: NaN weights; Q4_0: NaN scales)
     w_in_p, w_dn_p = w_in.copy(), w_dn.copy()
     out = np.setdiff1d(np.arange(f), idx)
-    w_in_p[out] = 0x7E00
-    w_dn_p[out] = 0x7E00
+    if wtype == F16:
+        w_in_p[out] = 0x7E00
+        w_dn_p[out] = 0x7E00
+    else:
+        w_in_p[out, d // 2:] = 0x7E
+        w_dn_p[out, d // 2:] = 0x7E
     dl = DeviceLayer(p1=np.zeros((8, d), np.uint16), p2=np.zeros((f, 8), np.uint16), c=np.zeros(f, np.uint16),
-                     w_in=w_in_p, w_down_t=w_dn_p, d_model=d, d_ffn=f, gated=gated, wtype=F16, b_up=b_up,
+                     w_in=w_in_p, w_down_t=w_dn_p, d_model=d, d_ffn=f, gated=gated, wtype=wtype, b_up=b_up,
                      b_down=b_down, act=act)
     y, _ = _run_wide(dl, x, B, idx)
-    check_y(y, y_ref, F16, "sparse_ffn_wide")
+    check_y(y, y_ref, wtype, "sparse_ffn_wide")
     y2, _ = _run_wide(dl, x, B, idx)
     assert np.array_equal(y, y2), "not bitwise repeatable"
     if B <= _abi.PI_MAX_BATCH:
@@ -87,7 +97,7 @@ def test_sparse_ffn_wide(d, f, gated, act, B, share):
         idx_d = to_dev(idx) if idx.size else torch.zeros(1, dtype=torch.int32, device="cuda")
         _abi.pi_sparse_ffn(dl.ffn, to_dev(x), B, idx_d, counts, yv, ws)
         torch.cuda.synchronize()
-        check_y(y, yv.cpu().numpy().reshape(B, d).astype(np.float64), F16, "wide vs GEMV form")
+        check_y(y, yv.cpu().numpy().reshape(B, d).astype(np.float64), wtype, "wide vs GEMV form")
 
 
 def test_sparse_ffn_wide_placement_and_bad_entries():
@@ -128,6 +138,23 @@ def test_sparse_ffn_wide_full_shape_sampled():
     for b in (0, 5, 10, 15):
         y_ref = oracle.sparse_ffn(d, f, True, F16, w_in, w_dn, x[b:b + 1], idx, b_down=b_down)
         check_y(y[b:b + 1], y_ref, F16, f"full shape token {b}")
+
+
+def test_sparse_ffn_wide_q4_full_shape_sampled():
+    """The 175B-shaped Q4_0 FFN (d 12288, 49152 neurons) at 16 tokens with a 15% union: y against
+    the oracle on two sampled tokens."""
+    d, f, B = 12288, 49152, 16
+    announce(f"sparse_ffn_wide Q4_0 full shape d={d} f={f} B={B}")
+    cfg, w_in, w_dn, b_up, b_down = _layer(d, f, False, 0, seed=9, wtype=Q4)
+    rng = np.random.default_rng(12)
+    idx = np.sort(rng.choice(f, int(0.15 * f), replace=False)).astype(np.int32)
+    x = synth.normal_f16(cfg.seed, 0, synth.T_X, B, d, 1.0)
+    dl = DeviceLayer(p1=np.zeros((8, d), np.uint16), p2=np.zeros((f, 8), np.uint16), c=np.zeros(f, np.uint16),
+                     w_in=w_in, w_down_t=w_dn, d_model=d, d_ffn=f, gated=False, wtype=Q4, b_up=b_up, b_down=b_down)
+    y, _ = _run_wide(dl, x, B, idx)
+    for b in (3, 14):
+        y_ref = oracle.sparse_ffn(d, f, False, Q4, w_in, w_dn, x[b:b + 1], idx, b_up=b_up, b_down=b_down)
+        check_y(y[b:b + 1], y_ref, Q4, f"Q4_0 full shape token {b}")
 
 
 def test_sparse_ffn_wide_rejects():
