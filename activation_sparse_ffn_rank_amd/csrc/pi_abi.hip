@@ -80,7 +80,7 @@ struct WideGeom {
 WideGeom wide_geom(const pi_ffn *fn, int B) {
     WideGeom g{};
     const int d = fn->d_model;
-    g.S = ceil_div(d, kWideDownCols);
+    g.S = ceil_div(d, 16 * wide_down_cpl(fn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16));
     g.C = std::min(kWideMaxChunks, std::max(1, ceil_div(kWideTargetGroups, g.S)));
     g.hs = ceil_div(std::max(fn->n_slots, 1), 32) * 32;    // k_wide_up writes whole 32-position groups
     g.hi = align_up((size_t)g.S * 4);

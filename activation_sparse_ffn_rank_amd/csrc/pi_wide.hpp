@@ -18,7 +18,7 @@
 //                the eight waves taking interleaved 256-column blocks, summed in LDS; writes h
 //                as fp16 hi + fp16 lo parts (h = hi + lo to ~2^-22 relative), so that feeding h to
 //                the f16 MFMA of the down step costs no accuracy.
-//   k_wide_down  (128-column slab, neuron chunk) tiles: Y tile [16 tokens x 128 columns] over the
+//   k_wide_down  (slab, neuron chunk) tiles: Y tile [16 tokens x 128 (Q4_0: 256) columns] over the
 //                chunk's neurons, waves summed in LDS, chunk partials summed in chunk order by the
 //                last workgroup of each slab (deterministic), plus b_down.
 #pragma once
@@ -32,7 +32,8 @@ namespace pik {
 
 constexpr int kWideB = 16;            // the padded batch: one MFMA M (or N) dimension
 constexpr int kWideUpCols = 256;      // columns per k_wide_up block (8 column groups of 32)
-constexpr int kWideDownCols = 128;    // columns per k_wide_down slab (16 lanes x 8 columns)
+// columns per lane per row in k_wide_down (a slab is 16 lanes wide)
+constexpr int wide_down_cpl(int wt) { return wt == WT_Q4_0 ? 16 : 8; }
 constexpr int kWideMaxChunks = 16;    // chunk partials per slab summed by the last workgroup
 constexpr int kWideWaves = 8;         // waves per workgroup in both kernels
 constexpr int kWideThreads = kWideWaves * kWave;
@@ -190,16 +191,17 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
     h_lo[(size_t)b * hs + pt] = __builtin_bit_cast(uint16_t, lo);
 }
 
-// y over (128-column slab, neuron chunk) tiles.  The chunk's 16-position steps are split into eight
-// contiguous runs, one per wave.  In a step, lane l reads columns c0 + 8(l%16) .. +8 of the rows of
-// positions 4(l/16) + v (v < 4; 16 lanes cover 256 contiguous bytes of a row) and h of token l%16
-// at the same four positions; MFMA e (e < 8) then takes half e of each of the four row vectors as
-// its B operand, so its D holds columns c0 + 8(l%16) + e.  Slots are looked up 64 positions at a
-// time, one lane per position, and handed to the lanes that need them by ds_bpermute.  The waves'
-// tiles meet in LDS, each chunk's partial goes to `part` ([C][B][d] fp32), and the last workgroup
-// to finish a slab (slab ticket) sums the partials in chunk order and adds b_down, every thread
-// issuing all of its loads before the first add.  Tickets must be zero on entry (k_wide_up clears
-// them) and are left zero.
+// y over (slab, neuron chunk) tiles; a slab is 16 lanes x CPL columns (fp16: 8 columns, one 16-byte
+// load per row; Q4_0: 16 columns, 8 code bytes and a scale per row, so 16 lanes read a whole 128-byte
+// line of a row's codes).  The chunk's 16-position steps are split into eight contiguous runs, one
+// per wave.  In a step, lane l reads its CPL columns of the rows of positions 4(l/16) + v (v < 4)
+// and h of token l%16 at the same four positions; MFMA e then takes half e of each of the four
+// rows' decoded vectors as its B operand.  Slots are looked up 64 positions at a time, one lane per
+// position, and handed to the lanes that need them by ds_bpermute.  The waves' tiles meet in LDS
+// (eight MFMA outputs at a time), each chunk's partial goes to `part` ([C][B][d] fp32), and the last
+// workgroup to finish a slab (slab ticket) sums the partials in chunk order and adds b_down, each
+// thread issuing the loads of four outputs before the first add.  Tickets must be zero on entry
+// (k_wide_up clears them) and are left zero.
 template <int WT>
 __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__restrict__ w_dn, int64_t row_bytes,
                                                             int d, int B, const int32_t *__restrict__ idx,
@@ -211,6 +213,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
                                                             int32_t *__restrict__ tickets,
                                                             const uint16_t *__restrict__ b_down,
                                                             float *__restrict__ y) {
+    constexpr int CPL = wide_down_cpl(WT), NW = CPL / 2, SC = 16 * CPL;
     __shared__ f4 red[4][8][kWave];
     __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -220,12 +223,12 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
     const int c_lo = (int)((int64_t)T * ck / C), c_hi = (int)((int64_t)T * (ck + 1) / C);
     const int w_lo = c_lo + (c_hi - c_lo) * wave / kWideWaves, w_hi = c_lo + (c_hi - c_lo) * (wave + 1) / kWideWaves;
     const int r = lane & 15, g = lane >> 4;
-    const int col = slab * kWideDownCols + 8 * r;
-    const bool colok = col < d;
-    const int64_t coff = (int64_t)(colok ? col : 0) * 2;
-    f4 acc[8];
+    const int col = slab * SC + CPL * r;
+    const bool colok = col < d;                                  // d % 8 (fp16) or % 256 (Q4_0): all or none
+    const int cq = colok ? col : 0;
+    f4 acc[CPL];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < CPL; ++e) acc[e] = f4{0.f, 0.f, 0.f, 0.f};
 
     for (int st0 = w_lo; st0 < w_hi; st0 += 4) {                 // four steps per slot lookup
         const int p = st0 * 16 + lane;                           // this lane's lookup position
@@ -233,8 +236,9 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
         // every load of the four steps goes out before the first MFMA; a step past the wave's run
         // (its positions looked up as -1) reads slot 0 and the last valid step's h, and is zeroed
         int sv[4][4];
-        uint4 wv[4][4];
-        uint32_t qc[4][4], qs[4][4];                             // Q4_0: code word and scale
+        uint4 wv[4][4];                                          // fp16: 8 columns
+        uint2 qc[4][4];                                          // Q4_0: 16 columns of codes
+        uint32_t qs[4][4];                                       // Q4_0: their block scale
         uint2 ahi[4], alo[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -244,10 +248,9 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
                 sv[q][v] = __shfl(sl, q * 16 + 4 * g + v);
                 const uint8_t *rw = w_dn + (int64_t)(sv[q][v] >= 0 ? sv[q][v] : 0) * row_bytes;
                 if (WT == WT_F16) {
-                    wv[q][v] = ld16(rw + coff);
+                    wv[q][v] = ld16(rw + (int64_t)cq * 2);
                 } else {
-                    const int cq = colok ? col : 0;
-                    qc[q][v] = *reinterpret_cast<const uint32_t *>(rw + cq / 2);
+                    qc[q][v] = *reinterpret_cast<const uint2 *>(rw + cq / 2);
                     qs[q][v] = *reinterpret_cast<const uint16_t *>(rw + d / 2 + (cq / 32) * 2);
                 }
             }
@@ -261,28 +264,28 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
                 ahi[q] = make_uint2(0u, 0u);
                 alo[q] = make_uint2(0u, 0u);
             }
+            uint32_t wq[4][NW];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const bool okv = sv[q][v] >= 0 && colok;
                 if (WT == WT_F16) {
-                    if (!okv) wv[q][v] = zero4();
+                    const uint4 u = okv ? wv[q][v] : zero4();
+                    wq[v][0] = u.x; wq[v][1] = u.y; wq[v][2] = u.z; wq[v][3] = u.w;
                 } else {
-                    // exact (code - 8) pairs times the row's block scale: halves in the order
-                    // (w0, w4, w1, w5, w2, w6, w3, w7) of the 8 columns
+                    // exact (code - 8) pairs times the row's block scale; code word k gives the
+                    // halves (w8k, w8k+4, w8k+1, w8k+5, w8k+2, w8k+6, w8k+3, w8k+7) of its 8 columns
                     const h2 s2 = __builtin_bit_cast(h2, okv ? (qs[q][v] | (qs[q][v] << 16)) : 0u);
-                    uint32_t w[4];
+                    const uint32_t words[2] = {qc[q][v].x, qc[q][v].y};
 #pragma unroll
-                    for (int p = 0; p < 4; ++p)
-                        w[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, q4pair(qc[q][v], 4 * p)) * s2);
-                    wv[q][v] = make_uint4(w[0], w[1], w[2], w[3]);
+                    for (int k = 0; k < 2; ++k)
+#pragma unroll
+                        for (int pp = 0; pp < 4; ++pp)
+                            wq[v][4 * k + pp] = __builtin_bit_cast(
+                                uint32_t, __builtin_bit_cast(h2, q4pair(words[k], 4 * pp)) * s2);
                 }
             }
-            const uint32_t wq[4][4] = {{wv[q][0].x, wv[q][0].y, wv[q][0].z, wv[q][0].w},
-                                       {wv[q][1].x, wv[q][1].y, wv[q][1].z, wv[q][1].w},
-                                       {wv[q][2].x, wv[q][2].y, wv[q][2].z, wv[q][2].w},
-                                       {wv[q][3].x, wv[q][3].y, wv[q][3].z, wv[q][3].w}};
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
+            for (int c = 0; c < NW; ++c) {
                 // halves 2c (low) and 2c+1 (high) of the four rows, packed as k = 0..3
                 const uint32_t e0 = (wq[0][c] & 0xffffu) | (wq[1][c] << 16);
                 const uint32_t e1 = (wq[2][c] & 0xffffu) | (wq[3][c] << 16);
@@ -295,58 +298,64 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
             }
         }
     }
-    // waves 4..7 hand their tiles to waves 0..3, which then hold pairwise sums
-    if (wave >= 4) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) red[wave - 4][e][lane] = acc[e];
-    }
-    __syncthreads();
-    if (wave < 4) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) red[wave][e][lane] = acc[e] + red[wave][e][lane];
-    }
-    __syncthreads();
-    // output (token b, column cc of the slab): lane 16(b/4) + cc/8, element b%4 of MFMA e, where
-    // e = cc%8 for fp16 rows and the position of column cc%8 in the Q4_0 half order
     const int Bd = B * d;
-    for (int o = tid; o < B * kWideDownCols; o += blockDim.x) {
-        const int b = o / kWideDownCols, cc = o - b * kWideDownCols;
-        const int c8 = cc & 7;
-        const int e = WT == WT_F16 ? c8 : (((c8 & 3) << 1) | (c8 >> 2));
-        const int ln = 16 * (b >> 2) + (cc >> 3), v = b & 3;
-        const int gcol = slab * kWideDownCols + cc;
-        if (gcol < d)
-            store_coherent(part + (size_t)ck * Bd + (size_t)b * d + gcol,
-                           red[0][e][ln][v] + red[1][e][ln][v] + red[2][e][ln][v] + red[3][e][ln][v]);
+#pragma unroll
+    for (int hh = 0; hh < CPL / 8; ++hh) {                       // MFMA outputs 8hh .. 8hh+7
+        if (hh > 0) __syncthreads();                             // the previous half has been read
+        // waves 4..7 hand their tiles to waves 0..3, which then hold pairwise sums
+        if (wave >= 4) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[wave - 4][e][lane] = acc[8 * hh + e];
+        }
+        __syncthreads();
+        if (wave < 4) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[wave][e][lane] = acc[8 * hh + e] + red[wave][e][lane];
+        }
+        __syncthreads();
+        // output (token b, lane column lc, column c8 of the half): lane 16(b/4) + lc, element b%4
+        // of MFMA e, where e = c8 for fp16 rows and the position of column c8 in the Q4_0 half order
+        for (int o = tid; o < B * 128; o += blockDim.x) {
+            const int b = o >> 7, lc = (o >> 3) & 15, c8 = o & 7;
+            const int e = WT == WT_F16 ? c8 : (((c8 & 3) << 1) | (c8 >> 2));
+            const int ln = 16 * (b >> 2) + lc, v = b & 3;
+            const int gcol = slab * SC + lc * CPL + 8 * hh + c8;
+            if (gcol < d)
+                store_coherent(part + (size_t)ck * Bd + (size_t)b * d + gcol,
+                               red[0][e][ln][v] + red[1][e][ln][v] + red[2][e][ln][v] + red[3][e][ln][v]);
+        }
     }
     wait_stores_done();                                          // this thread's partials are out
     __syncthreads();                                             // ... and so are everyone's
     if (tid == 0) s_last = (atomicAdd(&tickets[slab], 1) == C - 1);
     __syncthreads();
     if (!s_last) return;
-    constexpr int OPT = kWideB * kWideDownCols / kWideThreads;   // outputs per thread
-    float pv[OPT][kWideMaxChunks];
+    constexpr int OPT = kWideB * SC / kWideThreads;              // outputs per thread (4 or 8)
 #pragma unroll
-    for (int k = 0; k < OPT; ++k) {
-        const int o = tid + k * kWideThreads;
-        const int b = o / kWideDownCols, cc = o - b * kWideDownCols;
-        const int gcol = slab * kWideDownCols + cc;
-        const bool ok = b < B && gcol < d;
-        const size_t off = ok ? (size_t)b * d + gcol : 0;
+    for (int k0 = 0; k0 < OPT; k0 += 4) {
+        float pv[4][kWideMaxChunks];
 #pragma unroll
-        for (int c = 0; c < kWideMaxChunks; ++c)
-            pv[k][c] = (ok && c < C) ? load_coherent(part + (size_t)c * Bd + off) : 0.f;
-    }
+        for (int k = 0; k < 4; ++k) {
+            const int o = tid + (k0 + k) * kWideThreads;
+            const int b = o / SC, cc = o - b * SC;
+            const int gcol = slab * SC + cc;
+            const bool ok = b < B && gcol < d;
+            const size_t off = ok ? (size_t)b * d + gcol : 0;
 #pragma unroll
-    for (int k = 0; k < OPT; ++k) {
-        const int o = tid + k * kWideThreads;
-        const int b = o / kWideDownCols, cc = o - b * kWideDownCols;
-        const int gcol = slab * kWideDownCols + cc;
-        if (b >= B || gcol >= d) continue;
-        float sum = b_down ? half_to_float(b_down[gcol]) : 0.f;
+            for (int c = 0; c < kWideMaxChunks; ++c)
+                pv[k][c] = (ok && c < C) ? load_coherent(part + (size_t)c * Bd + off) : 0.f;
+        }
 #pragma unroll
-        for (int c = 0; c < kWideMaxChunks; ++c) sum += pv[k][c];
-        y[(size_t)b * d + gcol] = sum;
+        for (int k = 0; k < 4; ++k) {
+            const int o = tid + (k0 + k) * kWideThreads;
+            const int b = o / SC, cc = o - b * SC;
+            const int gcol = slab * SC + cc;
+            if (b >= B || gcol >= d) continue;
+            float sum = b_down ? half_to_float(b_down[gcol]) : 0.f;
+#pragma unroll
+            for (int c = 0; c < kWideMaxChunks; ++c) sum += pv[k][c];
+            y[(size_t)b * d + gcol] = sum;
+        }
     }
     if (tid == 0) tickets[slab] = 0;
 }
