@@ -227,6 +227,13 @@ def sparse_ffn_h(ffn, batch: int, ws: torch.Tensor, n: int) -> tuple[torch.Tenso
         h = words[:, 2::2].contiguous().view(torch.float32).t()
         ok = words[:, 0] >= 0
         return h, ok
+    if kind == 3:
+        # MFMA form: h = hi + lo, fp16 [16][hs] each, hs = n_slots rounded up to 32, lo 256-aligned after hi
+        hs = (max(int(ffn.n_slots), 1) + 31) // 32 * 32
+        lo_off = off + (32 * hs + 255) // 256 * 256
+        hi = ws[off: off + 2 * batch * hs].view(torch.float16).view(batch, hs)[:, :n].float()
+        lo = ws[lo_off: lo_off + 2 * batch * hs].view(torch.float16).view(batch, hs)[:, :n].float()
+        return hi + lo, torch.ones(n, dtype=torch.bool, device=ws.device)
     stride = max(int(ffn.n_slots), 1)
     h = ws[off: off + 4 * batch * stride].view(torch.float32).view(batch, stride)[:, :n]
     return h, torch.ones(n, dtype=torch.bool, device=ws.device)

@@ -190,7 +190,13 @@ size_t tail_ws(const pi_ffn *fn, int B) {
 // Scratch of pi_sparse_ffn: a control block first on every path, so that the status word sits at
 // a fixed offset (the two-kernel form never waits and leaves it as it found it), then the
 // persistent kernel's regions, or the two-kernel form's (batch > 2, or x does not fit LDS).
+// Batches from kWideFromBatch on run the sparse FFN on MFMA tiles (k_wide_up / k_wide_down): at
+// these batches the GEMV kernels are bound by the vector ALU.
+constexpr int kWideFromBatch = 6;
+bool sparse_wide(const pi_ffn *f, int B) { return B >= kWideFromBatch && !sparse_persistent(f, B); }
+
 size_t ffn_ws(const pi_ffn *f, int B) {
+    if (sparse_wide(f, B)) return ctl_bytes(f->d_model) + wide_geom(f, B).total;
     if (sparse_persistent(f, B)) {
         const SparseGeom g = sparse_geom(f, B);
         return g.ctl + g.ent + g.part;
@@ -467,8 +473,43 @@ int enqueue_sparse_persistent(const pi_ffn *fn, const void *x, int B, const int3
 }
 
 // pi_sparse_ffn's work on a workspace laid out by ffn_ws (ctl: the control block to use).
+// The MFMA form of the sparse FFN (k_wide_up, then k_wide_down) on a wide workspace at w.
+int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y, char *w,
+                 hipStream_t st) {
+    const WideGeom g = wide_geom(fn, B);
+    int32_t *tickets = reinterpret_cast<int32_t *>(w);
+    uint16_t *h_hi = reinterpret_cast<uint16_t *>(w + g.hi), *h_lo = reinterpret_cast<uint16_t *>(w + g.lo);
+    float *part = reinterpret_cast<float *>(w + g.part);
+    const int d = fn->d_model, f = fn->d_ffn, ns = fn->n_slots;
+    const int64_t rb = row_bytes_of(fn);
+    const uint8_t *w_in = static_cast<const uint8_t *>(fn->w_in);
+    const uint16_t *xx = static_cast<const uint16_t *>(x), *b_up = static_cast<const uint16_t *>(fn->b_up);
+    const dim3 up_grid(std::max(1, ceil_div(ns, 16)));
+    if (fn->wtype == PI_Q4_0)
+        hipLaunchKernelGGL((k_wide_up<false, WT_Q4_0, 2>), dim3(std::max(1, ceil_div(ns, 32))), dim3(kWideThreads), 0,
+                           st, w_in, rb, d, b_up, xx, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets,
+                           g.S, fn->act);
+    else if (fn->gated)
+        hipLaunchKernelGGL((k_wide_up<true, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
+                           B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, fn->act);
+    else
+        hipLaunchKernelGGL((k_wide_up<false, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
+                           B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, fn->act);
+    const uint8_t *w_dn = static_cast<const uint8_t *>(fn->w_down_t);
+    const uint16_t *b_dn = static_cast<const uint16_t *>(fn->b_down);
+    if (fn->wtype == PI_Q4_0)
+        hipLaunchKernelGGL(k_wide_down<WT_Q4_0>, dim3(g.S, g.C), dim3(kWideThreads), 0, st, w_dn, rb, d, B, idx,
+                           counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, part, g.C, tickets, b_dn, y);
+    else
+        hipLaunchKernelGGL(k_wide_down<WT_F16>, dim3(g.S, g.C), dim3(kWideThreads), 0, st, w_dn, rb, d, B, idx,
+                           counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, part, g.C, tickets, b_dn, y);
+    return launch_status();
+}
+
 int enqueue_sparse(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y,
                    void *ws, int32_t *ctl, hipStream_t st) {
+    if (sparse_wide(fn, B))
+        return enqueue_wide(fn, x, B, idx, counts, y, static_cast<char *>(ws) + ctl_bytes(fn->d_model), st);
     if (sparse_persistent(fn, B)) {
         char *w = static_cast<char *>(ws);
         return enqueue_sparse_persistent(fn, x, B, idx, counts, y, ctl ? ctl : reinterpret_cast<int32_t *>(w),
@@ -589,34 +630,7 @@ int pi_sparse_ffn_wide(const pi_ffn *ffn, const void *x, int32_t batch, const in
     const WideGeom g = wide_geom(ffn, batch);
     if (!ws || ws_bytes < g.total) return PI_ERR_WORKSPACE;
     if (!aligned16(ws)) return PI_ERR_ALIGN;
-    hipStream_t st = static_cast<hipStream_t>(stream);
-    char *w = static_cast<char *>(ws);
-    int32_t *tickets = reinterpret_cast<int32_t *>(w);
-    uint16_t *h_hi = reinterpret_cast<uint16_t *>(w + g.hi), *h_lo = reinterpret_cast<uint16_t *>(w + g.lo);
-    float *part = reinterpret_cast<float *>(w + g.part);
-    const int d = ffn->d_model, f = ffn->d_ffn, ns = ffn->n_slots;
-    const int64_t rb = row_bytes_of(ffn);
-    const uint8_t *w_in = static_cast<const uint8_t *>(ffn->w_in);
-    const uint16_t *xx = static_cast<const uint16_t *>(x), *b_up = static_cast<const uint16_t *>(ffn->b_up);
-    const dim3 up_grid(std::max(1, ceil_div(ns, 16)));
-    if (ffn->wtype == PI_Q4_0)
-        hipLaunchKernelGGL((k_wide_up<false, WT_Q4_0, 2>), dim3(std::max(1, ceil_div(ns, 32))), dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
-                           batch, idx, counts, ffn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, ffn->act);
-    else if (ffn->gated)
-        hipLaunchKernelGGL((k_wide_up<true, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
-                           batch, idx, counts, ffn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, ffn->act);
-    else
-        hipLaunchKernelGGL((k_wide_up<false, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
-                           batch, idx, counts, ffn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, ffn->act);
-    const uint8_t *w_dn = static_cast<const uint8_t *>(ffn->w_down_t);
-    const uint16_t *b_dn = static_cast<const uint16_t *>(ffn->b_down);
-    if (ffn->wtype == PI_Q4_0)
-        hipLaunchKernelGGL(k_wide_down<WT_Q4_0>, dim3(g.S, g.C), dim3(kWideThreads), 0, st, w_dn, rb, d, batch, idx,
-                           counts, ffn->slot_of, f, ns, h_hi, h_lo, g.hs, part, g.C, tickets, b_dn, y);
-    else
-        hipLaunchKernelGGL(k_wide_down<WT_F16>, dim3(g.S, g.C), dim3(kWideThreads), 0, st, w_dn, rb, d, batch, idx,
-                           counts, ffn->slot_of, f, ns, h_hi, h_lo, g.hs, part, g.C, tickets, b_dn, y);
-    return launch_status();
+    return enqueue_wide(ffn, x, batch, idx, counts, y, static_cast<char *>(ws), static_cast<hipStream_t>(stream));
 }
 
 int pi_predict_hidden(const pi_predictor *pred, const void *x, int32_t batch, float *z, void *stream) {
@@ -727,6 +741,10 @@ size_t pi_sparse_ffn_h_offset(const pi_ffn *ffn, int32_t batch, int32_t *kind) {
     if (sparse_persistent(ffn, batch)) {
         *kind = 1;
         return sparse_geom(ffn, batch).ctl;
+    }
+    if (sparse_wide(ffn, batch)) {
+        *kind = 3;
+        return ctl_bytes(ffn->d_model) + wide_geom(ffn, batch).hi;
     }
     *kind = 2;
     return ctl_bytes(ffn->d_model);

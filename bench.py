@@ -221,10 +221,11 @@ def main():
     n_act, n_pred = cnt_host[:, 0], cnt_host[:, 1]
     vec_bytes = B * cfg.d * (2 + 4) + 2 * cfg.d                  # x in, y out, b_down
     slot_bytes = 4 * cfg.f if layers[0].slot_of is not None else 0
-    # sparse FFN alone: the persistent kernel reads every listed row (its down-row loads go out
-    # before h is known); the two-kernel form skips down rows whose h is zero for every token
+    # sparse FFN alone: the persistent kernel and the MFMA form read every listed row (the former's
+    # down-row loads go out before h is known); the GEMV two-kernel form skips down rows whose h is
+    # zero for every token
     _, h_kind = _abi.pi_sparse_ffn_h_offset(layers[0].ffn, B)
-    n_read_down = n_act if h_kind == 1 else n_live
+    n_read_down = n_act if h_kind in (1, 3) else n_live
     ffn_touched = n_act * in_rows * rb + n_read_down * rb + 8 * n_act + vec_bytes
     ffn_predicted = n_act * (in_rows + 1) * rb + 8 * n_act + vec_bytes
     # the rest of the layer on path 1 (one kernel): P2 and c, z, every listed row in and down

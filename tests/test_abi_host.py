@@ -186,10 +186,15 @@ def test_h_offset(L):
     small, large = ffn(d=1024, f=4096), ffn(d=12288, f=4096)
     off = L.pi_sparse_ffn_h_offset(ctypes.byref(small), 1, ctypes.byref(kind))
     assert kind.value == 1 and 0 < off < ws_for(L, None, small, 1)
-    off = L.pi_sparse_ffn_h_offset(ctypes.byref(large), 8, ctypes.byref(kind))
-    assert kind.value == 2 and off >= 512                     # x [8][12288] does not fit LDS: two kernels,
-    assert off % 256 == 0 and off < ws_for(L, None, large, 8)  # after the control block
+    off = L.pi_sparse_ffn_h_offset(ctypes.byref(large), 4, ctypes.byref(kind))
+    assert kind.value == 2 and off >= 512                     # x [4][12288] does not fit LDS: two kernels,
+    assert off % 256 == 0 and off < ws_for(L, None, large, 4)  # after the control block
     L.pi_sparse_ffn_h_offset(ctypes.byref(small), 4, ctypes.byref(kind))
     assert kind.value == 2                                    # batch > 2: two kernels
+    off = L.pi_sparse_ffn_h_offset(ctypes.byref(large), 8, ctypes.byref(kind))
+    assert kind.value == 3 and off >= 512 and off % 256 == 0   # batch >= 6: the MFMA kernels
+    assert off + 2 * 16 * 4096 * 2 <= ws_for(L, None, large, 8)  # hi and lo tables inside the workspace
+    L.pi_sparse_ffn_h_offset(ctypes.byref(small), 6, ctypes.byref(kind))
+    assert kind.value == 3
     assert L.pi_sparse_ffn_h_offset(ctypes.byref(small), 9, ctypes.byref(kind)) == 2**64 - 1
     assert L.pi_sparse_ffn_h_offset(ctypes.byref(small), 1, None) == 2**64 - 1
