@@ -190,10 +190,11 @@ size_t tail_ws(const pi_ffn *fn, int B) {
 // Scratch of pi_sparse_ffn: a control block first on every path, so that the status word sits at
 // a fixed offset (the two-kernel form never waits and leaves it as it found it), then the
 // persistent kernel's regions, or the two-kernel form's (batch > 2, or x does not fit LDS).
-// Batches from kWideFromBatch on run the sparse FFN on MFMA tiles (k_wide_up / k_wide_down): at
-// these batches the GEMV kernels are bound by the vector ALU.
-constexpr int kWideFromBatch = 6;
-bool sparse_wide(const pi_ffn *f, int B) { return B >= kWideFromBatch && !sparse_persistent(f, B); }
+// From these batches on the sparse FFN runs on MFMA tiles (k_wide_up / k_wide_down), where the
+// GEMV kernels become bound by the vector ALU: batch 3 for gated (two dot products per neuron) and
+// Q4_0 rows (decode work per weight), batch 6 for plain fp16 rows (measured crossovers).
+int wide_from_batch(const pi_ffn *f) { return (f->gated || f->wtype == PI_Q4_0) ? 3 : 6; }
+bool sparse_wide(const pi_ffn *f, int B) { return B >= wide_from_batch(f) && !sparse_persistent(f, B); }
 
 size_t ffn_ws(const pi_ffn *f, int B) {
     if (sparse_wide(f, B)) return ctl_bytes(f->d_model) + wide_geom(f, B).total;

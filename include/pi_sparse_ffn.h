@@ -127,7 +127,8 @@ int pi_compact(const uint8_t *mask, int32_t d_ffn, const int32_t *slot_of, int32
  *  - the int32 at byte offset 384 of the workspace is a sticky status word: nonzero means a
  *    cross-workgroup wait ran out its time limit (20 ms) and the outputs of that call are invalid.
  * Every wait inside the kernel is bounded.  Other shapes and batches run two kernels (h, then the
- * rows of W_down^T; from batch 6 on, the MFMA kernels of pi_sparse_ffn_wide), which never wait and
+ * rows of W_down^T; from batch 3 for gated or Q4_0 rows and from batch 6 for other fp16 rows, the
+ * MFMA kernels of pi_sparse_ffn_wide), which never wait and
  * need no zero fill; their workspace starts with the same control block, which they leave
  * untouched, so a zero-filled workspace reads status 0 on every form. */
 int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx,
@@ -191,7 +192,7 @@ int pi_ffn_layer_fused(const pi_predictor *pred, const pi_ffn *ffn, const void *
  *  1 = persistent kernel: position k is (1 + batch) uint64 words at offset + 8*k*(1 + batch);
  *      the low 32 bits of word 0 are the slot (-1 = skipped), those of word 1 + b the fp32 bits of h;
  *  2 = two-kernel form: fp32 h at offset + 4*(b*max(n_slots, 1) + k);
- *  3 = MFMA form (batch >= 6): h = hi + lo, fp16 hi at offset + 2*(b*hs + k) and fp16 lo at
+ *  3 = MFMA form (the batches named above): h = hi + lo, fp16 hi at offset + 2*(b*hs + k) and fp16 lo at
  *      offset + L + 2*(b*hs + k), hs = max(n_slots, 1) rounded up to 32, L = 32*hs rounded up to 256.
  * Positions k >= counts[0] hold stale values.  Returns (size_t)-1 on invalid arguments. */
 size_t pi_sparse_ffn_h_offset(const pi_ffn *ffn, int32_t batch, int32_t *kind);

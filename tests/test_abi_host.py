@@ -196,5 +196,8 @@ def test_h_offset(L):
     assert off + 2 * 16 * 4096 * 2 <= ws_for(L, None, large, 8)  # hi and lo tables inside the workspace
     L.pi_sparse_ffn_h_offset(ctypes.byref(small), 6, ctypes.byref(kind))
     assert kind.value == 3
+    for gated_or_q4 in (ffn(d=1024, f=4096, gated=1), ffn(d=1024, f=4096, wtype=_abi.PI_Q4_0)):
+        L.pi_sparse_ffn_h_offset(ctypes.byref(gated_or_q4), 3, ctypes.byref(kind))
+        assert kind.value == 3                                # gated / Q4_0: MFMA kernels from batch 3
     assert L.pi_sparse_ffn_h_offset(ctypes.byref(small), 9, ctypes.byref(kind)) == 2**64 - 1
     assert L.pi_sparse_ffn_h_offset(ctypes.byref(small), 1, None) == 2**64 - 1
