@@ -2,11 +2,12 @@
 //
 // The sparse operator of the method (PowerInfer, arXiv 2312.12456, method section: only the
 // predicted neurons' rows are read and computed) is, at a batch of B tokens, a contraction over
-// the gathered rows: H = act(X W_in[idx]^T + b) is [B x n], Y = H W_down^T[idx] is [B x d].  At
-// B <= 8 the GEMV kernels of pi_kernels.hpp keep the vector ALU below the HBM rate; at B = 16
-// the down step alone needs 16 FMAs per fp16 weight (64 T FMA/s at 8 TB/s, most of the vector
-// ALU's 78.6 T), so here both steps run on v_mfma_f32_16x16x16_f16 tiles with the batch padded
-// to 16 (tokens >= B read as zero and are never stored).
+// the gathered rows: H = act(X W_in[idx]^T + b) is [B x n], Y = H W_down^T[idx] is [B x d].  The
+// GEMV kernels of pi_kernels.hpp spend vector-ALU work per weight that grows with B (at B = 16 the
+// down step alone needs 16 FMAs per fp16 weight: 64 T FMA/s at 8 TB/s, most of the vector ALU's
+// 78.6 T), so here both steps run on v_mfma_f32_16x16x16_f16 tiles with the batch padded to 16
+// (tokens >= B read as zero and are never stored); pi_sparse_ffn uses these kernels from batch 3
+// for gated or Q4_0 rows and from batch 6 for plain fp16 rows.
 //
 // Operand layout of a 16x16x16 f16 MFMA (wave64): lane l supplies A[m = l%16][k = 4(l/16)+v] and
 // B[k = 4(l/16)+v][n = l%16] for v < 4, and receives D[m = 4(l/16)+v][n = l%16].  A contraction
