@@ -24,7 +24,7 @@ PI_MAX_WIDE_BATCH = 16
 # Every function the header declares; the CPU tests check that libpi.so exports them all.
 EXPORTS = ("pi_workspace_bytes", "pi_predict", "pi_compact", "pi_sparse_ffn", "pi_sparse_ffn_wide_workspace_bytes", "pi_sparse_ffn_wide",
            "pi_ffn_layer",
-           "pi_predict_hidden", "pi_ffn_layer_from_hidden", "pi_layer_path", "pi_ffn_layer_fused", "pi_sparse_ffn_h_offset",
+           "pi_predict_hidden", "pi_ffn_layer_from_hidden", "pi_layer_path", "pi_sparse_ffn_h_offset",
            "pi_cold_workspace_bytes", "pi_cold_ffn_host", "pi_place", "pi_status_string", "pi_version")
 
 
@@ -77,8 +77,6 @@ def lib() -> ctypes.CDLL:
         L.pi_ffn_layer_from_hidden.argtypes = [P(pi_predictor), P(pi_ffn), vp, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.pi_layer_path.restype = ctypes.c_int
         L.pi_layer_path.argtypes = [P(pi_predictor), P(pi_ffn), i32]
-        L.pi_ffn_layer_fused.restype = ctypes.c_int
-        L.pi_ffn_layer_fused.argtypes = [P(pi_predictor), P(pi_ffn), vp, i32, vp, vp, vp, vp, vp, sz, vp]
         L.pi_sparse_ffn_h_offset.restype = sz
         L.pi_sparse_ffn_h_offset.argtypes = [P(pi_ffn), i32, P(i32)]
         L.pi_cold_workspace_bytes.restype = sz
@@ -195,12 +193,6 @@ def pi_layer_path(pred, ffn, batch) -> int:
     return int(lib().pi_layer_path(_byref(pred), _byref(ffn), batch))
 
 
-def pi_ffn_layer_fused(pred, ffn, x, batch, y, mask_out, idx_out, counts_out, ws, stream=None) -> None:
-    _check("pi_ffn_layer_fused", lib().pi_ffn_layer_fused(
-        _byref(pred), _byref(ffn), _ptr(x), batch, _ptr(y), _ptr(mask_out), _ptr(idx_out), _ptr(counts_out),
-        _ptr(ws), _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0, _stream(stream)))
-
-
 PI_WS_STATUS_OFFSET = 384      # byte offset of the layer workspace's sticky status word
 
 
@@ -223,10 +215,9 @@ def sparse_ffn_h(ffn, batch: int, ws: torch.Tensor, n: int) -> tuple[torch.Tenso
     for list positions 0..n-1 (a device-side view, for counting the rows that had to be read)."""
     off, kind = pi_sparse_ffn_h_offset(ffn, batch)
     if kind == 1:
-        words = ws[off: off + 8 * n * (1 + batch)].view(torch.int32).view(n, 2 * (1 + batch))
-        h = words[:, 2::2].contiguous().view(torch.float32).t()
-        ok = words[:, 0] >= 0
-        return h, ok
+        f = int(ffn.d_ffn)
+        h = ws[off: off + 4 * batch * f].view(torch.float32).view(batch, f)[:, :n]
+        return h, torch.ones(n, dtype=torch.bool, device=ws.device)
     if kind == 3:
         # MFMA form: h = hi + lo, fp16 [16][hs] each, hs = n_slots rounded up to 32, lo 256-aligned after hi
         hs = (max(int(ffn.n_slots), 1) + 31) // 32 * 32

@@ -14,10 +14,10 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libpi.so")
 CSRC = os.path.join(PKG, "csrc")
-SOURCES = [os.path.join(CSRC, "pi_abi.hip"), os.path.join(CSRC, "pi_fused_b.hip")]
+SOURCES = [os.path.join(CSRC, "pi_abi.hip"), os.path.join(CSRC, "pi_persist_b.hip"), os.path.join(CSRC, "pi_split.hip")]
 HOST_SOURCES = [os.path.join(CSRC, "pi_cold.cpp"),   # host half of the hybrid split (g++, OpenMP)
                 os.path.join(CSRC, "pi_place.cpp")]  # offline placement under a memory budget
-DEPENDS = SOURCES + HOST_SOURCES + [os.path.join(CSRC, n) for n in ("pi_kernels.hpp", "pi_fused.hpp", "pi_tail.hpp", "pi_sparse.hpp", "pi_wide.hpp")] + [
+DEPENDS = SOURCES + HOST_SOURCES + [os.path.join(CSRC, n) for n in ("pi_kernels.hpp", "pi_sync.hpp", "pi_occupancy.hpp", "pi_tail.hpp", "pi_split.hpp", "pi_wide.hpp")] + [
                      os.path.join(ROOT, "include", "pi_sparse_ffn.h")]
 OBJDIR = os.path.join(ROOT, "_build")
 
@@ -34,10 +34,12 @@ HOST_OBJS = [os.path.join(OBJDIR, os.path.basename(p).replace(".cpp", ".o")) for
 
 
 def _units():
-    """(source, object, extra flags): the ABI unit plus one fused-kernel unit per batch width."""
+    """(source, object, extra flags): the ABI unit, one tail-kernel unit per batch width, the split
+    sparse-FFN unit."""
     units = [(SOURCES[0], os.path.join(OBJDIR, "pi_abi.o"), [])]
     for b in range(1, 9):
-        units.append((SOURCES[1], os.path.join(OBJDIR, f"pi_fused_b{b}.o"), [f"-DPIK_B={b}"]))
+        units.append((SOURCES[1], os.path.join(OBJDIR, f"pi_persist_b{b}.o"), [f"-DPIK_B={b}"]))
+    units.append((SOURCES[2], os.path.join(OBJDIR, "pi_split.o"), []))
     return units
 
 

@@ -6,6 +6,7 @@
 // No C++ exception crosses the ABI.
 #include "pi_sparse_ffn.h"
 #include "pi_kernels.hpp"
+#include "pi_split.hpp"
 #include "pi_tail.hpp"
 #include "pi_wide.hpp"
 
@@ -112,38 +113,34 @@ size_t ffn_legacy_ws(const pi_ffn *f, int B) {
     return ffn_h_bytes(f, B) + ffn_part_bytes(f, B) + align_up((size_t)down_slabs(f->d_model) * sizeof(int32_t));
 }
 
-// Both persistent kernels keep x [B][d] (fp16) in LDS next to their static arrays (4*B*8*64
-// floats of wave partials and ~2 KB of indices); all of it must fit one workgroup.
-bool persistent_fits(int d, int B) {
-    const size_t x = (size_t)B * d * 2, fixed = (size_t)B * 8192 + 4096;
-    return x <= (size_t)kLdsXBytes && x + fixed <= 160 * 1024;
-}
+// The control block shared by every persistent launch on a workspace (pi_sync.hpp): epoch, exit
+// count, abort flag, status word (byte offset 384).
+size_t ctl_bytes(int) { return align_up((size_t)CTL_WORDS * sizeof(int32_t)); }
 
-// Scratch of the persistent sparse-FFN kernel: the control block, (1 + B) stamped words per list
-// position (slot, h per token), stamped chunk partials [kSparseMaxChunks][B][d].  The chunk count
-// itself is chosen at launch from the device's occupancy.
-struct SparseGeom {
-    int slabs;
-    size_t ctl, ent, part;
+// Scratch of the (column slab x list chunk) kernels of pi_split.hpp, batch <= 2: partial dot
+// products [positions][S][B*G] fp32, chunk partials of y [kSplitMaxChunks][B][d] fp32 (the chunk
+// count is chosen at launch), and h per position [B][d_ffn] fp32 (diagnostics).
+struct SplitGeom {
+    int S;
+    size_t part, ypart, hout;
 };
-
-// Control block of either persistent kernel: room for the tickets of the most column slabs
-// either one uses (256-column slabs).
-size_t ctl_bytes(int d) { return align_up((size_t)(CTL_LAYER0 + ctl_layer_stride(ceil_div(d, 256))) * sizeof(int32_t)); }
-
-SparseGeom sparse_geom(const pi_ffn *fn, int B) {
-    SparseGeom g;
-    const int d = fn->d_model;
-    g.slabs = sparse_slabs(d, fn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16);
-    g.ctl = ctl_bytes(d);
-    g.ent = align_up((size_t)std::max(fn->n_slots, 1) * (1 + B) * sizeof(uint64_t));
-    g.part = align_up((size_t)kSparseMaxChunks * B * d * sizeof(uint64_t));
+SplitGeom split_geom(const pi_ffn *fn, int B) {
+    SplitGeom g;
+    const int wt = fn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16;
+    g.S = split_slabs(fn->d_model, wt);
+    g.part = align_up((size_t)fn->d_ffn * g.S * B * (fn->gated ? 2 : 1) * sizeof(float));
+    g.ypart = align_up((size_t)kSplitMaxChunks * B * fn->d_model * sizeof(float));
+    g.hout = align_up((size_t)B * fn->d_ffn * sizeof(float));
     return g;
 }
-
-// The persistent form needs every workgroup resident; at batch > 2 its x copy and partial arrays
-// leave too few resident workgroups per CU, and the two-kernel form is faster (measured).
-bool sparse_persistent(const pi_ffn *fn, int B) { return B <= 2 && persistent_fits(fn->d_model, B); }
+// Batches 1 and 2 run the split kernels whenever the slab count allows (d_model up to 32768 for fp16
+// rows, 65536 for Q4_0); they need no copy of x in LDS.
+bool sparse_split(const pi_ffn *fn, int B) {
+    return B <= 2 && split_slabs(fn->d_model, fn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16) <= kSplitMaxSlabs;
+}
+int mask_words(int f) { return ceil_div(f, 32); }
+// In a layer, the split kernel reads the predictor's listed-bit words directly (no compaction).
+bool layer_split(const pi_ffn *fn, int B) { return sparse_split(fn, B) && mask_words(fn->d_ffn) <= kSplitMaxWords; }
 
 // The tail kernel (second predictor matrix + mask + sparse FFN) keeps x [B][d] fp16 and z [B][r]
 // fp32 in dynamic LDS next to its static arrays (wave partials of the down tiles, the list of a
@@ -187,21 +184,21 @@ size_t tail_ws(const pi_ffn *fn, int B) {
     return g.tword + g.ent + g.part;
 }
 
-// Scratch of pi_sparse_ffn: a control block first on every path, so that the status word sits at
-// a fixed offset (the two-kernel form never waits and leaves it as it found it), then the
-// persistent kernel's regions, or the two-kernel form's (batch > 2, or x does not fit LDS).
 // From these batches on the sparse FFN runs on MFMA tiles (k_wide_up / k_wide_down), where the
 // GEMV kernels become bound by the vector ALU: batch 3 for gated (two dot products per neuron) and
 // Q4_0 rows (decode work per weight), batch 6 for plain fp16 rows (measured crossovers).
 int wide_from_batch(const pi_ffn *f) { return (f->gated || f->wtype == PI_Q4_0) ? 3 : 6; }
-bool sparse_wide(const pi_ffn *f, int B) { return B >= wide_from_batch(f) && !sparse_persistent(f, B); }
+bool sparse_wide(const pi_ffn *f, int B) { return B >= wide_from_batch(f) && !sparse_split(f, B); }
 
+// Scratch of pi_sparse_ffn: a control block first on every path, so that the status word sits at
+// a fixed offset (the kernels that never wait leave it as they found it), then the split kernel's
+// regions, the MFMA form's, or the GEMV two-kernel form's.
 size_t ffn_ws(const pi_ffn *f, int B) {
-    if (sparse_wide(f, B)) return ctl_bytes(f->d_model) + wide_geom(f, B).total;
-    if (sparse_persistent(f, B)) {
-        const SparseGeom g = sparse_geom(f, B);
-        return g.ctl + g.ent + g.part;
+    if (sparse_split(f, B)) {
+        const SplitGeom g = split_geom(f, B);
+        return ctl_bytes(f->d_model) + g.part + g.ypart + g.hout;
     }
+    if (sparse_wide(f, B)) return ctl_bytes(f->d_model) + wide_geom(f, B).total;
     return ctl_bytes(f->d_model) + ffn_legacy_ws(f, B);
 }
 
@@ -214,75 +211,43 @@ FfnScratch ffn_scratch(const pi_ffn *f, int B, void *base) {
     return s;
 }
 
-size_t layer_extra_ws(int f) {
-    return align_up((size_t)f) + align_up((size_t)f * sizeof(int32_t)) + align_up(2 * sizeof(int32_t));
-}
-
-// ------------------------------------------------------------------ fused layer geometry
-
-struct FusedGeom {
-    int NT, TPD, NA, NB, ND, slabs, C, NE;
-    size_t ctl, z, tword, ghead, ent, part;   // region sizes (aligned); tword also sizes pword
-};
-
-FusedGeom fused_geom(const pi_predictor *p, const pi_ffn *fn, int B) {
-    FusedGeom g;
-    const int f = p->d_ffn, d = p->d_model, r = p->rank;
-    g.NT = r <= 512 ? 1 : (r <= 1024 ? 2 : 4);
-    g.TPD = std::min(4, std::max(1, (f + 8192) / 16384));
-    g.NA = ceil_div(r, 4);
-    g.NB = ceil_div(f, kTile);
-    g.ND = ceil_div(g.NB, g.TPD);
-    g.slabs = down_slabs(d);
-    g.C = std::min(kFusedMaxChunks, std::max(1, std::min(g.ND, ceil_div(kDownTargetTiles, g.slabs))));
-    g.NE = g.slabs * g.C;
-    g.ctl = ctl_bytes(d);
-    g.z = align_up((size_t)B * r * sizeof(uint64_t));
-    g.tword = align_up((size_t)g.NB * sizeof(uint64_t));
-    g.ghead = align_up((size_t)g.ND * sizeof(uint64_t));
-    g.ent = align_up((size_t)g.ND * kTile * g.TPD * (1 + B) * sizeof(uint64_t));
-    g.part = align_up((size_t)g.C * B * d * sizeof(uint64_t));
-    (void)fn;
-    return g;
-}
-
-size_t fused_ws(const FusedGeom &g) { return g.ctl + g.z + 2 * g.tword + g.ghead + g.ent + g.part; }
-
-bool fused_eligible(const pi_predictor *p, const pi_ffn *fn, int B) {
-    (void)p;
-    return persistent_fits(fn->d_model, B);
-}
 
 int launch_status() { return hipGetLastError() == hipSuccess ? PI_OK : PI_ERR_HIP; }
 
 // ------------------------------------------------------------------ enqueue helpers
 
+// bits (optional, with slot_of/n_slots): the placement-restricted listed flags, one word per 32 rows.
 template <int B>
-int enqueue_pred_l2_b(const pi_predictor *p, const float *z, uint8_t *mask, float *logits, hipStream_t st) {
+int enqueue_pred_l2_b(const pi_predictor *p, const float *z, uint8_t *mask, float *logits, uint32_t *bits,
+                      const int32_t *slot_of, int n_slots, hipStream_t st) {
     const int r = p->rank, f = p->d_ffn;
     constexpr int R = 8;                               // predictor rows per wave
     const int groups = ceil_div(f, 4 * R);
     const uint16_t *p2 = static_cast<const uint16_t *>(p->p2), *c = static_cast<const uint16_t *>(p->c);
     const size_t zb = (size_t)B * r * sizeof(float);       // z staged in LDS (<= 64 KB)
     if (r <= 512)
-        hipLaunchKernelGGL((k_pred_l2<B, 1, R>), dim3(groups), dim3(256), zb, st, p2, c, z, r, f, logits, mask);
+        hipLaunchKernelGGL((k_pred_l2<B, 1, R>), dim3(groups), dim3(256), zb, st, p2, c, z, r, f, logits, mask, bits,
+                           slot_of, n_slots);
     else if (r <= 1024)
-        hipLaunchKernelGGL((k_pred_l2<B, 2, R>), dim3(groups), dim3(256), zb, st, p2, c, z, r, f, logits, mask);
+        hipLaunchKernelGGL((k_pred_l2<B, 2, R>), dim3(groups), dim3(256), zb, st, p2, c, z, r, f, logits, mask, bits,
+                           slot_of, n_slots);
     else
-        hipLaunchKernelGGL((k_pred_l2<B, 4, R>), dim3(groups), dim3(256), zb, st, p2, c, z, r, f, logits, mask);
+        hipLaunchKernelGGL((k_pred_l2<B, 4, R>), dim3(groups), dim3(256), zb, st, p2, c, z, r, f, logits, mask, bits,
+                           slot_of, n_slots);
     return launch_status();
 }
 
-int enqueue_pred_l2(const pi_predictor *p, const float *z, int B, uint8_t *mask, float *logits, hipStream_t st) {
+int enqueue_pred_l2(const pi_predictor *p, const float *z, int B, uint8_t *mask, float *logits, hipStream_t st,
+                    uint32_t *bits = nullptr, const int32_t *slot_of = nullptr, int n_slots = 0) {
     switch (B) {
-        case 1: return enqueue_pred_l2_b<1>(p, z, mask, logits, st);
-        case 2: return enqueue_pred_l2_b<2>(p, z, mask, logits, st);
-        case 3: return enqueue_pred_l2_b<3>(p, z, mask, logits, st);
-        case 4: return enqueue_pred_l2_b<4>(p, z, mask, logits, st);
-        case 5: return enqueue_pred_l2_b<5>(p, z, mask, logits, st);
-        case 6: return enqueue_pred_l2_b<6>(p, z, mask, logits, st);
-        case 7: return enqueue_pred_l2_b<7>(p, z, mask, logits, st);
-        case 8: return enqueue_pred_l2_b<8>(p, z, mask, logits, st);
+        case 1: return enqueue_pred_l2_b<1>(p, z, mask, logits, bits, slot_of, n_slots, st);
+        case 2: return enqueue_pred_l2_b<2>(p, z, mask, logits, bits, slot_of, n_slots, st);
+        case 3: return enqueue_pred_l2_b<3>(p, z, mask, logits, bits, slot_of, n_slots, st);
+        case 4: return enqueue_pred_l2_b<4>(p, z, mask, logits, bits, slot_of, n_slots, st);
+        case 5: return enqueue_pred_l2_b<5>(p, z, mask, logits, bits, slot_of, n_slots, st);
+        case 6: return enqueue_pred_l2_b<6>(p, z, mask, logits, bits, slot_of, n_slots, st);
+        case 7: return enqueue_pred_l2_b<7>(p, z, mask, logits, bits, slot_of, n_slots, st);
+        case 8: return enqueue_pred_l2_b<8>(p, z, mask, logits, bits, slot_of, n_slots, st);
     }
     return PI_ERR_BATCH;
 }
@@ -306,31 +271,6 @@ void enqueue_pred_l1_b(const pi_predictor *p, const uint16_t *x, float *z, hipSt
     else enqueue_pred_l1_bu<B, UMAX>(p, x, z, st);
 }
 
-template <int B>
-int enqueue_predict_b(const pi_predictor *p, const uint16_t *x, uint8_t *mask, float *logits, float *z,
-                      hipStream_t st) {
-    enqueue_pred_l1_b<B>(p, x, z, st);
-    if (launch_status() != PI_OK) return PI_ERR_HIP;
-    return enqueue_pred_l2_b<B>(p, z, mask, logits, st);
-}
-
-int enqueue_predict(const pi_predictor *p, const void *x, int B, uint8_t *mask, float *logits, float *z,
-                    hipStream_t st) {
-    const uint16_t *xx = static_cast<const uint16_t *>(x);
-    switch (B) {
-        case 1: return enqueue_predict_b<1>(p, xx, mask, logits, z, st);
-        case 2: return enqueue_predict_b<2>(p, xx, mask, logits, z, st);
-        case 3: return enqueue_predict_b<3>(p, xx, mask, logits, z, st);
-        case 4: return enqueue_predict_b<4>(p, xx, mask, logits, z, st);
-        case 5: return enqueue_predict_b<5>(p, xx, mask, logits, z, st);
-        case 6: return enqueue_predict_b<6>(p, xx, mask, logits, z, st);
-        case 7: return enqueue_predict_b<7>(p, xx, mask, logits, z, st);
-        case 8: return enqueue_predict_b<8>(p, xx, mask, logits, z, st);
-    }
-    return PI_ERR_BATCH;
-}
-
-
 int enqueue_pred_l1(const pi_predictor *p, const void *x, int B, float *z, hipStream_t st) {
     const uint16_t *xx = static_cast<const uint16_t *>(x);
     switch (B) {
@@ -345,6 +285,12 @@ int enqueue_pred_l1(const pi_predictor *p, const void *x, int B, float *z, hipSt
         default: return PI_ERR_BATCH;
     }
     return launch_status();
+}
+
+int enqueue_predict(const pi_predictor *p, const void *x, int B, uint8_t *mask, float *logits, float *z,
+                    hipStream_t st) {
+    int rc = enqueue_pred_l1(p, x, B, z, st);
+    return rc ? rc : enqueue_pred_l2(p, z, B, mask, logits, st);
 }
 
 // The tail kernel: z (from k_pred_l1) -> mask -> sparse FFN -> y; ctl is the shared control block,
@@ -420,7 +366,7 @@ int enqueue_sparse_bt(const pi_ffn *fn, const uint16_t *x, const int32_t *idx, c
 }
 
 int enqueue_sparse_legacy(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y,
-                   const FfnScratch &sc, hipStream_t st) {
+                          const FfnScratch &sc, hipStream_t st) {
     const uint16_t *xx = static_cast<const uint16_t *>(x);
     switch (B) {
         case 1: return enqueue_sparse_bt<1>(fn, xx, idx, counts, y, sc, st);
@@ -435,45 +381,32 @@ int enqueue_sparse_legacy(const pi_ffn *fn, const void *x, int B, const int32_t 
     return PI_ERR_BATCH;
 }
 
-// The persistent sparse-FFN kernel; ctl is the control block (shared with the fused layer kernel
-// inside a layer workspace), data the entry table and the partials.
-int enqueue_sparse_persistent(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts,
-                              float *y, int32_t *ctl, char *data, hipStream_t st, uint64_t *trace = nullptr) {
-    const SparseGeom g = sparse_geom(fn, B);
-    SparseArgs a{};
-    a.d = fn->d_model; a.f = fn->d_ffn; a.n_slots = fn->n_slots; a.slabs = g.slabs;
+// The split kernels on a pi_sparse_ffn workspace `w` (past its control block).  Positions from
+// idx/counts, or (bits != nullptr) from the listed-flag words.
+int enqueue_split(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts,
+                  const uint32_t *bits, float *y, char *w, hipStream_t st, uint64_t *trace = nullptr) {
+    const SplitGeom g = split_geom(fn, B);
+    SplitArgs a{};
+    a.d = fn->d_model; a.f = fn->d_ffn; a.n_slots = fn->n_slots; a.S = g.S; a.act = fn->act;
+    a.nwords = bits != nullptr ? mask_words(fn->d_ffn) : 0;
     a.row_bytes = row_bytes_of(fn);
-    a.act = fn->act;
     a.w_in = static_cast<const uint8_t *>(fn->w_in); a.w_dn = static_cast<const uint8_t *>(fn->w_down_t);
     a.b_up = static_cast<const uint16_t *>(fn->b_up); a.b_down = static_cast<const uint16_t *>(fn->b_down);
     a.slot_of = fn->slot_of;
     a.x = static_cast<const uint16_t *>(x); a.y = y;
-    a.idx = idx; a.counts = counts;
-    a.ctl = ctl;
-    a.ent = reinterpret_cast<uint64_t *>(data); data += g.ent;
-    a.part = reinterpret_cast<uint64_t *>(data);
+    a.idx = idx; a.counts = counts; a.bits = bits;
+    a.part = reinterpret_cast<float *>(w); w += g.part;
+    a.ypart = reinterpret_cast<float *>(w); w += g.ypart;
+    a.hout = reinterpret_cast<float *>(w);
 #ifdef PIK_TRACE
     a.trace = trace;
 #else
     (void)trace;
 #endif
     const int wt = fn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16;
-    int rc;
-    switch (B) {
-        case 1: rc = launch_sparse_batch<1>(a, wt, fn->gated, st); break;
-        case 2: rc = launch_sparse_batch<2>(a, wt, fn->gated, st); break;
-        case 3: rc = launch_sparse_batch<3>(a, wt, fn->gated, st); break;
-        case 4: rc = launch_sparse_batch<4>(a, wt, fn->gated, st); break;
-        case 5: rc = launch_sparse_batch<5>(a, wt, fn->gated, st); break;
-        case 6: rc = launch_sparse_batch<6>(a, wt, fn->gated, st); break;
-        case 7: rc = launch_sparse_batch<7>(a, wt, fn->gated, st); break;
-        case 8: rc = launch_sparse_batch<8>(a, wt, fn->gated, st); break;
-        default: return PI_ERR_BATCH;
-    }
-    return rc == 0 ? PI_OK : PI_ERR_HIP;
+    return launch_split(a, B, wt, fn->gated, st) == 0 ? PI_OK : PI_ERR_HIP;
 }
 
-// pi_sparse_ffn's work on a workspace laid out by ffn_ws (ctl: the control block to use).
 // The MFMA form of the sparse FFN (k_wide_up, then k_wide_down) on a wide workspace at w.
 int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y, char *w,
                  hipStream_t st) {
@@ -507,64 +440,44 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
     return launch_status();
 }
 
+// pi_sparse_ffn's work on a workspace laid out by ffn_ws; bits: listed-flag words to take the
+// positions from instead of idx/counts.
 int enqueue_sparse(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y,
-                   void *ws, int32_t *ctl, hipStream_t st) {
-    if (sparse_wide(fn, B))
-        return enqueue_wide(fn, x, B, idx, counts, y, static_cast<char *>(ws) + ctl_bytes(fn->d_model), st);
-    if (sparse_persistent(fn, B)) {
-        char *w = static_cast<char *>(ws);
-        return enqueue_sparse_persistent(fn, x, B, idx, counts, y, ctl ? ctl : reinterpret_cast<int32_t *>(w),
-                                         w + sparse_geom(fn, B).ctl, st);
-    }
-    return enqueue_sparse_legacy(fn, x, B, idx, counts, y,
-                                 ffn_scratch(fn, B, static_cast<char *>(ws) + ctl_bytes(fn->d_model)), st);
+                   void *ws, hipStream_t st, const uint32_t *bits = nullptr) {
+    char *w = static_cast<char *>(ws);
+    if (sparse_split(fn, B))
+        return enqueue_split(fn, x, B, idx, counts, bits, y, w + ctl_bytes(fn->d_model), st);
+    if (sparse_wide(fn, B)) return enqueue_wide(fn, x, B, idx, counts, y, w + ctl_bytes(fn->d_model), st);
+    return enqueue_sparse_legacy(fn, x, B, idx, counts, y, ffn_scratch(fn, B, w + ctl_bytes(fn->d_model)), st);
 }
 
-int enqueue_fused(const pi_predictor *p, const pi_ffn *fn, const void *x, int B, float *y, uint8_t *mask_out,
-                  int32_t *idx_out, int32_t *counts_out, void *ws, hipStream_t st, uint64_t *trace = nullptr) {
-    const FusedGeom g = fused_geom(p, fn, B);
-    char *w = static_cast<char *>(ws);
-    FusedArgs a{};
-    a.d = p->d_model; a.f = p->d_ffn; a.r = p->rank; a.n_slots = fn->n_slots;
-    a.slabs = g.slabs; a.C = g.C; a.TPD = g.TPD; a.NA = g.NA; a.NB = g.NB; a.ND = g.ND; a.NE = g.NE;
-    a.cap = kTile * g.TPD;
-    a.want_x = (idx_out != nullptr || counts_out != nullptr) ? 1 : 0;
-    a.tasks = g.NA + g.NB + g.ND + g.NE + a.want_x;
-    a.row_bytes = row_bytes_of(fn);
-    a.act = fn->act;
-    a.p1 = static_cast<const uint16_t *>(p->p1); a.p2 = static_cast<const uint16_t *>(p->p2);
-    a.c = static_cast<const uint16_t *>(p->c);
-    a.w_in = static_cast<const uint8_t *>(fn->w_in); a.w_dn = static_cast<const uint8_t *>(fn->w_down_t);
-    a.b_up = static_cast<const uint16_t *>(fn->b_up); a.b_down = static_cast<const uint16_t *>(fn->b_down);
-    a.slot_of = fn->slot_of;
-    a.x = static_cast<const uint16_t *>(x); a.y = y;
-    a.mask_out = mask_out; a.idx_out = idx_out; a.counts_out = counts_out;
-    a.ctl = reinterpret_cast<int32_t *>(w); w += g.ctl;
-    a.z = reinterpret_cast<uint64_t *>(w); w += g.z;
-    a.tword = reinterpret_cast<uint64_t *>(w); w += g.tword;
-    a.pword = reinterpret_cast<uint64_t *>(w); w += g.tword;
-    a.ghead = reinterpret_cast<uint64_t *>(w); w += g.ghead;
-    a.ent = reinterpret_cast<uint64_t *>(w); w += g.ent;
-    a.part = reinterpret_cast<uint64_t *>(w);
-#ifdef PIK_TRACE
-    a.trace = trace;
-#else
-    (void)trace;
-#endif
-    const int wt = fn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16;
-    int rc;
-    switch (B) {
-        case 1: rc = launch_fused_batch<1>(a, wt, fn->gated, g.NT, st); break;
-        case 2: rc = launch_fused_batch<2>(a, wt, fn->gated, g.NT, st); break;
-        case 3: rc = launch_fused_batch<3>(a, wt, fn->gated, g.NT, st); break;
-        case 4: rc = launch_fused_batch<4>(a, wt, fn->gated, g.NT, st); break;
-        case 5: rc = launch_fused_batch<5>(a, wt, fn->gated, g.NT, st); break;
-        case 6: rc = launch_fused_batch<6>(a, wt, fn->gated, g.NT, st); break;
-        case 7: rc = launch_fused_batch<7>(a, wt, fn->gated, g.NT, st); break;
-        case 8: rc = launch_fused_batch<8>(a, wt, fn->gated, g.NT, st); break;
-        default: return PI_ERR_BATCH;
-    }
-    return rc == 0 ? PI_OK : PI_ERR_HIP;
+// Layout of a pi_ffn_layer workspace: the shared control block, z [B][r] fp32, the union mask [f]
+// u8, idx [f] and counts [2] int32, the listed-bit words [ceil(f/32)], the sparse-FFN scratch
+// (ffn_ws), the tail kernel's scratch (tail_ws).
+struct LayerWs {
+    int32_t *ctl;
+    float *z;
+    uint8_t *mask;
+    int32_t *idx, *counts;
+    uint32_t *bits;
+    char *ffn, *tail;
+};
+size_t layer_ws_bytes(const pi_predictor *p, const pi_ffn *fn, int B) {
+    return ctl_bytes(p->d_model) + pred_ws(p, B) + align_up((size_t)p->d_ffn) + align_up((size_t)p->d_ffn * 4) +
+           align_up(2 * sizeof(int32_t)) + align_up((size_t)mask_words(p->d_ffn) * 4) + ffn_ws(fn, B) + tail_ws(fn, B);
+}
+LayerWs layer_ws(const pi_predictor *p, const pi_ffn *fn, int B, void *ws) {
+    LayerWs L;
+    char *q = static_cast<char *>(ws);
+    L.ctl = reinterpret_cast<int32_t *>(q); q += ctl_bytes(p->d_model);
+    L.z = reinterpret_cast<float *>(q); q += pred_ws(p, B);
+    L.mask = reinterpret_cast<uint8_t *>(q); q += align_up((size_t)p->d_ffn);
+    L.idx = reinterpret_cast<int32_t *>(q); q += align_up((size_t)p->d_ffn * 4);
+    L.counts = reinterpret_cast<int32_t *>(q); q += align_up(2 * sizeof(int32_t));
+    L.bits = reinterpret_cast<uint32_t *>(q); q += align_up((size_t)mask_words(p->d_ffn) * 4);
+    L.ffn = q; q += ffn_ws(fn, B);
+    L.tail = q;
+    return L;
 }
 
 }  // namespace
@@ -579,8 +492,7 @@ size_t pi_workspace_bytes(const pi_predictor *pred, const pi_ffn *ffn, int32_t b
     if (ffn && check_ffn(ffn) != PI_OK) return 0;
     if (pred && ffn) {
         if (pred->d_model != ffn->d_model || pred->d_ffn != ffn->d_ffn) return 0;
-        return fused_ws(fused_geom(pred, ffn, batch)) + pred_ws(pred, batch) + layer_extra_ws(pred->d_ffn) +
-               ffn_ws(ffn, batch) + tail_ws(ffn, batch);
+        return layer_ws_bytes(pred, ffn, batch);
     }
     return pred ? pred_ws(pred, batch) : ffn_ws(ffn, batch);
 }
@@ -613,7 +525,7 @@ int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t
     if (!aligned16(x)) return PI_ERR_ALIGN;
     if (!ws || ws_bytes < ffn_ws(ffn, batch)) return PI_ERR_WORKSPACE;
     if (!aligned16(ws)) return PI_ERR_ALIGN;
-    return enqueue_sparse(ffn, x, batch, idx, counts, y, ws, nullptr, static_cast<hipStream_t>(stream));
+    return enqueue_sparse(ffn, x, batch, idx, counts, y, ws, static_cast<hipStream_t>(stream));
 }
 
 size_t pi_sparse_ffn_wide_workspace_bytes(const pi_ffn *ffn, int32_t batch) {
@@ -649,31 +561,27 @@ namespace {
 int layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, const float *z,
                       float *y, uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws, hipStream_t st) {
     const int f = pred->d_ffn;
-    char *p = static_cast<char *>(ws) + fused_ws(fused_geom(pred, ffn, batch)) + pred_ws(pred, batch);
-    uint8_t *mask = reinterpret_cast<uint8_t *>(p);
-    p += align_up((size_t)f);
-    int32_t *idx = reinterpret_cast<int32_t *>(p);
-    p += align_up((size_t)f * sizeof(int32_t));
-    int32_t *counts = reinterpret_cast<int32_t *>(p);
-    p += align_up(2 * sizeof(int32_t));
-    char *ffn_scr = p;
-    char *tail_scr = p + ffn_ws(ffn, batch);
-    if (mask_out) mask = mask_out;
-    if (idx_out) idx = idx_out;
-    if (counts_out) counts = counts_out;
+    const LayerWs L = layer_ws(pred, ffn, batch, ws);
+    uint8_t *mask = mask_out ? mask_out : L.mask;
+    int32_t *idx = idx_out ? idx_out : L.idx;
+    int32_t *counts = counts_out ? counts_out : L.counts;
+    const bool want_list = idx_out != nullptr || counts_out != nullptr;
     int rc;
     if (tail_persistent(pred, ffn, batch)) {
         // one kernel for the mask and the sparse FFN; the list only when it is asked for
-        const bool want_list = idx_out != nullptr || counts_out != nullptr;
-        if ((rc = enqueue_tail(pred, ffn, x, batch, z, y, (mask_out || want_list) ? mask : nullptr,
-                               static_cast<int32_t *>(ws), tail_scr, st)))
+        if ((rc = enqueue_tail(pred, ffn, x, batch, z, y, (mask_out || want_list) ? mask : nullptr, L.ctl, L.tail, st)))
             return rc;
+        return want_list ? enqueue_compact(mask, f, ffn->slot_of, idx, counts, st) : PI_OK;
+    }
+    if (layer_split(ffn, batch)) {
+        // the predictor leaves the listed flags as bit words, which the sparse FFN reads directly
+        if ((rc = enqueue_pred_l2(pred, z, batch, mask, nullptr, st, L.bits, ffn->slot_of, ffn->n_slots))) return rc;
+        if ((rc = enqueue_sparse(ffn, x, batch, nullptr, nullptr, y, L.ffn, st, L.bits))) return rc;
         return want_list ? enqueue_compact(mask, f, ffn->slot_of, idx, counts, st) : PI_OK;
     }
     if ((rc = enqueue_pred_l2(pred, z, batch, mask, nullptr, st))) return rc;
     if ((rc = enqueue_compact(mask, f, ffn->slot_of, idx, counts, st))) return rc;
-    // the sparse kernel shares the control block at the start of the workspace
-    return enqueue_sparse(ffn, x, batch, idx, counts, y, ffn_scr, static_cast<int32_t *>(ws), st);
+    return enqueue_sparse(ffn, x, batch, idx, counts, y, L.ffn, st);
 }
 
 int check_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, const float *y,
@@ -715,33 +623,17 @@ int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int
     int rc = check_layer(pred, ffn, x, batch, y, ws, ws_bytes);
     if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    float *z = reinterpret_cast<float *>(static_cast<char *>(ws) + fused_ws(fused_geom(pred, ffn, batch)));
-    if ((rc = enqueue_pred_l1(pred, x, batch, z, st))) return rc;
-    return layer_from_hidden(pred, ffn, x, batch, z, y, mask_out, idx_out, counts_out, ws, st);
-}
-
-int pi_ffn_layer_fused(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y,
-                       uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws, size_t ws_bytes,
-                       void *stream) {
-    int rc = check_pred(pred);
-    if (rc) return rc;
-    if ((rc = check_ffn(ffn))) return rc;
-    if ((rc = check_batch(batch))) return rc;
-    if (pred->d_model != ffn->d_model || pred->d_ffn != ffn->d_ffn) return PI_ERR_SHAPE;
-    if (!x || !y) return PI_ERR_NULL;
-    if (!aligned16(x)) return PI_ERR_ALIGN;
-    if (!fused_eligible(pred, ffn, batch)) return PI_ERR_SHAPE;
-    const size_t need = pi_workspace_bytes(pred, ffn, batch);
-    if (!ws || ws_bytes < need) return PI_ERR_WORKSPACE;
-    if (!aligned16(ws)) return PI_ERR_ALIGN;
-    return enqueue_fused(pred, ffn, x, batch, y, mask_out, idx_out, counts_out, ws, static_cast<hipStream_t>(stream));
+    const LayerWs L = layer_ws(pred, ffn, batch, ws);
+    if ((rc = enqueue_pred_l1(pred, x, batch, L.z, st))) return rc;
+    return layer_from_hidden(pred, ffn, x, batch, L.z, y, mask_out, idx_out, counts_out, ws, st);
 }
 
 size_t pi_sparse_ffn_h_offset(const pi_ffn *ffn, int32_t batch, int32_t *kind) {
     if (check_ffn(ffn) != PI_OK || check_batch(batch) != PI_OK || !kind) return (size_t)-1;
-    if (sparse_persistent(ffn, batch)) {
+    if (sparse_split(ffn, batch)) {
+        const SplitGeom g = split_geom(ffn, batch);
         *kind = 1;
-        return sparse_geom(ffn, batch).ctl;
+        return ctl_bytes(ffn->d_model) + g.part + g.ypart;
     }
     if (sparse_wide(ffn, batch)) {
         *kind = 3;
@@ -765,36 +657,26 @@ const char *pi_status_string(int status) {
     return "unknown status";
 }
 
-int pi_version(void) { return 100; }
+int pi_version(void) { return 200; }
 
 #ifdef PIK_TRACE
-// Diagnostic build only: pi_ffn_layer through the fused kernel with per-task timestamps.
-int pi_trace_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y, void *ws,
-                   uint64_t *trace, int32_t *tasks_out, void *stream) {
-    const FusedGeom g = fused_geom(pred, ffn, batch);
-    *tasks_out = g.NA + g.NB + g.ND + g.NE;
-    return enqueue_fused(pred, ffn, x, batch, y, nullptr, nullptr, nullptr, ws, static_cast<hipStream_t>(stream),
-                         trace);
-}
-
+// Diagnostic build only: the tail kernel and the split kernel with per-workgroup timestamps.
 int pi_trace_tail(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y, void *ws,
                   uint64_t *trace, void *stream) {
     if (!tail_persistent(pred, ffn, batch)) return PI_ERR_SHAPE;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    char *p = static_cast<char *>(ws) + fused_ws(fused_geom(pred, ffn, batch));
-    float *z = reinterpret_cast<float *>(p);
-    p += pred_ws(pred, batch) + layer_extra_ws(pred->d_ffn) + ffn_ws(ffn, batch);
-    int rc = enqueue_pred_l1(pred, x, batch, z, st);
+    const LayerWs L = layer_ws(pred, ffn, batch, ws);
+    int rc = enqueue_pred_l1(pred, x, batch, L.z, st);
     if (rc) return rc;
-    return enqueue_tail(pred, ffn, x, batch, z, y, nullptr, static_cast<int32_t *>(ws), p, st, trace);
+    return enqueue_tail(pred, ffn, x, batch, L.z, y, nullptr, L.ctl, L.tail, st, trace);
 }
 
 int pi_trace_sparse(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx, const int32_t *counts,
                     float *y, void *ws, uint64_t *trace, void *stream) {
-    if (!sparse_persistent(ffn, batch)) return PI_ERR_SHAPE;
+    if (!sparse_split(ffn, batch)) return PI_ERR_SHAPE;
     char *w = static_cast<char *>(ws);
-    return enqueue_sparse_persistent(ffn, x, batch, idx, counts, y, reinterpret_cast<int32_t *>(w),
-                                     w + sparse_geom(ffn, batch).ctl, static_cast<hipStream_t>(stream), trace);
+    return enqueue_split(ffn, x, batch, idx, counts, nullptr, y, w + ctl_bytes(ffn->d_model),
+                         static_cast<hipStream_t>(stream), trace);
 }
 #endif
 

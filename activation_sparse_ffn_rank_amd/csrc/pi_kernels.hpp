@@ -324,10 +324,18 @@ __global__ __launch_bounds__(256) void k_pred_l1(const uint16_t *__restrict__ p1
 // issues all R*NT row loads at once; lane L covers columns L*8 + 512t (t < NT, r <= 512*NT), whose
 // z values it reads from the workgroup's LDS copy of z once per token and reuses for all R rows;
 // the R sums are finished with one reduce-scatter, after which lane (64/R)*i owns row i.
+//
+// When `bits` is given, the workgroup's 32 rows (R = 8) also leave one 32-bit word of listed flags:
+// bit e of bits[blockIdx] is set when neuron 32*blockIdx + e fired for some token AND is resident
+// (slot_of == nullptr, or 0 <= slot_of[i] < n_slots) -- the placement-restricted set the sparse FFN
+// computes, which it can then read without a compaction pass.
 template <int B, int NT, int R>
 __global__ __launch_bounds__(256) void k_pred_l2(const uint16_t *__restrict__ p2, const uint16_t *__restrict__ c,
                                                  const float *__restrict__ z, int r, int f,
-                                                 float *__restrict__ logits, uint8_t *__restrict__ mask) {
+                                                 float *__restrict__ logits, uint8_t *__restrict__ mask,
+                                                 uint32_t *__restrict__ bits, const int32_t *__restrict__ slot_of,
+                                                 int n_slots) {
+    __shared__ uint32_t s_bits[4];
     extern __shared__ __align__(16) float zs[];                // z [B][r], staged once per workgroup
     const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int row0 = min((blockIdx.x * 4 + wave) * R, f);        // f: this wave has no rows
@@ -346,7 +354,13 @@ __global__ __launch_bounds__(256) void k_pred_l2(const uint16_t *__restrict__ p2
     // on a load of its own
     stage_vec16(zs, z, B * r / 4);
     __syncthreads();
-    if (row0 >= f) return;
+    if (row0 >= f) {
+        if (bits != nullptr) {
+            if (lane == 0) s_bits[wave] = 0u;
+            __syncthreads();
+        }
+        return;
+    }
     const float c_lane = (lane < R && row0 + lane < f) ? half_to_float(c[row0 + lane]) : 0.f;
     constexpr int G = kWave / R;
     const int ri = lane / G;                                  // row owned after the reduce-scatter
@@ -388,6 +402,21 @@ __global__ __launch_bounds__(256) void k_pred_l2(const uint16_t *__restrict__ p2
         }
     }
     if (owner) mask[row0 + ri] = m;
+    if (bits != nullptr) {
+        static_assert(R == 8, "a workgroup's four waves cover one 32-row word");
+        bool listed = false;
+        if (owner && m) {
+            const int sl = slot_of != nullptr ? slot_of[row0 + ri] : 0;
+            listed = sl >= 0 && sl < n_slots;
+        }
+        const uint64_t bal = __ballot(listed);                 // owners sit at lanes 8*i
+        uint32_t piece = 0;
+#pragma unroll
+        for (int i = 0; i < R; ++i) piece |= (uint32_t)((bal >> (i * G)) & 1u) << i;
+        if (lane == 0) s_bits[wave] = piece;
+        __syncthreads();
+        if (threadIdx.x == 0) bits[blockIdx.x] = s_bits[0] | (s_bits[1] << 8) | (s_bits[2] << 16) | (s_bits[3] << 24);
+    }
 }
 
 // ------------------------------------------------------------------------------ compaction

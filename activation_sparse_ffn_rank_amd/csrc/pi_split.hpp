@@ -1,0 +1,452 @@
+// pi_split.hpp -- the neuron-aware sparse FFN at batch <= 2 as two launches of (column slab x list
+// chunk) workgroups (PowerInfer, arXiv 2312.12456, method section: operators that compute only the
+// neurons predicted to fire, each neuron's weights read as contiguous rows).
+//
+// For list positions k < n, slot s_k of neuron idx[k]:
+//   h[b][k] = act(W_up[s_k] x_b + b_up[s_k])  or  max(0, W_gate[s_k] x_b) * (W_up[s_k] x_b)
+//   y[b]    = b_down + sum_k h[b][k] W_down^T[s_k]
+//
+// At batch 1 the operator reads a few thousand scattered rows once each: tens of MB, a few
+// microseconds of HBM time, so what bounds it is the number of dependent round trips between the
+// first load and y, and how evenly the bytes spread over the compute units.  Workgroup (slab s,
+// chunk c) owns columns [s*SLAB, (s+1)*SLAB) of every row of list positions [n*c/C, n*(c+1)/C):
+// every workgroup moves the same bytes, and the x values a lane needs -- its own columns -- sit in
+// its registers, so nothing is staged.
+//   k_up_split    loads its columns of the input row(s) of its positions (all at once), forms the
+//                 partial dot products (one wave-wide reduction per row) and stores them:
+//                 part[k][s][b*G + g].
+//   k_down_split  reads the S partial products of each of its positions (written by the previous
+//                 launch; those loads go out first, so h is ready early), issues the loads of its
+//                 columns of the W_down^T rows, sums the partials in slab order, applies bias and
+//                 activation, accumulates h times its columns as the rows arrive (rows whose h is
+//                 zero for every token are skipped: exact zeros), reduces its four waves in LDS and
+//                 stores its chunk partial of y.
+//   k_sum_split   one thread per output: the C chunk partials in chunk order, plus b_down.
+// The kernel boundaries are the only hand-offs: no workgroup waits on another, so any grid works,
+// and every sum runs in an order fixed by the list and the launch shape, so y is deterministic.
+// (Measured on MI355X: a kernel boundary costs less than making the last workgroups of a slab wait
+// for the others inside one launch, and far less than polling stamped words.)
+// Positions come from a device list (idx, counts: pi_sparse_ffn) or from the listed-flag words the
+// predictor wrote (each workgroup counts the set bits of all words and finds its positions by a
+// prefix sum: the ascending ranks of the set bits, exactly the list pi_compact would build).
+#pragma once
+
+#include "pi_sync.hpp"
+
+namespace pik {
+
+constexpr int kSplitMaxSlabs = 64;
+constexpr int kSplitMaxChunks = 64;
+constexpr int kSplitMaxWords = 4096;            // mask words a workgroup scans (d_ffn <= 131072)
+constexpr int kSplitThreads = 256;
+
+// Columns of a slab: 64 lanes x CPL (fp16: one 16-byte vector of 8 columns per row; Q4_0: 8 code
+// bytes = 16 columns, half of a 32-weight block, plus that block's scale).
+template <int WT>
+struct SplitCols {
+    static constexpr int CPL = WT == WT_F16 ? 8 : 16;
+    static constexpr int SLAB = CPL * kWave;
+};
+// Rows per wave per round (a round covers 4*NR positions), bounded by the registers that hold a
+// round's row pieces.
+template <int B, bool GATED, int WT>
+struct SplitRows {
+    static constexpr int NR = GATED ? 8 : 16;
+};
+
+__host__ __device__ inline int split_slab_cols(int wt) {
+    return wt == WT_F16 ? SplitCols<WT_F16>::SLAB : SplitCols<WT_Q4_0>::SLAB;
+}
+__host__ __device__ inline int split_slabs(int d, int wt) { return (d + split_slab_cols(wt) - 1) / split_slab_cols(wt); }
+// dynamic LDS of either kernel: the mask words and their prefix sums (bits mode); the down kernel
+// reuses it for the four waves' partials of its slab
+__host__ __device__ inline size_t split_dyn_lds(int B, int wt, int nwords, bool down) {
+    const size_t scan = (size_t)2 * (nwords > 0 ? nwords : 0) * sizeof(int);
+    const size_t red = down ? (size_t)4 * B * split_slab_cols(wt) * sizeof(float) : 0;
+    const size_t m = scan > red ? scan : red;
+    return m > 0 ? m : 16;
+}
+
+struct SplitArgs {
+    int d, f, n_slots, S, C, act, nwords;   // nwords > 0: positions from `bits`, else from idx/counts
+    int64_t row_bytes;
+    const uint8_t *w_in, *w_dn;
+    const uint16_t *b_up, *b_down;
+    const int32_t *slot_of;
+    const uint16_t *x;
+    float *y;
+    const int32_t *idx, *counts;            // list mode
+    const uint32_t *bits;                   // bits mode: bit i%32 of word i/32 = neuron i is listed
+    float *part;                            // [position][S][B*G] partial dot products
+    float *ypart;                           // [C][B][d] chunk partials of y
+    float *hout;                            // [B][d_ffn] h per position (slab 0 writes it), or nullptr
+#ifdef PIK_TRACE
+    uint64_t *trace;                        // [grid][8] timestamps
+#endif
+};
+
+#ifdef PIK_TRACE
+#define SPLIT_TRACE(slot)                                                                           \
+    do {                                                                                            \
+        if (a.trace != nullptr && threadIdx.x == 0) a.trace[(size_t)blockIdx.x * 8 + (slot)] = wall_clock64(); \
+    } while (0)
+#else
+#define SPLIT_TRACE(slot) ((void)0)
+#endif
+
+// Position of the k-th (0-based) set bit of w; w has more than k bits set.
+__device__ __forceinline__ int select_bit(uint32_t w, int k) {
+    int pos = 0, c;
+    c = __popc(w & 0xFFFFu); if (k >= c) { k -= c; w >>= 16; pos += 16; }
+    c = __popc(w & 0xFFu);   if (k >= c) { k -= c; w >>= 8;  pos += 8; }
+    c = __popc(w & 0xFu);    if (k >= c) { k -= c; w >>= 4;  pos += 4; }
+    c = __popc(w & 0x3u);    if (k >= c) { k -= c; w >>= 2;  pos += 2; }
+    if (k >= (int)(w & 1u)) pos += 1;
+    return pos;
+}
+
+// Exclusive prefix of v over the workgroup (4 waves) and the total; s_w holds 4 ints.
+__device__ __forceinline__ int block_excl_scan(int v, int *s_w, int lane, int wave, int &total) {
+    const int incl = wave_incl_scan(v);
+    if (lane == kWave - 1) s_w[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        before += w < wave ? s_w[w] : 0;
+        total += s_w[w];
+    }
+    return before + incl - v;
+}
+
+// The list of a launch: n, and in bits mode the mask words and their inclusive popcount prefix in
+// LDS (dyn: [nwords] words then [nwords] prefix).  Workgroup-uniform result.
+__device__ __forceinline__ int split_count(const SplitArgs &a, int *dyn, int *s_w, int tid, int lane, int wave) {
+    if (a.nwords <= 0) return __builtin_amdgcn_readfirstlane(min(max(a.counts[0], 0), a.n_slots));
+    int *s_words = dyn, *s_scan = dyn + a.nwords;
+    // thread t owns words [t*per, (t+1)*per): counts, a block scan, then inclusive prefixes
+    const int per = (a.nwords + kSplitThreads - 1) / kSplitThreads;        // <= 16
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(a.bits, (uint32_t)a.nwords * 4u);
+    uint32_t wv[16];
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int wi = tid * per + i;
+        wv[i] = bld4(rw, (i < per && wi < a.nwords) ? (uint32_t)wi * 4u : kOOB);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) cnt += __popc(wv[i]);
+    int total;
+    int run = block_excl_scan(cnt, s_w, lane, wave, total);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int wi = tid * per + i;
+        run += __popc(wv[i]);
+        if (i < per && wi < a.nwords) {
+            s_words[wi] = (int)wv[i];
+            s_scan[wi] = run;
+        }
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(total);
+}
+
+// Slot of list position q (the q-th listed neuron), or -1.
+__device__ __forceinline__ int split_slot(const SplitArgs &a, const int *dyn, int q) {
+    int id;
+    if (a.nwords > 0) {
+        const int *s_words = dyn, *s_scan = dyn + a.nwords;
+        int lo = 0, hi = a.nwords - 1;                       // first word whose prefix exceeds q
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (s_scan[mid] > q) hi = mid; else lo = mid + 1;
+        }
+        const int before = lo > 0 ? s_scan[lo - 1] : 0;
+        id = lo * 32 + select_bit((uint32_t)s_words[lo], q - before);
+    } else {
+        id = a.idx[q];
+    }
+    return slot_of_id(id, a.slot_of, a.f, a.n_slots);
+}
+
+// ------------------------------------------------------------------------------ up: partial dots
+
+template <int B, bool GATED, int WT>
+__global__ __launch_bounds__(kSplitThreads) void k_up_split(SplitArgs a) {
+    constexpr int CPL = SplitCols<WT>::CPL, SLAB = SplitCols<WT>::SLAB;
+    constexpr int G = GATED ? 2 : 1, BG = B * G;
+    constexpr int NR = SplitRows<B, GATED, WT>::NR, RMAX = 4 * NR;
+    constexpr int XV = WT == WT_F16 ? 1 : 2;              // 16-byte x vectors per lane per token
+    extern __shared__ __align__(16) int dyn[];
+    __shared__ int s_slot[RMAX];
+    __shared__ int s_w[4];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int s = blockIdx.x % a.S, c = blockIdx.x / a.S;
+    SPLIT_TRACE(1);
+    const int col = s * SLAB + lane * CPL;
+    const bool colok = col < a.d;
+    const int cc = colok ? col : 0;                       // a lane past d reads column 0, adds zeros
+    const int64_t rb = a.row_bytes;
+    const int64_t in_stride = GATED ? 2 * rb : rb;
+    // this lane's columns of x; loaded now, used (zeroed past d, q4-paired for Q4_0 rows) only after
+    // the row loads are out, so the latencies overlap
+    uint4 xr[B][XV];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int v = 0; v < XV; ++v) xr[b][v] = ld16(a.x + (size_t)b * a.d + cc + 8 * v);
+    bool x_ready = false;
+
+    const int n = split_count(a, dyn, s_w, tid, lane, wave);
+    const int p0 = (int)((int64_t)n * c / a.C), p1 = (int)((int64_t)n * (c + 1) / a.C);
+    SPLIT_TRACE(2);
+    for (int r0 = p0; r0 < p1; r0 += RMAX) {
+        const int nr = min(RMAX, p1 - r0);
+        if (tid < nr) s_slot[tid] = split_slot(a, dyn, r0 + tid);
+        __syncthreads();
+        // this wave's rows j = wave + 4i: its columns of the input row(s)
+        uint4 wu[WT == WT_F16 ? NR : 1], wg[GATED ? NR : 1];
+        uint2 qu[WT == WT_Q4_0 ? NR : 1];
+        uint16_t su[WT == WT_Q4_0 ? NR : 1];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int j = wave + 4 * i;
+            const int sl = j < nr ? s_slot[j] : -1;          // wave-uniform
+            const int64_t so = sl > 0 ? sl : 0;               // an absent row reads row 0 and is dropped
+            const uint8_t *ri = a.w_in + so * in_stride;
+            if (WT == WT_F16) {
+                wu[WT == WT_F16 ? i : 0] = ld16(ri + (GATED ? rb : 0) + (int64_t)cc * 2);
+                if (GATED) wg[GATED ? i : 0] = ld16(ri + (int64_t)cc * 2);
+            } else {
+                qu[WT == WT_Q4_0 ? i : 0] = *reinterpret_cast<const uint2 *>(ri + cc / 2);
+                su[WT == WT_Q4_0 ? i : 0] = *reinterpret_cast<const uint16_t *>(ri + a.d / 2 + (cc / 32) * 2);
+            }
+        }
+        SPLIT_TRACE(3);
+        if (!x_ready) {
+            x_ready = true;
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+#pragma unroll
+                for (int v = 0; v < XV; ++v) xr[b][v] = colok ? (WT == WT_Q4_0 ? pair_for_q4(xr[b][v]) : xr[b][v]) : zero4();
+        }
+        float pv[BG][NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                if (WT == WT_F16) {
+                    pv[b * G + G - 1][i] = dot8(wu[WT == WT_F16 ? i : 0], xr[b][0], 0.f);
+                    if (GATED) pv[b * G][i] = dot8(wg[GATED ? i : 0], xr[b][0], 0.f);
+                } else {
+                    const uint2 q = qu[WT == WT_Q4_0 ? i : 0];
+                    float t = 0.f;
+#pragma unroll
+                    for (int k = 0; k < 2; ++k) {
+                        const uint32_t w = k == 0 ? q.x : q.y;
+                        const uint4 xv = xr[b][WT == WT_Q4_0 ? k : 0];
+                        t = fdot2(q4pair(w, 0), xv.x, t);
+                        t = fdot2(q4pair(w, 4), xv.y, t);
+                        t = fdot2(q4pair(w, 8), xv.z, t);
+                        t = fdot2(q4pair(w, 12), xv.w, t);
+                    }
+                    pv[b][i] = t * half_to_float(su[WT == WT_Q4_0 ? i : 0]);
+                }
+            }
+        }
+        // one reduce-scatter per component: lane l then holds row l / (64/NR)'s sum
+#pragma unroll
+        for (int k = 0; k < BG; ++k) {
+            const float tot = reduce_scatter<NR>(pv[k], lane);
+            const int j = wave + 4 * (lane / (kWave / NR));
+            if ((lane % (kWave / NR)) == 0 && j < nr) a.part[((size_t)(r0 + j) * a.S + s) * BG + k] = tot;
+        }
+        __syncthreads();                                       // s_slot is refilled next round
+    }
+    SPLIT_TRACE(0);
+}
+
+// ------------------------------------------------------------------------------ down: h, y
+
+template <int B, bool GATED, int WT>
+__global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
+    constexpr int CPL = SplitCols<WT>::CPL, SLAB = SplitCols<WT>::SLAB;
+    constexpr int G = GATED ? 2 : 1, BG = B * G;
+    constexpr int NR = SplitRows<B, GATED, WT>::NR, RMAX = 4 * NR;
+    static_assert(RMAX * BG <= kSplitThreads, "one thread per (position, component) in the gather");
+    extern __shared__ __align__(16) int dyn[];            // scan (bits mode) | wave partials of y
+    __shared__ int s_slot[RMAX];
+    __shared__ float s_hc[RMAX][BG];
+    __shared__ float s_h[RMAX][B];
+    __shared__ int s_w[4];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int s = blockIdx.x % a.S, c = blockIdx.x / a.S;
+    SPLIT_TRACE(1);
+    const int col = s * SLAB + lane * CPL;
+    const int cc = col < a.d ? col : 0;
+    const int64_t rb = a.row_bytes;
+
+    const int n = split_count(a, dyn, s_w, tid, lane, wave);
+    const int p0 = (int)((int64_t)n * c / a.C), p1 = (int)((int64_t)n * (c + 1) / a.C);
+    SPLIT_TRACE(2);
+    float acc[B][CPL];
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int t = 0; t < CPL; ++t) acc[b][t] = 0.f;
+
+    for (int r0 = p0; r0 < p1; r0 += RMAX) {
+        const int nr = min(RMAX, p1 - r0);
+        if (tid < nr) s_slot[tid] = split_slot(a, dyn, r0 + tid);
+        __syncthreads();
+        // thread (j, k) reads component k of position j from every slab; these loads go out before
+        // the row loads, so they return first and h is ready while the rows still stream
+        // (through a buffer resource over the round's partials: no branch, an absent one reads 0)
+        const bool mine = tid < nr * BG;
+        const int jh = mine ? tid / BG : 0, kh = tid - jh * BG;
+        const __amdgpu_buffer_rsrc_t rp = buf_rsrc(a.part + (size_t)r0 * a.S * BG, (uint32_t)(nr * a.S * BG) * 4u);
+        auto part_off = [&](int u) -> uint32_t {
+            return (mine && u < a.S) ? (uint32_t)((jh * a.S + u) * BG + kh) * 4u : kOOB;
+        };
+        float pv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) pv[u] = __builtin_bit_cast(float, bld4(rp, part_off(u)));
+        // this wave's rows j = wave + 4i: its columns of the W_down^T rows
+        uint4 wd[WT == WT_F16 ? NR : 1];
+        uint2 qd[WT == WT_Q4_0 ? NR : 1];
+        uint16_t sd[WT == WT_Q4_0 ? NR : 1];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int j = wave + 4 * i;
+            const int sl = j < nr ? s_slot[j] : -1;           // wave-uniform
+            const int64_t so = sl > 0 ? sl : 0;
+            const uint8_t *rd = a.w_dn + so * rb;
+            if (WT == WT_F16) {
+                wd[WT == WT_F16 ? i : 0] = ld16(rd + (int64_t)cc * 2);
+            } else {
+                qd[WT == WT_Q4_0 ? i : 0] = *reinterpret_cast<const uint2 *>(rd + cc / 2);
+                sd[WT == WT_Q4_0 ? i : 0] = *reinterpret_cast<const uint16_t *>(rd + a.d / 2 + (cc / 32) * 2);
+            }
+        }
+        float sum = 0.f;                                        // slab order
+#pragma unroll
+        for (int u = 0; u < 16; ++u) sum += pv[u];
+        for (int s0 = 16; s0 < a.S; s0 += 16) {                 // more than 16 slabs (wide rows)
+#pragma unroll
+            for (int u = 0; u < 16; ++u) pv[u] = __builtin_bit_cast(float, bld4(rp, part_off(s0 + u)));
+#pragma unroll
+            for (int u = 0; u < 16; ++u) sum += pv[u];
+        }
+        if (mine) s_hc[jh][kh] = sum;
+        __syncthreads();
+        if (tid < nr * B) {
+            const int j = tid / B, b = tid - j * B;
+            const int sl = s_slot[j];
+            float hv;
+            if (GATED) {
+                hv = fmaxf(s_hc[j][b * 2], 0.f) * s_hc[j][b * 2 + 1];
+            } else {
+                const float bias = (a.b_up != nullptr && sl >= 0) ? half_to_float(a.b_up[sl]) : 0.f;
+                hv = fmaxf(s_hc[j][b] + bias, 0.f);
+                if (a.act) hv *= hv;                          // squared ReLU
+            }
+            if (sl < 0) hv = 0.f;
+            s_h[j][b] = hv;
+            if (s == 0 && a.hout != nullptr) a.hout[(size_t)b * a.f + r0 + j] = hv;
+        }
+        __syncthreads();
+        SPLIT_TRACE(3);
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int j = wave + 4 * i;
+            if (j >= nr) break;                                 // wave-uniform
+            float hb[B];
+            bool any = false;
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                hb[b] = s_h[j][b];
+                any |= hb[b] != 0.f;
+            }
+            if (!any) continue;                                 // adds exact zeros
+            if (WT == WT_F16) {
+                const uint4 w = wd[WT == WT_F16 ? i : 0];
+                const uint32_t wq[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const h2 pr = __builtin_bit_cast(h2, wq[p]);
+#pragma unroll
+                    for (int b = 0; b < B; ++b) {
+                        acc[b][2 * p] = fmaf(hb[b], (float)pr.x, acc[b][2 * p]);
+                        acc[b][2 * p + 1] = fmaf(hb[b], (float)pr.y, acc[b][2 * p + 1]);
+                    }
+                }
+            } else {
+                const float sc = half_to_float(sd[WT == WT_Q4_0 ? i : 0]);
+                const uint2 q = qd[WT == WT_Q4_0 ? i : 0];
+                float cf[B];
+#pragma unroll
+                for (int b = 0; b < B; ++b) cf[b] = hb[b] * sc;
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const uint32_t w = k == 0 ? q.x : q.y;
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) {
+                        // q4pair(w, 4p) = (code_p - 8, code_{p+4} - 8): columns 8k + p and 8k + p + 4
+                        const h2 pr = __builtin_bit_cast(h2, q4pair(w, 4 * p));
+#pragma unroll
+                        for (int b = 0; b < B; ++b) {
+                            acc[b][8 * k + p] = fmaf(cf[b], (float)pr.x, acc[b][8 * k + p]);
+                            acc[b][8 * k + p + 4] = fmaf(cf[b], (float)pr.y, acc[b][8 * k + p + 4]);
+                        }
+                    }
+                }
+            }
+        }
+        __syncthreads();                                        // s_slot and s_h are refilled next round
+    }
+    SPLIT_TRACE(4);
+
+    // The chunk partial of this slab: the four waves meet in LDS (fixed order), then plain stores.
+    float *s_red = reinterpret_cast<float *>(dyn);             // [4][B][CPL][64]
+#pragma unroll
+    for (int b = 0; b < B; ++b)
+#pragma unroll
+        for (int t = 0; t < CPL; ++t) s_red[((wave * B + b) * CPL + t) * kWave + lane] = acc[b][t];
+    __syncthreads();
+    for (int o = tid; o < B * SLAB; o += kSplitThreads) {
+        const int b = o / SLAB, ci = o - b * SLAB;
+        const int ln = ci / CPL, t = ci - ln * CPL;
+        const int e = (b * CPL + t) * kWave + ln;
+        const int gcol = s * SLAB + ci;
+        if (gcol < a.d)
+            a.ypart[((size_t)c * B + b) * a.d + gcol] = s_red[e] + s_red[B * CPL * kWave + e] +
+                                                          s_red[2 * B * CPL * kWave + e] + s_red[3 * B * CPL * kWave + e];
+    }
+    SPLIT_TRACE(0);
+}
+
+// ------------------------------------------------------------------------------ sum of the chunks
+
+// y[o] = b_down + sum over chunks q, in order, of ypart[q][o] (o = b*d + column); one thread per
+// output, all C loads in flight at once.
+static __global__ __launch_bounds__(kSplitThreads) void k_sum_split(const float *__restrict__ ypart, int C, int Bd,
+                                                                    int d, const uint16_t *__restrict__ b_down,
+                                                                    float *__restrict__ y) {
+    const int o = blockIdx.x * kSplitThreads + threadIdx.x;
+    if (o >= Bd) return;
+    float v[kSplitMaxChunks];
+#pragma unroll
+    for (int q = 0; q < kSplitMaxChunks; ++q) v[q] = q < C ? ypart[(size_t)q * Bd + o] : 0.f;
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < kSplitMaxChunks; ++q) sum += v[q];
+    y[o] = sum + (b_down != nullptr ? half_to_float(b_down[o % d]) : 0.f);
+}
+
+// Launch of the three kernels for batch width B in {1, 2}; C is chosen here.
+int launch_split(SplitArgs &a, int B, int wtype, int gated, hipStream_t st);
+
+}  // namespace pik

@@ -23,14 +23,15 @@
 // No compaction pass is needed: a chunk's neurons are found from its own tile words, and every
 // sum runs in an order fixed by the mask alone, so results do not depend on timing.
 //
-// Hand-offs use the stamped-word protocol of pi_fused.hpp; the workspace must be zero-filled
+// Hand-offs use the stamped-word protocol of pi_sync.hpp; the workspace must be zero-filled
 // before its first use, and every wait is bounded.
 #pragma once
 
-#include "pi_sparse.hpp"
+#include "pi_sync.hpp"
 
 namespace pik {
 
+constexpr int kSparseMaxChunks = 16;           // chunk partials per slab
 constexpr int kTailListMax = 2048;             // listed neurons a down tile handles per round
 constexpr int kTailMaxTiles = 384;             // neuron tiles up to which the tail kernel is used
 constexpr int kTailMaxTilesB2 = 1024;          // ... and at batch <= 2 (up workgroups then take
@@ -439,16 +440,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     TAIL_TRACE(0, up ? 1 : 2);
     TAIL_TRACE(9, wall_clock64());
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        if (atomicAdd(a.ctl + CTL_EXIT, 1) == a.PU + a.NE - 1) {
-            const int ls = ctl_layer_stride(a.slabs);
-            for (int i = 0; i < ls; i += 32) store_coherent_i(a.ctl + CTL_LAYER0 + i, 0);
-            store_coherent_i(a.ctl + CTL_ABORT, 0);
-            store_coherent_i(a.ctl + CTL_EXIT, 0);
-            store_coherent_i(a.ctl + CTL_EPOCH, (int32_t)stamp);
-        }
-    }
+    persistent_exit(a.ctl, stamp, a.PU + a.NE);   // the last workgroup out advances the epoch
 }
 
 // Launch of the tail kernel for batch width B (one translation unit per B); PU and C come from

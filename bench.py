@@ -1,22 +1,34 @@
 #!/usr/bin/env python3
-"""Decode-step benchmark of the predictor-gated sparse FFN stack on one MI355X.
+"""Decode-step benchmark of the predictor-gated sparse FFN stacks on one MI355X.
 
-A step is one token (or one batch of B tokens) through every layer of the stack: per layer the
-predictor GEMVs, the firing mask and its compaction, and the sparse FFN over the active neurons
-(pi_ffn_layer), with each (layer, token) fed its own seeded input vector.  Inputs and weights
-are resident in HBM before timing starts.  W warmup steps and K timed steps are replayed from
-HIP graphs captured on one stream; the timed region is bracketed by device synchronizations.
+A step is one token (or one batch of B tokens) through every layer of a stack: per layer the
+predictor GEMVs, the firing mask, the placement restriction and the sparse FFN over the active
+neurons (pi_ffn_layer), each (layer, token) fed its own seeded input vector.  Weights and inputs
+are resident in HBM before timing starts.  W warmup steps and K timed steps are replayed from HIP
+graphs captured on one stream; the timed graph is replayed 5 times, each replay bracketed by HIP
+events on that stream after a device synchronization, and the median is reported.
 
-Printed: one JSON line with tokens/s, ms per step, per-layer microseconds, the roofline of the
-step's dominant kernel on the bytes it reads (HIP events on the launch stream around a graph of
-its launches), and
-the CPU oracle's rate on a bounded sample of the same workload.
+The headline (`value`) is the largest stack that fits one GPU at batch 1: 96 layers of
+d_model 12288 / d_ffn 49152 with Q4_0 FFN rows (OPT-175B-shaped).  The same run measures every
+other workload (the 7B-, 30B- and 40B-shaped stacks, the batch-4 and batch-8 variants and the
+single small layer) into `detail.workloads`, each with its tokens/s, microseconds per layer and
+the HBM fraction of its kernels.
+
+Printed: one JSON line.  `roofline` is the sparse-FFN kernel of the headline workload (the
+kernel that reads the active rows) on its algorithmic bytes, timed with HIP events on its launch
+stream around a graph of its launches; `cpu_baseline` is the CPU oracle on a bounded sample of
+the same workload on this host's cores.
+
+`python bench.py --pmc-summary WORKLOAD DIR [DIR ...]` (no GPU needed) turns rocprofv3 --pmc
+output directories of runs of this script into profiles/counters_<WORKLOAD>.md and, when they hold
+FETCH_SIZE and WRITE_SIZE, profiles/traffic_<WORKLOAD>.json.
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -26,6 +38,10 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+HEADLINE = (5, 1)              # (stack id, batch): OPT-175B-shaped Q4_0 stack at batch 1
+DETAIL = ((5, 8), (2, 1), (3, 1), (3, 4), (4, 1), (1, 1))
+REPS = 5                       # replays of each timed graph; the median is reported
+COPY_PROBE_MIB = 256
 
 
 def kernel_sources_sha256() -> str:
@@ -41,9 +57,10 @@ def kernel_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, kernel_prefix: str):
-    """HBM bytes per launch (read + written) of the kernel whose name starts with kernel_prefix, from the
-    counter summary in profiles/ for this workload -- None when there is none or the sources changed."""
+def measured_traffic(workload: str, kernel_prefixes):
+    """HBM bytes per launch (read + written) summed over the kernels whose names start with one of
+    kernel_prefixes, from profiles/traffic_<workload>.json -- None when there is no record, a kernel
+    is missing from it, or the sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -51,27 +68,46 @@ def measured_traffic(workload: str, kernel_prefix: str):
         rec = json.load(fh)
     if rec.get("sources_sha256") != kernel_sources_sha256():
         return None
-    for name, v in rec.get("kernels", {}).items():
-        if name.startswith(kernel_prefix):
-            return int(v["read_bytes"]) + int(v["write_bytes"])
-    return None
+    total = 0
+    for pre in kernel_prefixes:
+        hits = [v for name, v in rec.get("kernels", {}).items() if name.startswith(pre)]
+        if not hits:
+            return None
+        total += int(hits[0]["read_bytes"]) + int(hits[0]["write_bytes"])
+    return total
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=128, help="timed decode steps (tokens per sequence)")
-    ap.add_argument("--warmup", type=int, default=16)
-    ap.add_argument("--config", type=int, default=2, help="layer-stack configuration id (1-5)")
-    ap.add_argument("--batch", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=56, help="timed decode steps of the headline workload")
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--config", type=int, default=HEADLINE[0], help="stack id (1-5) of the headline workload")
+    ap.add_argument("--batch", type=int, default=HEADLINE[1])
     ap.add_argument("--layers", type=int, default=0, help="use only the first N layers (0 = all)")
-    ap.add_argument("--roofline-steps", type=int, default=16, help="tokens whose launches the roofline pass times")
+    ap.add_argument("--roofline-steps", type=int, default=16, help="tokens whose launches the per-kernel legs time")
+    ap.add_argument("--detail-steps", type=int, default=24, help="timed steps of each detail workload")
+    ap.add_argument("--no-detail", action="store_true", help="measure the headline workload only")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after the measurement, run one device-to-device copy of this many MiB (a kernel of "
                          "known traffic, for scaling hardware byte counters)")
+    ap.add_argument("--pmc-summary", nargs="+", metavar=("WORKLOAD", "DIR"),
+                    help="summarize rocprofv3 --pmc directories into profiles/ (no GPU) and exit")
+    ap.add_argument("--pmc-command", action="append", default=[],
+                    help="with --pmc-summary: the command that made each directory (recorded in the summary)")
     return ap.parse_args()
 
 
@@ -79,36 +115,51 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the sparse-FFN hot path has no multi-GPU leg "
-              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import synth
-    from activation_sparse_ffn_rank_amd import DeviceLayer, _abi
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    cfg = synth.CONFIGS[args.config]
-    B = args.batch
-    L = cfg.layers if args.layers <= 0 else min(args.layers, cfg.layers)
-    K, W = args.steps, args.warmup
-    dev = torch.device("cuda:0")
-
-    # ------------------------------------------------------------------ weights and inputs
-    t0 = time.time()
-    layers = []
-    for l in range(L):
-        host = synth.make_layer(cfg, l)
-        layers.append(DeviceLayer.from_host(host, device=dev))
-        del host
-    x_all = synth.make_x_all(cfg, L, W + K, B)                  # [T][L][B][d] fp16 bits
-    xd = torch.from_numpy(x_all.view(np.int16)).to(dev)
+def timed_graph(torch, stream, fn, reps=REPS):
+    """Capture fn() into a graph, replay once to warm, then time `reps` replays with HIP events on
+    `stream` (each after a device synchronization); returns the median elapsed ms."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        fn()
+    g.replay()
     torch.cuda.synchronize()
-    log(f"config {cfg.cid} ({cfg.name}): {L} layers generated and resident in {time.time() - t0:.1f}s")
+    times = []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del g
+    return statistics.median(times), times
 
+
+def ffn_kernel_names(h_kind: int, B: int, cfg, synth):
+    """(label, rocprof name prefixes) of the kernels one pi_sparse_ffn call runs, by its form."""
+    g = "true" if cfg.gated else "false"
+    w = 1 if cfg.wtype == synth.F16 else 2
+    if h_kind == 1:
+        return "k_sparse_ffn", [f"void pik::k_sparse_ffn<{B}, {g}, {w}>"]
+    if h_kind == 2:
+        return "k_sparse_up + k_sparse_down", [f"void pik::k_sparse_up<{B}, {g}, {w}>", f"void pik::k_sparse_down<{B}, {w}>"]
+    if h_kind == 3:
+        return "k_wide_up + k_wide_down", ["void pik::k_wide_up<", "void pik::k_wide_down<"]
+    if h_kind == 4:
+        return "k_ffn_split", [f"void pik::k_ffn_split<{B}, {g}, {w},"]
+    return f"kind {h_kind}", []
+
+
+# ---------------------------------------------------------------------------------- one workload
+
+def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=False, cold=False):
+    """Time K decode steps of `layers` at batch B (median of REPS graph replays) and the per-kernel
+    legs; returns the workload's record (plus private fields starting with '_')."""
+    L = len(layers)
+    tokens = W + K
+    x_all = synth.make_x_all(cfg, L, tokens, B)                 # [T][L][B][d] fp16 bits
+    xd = torch.from_numpy(x_all.view(np.int16)).to(dev)
     ws = layers[0].workspace(B, device=dev)
     y = torch.empty((L, B, cfg.d), dtype=torch.float32, device=dev)
 
@@ -117,49 +168,34 @@ def main():
             lay = layers[l]
             _abi.pi_ffn_layer(lay.pred, lay.ffn, xd[t, l], B, y[l], None, None, None, ws)
 
-    # ------------------------------------------------------------------ graph capture + timing
-    stream = torch.cuda.Stream(device=dev)
     with torch.cuda.stream(stream):
         step(0)
         torch.cuda.synchronize()
-        if not args.no_graph:
-            g_warm, g_timed = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g_warm, stream=stream):
-                for t in range(W):
-                    step(t)
-            with torch.cuda.graph(g_timed, stream=stream):
-                for t in range(W, W + K):
-                    step(t)
-            torch.cuda.synchronize()
-            g_warm.replay()
-        else:
+
+        def warm():
             for t in range(W):
                 step(t)
-        torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(stream)
-        if not args.no_graph:
-            g_timed.replay()
-        else:
+
+        def timed():
             for t in range(W, W + K):
                 step(t)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        elapsed_ms = ev0.elapsed_time(ev1)
-    status = _abi.workspace_status(ws)
-    if status != 0:
-        raise RuntimeError(f"workspace status {status}: a cross-workgroup wait timed out; results invalid")
-    log(f"timed {K} steps: {elapsed_ms:.3f} ms")
 
-    # ------------------------------------------------------------------ per-kernel legs (HIP events)
-    # pi_ffn_layer is pi_predict_hidden (z = ReLU(P1 x), one kernel) followed by
-    # pi_ffn_layer_from_hidden (logits, mask and the sparse FFN: one persistent kernel on path 1).
-    # An eager pass runs both on R tokens x L layers, keeping every z and every index list, and
-    # runs pi_sparse_ffn on each list (the sparse FFN alone, one kernel) to count the listed
-    # neurons whose h is nonzero for some token.  Then the R*L launches of each entry point are
-    # captured into a graph of their own and timed with HIP events on the launch stream around
-    # its replay: elapsed / launches is the average launch duration, back to back as in the step.
-    R = min(args.roofline_steps, K)
+        g_warm = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_warm, stream=stream):
+            warm()
+        g_warm.replay()
+        torch.cuda.synchronize()
+        del g_warm
+        elapsed_ms, rep_ms = timed_graph(torch, stream, timed)
+    if _abi.workspace_status(ws) != 0:
+        raise RuntimeError(f"workspace status {_abi.workspace_status(ws)}: a cross-workgroup wait timed out")
+
+    # ---- per-kernel legs.  pi_ffn_layer = pi_predict_hidden (z = ReLU(P1 x)) followed by
+    # pi_ffn_layer_from_hidden (logits, mask and the sparse FFN).  An eager pass runs both on R tokens
+    # x L layers, keeping every z and index list, and runs pi_sparse_ffn on each list (the sparse FFN
+    # alone) to count the listed neurons whose h is nonzero for some token.  Each entry point's R*L
+    # launches are then captured into a graph of their own and timed (median of REPS replays).
+    R = min(R, K)
     N = R * L
     rb = cfg.row_bytes()
     in_rows = 2 if cfg.gated else 1
@@ -203,243 +239,419 @@ def main():
         cnt_host = cnt_all.cpu().numpy().astype(np.float64)
         leg_us = {}
         for name, fn in (("hidden", run_hidden), ("rest", run_rest), ("sparse_ffn", run_sparse)):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                fn()
-            g.replay()                                          # warm
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            leg_us[name] = e0.elapsed_time(e1) * 1000.0 / N
-            del g
+            ms, _ = timed_graph(torch, stream, fn)
+            leg_us[name] = ms * 1000.0 / N
     for w in (ws, ws_f):
         if _abi.workspace_status(w) != 0:
             raise RuntimeError("workspace status nonzero: a cross-workgroup wait timed out")
     n_act, n_pred = cnt_host[:, 0], cnt_host[:, 1]
     vec_bytes = B * cfg.d * (2 + 4) + 2 * cfg.d                  # x in, y out, b_down
     slot_bytes = 4 * cfg.f if layers[0].slot_of is not None else 0
-    # sparse FFN alone: the persistent kernel and the MFMA form read every listed row (the former's
-    # down-row loads go out before h is known); the GEMV two-kernel form skips down rows whose h is
-    # zero for every token
     _, h_kind = _abi.pi_sparse_ffn_h_offset(layers[0].ffn, B)
-    n_read_down = n_act if h_kind in (1, 3) else n_live
+    # rows the sparse FFN reads: every listed input row; the down rows of every listed neuron except
+    # in the GEMV two-kernel form, which skips those whose h is zero for every token
+    n_read_down = n_live if h_kind == 2 else n_act
     ffn_touched = n_act * in_rows * rb + n_read_down * rb + 8 * n_act + vec_bytes
     ffn_predicted = n_act * (in_rows + 1) * rb + 8 * n_act + vec_bytes
-    # the rest of the layer on path 1 (one kernel): P2 and c, z, every listed row in and down
+    # the rest of the layer: P2 and c, z, every listed row in and down
     rest_bytes = 2 * cfg.f * cfg.r + 2 * cfg.f + 4 * B * cfg.r + slot_bytes + n_act * (in_rows + 1) * rb + vec_bytes
     hidden_bytes = 2 * cfg.r * cfg.d + 2 * B * cfg.d + 4 * B * cfg.r
-    gname = "true" if cfg.gated else "false"
-    wname = 1 if cfg.wtype == synth.F16 else 2
+    ffn_label, ffn_prefixes = ffn_kernel_names(h_kind, B, cfg, synth)
+    g = "true" if cfg.gated else "false"
+    w = 1 if cfg.wtype == synth.F16 else 2
     if path == 1:
-        roof_kernel = ("k_layer_tail (pi_ffn_layer_from_hidden: predictor logits and mask, gathered up/gate rows "
-                       "with ReLU/ReGLU, active rows of W_down^T)")
-        roof_bytes, roof_us = float(rest_bytes.mean()), leg_us["rest"]
-        roof_prefix = f"void pik::k_layer_tail<{B}, {gname}, {wname},"
+        rest_label, rest_prefixes = "k_layer_tail", [f"void pik::k_layer_tail<{B}, {g}, {w},"]
     else:
-        roof_kernel = "k_sparse_ffn (pi_sparse_ffn: gathered up/gate rows with ReLU/ReGLU + active rows of W_down^T)"
-        roof_bytes, roof_us = float(ffn_touched.mean()), leg_us["sparse_ffn"]
-        roof_prefix = f"void pik::k_sparse_ffn<{B}, {gname}, {wname}>"
-    workload_tag = f"{cfg.name}_b{B}"
-    roof_traffic = measured_traffic(workload_tag, roof_prefix) if L == cfg.layers else None
-    roof_gbs = roof_bytes / (roof_us * 1e-6) / 1e9
+        rest_label, rest_prefixes = "k_pred_l2 + " + ffn_label, ["void pik::k_pred_l2<"] + ffn_prefixes
     step_bytes = (pred_bytes + float(ffn_touched.mean())) * L
-    # ------------------------------------------------------------------ host half (placement stacks)
-    # With a placement, the predicted neurons that are not resident are the host's share of the
-    # hybrid split (pi_cold_ffn_host over the cold rows in host memory).  Timed here on the masks
-    # the device produced, for the first layers of the stack.
-    cold = None
-    if layers[0].slot_of is not None:
-        import synth as _s
-        n_lay = min(L, 2)
-        masks_h = masks.cpu().numpy()
-        hosts = []
-        for l in range(n_lay):
-            _, _, _, freq = _s.make_predictor(cfg, l)
-            cold_ids = np.setdiff1d(np.arange(cfg.f, dtype=np.int32), _s.hot_set(freq, cfg.n_hot()))
-            w_in_c, w_dn_c, b_up_c, _ = _s.make_ffn(cfg, l, cold_ids)
-            slot_c = np.full(cfg.f, -1, np.int32)
-            slot_c[cold_ids] = np.arange(cold_ids.size, dtype=np.int32)
-            hosts.append(_abi.HostFFN(w_in_c, w_dn_c, d_model=cfg.d, d_ffn=cfg.f, gated=cfg.gated, wtype=cfg.wtype,
-                                      slot_of=slot_c, b_up=b_up_c))
-        ws_h = np.zeros(_abi.pi_cold_workspace_bytes(hosts[0], B), np.uint8)
-        y_h = np.empty((B, cfg.d), np.float32)
-        # every host thread, and half of them (hosts that expose two threads per core often run this
-        # memory-bound loop faster on one per core); the faster is reported, with its count
-        best = None
-        for nthr in sorted({_s.num_threads(), max(1, _s.num_threads() // 2)}):
-            times, counts_c = [], []
+    ms_per_step = elapsed_ms / K
+
+    def gbs(nbytes, us):
+        return nbytes / (us * 1e-6) / 1e9
+
+    rec = {
+        "workload": f"{cfg.name}_b{B}",
+        "description": describe(cfg, L, B, synth),
+        "batch": B, "layers": L, "steps": K, "warmup": W,
+        "tokens_per_s": round(B * K / (elapsed_ms / 1e3), 2),
+        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_replays": [round(t / K, 4) for t in rep_ms],
+        "us_per_layer": round(ms_per_step * 1000.0 / L, 3),
+        "step_gb_algorithmic": round(step_bytes / 1e9, 4),
+        "step_gbs": round(step_bytes / 1e9 / (ms_per_step / 1e3), 1),
+        "step_hbm_frac": round(step_bytes / 1e9 / (ms_per_step / 1e3) / PEAK_HBM_GBS, 4),
+        "layer_path": path,
+        "kernels": {
+            "predict_hidden": {"kernel": "k_pred_l1", "us": round(leg_us["hidden"], 3), "bytes": hidden_bytes,
+                               "gbs": round(gbs(hidden_bytes, leg_us["hidden"]), 1),
+                               "frac": round(gbs(hidden_bytes, leg_us["hidden"]) / PEAK_HBM_GBS, 4)},
+            "layer_from_hidden": {"kernel": rest_label, "us": round(leg_us["rest"], 3),
+                                  "bytes": round(float(rest_bytes.mean())),
+                                  "gbs": round(gbs(float(rest_bytes.mean()), leg_us["rest"]), 1),
+                                  "frac": round(gbs(float(rest_bytes.mean()), leg_us["rest"]) / PEAK_HBM_GBS, 4)},
+            "sparse_ffn": {"kernel": ffn_label, "us": round(leg_us["sparse_ffn"], 3),
+                           "bytes": round(float(ffn_touched.mean())),
+                           "bytes_predicted_rows": round(float(ffn_predicted.mean())),
+                           "gbs": round(gbs(float(ffn_touched.mean()), leg_us["sparse_ffn"]), 1),
+                           "frac": round(gbs(float(ffn_touched.mean()), leg_us["sparse_ffn"]) / PEAK_HBM_GBS, 4)},
+        },
+        "predictor_bytes": pred_bytes,
+        "active_density": round(float(n_act.mean()) / cfg.f, 4),
+        "predicted_density": round(float(n_pred.mean()) / cfg.f, 4),
+        "covered_share": round(float(n_act.sum() / max(n_pred.sum(), 1)), 4),
+        "down_rows_zero_h_share": round(1.0 - float(n_live.sum()) / max(float(n_act.sum()), 1.0), 4),
+        "_ffn_prefixes": ffn_prefixes, "_rest_prefixes": rest_prefixes,
+        "_ffn": (float(ffn_touched.mean()), leg_us["sparse_ffn"], ffn_label, N),
+        "_rest": (float(rest_bytes.mean()), leg_us["rest"], rest_label, N),
+    }
+    if cold and layers[0].slot_of is not None:
+        rec["cold_host"] = cold_leg(torch, synth, _abi, cfg, layers, B, x_all, xd, masks, cases, ws, stream, dev,
+                                    ms_per_step)
+    if wide and B == 1 and R >= 16 and layers[0].slot_of is None:
+        rec["wide_b16"] = wide_leg(torch, _abi, cfg, layers, xd, masks, cases, stream, dev, in_rows, rb)
+    del xd, z_all, masks, idx_all, ws_f, ws
+    return rec
+
+
+def describe(cfg, L, B, synth):
+    return (f"{cfg.name}: {L} layers, d_model={cfg.d}, d_ffn={cfg.f}, predictor rank {cfg.r}, "
+            f"{'ReGLU' if cfg.gated else 'ReLU'}, {'fp16' if cfg.wtype == synth.F16 else 'Q4_0'} weights, "
+            f"batch {B}, Zipf firing at {cfg.density:.0%} target density"
+            + (f", hottest {cfg.hot_frac:.0%} resident" if cfg.hot_frac else ""))
+
+
+def cold_leg(torch, synth, _abi, cfg, layers, B, x_all, xd, masks, cases, ws, stream, dev, ms_per_step):
+    """Host half of the hybrid split: the predicted neurons that are not resident, computed by
+    pi_cold_ffn_host on the masks the device produced (first two layers), and the hybrid layer end
+    to end (device layer -> mask to pinned host memory -> host half -> host y added on the device)."""
+    L = len(layers)
+    in_rows = 2 if cfg.gated else 1
+    n_lay = min(L, 2)
+    masks_h = masks.cpu().numpy()
+    hosts = []
+    for l in range(n_lay):
+        _, _, _, freq = synth.make_predictor(cfg, l)
+        cold_ids = np.setdiff1d(np.arange(cfg.f, dtype=np.int32), synth.hot_set(freq, cfg.n_hot()))
+        w_in_c, w_dn_c, b_up_c, _ = synth.make_ffn(cfg, l, cold_ids)
+        slot_c = np.full(cfg.f, -1, np.int32)
+        slot_c[cold_ids] = np.arange(cold_ids.size, dtype=np.int32)
+        hosts.append(_abi.HostFFN(w_in_c, w_dn_c, d_model=cfg.d, d_ffn=cfg.f, gated=cfg.gated, wtype=cfg.wtype,
+                                  slot_of=slot_c, b_up=b_up_c))
+    ws_h = np.zeros(_abi.pi_cold_workspace_bytes(hosts[0], B), np.uint8)
+    y_h = np.empty((B, cfg.d), np.float32)
+    # every host thread, and half of them (hosts that expose two threads per core often run this
+    # memory-bound loop faster on one per core); the faster is reported, with its count
+    best = None
+    for nthr in sorted({synth.num_threads(), max(1, synth.num_threads() // 2)}):
+        times, counts_c = [], []
+        for i, (t, l) in enumerate(cases):
+            if l >= n_lay:
+                continue
+            x_h = np.ascontiguousarray(x_all[t, l])
+            s0 = time.perf_counter()
+            counts_c.append(_abi.pi_cold_ffn_host(hosts[l], x_h, B, masks_h[i], y_h, ws_h, nthr))
+            times.append(time.perf_counter() - s0)
+        med = float(np.median(times))
+        if best is None or med < best[0]:
+            best = (med, nthr, counts_c, len(times))
+    nthr = best[1]
+    mask_pin = torch.empty(cfg.f, dtype=torch.uint8, pin_memory=True)
+    ycold_pin = torch.empty((B, cfg.d), dtype=torch.float32, pin_memory=True)
+    y_dev = torch.empty((B, cfg.d), dtype=torch.float32, device=dev)
+    m_dev = torch.empty(cfg.f, dtype=torch.uint8, device=dev)
+    yc_dev = torch.empty((B, cfg.d), dtype=torch.float32, device=dev)
+    hyb = []
+    with torch.cuda.stream(stream):
+        for rep in range(2):
             for i, (t, l) in enumerate(cases):
                 if l >= n_lay:
                     continue
-                x_h = np.ascontiguousarray(x_all[t, l])
+                torch.cuda.synchronize()
                 s0 = time.perf_counter()
-                counts_c.append(_abi.pi_cold_ffn_host(hosts[l], x_h, B, masks_h[i], y_h, ws_h, nthr))
-                times.append(time.perf_counter() - s0)
-            med = float(np.median(times))
-            if best is None or med < best[0]:
-                best = (med, nthr, counts_c, len(times))
-        # the hybrid layer end to end, as the method runs it (device over the resident neurons,
-        # host over the rest, y's added), with the layer's dependencies kept in order: device
-        # layer -> mask to pinned host memory -> host half -> host y to the device -> added to y
-        nthr = best[1]
-        mask_pin = torch.empty(cfg.f, dtype=torch.uint8, pin_memory=True)
-        ycold_pin = torch.empty((B, cfg.d), dtype=torch.float32, pin_memory=True)
-        y_dev = torch.empty((B, cfg.d), dtype=torch.float32, device=dev)
-        m_dev = torch.empty(cfg.f, dtype=torch.uint8, device=dev)
-        yc_dev = torch.empty((B, cfg.d), dtype=torch.float32, device=dev)
-        hyb = []
-        with torch.cuda.stream(stream):
-            for rep in range(2):
-                for i, (t, l) in enumerate(cases):
-                    if l >= n_lay:
-                        continue
-                    torch.cuda.synchronize()
-                    s0 = time.perf_counter()
-                    _abi.pi_ffn_layer(layers[l].pred, layers[l].ffn, xd[t, l], B, y_dev, m_dev, None, None, ws)
-                    mask_pin.copy_(m_dev, non_blocking=True)
-                    stream.synchronize()
-                    _abi.pi_cold_ffn_host(hosts[l], np.ascontiguousarray(x_all[t, l]), B, mask_pin.numpy(),
-                                          ycold_pin.numpy(), ws_h, nthr)
-                    yc_dev.copy_(ycold_pin, non_blocking=True)
-                    y_dev.add_(yc_dev)
-                    stream.synchronize()
-                    if rep == 1:
-                        hyb.append(time.perf_counter() - s0)
-        del hosts
-        cold_us = 1e6 * best[0]
-        counts_c = best[2]
-        cold = {"host_us_per_layer": round(cold_us, 2), "neurons_per_layer": round(float(np.mean(counts_c)), 1),
-                "rows_mb_per_layer": round(float(np.mean(counts_c)) * (in_rows + 1) * rb / 1e6, 3),
-                "threads": best[1], "calls": best[3],
-                "hybrid_layer_us": round(1e6 * float(np.median(hyb)), 2),
-                "device_only_layer_us": round(elapsed_ms * 1000.0 / (K * L), 2)}
-    # ------------------------------------------------------------------ 16-token batches on MFMA
-    # pi_sparse_ffn_wide over each layer's union of 16 tokens' predicted lists (the masks of the
-    # eager pass above, ORed and compacted outside the timed region), x of those 16 tokens; one
-    # graph of L launches, timed with HIP events on the launch stream.
-    wide = None
-    if B == 1 and R >= 16 and layers[0].slot_of is None:
-        with torch.cuda.stream(stream):
-            idx_w = torch.empty((L, cfg.f), dtype=torch.int32, device=dev)
-            cnt_w = torch.empty((L, 2), dtype=torch.int32, device=dev)
-            x_w = torch.empty((L, 16, cfg.d), dtype=torch.int16, device=dev)
+                _abi.pi_ffn_layer(layers[l].pred, layers[l].ffn, xd[t, l], B, y_dev, m_dev, None, None, ws)
+                mask_pin.copy_(m_dev, non_blocking=True)
+                stream.synchronize()
+                _abi.pi_cold_ffn_host(hosts[l], np.ascontiguousarray(x_all[t, l]), B, mask_pin.numpy(),
+                                      ycold_pin.numpy(), ws_h, nthr)
+                yc_dev.copy_(ycold_pin, non_blocking=True)
+                y_dev.add_(yc_dev)
+                stream.synchronize()
+                if rep == 1:
+                    hyb.append(time.perf_counter() - s0)
+    rb = cfg.row_bytes()
+    return {"host_us_per_layer": round(1e6 * best[0], 2), "neurons_per_layer": round(float(np.mean(best[2])), 1),
+            "rows_mb_per_layer": round(float(np.mean(best[2])) * (in_rows + 1) * rb / 1e6, 3),
+            "threads": best[1], "calls": best[3],
+            "hybrid_layer_us": round(1e6 * float(np.median(hyb)), 2),
+            "device_only_layer_us": round(ms_per_step * 1000.0 / L, 2)}
+
+
+def wide_leg(torch, _abi, cfg, layers, xd, masks, cases, stream, dev, in_rows, rb):
+    """pi_sparse_ffn_wide over each layer's union of 16 tokens' predicted lists (the masks of the
+    eager pass, ORed and compacted outside the timed region), x of those 16 tokens."""
+    L = len(layers)
+    with torch.cuda.stream(stream):
+        idx_w = torch.empty((L, cfg.f), dtype=torch.int32, device=dev)
+        cnt_w = torch.empty((L, 2), dtype=torch.int32, device=dev)
+        x_w = torch.empty((L, 16, cfg.d), dtype=torch.int16, device=dev)
+        for l in range(L):
+            sel = [i for i, (t, ll) in enumerate(cases) if ll == l][:16]
+            union = masks[sel].amax(dim=0).contiguous()
+            _abi.pi_compact(union, cfg.f, None, idx_w[l], cnt_w[l])
+            x_w[l] = xd[[cases[i][0] for i in sel], l, 0]
+        ws_w = torch.empty(_abi.pi_sparse_ffn_wide_workspace_bytes(layers[0].ffn, 16), dtype=torch.uint8, device=dev)
+        y_w = torch.empty((16, cfg.d), dtype=torch.float32, device=dev)
+
+        def run_wide():
             for l in range(L):
-                sel = [i for i, (t, ll) in enumerate(cases) if ll == l][:16]
-                union = masks[sel].amax(dim=0).contiguous()
-                _abi.pi_compact(union, cfg.f, None, idx_w[l], cnt_w[l])
-                x_w[l] = xd[[cases[i][0] for i in sel], l, 0]
-            ws_w = torch.empty(_abi.pi_sparse_ffn_wide_workspace_bytes(layers[0].ffn, 16), dtype=torch.uint8,
-                               device=dev)
-            y_w = torch.empty((16, cfg.d), dtype=torch.float32, device=dev)
+                _abi.pi_sparse_ffn_wide(layers[l].ffn, x_w[l], 16, idx_w[l], cnt_w[l], y_w, ws_w)
 
-            def run_wide():
-                for l in range(L):
-                    _abi.pi_sparse_ffn_wide(layers[l].ffn, x_w[l], 16, idx_w[l], cnt_w[l], y_w, ws_w)
+        ms, _ = timed_graph(torch, stream, run_wide)
+        wide_us = ms * 1000.0 / L
+    n_w = cnt_w[:, 0].cpu().numpy().astype(np.float64)
+    wide_bytes = float((n_w * (in_rows + 1) * rb + 4 * n_w).mean()) + 16 * cfg.d * (2 + 4) + 2 * cfg.d
+    return {"batch": 16, "us_per_layer": round(wide_us, 3), "neurons_per_layer": round(float(n_w.mean()), 1),
+            "algorithmic_bytes_per_layer": int(wide_bytes),
+            "gbs": round(wide_bytes / (wide_us * 1e-6) / 1e9, 1),
+            "hbm_frac": round(wide_bytes / (wide_us * 1e-6) / 8e12, 4),
+            "kernels": "k_wide_up + k_wide_down (pi_sparse_ffn_wide, MFMA f16)"}
 
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                run_wide()
-            g.replay()
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            wide_us = e0.elapsed_time(e1) * 1000.0 / L
-            del g
-        n_w = cnt_w[:, 0].cpu().numpy().astype(np.float64)
-        wide_bytes = float((n_w * (in_rows + 1) * rb + 4 * n_w).mean()) + 16 * cfg.d * (2 + 4) + 2 * cfg.d
-        wide = {"batch": 16, "us_per_layer": round(wide_us, 3), "neurons_per_layer": round(float(n_w.mean()), 1),
-                "algorithmic_bytes_per_layer": int(wide_bytes),
-                "gb_per_s": round(wide_bytes / (wide_us * 1e-6) / 1e9, 1),
-                "hbm_frac": round(wide_bytes / (wide_us * 1e-6) / 8e12, 4),
-                "kernels": "k_wide_up + k_wide_down (pi_sparse_ffn_wide, MFMA 16x16x16 f16)"}
-        log(f"16-token sparse FFN (MFMA): {wide_us:.1f} us/layer over {n_w.mean():.0f} neurons")
 
-    # ------------------------------------------------------------------ CPU oracle baseline
+def cpu_oracle(synth, oracle, cfg, L, B, tokens, budget_s, threads=None):
+    """The oracle's whole layer (predictor, mask, compaction, sparse FFN) on layers 0..3 of the stack,
+    cycling over the seeded tokens until `budget_s` seconds of wall time, scaled to an L-layer step."""
+    if threads is not None:
+        oracle.set_num_threads(threads)
+    n_lay = min(L, 4)
+    hosts = [synth.make_layer(cfg, l) for l in range(n_lay)]
+    x_all = synth.make_x_all(cfg, n_lay, tokens, B)
+    done, spent, t = 0, 0.0, 0
+    while spent < budget_s:
+        for l in range(n_lay):
+            s0 = time.perf_counter()
+            oracle.ffn_layer(hosts[l], x_all[t % tokens, l], want_logits=False)
+            spent += time.perf_counter() - s0
+            done += 1
+        t += 1
+    used = oracle.num_threads()
+    per_layer = spent / done
+    return {"value": round(B / (per_layer * L), 3), "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{done} evaluations of the whole layer (predictor, mask, compaction, sparse FFN over the "
+                      f"listed neurons, fp64) at batch {B} on {used} threads of {cpu_model()}: layers 0..{n_lay - 1} "
+                      f"of the {cfg.name} stack, {t} token steps cycling over {tokens} seeded inputs; {spent:.1f}s, "
+                      f"{per_layer * 1e3:.2f} ms per layer, scaled to the {L}-layer step"}
+
+
+# ---------------------------------------------------------------------------------- counters
+
+def pmc_summary(args):
+    """Summarize rocprofv3 --pmc output directories (runs of this script) per kernel."""
+    import collections
+    import csv
+    import glob
+    workload, dirs = args.pmc_summary[0], args.pmc_summary[1:]
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))   # counter -> kernel -> values
+    probe = {}
+    for dd in dirs:
+        files = glob.glob(os.path.join(dd, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {dd}")
+        rows = [r for f in files for r in csv.DictReader(open(f))]
+        for r in rows:
+            vals[r["Counter_Name"]][r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        # the copy probe is the last device copy of the run (COPY_PROBE_MIB MiB read and written)
+        copies = [r for r in rows if "copyBuffer" in r["Kernel_Name"] or "copy" in r["Kernel_Name"].lower()]
+        for cname in ("FETCH_SIZE", "WRITE_SIZE"):
+            cr = [r for r in copies if r["Counter_Name"] == cname]
+            if cr:
+                last = max(cr, key=lambda r: int(r["Dispatch_Id"]))
+                probe[cname] = (last["Kernel_Name"], float(last["Counter_Value"]))
+    ours = sorted({k for c in vals.values() for k in c if k.startswith(("void pik::", "pik::"))})
+    probe_kib = COPY_PROBE_MIB * 1024
+    scale = {c: probe_kib / v for c, (_, v) in probe.items() if v > 0}
+    lines = [f"# Hardware counters per dispatch: {workload}", "",
+             "Commands (from the repository root; one counter group per run):", "", "```"]
+    lines += args.pmc_command or ["(not recorded)"]
+    lines += ["```", "", f"Sources sha256: `{kernel_sources_sha256()}`", ""]
+    if scale:
+        lines.append("Calibration: the last device copy of each run moves "
+                     f"{COPY_PROBE_MIB} MiB ({probe_kib} KiB) read and written; "
+                     + ", ".join(f"{c} reads {probe[c][1]:.0f} KiB for it (scale {scale[c]:.3f})" for c in scale) + ".")
+        lines.append("")
+    counters = sorted(vals)
+    lines.append("| kernel | dispatches | " + " | ".join(counters) + " |")
+    lines.append("|---|---:|" + "---:|" * len(counters))
+    for k in ours:
+        n = max(len(vals[c].get(k, [])) for c in counters)
+        cells = []
+        for c in counters:
+            v = vals[c].get(k)
+            cells.append(f"{sum(v) / len(v):.4g}" if v else "")
+        lines.append(f"| `{k[:90]}` | {n} | " + " | ".join(cells) + " |")
+    derived = []
+    for k in ours:
+        d = {}
+        mean = lambda c: (sum(vals[c][k]) / len(vals[c][k])) if k in vals.get(c, {}) else None
+        if mean("FETCH_SIZE") is not None and "FETCH_SIZE" in scale:
+            d["read MB"] = mean("FETCH_SIZE") * 1024 * scale["FETCH_SIZE"] / 1e6
+        if mean("WRITE_SIZE") is not None and "WRITE_SIZE" in scale:
+            d["written MB"] = mean("WRITE_SIZE") * 1024 * scale["WRITE_SIZE"] / 1e6
+        hit, miss = mean("TCC_HIT_sum"), mean("TCC_MISS_sum")
+        if hit is not None and miss is not None and hit + miss > 0:
+            d["L2 hit rate"] = hit / (hit + miss)
+        wc, gui = mean("SQ_WAVE_CYCLES"), mean("GRBM_GUI_ACTIVE")
+        if wc is not None and gui:
+            d["mean waves per CU"] = wc / gui / 256.0
+        iv, av = mean("SQ_INSTS_VALU"), mean("SQ_ACTIVE_INST_VALU")
+        if iv is not None and mean("SQ_WAVES"):
+            d["VALU insts per wave"] = iv / mean("SQ_WAVES")
+        if av is not None and gui:
+            d["VALU busy per CU-cycle"] = av / gui / 256.0
+        if d:
+            derived.append((k, d))
+    if derived:
+        lines += ["", "Derived (means over the dispatches above):", ""]
+        for k, d in derived:
+            lines.append(f"- `{k[:90]}`: " + ", ".join(f"{n} {v:.4g}" for n, v in d.items()))
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"counters_{workload}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    if "FETCH_SIZE" in scale and "WRITE_SIZE" in scale:
+        kernels = {}
+        for k in ours:
+            f = vals["FETCH_SIZE"].get(k)
+            w = vals["WRITE_SIZE"].get(k)
+            if f and w:
+                kernels[k] = {"read_bytes": int(round(sum(f) / len(f) * 1024 * scale["FETCH_SIZE"])),
+                              "write_bytes": int(round(sum(w) / len(w) * 1024 * scale["WRITE_SIZE"]))}
+        rec = {"workload": workload, "sources_sha256": kernel_sources_sha256(), "fetch_scale": scale["FETCH_SIZE"],
+               "write_scale": scale["WRITE_SIZE"], "commands": args.pmc_command, "kernels": kernels}
+        with open(os.path.join(ROOT, "profiles", f"traffic_{workload}.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+    print("\n".join(lines))
+
+
+# ---------------------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the sparse-FFN hot path has no multi-GPU leg "
+              f"(asked for --gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from activation_sparse_ffn_rank_amd import DeviceLayer, _abi
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    head = (args.config, args.batch)
+    plan = [head] + ([] if args.no_detail else [w for w in DETAIL if w != head])
+    # one stack at a time: every batch of a stack is measured on the same resident layers
+    order = []
+    for cid, _ in plan:
+        if cid not in order:
+            order.append(cid)
+    results = {}
+    for cid in order:
+        cfg = synth.CONFIGS[cid]
+        L = cfg.layers if args.layers <= 0 else min(args.layers, cfg.layers)
+        t0 = time.time()
+        layers = []
+        for l in range(L):
+            host = synth.make_layer(cfg, l)
+            layers.append(DeviceLayer.from_host(host, device=dev))
+            del host
+        torch.cuda.synchronize()
+        log(f"stack {cfg.cid} ({cfg.name}): {L} layers generated and resident in {time.time() - t0:.1f}s")
+        for wcid, B in plan:
+            if wcid != cid:
+                continue
+            is_head = (wcid, B) == head
+            if is_head:
+                W, K = args.warmup, args.steps
+            else:
+                W, K = 4, max(1, min(args.detail_steps, cfg.tokens - 4))
+            rec = measure(torch, synth, _abi, cfg, layers, B, W, K, args.roofline_steps, dev, stream,
+                          wide=(cid in (2, 5)), cold=(cid == 4))
+            results[(wcid, B)] = rec
+            log(f"{rec['workload']}: {rec['tokens_per_s']} tokens/s, {rec['us_per_layer']} us/layer, sparse FFN "
+                f"{rec['kernels']['sparse_ffn']['us']} us ({rec['kernels']['sparse_ffn']['frac']} of HBM peak)")
+        del layers
+        torch.cuda.empty_cache()
+
+    h = results[head]
+    cfg = synth.CONFIGS[head[0]]
+    L = h["layers"]
+    ffn_bytes, ffn_us, ffn_label, ffn_n = h["_ffn"]
+    roof_traffic = measured_traffic(h["workload"], h["_ffn_prefixes"]) if L == cfg.layers else None
+    roof_gbs = ffn_bytes / (ffn_us * 1e-6) / 1e9
+
     cpu = None
+    c1_single = None
     if not args.no_cpu_baseline:
         import oracle
-        budget = args.cpu_seconds
-        n_lay = min(L, 4)
-        hosts = [synth.make_layer(cfg, l) for l in range(n_lay)]
-        done, spent, t = 0, 0.0, 0
-        while spent < budget:
-            for l in range(n_lay):
-                s0 = time.perf_counter()
-                oracle.ffn_layer(hosts[l], x_all[t % (W + K), l], want_logits=False)
-                spent += time.perf_counter() - s0
-                done += 1
-            t += 1
-        del hosts
-        per_layer = spent / done
-        cpu = {"value": round(B / (per_layer * L), 3), "unit": "tokens/s", "cores": oracle.num_threads(),
-               "kind": "oracle",
-               "sample": f"{done} evaluations of the whole layer (predictor, mask, compaction, sparse FFN) at "
-                         f"batch {B}: layers 0..{n_lay - 1} of the same stack, {t} token steps cycling over the "
-                         f"{W + K} seeded inputs; {spent:.1f}s, {per_layer * 1e3:.2f} ms per layer, scaled to the "
-                         f"{L}-layer step"}
+        cpu = cpu_oracle(synth, oracle, cfg, L, head[1], cfg.tokens, args.cpu_seconds)
+        if not args.no_detail:
+            # the single small layer on one thread (all of its seeded tokens), as a fixed reference
+            c1 = synth.CONFIGS[1]
+            n_all = oracle.num_threads()
+            oracle.set_num_threads(1)
+            lay = synth.make_layer(c1, 0)
+            xs = synth.make_x_all(c1, 1, c1.tokens, 1)
+            s0 = time.perf_counter()
+            for t in range(c1.tokens):
+                oracle.ffn_layer(lay, xs[t, 0], want_logits=False)
+            c1_s = time.perf_counter() - s0
+            oracle.set_num_threads(n_all)
+            c1_single = {"stack": c1.name, "tokens": c1.tokens, "threads": 1, "seconds": round(c1_s, 3),
+                         "tokens_per_s": round(c1.tokens / c1_s, 2), "cpu_model": cpu_model()}
 
-    ms_per_step = elapsed_ms / K
-    tokens_per_s = B * K / (elapsed_ms / 1e3)
+    def public(rec):
+        return {k: v for k, v in rec.items() if not k.startswith("_")}
+
     out = {
         "metric": "sparse-FFN decode tokens/s (batch 1) + achieved HBM GB/s on active-row bytes",
-        "value": round(tokens_per_s, 2),
+        "value": h["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
-        "warmup": W,
-        "ms_per_step": round(ms_per_step, 4),
+        "steps": h["steps"],
+        "warmup": h["warmup"],
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if cfg.wtype == synth.F16 else "q4_0",
+        "dtype": "q4_0" if cfg.wtype == synth.Q4_0 else "f16",
         "data": "synthetic",
         "config": {
-            "workload": f"{cfg.name}: {L} layers, d_model={cfg.d}, d_ffn={cfg.f}, predictor rank {cfg.r}, "
-                        f"{'ReGLU' if cfg.gated else 'ReLU'}, {'fp16' if cfg.wtype == synth.F16 else 'Q4_0'} "
-                        f"weights, batch {B}, Zipf firing at {cfg.density:.0%} target density"
-                        + (f", hottest {cfg.hot_frac:.0%} resident" if cfg.hot_frac else ""),
-            "global_batch": B, "layers": L, "d_model": cfg.d, "d_ffn": cfg.f, "rank": cfg.r,
+            "workload": h["description"],
+            "global_batch": head[1], "layers": L, "d_model": cfg.d, "d_ffn": cfg.f, "rank": cfg.r,
             "parallelism": "single GPU",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": roof_kernel,
+            "kernel": f"{ffn_label} (pi_sparse_ffn: gathered up rows with bias + ReLU, active rows of W_down^T)",
             "achieved": round(roof_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(roof_gbs / PEAK_HBM_GBS, 4),
             "traffic": roof_traffic,
-            "bytes_per_launch": round(roof_bytes),
-            "launch_us": round(roof_us, 3),
-            "launches": int(N),
+            "bytes_per_launch": round(ffn_bytes),
+            "launch_us": round(ffn_us, 3),
+            "launches": int(ffn_n),
         },
         "cpu_baseline": cpu,
         "detail": {
-            "us_per_layer": round(ms_per_step * 1000.0 / L, 3),
-            "layer_path": path,
-            "graph_us_predict_hidden": round(leg_us["hidden"], 3),
-            "graph_us_layer_from_hidden": round(leg_us["rest"], 3),
-            "graph_us_sparse_ffn": round(leg_us["sparse_ffn"], 3),
-            "bytes_predict_hidden": hidden_bytes,
-            "bytes_layer_from_hidden": round(float(rest_bytes.mean())),
-            "bytes_sparse_ffn_read": round(float(ffn_touched.mean())),
-            "bytes_sparse_ffn_predicted_rows": round(float(ffn_predicted.mean())),
-            "gbs_sparse_ffn": round(float(ffn_touched.mean()) / (leg_us["sparse_ffn"] * 1e-6) / 1e9, 1),
-            "predictor_bytes": pred_bytes,
-            "step_gb_algorithmic": round(step_bytes / 1e9, 4),
-            "step_gbs": round(step_bytes / 1e9 / (ms_per_step / 1e3), 1),
-            "active_density": round(float(n_act.mean()) / cfg.f, 4),
-            "predicted_density": round(float(n_pred.mean()) / cfg.f, 4),
-            "covered_share": round(float(n_act.sum() / max(n_pred.sum(), 1)), 4),
-            "down_rows_zero_h_share": round(1.0 - float(n_live.sum()) / max(float(n_act.sum()), 1.0), 4),
-            "cold_host": cold,
-            "wide_b16": wide,
+            "headline": public(h),
+            "workloads": [public(results[w]) for w in plan if w != head],
+            "cpu_c1_single_thread": c1_single,
+            "timing": f"median of {REPS} replays of each timed graph (HIP events on the launch stream)",
         },
     }
     print(json.dumps(out), flush=True)

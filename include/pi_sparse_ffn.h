@@ -119,18 +119,16 @@ int pi_compact(const uint8_t *mask, int32_t d_ffn, const int32_t *slot_of, int32
  * compute only the active neurons).  idx and counts are device memory (as pi_compact writes
  * them); n is clamped to [0, n_slots] and entries whose neuron or slot is out of range are
  * skipped.  y [batch][d_model] fp32 is overwritten.
- * When batch <= 2 and batch * d_model <= 32768 this is ONE persistent kernel: workgroups
- * computing h for groups of four listed neurons hand (slot, h) entries, through the workspace, to
- * the workgroups that accumulate the rows of W_down^T.  Then:
- *  - the workspace must be zero-filled before the first call that uses it, and each call leaves
- *    it ready for the next one (never clear or share it while a call is in flight);
- *  - the int32 at byte offset 384 of the workspace is a sticky status word: nonzero means a
- *    cross-workgroup wait ran out its time limit (20 ms) and the outputs of that call are invalid.
- * Every wait inside the kernel is bounded.  Other shapes and batches run two kernels (h, then the
- * rows of W_down^T; from batch 3 for gated or Q4_0 rows and from batch 6 for other fp16 rows, the
- * MFMA kernels of pi_sparse_ffn_wide), which never wait and
- * need no zero fill; their workspace starts with the same control block, which they leave
- * untouched, so a zero-filled workspace reads status 0 on every form. */
+ * At batch <= 2 (and d_model <= 32768 for fp16 rows, <= 65536 for Q4_0) this is three kernels over
+ * (column slab x list chunk) workgroups: partial dot products of each slab, then h and the rows of
+ * W_down^T, then the sum of the chunks' partial y in a fixed order.  Other batches run two kernels
+ * (h, then the rows of W_down^T; from batch 3 for gated or Q4_0 rows and from batch 6 for other
+ * fp16 rows, the MFMA kernels of pi_sparse_ffn_wide).  None of these kernels waits on another
+ * workgroup; y is deterministic.  The workspace starts with a 512-byte control block whose int32 at
+ * byte offset 384 is the sticky status word of the persistent layer kernel (pi_ffn_layer); the
+ * sparse-FFN kernels leave it untouched, so a zero-filled workspace reads status 0 after any of
+ * them.  The workspace needs no zero fill for pi_sparse_ffn itself and must not be shared by calls
+ * in flight at the same time. */
 int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx,
                   const int32_t *counts, float *y, void *ws, size_t ws_bytes, void *stream);
 
@@ -149,10 +147,21 @@ size_t pi_sparse_ffn_wide_workspace_bytes(const pi_ffn *ffn, int32_t batch);
 int pi_sparse_ffn_wide(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx,
                        const int32_t *counts, float *y, void *ws, size_t ws_bytes, void *stream);
 
-/* Whole layer: pi_predict -> pi_compact -> pi_sparse_ffn, stream-ordered.  pred and ffn must
- * agree on d_model and d_ffn.  mask_out [d_ffn], idx_out [d_ffn] and counts_out [2] receive the
- * intermediate results when non-NULL (otherwise they live in the workspace).  The workspace
- * rules of pi_sparse_ffn apply (zero-filled before first use; status word at byte offset 384). */
+/* Whole layer (the decode step of one FFN layer as the method section describes it: the online
+ * predictor picks the neurons that fire, the GPU index restricts them to the resident ones, and the
+ * neuron-aware operator computes only those): the result of pi_predict -> pi_compact ->
+ * pi_sparse_ffn, stream-ordered.  pred and ffn must agree on d_model and d_ffn.  mask_out [d_ffn],
+ * idx_out [d_ffn] and counts_out [2] receive the intermediate results when non-NULL (otherwise they
+ * live in the workspace; the list is only built when idx_out or counts_out is given -- the sparse
+ * FFN itself reads the predictor's listed flags).
+ * For layers of at most 12288 neurons (32768 at batch <= 2) whose x and z fit one workgroup's LDS
+ * (pi_layer_path == 1), everything after the first predictor matrix is ONE persistent kernel whose
+ * workgroups hand the mask and h to each other through the workspace.  Then:
+ *  - the workspace must be zero-filled before the first call that uses it, and each call leaves it
+ *    ready for the next one (never clear or share it while a call is in flight);
+ *  - the int32 at byte offset 384 of the workspace is a sticky status word: nonzero means a
+ *    cross-workgroup wait ran out its time limit (20 ms) and the outputs of that call are invalid.
+ * Every wait inside the kernel is bounded.  Zero-filling the workspace once is always safe. */
 int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch,
                  float *y, uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws,
                  size_t ws_bytes, void *stream);
@@ -174,23 +183,10 @@ int pi_ffn_layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const 
  * compaction, sparse FFN).  0 on invalid arguments. */
 int pi_layer_path(const pi_predictor *pred, const pi_ffn *ffn, int32_t batch);
 
-/* The same layer as ONE persistent kernel whose workgroups hand work to each other through the
- * workspace (same arguments and results as pi_ffn_layer).  Requires batch * d_model <= 32768 so
- * that x and the kernel's own arrays fit one workgroup's LDS (PI_ERR_SHAPE otherwise).
- *  - The workspace must be zero-filled before the first call that uses it, and each call leaves it
- *    ready for the next one (never clear or share it while a call is in flight).
- *  - The int32 at byte offset 384 of the workspace is a sticky status word: nonzero means a
- *    cross-workgroup wait ran out its time limit (20 ms) and the outputs of that call are invalid.
- * Every wait inside the kernel is bounded, so a failure cannot hang the device. */
-int pi_ffn_layer_fused(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch,
-                       float *y, uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws,
-                       size_t ws_bytes, void *stream);
-
 /* Diagnostics: where a pi_sparse_ffn call leaves h (list position k, token b) in its workspace,
  * for callers that count the rows of W_down^T that had to be read (h != 0 for some token).
  * Returns the byte offset of the table inside a pi_sparse_ffn workspace and sets *kind:
- *  1 = persistent kernel: position k is (1 + batch) uint64 words at offset + 8*k*(1 + batch);
- *      the low 32 bits of word 0 are the slot (-1 = skipped), those of word 1 + b the fp32 bits of h;
+ *  1 = slab x chunk kernels (batch <= 2): fp32 h at offset + 4*(b*d_ffn + k);
  *  2 = two-kernel form: fp32 h at offset + 4*(b*max(n_slots, 1) + k);
  *  3 = MFMA form (the batches named above): h = hi + lo, fp16 hi at offset + 2*(b*hs + k) and fp16 lo at
  *      offset + L + 2*(b*hs + k), hs = max(n_slots, 1) rounded up to 32, L = 32*hs rounded up to 256.

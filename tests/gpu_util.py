@@ -67,19 +67,14 @@ def gpu_predict(dl: DeviceLayer, x: np.ndarray):
     return logits.cpu().numpy(), mask.cpu().numpy()
 
 
-def fused_fits(d_model: int, batch: int) -> bool:
-    """pi_ffn_layer_fused takes batch * d_model <= 32768 (x must fit one workgroup's LDS)."""
-    return batch * d_model <= 32768
-
-
-def _layer_split(pred, ffn, x, batch, y, mask_out, idx_out, counts_out, ws, stream=None):
+def _layer_two_step(pred, ffn, x, batch, y, mask_out, idx_out, counts_out, ws, stream=None):
     """pi_ffn_layer as its two published steps: pi_predict_hidden, then pi_ffn_layer_from_hidden."""
     z = torch.empty((batch, pred.rank), dtype=torch.float32, device="cuda")
     _abi.pi_predict_hidden(pred, x, batch, z, stream)
     _abi.pi_ffn_layer_from_hidden(pred, ffn, x, batch, z, y, mask_out, idx_out, counts_out, ws, stream)
 
 
-LAYER_ENTRIES = {"layer": _abi.pi_ffn_layer, "fused": _abi.pi_ffn_layer_fused, "split": _layer_split}
+LAYER_ENTRIES = {"layer": _abi.pi_ffn_layer, "two_step": _layer_two_step}
 
 
 def gpu_layer(dl: DeviceLayer, x: np.ndarray, ws: torch.Tensor | None = None, entry: str = "layer"):
@@ -99,7 +94,7 @@ def gpu_layer(dl: DeviceLayer, x: np.ndarray, ws: torch.Tensor | None = None, en
 
 
 def check_layer_against_oracle(layer, dl: DeviceLayer, x: np.ndarray, what: str, b_down=None,
-                               entries=("layer", "fused")) -> dict:
+                               entries=("layer",)) -> dict:
     """End-to-end rule: masks agree outside the band; given the GPU's mask the oracle's index list
     is identical; given that list the oracle's y agrees within tolerance.  Checked for every
     layer entry point named in `entries` that takes this shape."""
@@ -109,8 +104,6 @@ def check_layer_against_oracle(layer, dl: DeviceLayer, x: np.ndarray, what: str,
     bd = layer.b_down if b_down is None else b_down
     worst = None
     for entry in entries:
-        if entry == "fused" and not fused_fits(cfg.d, B):
-            continue
         tag = f"{what} [{entry}]"
         got = gpu_layer(dl, x, entry=entry)
         dont_care = check_mask(got["mask"], logits_ref, tag)

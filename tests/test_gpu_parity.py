@@ -87,6 +87,11 @@ FFN_CASES = [  # (d, f, gated, wtype, B, active share)
     (8192, 301, True, F16, 6, 0.3), (256, 12000, False, Q4, 3, 0.8),
     # edges of the batch > 2 form: the smallest d_model, a single neuron, an empty list
     (8, 40, False, F16, 3, 0.5), (8, 33, True, F16, 8, 1.0), (256, 1, False, Q4, 4, 1.0), (512, 300, False, Q4, 5, 0.0),
+    # batch <= 2 (one launch of slab x chunk workgroups): ragged last slab, chunks that take several
+    # rounds, both batch widths for every row kind, the 7B- and 175B-shaped row widths
+    (1280, 20000, False, Q4, 2, 0.5), (2056, 5000, True, F16, 2, 0.6), (1032, 9000, False, F16, 1, 0.7),
+    (2048, 3000, False, Q4, 1, 1.0), (1024, 2000, False, F16, 2, 0.3), (8, 50, False, F16, 1, 0.5),
+    (4096, 11008, True, F16, 1, 0.12), (12288, 6000, False, Q4, 1, 0.4), (12288, 3000, False, Q4, 2, 0.2),
 ]
 
 
@@ -185,11 +190,15 @@ LAYER_CASES = [  # small layers spanning several tiles, ragged f, placement, all
     # squared ReLU: the tail kernel (small f) and separate kernels (large f), fp16 and Q4_0
     dict(d=1024, f=4096, r=128, gated=False, wtype=F16, bias_up=True, density=0.1, act=1),
     dict(d=1024, f=40000, r=128, gated=False, wtype=Q4, bias_up=True, density=0.05, act=1),
+    # separate kernels at every batch (too many neurons for the tail kernel): placement, ReGLU
+    dict(d=1024, f=40000, r=128, gated=False, wtype=F16, bias_up=True, density=0.05, hot_frac=0.26),
+    dict(d=1024, f=33000, r=256, gated=True, wtype=F16, bias_up=False, density=0.06),
 ]
 
 
 @pytest.mark.parametrize("case", LAYER_CASES, ids=["relu", "reglu", "placement", "q4_0", "squared_relu",
-                                                  "squared_relu_q4_0_large_f"])
+                                                  "squared_relu_q4_0_large_f", "placement_large_f",
+                                                  "reglu_large_f"])
 @pytest.mark.parametrize("B", [1, 4, 8])
 def test_ffn_layer(case, B):
     announce(f"ffn_layer {case} B={B}")
@@ -252,7 +261,7 @@ def test_layer_is_deterministic():
     assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["idx"], b["idx"])
 
 
-@pytest.mark.parametrize("entry", ["layer", "fused"])
+@pytest.mark.parametrize("entry", ["layer", "two_step"])
 def test_graph_replay_matches_eager(entry):
     """The launch sequence captured into a HIP graph (as the benchmark runs it) gives, on every
     replay, exactly what eager calls give."""
@@ -285,7 +294,7 @@ def test_graph_replay_matches_eager(entry):
         torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("entry", ["layer", "fused"])
+@pytest.mark.parametrize("entry", ["layer", "two_step"])
 def test_layer_outputs_are_optional(entry):
     """mask/idx/counts outputs change nothing about y (bitwise)."""
     run = LAYER_ENTRIES[entry]
@@ -304,7 +313,7 @@ def test_layer_outputs_are_optional(entry):
     assert torch.equal(y1, y2) and np.array_equal(y1.cpu().numpy(), got["y"])
 
 
-@pytest.mark.parametrize("entry", ["layer", "fused"])
+@pytest.mark.parametrize("entry", ["layer", "two_step"])
 def test_many_calls_share_one_workspace(entry):
     """Back-to-back launches on one workspace (epochs advance, counters reset) stay exact."""
     run = LAYER_ENTRIES[entry]
@@ -342,10 +351,10 @@ def test_split_layer_matches_whole_layer():
             announce(f"split layer {case} B={B}")
             x = synth.make_x(cfg, 0, 1, B)
             whole = gpu_layer(dl, x, entry="layer")
-            split = gpu_layer(dl, x, entry="split")
+            split = gpu_layer(dl, x, entry="two_step")
             assert np.array_equal(whole["y"], split["y"]) and np.array_equal(whole["idx"], split["idx"])
             z = torch.empty((B, cfg.r), dtype=torch.float32, device="cuda")
             _abi.pi_predict_hidden(dl.pred, to_dev(x), B, z)
             torch.cuda.synchronize()
             assert bool((z >= 0).all()) and bool(torch.isfinite(z).all())
-            check_layer_against_oracle(layer, dl, x, f"split B={B}", entries=("split",))
+            check_layer_against_oracle(layer, dl, x, f"split B={B}", entries=("two_step",))
