@@ -25,7 +25,9 @@ PI_MAX_WIDE_BATCH = 16
 EXPORTS = ("pi_workspace_bytes", "pi_predict", "pi_compact", "pi_sparse_ffn", "pi_sparse_ffn_wide_workspace_bytes", "pi_sparse_ffn_wide",
            "pi_ffn_layer",
            "pi_predict_hidden", "pi_ffn_layer_from_hidden", "pi_layer_path", "pi_sparse_ffn_h_offset",
-           "pi_cold_workspace_bytes", "pi_cold_ffn_host", "pi_place", "pi_status_string", "pi_version")
+           "pi_cold_workspace_bytes", "pi_cold_ffn_host", "pi_place", "pi_sparse_ffn_noalloc", "pi_status_string",
+           "pi_version")
+PI_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 
 class pi_predictor(ctypes.Structure):
@@ -86,6 +88,8 @@ def lib() -> ctypes.CDLL:
         L.pi_place.restype = ctypes.c_int
         L.pi_place.argtypes = [i32, vp, vp, vp, ctypes.c_int64, ctypes.c_double, ctypes.c_double, vp, vp,
                                P(ctypes.c_double)]
+        L.pi_sparse_ffn_noalloc.restype = ctypes.c_int
+        L.pi_sparse_ffn_noalloc.argtypes = [P(pi_ffn), vp, i32, vp, vp, vp, vp]
         L.pi_status_string.restype = ctypes.c_char_p
         L.pi_status_string.argtypes = [ctypes.c_int]
         L.pi_version.restype = ctypes.c_int
@@ -158,6 +162,12 @@ def pi_sparse_ffn(ffn, x, batch, idx, counts, y, ws, stream=None) -> None:
     _check("pi_sparse_ffn", lib().pi_sparse_ffn(_byref(ffn), _ptr(x), batch, _ptr(idx), _ptr(counts), _ptr(y),
                                                 _ptr(ws), _nbytes(ws) if ws is not None and not isinstance(ws, int) else 0,
                                                 _stream(stream)))
+
+
+def pi_sparse_ffn_noalloc(ffn, x, batch, idx, counts, y, stream=None) -> None:
+    """pi_sparse_ffn with the library's own device scratch (no caller workspace, no allocation)."""
+    _check("pi_sparse_ffn_noalloc", lib().pi_sparse_ffn_noalloc(_byref(ffn), _ptr(x), batch, _ptr(idx), _ptr(counts),
+                                                                _ptr(y), _stream(stream)))
 
 
 def pi_sparse_ffn_wide_workspace_bytes(ffn, batch: int) -> int:

@@ -11,6 +11,12 @@
 #include "pi_wide.hpp"
 
 #include <algorithm>
+#include <mutex>
+
+// Scratch of pi_sparse_ffn_noalloc: a file-scope device array, one copy per GPU, held until the
+// process ends.  Host code never uses this name as an address (on the host it is a stand-in for the
+// device symbol); it asks for each device's address with hipGetSymbolAddress and passes that.
+static __device__ __align__(256) uint8_t scratch[PI_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -482,6 +488,27 @@ LayerWs layer_ws(const pi_predictor *p, const pi_ffn *fn, int B, void *ws) {
 
 }  // namespace
 
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices] = {};
+
+// Address of the current device's copy of `scratch` (looked up once per device), or nullptr.
+void *noalloc_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+        g_scratch[dev] = ptr;
+    }
+    return g_scratch[dev];
+}
+
+}  // namespace
+
 // ==================================================================== C ABI
 
 extern "C" {
@@ -641,6 +668,21 @@ size_t pi_sparse_ffn_h_offset(const pi_ffn *ffn, int32_t batch, int32_t *kind) {
     }
     *kind = 2;
     return ctl_bytes(ffn->d_model);
+}
+
+int pi_sparse_ffn_noalloc(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx, const int32_t *counts,
+                          float *y, void *stream) {
+    int rc = check_ffn(ffn);
+    if (rc) return rc;
+    if ((rc = check_batch(batch))) return rc;
+    if (!x || !idx || !counts || !y) return PI_ERR_NULL;
+    if (!aligned16(x)) return PI_ERR_ALIGN;
+    if (ffn_ws(ffn, batch) > (size_t)PI_NOALLOC_SCRATCH_BYTES) return PI_ERR_WORKSPACE;
+    void *ws = noalloc_scratch();
+    if (ws == nullptr) return PI_ERR_HIP;
+    // every form of the sparse FFN writes each scratch value before reading it within the call, so
+    // the array's contents from earlier calls never matter and nothing is cleared
+    return enqueue_sparse(ffn, x, batch, idx, counts, y, ws, static_cast<hipStream_t>(stream));
 }
 
 const char *pi_status_string(int status) {

@@ -233,6 +233,22 @@ int pi_place(int32_t n_layers, const int32_t *d_ffn, const int64_t *neuron_bytes
              int64_t budget_bytes, double gpu_bytes_per_s, double host_bytes_per_s, int32_t *slot_of,
              int32_t *n_placed, double *expected_s);
 
+/* ---- the same sparse FFN without a caller workspace ----
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  pi_sparse_ffn_noalloc is pi_sparse_ffn (same arguments, kernels
+ * and results, bit for bit) with its scratch in a device array that the library holds, one copy per
+ * GPU, from the first call on that GPU until the process ends; it calls no hipMalloc, hipFree or
+ * allocating routine.  The layer and batch must need at most PI_NOALLOC_SCRATCH_BYTES of scratch
+ * (pi_workspace_bytes(NULL, ffn, batch) <= PI_NOALLOC_SCRATCH_BYTES), else PI_ERR_WORKSPACE and
+ * nothing is enqueued; PI_ERR_HIP if the array's address cannot be obtained.  Every call on one GPU
+ * uses the same array, so calls that overlap in time on one GPU (two streams, or two host threads
+ * without ordering) race and must not be made; calls ordered on one stream are fine.  The array
+ * needs no clearing: each call writes every scratch value before reading it. */
+#define PI_NOALLOC_SCRATCH_BYTES (32u << 20)
+int pi_sparse_ffn_noalloc(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx,
+                          const int32_t *counts, float *y, void *stream);
+
 /* Human-readable name of a pi_status value (static storage). */
 const char *pi_status_string(int status);
 

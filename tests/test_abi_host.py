@@ -78,6 +78,25 @@ def test_predict_rejects(L):
     assert call(ctypes.byref(p), n=big - 1) == _abi.PI_ERR_WORKSPACE
 
 
+def test_sparse_ffn_noalloc_rejects(L):
+    """Argument checks of the no-allocation entry point run on the host before any HIP call,
+    including the bound on the library-held scratch (a layer that needs more is refused)."""
+    call = lambda ff, x=A, B=1, idx=A, cnt=A, y=A: L.pi_sparse_ffn_noalloc(ff, x, B, idx, cnt, y, None)
+    f = ffn()
+    assert call(None) == _abi.PI_ERR_NULL
+    for kw in (dict(x=0), dict(idx=0), dict(cnt=0), dict(y=0)):
+        assert call(ctypes.byref(f), **kw) == _abi.PI_ERR_NULL
+    assert call(ctypes.byref(f), x=U) == _abi.PI_ERR_ALIGN
+    assert call(ctypes.byref(f), B=0) == _abi.PI_ERR_BATCH and call(ctypes.byref(f), B=9) == _abi.PI_ERR_BATCH
+    assert call(ctypes.byref(ffn(wtype=3))) == _abi.PI_ERR_DTYPE
+    big = ffn(d=16384, f=1 << 20)
+    assert ws_for(L, None, big, 1) > _abi.PI_NOALLOC_SCRATCH_BYTES
+    assert call(ctypes.byref(big)) == _abi.PI_ERR_WORKSPACE
+    # the benchmarked shapes fit: the 175B-shaped Q4_0 layer at batch 1 and 8
+    q = ffn(d=12288, f=49152, wtype=_abi.PI_Q4_0)
+    assert ws_for(L, None, q, 1) <= _abi.PI_NOALLOC_SCRATCH_BYTES and ws_for(L, None, q, 8) <= _abi.PI_NOALLOC_SCRATCH_BYTES
+
+
 def test_compact_rejects(L):
     assert L.pi_compact(None, 10, None, A, A, None) == _abi.PI_ERR_NULL
     assert L.pi_compact(A, 10, None, None, A, None) == _abi.PI_ERR_NULL
