@@ -145,8 +145,16 @@ bool sparse_split(const pi_ffn *fn, int B) {
     return B <= 2 && split_slabs(fn->d_model, fn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16) <= kSplitMaxSlabs;
 }
 int mask_words(int f) { return ceil_div(f, 32); }
-// In a layer, the split kernel reads the predictor's listed-bit words directly (no compaction).
+// In a layer, the split kernels read the predictor's listed-flag words directly (no compaction).
 bool layer_split(const pi_ffn *fn, int B) { return sparse_split(fn, B) && mask_words(fn->d_ffn) <= kSplitMaxWords; }
+// ... and when x and z fit one workgroup's LDS and the matrices stay below the 32-bit offsets of its
+// buffer loads, the second predictor matrix and the up rows run as one kernel (k_pred_up).
+bool layer_pred_up(const pi_predictor *p, const pi_ffn *fn, int B) {
+    const int64_t in_bytes = (int64_t)fn->n_slots * row_bytes_of(fn) * (fn->gated ? 2 : 1);
+    const int64_t p2_bytes = (int64_t)p->d_ffn * p->rank * 2;
+    return layer_split(fn, B) && in_bytes < (int64_t)kBufMax && p2_bytes < (int64_t)kBufMax &&
+           pred_up_lds(B, fn->d_model, p->rank) <= (size_t)kLdsXBytes + 16 * 1024;
+}
 
 // The tail kernel (second predictor matrix + mask + sparse FFN) keeps x [B][d] fp16 and z [B][r]
 // fp32 in dynamic LDS next to its static arrays (wave partials of the down tiles, the list of a
@@ -598,6 +606,34 @@ int layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const void *x
         // one kernel for the mask and the sparse FFN; the list only when it is asked for
         if ((rc = enqueue_tail(pred, ffn, x, batch, z, y, (mask_out || want_list) ? mask : nullptr, L.ctl, L.tail, st)))
             return rc;
+        return want_list ? enqueue_compact(mask, f, ffn->slot_of, idx, counts, st) : PI_OK;
+    }
+    if (layer_pred_up(pred, ffn, batch)) {
+        // logits, mask, listed flags and h of the listed neurons in one kernel, then the down rows
+        const SplitGeom g = split_geom(ffn, batch);
+        PredUpArgs p{};
+        p.d = pred->d_model; p.f = f; p.r = pred->rank; p.n_slots = ffn->n_slots; p.act = ffn->act;
+        p.row_bytes = row_bytes_of(ffn);
+        p.p2 = static_cast<const uint16_t *>(pred->p2); p.c = static_cast<const uint16_t *>(pred->c); p.z = z;
+        p.w_in = static_cast<const uint8_t *>(ffn->w_in); p.b_up = static_cast<const uint16_t *>(ffn->b_up);
+        p.slot_of = ffn->slot_of; p.x = static_cast<const uint16_t *>(x);
+        p.mask = mask; p.bits = L.bits;
+        char *w = L.ffn + ctl_bytes(ffn->d_model);
+        SplitArgs a{};
+        a.d = ffn->d_model; a.f = f; a.n_slots = ffn->n_slots; a.S = g.S; a.act = ffn->act;
+        a.nwords = mask_words(f);
+        a.row_bytes = row_bytes_of(ffn);
+        a.w_in = static_cast<const uint8_t *>(ffn->w_in); a.w_dn = static_cast<const uint8_t *>(ffn->w_down_t);
+        a.b_up = p.b_up; a.b_down = static_cast<const uint16_t *>(ffn->b_down);
+        a.slot_of = ffn->slot_of; a.x = p.x; a.y = y; a.bits = L.bits;
+        a.part = reinterpret_cast<float *>(w);
+        a.ypart = reinterpret_cast<float *>(w + g.part);
+        a.hout = nullptr;
+        p.h = reinterpret_cast<float *>(w + g.part + g.ypart);        // the hout region: [B][f]
+        a.hin = p.h;
+        const int wt = ffn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16;
+        const int NT = pred->rank <= 512 ? 1 : (pred->rank <= 1024 ? 2 : 4);
+        if (launch_pred_up_split(p, a, batch, wt, ffn->gated, NT, st)) return PI_ERR_HIP;
         return want_list ? enqueue_compact(mask, f, ffn->slot_of, idx, counts, st) : PI_OK;
     }
     if (layer_split(ffn, batch)) {

@@ -1,31 +1,56 @@
-// pi_split.hip -- instantiates the (column slab x list chunk) sparse-FFN kernels of pi_split.hpp
-// for batch 1 and 2 and every row kind, and launches them.
+// pi_split.hip -- instantiates the (column slab x list chunk) sparse-FFN kernels and the fused
+// predictor + up kernel of pi_split.hpp for batch 1 and 2 and every row kind, and launches them.
 #include "pi_split.hpp"
 #include "pi_occupancy.hpp"
 
 namespace pik {
 namespace {
 
+// C: about two workgroups per compute unit -- every workgroup moves the same bytes, so the grid
+// spreads them evenly; nothing waits on another workgroup, so residency is not required.
 template <int B, bool GATED, int WT>
-int launch_one(SplitArgs &a, hipStream_t st) {
-    auto up = k_up_split<B, GATED, WT>;
-    auto down = k_down_split<B, GATED, WT>;
-    const size_t lds_up = split_dyn_lds(B, WT, a.nwords, false), lds_down = split_dyn_lds(B, WT, a.nwords, true);
+int choose_chunks(SplitArgs &a) {
     int cus = 0, per_cu = 0;
-    if (resident_slots(reinterpret_cast<const void *>(down), kSplitThreads, lds_down, &cus, &per_cu)) return 1;
-    // about two workgroups per compute unit: every workgroup moves the same bytes, so the grid
-    // spreads them evenly; nothing waits on another workgroup, so residency is not required
+    const size_t lds_down = split_dyn_lds(B, WT, a.nwords, true);
+    if (resident_slots(reinterpret_cast<const void *>(k_down_split<B, GATED, WT>), kSplitThreads, lds_down, &cus,
+                       &per_cu))
+        return 1;
     int C = (2 * cus) / a.S;
-    C = C < 1 ? 1 : (C > kSplitMaxChunks ? kSplitMaxChunks : C);
-    a.C = C;
-    const int grid = a.S * C, Bd = B * a.d;
-    hipLaunchKernelGGL(up, dim3(grid), dim3(kSplitThreads), lds_up, st, a);
-    if (hipGetLastError() != hipSuccess) return 1;
-    hipLaunchKernelGGL(down, dim3(grid), dim3(kSplitThreads), lds_down, st, a);
+    a.C = C < 1 ? 1 : (C > kSplitMaxChunks ? kSplitMaxChunks : C);
+    return 0;
+}
+
+// k_down_split then k_sum_split (a.C set).
+template <int B, bool GATED, int WT>
+int launch_down_sum(SplitArgs &a, hipStream_t st) {
+    const int Bd = B * a.d;
+    hipLaunchKernelGGL((k_down_split<B, GATED, WT>), dim3(a.S * a.C), dim3(kSplitThreads),
+                       split_dyn_lds(B, WT, a.nwords, true), st, a);
     if (hipGetLastError() != hipSuccess) return 1;
     hipLaunchKernelGGL(k_sum_split, dim3((Bd + kSplitThreads - 1) / kSplitThreads), dim3(kSplitThreads), 0, st,
-                       a.ypart, C, Bd, a.d, a.b_down, a.y);
+                       a.ypart, a.C, Bd, a.d, a.b_down, a.y);
     return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
+template <int B, bool GATED, int WT>
+int launch_one(SplitArgs &a, hipStream_t st) {
+    if (choose_chunks<B, GATED, WT>(a)) return 1;
+    hipLaunchKernelGGL((k_up_split<B, GATED, WT>), dim3(a.S * a.C), dim3(kSplitThreads),
+                       split_dyn_lds(B, WT, a.nwords, false), st, a);
+    if (hipGetLastError() != hipSuccess) return 1;
+    return launch_down_sum<B, GATED, WT>(a, st);
+}
+
+template <int B, bool GATED, int WT>
+int launch_layer_one(PredUpArgs &p, SplitArgs &a, int NT, hipStream_t st) {
+    if (choose_chunks<B, GATED, WT>(a)) return 1;
+    const dim3 grid((p.f + 31) / 32);
+    const size_t lds = pred_up_lds(B, p.d, p.r);
+    if (NT == 1) hipLaunchKernelGGL((k_pred_up<B, GATED, WT, 1>), grid, dim3(256), lds, st, p);
+    else if (NT == 2) hipLaunchKernelGGL((k_pred_up<B, GATED, WT, 2>), grid, dim3(256), lds, st, p);
+    else hipLaunchKernelGGL((k_pred_up<B, GATED, WT, 4>), grid, dim3(256), lds, st, p);
+    if (hipGetLastError() != hipSuccess) return 1;
+    return launch_down_sum<B, GATED, WT>(a, st);
 }
 
 template <int B>
@@ -35,11 +60,24 @@ int launch_b(SplitArgs &a, int wtype, int gated, hipStream_t st) {
     return launch_one<B, false, WT_F16>(a, st);
 }
 
+template <int B>
+int launch_layer_b(PredUpArgs &p, SplitArgs &a, int wtype, int gated, int NT, hipStream_t st) {
+    if (wtype == WT_Q4_0) return launch_layer_one<B, false, WT_Q4_0>(p, a, NT, st);
+    if (gated) return launch_layer_one<B, true, WT_F16>(p, a, NT, st);
+    return launch_layer_one<B, false, WT_F16>(p, a, NT, st);
+}
+
 }  // namespace
 
 int launch_split(SplitArgs &a, int B, int wtype, int gated, hipStream_t st) {
     if (B == 1) return launch_b<1>(a, wtype, gated, st);
     if (B == 2) return launch_b<2>(a, wtype, gated, st);
+    return 1;
+}
+
+int launch_pred_up_split(PredUpArgs &p, SplitArgs &a, int B, int wtype, int gated, int NT, hipStream_t st) {
+    if (B == 1) return launch_layer_b<1>(p, a, wtype, gated, NT, st);
+    if (B == 2) return launch_layer_b<2>(p, a, wtype, gated, NT, st);
     return 1;
 }
 

@@ -80,6 +80,8 @@ struct SplitArgs {
     float *part;                            // [position][S][B*G] partial dot products
     float *ypart;                           // [C][B][d] chunk partials of y
     float *hout;                            // [B][d_ffn] h per position (slab 0 writes it), or nullptr
+    const float *hin;                       // [B][d_ffn] h by neuron id (k_pred_up wrote it; bits mode),
+                                            // or nullptr: h from the partial products of k_up_split
 #ifdef PIK_TRACE
     uint64_t *trace;                        // [grid][8] timestamps
 #endif
@@ -152,8 +154,8 @@ __device__ __forceinline__ int split_count(const SplitArgs &a, int *dyn, int *s_
     return __builtin_amdgcn_readfirstlane(total);
 }
 
-// Slot of list position q (the q-th listed neuron), or -1.
-__device__ __forceinline__ int split_slot(const SplitArgs &a, const int *dyn, int q) {
+// Slot of list position q (the q-th listed neuron), or -1; *id_out receives the neuron id.
+__device__ __forceinline__ int split_slot(const SplitArgs &a, const int *dyn, int q, int *id_out = nullptr) {
     int id;
     if (a.nwords > 0) {
         const int *s_words = dyn, *s_scan = dyn + a.nwords;
@@ -167,6 +169,7 @@ __device__ __forceinline__ int split_slot(const SplitArgs &a, const int *dyn, in
     } else {
         id = a.idx[q];
     }
+    if (id_out != nullptr) *id_out = id;
     return slot_of_id(id, a.slot_of, a.f, a.n_slots);
 }
 
@@ -278,6 +281,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
     static_assert(RMAX * BG <= kSplitThreads, "one thread per (position, component) in the gather");
     extern __shared__ __align__(16) int dyn[];            // scan (bits mode) | wave partials of y
     __shared__ int s_slot[RMAX];
+    __shared__ int s_id[RMAX];
     __shared__ float s_hc[RMAX][BG];
     __shared__ float s_h[RMAX][B];
     __shared__ int s_w[4];
@@ -287,6 +291,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
     SPLIT_TRACE(1);
     const int col = s * SLAB + lane * CPL;
     const int cc = col < a.d ? col : 0;
+    const bool hmode = a.hin != nullptr;
     const int64_t rb = a.row_bytes;
 
     const int n = split_count(a, dyn, s_w, tid, lane, wave);
@@ -300,12 +305,22 @@ __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
 
     for (int r0 = p0; r0 < p1; r0 += RMAX) {
         const int nr = min(RMAX, p1 - r0);
-        if (tid < nr) s_slot[tid] = split_slot(a, dyn, r0 + tid);
+        if (tid < nr) {
+            int id;
+            s_slot[tid] = split_slot(a, dyn, r0 + tid, &id);
+            s_id[tid] = id;
+        }
         __syncthreads();
+        // h mode: thread (j, b) reads h of position j's neuron, token b (goes out before the rows)
+        float hpre = 0.f;
+        if (hmode && tid < nr * B) {
+            const int j = tid / B, b = tid - j * B;
+            hpre = a.hin[(size_t)b * a.f + s_id[j]];
+        }
         // thread (j, k) reads component k of position j from every slab; these loads go out before
         // the row loads, so they return first and h is ready while the rows still stream
         // (through a buffer resource over the round's partials: no branch, an absent one reads 0)
-        const bool mine = tid < nr * BG;
+        const bool mine = !hmode && tid < nr * BG;
         const int jh = mine ? tid / BG : 0, kh = tid - jh * BG;
         const __amdgpu_buffer_rsrc_t rp = buf_rsrc(a.part + (size_t)r0 * a.S * BG, (uint32_t)(nr * a.S * BG) * 4u);
         auto part_off = [&](int u) -> uint32_t {
@@ -334,7 +349,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
         float sum = 0.f;                                        // slab order
 #pragma unroll
         for (int u = 0; u < 16; ++u) sum += pv[u];
-        for (int s0 = 16; s0 < a.S; s0 += 16) {                 // more than 16 slabs (wide rows)
+        for (int s0 = 16; !hmode && s0 < a.S; s0 += 16) {       // more than 16 slabs (wide rows)
 #pragma unroll
             for (int u = 0; u < 16; ++u) pv[u] = __builtin_bit_cast(float, bld4(rp, part_off(s0 + u)));
 #pragma unroll
@@ -346,7 +361,9 @@ __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
             const int j = tid / B, b = tid - j * B;
             const int sl = s_slot[j];
             float hv;
-            if (GATED) {
+            if (hmode) {
+                hv = hpre;
+            } else if (GATED) {
                 hv = fmaxf(s_hc[j][b * 2], 0.f) * s_hc[j][b * 2 + 1];
             } else {
                 const float bias = (a.b_up != nullptr && sl >= 0) ? half_to_float(a.b_up[sl]) : 0.f;
@@ -446,7 +463,161 @@ static __global__ __launch_bounds__(kSplitThreads) void k_sum_split(const float 
     y[o] = sum + (b_down != nullptr ? half_to_float(b_down[o % d]) : 0.f);
 }
 
+// ------------------------------------------------------------------------------ predictor + up
+
+// The second predictor matrix, the mask and the up rows in one launch (layer path, batch <= 2):
+// workgroup t owns the 32-neuron tile t.  It loads the tile's rows of P2 first (they depend on
+// nothing), stages x and z in LDS meanwhile, forms the logits, writes the union mask and the tile's
+// word of listed flags (fired and resident), then each listed neuron of the tile goes to one wave,
+// which reads the neuron's input row(s) against x and stores h by neuron id.  The up rows of a
+// tile are read while other tiles still stream P2, so the up step costs little beyond its bytes.
+// k_down_split then reads h by id (hin) and needs no partial products.
+struct PredUpArgs {
+    int d, f, r, n_slots, act;
+    int64_t row_bytes;
+    const uint16_t *p2, *c;
+    const float *z;                         // [B][r]
+    const uint8_t *w_in;
+    const uint16_t *b_up;
+    const int32_t *slot_of;
+    const uint16_t *x;
+    uint8_t *mask;                          // [f] union flags
+    uint32_t *bits;                         // [ceil(f/32)] listed flags
+    float *h;                               // [B][f] h of listed neurons by id (others untouched)
+};
+
+// Dynamic LDS of k_pred_up: x [B][d] fp16 (q4-paired for Q4_0), then z [B][r] fp32.
+__host__ __device__ inline size_t pred_up_lds(int B, int d, int r) {
+    return ((size_t)B * d * 2 + 15) / 16 * 16 + (size_t)B * r * 4;
+}
+
+template <int B, bool GATED, int WT, int NT>
+__global__ __launch_bounds__(256) void k_pred_up(PredUpArgs a) {
+    constexpr int R = 8;                                  // P2 rows per wave (the tile: 4 x 8)
+    extern __shared__ __align__(16) uint16_t dynx[];
+    __shared__ uint32_t s_words[4];
+    __shared__ int s_slot[32];
+    const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int t = blockIdx.x;
+    const int row0 = t * 32 + wave * R;
+    const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.p2, (uint32_t)((size_t)a.f * a.r * 2));
+    uint4 w[R][NT];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            const int row = row0 + i, col = lane * 8 + q * 512;
+            w[i][q] = bld16(rs, (row < a.f && col < a.r) ? ((uint32_t)row * a.r + col) * 2 : kOOB);
+        }
+    const int rowl = row0 + lane;                         // lane i < R: offset and slot of row i
+    const bool mine = lane < R && rowl < a.f;
+    const uint16_t cbits = mine ? a.c[rowl] : (uint16_t)0;
+    const int slot = mine ? (a.slot_of ? a.slot_of[rowl] : rowl) : -1;
+    uint16_t *xs = dynx;
+    float *zs = reinterpret_cast<float *>(dynx + ((size_t)B * a.d + 7) / 8 * 8);
+    stage_x<B, WT == WT_Q4_0>(xs, a.x, a.d, 0, a.d, a.d);
+    stage_vec16(zs, a.z, B * a.r / 4);
+    __syncthreads();
+    const float ci = half_to_float(cbits);
+    uint32_t mb = 0;                                      // fired bits of the wave's rows (uniform)
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float v[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) v[i] = 0.f;
+#pragma unroll
+        for (int q = 0; q < NT; ++q) {
+            const int col = lane * 8 + q * 512;
+            if (col < a.r) {
+                const float4 za = *reinterpret_cast<const float4 *>(zs + b * a.r + col);
+                const float4 zb = *reinterpret_cast<const float4 *>(zs + b * a.r + col + 4);
+                const float zr[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const uint32_t qq[4] = {w[i][q].x, w[i][q].y, w[i][q].z, w[i][q].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const h2 p = __builtin_bit_cast(h2, qq[e]);
+                        v[i] = fmaf((float)p.x, zr[2 * e], v[i]);
+                        v[i] = fmaf((float)p.y, zr[2 * e + 1], v[i]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const float l = wave_sum(v[i]) + bcastf(ci, i);
+            mb |= (uint32_t)(l > 0.f) << i;
+        }
+    }
+    if (mine) a.mask[rowl] = (uint8_t)((mb >> lane) & 1u);
+    const bool resident = slot >= 0 && slot < a.n_slots;
+    if (lane < R) s_slot[wave * R + lane] = resident ? slot : -1;
+    const uint32_t byte = mb & (uint32_t)__ballot(mine && resident);   // wave w: tile rows 8w .. 8w+7
+    if (lane == 0) s_words[wave] = byte;
+    __syncthreads();
+    const uint32_t word = s_words[0] | (s_words[1] << 8) | (s_words[2] << 16) | (s_words[3] << 24);
+    if (threadIdx.x == 0) a.bits[t] = word;
+    // listed neurons in ascending order: wave w takes the w-th, (w+4)-th, ...; for fp16 rows that one
+    // pass covers, a wave reads two neurons' rows at once (Q4_0 tiles list ~1-2 neurons, and the
+    // second row's registers would cost occupancy)
+    using P = RowPass<B, GATED, WT>;
+    const int64_t in_stride = GATED ? 2 * a.row_bytes : a.row_bytes;
+    const __amdgpu_buffer_rsrc_t rin = buf_rsrc(a.w_in, (uint32_t)(a.n_slots * in_stride));
+    const int cnt = __builtin_popcount(word);
+    const bool pairs = WT == WT_F16 && P::extent(a.d) <= P::STEP;
+    for (int j = wave; j < cnt; j += pairs ? 8 : 4) {
+        const int j2 = j + 4;
+        const bool two = pairs && j2 < cnt;
+        int bit = 0, bit2 = 0;
+        {
+            uint32_t bw = word;
+            for (int q = 0; q < j; ++q) bw &= bw - 1;
+            bit = __builtin_ctz(bw);
+            if (two) {
+                for (int q = j; q < j2; ++q) bw &= bw - 1;
+                bit2 = __builtin_ctz(bw);
+            }
+        }
+        const int s1 = s_slot[bit], s2 = two ? s_slot[bit2] : 0;
+        float ag[B], au[B], ag2[B], au2[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) ag[b] = au[b] = ag2[b] = au2[b] = 0.f;
+        if (pairs) {
+            const int d2 = two ? a.d : 0;                 // a missing second neuron reads nothing
+            P q1, q2;
+            q1.issue_buf(rin, (uint32_t)(s1 * in_stride), a.row_bytes, a.d, 0, lane);
+            q2.issue_buf(rin, (uint32_t)(s2 * in_stride), a.row_bytes, d2, 0, lane);
+            q1.consume(xs, a.d, a.d, 0, lane, ag, au);
+            q2.consume(xs, a.d, d2, 0, lane, ag2, au2);
+        } else {
+            neuron_dots<B, GATED, WT>(a.w_in + (int64_t)s1 * in_stride, a.row_bytes, a.d, xs, a.d, lane, ag, au);
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            if (n == 1 && !two) break;                    // wave-uniform
+            const int sl = n == 0 ? s1 : s2, id = t * 32 + (n == 0 ? bit : bit2);
+            const float bias = (!GATED && a.b_up != nullptr) ? half_to_float(a.b_up[sl]) : 0.f;
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const float u = wave_sum(n == 0 ? au[b] : au2[b]);
+                float hv;
+                if (GATED) {
+                    hv = fmaxf(wave_sum(n == 0 ? ag[b] : ag2[b]), 0.f) * u;
+                } else {
+                    hv = fmaxf(u + bias, 0.f);
+                    if (a.act) hv *= hv;                  // squared ReLU
+                }
+                if (lane == 0) a.h[(size_t)b * a.f + id] = hv;
+            }
+        }
+    }
+}
+
 // Launch of the three kernels for batch width B in {1, 2}; C is chosen here.
 int launch_split(SplitArgs &a, int B, int wtype, int gated, hipStream_t st);
+// The layer path: k_pred_up (NT = rank / 512 rounded up to 1, 2 or 4), then k_down_split on h by
+// id and k_sum_split.
+int launch_pred_up_split(PredUpArgs &p, SplitArgs &a, int B, int wtype, int gated, int NT, hipStream_t st);
 
 }  // namespace pik
