@@ -42,6 +42,8 @@ HEADLINE = (5, 1)              # (stack id, batch): OPT-175B-shaped Q4_0 stack a
 DETAIL = ((5, 8), (2, 1), (3, 1), (3, 4), (4, 1), (1, 1))
 REPS = 5                       # replays of each timed graph; the median is reported
 COPY_PROBE_MIB = 256
+CU_NUM = 256                   # MI355X compute units (the counter formulas divide by it)
+NUM_XCC = 8                    # ... in 8 XCDs
 
 
 def kernel_sources_sha256() -> str:
@@ -106,6 +108,8 @@ def parse():
                          "known traffic, for scaling hardware byte counters)")
     ap.add_argument("--pmc-summary", nargs="+", metavar=("WORKLOAD", "DIR"),
                     help="summarize rocprofv3 --pmc directories into profiles/ (no GPU) and exit")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("WORKLOAD", "DIR"),
+                    help="summarize a rocprofv3 --kernel-trace --stats directory into profiles/ (no GPU) and exit")
     ap.add_argument("--pmc-command", action="append", default=[],
                     help="with --pmc-summary: the command that made each directory (recorded in the summary)")
     return ap.parse_args()
@@ -141,13 +145,13 @@ def ffn_kernel_names(h_kind: int, B: int, cfg, synth):
     g = "true" if cfg.gated else "false"
     w = 1 if cfg.wtype == synth.F16 else 2
     if h_kind == 1:
-        return "k_sparse_ffn", [f"void pik::k_sparse_ffn<{B}, {g}, {w}>"]
+        return "k_up_split + k_down_split + k_sum_split", [f"void pik::k_up_split<{B}, {g}, {w}>",
+                                                         f"void pik::k_down_split<{B}, {g}, {w}>",
+                                                         "pik::k_sum_split("]
     if h_kind == 2:
         return "k_sparse_up + k_sparse_down", [f"void pik::k_sparse_up<{B}, {g}, {w}>", f"void pik::k_sparse_down<{B}, {w}>"]
     if h_kind == 3:
         return "k_wide_up + k_wide_down", ["void pik::k_wide_up<", "void pik::k_wide_down<"]
-    if h_kind == 4:
-        return "k_ffn_split", [f"void pik::k_ffn_split<{B}, {g}, {w},"]
     return f"kind {h_kind}", []
 
 
@@ -261,6 +265,12 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
     w = 1 if cfg.wtype == synth.F16 else 2
     if path == 1:
         rest_label, rest_prefixes = "k_layer_tail", [f"void pik::k_layer_tail<{B}, {g}, {w},"]
+    elif h_kind == 1:
+        # the layer's own form at batch <= 2: logits, mask and up rows in one kernel, then the down
+        # rows on h by neuron id
+        rest_label = "k_pred_up + k_down_split + k_sum_split"
+        rest_prefixes = [f"void pik::k_pred_up<{B}, {g}, {w},", f"void pik::k_down_split<{B}, {g}, {w}>",
+                         "pik::k_sum_split("]
     else:
         rest_label, rest_prefixes = "k_pred_l2 + " + ffn_label, ["void pik::k_pred_l2<"] + ffn_prefixes
     step_bytes = (pred_bytes + float(ffn_touched.mean())) * L
@@ -501,13 +511,17 @@ def pmc_summary(args):
         if hit is not None and miss is not None and hit + miss > 0:
             d["L2 hit rate"] = hit / (hit + miss)
         wc, gui = mean("SQ_WAVE_CYCLES"), mean("GRBM_GUI_ACTIVE")
+        if gui:
+            gui /= NUM_XCC                    # the CSV sums the per-XCD busy counters; the formula takes one
         if wc is not None and gui:
-            d["mean waves per CU"] = wc / gui / 256.0
-        iv, av = mean("SQ_INSTS_VALU"), mean("SQ_ACTIVE_INST_VALU")
+            # rocprofv3's OccupancyPercent: 400 * SQ_WAVE_CYCLES / GRBM_GUI_ACTIVE / CU_NUM / 32
+            d["occupancy %"] = 400.0 * wc / gui / CU_NUM / 32.0
+            d["mean resident waves per CU"] = 4.0 * wc / gui / CU_NUM
+        iv = mean("SQ_INSTS_VALU")
         if iv is not None and mean("SQ_WAVES"):
-            d["VALU insts per wave"] = iv / mean("SQ_WAVES")
-        if av is not None and gui:
-            d["VALU busy per CU-cycle"] = av / gui / 256.0
+            d["VALU instructions per wave"] = iv / mean("SQ_WAVES")
+        if gui:
+            d["GPU busy cycles per XCD"] = gui
         if d:
             derived.append((k, d))
     if derived:
@@ -532,12 +546,37 @@ def pmc_summary(args):
     print("\n".join(lines))
 
 
+def trace_summary(args):
+    """Summarize a rocprofv3 --kernel-trace --stats directory (a run of this script) per kernel."""
+    import csv
+    import glob
+    workload, dd = args.trace_summary
+    files = glob.glob(os.path.join(dd, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {dd}")
+    rows = list(csv.DictReader(open(files[0])))
+    lines = [f"# Kernel trace: {workload}", "", "Command (from the repository root):", "", "```"]
+    lines += args.pmc_command or ["(not recorded)"]
+    lines += ["```", "", f"Sources sha256: `{kernel_sources_sha256()}`", "",
+              "| kernel | calls | average us | min us | max us | share of GPU time |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        lines.append(f"| `{r['Name'][:100]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.2f}% |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 # ---------------------------------------------------------------------------------- main
 
 def main():
     args = parse()
     if args.pmc_summary:
         pmc_summary(args)
+        return
+    if args.trace_summary:
+        trace_summary(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the sparse-FFN hot path has no multi-GPU leg "
@@ -636,7 +675,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": f"{ffn_label} (pi_sparse_ffn: gathered up rows with bias + ReLU, active rows of W_down^T)",
+            "kernel": f"{ffn_label} (pi_sparse_ffn: the listed neurons' up rows with bias and ReLU, their rows "
+                      f"of W_down^T)",
             "achieved": round(roof_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
