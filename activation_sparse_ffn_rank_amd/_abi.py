@@ -206,9 +206,18 @@ def pi_layer_path(pred, ffn, batch) -> int:
 PI_WS_STATUS_OFFSET = 384      # byte offset of the layer workspace's sticky status word
 
 
+PI_STATUS_H_RANGE = 64        # status bit: an |h| the MFMA form's fp16 pair cannot carry
+
+
 def workspace_status(ws) -> int:
-    """Sticky status word of a pi_ffn_layer workspace (0 = every cross-workgroup wait completed)."""
+    """Sticky status word of a pi_ffn_layer or pi_sparse_ffn workspace (0 = every cross-workgroup
+    wait completed and every h was in range)."""
     return int(ws[PI_WS_STATUS_OFFSET:PI_WS_STATUS_OFFSET + 4].view(torch.int32).item())
+
+
+def wide_workspace_status(ws) -> int:
+    """Sticky status word of a pi_sparse_ffn_wide workspace (its first int32)."""
+    return int(ws[0:4].view(torch.int32).item())
 
 
 def pi_sparse_ffn_h_offset(ffn, batch: int) -> tuple[int, int]:

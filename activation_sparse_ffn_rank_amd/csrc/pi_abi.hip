@@ -77,12 +77,13 @@ int x_chunk(int d, int B) {
 
 int down_slabs(int d) { return ceil_div(d, 512); }
 
-// Workspace of pi_sparse_ffn_wide: slab tickets, h as fp16 hi and lo parts [16][hs], and the
-// chunk partials [C][B][d] fp32.
+// Workspace of pi_sparse_ffn_wide: a status word (its first int32; 256 bytes reserved), slab
+// tickets, h as fp16 hi and lo parts [16][hs], and the chunk partials [C][B][d] fp32.
 constexpr int kWideTargetGroups = 256;   // (slab, chunk) workgroups of k_wide_down (8 waves each)
+constexpr size_t kWideStatusBytes = 256;
 struct WideGeom {
     int S, C, hs;
-    size_t hi, lo, part, total;
+    size_t tick, hi, lo, part, total;
 };
 WideGeom wide_geom(const pi_ffn *fn, int B) {
     WideGeom g{};
@@ -90,7 +91,8 @@ WideGeom wide_geom(const pi_ffn *fn, int B) {
     g.S = ceil_div(d, 16 * wide_down_cpl(fn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16));
     g.C = std::min(kWideMaxChunks, std::max(1, ceil_div(kWideTargetGroups, g.S)));
     g.hs = ceil_div(std::max(fn->n_slots, 1), 32) * 32;    // k_wide_up writes whole 32-position groups
-    g.hi = align_up((size_t)g.S * 4);
+    g.tick = kWideStatusBytes;
+    g.hi = g.tick + align_up((size_t)g.S * 4);
     g.lo = g.hi + align_up((size_t)kWideB * g.hs * 2);
     g.part = g.lo + align_up((size_t)kWideB * g.hs * 2);
     g.total = g.part + align_up((size_t)g.C * B * d * 4);
@@ -421,11 +423,14 @@ int enqueue_split(const pi_ffn *fn, const void *x, int B, const int32_t *idx, co
     return launch_split(a, B, wt, fn->gated, st) == 0 ? PI_OK : PI_ERR_HIP;
 }
 
-// The MFMA form of the sparse FFN (k_wide_up, then k_wide_down) on a wide workspace at w.
+// The MFMA form of the sparse FFN (k_wide_up, then k_wide_down) on a wide workspace at w; status:
+// the sticky status word that an h outside the fp16 pair's range is reported in (NULL: the wide
+// workspace's own).
 int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y, char *w,
-                 hipStream_t st) {
+                 hipStream_t st, int32_t *status = nullptr) {
     const WideGeom g = wide_geom(fn, B);
-    int32_t *tickets = reinterpret_cast<int32_t *>(w);
+    int32_t *tickets = reinterpret_cast<int32_t *>(w + g.tick);
+    if (status == nullptr) status = reinterpret_cast<int32_t *>(w);
     uint16_t *h_hi = reinterpret_cast<uint16_t *>(w + g.hi), *h_lo = reinterpret_cast<uint16_t *>(w + g.lo);
     float *part = reinterpret_cast<float *>(w + g.part);
     const int d = fn->d_model, f = fn->d_ffn, ns = fn->n_slots;
@@ -436,13 +441,13 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
     if (fn->wtype == PI_Q4_0)
         hipLaunchKernelGGL((k_wide_up<false, WT_Q4_0, 2>), dim3(std::max(1, ceil_div(ns, 32))), dim3(kWideThreads), 0,
                            st, w_in, rb, d, b_up, xx, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets,
-                           g.S, fn->act);
+                           g.S, fn->act, status);
     else if (fn->gated)
         hipLaunchKernelGGL((k_wide_up<true, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
-                           B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, fn->act);
+                           B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, fn->act, status);
     else
         hipLaunchKernelGGL((k_wide_up<false, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
-                           B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, fn->act);
+                           B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, fn->act, status);
     const uint8_t *w_dn = static_cast<const uint8_t *>(fn->w_down_t);
     const uint16_t *b_dn = static_cast<const uint16_t *>(fn->b_down);
     if (fn->wtype == PI_Q4_0)
@@ -455,13 +460,15 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
 }
 
 // pi_sparse_ffn's work on a workspace laid out by ffn_ws; bits: listed-flag words to take the
-// positions from instead of idx/counts.
+// positions from instead of idx/counts; status: the status word to report in (NULL: the
+// workspace's own, at byte offset 384).
 int enqueue_sparse(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y,
-                   void *ws, hipStream_t st, const uint32_t *bits = nullptr) {
+                   void *ws, hipStream_t st, const uint32_t *bits = nullptr, int32_t *status = nullptr) {
     char *w = static_cast<char *>(ws);
     if (sparse_split(fn, B))
         return enqueue_split(fn, x, B, idx, counts, bits, y, w + ctl_bytes(fn->d_model), st);
-    if (sparse_wide(fn, B)) return enqueue_wide(fn, x, B, idx, counts, y, w + ctl_bytes(fn->d_model), st);
+    if (status == nullptr) status = reinterpret_cast<int32_t *>(w) + CTL_STATUS;
+    if (sparse_wide(fn, B)) return enqueue_wide(fn, x, B, idx, counts, y, w + ctl_bytes(fn->d_model), st, status);
     return enqueue_sparse_legacy(fn, x, B, idx, counts, y, ffn_scratch(fn, B, w + ctl_bytes(fn->d_model)), st);
 }
 
@@ -644,7 +651,7 @@ int layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const void *x
     }
     if ((rc = enqueue_pred_l2(pred, z, batch, mask, nullptr, st))) return rc;
     if ((rc = enqueue_compact(mask, f, ffn->slot_of, idx, counts, st))) return rc;
-    return enqueue_sparse(ffn, x, batch, idx, counts, y, L.ffn, st);
+    return enqueue_sparse(ffn, x, batch, idx, counts, y, L.ffn, st, nullptr, L.ctl + CTL_STATUS);
 }
 
 int check_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, const float *y,

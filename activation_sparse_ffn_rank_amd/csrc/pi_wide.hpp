@@ -33,6 +33,7 @@ namespace pik {
 
 constexpr int kWideB = 16;            // the padded batch: one MFMA M (or N) dimension
 constexpr int kWideUpCols = 256;      // columns per k_wide_up block (8 column groups of 32)
+constexpr int kStatusHRange = 64;     // status bit: some |h| reached 65504 (outside the fp16 pair)
 // columns per lane per row in k_wide_down (a slab is 16 lanes wide)
 constexpr int wide_down_cpl(int wt) { return wt == WT_Q4_0 ? 16 : 8; }
 constexpr int kWideMaxChunks = 16;    // chunk partials per slab summed by the last workgroup
@@ -63,7 +64,8 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
                                                  const int32_t *__restrict__ counts,
                                                  const int32_t *__restrict__ slot_of, int f, int n_slots,
                                                  uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int hs,
-                                                 int32_t *__restrict__ zero_ptr, int nzero, int act) {
+                                                 int32_t *__restrict__ zero_ptr, int nzero, int act,
+                                                 int32_t *__restrict__ status) {
     __shared__ f4 red[GATED ? 2 : NT][kWideWaves][kWave];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     if (blockIdx.x == 0)
@@ -185,6 +187,9 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
     }
     const int st = tile == 0 ? sl[0] : sl[NT - 1];
     if (st < 0 || b >= B) hv = 0.f;
+    // h travels to the down kernel as an fp16 pair; beyond fp16's range the pair cannot hold it,
+    // and y would not be finite: say so in the status word instead of failing silently
+    if (!(fabsf(hv) < 65504.f)) atomicOr(status, kStatusHRange);
     const int pt = pos + 16 * tile;
     const f16 hi = (f16)hv;
     const f16 lo = (f16)(hv - (float)hi);

@@ -125,10 +125,11 @@ int pi_compact(const uint8_t *mask, int32_t d_ffn, const int32_t *slot_of, int32
  * (h, then the rows of W_down^T; from batch 3 for gated or Q4_0 rows and from batch 6 for other
  * fp16 rows, the MFMA kernels of pi_sparse_ffn_wide).  None of these kernels waits on another
  * workgroup; y is deterministic.  The workspace starts with a 512-byte control block whose int32 at
- * byte offset 384 is the sticky status word of the persistent layer kernel (pi_ffn_layer); the
- * sparse-FFN kernels leave it untouched, so a zero-filled workspace reads status 0 after any of
- * them.  The workspace needs no zero fill for pi_sparse_ffn itself and must not be shared by calls
- * in flight at the same time. */
+ * byte offset 384 is a sticky status word: the MFMA form hands h to its second kernel as an fp16
+ * pair, so an |h| of 65504 or more cannot be carried -- it ORs 64 into the status word and that
+ * call's y is invalid; the other forms have no such limit and leave the word untouched.  Zero-fill
+ * the workspace once to read the status; the calls themselves need no zero fill.  A workspace must
+ * not be shared by calls in flight at the same time. */
 int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx,
                   const int32_t *counts, float *y, void *ws, size_t ws_bytes, void *stream);
 
@@ -139,10 +140,12 @@ int pi_sparse_ffn(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t
  * y as in pi_sparse_ffn, with 1 <= batch <= PI_MAX_WIDE_BATCH (PI_ERR_BATCH otherwise); fp16 and
  * Q4_0 rows (Q4_0 weights enter the MFMA as fp16 scale * (code - 8), rounded once to fp16).
  * Two kernels; the workspace of
- * pi_sparse_ffn_wide_workspace_bytes(ffn, batch) bytes (16-byte aligned) needs no zero fill, holds
- * no status word, and must not be shared by calls in flight at the same time.  h passes between
- * the kernels as an fp16 pair (h = hi + lo), so |h| must stay below 65504.  y is deterministic
- * (fixed summation order).  The workspace-size call returns 0 on invalid arguments. */
+ * pi_sparse_ffn_wide_workspace_bytes(ffn, batch) bytes (16-byte aligned) must not be shared by calls
+ * in flight at the same time.  h passes between the kernels as an fp16 pair (h = hi + lo), so |h|
+ * must stay below 65504: a larger one ORs 64 into the sticky status word that is the workspace's
+ * first int32 (zero-fill the workspace once to read it; the calls need no zero fill otherwise) and
+ * that call's y is invalid.  y is deterministic (fixed summation order).  The workspace-size call
+ * returns 0 on invalid arguments. */
 size_t pi_sparse_ffn_wide_workspace_bytes(const pi_ffn *ffn, int32_t batch);
 int pi_sparse_ffn_wide(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx,
                        const int32_t *counts, float *y, void *ws, size_t ws_bytes, void *stream);
@@ -161,7 +164,9 @@ int pi_sparse_ffn_wide(const pi_ffn *ffn, const void *x, int32_t batch, const in
  *    ready for the next one (never clear or share it while a call is in flight);
  *  - the int32 at byte offset 384 of the workspace is a sticky status word: nonzero means a
  *    cross-workgroup wait ran out its time limit (20 ms) and the outputs of that call are invalid.
- * Every wait inside the kernel is bounded.  Zero-filling the workspace once is always safe. */
+ * Every wait inside the kernel is bounded.  Zero-filling the workspace once is always safe.  At the
+ * batches where the sparse FFN runs on the MFMA form, an |h| of 65504 or more ORs 64 into the same
+ * status word (see pi_sparse_ffn). */
 int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch,
                  float *y, uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws,
                  size_t ws_bytes, void *stream);

@@ -282,6 +282,15 @@ def test_graph_replay_matches_eager(entry):
         with torch.cuda.graph(g, stream=s):
             for l in range(3):
                 run(dls[l].pred, dls[l].ffn, xs[l], 1, ys[l], None, None, None, ws)
+    # the eager result of each layer against the oracle, given the GPU's own list (same launches)
+    refs = []
+    for l in range(3):
+        x = synth.make_x(cfg, l, 0, 1)
+        got = gpu_layer(dls[l], x)
+        assert np.array_equal(got["y"], eager[l].cpu().numpy()), f"layer {l}: outputs depend on the requested lists"
+        check_mask(got["mask"], oracle.predict(layers[l].p1, layers[l].p2, layers[l].c, x)[0], f"layer {l}")
+        refs.append(oracle.sparse_ffn(cfg.d, cfg.f, False, cfg.wtype, layers[l].w_in, layers[l].w_down_t, x,
+                                      got["idx"], b_up=layers[l].b_up))
     for rep in range(4):
         for y in ys:
             y.fill_(float("nan"))
@@ -289,6 +298,7 @@ def test_graph_replay_matches_eager(entry):
         torch.cuda.synchronize()
         for l in range(3):
             assert torch.equal(ys[l], eager[l]), f"replay {rep} layer {l}"
+            check_y(ys[l].cpu().numpy(), refs[l], cfg.wtype, f"replay {rep} layer {l} vs oracle")
         # eager work between replays
         run(dls[0].pred, dls[0].ffn, xs[0], 1, ys[0], None, None, None, ws)
         torch.cuda.synchronize()
@@ -337,6 +347,52 @@ def test_many_calls_share_one_workspace(entry):
     assert _abi.workspace_status(ws) == 0
     got = check_layer_against_oracle(layers[1], dls[1], synth.make_x(cfg, 1, 4, 1), "after many calls", entries=(entry,))
     assert got["n"] > 0
+
+
+@pytest.mark.parametrize("case", [
+    dict(d=1024, f=4096, r=128, gated=False, wtype=F16, bias_up=True, density=0.1),          # tail kernel
+    dict(d=2048, f=5503, r=256, gated=True, wtype=F16, bias_up=False, density=0.12),         # tail kernel, ReGLU
+    dict(d=1024, f=40000, r=128, gated=False, wtype=F16, bias_up=True, density=0.05),        # separate kernels
+    dict(d=1024, f=40000, r=128, gated=False, wtype=Q4, bias_up=True, density=0.05),         # ... Q4_0
+    dict(d=1536, f=6001, r=512, gated=False, wtype=F16, bias_up=True, density=0.06, hot_frac=0.26),
+], ids=["tail_relu", "tail_reglu", "split_relu", "split_q4_0", "tail_placement"])
+@pytest.mark.parametrize("B", [1, 2])
+def test_layer_reads_no_unlisted_row(case, B):
+    """pi_ffn_layer reads no row outside the predicted, resident set: with every other row poisoned
+    with NaN (fp16 weights, or Q4_0 scales) y is bitwise the unpoisoned y and matches the oracle, and
+    nothing is written past y (guard band)."""
+    announce(f"poisoned layer {case} B={B}")
+    cfg = synth.custom_config(**case, seed=300 + B)
+    layer = synth.make_layer(cfg, 0, bias_scale=1.0, b_down=True)
+    dl = DeviceLayer.from_host(layer)
+    x = synth.make_x(cfg, 0, 0, B)
+    clean = gpu_layer(dl, x)
+    listed = clean["idx"]
+    assert clean["n"] > 0
+    slots = listed if layer.slot_of is None else layer.slot_of[listed]
+    keep = np.zeros(layer.w_in.shape[0], bool)
+    keep[slots] = True
+    w_in_p, w_dn_p = layer.w_in.copy(), layer.w_down_t.copy()
+    if cfg.wtype == F16:
+        w_in_p[~keep] = 0x7E00
+        w_dn_p[~keep] = 0x7E00
+    else:
+        w_in_p[~keep, cfg.d // 2:] = 0x7E
+        w_dn_p[~keep, cfg.d // 2:] = 0x7E
+    dlp = DeviceLayer(p1=layer.p1, p2=layer.p2, c=layer.c, w_in=w_in_p, w_down_t=w_dn_p, d_model=cfg.d, d_ffn=cfg.f,
+                      gated=cfg.gated, wtype=cfg.wtype, slot_of=layer.slot_of, b_up=layer.b_up, b_down=layer.b_down)
+    guard = 64
+    y = torch.full((B * cfg.d + guard,), 4242.0, dtype=torch.float32, device="cuda")
+    ws = dlp.workspace(B)
+    _abi.pi_ffn_layer(dlp.pred, dlp.ffn, to_dev(x), B, y, None, None, None, ws)
+    torch.cuda.synchronize()
+    assert _abi.workspace_status(ws) == 0
+    yh = y.cpu().numpy()
+    assert np.all(yh[B * cfg.d:] == 4242.0), "write past the end of y"
+    assert np.array_equal(yh[: B * cfg.d].reshape(B, cfg.d), clean["y"]), "an unlisted row changed y"
+    y_ref = oracle.sparse_ffn(cfg.d, cfg.f, cfg.gated, cfg.wtype, layer.w_in, layer.w_down_t, x, listed,
+                              b_up=layer.b_up, b_down=layer.b_down, slot_of=layer.slot_of)
+    check_y(yh[: B * cfg.d].reshape(B, cfg.d), y_ref, cfg.wtype, "poisoned layer")
 
 
 def test_split_layer_matches_whole_layer():

@@ -55,7 +55,7 @@ def _run_wide(dl, x, B, idx, n_listed=None):
     d = dl.ffn.d_model
     guard = 64
     y = torch.full((B * d + guard,), 12345.0, dtype=torch.float32, device="cuda")
-    ws = torch.empty(_abi.pi_sparse_ffn_wide_workspace_bytes(dl.ffn, B), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(_abi.pi_sparse_ffn_wide_workspace_bytes(dl.ffn, B), dtype=torch.uint8, device="cuda")
     n = idx.size if n_listed is None else n_listed
     counts = to_dev(np.array([n, n], np.int32))
     idx_d = to_dev(idx) if idx.size else torch.zeros(1, dtype=torch.int32, device="cuda")
@@ -63,6 +63,7 @@ def _run_wide(dl, x, B, idx, n_listed=None):
     torch.cuda.synchronize()
     yh = y.cpu().numpy()
     assert np.all(yh[B * d:] == 12345.0), "write past the end of y"
+    assert _abi.wide_workspace_status(ws) == 0
     return yh[: B * d].reshape(B, d), (x, idx_d, counts, ws)
 
 
@@ -182,3 +183,38 @@ def test_sparse_ffn_wide_rejects():
     assert call() == _abi.PI_OK                                  # empty list: y = b_down (none) = 0
     torch.cuda.synchronize()
     assert torch.all(y == 0).item()
+
+
+@pytest.mark.parametrize("gated,wtype", [(True, F16), (False, Q4)])
+@pytest.mark.parametrize("entry", ["sparse_ffn", "wide"])
+def test_h_beyond_fp16_range_is_reported(gated, wtype, entry):
+    """The MFMA form carries h as an fp16 pair: one neuron with |h| >= 65504 must set bit 64 of the
+    status word (pi_sparse_ffn at batch 3 runs that form for ReGLU and Q4_0 rows; pi_sparse_ffn_wide
+    always does), and the same layer without that neuron listed must not."""
+    announce(f"h range gated={gated} wtype={wtype} entry={entry}")
+    d, f, B, big = 1024, 64, 3, 5
+    cfg, w_in, w_dn, b_up, b_down = _layer(d, f, gated, 0, seed=77, wtype=wtype)
+    if wtype == F16:
+        w_in[big, :d] = 0x5400                    # gate row: 64.0 everywhere -> gate = 65536 at x = 1
+        w_in[big, d:] = 0x1400                    # up row: 2^-10 everywhere  -> up = 1
+    else:
+        w_in[big, : d // 2] = 0xFF                # every code 15: weight 7 * scale
+        w_in[big, d // 2:] = np.frombuffer(np.array([0x489A], np.uint16).tobytes() * (d // 32), np.uint8)
+    dl = DeviceLayer(p1=np.zeros((8, d), np.uint16), p2=np.zeros((f, 8), np.uint16), c=np.zeros(f, np.uint16),
+                     w_in=w_in, w_down_t=w_dn, d_model=d, d_ffn=f, gated=gated, wtype=wtype, b_up=b_up, b_down=b_down)
+    x = to_dev(np.full((B, d), 0x3C00, np.uint16))                    # x = 1
+    y = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    for listed, expect in ((np.array([1, 2, big, 9], np.int32), True), (np.array([1, 2, 9], np.int32), False)):
+        counts = to_dev(np.array([listed.size, listed.size], np.int32))
+        if entry == "wide":
+            ws = torch.zeros(_abi.pi_sparse_ffn_wide_workspace_bytes(dl.ffn, B), dtype=torch.uint8, device="cuda")
+            _abi.pi_sparse_ffn_wide(dl.ffn, x, B, to_dev(listed), counts, y, ws)
+            torch.cuda.synchronize()
+            st = _abi.wide_workspace_status(ws)
+        else:
+            ws = torch.zeros(_abi.pi_workspace_bytes(None, dl.ffn, B), dtype=torch.uint8, device="cuda")
+            assert _abi.pi_sparse_ffn_h_offset(dl.ffn, B)[1] == 3            # the MFMA form runs
+            _abi.pi_sparse_ffn(dl.ffn, x, B, to_dev(listed), counts, y, ws)
+            torch.cuda.synchronize()
+            st = _abi.workspace_status(ws)
+        assert bool(st & _abi.PI_STATUS_H_RANGE) == expect, (listed.tolist(), st)
