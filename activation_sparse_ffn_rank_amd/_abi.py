@@ -18,7 +18,7 @@ PI_OK, PI_ERR_NULL, PI_ERR_SHAPE, PI_ERR_DTYPE, PI_ERR_BATCH, PI_ERR_WORKSPACE, 
     0, -1, -2, -3, -4, -5, -6, -7)
 PI_F16, PI_Q4_0 = 1, 2
 PI_ACT_RELU, PI_ACT_SQUARED_RELU = 0, 1
-PI_MAX_BATCH = 8
+PI_MAX_BATCH = 16
 PI_MAX_WIDE_BATCH = 16
 
 # Every function the header declares; the CPU tests check that libpi.so exports them all.

@@ -34,6 +34,12 @@ inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
 int check_batch(int32_t B) { return (B >= 1 && B <= PI_MAX_BATCH) ? PI_OK : PI_ERR_BATCH; }
+// The GEMV kernels (first predictor matrix, tail kernel, GEMV sparse FFN) are instantiated for up to
+// 8 tokens; past that the first predictor matrix runs in two passes and the rest on MFMA.
+constexpr int kGemvMaxBatch = 8;
+// From this batch on the second predictor matrix runs on MFMA (k_pred_l2_mfma): the GEMV form's
+// vector-ALU work per weight grows with the batch.
+constexpr int kPredMfmaFrom = 9;
 
 int check_pred(const pi_predictor *p) {
     if (!p) return PI_ERR_NULL;
@@ -165,6 +171,7 @@ bool layer_pred_up(const pi_predictor *p, const pi_ffn *fn, int B) {
 // <= 2 up to d_ffn = 32 * kTailMaxTilesB2 (up workgroups then take several tiles each; measured
 // faster than separate kernels there, slower at larger batch).
 bool tail_persistent(const pi_predictor *p, const pi_ffn *fn, int B) {
+    if (B > kGemvMaxBatch) return false;
     const size_t stat = (size_t)4 * B * kTailCPL * 64 * 4 + (size_t)B * kTailSlab * 4 + (size_t)kTailListMax * 4 + 512;
     // the kernel reads through 32-bit buffer offsets: every matrix (and the partials) must stay
     // below kBufMax bytes
@@ -255,6 +262,18 @@ int enqueue_pred_l2_b(const pi_predictor *p, const float *z, uint8_t *mask, floa
 
 int enqueue_pred_l2(const pi_predictor *p, const float *z, int B, uint8_t *mask, float *logits, hipStream_t st,
                     uint32_t *bits = nullptr, const int32_t *slot_of = nullptr, int n_slots = 0) {
+    if (B >= kPredMfmaFrom) {
+        const int r = p->rank, f = p->d_ffn;
+        const uint16_t *p2 = static_cast<const uint16_t *>(p->p2), *c = static_cast<const uint16_t *>(p->c);
+        const dim3 grid(ceil_div(f, 64));
+        if (r >= 256)
+            hipLaunchKernelGGL(k_pred_l2_mfma<8>, grid, dim3(256), 0, st, p2, c, z, B, r, f, logits, mask, bits, slot_of,
+                               n_slots);
+        else
+            hipLaunchKernelGGL(k_pred_l2_mfma<4>, grid, dim3(256), 0, st, p2, c, z, B, r, f, logits, mask, bits, slot_of,
+                               n_slots);
+        return launch_status();
+    }
     switch (B) {
         case 1: return enqueue_pred_l2_b<1>(p, z, mask, logits, bits, slot_of, n_slots, st);
         case 2: return enqueue_pred_l2_b<2>(p, z, mask, logits, bits, slot_of, n_slots, st);
@@ -289,6 +308,13 @@ void enqueue_pred_l1_b(const pi_predictor *p, const uint16_t *x, float *z, hipSt
 
 int enqueue_pred_l1(const pi_predictor *p, const void *x, int B, float *z, hipStream_t st) {
     const uint16_t *xx = static_cast<const uint16_t *>(x);
+    if (B > kGemvMaxBatch) {
+        // tokens 0..7, then the rest: P1 is read twice, x and z rows are offset
+        int rc = enqueue_pred_l1(p, x, kGemvMaxBatch, z, st);
+        if (rc) return rc;
+        return enqueue_pred_l1(p, xx + (size_t)kGemvMaxBatch * p->d_model, B - kGemvMaxBatch,
+                               z + (size_t)kGemvMaxBatch * p->rank, st);
+    }
     switch (B) {
         case 1: enqueue_pred_l1_b<1>(p, xx, z, st); break;
         case 2: enqueue_pred_l1_b<2>(p, xx, z, st); break;
@@ -734,7 +760,7 @@ const char *pi_status_string(int status) {
         case PI_ERR_NULL: return "a required pointer is NULL";
         case PI_ERR_SHAPE: return "a size is out of range or inconsistent";
         case PI_ERR_DTYPE: return "unsupported weight kind or gating combination";
-        case PI_ERR_BATCH: return "batch outside [1, 8] ([1, 16] for pi_sparse_ffn_wide)";
+        case PI_ERR_BATCH: return "batch outside [1, 16]";
         case PI_ERR_WORKSPACE: return "workspace missing or too small";
         case PI_ERR_ALIGN: return "pointer or row not 16-byte aligned";
         case PI_ERR_HIP: return "HIP kernel launch failed";

@@ -197,6 +197,106 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
     h_lo[(size_t)b * hs + pt] = __builtin_bit_cast(uint16_t, lo);
 }
 
+// ------------------------------------------------------------------------------ predictor on MFMA
+
+typedef f16 h8 __attribute__((ext_vector_type(8)));
+
+// gfx950's v_mfma_f32_16x16x32_f16: lane l supplies 8 k-values of row l%16 of A and of column l%16
+// of B (lane group l/16 holds k-slots 8(l/16) .. +8) and receives D[4(l/16) + v][l%16], v < 4.
+__device__ __forceinline__ f4 mfma32(const uint4 &a, const uint4 &b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
+}
+
+// fp32 -> fp16 pair (hi = fp16(v), lo = fp16(v - hi)) of 8 consecutive values, so that v = hi + lo
+// to ~2^-22 relative and an f16 MFMA over both parts loses nothing against fp32 z.
+__device__ __forceinline__ void split8(const float4 &p, const float4 &q, uint4 &hi, uint4 &lo) {
+    const float v[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const f16 a0 = (f16)v[2 * i], a1 = (f16)v[2 * i + 1];
+        const f16 b0 = (f16)(v[2 * i] - (float)a0), b1 = (f16)(v[2 * i + 1] - (float)a1);
+        h[i] = (uint32_t)__builtin_bit_cast(uint16_t, a0) | ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
+        l[i] = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+    }
+    hi = make_uint4(h[0], h[1], h[2], h[3]);
+    lo = make_uint4(l[0], l[1], l[2], l[3]);
+}
+
+// l[b][i] = P2[i] . z_b + c[i], mask[i] = OR_{b < B} [l > 0] for up to 16 tokens, on MFMA: wave w of
+// workgroup t owns neurons 64t + 16w .. +16 (the MFMA's n = l%16) and all 16 token slots (m; tokens
+// >= B read z as zero and are never counted).  Per 32-column step lane group g reads columns
+// 32j + 8g .. +8 of its neuron's P2 row (16 bytes) and of its token's z (fp32, split into an fp16
+// hi + lo pair in registers), and issues two MFMAs.  P2 and z go through buffer resources, so a
+// column past r or a row past f reads zero without a branch.  Optional outputs as in k_pred_l2:
+// logits, and the placement-restricted listed flags as 32-bit words (bits[2t + w/2]).
+template <int KC>
+__global__ __launch_bounds__(256) void k_pred_l2_mfma(const uint16_t *__restrict__ p2, const uint16_t *__restrict__ c,
+                                                      const float *__restrict__ z, int B, int r, int f,
+                                                      float *__restrict__ logits, uint8_t *__restrict__ mask,
+                                                      uint32_t *__restrict__ bits, const int32_t *__restrict__ slot_of,
+                                                      int n_slots) {
+    __shared__ uint32_t s_half[4];
+    const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int n16 = lane & 15, g = lane >> 4;
+    const int nrow = blockIdx.x * 64 + wave * 16 + n16;               // this lane's neuron (B operand)
+    const __amdgpu_buffer_rsrc_t rp = buf_rsrc(p2, (uint32_t)((size_t)f * r * 2));
+    const __amdgpu_buffer_rsrc_t rz = buf_rsrc(z, (uint32_t)B * (uint32_t)r * 4u);
+    const uint32_t prow = nrow < f ? (uint32_t)nrow * (uint32_t)r * 2u : kOOB;
+    const uint32_t zrow = n16 < B ? (uint32_t)n16 * (uint32_t)r * 4u : kOOB;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < r; k0 += 32 * KC) {
+        uint4 w[KC];
+        float4 za[KC], zb[KC];
+#pragma unroll
+        for (int j = 0; j < KC; ++j) {
+            const int col = k0 + 32 * j + 8 * g;
+            const bool ok = col < r;                                   // r % 8 == 0
+            w[j] = bld16(rp, ok ? prow + (uint32_t)col * 2u : kOOB);
+            za[j] = __builtin_bit_cast(float4, bld16(rz, ok ? zrow + (uint32_t)col * 4u : kOOB));
+            zb[j] = __builtin_bit_cast(float4, bld16(rz, ok ? zrow + (uint32_t)col * 4u + 16u : kOOB));
+        }
+#pragma unroll
+        for (int j = 0; j < KC; ++j) {
+            uint4 hi, lo;
+            split8(za[j], zb[j], hi, lo);
+            acc = mfma32(hi, w[j], acc);
+            acc = mfma32(lo, w[j], acc);
+        }
+    }
+    // D[m = 4g + v][n = n16]: logits of tokens 4g .. 4g+3 for this lane's neuron
+    const float cn = nrow < f ? half_to_float(c[nrow]) : 0.f;
+    const float lv[4] = {acc.x + cn, acc.y + cn, acc.z + cn, acc.w + cn};
+    bool fired = false;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int b = 4 * g + v;
+        if (b < B) {
+            fired |= lv[v] > 0.f;
+            if (logits != nullptr && nrow < f) logits[(size_t)b * f + nrow] = lv[v];
+        }
+    }
+    const uint64_t bal = __ballot(fired);
+    const uint32_t m16 = (uint32_t)((bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xFFFFu);
+    const bool mine = g == 0 && nrow < f;
+    if (mine) mask[nrow] = (uint8_t)((m16 >> n16) & 1u);
+    if (bits != nullptr) {
+        bool resident = false;
+        if (mine) {
+            const int sl = slot_of != nullptr ? slot_of[nrow] : 0;
+            resident = sl >= 0 && sl < n_slots;
+        }
+        const uint32_t res16 = (uint32_t)(__ballot(resident) & 0xFFFFu);
+        if (lane == 0) s_half[wave] = m16 & res16;
+        __syncthreads();
+        if (threadIdx.x < 2) {
+            const int w2 = 2 * threadIdx.x;
+            const int word = blockIdx.x * 2 + threadIdx.x;
+            if (word * 32 < f) bits[word] = s_half[w2] | (s_half[w2 + 1] << 16);
+        }
+    }
+}
+
 // y over (slab, neuron chunk) tiles; a slab is 16 lanes x CPL columns (fp16: 8 columns, one 16-byte
 // load per row; Q4_0: 16 columns, 8 code bytes and a scale per row, so 16 lanes read a whole 128-byte
 // line of a row's codes).  The chunk's 16-position steps are split into eight contiguous runs, one

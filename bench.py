@@ -10,9 +10,9 @@ events on that stream after a device synchronization, and the median is reported
 
 The headline (`value`) is the largest stack that fits one GPU at batch 1: 96 layers of
 d_model 12288 / d_ffn 49152 with Q4_0 FFN rows (OPT-175B-shaped).  The same run measures every
-other workload (the 7B-, 30B- and 40B-shaped stacks, the batch-4 and batch-8 variants and the
-single small layer) into `detail.workloads`, each with its tokens/s, microseconds per layer and
-the HBM fraction of its kernels.
+other workload (the 7B-, 30B- and 40B-shaped stacks, the batch-4 and batch-8 variants, 16-token
+steps of the 175B- and 7B-shaped stacks, and the single small layer) into `detail.workloads`, each
+with its tokens/s, microseconds per layer and the HBM fraction of its kernels.
 
 Printed: one JSON line.  `roofline` is the sparse-FFN kernel of the headline workload (the
 kernel that reads the active rows) on its algorithmic bytes, timed with HIP events on its launch
@@ -39,7 +39,7 @@ import numpy as np  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 HEADLINE = (5, 1)              # (stack id, batch): OPT-175B-shaped Q4_0 stack at batch 1
-DETAIL = ((5, 8), (2, 1), (3, 1), (3, 4), (4, 1), (1, 1))
+DETAIL = ((5, 8), (5, 16), (2, 1), (2, 16), (3, 1), (3, 4), (4, 1), (1, 1))
 REPS = 5                       # replays of each timed graph; the median is reported
 COPY_PROBE_MIB = 256
 CU_NUM = 256                   # MI355X compute units (the counter formulas divide by it)

@@ -38,7 +38,7 @@
  *  - Q4_0 rows (32-weight blocks, one fp16 scale per block) of d weights are d/2 code bytes
  *    (byte j: weight 2j in the low nibble, weight 2j+1 in the high nibble; weight value
  *    scale*(code-8)) followed by d/32 fp16 scales: 9d/16 bytes per row.
- *  - Alignment: p1, p2, x, w_in, w_down_t must be 16-byte aligned.  Shapes: 1 <= batch <= 8,
+ *  - Alignment: p1, p2, x, w_in, w_down_t must be 16-byte aligned.  Shapes: 1 <= batch <= 16,
  *    d_model % 8 == 0 (fp16) or d_model % 256 == 0 (Q4_0), d_model <= 2^24, rank % 8 == 0 and
  *    rank <= 2048, 1 <= d_ffn <= 2^26, 0 <= n_slots <= d_ffn.
  */
@@ -68,7 +68,7 @@ typedef enum { PI_F16 = 1, PI_Q4_0 = 2 } pi_wtype;
  * squared ReLU). */
 typedef enum { PI_ACT_RELU = 0, PI_ACT_SQUARED_RELU = 1 } pi_act;
 
-#define PI_MAX_BATCH 8
+#define PI_MAX_BATCH 16
 #define PI_MAX_WIDE_BATCH 16      /* pi_sparse_ffn_wide */
 #define PI_MAX_RANK 2048
 #define PI_MAX_D_MODEL (1 << 24)  /* kernels address one token vector or row with 32-bit offsets */

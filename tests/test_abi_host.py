@@ -53,7 +53,7 @@ def test_workspace_sizes(L):
     both, only_p, only_f = ws_for(L, p, f, 1), ws_for(L, p, None, 1), ws_for(L, None, f, 1)
     assert only_p > 0 and only_f > 0 and both >= only_p + only_f
     assert ws_for(L, p, f, 8) > both
-    assert ws_for(L, p, f, 0) == 0 and ws_for(L, p, f, 9) == 0 and ws_for(L, None, None, 1) == 0
+    assert ws_for(L, p, f, 0) == 0 and ws_for(L, p, f, 17) == 0 and ws_for(L, None, None, 1) == 0
     assert ws_for(L, pred(d=512), f, 1) == 0                      # d_model mismatch
 
 
@@ -66,7 +66,7 @@ def test_predict_rejects(L):
     assert call(ctypes.byref(p), x=0) == _abi.PI_ERR_NULL
     assert call(ctypes.byref(p), mask=0) == _abi.PI_ERR_NULL
     assert call(ctypes.byref(p), B=0) == _abi.PI_ERR_BATCH
-    assert call(ctypes.byref(p), B=9) == _abi.PI_ERR_BATCH
+    assert call(ctypes.byref(p), B=17) == _abi.PI_ERR_BATCH
     assert call(ctypes.byref(pred(r=100))) == _abi.PI_ERR_SHAPE       # rank % 8
     assert call(ctypes.byref(pred(r=4096))) == _abi.PI_ERR_SHAPE      # rank > 2048
     assert call(ctypes.byref(pred(d=1020))) == _abi.PI_ERR_SHAPE
@@ -87,7 +87,7 @@ def test_sparse_ffn_noalloc_rejects(L):
     for kw in (dict(x=0), dict(idx=0), dict(cnt=0), dict(y=0)):
         assert call(ctypes.byref(f), **kw) == _abi.PI_ERR_NULL
     assert call(ctypes.byref(f), x=U) == _abi.PI_ERR_ALIGN
-    assert call(ctypes.byref(f), B=0) == _abi.PI_ERR_BATCH and call(ctypes.byref(f), B=9) == _abi.PI_ERR_BATCH
+    assert call(ctypes.byref(f), B=0) == _abi.PI_ERR_BATCH and call(ctypes.byref(f), B=17) == _abi.PI_ERR_BATCH
     assert call(ctypes.byref(ffn(wtype=3))) == _abi.PI_ERR_DTYPE
     big = ffn(d=16384, f=1 << 20)
     assert ws_for(L, None, big, 1) > _abi.PI_NOALLOC_SCRATCH_BYTES
@@ -120,7 +120,7 @@ def test_sparse_ffn_rejects(L):
     assert call(ctypes.byref(ffn(n_slots=100))) == _abi.PI_ERR_SHAPE                  # slot_of NULL: n_slots == f
     assert call(ctypes.byref(ffn(n_slots=5000, slot_of=A))) == _abi.PI_ERR_SHAPE      # n_slots > f
     assert call(ctypes.byref(ffn(w_dn=U))) == _abi.PI_ERR_ALIGN
-    assert call(ctypes.byref(f), B=9) == _abi.PI_ERR_BATCH
+    assert call(ctypes.byref(f), B=17) == _abi.PI_ERR_BATCH
     assert call(ctypes.byref(f), n=big - 1) == _abi.PI_ERR_WORKSPACE
 
 
@@ -171,7 +171,7 @@ def test_two_step_layer_rejects(L):
     assert hid(ctypes.byref(p), z=0) == _abi.PI_ERR_NULL
     assert hid(ctypes.byref(p), x=U) == _abi.PI_ERR_ALIGN
     assert hid(ctypes.byref(p), z=U) == _abi.PI_ERR_ALIGN
-    assert hid(ctypes.byref(p), B=9) == _abi.PI_ERR_BATCH
+    assert hid(ctypes.byref(p), B=17) == _abi.PI_ERR_BATCH
     rest = lambda pp, ff, B=2, z=A, n=big: L.pi_ffn_layer_from_hidden(pp, ff, A, B, z, A, None, None, None, A, n, None)
     assert rest(ctypes.byref(p), ctypes.byref(f), z=0) == _abi.PI_ERR_NULL
     assert rest(ctypes.byref(p), ctypes.byref(f), z=U) == _abi.PI_ERR_ALIGN
@@ -189,6 +189,9 @@ def test_layer_path(L):
     assert path(pred(d=8192, f=32768, r=1024), ffn(d=8192, f=32768), 4) == 2
     assert path(pred(d=12288, f=49152, r=1024), ffn(d=12288, f=49152), 1) == 2
     assert path(pred(d=12288, f=12288, r=1024), ffn(d=12288, f=12288), 8) == 2
+    # past 8 tokens the layer always runs separate kernels (MFMA second predictor matrix and FFN)
+    assert path(pred(d=1024, f=4096, r=128), ffn(d=1024, f=4096), 9) == 2
+    assert path(pred(d=1024, f=4096, r=128), ffn(d=1024, f=4096), 16) == 2
     # invalid
     assert path(pred(), ffn(), 0) == 0
     assert path(pred(d=512), ffn(), 1) == 0
@@ -213,5 +216,7 @@ def test_h_offset(L):
     for gated_or_q4 in (ffn(d=1024, f=4096, gated=1), ffn(d=1024, f=4096, wtype=_abi.PI_Q4_0)):
         L.pi_sparse_ffn_h_offset(ctypes.byref(gated_or_q4), 3, ctypes.byref(kind))
         assert kind.value == 3                                # gated / Q4_0: MFMA kernels from batch 3
-    assert L.pi_sparse_ffn_h_offset(ctypes.byref(small), 9, ctypes.byref(kind)) == 2**64 - 1
+    L.pi_sparse_ffn_h_offset(ctypes.byref(small), 16, ctypes.byref(kind))
+    assert kind.value == 3                                    # 9..16 tokens: the MFMA kernels
+    assert L.pi_sparse_ffn_h_offset(ctypes.byref(small), 17, ctypes.byref(kind)) == 2**64 - 1
     assert L.pi_sparse_ffn_h_offset(ctypes.byref(small), 1, None) == 2**64 - 1

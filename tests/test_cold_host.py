@@ -55,6 +55,7 @@ def _check(y, y_ref, wtype):
 CASES = [  # d, f, gated, wtype, B, predicted share, hot share
     (1024, 4096, False, F16, 1, 0.10, 0.26), (512, 1500, True, F16, 1, 0.2, 0.3), (768, 999, False, F16, 4, 0.3, 0.5),
     (1024, 2048, False, Q4, 1, 0.1, 0.26), (512, 700, False, Q4, 8, 0.2, 0.0), (256, 300, True, F16, 3, 1.0, 0.5),
+    (512, 800, False, F16, 16, 0.15, 0.3), (256, 600, False, Q4, 12, 0.2, 0.2),     # up to 16 tokens
 ]
 
 
@@ -154,7 +155,7 @@ def test_cold_rejects():
     assert call(f=None) == _abi.PI_ERR_NULL
     assert call(xp=None) == _abi.PI_ERR_NULL
     assert call(mp=None) == _abi.PI_ERR_NULL
-    assert call(B=0) == _abi.PI_ERR_BATCH and call(B=9) == _abi.PI_ERR_BATCH
+    assert call(B=0) == _abi.PI_ERR_BATCH and call(B=17) == _abi.PI_ERR_BATCH
     assert call(n=need - 1) == _abi.PI_ERR_WORKSPACE
     assert call(t=-1) == _abi.PI_ERR_SHAPE
     bad = _abi.pi_ffn(512, 600, 0, F16, 600, None, w_in.ctypes.data, w_dn.ctypes.data, None, b_up.ctypes.data)

@@ -35,6 +35,9 @@ def _gpu():
 PRED_CASES = [  # (d, f, r, B) -- ragged f, tiny and maximal rank, every batch width class
     (256, 1000, 8, 1), (1024, 4096, 128, 1), (512, 4099, 520, 3), (4096, 11008, 1024, 1),
     (1024, 2500, 2048, 2), (12288, 3001, 1024, 8), (8192, 777, 1024, 5),
+    # past 8 tokens: the first matrix in two passes, the second on MFMA (z as an fp16 pair)
+    (1024, 4096, 128, 9), (4096, 11008, 1024, 16), (512, 4099, 520, 13), (1024, 2500, 2048, 16),
+    (12288, 3001, 1024, 12), (256, 1000, 8, 16),
 ]
 
 
@@ -199,7 +202,7 @@ LAYER_CASES = [  # small layers spanning several tiles, ragged f, placement, all
 @pytest.mark.parametrize("case", LAYER_CASES, ids=["relu", "reglu", "placement", "q4_0", "squared_relu",
                                                   "squared_relu_q4_0_large_f", "placement_large_f",
                                                   "reglu_large_f"])
-@pytest.mark.parametrize("B", [1, 4, 8])
+@pytest.mark.parametrize("B", [1, 4, 8, 12, 16])
 def test_ffn_layer(case, B):
     announce(f"ffn_layer {case} B={B}")
     cfg = synth.custom_config(**case, seed=B * 100 + case["d"])
