@@ -38,6 +38,7 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+HOST_BW_GBS = 100.0            # host DRAM read bandwidth assumed by the placement policy
 HEADLINE = (5, 1)              # (stack id, batch): OPT-175B-shaped Q4_0 stack at batch 1
 DETAIL = ((5, 8), (5, 16), (2, 1), (2, 16), (3, 1), (3, 4), (4, 1), (1, 1))
 REPS = 5                       # replays of each timed graph; the median is reported
@@ -157,7 +158,7 @@ def ffn_kernel_names(h_kind: int, B: int, cfg, synth):
 
 # ---------------------------------------------------------------------------------- one workload
 
-def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=False, cold=False):
+def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=False, hots=None):
     """Time K decode steps of `layers` at batch B (median of REPS graph replays) and the per-kernel
     legs; returns the workload's record (plus private fields starting with '_')."""
     L = len(layers)
@@ -314,9 +315,9 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
         "_ffn": (float(ffn_touched.mean()), leg_us["sparse_ffn"], ffn_label, N),
         "_rest": (float(rest_bytes.mean()), leg_us["rest"], rest_label, N),
     }
-    if cold and layers[0].slot_of is not None:
-        rec["cold_host"] = cold_leg(torch, synth, _abi, cfg, layers, B, x_all, xd, masks, cases, ws, stream, dev,
-                                    ms_per_step)
+    if hots is not None:
+        rec["cold_host"] = cold_leg(torch, synth, _abi, cfg, layers, hots, B, x_all, xd, masks, cases, ws, stream,
+                                    dev, ms_per_step)
     if wide and B == 1 and R >= 16 and layers[0].slot_of is None:
         rec["wide_b16"] = wide_leg(torch, _abi, cfg, layers, xd, masks, cases, stream, dev, in_rows, rb)
     del xd, z_all, masks, idx_all, ws_f, ws
@@ -327,10 +328,34 @@ def describe(cfg, L, B, synth):
     return (f"{cfg.name}: {L} layers, d_model={cfg.d}, d_ffn={cfg.f}, predictor rank {cfg.r}, "
             f"{'ReGLU' if cfg.gated else 'ReLU'}, {'fp16' if cfg.wtype == synth.F16 else 'Q4_0'} weights, "
             f"batch {B}, Zipf firing at {cfg.density:.0%} target density"
-            + (f", hottest {cfg.hot_frac:.0%} resident" if cfg.hot_frac else ""))
+            + (f", resident set placed by pi_place under a {cfg.hot_frac:.0%} budget" if cfg.hot_frac else ""))
 
 
-def cold_leg(torch, synth, _abi, cfg, layers, B, x_all, xd, masks, cases, ws, stream, dev, ms_per_step):
+def place_stack(synth, _abi, cfg, L):
+    """Resident neurons of every layer, chosen by pi_place (offline policy over the firing
+    frequencies, the per-neuron bytes and the two memories' bandwidths) under a device budget of
+    cfg.hot_frac of the stack's FFN bytes.  Returns (ascending resident ids per layer, summary), or
+    (None, None) for a stack that is wholly resident."""
+    if cfg.hot_frac is None:
+        return None, None
+    nb = (3 if cfg.gated else 2) * cfg.row_bytes()
+    freqs = [synth.layer_freq(cfg, l) for l in range(L)]
+    budget = int(round(cfg.hot_frac * L * cfg.f * nb))
+    slot_ofs, n_placed, t_exp = _abi.pi_place([cfg.f] * L, [nb] * L, freqs, budget, PEAK_HBM_GBS * 1e9,
+                                              HOST_BW_GBS * 1e9)
+    hots = [np.flatnonzero(so >= 0).astype(np.int32) for so in slot_ofs]
+    share = n_placed / cfg.f
+    expected_rows = sum(float(fr[h].sum()) for fr, h in zip(freqs, hots))
+    all_rows = sum(float(fr.sum()) for fr in freqs)
+    return hots, {"policy": "pi_place", "budget_share": cfg.hot_frac, "budget_gb": round(budget / 1e9, 3),
+                  "resident_share": round(float(n_placed.sum()) / (L * cfg.f), 4),
+                  "resident_share_min": round(float(share.min()), 4), "resident_share_max": round(float(share.max()), 4),
+                  "expected_covered_share": round(expected_rows / all_rows, 4),
+                  "bandwidths_gbs": {"gpu": PEAK_HBM_GBS, "host": HOST_BW_GBS},
+                  "expected_us_per_token": round(t_exp * 1e6, 2)}
+
+
+def cold_leg(torch, synth, _abi, cfg, layers, hots, B, x_all, xd, masks, cases, ws, stream, dev, ms_per_step):
     """Host half of the hybrid split: the predicted neurons that are not resident, computed by
     pi_cold_ffn_host on the masks the device produced (first two layers), and the hybrid layer end
     to end (device layer -> mask to pinned host memory -> host half -> host y added on the device)."""
@@ -340,8 +365,7 @@ def cold_leg(torch, synth, _abi, cfg, layers, B, x_all, xd, masks, cases, ws, st
     masks_h = masks.cpu().numpy()
     hosts = []
     for l in range(n_lay):
-        _, _, _, freq = synth.make_predictor(cfg, l)
-        cold_ids = np.setdiff1d(np.arange(cfg.f, dtype=np.int32), synth.hot_set(freq, cfg.n_hot()))
+        cold_ids = np.setdiff1d(np.arange(cfg.f, dtype=np.int32), hots[l])
         w_in_c, w_dn_c, b_up_c, _ = synth.make_ffn(cfg, l, cold_ids)
         slot_c = np.full(cfg.f, -1, np.int32)
         slot_c[cold_ids] = np.arange(cold_ids.size, dtype=np.int32)
@@ -602,9 +626,10 @@ def main():
         cfg = synth.CONFIGS[cid]
         L = cfg.layers if args.layers <= 0 else min(args.layers, cfg.layers)
         t0 = time.time()
+        hots, placement = place_stack(synth, _abi, cfg, L)
         layers = []
         for l in range(L):
-            host = synth.make_layer(cfg, l)
+            host = synth.make_layer(cfg, l, hot=None if hots is None else hots[l])
             layers.append(DeviceLayer.from_host(host, device=dev))
             del host
         torch.cuda.synchronize()
@@ -618,7 +643,9 @@ def main():
             else:
                 W, K = 4, max(1, min(args.detail_steps, cfg.tokens - 4))
             rec = measure(torch, synth, _abi, cfg, layers, B, W, K, args.roofline_steps, dev, stream,
-                          wide=(cid in (2, 5)), cold=(cid == 4))
+                          wide=(cid in (2, 5)), hots=hots)
+            if placement is not None:
+                rec["placement"] = placement
             results[(wcid, B)] = rec
             log(f"{rec['workload']}: {rec['tokens_per_s']} tokens/s, {rec['us_per_layer']} us/layer, sparse FFN "
                 f"{rec['kernels']['sparse_ffn']['us']} us ({rec['kernels']['sparse_ffn']['frac']} of HBM peak)")

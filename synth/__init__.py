@@ -235,11 +235,24 @@ def make_ffn(cfg: Config, layer: int, rows: np.ndarray | None, bias_scale: float
     return w_in, w_down_t, b_up, bd
 
 
-def make_layer(cfg: Config, layer: int, bias_scale: float | None = None, b_down: bool = False) -> Layer:
+def layer_freq(cfg: Config, layer: int) -> np.ndarray:
+    """The layer's generated firing frequencies p_i (the law its predictor offsets are calibrated to)."""
+    s, A = zipf_solve(cfg.f, cfg.density)
+    freq, _ = zipf_freq(cfg.seed, layer, cfg.f, s, A)
+    return freq
+
+
+def make_layer(cfg: Config, layer: int, bias_scale: float | None = None, b_down: bool = False,
+               hot: np.ndarray | None = None) -> Layer:
+    """One layer's predictor and FFN rows.  With a placement (cfg.hot_frac, or an explicit ascending
+    `hot` list of resident neuron ids), only the resident neurons' rows are generated, in ascending
+    id order, and slot_of maps ids to them."""
     p1, p2, c, freq = make_predictor(cfg, layer)
-    hot = slot_of = None
-    if cfg.hot_frac is not None:
+    slot_of = None
+    if hot is None and cfg.hot_frac is not None:
         hot = hot_set(freq, cfg.n_hot())
+    if hot is not None:
+        hot = np.ascontiguousarray(hot, dtype=np.int32)
         slot_of = np.full(cfg.f, -1, dtype=np.int32)
         slot_of[hot] = np.arange(hot.size, dtype=np.int32)
     w_in, w_down_t, b_up, bd = make_ffn(cfg, layer, hot, bias_scale, b_down)
