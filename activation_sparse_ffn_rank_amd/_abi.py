@@ -25,7 +25,8 @@ PI_MAX_WIDE_BATCH = 16
 EXPORTS = ("pi_workspace_bytes", "pi_predict", "pi_compact", "pi_sparse_ffn", "pi_sparse_ffn_wide_workspace_bytes", "pi_sparse_ffn_wide",
            "pi_ffn_layer",
            "pi_predict_hidden", "pi_ffn_layer_from_hidden", "pi_layer_path", "pi_sparse_ffn_h_offset",
-           "pi_cold_workspace_bytes", "pi_cold_ffn_host", "pi_place", "pi_sparse_ffn_noalloc", "pi_status_string",
+           "pi_cold_workspace_bytes", "pi_cold_ffn_host", "pi_place", "pi_predictor_ranks", "pi_sparse_ffn_noalloc",
+           "pi_status_string",
            "pi_version")
 PI_NOALLOC_SCRATCH_BYTES = 32 << 20
 
@@ -88,6 +89,8 @@ def lib() -> ctypes.CDLL:
         L.pi_place.restype = ctypes.c_int
         L.pi_place.argtypes = [i32, vp, vp, vp, ctypes.c_int64, ctypes.c_double, ctypes.c_double, vp, vp,
                                P(ctypes.c_double)]
+        L.pi_predictor_ranks.restype = ctypes.c_int
+        L.pi_predictor_ranks.argtypes = [i32, vp, vp, vp, ctypes.c_int64, i32, i32, i32, vp, vp]
         L.pi_sparse_ffn_noalloc.restype = ctypes.c_int
         L.pi_sparse_ffn_noalloc.argtypes = [P(pi_ffn), vp, i32, vp, vp, vp, vp]
         L.pi_status_string.restype = ctypes.c_char_p
@@ -297,6 +300,22 @@ def pi_place(d_ffn, neuron_bytes, freq, budget_bytes: int, gpu_bytes_per_s: floa
                                       float(gpu_bytes_per_s), float(host_bytes_per_s), so.ctypes.data,
                                       npl.ctypes.data, ctypes.byref(t)))
     return np.split(so, np.cumsum(d)[:-1]), npl, float(t.value)
+
+
+def pi_predictor_ranks(d_model, d_ffn, freq, budget_bytes: int, r_min: int, r_max: int, r_step: int):
+    """Per-layer predictor ranks under a budget for the predictor matrices (host): returns (rank
+    array, rounded firing entropy in bits per layer).  d_model, d_ffn: per layer; freq: per-layer
+    float arrays."""
+    import numpy as np
+    dm = np.ascontiguousarray(d_model, dtype=np.int32)
+    df = np.ascontiguousarray(d_ffn, dtype=np.int32)
+    fr = np.ascontiguousarray(np.concatenate([np.asarray(p, np.float32) for p in freq]), dtype=np.float32)
+    rank = np.empty(df.size, np.int32)
+    ent = np.empty(df.size, np.float64)
+    _check("pi_predictor_ranks", lib().pi_predictor_ranks(df.size, dm.ctypes.data, df.ctypes.data, fr.ctypes.data,
+                                                          int(budget_bytes), r_min, r_max, r_step, rank.ctypes.data,
+                                                          ent.ctypes.data))
+    return rank, ent
 
 
 def pi_status_string(code: int) -> str:

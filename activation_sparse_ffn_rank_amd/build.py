@@ -16,7 +16,8 @@ LIB = os.path.join(PKG, "libpi.so")
 CSRC = os.path.join(PKG, "csrc")
 SOURCES = [os.path.join(CSRC, "pi_abi.hip"), os.path.join(CSRC, "pi_persist_b.hip"), os.path.join(CSRC, "pi_split.hip")]
 HOST_SOURCES = [os.path.join(CSRC, "pi_cold.cpp"),   # host half of the hybrid split (g++, OpenMP)
-                os.path.join(CSRC, "pi_place.cpp")]  # offline placement under a memory budget
+                os.path.join(CSRC, "pi_place.cpp"),  # offline placement under a memory budget
+                os.path.join(CSRC, "pi_ranks.cpp")]  # per-layer predictor rank under a memory budget
 DEPENDS = SOURCES + HOST_SOURCES + [os.path.join(CSRC, n) for n in ("pi_kernels.hpp", "pi_sync.hpp", "pi_occupancy.hpp", "pi_tail.hpp", "pi_split.hpp", "pi_wide.hpp")] + [
                      os.path.join(ROOT, "include", "pi_sparse_ffn.h")]
 OBJDIR = os.path.join(ROOT, "_build")

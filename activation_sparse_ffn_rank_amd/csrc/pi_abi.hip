@@ -498,9 +498,12 @@ int enqueue_sparse(const pi_ffn *fn, const void *x, int B, const int32_t *idx, c
     return enqueue_sparse_legacy(fn, x, B, idx, counts, y, ffn_scratch(fn, B, w + ctl_bytes(fn->d_model)), st);
 }
 
-// Layout of a pi_ffn_layer workspace: the shared control block, z [B][r] fp32, the union mask [f]
-// u8, idx [f] and counts [2] int32, the listed-bit words [ceil(f/32)], the sparse-FFN scratch
-// (ffn_ws), the tail kernel's scratch (tail_ws).
+// Layout of a pi_ffn_layer workspace: the shared control block, the sparse-FFN scratch (ffn_ws),
+// the tail kernel's scratch (tail_ws), the union mask [f] u8, idx [f] and counts [2] int32, the
+// listed-bit words [ceil(f/32)], z [B][r] fp32.  Everything that carries state from one call to
+// the next (the epoch, stamped words, slab tickets) sits at offsets that depend on the FFN
+// descriptor and the batch only; z, the one rank-dependent part, comes last, so layers whose
+// predictors differ in rank can share one workspace sized for the largest rank.
 struct LayerWs {
     int32_t *ctl;
     float *z;
@@ -517,13 +520,13 @@ LayerWs layer_ws(const pi_predictor *p, const pi_ffn *fn, int B, void *ws) {
     LayerWs L;
     char *q = static_cast<char *>(ws);
     L.ctl = reinterpret_cast<int32_t *>(q); q += ctl_bytes(p->d_model);
-    L.z = reinterpret_cast<float *>(q); q += pred_ws(p, B);
+    L.ffn = q; q += ffn_ws(fn, B);
+    L.tail = q; q += tail_ws(fn, B);
     L.mask = reinterpret_cast<uint8_t *>(q); q += align_up((size_t)p->d_ffn);
     L.idx = reinterpret_cast<int32_t *>(q); q += align_up((size_t)p->d_ffn * 4);
     L.counts = reinterpret_cast<int32_t *>(q); q += align_up(2 * sizeof(int32_t));
     L.bits = reinterpret_cast<uint32_t *>(q); q += align_up((size_t)mask_words(p->d_ffn) * 4);
-    L.ffn = q; q += ffn_ws(fn, B);
-    L.tail = q;
+    L.z = reinterpret_cast<float *>(q);
     return L;
 }
 

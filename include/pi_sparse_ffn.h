@@ -166,7 +166,11 @@ int pi_sparse_ffn_wide(const pi_ffn *ffn, const void *x, int32_t batch, const in
  *    cross-workgroup wait ran out its time limit (20 ms) and the outputs of that call are invalid.
  * Every wait inside the kernel is bounded.  Zero-filling the workspace once is always safe.  At the
  * batches where the sparse FFN runs on the MFMA form, an |h| of 65504 or more ORs 64 into the same
- * status word (see pi_sparse_ffn). */
+ * status word (see pi_sparse_ffn).
+ * One workspace may serve several layers, one call at a time, when their pi_ffn descriptors agree
+ * in d_model, d_ffn, n_slots, gated, wtype and act and the batch is the same: their predictors may
+ * differ in rank (size it by the largest rank; what carries state between calls does not move with
+ * the rank).  A layer of another FFN shape needs a workspace of its own, or a zero fill first. */
 int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch,
                  float *y, uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws,
                  size_t ws_bytes, void *stream);
@@ -237,6 +241,25 @@ int pi_cold_ffn_host(const pi_ffn *ffn, const void *x, int32_t batch, const uint
 int pi_place(int32_t n_layers, const int32_t *d_ffn, const int64_t *neuron_bytes, const float *freq,
              int64_t budget_bytes, double gpu_bytes_per_s, double host_bytes_per_s, int32_t *slot_of,
              int32_t *n_placed, double *expected_s);
+
+/* ---- adaptive predictor size (methodology and core innovations: adaptive predictors per layer,
+ * kept small in GPU memory) ----
+ *
+ * pi_predictor_ranks chooses the rank of each of n_layers layers' predictors (d_model[l],
+ * d_ffn[l]; freq: the firing frequencies, concatenated per layer, each in [0, 1]) under a budget
+ * for all predictor matrices, sum_l 2 rank[l] (d_model[l] + d_ffn[l]) <= budget_bytes (P1 and P2
+ * in fp16).  A layer's share follows the entropy of its firing pattern, H_l = sum_i h(p_i) bits
+ * (h the binary entropy, H_l rounded to 1/1024 bit): rank[l] is the largest of r_min, r_min +
+ * r_step, ..., r_max not above max(r_min, lambda H_l), for the largest lambda the budget allows;
+ * at equal lambda the lower layer is raised first, and raising stops at the first raise that
+ * does not fit.  Sparser and more skewed layers (lower H) get smaller predictors; a layer with
+ * H = 0 keeps r_min.  r_min, r_step: multiples of 8, r_min >= 8, r_max <= PI_MAX_RANK, r_max -
+ * r_min a multiple of r_step.  Outputs rank [n_layers] and, if non-NULL, entropy_bits [n_layers]
+ * (the rounded H_l).  PI_ERR_SHAPE if the budget cannot hold r_min in every layer or an argument
+ * is out of range (nothing written).  Host memory, synchronous; returns a pi_status. */
+int pi_predictor_ranks(int32_t n_layers, const int32_t *d_model, const int32_t *d_ffn, const float *freq,
+                       int64_t budget_bytes, int32_t r_min, int32_t r_max, int32_t r_step, int32_t *rank,
+                       double *entropy_bits);
 
 /* ---- the same sparse FFN without a caller workspace ----
  *

@@ -248,3 +248,68 @@ def place_exact_prefix(neuron_bytes, freq, budget, bw_gpu, bw_host):
         if best is None or t < best:
             best = t
     return best
+
+
+# ------------------------------------------------------------------ adaptive predictor size
+# The pages name adaptive predictors, sized per layer so that they take little GPU memory, without
+# a formula.  The reading checked here: a layer's rank follows the entropy of its firing pattern
+# (independent neurons: H = sum_i h(p_i) bits, h the binary entropy, rounded to 1/1024 bit); rank
+# r_l(lambda) = the largest grid rank (r_min + k step, <= r_max) not above max(r_min, lambda H_l),
+# for the largest lambda at which sum_l 2 r_l (d_l + f_l) fits the budget; at that budget's edge,
+# the raises that share the next lambda are taken in layer order while they fit.
+
+def binary_entropy_bits(p) -> float:
+    """sum_i h(p_i) in bits, h(p) = -p log2 p - (1-p) log2 (1-p), h(0) = h(1) = 0 (exact sum)."""
+    import math
+    terms = []
+    for v in np.asarray(p, np.float64).ravel():
+        if 0.0 < v < 1.0:
+            terms.append(-(v * math.log2(v) + (1.0 - v) * math.log2(1.0 - v)))
+    return math.fsum(terms)
+
+
+def predictor_ranks(d_model, d_ffn, freq, budget, r_min, r_max, step):
+    """Ranks by the definition above, in exact rational arithmetic: evaluate r(lambda) at every
+    lambda where some layer's rank changes, keep the largest that fits, then take the next
+    lambda's raises in layer order while they fit.  Returns (ranks, rounded entropies)."""
+    from fractions import Fraction
+    L = len(d_ffn)
+    H = [round(binary_entropy_bits(p) * 1024) / 1024 for p in freq]
+    per_rank = [2 * (int(d) + int(f)) for d, f in zip(d_model, d_ffn)]
+    if sum(r_min * c for c in per_rank) > budget:
+        raise ValueError("budget below r_min in every layer")
+
+    def ranks_at(lam):
+        out = []
+        for h in H:
+            r = r_min
+            if h > 0:
+                t = lam * Fraction(h)                 # the rank lambda H_l asks for
+                while r + step <= r_max and r + step <= t:
+                    r += step
+            out.append(r)
+        return out
+
+    def cost(rs):
+        return sum(r * c for r, c in zip(rs, per_rank))
+
+    lams = sorted({Fraction(r) / Fraction(h) for h in H if h > 0 for r in range(r_min + step, r_max + 1, step)})
+    ranks = [r_min] * L
+    nxt = None
+    for lam in lams:
+        rs = ranks_at(lam)
+        if cost(rs) <= budget:
+            ranks = rs
+        else:
+            nxt = lam
+            break
+    if nxt is not None:
+        target = ranks_at(nxt)
+        for l in range(L):
+            if target[l] > ranks[l]:
+                trial = list(ranks)
+                trial[l] = target[l]
+                if cost(trial) > budget:
+                    break
+                ranks = trial
+    return ranks, H
