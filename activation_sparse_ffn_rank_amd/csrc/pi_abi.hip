@@ -167,9 +167,9 @@ bool layer_pred_up(const pi_predictor *p, const pi_ffn *fn, int B) {
 // The tail kernel (second predictor matrix + mask + sparse FFN) keeps x [B][d] fp16 and z [B][r]
 // fp32 in dynamic LDS next to its static arrays (wave partials of the down tiles, the list of a
 // down tile's neurons, a few words); all of it must fit one workgroup.  It is used while every
-// 32-neuron tile can have an up workgroup of its own (d_ffn <= 32 * kTailMaxTiles), and at batch
-// <= 2 up to d_ffn = 32 * kTailMaxTilesB2 (up workgroups then take several tiles each; measured
-// faster than separate kernels there, slower at larger batch).
+// 32-neuron tile can have an up workgroup of its own (d_ffn <= 32 * kTailMaxTiles).  Larger layers
+// at batch <= 2 run k_pred_up and the split kernels instead (measured on MI355X: 9% faster than
+// this kernel at 28672 neurons, 14% at 32768; at 11008 this kernel is 11% faster).
 bool tail_persistent(const pi_predictor *p, const pi_ffn *fn, int B) {
     if (B > kGemvMaxBatch) return false;
     const size_t stat = (size_t)4 * B * kTailCPL * 64 * 4 + (size_t)B * kTailSlab * 4 + (size_t)kTailListMax * 4 + 512;
@@ -180,7 +180,7 @@ bool tail_persistent(const pi_predictor *p, const pi_ffn *fn, int B) {
     const int64_t part_bytes = (int64_t)kSparseMaxChunks * B * fn->d_model * 8;
     if (in_bytes >= (int64_t)kBufMax || p2_bytes >= (int64_t)kBufMax || part_bytes >= (int64_t)kBufMax) return false;
     const int tiles = ceil_div(fn->d_ffn, 32);
-    if (tiles > (B <= 2 ? kTailMaxTilesB2 : kTailMaxTiles)) return false;
+    if (tiles > kTailMaxTiles) return false;
     return (size_t)B * fn->d_model * 2 <= (size_t)kLdsXBytes &&
            tail_dyn_lds(B, fn->d_model, p->rank) + stat <= 160 * 1024;
 }
@@ -628,6 +628,43 @@ int pi_predict_hidden(const pi_predictor *pred, const void *x, int32_t batch, fl
 
 namespace {
 
+// The layer path of batches <= 2 on layers too large for the tail kernel: k_pred_up (logits, mask,
+// live flags, h of the listed neurons), then k_down_split on the live neurons and k_sum_split.
+int enqueue_pred_up(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int B, const float *z, float *y,
+                    uint8_t *mask, const LayerWs &L, hipStream_t st, uint64_t *trace = nullptr) {
+    const int f = pred->d_ffn;
+    const SplitGeom g = split_geom(ffn, B);
+    PredUpArgs p{};
+    p.d = pred->d_model; p.f = f; p.r = pred->rank; p.n_slots = ffn->n_slots; p.act = ffn->act;
+    p.row_bytes = row_bytes_of(ffn);
+    p.p2 = static_cast<const uint16_t *>(pred->p2); p.c = static_cast<const uint16_t *>(pred->c); p.z = z;
+    p.w_in = static_cast<const uint8_t *>(ffn->w_in); p.b_up = static_cast<const uint16_t *>(ffn->b_up);
+    p.slot_of = ffn->slot_of; p.x = static_cast<const uint16_t *>(x);
+    p.mask = mask; p.bits = L.bits;
+    char *w = L.ffn + ctl_bytes(ffn->d_model);
+    SplitArgs a{};
+    a.d = ffn->d_model; a.f = f; a.n_slots = ffn->n_slots; a.S = g.S; a.act = ffn->act;
+    a.nwords = mask_words(f);
+    a.row_bytes = row_bytes_of(ffn);
+    a.w_in = static_cast<const uint8_t *>(ffn->w_in); a.w_dn = static_cast<const uint8_t *>(ffn->w_down_t);
+    a.b_up = p.b_up; a.b_down = static_cast<const uint16_t *>(ffn->b_down);
+    a.slot_of = ffn->slot_of; a.x = p.x; a.y = y; a.bits = L.bits;
+    a.part = reinterpret_cast<float *>(w);
+    a.ypart = reinterpret_cast<float *>(w + g.part);
+    a.hout = nullptr;
+    p.h = reinterpret_cast<float *>(w + g.part + g.ypart);        // the hout region: [B][f]
+    a.hin = p.h;
+#ifdef PIK_TRACE
+    a.trace = trace;
+    p.trace = trace != nullptr ? trace + 8192 * 8 : nullptr;
+#else
+    (void)trace;
+#endif
+    const int wt = ffn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16;
+    const int NT = pred->rank <= 512 ? 1 : (pred->rank <= 1024 ? 2 : 4);
+    return launch_pred_up_split(p, a, B, wt, ffn->gated, NT, st) ? PI_ERR_HIP : PI_OK;
+}
+
 // The layer from z on (mask, placement restriction, sparse FFN) on a layer workspace.
 int layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, const float *z,
                       float *y, uint8_t *mask_out, int32_t *idx_out, int32_t *counts_out, void *ws, hipStream_t st) {
@@ -645,31 +682,8 @@ int layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const void *x
         return want_list ? enqueue_compact(mask, f, ffn->slot_of, idx, counts, st) : PI_OK;
     }
     if (layer_pred_up(pred, ffn, batch)) {
-        // logits, mask, listed flags and h of the listed neurons in one kernel, then the down rows
-        const SplitGeom g = split_geom(ffn, batch);
-        PredUpArgs p{};
-        p.d = pred->d_model; p.f = f; p.r = pred->rank; p.n_slots = ffn->n_slots; p.act = ffn->act;
-        p.row_bytes = row_bytes_of(ffn);
-        p.p2 = static_cast<const uint16_t *>(pred->p2); p.c = static_cast<const uint16_t *>(pred->c); p.z = z;
-        p.w_in = static_cast<const uint8_t *>(ffn->w_in); p.b_up = static_cast<const uint16_t *>(ffn->b_up);
-        p.slot_of = ffn->slot_of; p.x = static_cast<const uint16_t *>(x);
-        p.mask = mask; p.bits = L.bits;
-        char *w = L.ffn + ctl_bytes(ffn->d_model);
-        SplitArgs a{};
-        a.d = ffn->d_model; a.f = f; a.n_slots = ffn->n_slots; a.S = g.S; a.act = ffn->act;
-        a.nwords = mask_words(f);
-        a.row_bytes = row_bytes_of(ffn);
-        a.w_in = static_cast<const uint8_t *>(ffn->w_in); a.w_dn = static_cast<const uint8_t *>(ffn->w_down_t);
-        a.b_up = p.b_up; a.b_down = static_cast<const uint16_t *>(ffn->b_down);
-        a.slot_of = ffn->slot_of; a.x = p.x; a.y = y; a.bits = L.bits;
-        a.part = reinterpret_cast<float *>(w);
-        a.ypart = reinterpret_cast<float *>(w + g.part);
-        a.hout = nullptr;
-        p.h = reinterpret_cast<float *>(w + g.part + g.ypart);        // the hout region: [B][f]
-        a.hin = p.h;
-        const int wt = ffn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16;
-        const int NT = pred->rank <= 512 ? 1 : (pred->rank <= 1024 ? 2 : 4);
-        if (launch_pred_up_split(p, a, batch, wt, ffn->gated, NT, st)) return PI_ERR_HIP;
+        // logits, mask, live flags and h of the listed neurons in one kernel, then the down rows
+        if ((rc = enqueue_pred_up(pred, ffn, x, batch, z, y, mask, L, st))) return rc;
         return want_list ? enqueue_compact(mask, f, ffn->slot_of, idx, counts, st) : PI_OK;
     }
     if (layer_split(ffn, batch)) {
@@ -783,6 +797,16 @@ int pi_trace_tail(const pi_predictor *pred, const pi_ffn *ffn, const void *x, in
     int rc = enqueue_pred_l1(pred, x, batch, L.z, st);
     if (rc) return rc;
     return enqueue_tail(pred, ffn, x, batch, L.z, y, nullptr, L.ctl, L.tail, st, trace);
+}
+
+int pi_trace_layer_split(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, float *y,
+                         void *ws, uint64_t *trace, void *stream) {
+    if (tail_persistent(pred, ffn, batch) || !layer_pred_up(pred, ffn, batch)) return PI_ERR_SHAPE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const LayerWs L = layer_ws(pred, ffn, batch, ws);
+    int rc = enqueue_pred_l1(pred, x, batch, L.z, st);
+    if (rc) return rc;
+    return enqueue_pred_up(pred, ffn, x, batch, L.z, y, L.mask, L, st, trace);
 }
 
 int pi_trace_sparse(const pi_ffn *ffn, const void *x, int32_t batch, const int32_t *idx, const int32_t *counts,

@@ -41,15 +41,29 @@ int launch_one(SplitArgs &a, hipStream_t st) {
     return launch_down_sum<B, GATED, WT>(a, st);
 }
 
+// Grid of k_pred_up: as many workgroups as fit on the chip at once, evened out so that every
+// workgroup takes the same number of tiles (or one fewer).
+template <int B, bool GATED, int WT, int NT>
+int launch_pred_up(PredUpArgs &p, hipStream_t st) {
+    const void *kern = reinterpret_cast<const void *>(k_pred_up<B, GATED, WT, NT>);
+    const size_t lds = pred_up_lds(B, p.d, p.r);
+    int cus = 0, per_cu = 0;
+    if (resident_slots(kern, 256, lds, &cus, &per_cu)) return 1;
+    const int tiles = (p.f + 31) / 32, slots = cus * per_cu;
+    const int rounds = (tiles + slots - 1) / slots;
+    const int grid = (tiles + rounds - 1) / rounds;
+    hipLaunchKernelGGL((k_pred_up<B, GATED, WT, NT>), dim3(grid), dim3(256), lds, st, p);
+    return hipGetLastError() == hipSuccess ? 0 : 1;
+}
+
 template <int B, bool GATED, int WT>
 int launch_layer_one(PredUpArgs &p, SplitArgs &a, int NT, hipStream_t st) {
     if (choose_chunks<B, GATED, WT>(a)) return 1;
-    const dim3 grid((p.f + 31) / 32);
-    const size_t lds = pred_up_lds(B, p.d, p.r);
-    if (NT == 1) hipLaunchKernelGGL((k_pred_up<B, GATED, WT, 1>), grid, dim3(256), lds, st, p);
-    else if (NT == 2) hipLaunchKernelGGL((k_pred_up<B, GATED, WT, 2>), grid, dim3(256), lds, st, p);
-    else hipLaunchKernelGGL((k_pred_up<B, GATED, WT, 4>), grid, dim3(256), lds, st, p);
-    if (hipGetLastError() != hipSuccess) return 1;
+    int rc;
+    if (NT == 1) rc = launch_pred_up<B, GATED, WT, 1>(p, st);
+    else if (NT == 2) rc = launch_pred_up<B, GATED, WT, 2>(p, st);
+    else rc = launch_pred_up<B, GATED, WT, 4>(p, st);
+    if (rc) return 1;
     return launch_down_sum<B, GATED, WT>(a, st);
 }
 

@@ -88,13 +88,16 @@ struct SplitArgs {
 };
 
 #ifdef PIK_TRACE
-#define SPLIT_TRACE(slot)                                                                           \
+#define SPLIT_TRACE_AT(row0, slot)                                                                  \
     do {                                                                                            \
-        if (a.trace != nullptr && threadIdx.x == 0) a.trace[(size_t)blockIdx.x * 8 + (slot)] = wall_clock64(); \
+        if (a.trace != nullptr && threadIdx.x == 0)                                                 \
+            a.trace[((size_t)(row0) + blockIdx.x) * 8 + (slot)] = wall_clock64();                   \
     } while (0)
 #else
-#define SPLIT_TRACE(slot) ((void)0)
+#define SPLIT_TRACE_AT(row0, slot) ((void)0)
 #endif
+#define SPLIT_TRACE(slot) SPLIT_TRACE_AT(0, slot)
+#define DOWN_TRACE(slot) SPLIT_TRACE_AT(4096, slot)
 
 // Position of the k-th (0-based) set bit of w; w has more than k bits set.
 __device__ __forceinline__ int select_bit(uint32_t w, int k) {
@@ -288,7 +291,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int s = blockIdx.x % a.S, c = blockIdx.x / a.S;
-    SPLIT_TRACE(1);
+    DOWN_TRACE(1);
     const int col = s * SLAB + lane * CPL;
     const int cc = col < a.d ? col : 0;
     const bool hmode = a.hin != nullptr;
@@ -296,7 +299,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
 
     const int n = split_count(a, dyn, s_w, tid, lane, wave);
     const int p0 = (int)((int64_t)n * c / a.C), p1 = (int)((int64_t)n * (c + 1) / a.C);
-    SPLIT_TRACE(2);
+    DOWN_TRACE(2);
     float acc[B][CPL];
 #pragma unroll
     for (int b = 0; b < B; ++b)
@@ -375,7 +378,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
             if (s == 0 && a.hout != nullptr) a.hout[(size_t)b * a.f + r0 + j] = hv;
         }
         __syncthreads();
-        SPLIT_TRACE(3);
+        DOWN_TRACE(3);
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
             const int j = wave + 4 * i;
@@ -424,7 +427,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
         }
         __syncthreads();                                        // s_slot and s_h are refilled next round
     }
-    SPLIT_TRACE(4);
+    DOWN_TRACE(4);
 
     // The chunk partial of this slab: the four waves meet in LDS (fixed order), then plain stores.
     float *s_red = reinterpret_cast<float *>(dyn);             // [4][B][CPL][64]
@@ -442,7 +445,7 @@ __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
             a.ypart[((size_t)c * B + b) * a.d + gcol] = s_red[e] + s_red[B * CPL * kWave + e] +
                                                           s_red[2 * B * CPL * kWave + e] + s_red[3 * B * CPL * kWave + e];
     }
-    SPLIT_TRACE(0);
+    DOWN_TRACE(0);
 }
 
 // ------------------------------------------------------------------------------ sum of the chunks
@@ -466,12 +469,18 @@ static __global__ __launch_bounds__(kSplitThreads) void k_sum_split(const float 
 // ------------------------------------------------------------------------------ predictor + up
 
 // The second predictor matrix, the mask and the up rows in one launch (layer path, batch <= 2):
-// workgroup t owns the 32-neuron tile t.  It loads the tile's rows of P2 first (they depend on
-// nothing), stages x and z in LDS meanwhile, forms the logits, writes the union mask and the tile's
-// word of listed flags (fired and resident), then each listed neuron of the tile goes to one wave,
-// which reads the neuron's input row(s) against x and stores h by neuron id.  The up rows of a
-// tile are read while other tiles still stream P2, so the up step costs little beyond its bytes.
-// k_down_split then reads h by id (hin) and needs no partial products.
+// 32-neuron tiles, workgroup g taking tiles g, g + grid, g + 2 grid, ... (the grid is sized so that
+// the workgroups fit on the chip together and each gets the same number of tiles, or one fewer).  A workgroup
+// stages x and z in LDS once, while its first tile's rows of P2 stream in.  Per tile: each wave
+// forms the partial logits of its eight rows in two halves, reloading a half's registers with the
+// next tile's rows as soon as that half is consumed (so P2 keeps streaming while it computes), sums
+// them with one reduce-scatter and writes the union mask; then each
+// listed neuron of the tile (fired and resident) goes to one wave, which reads the neuron's input
+// row(s) against x and stores h by neuron id.  Last, the tile's word of live flags (listed, and h
+// nonzero for some token) is stored.  The up rows of a tile are read while the next tile's P2 rows
+// stream, so the up step costs little beyond its bytes.  k_down_split then visits the live
+// neurons only (a row whose h is zero for every token adds exact zeros), reads h by id (hin) and
+// needs no partial products.
 struct PredUpArgs {
     int d, f, r, n_slots, act;
     int64_t row_bytes;
@@ -482,8 +491,11 @@ struct PredUpArgs {
     const int32_t *slot_of;
     const uint16_t *x;
     uint8_t *mask;                          // [f] union flags
-    uint32_t *bits;                         // [ceil(f/32)] listed flags
+    uint32_t *bits;                         // [ceil(f/32)] live flags (listed, h nonzero for some token)
     float *h;                               // [B][f] h of listed neurons by id (others untouched)
+#ifdef PIK_TRACE
+    uint64_t *trace;                        // [grid][8] timestamps
+#endif
 };
 
 // Dynamic LDS of k_pred_up: x [B][d] fp16 (q4-paired for Q4_0), then z [B][r] fp32.
@@ -493,125 +505,173 @@ __host__ __device__ inline size_t pred_up_lds(int B, int d, int r) {
 
 template <int B, bool GATED, int WT, int NT>
 __global__ __launch_bounds__(256) void k_pred_up(PredUpArgs a) {
-    constexpr int R = 8;                                  // P2 rows per wave (the tile: 4 x 8)
+    constexpr int R = 8, RH = 4;                          // P2 rows per wave (the tile: 4 x 8), in two halves
     extern __shared__ __align__(16) uint16_t dynx[];
     __shared__ uint32_t s_words[4];
+    __shared__ uint32_t s_live;
     __shared__ int s_slot[32];
     const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int t = blockIdx.x;
-    const int row0 = t * 32 + wave * R;
+    const int ntiles = (a.f + 31) / 32;
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.p2, (uint32_t)((size_t)a.f * a.r * 2));
-    uint4 w[R][NT];
+    // the two halves of this wave's rows of P2 (rows 0-3 and 4-7 of its eight); each half is
+    // reloaded with the next tile's rows as soon as its logits are formed, so a wave always has
+    // P2 loads in flight while it computes
+    uint4 w0[RH][NT], w1[RH][NT];
+    auto issue = [&](uint4 (&w)[RH][NT], int t, int h) {
+        const int row0 = t * 32 + wave * R + h * RH;
 #pragma unroll
-    for (int i = 0; i < R; ++i)
+        for (int i = 0; i < RH; ++i)
+#pragma unroll
+            for (int q = 0; q < NT; ++q) {
+                const int row = row0 + i, col = lane * 8 + q * 512;
+                w[i][q] = bld16(rs, (t < ntiles && row < a.f && col < a.r) ? ((uint32_t)row * a.r + col) * 2 : kOOB);
+            }
+    };
+    // partial logits of a half: lane-wise dot products of its columns with z
+    auto dots = [&](const uint4 (&w)[RH][NT], const float *zs, float (&v)[B][R], int h) {
 #pragma unroll
         for (int q = 0; q < NT; ++q) {
-            const int row = row0 + i, col = lane * 8 + q * 512;
-            w[i][q] = bld16(rs, (row < a.f && col < a.r) ? ((uint32_t)row * a.r + col) * 2 : kOOB);
+            const int col = lane * 8 + q * 512;
+            if (col < a.r) {
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const float4 za = *reinterpret_cast<const float4 *>(zs + b * a.r + col);
+                    const float4 zb = *reinterpret_cast<const float4 *>(zs + b * a.r + col + 4);
+                    const float zr[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
+#pragma unroll
+                    for (int i = 0; i < RH; ++i) {
+                        const uint32_t qq[4] = {w[i][q].x, w[i][q].y, w[i][q].z, w[i][q].w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const h2 p = __builtin_bit_cast(h2, qq[e]);
+                            v[b][h * RH + i] = fmaf((float)p.x, zr[2 * e], v[b][h * RH + i]);
+                            v[b][h * RH + i] = fmaf((float)p.y, zr[2 * e + 1], v[b][h * RH + i]);
+                        }
+                    }
+                }
+            }
         }
-    const int rowl = row0 + lane;                         // lane i < R: offset and slot of row i
-    const bool mine = lane < R && rowl < a.f;
-    const uint16_t cbits = mine ? a.c[rowl] : (uint16_t)0;
-    const int slot = mine ? (a.slot_of ? a.slot_of[rowl] : rowl) : -1;
+    };
+    const int G = gridDim.x;
+    int t = blockIdx.x;
+    SPLIT_TRACE(1);
+    if (threadIdx.x == 0) s_live = 0u;
+    issue(w0, t, 0);
+    issue(w1, t, 1);
     uint16_t *xs = dynx;
     float *zs = reinterpret_cast<float *>(dynx + ((size_t)B * a.d + 7) / 8 * 8);
     stage_x<B, WT == WT_Q4_0>(xs, a.x, a.d, 0, a.d, a.d);
     stage_vec16(zs, a.z, B * a.r / 4);
     __syncthreads();
-    const float ci = half_to_float(cbits);
-    uint32_t mb = 0;                                      // fired bits of the wave's rows (uniform)
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-        float v[R];
-#pragma unroll
-        for (int i = 0; i < R; ++i) v[i] = 0.f;
-#pragma unroll
-        for (int q = 0; q < NT; ++q) {
-            const int col = lane * 8 + q * 512;
-            if (col < a.r) {
-                const float4 za = *reinterpret_cast<const float4 *>(zs + b * a.r + col);
-                const float4 zb = *reinterpret_cast<const float4 *>(zs + b * a.r + col + 4);
-                const float zr[8] = {za.x, za.y, za.z, za.w, zb.x, zb.y, zb.z, zb.w};
-#pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    const uint32_t qq[4] = {w[i][q].x, w[i][q].y, w[i][q].z, w[i][q].w};
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const h2 p = __builtin_bit_cast(h2, qq[e]);
-                        v[i] = fmaf((float)p.x, zr[2 * e], v[i]);
-                        v[i] = fmaf((float)p.y, zr[2 * e + 1], v[i]);
-                    }
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < R; ++i) {
-            const float l = wave_sum(v[i]) + bcastf(ci, i);
-            mb |= (uint32_t)(l > 0.f) << i;
-        }
-    }
-    if (mine) a.mask[rowl] = (uint8_t)((mb >> lane) & 1u);
-    const bool resident = slot >= 0 && slot < a.n_slots;
-    if (lane < R) s_slot[wave * R + lane] = resident ? slot : -1;
-    const uint32_t byte = mb & (uint32_t)__ballot(mine && resident);   // wave w: tile rows 8w .. 8w+7
-    if (lane == 0) s_words[wave] = byte;
-    __syncthreads();
-    const uint32_t word = s_words[0] | (s_words[1] << 8) | (s_words[2] << 16) | (s_words[3] << 24);
-    if (threadIdx.x == 0) a.bits[t] = word;
-    // listed neurons in ascending order: wave w takes the w-th, (w+4)-th, ...; for fp16 rows that one
-    // pass covers, a wave reads two neurons' rows at once (Q4_0 tiles list ~1-2 neurons, and the
-    // second row's registers would cost occupancy)
+    int tn = t + G;
+    SPLIT_TRACE(2);
+    int it = 0;
     using P = RowPass<B, GATED, WT>;
     const int64_t in_stride = GATED ? 2 * a.row_bytes : a.row_bytes;
     const __amdgpu_buffer_rsrc_t rin = buf_rsrc(a.w_in, (uint32_t)(a.n_slots * in_stride));
-    const int cnt = __builtin_popcount(word);
     const bool pairs = WT == WT_F16 && P::extent(a.d) <= P::STEP;
-    for (int j = wave; j < cnt; j += pairs ? 8 : 4) {
-        const int j2 = j + 4;
-        const bool two = pairs && j2 < cnt;
-        int bit = 0, bit2 = 0;
-        {
-            uint32_t bw = word;
-            for (int q = 0; q < j; ++q) bw &= bw - 1;
-            bit = __builtin_ctz(bw);
-            if (two) {
-                for (int q = j; q < j2; ++q) bw &= bw - 1;
-                bit2 = __builtin_ctz(bw);
-            }
+    while (t < ntiles) {
+        // lanes 8k .. 8k+7 end up with row k of the wave's eight (reduce-scatter below); they load
+        // that row's offset and slot now
+        const int rowk = t * 32 + wave * R + (lane >> 3);
+        const bool rok = rowk < a.f;
+        const uint16_t cbits = rok ? a.c[rowk] : (uint16_t)0;
+        const int slot = rok ? (a.slot_of ? a.slot_of[rowk] : rowk) : -1;
+        float v[B][R];
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int i = 0; i < R; ++i) v[b][i] = 0.f;
+        dots(w0, zs, v, 0);
+        issue(w0, tn, 0);
+        dots(w1, zs, v, 1);
+        issue(w1, tn, 1);
+        const float ci = half_to_float(cbits);
+        bool fired = false;
+#pragma unroll
+        for (int b = 0; b < B; ++b) fired |= reduce_scatter<R>(v[b], lane) + ci > 0.f;
+        // bit 8k of the ballot = row k fired (its eight lanes agree)
+        const uint64_t fb = __ballot(fired && rok);
+        const bool resident = slot >= 0 && slot < a.n_slots;
+        const uint64_t rb8 = __ballot(rok && resident);
+        uint32_t mb = 0, byte = 0;
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            mb |= (uint32_t)((fb >> (8 * k)) & 1u) << k;
+            byte |= (uint32_t)((fb & rb8) >> (8 * k) & 1u) << k;
         }
-        const int s1 = s_slot[bit], s2 = two ? s_slot[bit2] : 0;
-        float ag[B], au[B], ag2[B], au2[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) ag[b] = au[b] = ag2[b] = au2[b] = 0.f;
-        if (pairs) {
-            const int d2 = two ? a.d : 0;                 // a missing second neuron reads nothing
-            P q1, q2;
-            q1.issue_buf(rin, (uint32_t)(s1 * in_stride), a.row_bytes, a.d, 0, lane);
-            q2.issue_buf(rin, (uint32_t)(s2 * in_stride), a.row_bytes, d2, 0, lane);
-            q1.consume(xs, a.d, a.d, 0, lane, ag, au);
-            q2.consume(xs, a.d, d2, 0, lane, ag2, au2);
-        } else {
-            neuron_dots<B, GATED, WT>(a.w_in + (int64_t)s1 * in_stride, a.row_bytes, a.d, xs, a.d, lane, ag, au);
-        }
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            if (n == 1 && !two) break;                    // wave-uniform
-            const int sl = n == 0 ? s1 : s2, id = t * 32 + (n == 0 ? bit : bit2);
-            const float bias = (!GATED && a.b_up != nullptr) ? half_to_float(a.b_up[sl]) : 0.f;
-#pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const float u = wave_sum(n == 0 ? au[b] : au2[b]);
-                float hv;
-                if (GATED) {
-                    hv = fmaxf(wave_sum(n == 0 ? ag[b] : ag2[b]), 0.f) * u;
-                } else {
-                    hv = fmaxf(u + bias, 0.f);
-                    if (a.act) hv *= hv;                  // squared ReLU
+        if ((lane & 7) == 0 && rok) a.mask[rowk] = (uint8_t)((mb >> (lane >> 3)) & 1u);
+        if ((lane & 7) == 0) s_slot[wave * R + (lane >> 3)] = resident ? slot : -1;
+        if (lane == 0) s_words[wave] = byte;
+        __syncthreads();
+        const uint32_t word = s_words[0] | (s_words[1] << 8) | (s_words[2] << 16) | (s_words[3] << 24);
+        if (it < 2) SPLIT_TRACE(3 + 2 * it);
+        // listed neurons in ascending order: wave w takes the w-th, (w+4)-th, ...; for fp16 rows that
+        // one pass covers, a wave reads two neurons' rows at once (Q4_0 tiles list ~1-2 neurons, and
+        // the second row's registers would cost occupancy)
+        const int cnt = __builtin_popcount(word);
+        for (int j = wave; j < cnt; j += pairs ? 8 : 4) {
+            const int j2 = j + 4;
+            const bool two = pairs && j2 < cnt;
+            int bit = 0, bit2 = 0;
+            {
+                uint32_t bw = word;
+                for (int q = 0; q < j; ++q) bw &= bw - 1;
+                bit = __builtin_ctz(bw);
+                if (two) {
+                    for (int q = j; q < j2; ++q) bw &= bw - 1;
+                    bit2 = __builtin_ctz(bw);
                 }
-                if (lane == 0) a.h[(size_t)b * a.f + id] = hv;
+            }
+            const int s1 = s_slot[bit], s2 = two ? s_slot[bit2] : 0;
+            float ag[B], au[B], ag2[B], au2[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) ag[b] = au[b] = ag2[b] = au2[b] = 0.f;
+            if (pairs) {
+                const int d2 = two ? a.d : 0;             // a missing second neuron reads nothing
+                P q1, q2;
+                q1.issue_buf(rin, (uint32_t)(s1 * in_stride), a.row_bytes, a.d, 0, lane);
+                q2.issue_buf(rin, (uint32_t)(s2 * in_stride), a.row_bytes, d2, 0, lane);
+                q1.consume(xs, a.d, a.d, 0, lane, ag, au);
+                q2.consume(xs, a.d, d2, 0, lane, ag2, au2);
+            } else {
+                neuron_dots<B, GATED, WT>(a.w_in + (int64_t)s1 * in_stride, a.row_bytes, a.d, xs, a.d, lane, ag, au);
+            }
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                if (n == 1 && !two) break;                // wave-uniform
+                const int sl = n == 0 ? s1 : s2, id = t * 32 + (n == 0 ? bit : bit2);
+                const float bias = (!GATED && a.b_up != nullptr) ? half_to_float(a.b_up[sl]) : 0.f;
+                bool live = false;
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const float u = wave_sum(n == 0 ? au[b] : au2[b]);
+                    float hv;
+                    if (GATED) {
+                        hv = fmaxf(wave_sum(n == 0 ? ag[b] : ag2[b]), 0.f) * u;
+                    } else {
+                        hv = fmaxf(u + bias, 0.f);
+                        if (a.act) hv *= hv;              // squared ReLU
+                    }
+                    live |= hv != 0.f;
+                    if (lane == 0) a.h[(size_t)b * a.f + id] = hv;
+                }
+                if (lane == 0 && live) atomicOr(&s_live, 1u << (n == 0 ? bit : bit2));
             }
         }
+        // the tile's word of live flags (listed, and h nonzero for some token): the down rows to read;
+        // s_slot, s_words and s_live are reused by the next tile only after this barrier
+        __syncthreads();
+        if (it < 2) SPLIT_TRACE(4 + 2 * it);
+        ++it;
+        if (threadIdx.x == 0) {
+            a.bits[t] = s_live;
+            s_live = 0u;
+        }
+        t = tn;
+        tn += G;
     }
+    SPLIT_TRACE(0);
 }
 
 // Launch of the three kernels for batch width B in {1, 2}; C is chosen here.

@@ -34,8 +34,6 @@ namespace pik {
 constexpr int kSparseMaxChunks = 16;           // chunk partials per slab
 constexpr int kTailListMax = 2048;             // listed neurons a down tile handles per round
 constexpr int kTailMaxTiles = 384;             // neuron tiles up to which the tail kernel is used
-constexpr int kTailMaxTilesB2 = 1024;          // ... and at batch <= 2 (up workgroups then take
-                                               // several tiles each, which pays off only there)
 constexpr int kTailCPL = 8;                    // columns per lane of a down tile (one 16-byte fp16
                                                // load or one Q4_0 code word per row)
 constexpr int kTailSlab = kTailCPL * kWave;    // columns of a down tile

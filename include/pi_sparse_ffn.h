@@ -157,14 +157,15 @@ int pi_sparse_ffn_wide(const pi_ffn *ffn, const void *x, int32_t batch, const in
  * idx_out [d_ffn] and counts_out [2] receive the intermediate results when non-NULL (otherwise they
  * live in the workspace; the list is only built when idx_out or counts_out is given -- the sparse
  * FFN itself reads the predictor's listed flags).
- * For layers of at most 12288 neurons (32768 at batch <= 2) whose x and z fit one workgroup's LDS
+ * The workspace must be zero-filled before the first call that uses it; each call leaves it ready
+ * for the next one (never clear or share it while a call is in flight; after a call that returned
+ * an error, zero-fill it again).
+ * For layers of at most 12288 neurons whose x and z fit one workgroup's LDS
  * (pi_layer_path == 1), everything after the first predictor matrix is ONE persistent kernel whose
- * workgroups hand the mask and h to each other through the workspace.  Then:
- *  - the workspace must be zero-filled before the first call that uses it, and each call leaves it
- *    ready for the next one (never clear or share it while a call is in flight);
- *  - the int32 at byte offset 384 of the workspace is a sticky status word: nonzero means a
- *    cross-workgroup wait ran out its time limit (20 ms) and the outputs of that call are invalid.
- * Every wait inside the kernel is bounded.  Zero-filling the workspace once is always safe.  At the
+ * workgroups hand the mask and h to each other through the workspace.  The int32 at byte offset
+ * 384 of the workspace is a sticky status word: nonzero means a cross-workgroup wait ran out its
+ * time limit (20 ms) and the outputs of that call are invalid.  Every wait inside the kernel is
+ * bounded.  At the
  * batches where the sparse FFN runs on the MFMA form, an |h| of 65504 or more ORs 64 into the same
  * status word (see pi_sparse_ffn).
  * One workspace may serve several layers, one call at a time, when their pi_ffn descriptors agree
@@ -188,8 +189,9 @@ int pi_ffn_layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const 
 
 /* Which launches pi_ffn_layer_from_hidden makes for this layer and batch: 1 = one persistent kernel
  * (logits, mask and sparse FFN together; x, z and the kernel's arrays fit one workgroup's LDS and
- * d_ffn <= 12288, or d_ffn <= 32768 at batch <= 2), 2 = separate kernels (logits and mask,
- * compaction, sparse FFN).  0 on invalid arguments. */
+ * d_ffn <= 12288, batch <= 8), 2 = separate kernels (at batch <= 2: logits, mask and up rows in
+ * one kernel, then the down rows and the sum of their partials; otherwise logits and mask, then
+ * the sparse FFN).  0 on invalid arguments. */
 int pi_layer_path(const pi_predictor *pred, const pi_ffn *ffn, int32_t batch);
 
 /* Diagnostics: where a pi_sparse_ffn call leaves h (list position k, token b) in its workspace,

@@ -184,8 +184,10 @@ def test_layer_path(L):
     # one persistent kernel: d_ffn <= 12288 and x, z fit LDS
     assert path(pred(d=4096, f=11008, r=1024), ffn(d=4096, f=11008, gated=1), 1) == 1
     assert path(pred(d=1024, f=4096, r=128), ffn(d=1024, f=4096), 8) == 1
-    assert path(pred(d=8192, f=32768, r=1024), ffn(d=8192, f=32768), 1) == 1    # several tiles per workgroup
-    # separate kernels: too many neurons for the batch, or x too large for LDS
+    # separate kernels: more than 12288 neurons (at batch <= 2: k_pred_up and the split kernels, faster
+    # there), or x too large for LDS
+    assert path(pred(d=8192, f=32768, r=1024), ffn(d=8192, f=32768), 1) == 2
+    assert path(pred(d=7168, f=28672, r=1024), ffn(d=7168, f=28672), 1) == 2
     assert path(pred(d=8192, f=32768, r=1024), ffn(d=8192, f=32768), 4) == 2
     assert path(pred(d=12288, f=49152, r=1024), ffn(d=12288, f=49152), 1) == 2
     assert path(pred(d=12288, f=12288, r=1024), ffn(d=12288, f=12288), 8) == 2
