@@ -16,8 +16,16 @@ int choose_chunks(SplitArgs &a) {
                        &per_cu))
         return 1;
     int C = (2 * cus) / a.S;
+    // range mode (h by id): a chunk's flag words must fit one word per thread
+    if (a.hin != nullptr && a.nwords > 0) C = C > (a.nwords + kRangeMaxWords - 1) / kRangeMaxWords
+                                                  ? C : (a.nwords + kRangeMaxWords - 1) / kRangeMaxWords;
     a.C = C < 1 ? 1 : (C > kSplitMaxChunks ? kSplitMaxChunks : C);
     return 0;
+}
+
+// Flag words per chunk in range mode, else 0.
+inline int range_words(const SplitArgs &a) {
+    return (a.hin != nullptr && a.nwords > 0) ? (a.nwords + a.C - 1) / a.C : 0;
 }
 
 // k_down_split then k_sum_split (a.C set).
@@ -25,7 +33,7 @@ template <int B, bool GATED, int WT>
 int launch_down_sum(SplitArgs &a, hipStream_t st) {
     const int Bd = B * a.d;
     hipLaunchKernelGGL((k_down_split<B, GATED, WT>), dim3(a.S * a.C), dim3(kSplitThreads),
-                       split_dyn_lds(B, WT, a.nwords, true), st, a);
+                       split_dyn_lds(B, WT, a.nwords, true, range_words(a)), st, a);
     if (hipGetLastError() != hipSuccess) return 1;
     hipLaunchKernelGGL(k_sum_split, dim3((Bd + kSplitThreads - 1) / kSplitThreads), dim3(kSplitThreads), 0, st,
                        a.ypart, a.C, Bd, a.d, a.b_down, a.y);

@@ -28,7 +28,9 @@
 // for the others inside one launch, and far less than polling stamped words.)
 // Positions come from a device list (idx, counts: pi_sparse_ffn) or from the listed-flag words the
 // predictor wrote (each workgroup counts the set bits of all words and finds its positions by a
-// prefix sum: the ascending ranks of the set bits, exactly the list pi_compact would build).
+// prefix sum: the ascending ranks of the set bits, exactly the list pi_compact would build).  When
+// k_pred_up has already formed h (the layer path), the down kernel's chunks are ranges of flag
+// words instead, so a workgroup reads only its own words (range mode).
 #pragma once
 
 #include "pi_sync.hpp"
@@ -39,6 +41,7 @@ constexpr int kSplitMaxSlabs = 64;
 constexpr int kSplitMaxChunks = 64;
 constexpr int kSplitMaxWords = 4096;            // mask words a workgroup scans (d_ffn <= 131072)
 constexpr int kSplitThreads = 256;
+constexpr int kRangeMaxWords = kSplitThreads;   // live-flag words of one chunk in range mode
 
 // Columns of a slab: 64 lanes x CPL (fp16: one 16-byte vector of 8 columns per row; Q4_0: 8 code
 // bytes = 16 columns, half of a 32-weight block, plus that block's scale).
@@ -58,10 +61,12 @@ __host__ __device__ inline int split_slab_cols(int wt) {
     return wt == WT_F16 ? SplitCols<WT_F16>::SLAB : SplitCols<WT_Q4_0>::SLAB;
 }
 __host__ __device__ inline int split_slabs(int d, int wt) { return (d + split_slab_cols(wt) - 1) / split_slab_cols(wt); }
-// dynamic LDS of either kernel: the mask words and their prefix sums (bits mode); the down kernel
-// reuses it for the four waves' partials of its slab
-__host__ __device__ inline size_t split_dyn_lds(int B, int wt, int nwords, bool down) {
-    const size_t scan = (size_t)2 * (nwords > 0 ? nwords : 0) * sizeof(int);
+// dynamic LDS of either kernel: the mask words and their prefix sums (bits mode; in range mode the
+// ids of the chunk's live neurons, at most 32 per word of its range); the down kernel reuses it for
+// the four waves' partials of its slab
+__host__ __device__ inline size_t split_dyn_lds(int B, int wt, int nwords, bool down, int range_words = 0) {
+    const size_t scan = range_words > 0 ? (size_t)32 * range_words * sizeof(int)
+                                        : (size_t)2 * (nwords > 0 ? nwords : 0) * sizeof(int);
     const size_t red = down ? (size_t)4 * B * split_slab_cols(wt) * sizeof(float) : 0;
     const size_t m = scan > red ? scan : red;
     return m > 0 ? m : 16;
@@ -174,6 +179,23 @@ __device__ __forceinline__ int split_slot(const SplitArgs &a, const int *dyn, in
     }
     if (id_out != nullptr) *id_out = id;
     return slot_of_id(id, a.slot_of, a.f, a.n_slots);
+}
+
+// Range mode (h by id): chunk c owns the flag words [c*nwords/C, (c+1)*nwords/C) (at most
+// kRangeMaxWords), and its positions are the set bits of those words in ascending id order.  Writes
+// their ids to ids[0..n) (LDS) and returns n (workgroup-uniform).  No scan over the whole mask and
+// no search per position; the chunks hold unequal numbers of neurons (as many as fired in their id
+// range), and every sum still runs in an order fixed by the ids.
+__device__ __forceinline__ int split_range(const SplitArgs &a, int c, int *ids, int *s_w, int tid, int lane,
+                                           int wave) {
+    const int w0 = (int)((int64_t)a.nwords * c / a.C), w1 = (int)((int64_t)a.nwords * (c + 1) / a.C);
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(a.bits, (uint32_t)a.nwords * 4u);
+    const uint32_t wv = bld4(rw, w0 + tid < w1 ? (uint32_t)(w0 + tid) * 4u : kOOB);
+    int total;
+    int pos = block_excl_scan(__popc(wv), s_w, lane, wave, total);
+    for (uint32_t m = wv; m != 0u; m &= m - 1u) ids[pos++] = (w0 + tid) * 32 + __builtin_ctz(m);
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(total);
 }
 
 // ------------------------------------------------------------------------------ up: partial dots
@@ -295,10 +317,18 @@ __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
     const int col = s * SLAB + lane * CPL;
     const int cc = col < a.d ? col : 0;
     const bool hmode = a.hin != nullptr;
+    const bool range = hmode && a.nwords > 0;               // positions: the live ids of this chunk's range
     const int64_t rb = a.row_bytes;
 
-    const int n = split_count(a, dyn, s_w, tid, lane, wave);
-    const int p0 = (int)((int64_t)n * c / a.C), p1 = (int)((int64_t)n * (c + 1) / a.C);
+    int p0, p1;
+    if (range) {
+        p0 = 0;
+        p1 = split_range(a, c, dyn, s_w, tid, lane, wave);
+    } else {
+        const int n = split_count(a, dyn, s_w, tid, lane, wave);
+        p0 = (int)((int64_t)n * c / a.C);
+        p1 = (int)((int64_t)n * (c + 1) / a.C);
+    }
     DOWN_TRACE(2);
     float acc[B][CPL];
 #pragma unroll
@@ -310,7 +340,12 @@ __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
         const int nr = min(RMAX, p1 - r0);
         if (tid < nr) {
             int id;
-            s_slot[tid] = split_slot(a, dyn, r0 + tid, &id);
+            if (range) {
+                id = dyn[r0 + tid];
+                s_slot[tid] = slot_of_id(id, a.slot_of, a.f, a.n_slots);
+            } else {
+                s_slot[tid] = split_slot(a, dyn, r0 + tid, &id);
+            }
             s_id[tid] = id;
         }
         __syncthreads();
