@@ -38,8 +38,9 @@ int check_batch(int32_t B) { return (B >= 1 && B <= PI_MAX_BATCH) ? PI_OK : PI_E
 // 8 tokens; past that the first predictor matrix runs in two passes and the rest on MFMA.
 constexpr int kGemvMaxBatch = 8;
 // From this batch on the second predictor matrix runs on MFMA (k_pred_l2_mfma): the GEMV form's
-// vector-ALU work per weight grows with the batch.
-constexpr int kPredMfmaFrom = 9;
+// vector-ALU work per weight grows with the batch (measured crossovers on MI355X, rank 1024: batch
+// 4 at 28672 and 49152 neurons, batch 6 at 11008).
+inline int pred_mfma_from(int d_ffn) { return d_ffn >= 16384 ? 4 : 6; }
 
 int check_pred(const pi_predictor *p) {
     if (!p) return PI_ERR_NULL;
@@ -262,7 +263,7 @@ int enqueue_pred_l2_b(const pi_predictor *p, const float *z, uint8_t *mask, floa
 
 int enqueue_pred_l2(const pi_predictor *p, const float *z, int B, uint8_t *mask, float *logits, hipStream_t st,
                     uint32_t *bits = nullptr, const int32_t *slot_of = nullptr, int n_slots = 0) {
-    if (B >= kPredMfmaFrom) {
+    if (B >= pred_mfma_from(p->d_ffn)) {
         const int r = p->rank, f = p->d_ffn;
         const uint16_t *p2 = static_cast<const uint16_t *>(p->p2), *c = static_cast<const uint16_t *>(p->c);
         const dim3 grid(ceil_div(f, 64));
