@@ -297,7 +297,8 @@ __global__ __launch_bounds__(256) void k_pred_l2_mfma(const uint16_t *__restrict
     }
 }
 
-// y over (slab, neuron chunk) tiles; a slab is 16 lanes x CPL columns (fp16: 8 columns, one 16-byte
+// y over (slab, neuron chunk) tiles (xmap: the XCD-grouped 1-D grid described below, else a 2-D grid
+// of S x C); a slab is 16 lanes x CPL columns (fp16: 8 columns, one 16-byte
 // load per row; Q4_0: 16 columns, 8 code bytes and a scale per row, so 16 lanes read a whole 128-byte
 // line of a row's codes).  The chunk's 16-position steps are split into eight contiguous runs, one
 // per wave.  In a step, lane l reads its CPL columns of the rows of positions 4(l/16) + v (v < 4)
@@ -318,12 +319,24 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
                                                             float *__restrict__ part, int C,
                                                             int32_t *__restrict__ tickets,
                                                             const uint16_t *__restrict__ b_down,
-                                                            float *__restrict__ y) {
+                                                            float *__restrict__ y, int xmap, int S) {
     constexpr int CPL = wide_down_cpl(WT), NW = CPL / 2, SC = 16 * CPL;
     __shared__ f4 red[4][8][kWave];
     __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int slab = blockIdx.x, ck = blockIdx.y;
+    int slab = blockIdx.x, ck = blockIdx.y;
+    if (xmap) {
+        // Q4_0: the scales of 8 consecutive slabs share one 128-byte line, so those 8 workgroups go to
+        // one XCD (workgroups are dealt to the 8 XCDs round robin) and meet in its L2 instead of each
+        // XCD fetching the line.  1-D grid of 8*ceil(S/8)*C workgroups, C a multiple of 8: XCD x takes
+        // the (slab group, chunk) pairs x, x + 8, ..., each as 8 consecutive workgroups.
+        const int L = blockIdx.x, x = L & 7, q = L >> 3;
+        const int j = q & 7, pp = (q >> 3) * 8 + x;
+        const int ng = (S + 7) / 8;
+        slab = (pp % ng) * 8 + j;
+        ck = pp / ng;
+        if (slab >= S) return;                                   // padding of the last group
+    }
     const int n = min(max(counts[0], 0), n_slots);
     const int T = (n + 15) / 16;                                 // 16-position steps
     const int c_lo = (int)((int64_t)T * ck / C), c_hi = (int)((int64_t)T * (ck + 1) / C);
