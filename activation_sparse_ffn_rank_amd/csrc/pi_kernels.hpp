@@ -523,6 +523,58 @@ static __global__ __launch_bounds__(1024) void k_compact(const uint8_t *__restri
     }
 }
 
+// The same list from the predictor's flag words instead of the mask bytes (one workgroup; at most
+// 4 words per thread, so d_ffn <= 131072): bit e of bits[w] = neuron 32w + e predicted.  A 32-fold
+// smaller read than the mask; slot_of (or NULL) is looked up only for the predicted neurons.
+static __global__ __launch_bounds__(1024) void k_compact_bits(const uint32_t *__restrict__ bits, int nwords,
+                                                       const int32_t *__restrict__ slot_of, int n_slots,
+                                                       int32_t *__restrict__ idx, int32_t *__restrict__ counts) {
+    __shared__ int wsum[16], wpred[16];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int per = (nwords + 1023) / 1024;                  // <= 4
+    const int w0 = tid * per;
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(bits, (uint32_t)nwords * 4u);
+    uint32_t wv[4], act[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) wv[v] = bld4(rw, (v < per && w0 + v < nwords) ? (uint32_t)(w0 + v) * 4u : kOOB);
+    int cnt = 0, npred = 0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        act[v] = wv[v];
+        if (slot_of != nullptr) {
+            act[v] = 0u;
+            for (uint32_t m = wv[v]; m != 0u; m &= m - 1u) {
+                const int b = __builtin_ctz(m), sl = slot_of[(w0 + v) * 32 + b];
+                if (sl >= 0 && sl < n_slots) act[v] |= 1u << b;
+            }
+        }
+        npred += __popc(wv[v]);
+        cnt += __popc(act[v]);
+    }
+    const int incl = wave_incl_scan(cnt);
+    int wp = npred;
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) wp += __shfl_xor(wp, o, kWave);
+    if (lane == kWave - 1) wsum[wave] = incl;
+    if (lane == 0) wpred[wave] = wp;
+    __syncthreads();
+    int before = 0, total = 0, tpred = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) {
+        before += (w < wave) ? wsum[w] : 0;
+        total += wsum[w];
+        tpred += wpred[w];
+    }
+    int pos = before + incl - cnt;
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+        for (uint32_t m = act[v]; m != 0u; m &= m - 1u) idx[pos++] = (w0 + v) * 32 + __builtin_ctz(m);
+    if (tid == 0) {
+        counts[0] = total;
+        counts[1] = tpred;
+    }
+}
+
 // ------------------------------------------------------------------------------ sparse FFN
 
 // One pass of a neuron's row dot products, split into "issue the loads" and "consume them" so
