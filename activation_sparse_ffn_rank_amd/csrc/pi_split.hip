@@ -12,7 +12,7 @@ template <int B, bool GATED, int WT>
 int choose_chunks(SplitArgs &a) {
     int cus = 0, per_cu = 0;
     const size_t lds_down = split_dyn_lds(B, WT, a.nwords, true);
-    if (resident_slots(reinterpret_cast<const void *>(k_down_split<B, GATED, WT>), kSplitThreads, lds_down, &cus,
+    if (resident_slots(reinterpret_cast<const void *>(k_down_split<B, GATED, WT, false>), kSplitThreads, lds_down, &cus,
                        &per_cu))
         return 1;
     int C = (2 * cus) / a.S;
@@ -32,8 +32,11 @@ inline int range_words(const SplitArgs &a) {
 template <int B, bool GATED, int WT>
 int launch_down_sum(SplitArgs &a, hipStream_t st) {
     const int Bd = B * a.d;
-    hipLaunchKernelGGL((k_down_split<B, GATED, WT>), dim3(a.S * a.C), dim3(kSplitThreads),
-                       split_dyn_lds(B, WT, a.nwords, true, range_words(a)), st, a);
+    const size_t lds = split_dyn_lds(B, WT, a.nwords, true, range_words(a));
+    if (a.hin != nullptr && a.nwords > 0)
+        hipLaunchKernelGGL((k_down_split<B, GATED, WT, true>), dim3(a.S * a.C), dim3(kSplitThreads), lds, st, a);
+    else
+        hipLaunchKernelGGL((k_down_split<B, GATED, WT, false>), dim3(a.S * a.C), dim3(kSplitThreads), lds, st, a);
     if (hipGetLastError() != hipSuccess) return 1;
     hipLaunchKernelGGL(k_sum_split, dim3((Bd + kSplitThreads - 1) / kSplitThreads), dim3(kSplitThreads), 0, st,
                        a.ypart, a.C, Bd, a.d, a.b_down, a.y);

@@ -298,7 +298,9 @@ __global__ __launch_bounds__(kSplitThreads) void k_up_split(SplitArgs a) {
 
 // ------------------------------------------------------------------------------ down: h, y
 
-template <int B, bool GATED, int WT>
+// HID: h by neuron id (k_pred_up formed it; positions in range mode), else h from the partial
+// products of k_up_split (list or bits mode).
+template <int B, bool GATED, int WT, bool HID>
 __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
     constexpr int CPL = SplitCols<WT>::CPL, SLAB = SplitCols<WT>::SLAB;
     constexpr int G = GATED ? 2 : 1, BG = B * G;
@@ -316,8 +318,8 @@ __global__ __launch_bounds__(kSplitThreads) void k_down_split(SplitArgs a) {
     DOWN_TRACE(1);
     const int col = s * SLAB + lane * CPL;
     const int cc = col < a.d ? col : 0;
-    const bool hmode = a.hin != nullptr;
-    const bool range = hmode && a.nwords > 0;               // positions: the live ids of this chunk's range
+    constexpr bool hmode = HID;
+    constexpr bool range = HID;                             // positions: the live ids of this chunk's range
     const int64_t rb = a.row_bytes;
 
     int p0, p1;

@@ -147,7 +147,7 @@ def ffn_kernel_names(h_kind: int, B: int, cfg, synth):
     w = 1 if cfg.wtype == synth.F16 else 2
     if h_kind == 1:
         return "k_up_split + k_down_split + k_sum_split", [f"void pik::k_up_split<{B}, {g}, {w}>",
-                                                         f"void pik::k_down_split<{B}, {g}, {w}>",
+                                                         f"void pik::k_down_split<{B}, {g}, {w}, false>",
                                                          "pik::k_sum_split("]
     if h_kind == 2:
         return "k_sparse_up + k_sparse_down", [f"void pik::k_sparse_up<{B}, {g}, {w}>", f"void pik::k_sparse_down<{B}, {w}>"]
@@ -258,8 +258,12 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
     n_read_down = n_live if h_kind == 2 else n_act
     ffn_touched = n_act * in_rows * rb + n_read_down * rb + 8 * n_act + vec_bytes
     ffn_predicted = n_act * (in_rows + 1) * rb + 8 * n_act + vec_bytes
-    # the rest of the layer: P2 and c, z, every listed row in and down
-    rest_bytes = 2 * cfg.f * cfg.r + 2 * cfg.f + 4 * B * cfg.r + slot_bytes + n_act * (in_rows + 1) * rb + vec_bytes
+    # the rest of the layer: P2 and c, z, every listed input row, and the down rows the form reads --
+    # at batch <= 2 (k_pred_up) only those whose h is nonzero for some token
+    pred_up = path == 2 and h_kind == 1
+    rest_down = n_live if (pred_up or h_kind == 2) else n_act
+    rest_bytes = (2 * cfg.f * cfg.r + 2 * cfg.f + 4 * B * cfg.r + slot_bytes + n_act * in_rows * rb + rest_down * rb
+                  + vec_bytes)
     hidden_bytes = 2 * cfg.r * cfg.d + 2 * B * cfg.d + 4 * B * cfg.r
     ffn_label, ffn_prefixes = ffn_kernel_names(h_kind, B, cfg, synth)
     g = "true" if cfg.gated else "false"
@@ -270,10 +274,14 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
         # the layer's own form at batch <= 2: logits, mask and up rows in one kernel, then the down
         # rows on h by neuron id
         rest_label = "k_pred_up + k_down_split + k_sum_split"
-        rest_prefixes = [f"void pik::k_pred_up<{B}, {g}, {w},", f"void pik::k_down_split<{B}, {g}, {w}>",
+        rest_prefixes = [f"void pik::k_pred_up<{B}, {g}, {w},", f"void pik::k_down_split<{B}, {g}, {w}, true>",
                          "pik::k_sum_split("]
     else:
-        rest_label, rest_prefixes = "k_pred_l2 + " + ffn_label, ["void pik::k_pred_l2<"] + ffn_prefixes
+        # the second predictor matrix on MFMA from batch 4 (d_ffn >= 16384) or 6, then the list from its
+        # flag words
+        pl2 = "k_pred_l2_mfma" if B >= (4 if cfg.f >= 16384 else 6) else "k_pred_l2"
+        rest_label = f"{pl2} + k_compact_bits + {ffn_label}"
+        rest_prefixes = [f"void pik::{pl2}<", "pik::k_compact_bits("] + ffn_prefixes
     step_bytes = (pred_bytes + float(ffn_touched.mean())) * L
     ms_per_step = elapsed_ms / K
 
@@ -655,9 +663,15 @@ def main():
     h = results[head]
     cfg = synth.CONFIGS[head[0]]
     L = h["layers"]
+    # the roofline: the launches of pi_ffn_layer_from_hidden (second predictor matrix, mask, sparse FFN:
+    # the step's dominant kernels, most of its time); beside it the sparse FFN alone on the same lists
+    # (the metric's GB/s on active-row bytes)
+    rest_b, rest_us, rest_label, rest_n = h["_rest"]
+    roof_traffic = measured_traffic(h["workload"], h["_rest_prefixes"]) if L == cfg.layers else None
+    roof_gbs = rest_b / (rest_us * 1e-6) / 1e9
     ffn_bytes, ffn_us, ffn_label, ffn_n = h["_ffn"]
-    roof_traffic = measured_traffic(h["workload"], h["_ffn_prefixes"]) if L == cfg.layers else None
-    roof_gbs = ffn_bytes / (ffn_us * 1e-6) / 1e9
+    ffn_traffic = measured_traffic(h["workload"], h["_ffn_prefixes"]) if L == cfg.layers else None
+    ffn_gbs = ffn_bytes / (ffn_us * 1e-6) / 1e9
 
     cpu = None
     c1_single = None
@@ -702,13 +716,25 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": f"{ffn_label} (pi_sparse_ffn: the listed neurons' up rows with bias and ReLU, their rows "
-                      f"of W_down^T)",
+            "kernel": f"{rest_label} (pi_ffn_layer_from_hidden: second predictor matrix, mask, the listed "
+                      f"neurons' up rows, the down rows they need)",
             "achieved": round(roof_gbs, 1),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(roof_gbs / PEAK_HBM_GBS, 4),
             "traffic": roof_traffic,
+            "bytes_per_launch": round(rest_b),
+            "launch_us": round(rest_us, 3),
+            "launches": int(rest_n),
+        },
+        "active_rows": {
+            "kernel": f"{ffn_label} (pi_sparse_ffn on the same lists: the listed neurons' up rows with bias "
+                      f"and ReLU, their rows of W_down^T)",
+            "achieved": round(ffn_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(ffn_gbs / PEAK_HBM_GBS, 4),
+            "traffic": ffn_traffic,
             "bytes_per_launch": round(ffn_bytes),
             "launch_us": round(ffn_us, 3),
             "launches": int(ffn_n),
