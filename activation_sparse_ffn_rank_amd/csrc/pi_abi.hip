@@ -115,7 +115,31 @@ int down_chunks(int d) {
     return std::min(kDownMaxChunks, std::max(1, ceil_div(kDownTargetTiles, down_slabs(d))));
 }
 
-size_t pred_ws(const pi_predictor *p, int B) { return align_up((size_t)B * p->rank * sizeof(float)); }
+// The first predictor matrix on MFMA (k_pred_l1_mfma, split over d into KS column chunks of cw, then
+// k_zsum) past the GEMV kernels' 8 tokens, where the caller gives a workspace for the chunk sums
+// (pi_predict, the layer entry points; pi_predict_hidden has none and runs the GEMV form in two
+// passes).  Measured on MI355X, pi_predict at 16 tokens: 54.7 -> 48.3 us (49152 neurons), 24.7 ->
+// 21.7 (11008); at 8 tokens the single GEMV pass is as fast.
+constexpr int pred_l1_mfma_from() { return kGemvMaxBatch + 1; }
+struct L1Geom {
+    int KS, cw;
+};
+L1Geom l1_geom(const pi_predictor *p) {
+    const int groups = ceil_div(p->rank, 64);
+    int KS = std::min(64, std::max(1, ceil_div(512, groups)));
+    const int cw = ceil_div(ceil_div(p->d_model, KS), 32) * 32;
+    KS = ceil_div(p->d_model, cw);
+    return L1Geom{KS, cw};
+}
+// z [B][r] fp32, then (batches on MFMA) the chunk sums [KS][B][r]
+size_t pred_ws(const pi_predictor *p, int B) {
+    size_t n = align_up((size_t)B * p->rank * sizeof(float));
+    if (B >= pred_l1_mfma_from()) n += align_up((size_t)l1_geom(p).KS * B * p->rank * sizeof(float));
+    return n;
+}
+float *pred_zpart(const pi_predictor *p, int B, float *z) {
+    return B >= pred_l1_mfma_from() ? z + align_up((size_t)B * p->rank * sizeof(float)) / sizeof(float) : nullptr;
+}
 
 // Sparse-FFN scratch: h [B][max(n_slots,1)] fp32, chunk partials [C][B][d] fp32, slab tickets.
 struct FfnScratch {
@@ -311,8 +335,16 @@ void enqueue_pred_l1_b(const pi_predictor *p, const uint16_t *x, float *z, hipSt
     else enqueue_pred_l1_bu<B, UMAX>(p, x, z, st);
 }
 
-int enqueue_pred_l1(const pi_predictor *p, const void *x, int B, float *z, hipStream_t st) {
+int enqueue_pred_l1(const pi_predictor *p, const void *x, int B, float *z, hipStream_t st, float *zpart = nullptr) {
     const uint16_t *xx = static_cast<const uint16_t *>(x);
+    if (zpart != nullptr && B >= pred_l1_mfma_from()) {
+        const L1Geom g = l1_geom(p);
+        hipLaunchKernelGGL(k_pred_l1_mfma<4>, dim3(ceil_div(p->rank, 64), g.KS), dim3(256), 0, st,
+                           static_cast<const uint16_t *>(p->p1), xx, B, p->d_model, p->rank, g.cw, zpart);
+        if (hipGetLastError() != hipSuccess) return PI_ERR_HIP;
+        hipLaunchKernelGGL(k_zsum, dim3(ceil_div(B * p->rank, 256)), dim3(256), 0, st, zpart, g.KS, B * p->rank, z);
+        return launch_status();
+    }
     if (B > kGemvMaxBatch) {
         // tokens 0..7, then the rest: P1 is read twice, x and z rows are offset
         int rc = enqueue_pred_l1(p, x, kGemvMaxBatch, z, st);
@@ -336,7 +368,7 @@ int enqueue_pred_l1(const pi_predictor *p, const void *x, int B, float *z, hipSt
 
 int enqueue_predict(const pi_predictor *p, const void *x, int B, uint8_t *mask, float *logits, float *z,
                     hipStream_t st) {
-    int rc = enqueue_pred_l1(p, x, B, z, st);
+    int rc = enqueue_pred_l1(p, x, B, z, st, pred_zpart(p, B, z));
     return rc ? rc : enqueue_pred_l2(p, z, B, mask, logits, st);
 }
 
@@ -752,7 +784,7 @@ int pi_ffn_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int
     if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const LayerWs L = layer_ws(pred, ffn, batch, ws);
-    if ((rc = enqueue_pred_l1(pred, x, batch, L.z, st))) return rc;
+    if ((rc = enqueue_pred_l1(pred, x, batch, L.z, st, pred_zpart(pred, batch, L.z)))) return rc;
     return layer_from_hidden(pred, ffn, x, batch, L.z, y, mask_out, idx_out, counts_out, ws, st);
 }
 

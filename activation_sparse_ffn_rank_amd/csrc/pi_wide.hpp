@@ -207,6 +207,64 @@ __device__ __forceinline__ f4 mfma32(const uint4 &a, const uint4 &b, f4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
 }
 
+// Partial z for up to 16 tokens on MFMA (the first predictor matrix, split over d): workgroup
+// (t, ks) covers rows 64t .. 64t+63 of P1 (wave w: 16 rows, the MFMA's n) over columns
+// [ks*cw, min(d, (ks+1)*cw)); per 32-column step lane group g reads columns 32j + 8g .. +8 of its row
+// and of its token's x (the A operand: fp16 as given, so every product is exact) and issues one MFMA.
+// zpart[ks][b][row] receives the chunk's sums (tokens >= B read x as zero and are not stored);
+// k_zsum adds the chunks in order and applies the ReLU.
+template <int KC>
+__global__ __launch_bounds__(256) void k_pred_l1_mfma(const uint16_t *__restrict__ p1, const uint16_t *__restrict__ x,
+                                                      int B, int d, int r, int cw, float *__restrict__ zpart) {
+    const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int n16 = lane & 15, g = lane >> 4;
+    const int row = blockIdx.x * 64 + wave * 16 + n16;
+    const int ks = blockIdx.y;
+    const int c0 = ks * cw, c1 = min(d, c0 + cw);
+    const __amdgpu_buffer_rsrc_t rp = buf_rsrc(p1, (uint32_t)((size_t)r * d * 2));
+    const __amdgpu_buffer_rsrc_t rx = buf_rsrc(x, (uint32_t)B * (uint32_t)d * 2u);
+    const uint32_t prow = row < r ? (uint32_t)row * (uint32_t)d * 2u : kOOB;
+    const uint32_t xrow = n16 < B ? (uint32_t)n16 * (uint32_t)d * 2u : kOOB;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = c0; k0 < c1; k0 += 32 * KC) {
+        uint4 w[KC], xv[KC];
+#pragma unroll
+        for (int j = 0; j < KC; ++j) {
+            const int col = k0 + 32 * j + 8 * g;
+            const bool ok = col < c1;                                  // d and cw are multiples of 8
+            w[j] = bld16(rp, ok ? prow + (uint32_t)col * 2u : kOOB);
+            xv[j] = bld16(rx, ok ? xrow + (uint32_t)col * 2u : kOOB);
+        }
+#pragma unroll
+        for (int j = 0; j < KC; ++j) acc = mfma32(xv[j], w[j], acc);
+    }
+    // D[m = 4g + v][n = n16]: tokens 4g .. 4g+3 of this lane's row
+    if (row < r) {
+        const float av[4] = {acc.x, acc.y, acc.z, acc.w};
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int b = 4 * g + v;
+            if (b < B) zpart[((size_t)ks * B + b) * r + row] = av[v];
+        }
+    }
+}
+
+// z[o] = max(0, sum over ks, in order, of zpart[ks][o]), o < n = B * r.
+static __global__ __launch_bounds__(256) void k_zsum(const float *__restrict__ zpart, int KS, int n,
+                                                     float *__restrict__ z) {
+    const int o = blockIdx.x * 256 + threadIdx.x;
+    if (o >= n) return;
+    float s = 0.f;
+    for (int k0 = 0; k0 < KS; k0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = k0 + k < KS ? zpart[(size_t)(k0 + k) * n + o] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) s += v[k];
+    }
+    z[o] = fmaxf(s, 0.f);
+}
+
 // fp32 -> fp16 pair (hi = fp16(v), lo = fp16(v - hi)) of 8 consecutive values, so that v = hi + lo
 // to ~2^-22 relative and an f16 MFMA over both parts loses nothing against fp32 z.
 __device__ __forceinline__ void split8(const float4 &p, const float4 &q, uint4 &hi, uint4 &lo) {
