@@ -104,7 +104,8 @@ size_t pi_workspace_bytes(const pi_predictor *pred, const pi_ffn *ffn, int32_t b
 
 /* Predictor (method section: online prediction of the neurons that fire).
  * x [batch][d_model] fp16.  mask [d_ffn] u8 receives the batch union {0,1}.  logits
- * [batch][d_ffn] fp32 receives l_b when non-NULL.  Uses the workspace for z. */
+ * [batch][d_ffn] fp32 receives l_b when non-NULL.  Uses the workspace for z (and, past 8 tokens, for
+ * the column-chunk sums of z that the MFMA form adds in order). */
 int pi_predict(const pi_predictor *pred, const void *x, int32_t batch, uint8_t *mask,
                float *logits, void *ws, size_t ws_bytes, void *stream);
 
