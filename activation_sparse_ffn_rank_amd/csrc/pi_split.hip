@@ -53,7 +53,9 @@ int launch_one(SplitArgs &a, hipStream_t st) {
 }
 
 // Grid of k_pred_up: as many workgroups as fit on the chip at once, evened out so that every
-// workgroup takes the same number of tiles (or one fewer).
+// workgroup takes the same number of tiles (or one fewer), at most kPredUpMaxTiles.  (Measured on
+// the 49152 x 1024 predictor: one tile per workgroup, or 3 and 4 per workgroup on fewer
+// workgroups, were all slower than the 2 per workgroup this gives there.)
 template <int B, bool GATED, int WT, int NT>
 int launch_pred_up(PredUpArgs &p, hipStream_t st) {
     const void *kern = reinterpret_cast<const void *>(k_pred_up<B, GATED, WT, NT>);
@@ -61,7 +63,8 @@ int launch_pred_up(PredUpArgs &p, hipStream_t st) {
     int cus = 0, per_cu = 0;
     if (resident_slots(kern, 256, lds, &cus, &per_cu)) return 1;
     const int tiles = (p.f + 31) / 32, slots = cus * per_cu;
-    const int rounds = (tiles + slots - 1) / slots;
+    int rounds = (tiles + slots - 1) / slots;
+    if (rounds > kPredUpMaxTiles) rounds = kPredUpMaxTiles;   // then more workgroups than fit at once
     const int grid = (tiles + rounds - 1) / rounds;
     hipLaunchKernelGGL((k_pred_up<B, GATED, WT, NT>), dim3(grid), dim3(256), lds, st, p);
     return hipGetLastError() == hipSuccess ? 0 : 1;

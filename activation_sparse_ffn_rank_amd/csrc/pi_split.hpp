@@ -540,19 +540,24 @@ __host__ __device__ inline size_t pred_up_lds(int B, int d, int r) {
     return ((size_t)B * d * 2 + 15) / 16 * 16 + (size_t)B * r * 4;
 }
 
+// Tiles of P2 one k_pred_up workgroup takes at most: their listed neurons are handled together
+// after the last tile's logits.
+constexpr int kPredUpMaxTiles = 8;
+
 template <int B, bool GATED, int WT, int NT>
 __global__ __launch_bounds__(256) void k_pred_up(PredUpArgs a) {
     constexpr int R = 8, RH = 4;                          // P2 rows per wave (the tile: 4 x 8), in two halves
     extern __shared__ __align__(16) uint16_t dynx[];
-    __shared__ uint32_t s_words[4];
-    __shared__ uint32_t s_live;
-    __shared__ int s_slot[32];
+    __shared__ uint32_t s_bytes[kPredUpMaxTiles][4];      // per tile, per wave: listed rows of the wave's eight
+    __shared__ uint32_t s_live[kPredUpMaxTiles];
+    __shared__ int s_slot[kPredUpMaxTiles][32];
     const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int ntiles = (a.f + 31) / 32;
     const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.p2, (uint32_t)((size_t)a.f * a.r * 2));
     // the two halves of this wave's rows of P2 (rows 0-3 and 4-7 of its eight); each half is
     // reloaded with the next tile's rows as soon as its logits are formed, so a wave always has
-    // P2 loads in flight while it computes
+    // P2 loads in flight while it computes (two tiles in flight measured slower: the registers
+    // cost a third of the resident waves)
     uint4 w0[RH][NT], w1[RH][NT];
     auto issue = [&](uint4 (&w)[RH][NT], int t, int h) {
         const int row0 = t * 32 + wave * R + h * RH;
@@ -590,25 +595,22 @@ __global__ __launch_bounds__(256) void k_pred_up(PredUpArgs a) {
         }
     };
     const int G = gridDim.x;
-    int t = blockIdx.x;
     SPLIT_TRACE(1);
-    if (threadIdx.x == 0) s_live = 0u;
-    issue(w0, t, 0);
-    issue(w1, t, 1);
+    if (threadIdx.x < kPredUpMaxTiles) s_live[threadIdx.x] = 0u;
+    issue(w0, blockIdx.x, 0);
+    issue(w1, blockIdx.x, 1);
     uint16_t *xs = dynx;
     float *zs = reinterpret_cast<float *>(dynx + ((size_t)B * a.d + 7) / 8 * 8);
     stage_x<B, WT == WT_Q4_0>(xs, a.x, a.d, 0, a.d, a.d);
     stage_vec16(zs, a.z, B * a.r / 4);
     __syncthreads();
-    int tn = t + G;
     SPLIT_TRACE(2);
-    int it = 0;
-    using P = RowPass<B, GATED, WT>;
-    const int64_t in_stride = GATED ? 2 * a.row_bytes : a.row_bytes;
-    const __amdgpu_buffer_rsrc_t rin = buf_rsrc(a.w_in, (uint32_t)(a.n_slots * in_stride));
-    const bool pairs = WT == WT_F16 && P::extent(a.d) <= P::STEP;
-    while (t < ntiles) {
-        // lanes 8k .. 8k+7 end up with row k of the wave's eight (reduce-scatter below); they load
+    // 1. the logits of every tile of this workgroup (tiles blockIdx.x, +G, +2G, ...): mask flags to
+    //    memory, listed rows and their slots to LDS (entry nt for the nt-th tile); the waves need
+    //    not meet between tiles
+    int nt = 0;
+    for (int t = blockIdx.x; t < ntiles && nt < kPredUpMaxTiles; t += G, ++nt) {   // the launch gives no workgroup more tiles
+        // lanes 8j .. 8j+7 end up with row j of the wave's eight (reduce-scatter below); they load
         // that row's offset and slot now
         const int rowk = t * 32 + wave * R + (lane >> 3);
         const bool rok = rowk < a.f;
@@ -620,94 +622,106 @@ __global__ __launch_bounds__(256) void k_pred_up(PredUpArgs a) {
 #pragma unroll
             for (int i = 0; i < R; ++i) v[b][i] = 0.f;
         dots(w0, zs, v, 0);
-        issue(w0, tn, 0);
+        issue(w0, t + G, 0);
         dots(w1, zs, v, 1);
-        issue(w1, tn, 1);
+        issue(w1, t + G, 1);
         const float ci = half_to_float(cbits);
         bool fired = false;
 #pragma unroll
         for (int b = 0; b < B; ++b) fired |= reduce_scatter<R>(v[b], lane) + ci > 0.f;
-        // bit 8k of the ballot = row k fired (its eight lanes agree)
+        // bit 8j of the ballot = row j fired (its eight lanes agree)
         const uint64_t fb = __ballot(fired && rok);
         const bool resident = slot >= 0 && slot < a.n_slots;
         const uint64_t rb8 = __ballot(rok && resident);
         uint32_t mb = 0, byte = 0;
 #pragma unroll
-        for (int k = 0; k < R; ++k) {
-            mb |= (uint32_t)((fb >> (8 * k)) & 1u) << k;
-            byte |= (uint32_t)((fb & rb8) >> (8 * k) & 1u) << k;
+        for (int j = 0; j < R; ++j) {
+            mb |= (uint32_t)((fb >> (8 * j)) & 1u) << j;
+            byte |= (uint32_t)((fb & rb8) >> (8 * j) & 1u) << j;
         }
         if ((lane & 7) == 0 && rok) a.mask[rowk] = (uint8_t)((mb >> (lane >> 3)) & 1u);
-        if ((lane & 7) == 0) s_slot[wave * R + (lane >> 3)] = resident ? slot : -1;
-        if (lane == 0) s_words[wave] = byte;
-        __syncthreads();
-        const uint32_t word = s_words[0] | (s_words[1] << 8) | (s_words[2] << 16) | (s_words[3] << 24);
-        if (it < 2) SPLIT_TRACE(3 + 2 * it);
-        // listed neurons in ascending order: wave w takes the w-th, (w+4)-th, ...; for fp16 rows that
-        // one pass covers, a wave reads two neurons' rows at once (Q4_0 tiles list ~1-2 neurons, and
-        // the second row's registers would cost occupancy)
-        const int cnt = __builtin_popcount(word);
-        for (int j = wave; j < cnt; j += pairs ? 8 : 4) {
-            const int j2 = j + 4;
-            const bool two = pairs && j2 < cnt;
-            int bit = 0, bit2 = 0;
-            {
-                uint32_t bw = word;
-                for (int q = 0; q < j; ++q) bw &= bw - 1;
-                bit = __builtin_ctz(bw);
-                if (two) {
-                    for (int q = j; q < j2; ++q) bw &= bw - 1;
-                    bit2 = __builtin_ctz(bw);
-                }
-            }
-            const int s1 = s_slot[bit], s2 = two ? s_slot[bit2] : 0;
-            float ag[B], au[B], ag2[B], au2[B];
-#pragma unroll
-            for (int b = 0; b < B; ++b) ag[b] = au[b] = ag2[b] = au2[b] = 0.f;
-            if (pairs) {
-                const int d2 = two ? a.d : 0;             // a missing second neuron reads nothing
-                P q1, q2;
-                q1.issue_buf(rin, (uint32_t)(s1 * in_stride), a.row_bytes, a.d, 0, lane);
-                q2.issue_buf(rin, (uint32_t)(s2 * in_stride), a.row_bytes, d2, 0, lane);
-                q1.consume(xs, a.d, a.d, 0, lane, ag, au);
-                q2.consume(xs, a.d, d2, 0, lane, ag2, au2);
-            } else {
-                neuron_dots<B, GATED, WT>(a.w_in + (int64_t)s1 * in_stride, a.row_bytes, a.d, xs, a.d, lane, ag, au);
-            }
-#pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                if (n == 1 && !two) break;                // wave-uniform
-                const int sl = n == 0 ? s1 : s2, id = t * 32 + (n == 0 ? bit : bit2);
-                const float bias = (!GATED && a.b_up != nullptr) ? half_to_float(a.b_up[sl]) : 0.f;
-                bool live = false;
-#pragma unroll
-                for (int b = 0; b < B; ++b) {
-                    const float u = wave_sum(n == 0 ? au[b] : au2[b]);
-                    float hv;
-                    if (GATED) {
-                        hv = fmaxf(wave_sum(n == 0 ? ag[b] : ag2[b]), 0.f) * u;
-                    } else {
-                        hv = fmaxf(u + bias, 0.f);
-                        if (a.act) hv *= hv;              // squared ReLU
-                    }
-                    live |= hv != 0.f;
-                    if (lane == 0) a.h[(size_t)b * a.f + id] = hv;
-                }
-                if (lane == 0 && live) atomicOr(&s_live, 1u << (n == 0 ? bit : bit2));
-            }
-        }
-        // the tile's word of live flags (listed, and h nonzero for some token): the down rows to read;
-        // s_slot, s_words and s_live are reused by the next tile only after this barrier
-        __syncthreads();
-        if (it < 2) SPLIT_TRACE(4 + 2 * it);
-        ++it;
-        if (threadIdx.x == 0) {
-            a.bits[t] = s_live;
-            s_live = 0u;
-        }
-        t = tn;
-        tn += G;
+        if ((lane & 7) == 0) s_slot[nt][wave * R + (lane >> 3)] = resident ? slot : -1;
+        if (lane == 0) s_bytes[nt][wave] = byte;
     }
+    __syncthreads();
+    SPLIT_TRACE(3);
+    // 2. the listed neurons of all those tiles, tile by tile in ascending id: wave w takes the
+    //    (8p+w)-th and (8p+w+4)-th for p = 0, 1, ... (two rows in flight per wave where one pass
+    //    covers a row; the P2 registers are free by now), else the (4p+w)-th
+    auto word_of = [&](int k) {
+        return s_bytes[k][0] | (s_bytes[k][1] << 8) | (s_bytes[k][2] << 16) | (s_bytes[k][3] << 24);
+    };
+    int total = 0;
+    for (int k = 0; k < nt; ++k) total += __builtin_popcount(word_of(k));
+#ifdef PIK_TRACE
+    if (a.trace != nullptr && threadIdx.x == 0) {
+        a.trace[(size_t)blockIdx.x * 8 + 5] = (uint64_t)total;
+        a.trace[(size_t)blockIdx.x * 8 + 6] = (uint64_t)nt;
+    }
+#endif
+    // tile and bit of the j-th listed neuron (j < total)
+    auto locate = [&](int j, int &k, int &bit) {
+        for (k = 0;; ++k) {
+            const uint32_t w = word_of(k);
+            const int c = __builtin_popcount(w);
+            if (j < c) {
+                bit = select_bit(w, j);
+                return;
+            }
+            j -= c;
+        }
+    };
+    using P = RowPass<B, GATED, WT>;
+    const int64_t in_stride = GATED ? 2 * a.row_bytes : a.row_bytes;
+    const __amdgpu_buffer_rsrc_t rin = buf_rsrc(a.w_in, (uint32_t)(a.n_slots * in_stride));
+    const bool pairs = P::extent(a.d) <= P::STEP;
+    for (int j = wave; j < total; j += pairs ? 8 : 4) {
+        const int j2 = j + 4;
+        const bool two = pairs && j2 < total;
+        int k1, bit1, k2 = 0, bit2 = 0;
+        locate(j, k1, bit1);
+        if (two) locate(j2, k2, bit2);
+        const int s1 = s_slot[k1][bit1], s2 = two ? s_slot[k2][bit2] : 0;
+        float ag[B], au[B], ag2[B], au2[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) ag[b] = au[b] = ag2[b] = au2[b] = 0.f;
+        if (pairs) {
+            const int d2 = two ? a.d : 0;                 // a missing second neuron reads nothing
+            P q1, q2;
+            q1.issue_buf(rin, (uint32_t)(s1 * in_stride), a.row_bytes, a.d, 0, lane);
+            q2.issue_buf(rin, (uint32_t)(s2 * in_stride), a.row_bytes, d2, 0, lane);
+            q1.consume(xs, a.d, a.d, 0, lane, ag, au);
+            q2.consume(xs, a.d, d2, 0, lane, ag2, au2);
+        } else {
+            neuron_dots<B, GATED, WT>(a.w_in + (int64_t)s1 * in_stride, a.row_bytes, a.d, xs, a.d, lane, ag, au);
+        }
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            if (n == 1 && !two) break;                    // wave-uniform
+            const int sl = n == 0 ? s1 : s2, kk = n == 0 ? k1 : k2, bit = n == 0 ? bit1 : bit2;
+            const int id = (blockIdx.x + kk * G) * 32 + bit;
+            const float bias = (!GATED && a.b_up != nullptr) ? half_to_float(a.b_up[sl]) : 0.f;
+            bool live = false;
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const float u = wave_sum(n == 0 ? au[b] : au2[b]);
+                float hv;
+                if (GATED) {
+                    hv = fmaxf(wave_sum(n == 0 ? ag[b] : ag2[b]), 0.f) * u;
+                } else {
+                    hv = fmaxf(u + bias, 0.f);
+                    if (a.act) hv *= hv;                  // squared ReLU
+                }
+                live |= hv != 0.f;
+                if (lane == 0) a.h[(size_t)b * a.f + id] = hv;
+            }
+            if (lane == 0 && live) atomicOr(&s_live[kk], 1u << bit);
+        }
+    }
+    // 3. each tile's word of live flags (listed, and h nonzero for some token): the down rows to read
+    __syncthreads();
+    SPLIT_TRACE(4);
+    if (threadIdx.x < nt) a.bits[blockIdx.x + threadIdx.x * G] = s_live[threadIdx.x];
     SPLIT_TRACE(0);
 }
 
