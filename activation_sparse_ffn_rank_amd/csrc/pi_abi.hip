@@ -9,6 +9,7 @@
 #include "pi_split.hpp"
 #include "pi_tail.hpp"
 #include "pi_wide.hpp"
+#include "pi_occupancy.hpp"
 
 #include <algorithm>
 #include <mutex>
@@ -85,12 +86,13 @@ int x_chunk(int d, int B) {
 int down_slabs(int d) { return ceil_div(d, 512); }
 
 // Workspace of pi_sparse_ffn_wide: a status word (its first int32; 256 bytes reserved), slab
-// tickets, h as fp16 hi and lo parts [16][hs], and the chunk partials [C][B][d] fp32.
+// tickets, h as fp16 hi and lo parts [16][hs], the chunk partials [C][B][d] fp32, and for Q4_0 rows
+// x in k_wide_up's operand order (d*32 bytes).
 constexpr int kWideTargetGroups = 256;   // (slab, chunk) workgroups of k_wide_down (8 waves each)
 constexpr size_t kWideStatusBytes = 256;
 struct WideGeom {
     int S, C, hs;
-    size_t tick, hi, lo, part, total;
+    size_t tick, hi, lo, part, xmf, total;
 };
 WideGeom wide_geom(const pi_ffn *fn, int B) {
     WideGeom g{};
@@ -106,7 +108,8 @@ WideGeom wide_geom(const pi_ffn *fn, int B) {
     g.hi = g.tick + align_up((size_t)g.S * 4);
     g.lo = g.hi + align_up((size_t)kWideB * g.hs * 2);
     g.part = g.lo + align_up((size_t)kWideB * g.hs * 2);
-    g.total = g.part + align_up((size_t)g.C * B * d * 4);
+    g.xmf = g.part + align_up((size_t)g.C * B * d * 4);
+    g.total = g.xmf + (fn->wtype == PI_Q4_0 ? align_up((size_t)d * 32) : 0);
     return g;
 }
 int check_wide_batch(int32_t B) { return (B >= 1 && B <= PI_MAX_WIDE_BATCH) ? PI_OK : PI_ERR_BATCH; }
@@ -501,16 +504,28 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
     const uint8_t *w_in = static_cast<const uint8_t *>(fn->w_in);
     const uint16_t *xx = static_cast<const uint16_t *>(x), *b_up = static_cast<const uint16_t *>(fn->b_up);
     const dim3 up_grid(std::max(1, ceil_div(ns, 16)));
-    if (fn->wtype == PI_Q4_0)
-        hipLaunchKernelGGL((k_wide_up<false, WT_Q4_0, 2>), dim3(std::max(1, ceil_div(ns, 32))), dim3(kWideThreads), 0,
-                           st, w_in, rb, d, b_up, xx, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets,
-                           g.S, fn->act, status);
-    else if (fn->gated)
+    if (fn->wtype == PI_Q4_0) {
+        uint4 *xmf = reinterpret_cast<uint4 *>(w + g.xmf);
+        hipLaunchKernelGGL(k_wide_xmf, dim3(ceil_div(2 * d, 256)), dim3(256), 0, st, xx, B, d, xmf);
+        int cus = 0, per_cu = 0;
+        if ((int64_t)ns * rb < (int64_t)kBufMax &&
+            resident_slots(reinterpret_cast<const void *>(k_wide_up_q4), kWideUpWaves * kWave, 0, &cus, &per_cu) == 0) {
+            WideUpQ4Args ua{w_in, rb, d, B, f, ns, g.hs, fn->act, b_up, xmf, idx, fn->slot_of, h_hi, h_lo, status};
+            hipLaunchKernelGGL(k_wide_up_q4, dim3(cus), dim3(kWideUpWaves * kWave), 0, st, ua, counts, tickets, g.S);
+        }
+        else
+            hipLaunchKernelGGL((k_wide_up<false, WT_Q4_0, 2>), dim3(std::max(1, ceil_div(ns, 32))), dim3(kWideThreads),
+                               0, st, w_in, rb, d, b_up, xx, xmf, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs,
+                               tickets, g.S, fn->act, status);
+    } else if (fn->gated) {
         hipLaunchKernelGGL((k_wide_up<true, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
-                           B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, fn->act, status);
-    else
+                           nullptr, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, fn->act,
+                           status);
+    } else {
         hipLaunchKernelGGL((k_wide_up<false, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
-                           B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, fn->act, status);
+                           nullptr, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, fn->act,
+                           status);
+    }
     const uint8_t *w_dn = static_cast<const uint8_t *>(fn->w_down_t);
     const uint16_t *b_dn = static_cast<const uint16_t *>(fn->b_down);
     if (fn->wtype == PI_Q4_0)

@@ -15,6 +15,9 @@
 // the kernels use to make every lane's loads contiguous.
 //
 // Kernels (stream-ordered):
+//   k_wide_xmf   (Q4_0 rows) x copied once into the B-operand order of k_wide_up's MFMAs, so that
+//                each of k_wide_up's x loads is one contiguous 1 KB line-aligned run for the wave
+//                (read in place, the 16 tokens' rows made every load touch 32 cache lines).
 //   k_wide_up    one workgroup per 16 listed neurons: H tile [16 tokens x 16 neurons] over all d,
 //                the eight waves taking interleaved 256-column blocks, summed in LDS; writes h
 //                as fp16 hi + fp16 lo parts (h = hi + lo to ~2^-22 relative), so that feeding h to
@@ -49,6 +52,18 @@ __device__ __forceinline__ f4 mfma16(uint32_t a0, uint32_t a1, uint32_t b0, uint
     return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
 }
 
+// x in k_wide_up's Q4_0 operand order: 16-byte vector ((kq*4 + i)*4 + g)*16 + r holds tokens r's
+// columns 32(4kq + g) + 8i .. +8, re-paired for q4pair (pair_for_q4), or zeros for a token r >= B;
+// 2d vectors (d*32 bytes), one thread each.  Lane r + 16g of a wave then reads the vectors of block
+// 4kq + g for its token r: a wave's load for one (kq, i) is 64 consecutive vectors.
+__global__ __launch_bounds__(256) void k_wide_xmf(const uint16_t *__restrict__ x, int B, int d,
+                                                  uint4 *__restrict__ xmf) {
+    const int v = blockIdx.x * 256 + threadIdx.x;
+    if (v >= 2 * d) return;
+    const int kq = v >> 8, i = (v >> 6) & 3, g = (v >> 4) & 3, r = v & 15;
+    xmf[v] = r < B ? pair_for_q4(ld16(x + (size_t)r * d + (4 * kq + g) * 32 + 8 * i)) : zero4();
+}
+
 // h[b][k] for the listed neurons, as fp16 hi and lo parts in [16][hs] arrays.  Workgroup t holds
 // list positions 16t .. 16t+15; lane l of every wave works on position 16t + l%16 and token l%16
 // (the MFMA's n and m) and columns blk + 32j + 8(l/16) .. +8 of block blk (j < 8), so each of a
@@ -60,7 +75,7 @@ __device__ __forceinline__ f4 mfma16(uint32_t a0, uint32_t a1, uint32_t b0, uint
 template <bool GATED, int WT, int NT>
 __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restrict__ w_in, int64_t row_bytes, int d,
                                                  const uint16_t *__restrict__ b_up, const uint16_t *__restrict__ x,
-                                                 int B, const int32_t *__restrict__ idx,
+                                                 const uint4 *__restrict__ xmf, int B, const int32_t *__restrict__ idx,
                                                  const int32_t *__restrict__ counts,
                                                  const int32_t *__restrict__ slot_of, int f, int n_slots,
                                                  uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int hs,
@@ -94,8 +109,8 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
         // Q4_0 (d % 256 == 0, so every block of the 256 columns exists): lane group g takes the
         // 32-weight blocks blk/32 + g + 4j (j < 2) of each of its NT rows, one 16-byte code load and
         // one scale each; the codes become exact fp16 (code - 8) pairs, times the block's scale (one
-        // fp16 rounding), and x -- read once for the NT rows -- is re-paired to the codes' order, so
-        // each code word feeds two MFMAs
+        // fp16 rounding), and x -- read once for the NT rows, from xmf, already re-paired to the
+        // codes' order -- feeds two MFMAs per code word
         uint4 cw[NT][2], xq[2][4];
         uint32_t sc[NT][2];
 #pragma unroll
@@ -108,13 +123,13 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
                 sc[u][j] = *reinterpret_cast<const uint16_t *>(ru + d / 2 + (int64_t)kb * 2);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xq[j][i] = bld16(xr, xrow + (uint32_t)(kb * 32 + 8 * i) * 2u);
+            for (int i = 0; i < 4; ++i) xq[j][i] = ld16(xmf + ((blk / 128 + j) * 4 + i) * kWave + lane);
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint4 xp = pair_for_q4(xq[j][q]);
+                const uint4 xp = xq[j][q];
 #pragma unroll
                 for (int u = 0; u < NT; ++u) {
                     const h2 s2 = __builtin_bit_cast(h2, sl[u] >= 0 ? (sc[u][j] | (sc[u][j] << 16)) : 0u);
@@ -195,6 +210,128 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
     const f16 lo = (f16)(hv - (float)hi);
     h_hi[(size_t)b * hs + pt] = __builtin_bit_cast(uint16_t, hi);
     h_lo[(size_t)b * hs + pt] = __builtin_bit_cast(uint16_t, lo);
+}
+
+// The Q4_0 form of k_wide_up on a grid of one kWideUpWaves-wave workgroup per compute unit: the
+// ceil(n/16) 16-position tiles are split into gridDim.x contiguous, even runs (one tile more or
+// less), and a workgroup sweeps d once per pass of NT tiles (3 or 4: its run in the fewest passes,
+// evened out), the waves taking interleaved 256-column blocks and sharing each x load among the
+// NT tiles as above.  On one workgroup per 32 neurons, the units that drew two workgroups set the
+// time; here every unit gets the same count of neurons.  Rows are read through a buffer resource
+// over w_in (n_slots * row_bytes < kBufMax), so absent positions read nothing.
+constexpr int kWideUpWaves = 12;
+constexpr int kWideUpMaxNT = 4;
+
+struct WideUpQ4Args {
+    const uint8_t *w_in;
+    int64_t row_bytes;
+    int d, B, f, n_slots, hs, act;
+    const uint16_t *b_up;
+    const uint4 *xmf;
+    const int32_t *idx, *slot_of;
+    uint16_t *h_hi, *h_lo;
+    int32_t *status;
+};
+
+// One pass: tiles t0 .. t0+NT-1 of the run ending at t_hi (n listed positions).
+template <int NT>
+__device__ __forceinline__ void wide_up_q4_pass(const WideUpQ4Args &a, __amdgpu_buffer_rsrc_t rw, int n, int t0,
+                                                int t_hi, f4 (*red)[kWideUpWaves][kWave]) {
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int r = lane & 15, g = lane >> 4, d = a.d;
+    int sl[NT];
+    uint32_t base[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+        const int pu = (t0 + u) * 16 + r;
+        sl[u] = (t0 + u < t_hi && pu < n) ? slot_of_id(a.idx[pu], a.slot_of, a.f, a.n_slots) : -1;
+        base[u] = sl[u] >= 0 ? (uint32_t)(sl[u] * a.row_bytes) : kOOB;
+    }
+    f4 aq[NT];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) aq[u] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int blk = wave * kWideUpCols; blk < d; blk += kWideUpWaves * kWideUpCols) {
+        uint4 cw[NT][2], xq[2][4];
+        uint32_t sc[NT][2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t kb = (uint32_t)(blk / 32 + g + 4 * j);
+#pragma unroll
+            for (int u = 0; u < NT; ++u) {
+                cw[u][j] = bld16(rw, base[u] + kb * 16u);
+                sc[u][j] = bld2(rw, base[u] + (uint32_t)(d / 2) + kb * 2u);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xq[j][i] = ld16(a.xmf + ((blk / 128 + j) * 4 + i) * kWave + lane);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint4 xp = xq[j][q];
+#pragma unroll
+                for (int u = 0; u < NT; ++u) {
+                    const h2 s2 = __builtin_bit_cast(h2, sc[u][j] | (sc[u][j] << 16));
+                    const uint32_t wd = q == 0 ? cw[u][j].x : q == 1 ? cw[u][j].y : q == 2 ? cw[u][j].z : cw[u][j].w;
+                    uint32_t w[4];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        w[p] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2, q4pair(wd, 4 * p)) * s2);
+                    aq[u] = mfma16(xp.x, xp.y, w[0], w[1], aq[u]);
+                    aq[u] = mfma16(xp.z, xp.w, w[2], w[3], aq[u]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < NT; ++u) red[u][wave][lane] = aq[u];
+    __syncthreads();
+    // (tile, v) pairs e = 4 tile + v go round the waves; lane l of the wave takes D element v of lane
+    // l of that tile = token 4(l/16) + v, position 16(t0 + tile) + l%16 -- a position whose slot
+    // this thread looked up itself (sl[tile])
+    for (int e = wave; e < NT * 4; e += kWideUpWaves) {
+        const int tile = e >> 2, v = e & 3, l = lane;
+        const int b = 4 * (l >> 4) + v;
+        float u = 0.f;
+#pragma unroll
+        for (int w = 0; w < kWideUpWaves; ++w) u += red[tile][w][l][v];
+        int st = -1;
+#pragma unroll
+        for (int k = 0; k < NT; ++k)
+            if (k == tile) st = sl[k];
+        const float bias = (a.b_up != nullptr && st >= 0) ? half_to_float(a.b_up[st]) : 0.f;
+        float hv = fmaxf(u + bias, 0.f);
+        if (a.act) hv *= hv;                                     // squared ReLU
+        if (st < 0 || b >= a.B) hv = 0.f;
+        if (!(fabsf(hv) < 65504.f)) atomicOr(a.status, kStatusHRange);
+        if (t0 + tile < t_hi) {
+            const int pt = (t0 + tile) * 16 + r;
+            const f16 hi = (f16)hv;
+            const f16 lo = (f16)(hv - (float)hi);
+            a.h_hi[(size_t)b * a.hs + pt] = __builtin_bit_cast(uint16_t, hi);
+            a.h_lo[(size_t)b * a.hs + pt] = __builtin_bit_cast(uint16_t, lo);
+        }
+    }
+    __syncthreads();                                             // red is refilled by the next pass
+}
+
+__global__ __launch_bounds__(kWideUpWaves * kWave) void k_wide_up_q4(WideUpQ4Args a, const int32_t *__restrict__ counts,
+                                                                    int32_t *__restrict__ zero_ptr, int nzero) {
+    __shared__ f4 red[kWideUpMaxNT][kWideUpWaves][kWave];
+    if (blockIdx.x == 0)
+        for (int t = threadIdx.x; t < nzero; t += blockDim.x) zero_ptr[t] = 0;
+    const int n = min(max(counts[0], 0), a.n_slots);
+    const int T = (n + 15) / 16, G = gridDim.x;
+    const int t_lo = (int)((int64_t)T * blockIdx.x / G), t_hi = (int)((int64_t)T * (blockIdx.x + 1) / G);
+    const int len = t_hi - t_lo;
+    if (len <= 0) return;                                        // workgroup-uniform
+    const __amdgpu_buffer_rsrc_t rw = buf_rsrc(a.w_in, (uint32_t)(a.n_slots * a.row_bytes));
+    const int passes = (len + kWideUpMaxNT - 1) / kWideUpMaxNT;
+    const int per = (len + passes - 1) / passes;                 // tiles per pass, <= 4
+    for (int t0 = t_lo; t0 < t_hi; t0 += per) {
+        if (per <= 3) wide_up_q4_pass<3>(a, rw, n, t0, min(t0 + per, t_hi), red);
+        else wide_up_q4_pass<4>(a, rw, n, t0, min(t0 + per, t_hi), red);
+    }
 }
 
 // ------------------------------------------------------------------------------ predictor on MFMA

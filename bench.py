@@ -152,6 +152,9 @@ def ffn_kernel_names(h_kind: int, B: int, cfg, synth):
     if h_kind == 2:
         return "k_sparse_up + k_sparse_down", [f"void pik::k_sparse_up<{B}, {g}, {w}>", f"void pik::k_sparse_down<{B}, {w}>"]
     if h_kind == 3:
+        if cfg.wtype != synth.F16:                              # x re-laid out for the Q4_0 MFMA operands first
+            return "k_wide_xmf + k_wide_up + k_wide_down", ["pik::k_wide_xmf(", "void pik::k_wide_up<",
+                                                            "void pik::k_wide_down<"]
         return "k_wide_up + k_wide_down", ["void pik::k_wide_up<", "void pik::k_wide_down<"]
     return f"kind {h_kind}", []
 
@@ -451,12 +454,13 @@ def wide_leg(torch, _abi, cfg, layers, xd, masks, cases, stream, dev, in_rows, r
         ms, _ = timed_graph(torch, stream, run_wide)
         wide_us = ms * 1000.0 / L
     n_w = cnt_w[:, 0].cpu().numpy().astype(np.float64)
+    q4 = rb < 2 * cfg.d                                          # Q4_0 rows are shorter than fp16 ones
     wide_bytes = float((n_w * (in_rows + 1) * rb + 4 * n_w).mean()) + 16 * cfg.d * (2 + 4) + 2 * cfg.d
     return {"batch": 16, "us_per_layer": round(wide_us, 3), "neurons_per_layer": round(float(n_w.mean()), 1),
             "algorithmic_bytes_per_layer": int(wide_bytes),
             "gbs": round(wide_bytes / (wide_us * 1e-6) / 1e9, 1),
             "hbm_frac": round(wide_bytes / (wide_us * 1e-6) / 8e12, 4),
-            "kernels": "k_wide_up + k_wide_down (pi_sparse_ffn_wide, MFMA f16)"}
+            "kernels": ("k_wide_xmf + " if q4 else "") + "k_wide_up + k_wide_down (pi_sparse_ffn_wide, MFMA f16)"}
 
 
 def cpu_oracle(synth, oracle, cfg, L, B, tokens, budget_s, threads=None):
