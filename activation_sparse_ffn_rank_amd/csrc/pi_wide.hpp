@@ -15,13 +15,14 @@
 // the kernels use to make every lane's loads contiguous.
 //
 // Kernels (stream-ordered):
-//   k_wide_xmf   (Q4_0 rows) x copied once into the B-operand order of k_wide_up's MFMAs, so that
-//                each of k_wide_up's x loads is one contiguous 1 KB line-aligned run for the wave
-//                (read in place, the 16 tokens' rows made every load touch 32 cache lines).
+//   k_wide_xmf   (Q4_0 rows) x copied once into the A-operand order of the up step's MFMAs, so that
+//                each of the up step's x loads is one contiguous 1 KB run for the wave (read in
+//                place, the 16 tokens' rows made every load touch 32 cache lines).
 //   k_wide_up    one workgroup per 16 listed neurons: H tile [16 tokens x 16 neurons] over all d,
 //                the eight waves taking interleaved 256-column blocks, summed in LDS; writes h
 //                as fp16 hi + fp16 lo parts (h = hi + lo to ~2^-22 relative), so that feeding h to
-//                the f16 MFMA of the down step costs no accuracy.
+//                the f16 MFMA of the down step costs no accuracy.  On Q4_0 rows k_wide_up_q4 does
+//                the same on one workgroup per compute unit, each taking an even run of tiles.
 //   k_wide_down  (slab, neuron chunk) tiles: Y tile [16 tokens x 128 (Q4_0: 256) columns] over the
 //                chunk's neurons, waves summed in LDS, chunk partials summed in chunk order by the
 //                last workgroup of each slab (deterministic), plus b_down.
@@ -40,7 +41,8 @@ constexpr int kStatusHRange = 64;     // status bit: some |h| reached 65504 (out
 // columns per lane per row in k_wide_down (a slab is 16 lanes wide)
 constexpr int wide_down_cpl(int wt) { return wt == WT_Q4_0 ? 16 : 8; }
 constexpr int kWideMaxChunks = 16;    // chunk partials per slab summed by the last workgroup
-constexpr int kWideWaves = 8;         // waves per workgroup in both kernels
+constexpr int kWideWaves = 8;         // waves per workgroup in both kernels (fp16 rows)
+constexpr int kWideDownWaves = 12;    // ... and in k_wide_down on Q4_0 rows
 constexpr int kWideThreads = kWideWaves * kWave;
 
 typedef f16 h4 __attribute__((ext_vector_type(4)));
@@ -495,17 +497,18 @@ __global__ __launch_bounds__(256) void k_pred_l2_mfma(const uint16_t *__restrict
 // y over (slab, neuron chunk) tiles (xmap: the XCD-grouped 1-D grid described below, else a 2-D grid
 // of S x C); a slab is 16 lanes x CPL columns (fp16: 8 columns, one 16-byte
 // load per row; Q4_0: 16 columns, 8 code bytes and a scale per row, so 16 lanes read a whole 128-byte
-// line of a row's codes).  The chunk's 16-position steps are split into eight contiguous runs, one
-// per wave.  In a step, lane l reads its CPL columns of the rows of positions 4(l/16) + v (v < 4)
+// line of a row's codes).  The chunk's 16-position steps are split into W contiguous runs, one per
+// wave.  In a step, lane l reads its CPL columns of the rows of positions 4(l/16) + v (v < 4)
 // and h of token l%16 at the same four positions; MFMA e then takes half e of each of the four
 // rows' decoded vectors as its B operand.  Slots are looked up 64 positions at a time, one lane per
 // position, and handed to the lanes that need them by ds_bpermute.  The waves' tiles meet in LDS
-// (eight MFMA outputs at a time), each chunk's partial goes to `part` ([C][B][d] fp32), and the last
+// (eight MFMA outputs at a time, summed in wave order), each chunk's partial goes to `part`
+// ([C][B][d] fp32; C is the launch's chunk count, at most the workspace's), and the last
 // workgroup to finish a slab (slab ticket) sums the partials in chunk order and adds b_down, each
 // thread issuing the loads of four outputs before the first add.  Tickets must be zero on entry
 // (k_wide_up clears them) and are left zero.
-template <int WT>
-__global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__restrict__ w_dn, int64_t row_bytes,
+template <int WT, int W = kWideWaves>
+__global__ __launch_bounds__(W * kWave) void k_wide_down(const uint8_t *__restrict__ w_dn, int64_t row_bytes,
                                                             int d, int B, const int32_t *__restrict__ idx,
                                                             const int32_t *__restrict__ counts,
                                                             const int32_t *__restrict__ slot_of, int f, int n_slots,
@@ -523,19 +526,19 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
     if (xmap) {
         // Q4_0: the scales of 8 consecutive slabs share one 128-byte line, so those 8 workgroups go to
         // one XCD (workgroups are dealt to the 8 XCDs round robin) and meet in its L2 instead of each
-        // XCD fetching the line.  1-D grid of 8*ceil(S/8)*C workgroups, C a multiple of 8: XCD x takes
-        // the (slab group, chunk) pairs x, x + 8, ..., each as 8 consecutive workgroups.
+        // XCD fetching the line.  1-D grid of 64*ceil(ceil(S/8)*C/8) workgroups: XCD x takes the
+        // (slab group, chunk) pairs x, x + 8, ..., each as 8 consecutive workgroups of its share.
         const int L = blockIdx.x, x = L & 7, q = L >> 3;
         const int j = q & 7, pp = (q >> 3) * 8 + x;
         const int ng = (S + 7) / 8;
         slab = (pp % ng) * 8 + j;
         ck = pp / ng;
-        if (slab >= S) return;                                   // padding of the last group
+        if (slab >= S || ck >= C) return;                        // padding: the last group, the last pairs
     }
     const int n = min(max(counts[0], 0), n_slots);
     const int T = (n + 15) / 16;                                 // 16-position steps
     const int c_lo = (int)((int64_t)T * ck / C), c_hi = (int)((int64_t)T * (ck + 1) / C);
-    const int w_lo = c_lo + (c_hi - c_lo) * wave / kWideWaves, w_hi = c_lo + (c_hi - c_lo) * (wave + 1) / kWideWaves;
+    const int w_lo = c_lo + (c_hi - c_lo) * wave / W, w_hi = c_lo + (c_hi - c_lo) * (wave + 1) / W;
     const int r = lane & 15, g = lane >> 4;
     const int col = slab * SC + CPL * r;
     const bool colok = col < d;                                  // d % 8 (fp16) or % 256 (Q4_0): all or none
@@ -616,15 +619,19 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
 #pragma unroll
     for (int hh = 0; hh < CPL / 8; ++hh) {                       // MFMA outputs 8hh .. 8hh+7
         if (hh > 0) __syncthreads();                             // the previous half has been read
-        // waves 4..7 hand their tiles to waves 0..3, which then hold pairwise sums
-        if (wave >= 4) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red[wave - 4][e][lane] = acc[8 * hh + e];
-        }
-        __syncthreads();
+        // waves 0..3 store their tiles, then waves 4k..4k+3 (k = 1, 2, ...) add theirs in turn:
+        // red[w] = tile of wave w + tile of wave w+4 + ...
         if (wave < 4) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) red[wave][e][lane] = acc[8 * hh + e] + red[wave][e][lane];
+            for (int e = 0; e < 8; ++e) red[wave][e][lane] = acc[8 * hh + e];
+        }
+#pragma unroll
+        for (int k = 1; k < W / 4; ++k) {
+            __syncthreads();
+            if (wave >= 4 * k && wave < 4 * k + 4) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) red[wave - 4 * k][e][lane] += acc[8 * hh + e];
+            }
         }
         __syncthreads();
         // output (token b, lane column lc, column c8 of the half): lane 16(b/4) + lc, element b%4
@@ -644,13 +651,13 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
     if (tid == 0) s_last = (atomicAdd(&tickets[slab], 1) == C - 1);
     __syncthreads();
     if (!s_last) return;
-    constexpr int OPT = kWideB * SC / kWideThreads;              // outputs per thread (4 or 8)
+    constexpr int OPT = kWideB * SC / (W * kWave);               // outputs per thread (2 to 8)
 #pragma unroll
     for (int k0 = 0; k0 < OPT; k0 += 4) {
         float pv[4][kWideMaxChunks];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int o = tid + (k0 + k) * kWideThreads;
+            const int o = tid + (k0 + k) * (W * kWave);
             const int b = o / SC, cc = o - b * SC;
             const int gcol = slab * SC + cc;
             const bool ok = b < B && gcol < d;
@@ -661,7 +668,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_down(const uint8_t *__res
         }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const int o = tid + (k0 + k) * kWideThreads;
+            const int o = tid + (k0 + k) * (W * kWave);
             const int b = o / SC, cc = o - b * SC;
             const int gcol = slab * SC + cc;
             if (b >= B || gcol >= d) continue;
