@@ -541,10 +541,12 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
         hipLaunchKernelGGL((k_wide_down<WT_Q4_0, kWideDownWaves>), dim3(64 * ceil_div(pairs, 8)),
                            dim3(kWideDownWaves * kWave), 0, st, w_dn, rb, d, B, idx, counts, fn->slot_of, f, ns, h_hi,
                            h_lo, g.hs, part, C, tickets, b_dn, y, 1, g.S);
+    } else {
+        // 12 waves (measured on the 11008-neuron layer at 16 tokens: 81.7 -> 79.7 us per layer)
+        hipLaunchKernelGGL((k_wide_down<WT_F16, kWideDownWaves>), dim3(g.S, g.C), dim3(kWideDownWaves * kWave), 0, st,
+                           w_dn, rb, d, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, part, g.C, tickets, b_dn,
+                           y, 0, g.S);
     }
-    else
-        hipLaunchKernelGGL(k_wide_down<WT_F16>, dim3(g.S, g.C), dim3(kWideThreads), 0, st, w_dn, rb, d, B, idx,
-                           counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, part, g.C, tickets, b_dn, y, 0, g.S);
     return launch_status();
 }
 

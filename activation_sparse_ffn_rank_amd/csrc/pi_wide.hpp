@@ -41,8 +41,8 @@ constexpr int kStatusHRange = 64;     // status bit: some |h| reached 65504 (out
 // columns per lane per row in k_wide_down (a slab is 16 lanes wide)
 constexpr int wide_down_cpl(int wt) { return wt == WT_Q4_0 ? 16 : 8; }
 constexpr int kWideMaxChunks = 16;    // chunk partials per slab summed by the last workgroup
-constexpr int kWideWaves = 8;         // waves per workgroup in both kernels (fp16 rows)
-constexpr int kWideDownWaves = 12;    // ... and in k_wide_down on Q4_0 rows
+constexpr int kWideWaves = 8;         // waves per workgroup of k_wide_up
+constexpr int kWideDownWaves = 12;    // ... and of k_wide_down
 constexpr int kWideThreads = kWideWaves * kWave;
 
 typedef f16 h4 __attribute__((ext_vector_type(4)));
@@ -74,8 +74,8 @@ __global__ __launch_bounds__(256) void k_wide_xmf(const uint16_t *__restrict__ x
 // of a block's loads are in flight together; x is read through a buffer resource (a token >= B or
 // a column past d reads zero).  Workgroup 0 also clears `zero_ptr[0..nzero)` (the down kernel's
 // slab tickets); the down kernel always runs after this one on the same stream.
-template <bool GATED, int WT, int NT>
-__global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restrict__ w_in, int64_t row_bytes, int d,
+template <bool GATED, int WT, int NT, int W = kWideWaves>
+__global__ __launch_bounds__(W * kWave) void k_wide_up(const uint8_t *__restrict__ w_in, int64_t row_bytes, int d,
                                                  const uint16_t *__restrict__ b_up, const uint16_t *__restrict__ x,
                                                  const uint4 *__restrict__ xmf, int B, const int32_t *__restrict__ idx,
                                                  const int32_t *__restrict__ counts,
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
                                                  uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int hs,
                                                  int32_t *__restrict__ zero_ptr, int nzero, int act,
                                                  int32_t *__restrict__ status) {
-    __shared__ f4 red[GATED ? 2 : NT][kWideWaves][kWave];
+    __shared__ f4 red[GATED ? 2 : NT][W][kWave];
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     if (blockIdx.x == 0)
         for (int t = tid; t < nzero; t += blockDim.x) zero_ptr[t] = 0;
@@ -107,7 +107,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
     f4 aq[NT];
 #pragma unroll
     for (int u = 0; u < NT; ++u) aq[u] = f4{0.f, 0.f, 0.f, 0.f};
-    for (int blk = wave * kWideUpCols; WT == WT_Q4_0 && blk < d; blk += kWideWaves * kWideUpCols) {
+    for (int blk = wave * kWideUpCols; WT == WT_Q4_0 && blk < d; blk += W * kWideUpCols) {
         // Q4_0 (d % 256 == 0, so every block of the 256 columns exists): lane group g takes the
         // 32-weight blocks blk/32 + g + 4j (j < 2) of each of its NT rows, one 16-byte code load and
         // one scale each; the codes become exact fp16 (code - 8) pairs, times the block's scale (one
@@ -147,7 +147,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
         }
     }
     if (WT == WT_Q4_0) au = aq[0];
-    for (int blk = wave * kWideUpCols; WT == WT_F16 && blk < d; blk += kWideWaves * kWideUpCols) {
+    for (int blk = wave * kWideUpCols; WT == WT_F16 && blk < d; blk += W * kWideUpCols) {
         uint4 wu[8], wg[8], xv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -189,7 +189,7 @@ __global__ __launch_bounds__(kWideThreads) void k_wide_up(const uint8_t *__restr
     const int b = 4 * (l >> 4) + v;
     float u = 0.f, gg = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWideWaves; ++w) {
+    for (int w = 0; w < W; ++w) {
         u += red[GATED ? 0 : tile][w][l][v];
         if (GATED) gg += red[GATED ? 1 : 0][w][l][v];
     }
@@ -507,7 +507,7 @@ __global__ __launch_bounds__(256) void k_pred_l2_mfma(const uint16_t *__restrict
 // workgroup to finish a slab (slab ticket) sums the partials in chunk order and adds b_down, each
 // thread issuing the loads of four outputs before the first add.  Tickets must be zero on entry
 // (k_wide_up clears them) and are left zero.
-template <int WT, int W = kWideWaves>
+template <int WT, int W = kWideDownWaves>
 __global__ __launch_bounds__(W * kWave) void k_wide_down(const uint8_t *__restrict__ w_dn, int64_t row_bytes,
                                                             int d, int B, const int32_t *__restrict__ idx,
                                                             const int32_t *__restrict__ counts,
