@@ -38,10 +38,10 @@ int check_batch(int32_t B) { return (B >= 1 && B <= PI_MAX_BATCH) ? PI_OK : PI_E
 // The GEMV kernels (first predictor matrix, tail kernel, GEMV sparse FFN) are instantiated for up to
 // 8 tokens; past that the first predictor matrix runs in two passes and the rest on MFMA.
 constexpr int kGemvMaxBatch = 8;
-// From this batch on the second predictor matrix runs on MFMA (k_pred_l2_mfma): the GEMV form's
-// vector-ALU work per weight grows with the batch (measured crossovers on MI355X, rank 1024: batch
-// 4 at 28672 and 49152 neurons, batch 6 at 11008).
-inline int pred_mfma_from(int d_ffn) { return d_ffn >= 16384 ? 4 : 6; }
+// From this batch on the second predictor matrix runs on MFMA (k_pred_l2_mfma_s, or k_pred_l2_mfma
+// past rank 1024): the GEMV form's vector-ALU work per weight grows with the batch (measured
+// crossovers on MI355X, rank 1024: batch 3 at 28672 and 49152 neurons, batch 6 at 11008).
+inline int pred_mfma_from(int d_ffn) { return d_ffn >= 16384 ? 3 : 6; }
 
 int check_pred(const pi_predictor *p) {
     if (!p) return PI_ERR_NULL;
@@ -201,9 +201,12 @@ bool layer_pred_up(const pi_predictor *p, const pi_ffn *fn, int B) {
 // down tile's neurons, a few words); all of it must fit one workgroup.  It is used while every
 // 32-neuron tile can have an up workgroup of its own (d_ffn <= 32 * kTailMaxTiles).  Larger layers
 // at batch <= 2 run k_pred_up and the split kernels instead (measured on MI355X: 9% faster than
-// this kernel at 28672 neurons, 14% at 32768; at 11008 this kernel is 11% faster).
+// this kernel at 28672 neurons, 14% at 32768; at 11008 this kernel is 11% faster).  Past 3 tokens
+// the separate predictor, compaction and sparse-FFN kernels win (11008 neurons: 81.9 -> 50.1 us
+// per layer at 4 tokens, 118.2 -> 55.0 at 6; at 3 the tail kernel still leads, 42.3 vs 46.7).
+constexpr int kTailMaxBatch = 3;
 bool tail_persistent(const pi_predictor *p, const pi_ffn *fn, int B) {
-    if (B > kGemvMaxBatch) return false;
+    if (B > kTailMaxBatch) return false;
     const size_t stat = (size_t)4 * B * kTailCPL * 64 * 4 + (size_t)B * kTailSlab * 4 + (size_t)kTailListMax * 4 + 512;
     // the kernel reads through 32-bit buffer offsets: every matrix (and the partials) must stay
     // below kBufMax bytes
@@ -298,7 +301,11 @@ int enqueue_pred_l2(const pi_predictor *p, const float *z, int B, uint8_t *mask,
         const int r = p->rank, f = p->d_ffn;
         const uint16_t *p2 = static_cast<const uint16_t *>(p->p2), *c = static_cast<const uint16_t *>(p->c);
         const dim3 grid(ceil_div(f, 64));
-        if (r >= 256)
+        if (r <= kPredL2StagedMaxRank)
+            hipLaunchKernelGGL(k_pred_l2_mfma_s<8>, dim3(ceil_div(f, 16 * kPredL2Waves)), dim3(kPredL2Waves * kWave),
+                               (size_t)ceil_div(r, 32) * 2 * kWave * 16, st, p2, c, z, B, r, f, logits, mask, bits,
+                               slot_of, n_slots);
+        else if (r >= 256)
             hipLaunchKernelGGL(k_pred_l2_mfma<8>, grid, dim3(256), 0, st, p2, c, z, B, r, f, logits, mask, bits, slot_of,
                                n_slots);
         else

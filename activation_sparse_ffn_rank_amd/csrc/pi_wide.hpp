@@ -681,4 +681,98 @@ __global__ __launch_bounds__(W * kWave) void k_wide_down(const uint8_t *__restri
     if (tid == 0) tickets[slab] = 0;
 }
 
+// The same logits and flags with z staged once per workgroup in LDS, already split into fp16 hi +
+// lo parts and laid out in the MFMA's A-operand order (entry (s, part, L) = 8 values of token L%16
+// at columns 32s + 8(L/16) .. +8; tokens >= B are zeros), so each wave reads one 16-byte LDS vector
+// per part and step instead of loading and splitting 32 bytes of fp32 z from L2 for every 16
+// neurons.  Workgroups of kPredL2Waves waves own 16 * kPredL2Waves neurons; the P2 loads of two
+// 32*KC-column steps are in flight per wave (the first go out before the staging).  LDS: 64 r bytes
+// (r <= kPredL2StagedMaxRank).
+constexpr int kPredL2Waves = 8;
+constexpr int kPredL2StagedMaxRank = 1024;
+template <int KC>
+__global__ __launch_bounds__(kPredL2Waves * kWave) void k_pred_l2_mfma_s(
+    const uint16_t *__restrict__ p2, const uint16_t *__restrict__ c, const float *__restrict__ z, int B, int r, int f,
+    float *__restrict__ logits, uint8_t *__restrict__ mask, uint32_t *__restrict__ bits,
+    const int32_t *__restrict__ slot_of, int n_slots) {
+    extern __shared__ __align__(16) uint4 zmf[];                       // [r/32][2][kWave]
+    __shared__ uint32_t s_half[kPredL2Waves];
+    const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int n16 = lane & 15, g = lane >> 4;
+    const int nrow = blockIdx.x * (16 * kPredL2Waves) + wave * 16 + n16;   // this lane's neuron (B operand)
+    const __amdgpu_buffer_rsrc_t rp = buf_rsrc(p2, (uint32_t)((size_t)f * r * 2));
+    const uint32_t prow = nrow < f ? (uint32_t)nrow * (uint32_t)r * 2u : kOOB;
+    auto issue = [&](uint4 (&w)[KC], int k0) {
+#pragma unroll
+        for (int j = 0; j < KC; ++j) {
+            const int col = k0 + 32 * j + 8 * g;
+            w[j] = bld16(rp, col < r ? prow + (uint32_t)col * 2u : kOOB);   // r % 8 == 0
+        }
+    };
+    uint4 wa[KC], wb[KC];
+    issue(wa, 0);
+    // staging: item (s, L) -> hi at zmf[2s*64 + L], lo at zmf[(2s+1)*64 + L]
+    const __amdgpu_buffer_rsrc_t rz = buf_rsrc(z, (uint32_t)B * (uint32_t)r * 4u);
+    const int steps = (r + 31) / 32;
+    for (int e = threadIdx.x; e < steps * kWave; e += blockDim.x) {
+        const int st = e / kWave, L = e - st * kWave, m = L & 15, col = 32 * st + 8 * (L >> 4);
+        const bool ok = m < B && col < r;
+        const uint32_t off = ok ? ((uint32_t)m * (uint32_t)r + (uint32_t)col) * 4u : kOOB;
+        uint4 hi, lo;
+        split8(__builtin_bit_cast(float4, bld16(rz, off)), __builtin_bit_cast(float4, bld16(rz, ok ? off + 16u : kOOB)),
+               hi, lo);
+        zmf[(2 * st) * kWave + L] = hi;
+        zmf[(2 * st + 1) * kWave + L] = lo;
+    }
+    __syncthreads();
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    auto step = [&](const uint4 (&w)[KC], int k0) {
+#pragma unroll
+        for (int j = 0; j < KC; ++j) {
+            const int st = k0 / 32 + j;
+            if (st < steps) {                                          // wave-uniform
+                acc = mfma32(zmf[(2 * st) * kWave + lane], w[j], acc);
+                acc = mfma32(zmf[(2 * st + 1) * kWave + lane], w[j], acc);
+            }
+        }
+    };
+    for (int k0 = 0; k0 < r; k0 += 64 * KC) {
+        issue(wb, k0 + 32 * KC);
+        step(wa, k0);
+        issue(wa, k0 + 64 * KC);
+        step(wb, k0 + 32 * KC);
+    }
+    // D[m = 4g + v][n = n16]: logits of tokens 4g .. 4g+3 for this lane's neuron
+    const float cn = nrow < f ? half_to_float(c[nrow]) : 0.f;
+    const float lv[4] = {acc.x + cn, acc.y + cn, acc.z + cn, acc.w + cn};
+    bool fired = false;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int b = 4 * g + v;
+        if (b < B) {
+            fired |= lv[v] > 0.f;
+            if (logits != nullptr && nrow < f) logits[(size_t)b * f + nrow] = lv[v];
+        }
+    }
+    const uint64_t bal = __ballot(fired);
+    const uint32_t m16 = (uint32_t)((bal | (bal >> 16) | (bal >> 32) | (bal >> 48)) & 0xFFFFu);
+    const bool mine = g == 0 && nrow < f;
+    if (mine) mask[nrow] = (uint8_t)((m16 >> n16) & 1u);
+    if (bits != nullptr) {
+        bool resident = false;
+        if (mine) {
+            const int sl = slot_of != nullptr ? slot_of[nrow] : 0;
+            resident = sl >= 0 && sl < n_slots;
+        }
+        const uint32_t res16 = (uint32_t)(__ballot(resident) & 0xFFFFu);
+        if (lane == 0) s_half[wave] = m16 & res16;
+        __syncthreads();
+        if (threadIdx.x < kPredL2Waves / 2) {
+            const int w2 = 2 * threadIdx.x;
+            const int word = blockIdx.x * (kPredL2Waves / 2) + threadIdx.x;
+            if (word * 32 < f) bits[word] = s_half[w2] | (s_half[w2 + 1] << 16);
+        }
+    }
+}
+
 }  // namespace pik

@@ -161,7 +161,7 @@ int pi_sparse_ffn_wide(const pi_ffn *ffn, const void *x, int32_t batch, const in
  * The workspace must be zero-filled before the first call that uses it; each call leaves it ready
  * for the next one (never clear or share it while a call is in flight; after a call that returned
  * an error, zero-fill it again).
- * For layers of at most 12288 neurons whose x and z fit one workgroup's LDS
+ * For layers of at most 12288 neurons at batch <= 3 whose x and z fit one workgroup's LDS
  * (pi_layer_path == 1), everything after the first predictor matrix is ONE persistent kernel whose
  * workgroups hand the mask and h to each other through the workspace.  The int32 at byte offset
  * 384 of the workspace is a sticky status word: nonzero means a cross-workgroup wait ran out its
@@ -190,7 +190,7 @@ int pi_ffn_layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const 
 
 /* Which launches pi_ffn_layer_from_hidden makes for this layer and batch: 1 = one persistent kernel
  * (logits, mask and sparse FFN together; x, z and the kernel's arrays fit one workgroup's LDS and
- * d_ffn <= 12288, batch <= 8), 2 = separate kernels (at batch <= 2: logits, mask and up rows in
+ * d_ffn <= 12288, batch <= 3), 2 = separate kernels (at batch <= 2: logits, mask and up rows in
  * one kernel, then the down rows and the sum of their partials; otherwise logits and mask, then
  * the sparse FFN).  0 on invalid arguments. */
 int pi_layer_path(const pi_predictor *pred, const pi_ffn *ffn, int32_t batch);

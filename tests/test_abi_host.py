@@ -181,9 +181,12 @@ def test_two_step_layer_rejects(L):
 
 def test_layer_path(L):
     path = lambda pp, ff, B: L.pi_layer_path(ctypes.byref(pp) if pp else None, ctypes.byref(ff) if ff else None, B)
-    # one persistent kernel: d_ffn <= 12288 and x, z fit LDS
+    # one persistent kernel: d_ffn <= 12288, batch <= 3 and x, z fit LDS
     assert path(pred(d=4096, f=11008, r=1024), ffn(d=4096, f=11008, gated=1), 1) == 1
-    assert path(pred(d=1024, f=4096, r=128), ffn(d=1024, f=4096), 8) == 1
+    assert path(pred(d=1024, f=4096, r=128), ffn(d=1024, f=4096), 3) == 1
+    # past 3 tokens separate kernels (faster there)
+    assert path(pred(d=4096, f=11008, r=1024), ffn(d=4096, f=11008, gated=1), 4) == 2
+    assert path(pred(d=1024, f=4096, r=128), ffn(d=1024, f=4096), 8) == 2
     # separate kernels: more than 12288 neurons (at batch <= 2: k_pred_up and the split kernels, faster
     # there), or x too large for LDS
     assert path(pred(d=8192, f=32768, r=1024), ffn(d=8192, f=32768), 1) == 2
@@ -191,7 +194,7 @@ def test_layer_path(L):
     assert path(pred(d=8192, f=32768, r=1024), ffn(d=8192, f=32768), 4) == 2
     assert path(pred(d=12288, f=49152, r=1024), ffn(d=12288, f=49152), 1) == 2
     assert path(pred(d=12288, f=12288, r=1024), ffn(d=12288, f=12288), 8) == 2
-    # past 8 tokens the layer always runs separate kernels (MFMA second predictor matrix and FFN)
+    # past 8 tokens too (MFMA second predictor matrix and FFN)
     assert path(pred(d=1024, f=4096, r=128), ffn(d=1024, f=4096), 9) == 2
     assert path(pred(d=1024, f=4096, r=128), ffn(d=1024, f=4096), 16) == 2
     # invalid
