@@ -295,8 +295,15 @@ int enqueue_pred_l2_b(const pi_predictor *p, const float *z, uint8_t *mask, floa
     return launch_status();
 }
 
+// Whether enqueue_pred_l2 runs k_pred_l2_mfma_s (which can also lay out x for the Q4_0 up step).
+bool pred_l2_staged(const pi_predictor *p, int B) {
+    return B >= pred_mfma_from(p->d_ffn) && p->rank <= kPredL2StagedMaxRank;
+}
+
+// x, d, xmf: with pred_l2_staged, also write x [B][d] in the Q4_0 up step's operand order to xmf.
 int enqueue_pred_l2(const pi_predictor *p, const float *z, int B, uint8_t *mask, float *logits, hipStream_t st,
-                    uint32_t *bits = nullptr, const int32_t *slot_of = nullptr, int n_slots = 0) {
+                    uint32_t *bits = nullptr, const int32_t *slot_of = nullptr, int n_slots = 0,
+                    const void *x = nullptr, uint4 *xmf = nullptr) {
     if (B >= pred_mfma_from(p->d_ffn)) {
         const int r = p->rank, f = p->d_ffn;
         const uint16_t *p2 = static_cast<const uint16_t *>(p->p2), *c = static_cast<const uint16_t *>(p->c);
@@ -304,7 +311,7 @@ int enqueue_pred_l2(const pi_predictor *p, const float *z, int B, uint8_t *mask,
         if (r <= kPredL2StagedMaxRank)
             hipLaunchKernelGGL(k_pred_l2_mfma_s<8>, dim3(ceil_div(f, 16 * kPredL2Waves)), dim3(kPredL2Waves * kWave),
                                (size_t)ceil_div(r, 32) * 2 * kWave * 16, st, p2, c, z, B, r, f, logits, mask, bits,
-                               slot_of, n_slots);
+                               slot_of, n_slots, static_cast<const uint16_t *>(x), p->d_model, xmf);
         else if (r >= 256)
             hipLaunchKernelGGL(k_pred_l2_mfma<8>, grid, dim3(256), 0, st, p2, c, z, B, r, f, logits, mask, bits, slot_of,
                                n_slots);
@@ -500,7 +507,7 @@ int enqueue_split(const pi_ffn *fn, const void *x, int B, const int32_t *idx, co
 // the sticky status word that an h outside the fp16 pair's range is reported in (NULL: the wide
 // workspace's own).
 int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y, char *w,
-                 hipStream_t st, int32_t *status = nullptr) {
+                 hipStream_t st, int32_t *status = nullptr, bool xmf_ready = false) {
     const WideGeom g = wide_geom(fn, B);
     int32_t *tickets = reinterpret_cast<int32_t *>(w + g.tick);
     if (status == nullptr) status = reinterpret_cast<int32_t *>(w);
@@ -513,7 +520,7 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
     const dim3 up_grid(std::max(1, ceil_div(ns, 16)));
     if (fn->wtype == PI_Q4_0) {
         uint4 *xmf = reinterpret_cast<uint4 *>(w + g.xmf);
-        hipLaunchKernelGGL(k_wide_xmf, dim3(ceil_div(2 * d, 256)), dim3(256), 0, st, xx, B, d, xmf);
+        if (!xmf_ready) hipLaunchKernelGGL(k_wide_xmf, dim3(ceil_div(2 * d, 256)), dim3(256), 0, st, xx, B, d, xmf);
         int cus = 0, per_cu = 0;
         if ((int64_t)ns * rb < (int64_t)kBufMax &&
             resident_slots(reinterpret_cast<const void *>(k_wide_up_q4), kWideUpWaves * kWave, 0, &cus, &per_cu) == 0) {
@@ -561,12 +568,14 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
 // positions from instead of idx/counts; status: the status word to report in (NULL: the
 // workspace's own, at byte offset 384).
 int enqueue_sparse(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y,
-                   void *ws, hipStream_t st, const uint32_t *bits = nullptr, int32_t *status = nullptr) {
+                   void *ws, hipStream_t st, const uint32_t *bits = nullptr, int32_t *status = nullptr,
+                   bool xmf_ready = false) {
     char *w = static_cast<char *>(ws);
     if (sparse_split(fn, B))
         return enqueue_split(fn, x, B, idx, counts, bits, y, w + ctl_bytes(fn->d_model), st);
     if (status == nullptr) status = reinterpret_cast<int32_t *>(w) + CTL_STATUS;
-    if (sparse_wide(fn, B)) return enqueue_wide(fn, x, B, idx, counts, y, w + ctl_bytes(fn->d_model), st, status);
+    if (sparse_wide(fn, B))
+        return enqueue_wide(fn, x, B, idx, counts, y, w + ctl_bytes(fn->d_model), st, status, xmf_ready);
     return enqueue_sparse_legacy(fn, x, B, idx, counts, y, ffn_scratch(fn, B, w + ctl_bytes(fn->d_model)), st);
 }
 
@@ -764,18 +773,22 @@ int layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const void *x
         if ((rc = enqueue_sparse(ffn, x, batch, nullptr, nullptr, y, L.ffn, st, L.bits))) return rc;
         return want_list ? enqueue_compact(mask, f, ffn->slot_of, idx, counts, st) : PI_OK;
     }
+    // the Q4_0 up step's copy of x comes from the predictor's grid when it runs k_pred_l2_mfma_s
+    uint4 *xmf = nullptr;
+    if (ffn->wtype == PI_Q4_0 && sparse_wide(ffn, batch) && pred_l2_staged(pred, batch))
+        xmf = reinterpret_cast<uint4 *>(static_cast<char *>(L.ffn) + ctl_bytes(ffn->d_model) + wide_geom(ffn, batch).xmf);
     if (mask_words(f) <= 4096) {
         // the list from the predictor's flag words (unrestricted: the placement is applied while
         // listing), a 32-fold smaller read than the mask bytes
-        if ((rc = enqueue_pred_l2(pred, z, batch, mask, nullptr, st, L.bits, nullptr, f))) return rc;
+        if ((rc = enqueue_pred_l2(pred, z, batch, mask, nullptr, st, L.bits, nullptr, f, x, xmf))) return rc;
         hipLaunchKernelGGL(k_compact_bits, dim3(1), dim3(1024), 0, st, L.bits, mask_words(f), ffn->slot_of,
                            ffn->n_slots, idx, counts);
         if ((rc = launch_status())) return rc;
     } else {
-        if ((rc = enqueue_pred_l2(pred, z, batch, mask, nullptr, st))) return rc;
+        if ((rc = enqueue_pred_l2(pred, z, batch, mask, nullptr, st, nullptr, nullptr, 0, x, xmf))) return rc;
         if ((rc = enqueue_compact(mask, f, ffn->slot_of, idx, counts, st))) return rc;
     }
-    return enqueue_sparse(ffn, x, batch, idx, counts, y, L.ffn, st, nullptr, L.ctl + CTL_STATUS);
+    return enqueue_sparse(ffn, x, batch, idx, counts, y, L.ffn, st, nullptr, L.ctl + CTL_STATUS, xmf != nullptr);
 }
 
 int check_layer(const pi_predictor *pred, const pi_ffn *ffn, const void *x, int32_t batch, const float *y,

@@ -58,12 +58,15 @@ __device__ __forceinline__ f4 mfma16(uint32_t a0, uint32_t a1, uint32_t b0, uint
 // columns 32(4kq + g) + 8i .. +8, re-paired for q4pair (pair_for_q4), or zeros for a token r >= B;
 // 2d vectors (d*32 bytes), one thread each.  Lane r + 16g of a wave then reads the vectors of block
 // 4kq + g for its token r: a wave's load for one (kq, i) is 64 consecutive vectors.
+__device__ __forceinline__ void wide_xmf_vec(const uint16_t *__restrict__ x, int B, int d, uint4 *__restrict__ xmf,
+                                             int v) {
+    const int kq = v >> 8, i = (v >> 6) & 3, g = (v >> 4) & 3, r = v & 15;
+    xmf[v] = r < B ? pair_for_q4(ld16(x + (size_t)r * d + (4 * kq + g) * 32 + 8 * i)) : zero4();
+}
 __global__ __launch_bounds__(256) void k_wide_xmf(const uint16_t *__restrict__ x, int B, int d,
                                                   uint4 *__restrict__ xmf) {
     const int v = blockIdx.x * 256 + threadIdx.x;
-    if (v >= 2 * d) return;
-    const int kq = v >> 8, i = (v >> 6) & 3, g = (v >> 4) & 3, r = v & 15;
-    xmf[v] = r < B ? pair_for_q4(ld16(x + (size_t)r * d + (4 * kq + g) * 32 + 8 * i)) : zero4();
+    if (v < 2 * d) wide_xmf_vec(x, B, d, xmf, v);
 }
 
 // h[b][k] for the listed neurons, as fp16 hi and lo parts in [16][hs] arrays.  Workgroup t holds
@@ -687,14 +690,17 @@ __global__ __launch_bounds__(W * kWave) void k_wide_down(const uint8_t *__restri
 // per part and step instead of loading and splitting 32 bytes of fp32 z from L2 for every 16
 // neurons.  Workgroups of kPredL2Waves waves own 16 * kPredL2Waves neurons; the P2 loads of two
 // 32*KC-column steps are in flight per wave (the first go out before the staging).  LDS: 64 r bytes
-// (r <= kPredL2StagedMaxRank).
+// (r <= kPredL2StagedMaxRank).  With xmf != nullptr the grid also writes x [B][d] in the operand
+// order of the Q4_0 up step (k_wide_xmf's work, spread over the grid: the layer then needs no
+// launch of its own for it).
 constexpr int kPredL2Waves = 8;
 constexpr int kPredL2StagedMaxRank = 1024;
 template <int KC>
 __global__ __launch_bounds__(kPredL2Waves * kWave) void k_pred_l2_mfma_s(
     const uint16_t *__restrict__ p2, const uint16_t *__restrict__ c, const float *__restrict__ z, int B, int r, int f,
     float *__restrict__ logits, uint8_t *__restrict__ mask, uint32_t *__restrict__ bits,
-    const int32_t *__restrict__ slot_of, int n_slots) {
+    const int32_t *__restrict__ slot_of, int n_slots, const uint16_t *__restrict__ x, int d,
+    uint4 *__restrict__ xmf) {
     extern __shared__ __align__(16) uint4 zmf[];                       // [r/32][2][kWave]
     __shared__ uint32_t s_half[kPredL2Waves];
     const int lane = threadIdx.x & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -711,6 +717,9 @@ __global__ __launch_bounds__(kPredL2Waves * kWave) void k_pred_l2_mfma_s(
     };
     uint4 wa[KC], wb[KC];
     issue(wa, 0);
+    if (xmf != nullptr)
+        for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < 2 * d; v += gridDim.x * blockDim.x)
+            wide_xmf_vec(x, B, d, xmf, v);
     // staging: item (s, L) -> hi at zmf[2s*64 + L], lo at zmf[(2s+1)*64 + L]
     const __amdgpu_buffer_rsrc_t rz = buf_rsrc(z, (uint32_t)B * (uint32_t)r * 4u);
     const int steps = (r + 31) / 32;

@@ -153,8 +153,8 @@ def ffn_kernel_names(h_kind: int, B: int, cfg, synth):
         return "k_sparse_up + k_sparse_down", [f"void pik::k_sparse_up<{B}, {g}, {w}>", f"void pik::k_sparse_down<{B}, {w}>"]
     if h_kind == 3:
         if cfg.wtype != synth.F16:                              # x re-laid out for the Q4_0 MFMA operands first
-            return "k_wide_xmf + k_wide_up + k_wide_down", ["pik::k_wide_xmf(", "void pik::k_wide_up<",
-                                                            "void pik::k_wide_down<"]
+            return "k_wide_xmf + k_wide_up_q4 + k_wide_down", ["pik::k_wide_xmf(", "pik::k_wide_up_q4(",
+                                                               "void pik::k_wide_down<"]
         return "k_wide_up + k_wide_down", ["void pik::k_wide_up<", "void pik::k_wide_down<"]
     return f"kind {h_kind}", []
 
@@ -280,11 +280,16 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
         rest_prefixes = [f"void pik::k_pred_up<{B}, {g}, {w},", f"void pik::k_down_split<{B}, {g}, {w}, true>",
                          "pik::k_sum_split("]
     else:
-        # the second predictor matrix on MFMA from batch 4 (d_ffn >= 16384) or 6, then the list from its
-        # flag words
-        pl2 = "k_pred_l2_mfma" if B >= (4 if cfg.f >= 16384 else 6) else "k_pred_l2"
-        rest_label = f"{pl2} + k_compact_bits + {ffn_label}"
-        rest_prefixes = [f"void pik::{pl2}<", "pik::k_compact_bits("] + ffn_prefixes
+        # the second predictor matrix on MFMA from batch 3 (d_ffn >= 16384) or 6 (z staged in LDS up
+        # to rank 1024), then the list from its flag words; the staged kernel's grid also lays out x
+        # for the Q4_0 up step, so the layer runs no k_wide_xmf of its own
+        mfma = B >= (3 if cfg.f >= 16384 else 6)
+        pl2 = ("k_pred_l2_mfma_s" if cfg.r <= 1024 else "k_pred_l2_mfma") if mfma else "k_pred_l2"
+        in_label, in_prefixes = ffn_label, ffn_prefixes
+        if mfma and cfg.r <= 1024 and in_prefixes and in_prefixes[0] == "pik::k_wide_xmf(":
+            in_label, in_prefixes = in_label.replace("k_wide_xmf + ", ""), in_prefixes[1:]
+        rest_label = f"{pl2} + k_compact_bits + {in_label}"
+        rest_prefixes = [f"void pik::{pl2}<", "pik::k_compact_bits("] + in_prefixes
     step_bytes = (pred_bytes + float(ffn_touched.mean())) * L
     ms_per_step = elapsed_ms / K
 
@@ -460,7 +465,7 @@ def wide_leg(torch, _abi, cfg, layers, xd, masks, cases, stream, dev, in_rows, r
             "algorithmic_bytes_per_layer": int(wide_bytes),
             "gbs": round(wide_bytes / (wide_us * 1e-6) / 1e9, 1),
             "hbm_frac": round(wide_bytes / (wide_us * 1e-6) / 8e12, 4),
-            "kernels": ("k_wide_xmf + " if q4 else "") + "k_wide_up + k_wide_down (pi_sparse_ffn_wide, MFMA f16)"}
+            "kernels": ("k_wide_xmf + k_wide_up_q4" if q4 else "k_wide_up") + " + k_wide_down (pi_sparse_ffn_wide, MFMA f16)"}
 
 
 def cpu_oracle(synth, oracle, cfg, L, B, tokens, budget_s, threads=None):
