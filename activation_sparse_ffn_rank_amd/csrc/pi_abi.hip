@@ -506,8 +506,27 @@ int enqueue_split(const pi_ffn *fn, const void *x, int B, const int32_t *idx, co
 // The MFMA form of the sparse FFN (k_wide_up, then k_wide_down) on a wide workspace at w; status:
 // the sticky status word that an h outside the fp16 pair's range is reported in (NULL: the wide
 // workspace's own).
+// Whether the Q4_0 up step runs k_wide_up_q4 (one workgroup per compute unit; *cus set).
+bool wide_up_q4(const pi_ffn *fn, int *cus) {
+    int per_cu = 0;
+    return fn->wtype == PI_Q4_0 && (int64_t)fn->n_slots * row_bytes_of(fn) < (int64_t)kBufMax &&
+           resident_slots(reinterpret_cast<const void *>(k_wide_up_q4), kWideUpWaves * kWave, 0, cus, &per_cu) == 0;
+}
+// Whether k_wide_up_q4 can take the positions from the predictor's flag words itself (every neuron
+// resident, the words and a workgroup's run within its limits), so the layer needs no k_compact_bits.
+bool wide_up_from_bits(const pi_ffn *fn, int B) {
+    int cus = 0;
+    const int f = fn->d_ffn;
+    return sparse_wide(fn, B) && fn->slot_of == nullptr && fn->n_slots == f && wide_up_q4(fn, &cus) &&
+           mask_words(f) <= kWideUpWordsPerThread * kWideUpWaves * kWave &&
+           ceil_div(ceil_div(f, 16), cus) * 16 <= kWideUpRunIds;
+}
+
+// bits, idx_w, counts_w: with wide_up_from_bits, the predictor's flag words; the positions and counts
+// are then written to idx_w / counts_w (the same arrays as idx / counts) by k_wide_up_q4.
 int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y, char *w,
-                 hipStream_t st, int32_t *status = nullptr, bool xmf_ready = false) {
+                 hipStream_t st, int32_t *status = nullptr, bool xmf_ready = false, const uint32_t *bits = nullptr,
+                 int32_t *idx_w = nullptr, int32_t *counts_w = nullptr) {
     const WideGeom g = wide_geom(fn, B);
     int32_t *tickets = reinterpret_cast<int32_t *>(w + g.tick);
     if (status == nullptr) status = reinterpret_cast<int32_t *>(w);
@@ -521,10 +540,10 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
     if (fn->wtype == PI_Q4_0) {
         uint4 *xmf = reinterpret_cast<uint4 *>(w + g.xmf);
         if (!xmf_ready) hipLaunchKernelGGL(k_wide_xmf, dim3(ceil_div(2 * d, 256)), dim3(256), 0, st, xx, B, d, xmf);
-        int cus = 0, per_cu = 0;
-        if ((int64_t)ns * rb < (int64_t)kBufMax &&
-            resident_slots(reinterpret_cast<const void *>(k_wide_up_q4), kWideUpWaves * kWave, 0, &cus, &per_cu) == 0) {
-            WideUpQ4Args ua{w_in, rb, d, B, f, ns, g.hs, fn->act, b_up, xmf, idx, fn->slot_of, h_hi, h_lo, status};
+        int cus = 0;
+        if (wide_up_q4(fn, &cus)) {
+            WideUpQ4Args ua{w_in, rb, d, B, f, ns, g.hs, fn->act, b_up, xmf, idx, fn->slot_of, h_hi, h_lo, status,
+                            bits, mask_words(f), idx_w, counts_w};
             hipLaunchKernelGGL(k_wide_up_q4, dim3(cus), dim3(kWideUpWaves * kWave), 0, st, ua, counts, tickets, g.S);
         }
         else
@@ -569,13 +588,15 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
 // workspace's own, at byte offset 384).
 int enqueue_sparse(const pi_ffn *fn, const void *x, int B, const int32_t *idx, const int32_t *counts, float *y,
                    void *ws, hipStream_t st, const uint32_t *bits = nullptr, int32_t *status = nullptr,
-                   bool xmf_ready = false) {
+                   bool xmf_ready = false, const uint32_t *up_bits = nullptr, int32_t *idx_w = nullptr,
+                   int32_t *counts_w = nullptr) {
     char *w = static_cast<char *>(ws);
     if (sparse_split(fn, B))
         return enqueue_split(fn, x, B, idx, counts, bits, y, w + ctl_bytes(fn->d_model), st);
     if (status == nullptr) status = reinterpret_cast<int32_t *>(w) + CTL_STATUS;
     if (sparse_wide(fn, B))
-        return enqueue_wide(fn, x, B, idx, counts, y, w + ctl_bytes(fn->d_model), st, status, xmf_ready);
+        return enqueue_wide(fn, x, B, idx, counts, y, w + ctl_bytes(fn->d_model), st, status, xmf_ready, up_bits,
+                            idx_w, counts_w);
     return enqueue_sparse_legacy(fn, x, B, idx, counts, y, ffn_scratch(fn, B, w + ctl_bytes(fn->d_model)), st);
 }
 
@@ -781,6 +802,9 @@ int layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const void *x
         // the list from the predictor's flag words (unrestricted: the placement is applied while
         // listing), a 32-fold smaller read than the mask bytes
         if ((rc = enqueue_pred_l2(pred, z, batch, mask, nullptr, st, L.bits, nullptr, f, x, xmf))) return rc;
+        if (wide_up_from_bits(ffn, batch))                     // the up step lists the positions itself
+            return enqueue_sparse(ffn, x, batch, idx, counts, y, L.ffn, st, nullptr, L.ctl + CTL_STATUS,
+                                  xmf != nullptr, L.bits, idx, counts);
         hipLaunchKernelGGL(k_compact_bits, dim3(1), dim3(1024), 0, st, L.bits, mask_words(f), ffn->slot_of,
                            ffn->n_slots, idx, counts);
         if ((rc = launch_status())) return rc;

@@ -236,12 +236,22 @@ struct WideUpQ4Args {
     const int32_t *idx, *slot_of;
     uint16_t *h_hi, *h_lo;
     int32_t *status;
+    // positions from the predictor's listed-flag words instead of idx/counts (every neuron resident,
+    // slot = id): each workgroup counts the set bits of all nwords words, takes its run and writes
+    // those positions' ids to idx_out; workgroup 0 writes counts_out {n, n}.  nullptr: idx/counts.
+    const uint32_t *bits;
+    int nwords;
+    int32_t *idx_out, *counts_out;
 };
+constexpr int kWideUpWordsPerThread = 6;   // bits mode: nwords <= 6 * kWideUpWaves * 64
+constexpr int kWideUpRunIds = 512;         // bits mode: a workgroup's run holds at most this many positions
 
-// One pass: tiles t0 .. t0+NT-1 of the run ending at t_hi (n listed positions).
+// One pass: tiles t0 .. t0+NT-1 of the run ending at t_hi (n listed positions); run_ids: the ids of
+// the run's positions from p_lo on (bits mode), else nullptr (ids from a.idx).
 template <int NT>
 __device__ __forceinline__ void wide_up_q4_pass(const WideUpQ4Args &a, __amdgpu_buffer_rsrc_t rw, int n, int t0,
-                                                int t_hi, f4 (*red)[kWideUpWaves][kWave]) {
+                                                int t_hi, f4 (*red)[kWideUpWaves][kWave], const int *run_ids,
+                                                int p_lo) {
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int r = lane & 15, g = lane >> 4, d = a.d;
     int sl[NT];
@@ -249,7 +259,9 @@ __device__ __forceinline__ void wide_up_q4_pass(const WideUpQ4Args &a, __amdgpu_
 #pragma unroll
     for (int u = 0; u < NT; ++u) {
         const int pu = (t0 + u) * 16 + r;
-        sl[u] = (t0 + u < t_hi && pu < n) ? slot_of_id(a.idx[pu], a.slot_of, a.f, a.n_slots) : -1;
+        sl[u] = (t0 + u < t_hi && pu < n)
+                    ? slot_of_id(run_ids != nullptr ? run_ids[pu - p_lo] : a.idx[pu], a.slot_of, a.f, a.n_slots)
+                    : -1;
         base[u] = sl[u] >= 0 ? (uint32_t)(sl[u] * a.row_bytes) : kOOB;
     }
     f4 aq[NT];
@@ -323,19 +335,79 @@ __device__ __forceinline__ void wide_up_q4_pass(const WideUpQ4Args &a, __amdgpu_
 __global__ __launch_bounds__(kWideUpWaves * kWave) void k_wide_up_q4(WideUpQ4Args a, const int32_t *__restrict__ counts,
                                                                     int32_t *__restrict__ zero_ptr, int nzero) {
     __shared__ f4 red[kWideUpMaxNT][kWideUpWaves][kWave];
+    __shared__ int s_wsum[kWideUpWaves];
+    __shared__ int s_ids[kWideUpRunIds];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     if (blockIdx.x == 0)
-        for (int t = threadIdx.x; t < nzero; t += blockDim.x) zero_ptr[t] = 0;
-    const int n = min(max(counts[0], 0), a.n_slots);
-    const int T = (n + 15) / 16, G = gridDim.x;
-    const int t_lo = (int)((int64_t)T * blockIdx.x / G), t_hi = (int)((int64_t)T * (blockIdx.x + 1) / G);
+        for (int t = tid; t < nzero; t += blockDim.x) zero_ptr[t] = 0;
+    const int G = gridDim.x;
+    int n, T, t_lo, t_hi;
+    const int *run_ids = nullptr;
+    int p_lo = 0;
+    if (a.bits != nullptr) {
+        // thread tid counts words [tid*per, tid*per + per); the ascending ranks of the set bits are
+        // the positions (exactly the list k_compact_bits would write)
+        const int per = (a.nwords + (int)blockDim.x - 1) / (int)blockDim.x;      // <= kWideUpWordsPerThread
+        const int w0 = tid * per;
+        const __amdgpu_buffer_rsrc_t rb = buf_rsrc(a.bits, (uint32_t)a.nwords * 4u);
+        uint32_t wv[kWideUpWordsPerThread];
+        int cnt = 0;
+#pragma unroll
+        for (int v = 0; v < kWideUpWordsPerThread; ++v) {
+            wv[v] = bld4(rb, (v < per && w0 + v < a.nwords) ? (uint32_t)(w0 + v) * 4u : kOOB);
+            cnt += __popc(wv[v]);
+        }
+        const int incl = wave_incl_scan(cnt);
+        if (lane == kWave - 1) s_wsum[wave] = incl;
+        __syncthreads();
+        int before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kWideUpWaves; ++w) {
+            before += w < wave ? s_wsum[w] : 0;
+            total += s_wsum[w];
+        }
+        n = min(total, a.n_slots);
+        T = (n + 15) / 16;
+        t_lo = (int)((int64_t)T * blockIdx.x / G);
+        t_hi = (int)((int64_t)T * (blockIdx.x + 1) / G);
+        p_lo = 16 * t_lo;
+        const int p_hi = min(16 * t_hi, n);
+        int pos = before + incl - cnt;
+#pragma unroll
+        for (int v = 0; v < kWideUpWordsPerThread; ++v) {
+            const int c = __popc(wv[v]);
+            if (pos < p_hi && pos + c > p_lo) {
+                for (uint32_t m = wv[v]; m != 0u && pos < p_hi; m &= m - 1u, ++pos) {
+                    if (pos >= p_lo) {
+                        const int id = (w0 + v) * 32 + __builtin_ctz(m);
+                        s_ids[pos - p_lo] = id;
+                        a.idx_out[pos] = id;
+                    }
+                }
+            } else {
+                pos += c;
+            }
+        }
+        if (blockIdx.x == 0 && tid == 0) {
+            a.counts_out[0] = n;
+            a.counts_out[1] = total;
+        }
+        __syncthreads();
+        run_ids = s_ids;
+    } else {
+        n = min(max(counts[0], 0), a.n_slots);
+        T = (n + 15) / 16;
+        t_lo = (int)((int64_t)T * blockIdx.x / G);
+        t_hi = (int)((int64_t)T * (blockIdx.x + 1) / G);
+    }
     const int len = t_hi - t_lo;
     if (len <= 0) return;                                        // workgroup-uniform
     const __amdgpu_buffer_rsrc_t rw = buf_rsrc(a.w_in, (uint32_t)(a.n_slots * a.row_bytes));
     const int passes = (len + kWideUpMaxNT - 1) / kWideUpMaxNT;
     const int per = (len + passes - 1) / passes;                 // tiles per pass, <= 4
     for (int t0 = t_lo; t0 < t_hi; t0 += per) {
-        if (per <= 3) wide_up_q4_pass<3>(a, rw, n, t0, min(t0 + per, t_hi), red);
-        else wide_up_q4_pass<4>(a, rw, n, t0, min(t0 + per, t_hi), red);
+        if (per <= 3) wide_up_q4_pass<3>(a, rw, n, t0, min(t0 + per, t_hi), red, run_ids, p_lo);
+        else wide_up_q4_pass<4>(a, rw, n, t0, min(t0 + per, t_hi), red, run_ids, p_lo);
     }
 }
 

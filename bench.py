@@ -286,10 +286,13 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
         mfma = B >= (3 if cfg.f >= 16384 else 6)
         pl2 = ("k_pred_l2_mfma_s" if cfg.r <= 1024 else "k_pred_l2_mfma") if mfma else "k_pred_l2"
         in_label, in_prefixes = ffn_label, ffn_prefixes
-        if mfma and cfg.r <= 1024 and in_prefixes and in_prefixes[0] == "pik::k_wide_xmf(":
+        q4_wide = bool(in_prefixes) and in_prefixes[0] == "pik::k_wide_xmf("
+        if mfma and cfg.r <= 1024 and q4_wide:
             in_label, in_prefixes = in_label.replace("k_wide_xmf + ", ""), in_prefixes[1:]
-        rest_label = f"{pl2} + k_compact_bits + {in_label}"
-        rest_prefixes = [f"void pik::{pl2}<", "pik::k_compact_bits("] + in_prefixes
+        # with every neuron resident, the Q4_0 up step lists the positions from the flag words itself
+        cb_label, cb_prefixes = ("", []) if (q4_wide and hots is None) else ("k_compact_bits + ", ["pik::k_compact_bits("])
+        rest_label = f"{pl2} + {cb_label}{in_label}"
+        rest_prefixes = [f"void pik::{pl2}<"] + cb_prefixes + in_prefixes
     step_bytes = (pred_bytes + float(ffn_touched.mean())) * L
     ms_per_step = elapsed_ms / K
 
