@@ -10,7 +10,8 @@
 // staging of the token vectors with those loads, fetch per-neuron metadata with one lane per
 // neuron, and accumulate fp16 products in fp32 with v_dot2.  Their ALU work grows with the batch,
 // so from batch 3 (gated or Q4_0 rows) or 6 (plain fp16 rows) the sparse FFN runs on the MFMA
-// kernels of pi_wide.hpp instead; the predictor stays here.
+// kernels of pi_wide.hpp instead, and so does the predictor's second matrix from batch 3 (layers of
+// 16384 neurons or more) or 6.
 //
 // Kernels (all stream-ordered; none needs a host sync):
 //   k_pred_l1     z = max(0, P1 x)                   one workgroup per row of P1 (4 rows at batch >= 4)
