@@ -168,13 +168,23 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
     tokens = W + K
     x_all = synth.make_x_all(cfg, L, tokens, B)                 # [T][L][B][d] fp16 bits
     xd = torch.from_numpy(x_all.view(np.int16)).to(dev)
-    ws = layers[0].workspace(B, device=dev)
+    # one workspace per group of layers whose FFN descriptors agree (placed layers may hold different
+    # counts of neurons, and a workspace may serve several layers only when their shapes agree)
+    wss = {}
+
+    def ws_of(lay):
+        if lay.n_slots not in wss:
+            wss[lay.n_slots] = lay.workspace(B, device=dev)
+        return wss[lay.n_slots]
+
+    for lay in layers:
+        ws_of(lay)
     y = torch.empty((L, B, cfg.d), dtype=torch.float32, device=dev)
 
     def step(t):
         for l in range(L):
             lay = layers[l]
-            _abi.pi_ffn_layer(lay.pred, lay.ffn, xd[t, l], B, y[l], None, None, None, ws)
+            _abi.pi_ffn_layer(lay.pred, lay.ffn, xd[t, l], B, y[l], None, None, None, ws_of(lay))
 
     with torch.cuda.stream(stream):
         step(0)
@@ -195,8 +205,9 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
         torch.cuda.synchronize()
         del g_warm
         elapsed_ms, rep_ms = timed_graph(torch, stream, timed)
-    if _abi.workspace_status(ws) != 0:
-        raise RuntimeError(f"workspace status {_abi.workspace_status(ws)}: a cross-workgroup wait timed out")
+    for w in wss.values():
+        if _abi.workspace_status(w) != 0:
+            raise RuntimeError(f"workspace status {_abi.workspace_status(w)}: a cross-workgroup wait timed out")
 
     # ---- per-kernel legs.  pi_ffn_layer = pi_predict_hidden (z = ReLU(P1 x)) followed by
     # pi_ffn_layer_from_hidden (logits, mask and the sparse FFN).  An eager pass runs both on R tokens
@@ -213,10 +224,11 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
     masks = torch.empty((N, cfg.f), dtype=torch.uint8, device=dev)
     idx_all = torch.empty((N, cfg.f), dtype=torch.int32, device=dev)
     cnt_all = torch.empty((N, 2), dtype=torch.int32, device=dev)
-    ws_f = torch.zeros(_abi.pi_workspace_bytes(None, layers[0].ffn, B), dtype=torch.uint8, device=dev)
+    # placed layers may hold different counts of neurons: size for the largest
+    ws_f = torch.zeros(max(_abi.pi_workspace_bytes(None, lay.ffn, B) for lay in layers), dtype=torch.uint8,
+                       device=dev)
     y_chk = torch.empty((B, cfg.d), dtype=torch.float32, device=dev)
-    ns = layers[0].n_slots
-    ar = torch.arange(ns, device=dev)
+    ar = torch.arange(max(lay.n_slots for lay in layers), device=dev)
     cases = [(W + i // L, i % L) for i in range(N)]             # (token, layer) of launch i
 
     def run_hidden():
@@ -226,7 +238,7 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
     def run_rest():
         for i, (t, l) in enumerate(cases):
             _abi.pi_ffn_layer_from_hidden(layers[l].pred, layers[l].ffn, xd[t, l], B, z_all[i], y_chk, None, None,
-                                          None, ws)
+                                          None, ws_of(layers[l]))
 
     def run_sparse():
         for i, (t, l) in enumerate(cases):
@@ -236,12 +248,13 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
         run_hidden()
         for i, (t, l) in enumerate(cases):
             _abi.pi_ffn_layer_from_hidden(layers[l].pred, layers[l].ffn, xd[t, l], B, z_all[i], y_chk, masks[i],
-                                          idx_all[i], cnt_all[i], ws)
+                                          idx_all[i], cnt_all[i], ws_of(layers[l]))
         live = []
         for i, (t, l) in enumerate(cases):
             _abi.pi_sparse_ffn(layers[l].ffn, xd[t, l], B, idx_all[i], cnt_all[i], y_chk, ws_f)
+            ns = layers[l].n_slots
             h, ok = _abi.sparse_ffn_h(layers[l].ffn, B, ws_f, ns)
-            live.append(((h != 0).any(dim=0) & ok & (ar < cnt_all[i, 0])).sum())
+            live.append(((h != 0).any(dim=0) & ok & (ar[:ns] < cnt_all[i, 0])).sum())
         torch.cuda.synchronize()
         n_live = torch.stack(live).cpu().numpy().astype(np.float64)
         cnt_host = cnt_all.cpu().numpy().astype(np.float64)
@@ -249,7 +262,7 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
         for name, fn in (("hidden", run_hidden), ("rest", run_rest), ("sparse_ffn", run_sparse)):
             ms, _ = timed_graph(torch, stream, fn)
             leg_us[name] = ms * 1000.0 / N
-    for w in (ws, ws_f):
+    for w in list(wss.values()) + [ws_f]:
         if _abi.workspace_status(w) != 0:
             raise RuntimeError("workspace status nonzero: a cross-workgroup wait timed out")
     n_act, n_pred = cnt_host[:, 0], cnt_host[:, 1]
@@ -335,11 +348,11 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
         "_rest": (float(rest_bytes.mean()), leg_us["rest"], rest_label, N),
     }
     if hots is not None:
-        rec["cold_host"] = cold_leg(torch, synth, _abi, cfg, layers, hots, B, x_all, xd, masks, cases, ws, stream,
+        rec["cold_host"] = cold_leg(torch, synth, _abi, cfg, layers, hots, B, x_all, xd, masks, cases, ws_of, stream,
                                     dev, ms_per_step)
     if wide and B == 1 and R >= 16 and layers[0].slot_of is None:
         rec["wide_b16"] = wide_leg(torch, _abi, cfg, layers, xd, masks, cases, stream, dev, in_rows, rb)
-    del xd, z_all, masks, idx_all, ws_f, ws
+    del xd, z_all, masks, idx_all, ws_f, wss
     return rec
 
 
@@ -374,7 +387,7 @@ def place_stack(synth, _abi, cfg, L):
                   "expected_us_per_token": round(t_exp * 1e6, 2)}
 
 
-def cold_leg(torch, synth, _abi, cfg, layers, hots, B, x_all, xd, masks, cases, ws, stream, dev, ms_per_step):
+def cold_leg(torch, synth, _abi, cfg, layers, hots, B, x_all, xd, masks, cases, ws_of, stream, dev, ms_per_step):
     """Host half of the hybrid split: the predicted neurons that are not resident, computed by
     pi_cold_ffn_host on the masks the device produced (first two layers), and the hybrid layer end
     to end (device layer -> mask to pinned host memory -> host half -> host y added on the device)."""
@@ -421,7 +434,8 @@ def cold_leg(torch, synth, _abi, cfg, layers, hots, B, x_all, xd, masks, cases, 
                     continue
                 torch.cuda.synchronize()
                 s0 = time.perf_counter()
-                _abi.pi_ffn_layer(layers[l].pred, layers[l].ffn, xd[t, l], B, y_dev, m_dev, None, None, ws)
+                _abi.pi_ffn_layer(layers[l].pred, layers[l].ffn, xd[t, l], B, y_dev, m_dev, None, None,
+                                  ws_of(layers[l]))
                 mask_pin.copy_(m_dev, non_blocking=True)
                 stream.synchronize()
                 _abi.pi_cold_ffn_host(hosts[l], np.ascontiguousarray(x_all[t, l]), B, mask_pin.numpy(),
