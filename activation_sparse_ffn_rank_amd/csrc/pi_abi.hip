@@ -109,7 +109,7 @@ WideGeom wide_geom(const pi_ffn *fn, int B) {
     g.lo = g.hi + align_up((size_t)kWideB * g.hs * 2);
     g.part = g.lo + align_up((size_t)kWideB * g.hs * 2);
     g.xmf = g.part + align_up((size_t)g.C * B * d * 4);
-    g.total = g.xmf + (fn->wtype == PI_Q4_0 ? align_up((size_t)d * 32) : 0);
+    g.total = g.xmf + align_up((size_t)wide_xmf_vectors(d, fn->wtype == PI_Q4_0) * 16);
     return g;
 }
 int check_wide_batch(int32_t B) { return (B >= 1 && B <= PI_MAX_WIDE_BATCH) ? PI_OK : PI_ERR_BATCH; }
@@ -303,7 +303,7 @@ bool pred_l2_staged(const pi_predictor *p, int B) {
 // x, d, xmf: with pred_l2_staged, also write x [B][d] in the Q4_0 up step's operand order to xmf.
 int enqueue_pred_l2(const pi_predictor *p, const float *z, int B, uint8_t *mask, float *logits, hipStream_t st,
                     uint32_t *bits = nullptr, const int32_t *slot_of = nullptr, int n_slots = 0,
-                    const void *x = nullptr, uint4 *xmf = nullptr) {
+                    const void *x = nullptr, uint4 *xmf = nullptr, bool xq4 = true) {
     if (B >= pred_mfma_from(p->d_ffn)) {
         const int r = p->rank, f = p->d_ffn;
         const uint16_t *p2 = static_cast<const uint16_t *>(p->p2), *c = static_cast<const uint16_t *>(p->c);
@@ -311,7 +311,7 @@ int enqueue_pred_l2(const pi_predictor *p, const float *z, int B, uint8_t *mask,
         if (r <= kPredL2StagedMaxRank)
             hipLaunchKernelGGL(k_pred_l2_mfma_s<8>, dim3(ceil_div(f, 16 * kPredL2Waves)), dim3(kPredL2Waves * kWave),
                                (size_t)ceil_div(r, 32) * 2 * kWave * 16, st, p2, c, z, B, r, f, logits, mask, bits,
-                               slot_of, n_slots, static_cast<const uint16_t *>(x), p->d_model, xmf);
+                               slot_of, n_slots, static_cast<const uint16_t *>(x), p->d_model, xq4 ? 1 : 0, xmf);
         else if (r >= 256)
             hipLaunchKernelGGL(k_pred_l2_mfma<8>, grid, dim3(256), 0, st, p2, c, z, B, r, f, logits, mask, bits, slot_of,
                                n_slots);
@@ -537,9 +537,17 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
     const uint8_t *w_in = static_cast<const uint8_t *>(fn->w_in);
     const uint16_t *xx = static_cast<const uint16_t *>(x), *b_up = static_cast<const uint16_t *>(fn->b_up);
     const dim3 up_grid(std::max(1, ceil_div(ns, 16)));
-    if (fn->wtype == PI_Q4_0) {
-        uint4 *xmf = reinterpret_cast<uint4 *>(w + g.xmf);
-        if (!xmf_ready) hipLaunchKernelGGL(k_wide_xmf, dim3(ceil_div(2 * d, 256)), dim3(256), 0, st, xx, B, d, xmf);
+    const bool q4 = fn->wtype == PI_Q4_0;
+    // x in the up step's operand order: always for Q4_0 rows; for fp16 rows when the predictor's grid
+    // wrote it, or past 8 tokens (a launch of its own costs more than it saves below that: measured,
+    // the 11008-neuron layer at 4 tokens 50.6 -> 53.5 us per layer; the 28672-neuron one at 16 tokens
+    // 158.7 -> 132.0, its 16 token rows 14336 bytes apart)
+    const bool use_xmf = q4 || xmf_ready || B > kGemvMaxBatch;
+    uint4 *xmf = reinterpret_cast<uint4 *>(w + g.xmf);
+    if (use_xmf && !xmf_ready)
+        hipLaunchKernelGGL(k_wide_xmf, dim3(ceil_div(wide_xmf_vectors(d, q4), 256)), dim3(256), 0, st, xx, B, d,
+                           q4 ? 1 : 0, xmf);
+    if (q4) {
         int cus = 0;
         if (wide_up_q4(fn, &cus)) {
             WideUpQ4Args ua{w_in, rb, d, B, f, ns, g.hs, fn->act, b_up, xmf, idx, fn->slot_of, h_hi, h_lo, status,
@@ -552,12 +560,12 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
                                tickets, g.S, fn->act, status);
     } else if (fn->gated) {
         hipLaunchKernelGGL((k_wide_up<true, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
-                           nullptr, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, fn->act,
-                           status);
+                           use_xmf ? xmf : nullptr, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs,
+                           tickets, g.S, fn->act, status);
     } else {
         hipLaunchKernelGGL((k_wide_up<false, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
-                           nullptr, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, tickets, g.S, fn->act,
-                           status);
+                           use_xmf ? xmf : nullptr, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs,
+                           tickets, g.S, fn->act, status);
     }
     const uint8_t *w_dn = static_cast<const uint8_t *>(fn->w_down_t);
     const uint16_t *b_dn = static_cast<const uint16_t *>(fn->b_down);
@@ -794,14 +802,16 @@ int layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const void *x
         if ((rc = enqueue_sparse(ffn, x, batch, nullptr, nullptr, y, L.ffn, st, L.bits))) return rc;
         return want_list ? enqueue_compact(mask, f, ffn->slot_of, idx, counts, st) : PI_OK;
     }
-    // the Q4_0 up step's copy of x comes from the predictor's grid when it runs k_pred_l2_mfma_s
+    // the up step's copy of x (MFMA form) comes from the predictor's grid when it runs k_pred_l2_mfma_s
     uint4 *xmf = nullptr;
-    if (ffn->wtype == PI_Q4_0 && sparse_wide(ffn, batch) && pred_l2_staged(pred, batch))
+    if (sparse_wide(ffn, batch) && pred_l2_staged(pred, batch))
         xmf = reinterpret_cast<uint4 *>(static_cast<char *>(L.ffn) + ctl_bytes(ffn->d_model) + wide_geom(ffn, batch).xmf);
     if (mask_words(f) <= 4096) {
         // the list from the predictor's flag words (unrestricted: the placement is applied while
         // listing), a 32-fold smaller read than the mask bytes
-        if ((rc = enqueue_pred_l2(pred, z, batch, mask, nullptr, st, L.bits, nullptr, f, x, xmf))) return rc;
+        if ((rc = enqueue_pred_l2(pred, z, batch, mask, nullptr, st, L.bits, nullptr, f, x, xmf,
+                                  ffn->wtype == PI_Q4_0)))
+            return rc;
         if (wide_up_from_bits(ffn, batch))                     // the up step lists the positions itself
             return enqueue_sparse(ffn, x, batch, idx, counts, y, L.ffn, st, nullptr, L.ctl + CTL_STATUS,
                                   xmf != nullptr, L.bits, idx, counts);
@@ -809,7 +819,8 @@ int layer_from_hidden(const pi_predictor *pred, const pi_ffn *ffn, const void *x
                            ffn->n_slots, idx, counts);
         if ((rc = launch_status())) return rc;
     } else {
-        if ((rc = enqueue_pred_l2(pred, z, batch, mask, nullptr, st, nullptr, nullptr, 0, x, xmf))) return rc;
+        if ((rc = enqueue_pred_l2(pred, z, batch, mask, nullptr, st, nullptr, nullptr, 0, x, xmf, ffn->wtype == PI_Q4_0)))
+            return rc;
         if ((rc = enqueue_compact(mask, f, ffn->slot_of, idx, counts, st))) return rc;
     }
     return enqueue_sparse(ffn, x, batch, idx, counts, y, L.ffn, st, nullptr, L.ctl + CTL_STATUS, xmf != nullptr);

@@ -15,9 +15,10 @@
 // the kernels use to make every lane's loads contiguous.
 //
 // Kernels (stream-ordered):
-//   k_wide_xmf   (Q4_0 rows) x copied once into the A-operand order of the up step's MFMAs, so that
-//                each of the up step's x loads is one contiguous 1 KB run for the wave (read in
-//                place, the 16 tokens' rows made every load touch 32 cache lines).
+//   k_wide_xmf   x copied once into the A-operand order of the up step's MFMAs (Q4_0 rows; fp16 rows
+//                past 8 tokens or when the predictor's grid does it), so that each of the up step's
+//                x loads is one contiguous 1 KB run for the wave (read in place, the 16 tokens'
+//                rows made every load touch 16 to 32 cache lines).
 //   k_wide_up    one workgroup per 16 listed neurons: H tile [16 tokens x 16 neurons] over all d,
 //                the eight waves taking interleaved 256-column blocks, summed in LDS; writes h
 //                as fp16 hi + fp16 lo parts (h = hi + lo to ~2^-22 relative), so that feeding h to
@@ -63,10 +64,23 @@ __device__ __forceinline__ void wide_xmf_vec(const uint16_t *__restrict__ x, int
     const int kq = v >> 8, i = (v >> 6) & 3, g = (v >> 4) & 3, r = v & 15;
     xmf[v] = r < B ? pair_for_q4(ld16(x + (size_t)r * d + (4 * kq + g) * 32 + 8 * i)) : zero4();
 }
-__global__ __launch_bounds__(256) void k_wide_xmf(const uint16_t *__restrict__ x, int B, int d,
+// The fp16-row counterpart: vector 64*k + L holds token L%16's columns 32k + 8(L/16) .. +8 (zeros for
+// a token >= B or columns past d), the A operand of k_wide_up's step k; 64*ceil(d/32) vectors.
+__device__ __forceinline__ void wide_xf16_vec(const uint16_t *__restrict__ x, int B, int d, uint4 *__restrict__ xmf,
+                                              int v) {
+    const int k = v >> 6, r = v & 15, col = 32 * k + 8 * ((v >> 4) & 3);
+    xmf[v] = (r < B && col < d) ? ld16(x + (size_t)r * d + col) : zero4();
+}
+// Vectors of the layout for either row kind (Q4_0: 2d; fp16: 64*ceil(d/32)).
+__host__ __device__ inline int wide_xmf_vectors(int d, bool q4) { return q4 ? 2 * d : 64 * ((d + 31) / 32); }
+
+__global__ __launch_bounds__(256) void k_wide_xmf(const uint16_t *__restrict__ x, int B, int d, int q4,
                                                   uint4 *__restrict__ xmf) {
     const int v = blockIdx.x * 256 + threadIdx.x;
-    if (v < 2 * d) wide_xmf_vec(x, B, d, xmf, v);
+    if (v < wide_xmf_vectors(d, q4 != 0)) {
+        if (q4) wide_xmf_vec(x, B, d, xmf, v);
+        else wide_xf16_vec(x, B, d, xmf, v);
+    }
 }
 
 // h[b][k] for the listed neurons, as fp16 hi and lo parts in [16][hs] arrays.  Workgroup t holds
@@ -163,7 +177,9 @@ __global__ __launch_bounds__(W * kWave) void k_wide_up(const uint8_t *__restrict
             } else {
                 wu[j] = ld16(row + off);
             }
-            xv[j] = bld16(xr, xrow + (ok ? (uint32_t)col * 2u : kOOB));
+            // (a step past d reads the last step's x, clamped in bounds; its weights are zeroed below)
+            xv[j] = xmf != nullptr ? ld16(xmf + min(blk / 32 + j, (d + 31) / 32 - 1) * kWave + lane)
+                                   : bld16(xr, xrow + (ok ? (uint32_t)col * 2u : kOOB));
         }
         const bool live = s >= 0;
 #pragma unroll
@@ -763,15 +779,15 @@ __global__ __launch_bounds__(W * kWave) void k_wide_down(const uint8_t *__restri
 // neurons.  Workgroups of kPredL2Waves waves own 16 * kPredL2Waves neurons; the P2 loads of two
 // 32*KC-column steps are in flight per wave (the first go out before the staging).  LDS: 64 r bytes
 // (r <= kPredL2StagedMaxRank).  With xmf != nullptr the grid also writes x [B][d] in the operand
-// order of the Q4_0 up step (k_wide_xmf's work, spread over the grid: the layer then needs no
-// launch of its own for it).
+// order of the up step (the Q4_0 layout if xq4, else the fp16 one: k_wide_xmf's work, spread over
+// the grid, so the layer needs no launch of its own for it).
 constexpr int kPredL2Waves = 8;
 constexpr int kPredL2StagedMaxRank = 1024;
 template <int KC>
 __global__ __launch_bounds__(kPredL2Waves * kWave) void k_pred_l2_mfma_s(
     const uint16_t *__restrict__ p2, const uint16_t *__restrict__ c, const float *__restrict__ z, int B, int r, int f,
     float *__restrict__ logits, uint8_t *__restrict__ mask, uint32_t *__restrict__ bits,
-    const int32_t *__restrict__ slot_of, int n_slots, const uint16_t *__restrict__ x, int d,
+    const int32_t *__restrict__ slot_of, int n_slots, const uint16_t *__restrict__ x, int d, int xq4,
     uint4 *__restrict__ xmf) {
     extern __shared__ __align__(16) uint4 zmf[];                       // [r/32][2][kWave]
     __shared__ uint32_t s_half[kPredL2Waves];
@@ -789,9 +805,13 @@ __global__ __launch_bounds__(kPredL2Waves * kWave) void k_pred_l2_mfma_s(
     };
     uint4 wa[KC], wb[KC];
     issue(wa, 0);
-    if (xmf != nullptr)
-        for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < 2 * d; v += gridDim.x * blockDim.x)
-            wide_xmf_vec(x, B, d, xmf, v);
+    if (xmf != nullptr) {
+        const int nv = wide_xmf_vectors(d, xq4 != 0);
+        for (int v = blockIdx.x * blockDim.x + threadIdx.x; v < nv; v += gridDim.x * blockDim.x) {
+            if (xq4) wide_xmf_vec(x, B, d, xmf, v);
+            else wide_xf16_vec(x, B, d, xmf, v);
+        }
+    }
     // staging: item (s, L) -> hi at zmf[2s*64 + L], lo at zmf[(2s+1)*64 + L]
     const __amdgpu_buffer_rsrc_t rz = buf_rsrc(z, (uint32_t)B * (uint32_t)r * 4u);
     const int steps = (r + 31) / 32;

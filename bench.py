@@ -155,6 +155,9 @@ def ffn_kernel_names(h_kind: int, B: int, cfg, synth):
         if cfg.wtype != synth.F16:                              # x re-laid out for the Q4_0 MFMA operands first
             return "k_wide_xmf + k_wide_up_q4 + k_wide_down", ["pik::k_wide_xmf(", "pik::k_wide_up_q4(",
                                                                "void pik::k_wide_down<"]
+        if B > 8:                                               # fp16 rows: x re-laid out past 8 tokens
+            return "k_wide_xmf + k_wide_up + k_wide_down", ["pik::k_wide_xmf(", "void pik::k_wide_up<",
+                                                            "void pik::k_wide_down<"]
         return "k_wide_up + k_wide_down", ["void pik::k_wide_up<", "void pik::k_wide_down<"]
     return f"kind {h_kind}", []
 
@@ -299,9 +302,11 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
         mfma = B >= (3 if cfg.f >= 16384 else 6)
         pl2 = ("k_pred_l2_mfma_s" if cfg.r <= 1024 else "k_pred_l2_mfma") if mfma else "k_pred_l2"
         in_label, in_prefixes = ffn_label, ffn_prefixes
-        q4_wide = bool(in_prefixes) and in_prefixes[0] == "pik::k_wide_xmf("
-        if mfma and cfg.r <= 1024 and q4_wide:
-            in_label, in_prefixes = in_label.replace("k_wide_xmf + ", ""), in_prefixes[1:]
+        q4_wide = h_kind == 3 and cfg.wtype != synth.F16
+        if mfma and cfg.r <= 1024 and h_kind == 3:
+            # the staged predictor's grid lays out x: no k_wide_xmf launch in the layer
+            in_label = in_label.replace("k_wide_xmf + ", "")
+            in_prefixes = [q for q in in_prefixes if q != "pik::k_wide_xmf("]
         # with every neuron resident, the Q4_0 up step lists the positions from the flag words itself
         cb_label, cb_prefixes = ("", []) if (q4_wide and hots is None) else ("k_compact_bits + ", ["pik::k_compact_bits("])
         rest_label = f"{pl2} + {cb_label}{in_label}"
