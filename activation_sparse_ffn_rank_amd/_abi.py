@@ -241,12 +241,13 @@ def sparse_ffn_h(ffn, batch: int, ws: torch.Tensor, n: int) -> tuple[torch.Tenso
         h = ws[off: off + 4 * batch * f].view(torch.float32).view(batch, f)[:, :n]
         return h, torch.ones(n, dtype=torch.bool, device=ws.device)
     if kind == 3:
-        # MFMA form: h = hi + lo, fp16 [16][hs] each, hs = n_slots rounded up to 32, lo 256-aligned after hi
+        # MFMA form: 16-byte units [hs/4][16 tokens] of (4 fp16 hi, 4 fp16 lo) for 4 positions each,
+        # hs = n_slots rounded up to 32
         hs = (max(int(ffn.n_slots), 1) + 31) // 32 * 32
-        lo_off = off + (32 * hs + 255) // 256 * 256
-        hi = ws[off: off + 2 * batch * hs].view(torch.float16).view(batch, hs)[:, :n].float()
-        lo = ws[lo_off: lo_off + 2 * batch * hs].view(torch.float16).view(batch, hs)[:, :n].float()
-        return hi + lo, torch.ones(n, dtype=torch.bool, device=ws.device)
+        t = ws[off: off + 64 * hs].view(torch.float16).view(hs // 4, 16, 8)
+        h = (t[:, :batch, :4].float() + t[:, :batch, 4:].float())       # [hs/4][batch][4]
+        h = h.permute(1, 0, 2).reshape(batch, hs)[:, :n]
+        return h, torch.ones(n, dtype=torch.bool, device=ws.device)
     stride = max(int(ffn.n_slots), 1)
     h = ws[off: off + 4 * batch * stride].view(torch.float32).view(batch, stride)[:, :n]
     return h, torch.ones(n, dtype=torch.bool, device=ws.device)

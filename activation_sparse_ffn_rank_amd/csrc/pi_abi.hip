@@ -86,8 +86,8 @@ int x_chunk(int d, int B) {
 int down_slabs(int d) { return ceil_div(d, 512); }
 
 // Workspace of pi_sparse_ffn_wide: a status word (its first int32; 256 bytes reserved), slab
-// tickets, h as fp16 hi and lo parts [16][hs], the chunk partials [C][B][d] fp32, and for Q4_0 rows
-// x in k_wide_up's operand order (d*32 bytes).
+// tickets, h as fp16 hi and lo parts (the interleaved table of wide_h_store, 64*hs bytes over the
+// hi and lo regions), the chunk partials [C][B][d] fp32, and x in the up step's operand order.
 constexpr int kWideTargetGroups = 256;   // (slab, chunk) workgroups of k_wide_down (8 waves each)
 constexpr size_t kWideStatusBytes = 256;
 struct WideGeom {
@@ -99,9 +99,8 @@ WideGeom wide_geom(const pi_ffn *fn, int B) {
     const int d = fn->d_model;
     g.S = ceil_div(d, 16 * wide_down_cpl(fn->wtype == PI_Q4_0 ? WT_Q4_0 : WT_F16));
     g.C = std::min(kWideMaxChunks, std::max(1, ceil_div(kWideTargetGroups, g.S)));
-    // Q4_0 runs the XCD-grouped grid of k_wide_down, which takes a multiple of 8 chunks (measured on
-    // the 49152-neuron layer: 8 chunks and XCD groups 143.9 -> 133.3 us per layer at batch 8,
-    // 197.8 -> 180.0 at 16)
+    // room for the chunk partials of up to 8 chunks on Q4_0 rows (the launch itself takes as many
+    // chunks as fit one workgroup per compute unit, 5 at d = 12288)
     if (fn->wtype == PI_Q4_0) g.C = std::min(kWideMaxChunks, (g.C + 7) / 8 * 8);
     g.hs = ceil_div(std::max(fn->n_slots, 1), 32) * 32;    // k_wide_up writes whole 32-position groups
     g.tick = kWideStatusBytes;
@@ -530,7 +529,7 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
     const WideGeom g = wide_geom(fn, B);
     int32_t *tickets = reinterpret_cast<int32_t *>(w + g.tick);
     if (status == nullptr) status = reinterpret_cast<int32_t *>(w);
-    uint16_t *h_hi = reinterpret_cast<uint16_t *>(w + g.hi), *h_lo = reinterpret_cast<uint16_t *>(w + g.lo);
+    uint16_t *h_hi = reinterpret_cast<uint16_t *>(w + g.hi);     // the h table (hi and lo regions together)
     float *part = reinterpret_cast<float *>(w + g.part);
     const int d = fn->d_model, f = fn->d_ffn, ns = fn->n_slots;
     const int64_t rb = row_bytes_of(fn);
@@ -550,21 +549,21 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
     if (q4) {
         int cus = 0;
         if (wide_up_q4(fn, &cus)) {
-            WideUpQ4Args ua{w_in, rb, d, B, f, ns, g.hs, fn->act, b_up, xmf, idx, fn->slot_of, h_hi, h_lo, status,
+            WideUpQ4Args ua{w_in, rb, d, B, f, ns, g.hs, fn->act, b_up, xmf, idx, fn->slot_of, h_hi, status,
                             bits, mask_words(f), idx_w, counts_w};
             hipLaunchKernelGGL(k_wide_up_q4, dim3(cus), dim3(kWideUpWaves * kWave), 0, st, ua, counts, tickets, g.S);
         }
         else
             hipLaunchKernelGGL((k_wide_up<false, WT_Q4_0, 2>), dim3(std::max(1, ceil_div(ns, 32))), dim3(kWideThreads),
-                               0, st, w_in, rb, d, b_up, xx, xmf, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs,
+                               0, st, w_in, rb, d, b_up, xx, xmf, B, idx, counts, fn->slot_of, f, ns, h_hi, g.hs,
                                tickets, g.S, fn->act, status);
     } else if (fn->gated) {
         hipLaunchKernelGGL((k_wide_up<true, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
-                           use_xmf ? xmf : nullptr, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs,
+                           use_xmf ? xmf : nullptr, B, idx, counts, fn->slot_of, f, ns, h_hi, g.hs,
                            tickets, g.S, fn->act, status);
     } else {
         hipLaunchKernelGGL((k_wide_up<false, WT_F16, 1>), up_grid, dim3(kWideThreads), 0, st, w_in, rb, d, b_up, xx,
-                           use_xmf ? xmf : nullptr, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs,
+                           use_xmf ? xmf : nullptr, B, idx, counts, fn->slot_of, f, ns, h_hi, g.hs,
                            tickets, g.S, fn->act, status);
     }
     const uint8_t *w_dn = static_cast<const uint8_t *>(fn->w_down_t);
@@ -581,11 +580,11 @@ int enqueue_wide(const pi_ffn *fn, const void *x, int B, const int32_t *idx, con
         const int pairs = ceil_div(g.S, 8) * C;
         hipLaunchKernelGGL((k_wide_down<WT_Q4_0, kWideDownWaves>), dim3(64 * ceil_div(pairs, 8)),
                            dim3(kWideDownWaves * kWave), 0, st, w_dn, rb, d, B, idx, counts, fn->slot_of, f, ns, h_hi,
-                           h_lo, g.hs, part, C, tickets, b_dn, y, 1, g.S);
+                           g.hs, part, C, tickets, b_dn, y, 1, g.S);
     } else {
         // 12 waves (measured on the 11008-neuron layer at 16 tokens: 81.7 -> 79.7 us per layer)
         hipLaunchKernelGGL((k_wide_down<WT_F16, kWideDownWaves>), dim3(g.S, g.C), dim3(kWideDownWaves * kWave), 0, st,
-                           w_dn, rb, d, B, idx, counts, fn->slot_of, f, ns, h_hi, h_lo, g.hs, part, g.C, tickets, b_dn,
+                           w_dn, rb, d, B, idx, counts, fn->slot_of, f, ns, h_hi, g.hs, part, g.C, tickets, b_dn,
                            y, 0, g.S);
     }
     return launch_status();

@@ -83,7 +83,20 @@ __global__ __launch_bounds__(256) void k_wide_xmf(const uint16_t *__restrict__ x
     }
 }
 
-// h[b][k] for the listed neurons, as fp16 hi and lo parts in [16][hs] arrays.  Workgroup t holds
+// The table of h that the up kernels hand to k_wide_down, in the down step's operand order: for
+// list position k and token b, the 16-byte unit (k/4)*16 + b holds the fp16 hi parts of positions
+// 4(k/4) .. +3 of token b, then their lo parts (h = hi + lo to ~2^-22 relative).  A wave of the down
+// kernel then reads one contiguous 1 KB run per step (lane 16g + r: positions 4g .. 4g+3 of the
+// step, token r).  hs (positions, a multiple of 32) * 64 bytes.
+__device__ __forceinline__ void wide_h_store(uint16_t *__restrict__ hl, int b, int k, float hv) {
+    const f16 hi = (f16)hv;
+    const f16 lo = (f16)(hv - (float)hi);
+    uint16_t *u = hl + ((size_t)(k >> 2) * 16 + b) * 8 + (k & 3);
+    u[0] = __builtin_bit_cast(uint16_t, hi);
+    u[4] = __builtin_bit_cast(uint16_t, lo);
+}
+
+// h[b][k] for the listed neurons, as fp16 hi and lo parts in the table above.  Workgroup t holds
 // list positions 16t .. 16t+15; lane l of every wave works on position 16t + l%16 and token l%16
 // (the MFMA's n and m) and columns blk + 32j + 8(l/16) .. +8 of block blk (j < 8), so each of a
 // row's 16-byte loads is contiguous with the next lane group's.  Row loads are unconditional (slot
@@ -97,7 +110,7 @@ __global__ __launch_bounds__(W * kWave) void k_wide_up(const uint8_t *__restrict
                                                  const uint4 *__restrict__ xmf, int B, const int32_t *__restrict__ idx,
                                                  const int32_t *__restrict__ counts,
                                                  const int32_t *__restrict__ slot_of, int f, int n_slots,
-                                                 uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo, int hs,
+                                                 uint16_t *__restrict__ hl, int hs,
                                                  int32_t *__restrict__ zero_ptr, int nzero, int act,
                                                  int32_t *__restrict__ status) {
     __shared__ f4 red[GATED ? 2 : NT][W][kWave];
@@ -226,11 +239,7 @@ __global__ __launch_bounds__(W * kWave) void k_wide_up(const uint8_t *__restrict
     // h travels to the down kernel as an fp16 pair; beyond fp16's range the pair cannot hold it,
     // and y would not be finite: say so in the status word instead of failing silently
     if (!(fabsf(hv) < 65504.f)) atomicOr(status, kStatusHRange);
-    const int pt = pos + 16 * tile;
-    const f16 hi = (f16)hv;
-    const f16 lo = (f16)(hv - (float)hi);
-    h_hi[(size_t)b * hs + pt] = __builtin_bit_cast(uint16_t, hi);
-    h_lo[(size_t)b * hs + pt] = __builtin_bit_cast(uint16_t, lo);
+    wide_h_store(hl, b, pos + 16 * tile, hv);                   // pos + 16 tile < hs
 }
 
 // The Q4_0 form of k_wide_up on a grid of one kWideUpWaves-wave workgroup per compute unit: the
@@ -250,7 +259,7 @@ struct WideUpQ4Args {
     const uint16_t *b_up;
     const uint4 *xmf;
     const int32_t *idx, *slot_of;
-    uint16_t *h_hi, *h_lo;
+    uint16_t *hl;                           // the h table (wide_h_store)
     int32_t *status;
     // positions from the predictor's listed-flag words instead of idx/counts (every neuron resident,
     // slot = id): each workgroup counts the set bits of all nwords words, takes its run and writes
@@ -337,13 +346,7 @@ __device__ __forceinline__ void wide_up_q4_pass(const WideUpQ4Args &a, __amdgpu_
         if (a.act) hv *= hv;                                     // squared ReLU
         if (st < 0 || b >= a.B) hv = 0.f;
         if (!(fabsf(hv) < 65504.f)) atomicOr(a.status, kStatusHRange);
-        if (t0 + tile < t_hi) {
-            const int pt = (t0 + tile) * 16 + r;
-            const f16 hi = (f16)hv;
-            const f16 lo = (f16)(hv - (float)hi);
-            a.h_hi[(size_t)b * a.hs + pt] = __builtin_bit_cast(uint16_t, hi);
-            a.h_lo[(size_t)b * a.hs + pt] = __builtin_bit_cast(uint16_t, lo);
-        }
+        if (t0 + tile < t_hi) wide_h_store(a.hl, b, (t0 + tile) * 16 + r, hv);
     }
     __syncthreads();                                             // red is refilled by the next pass
 }
@@ -603,8 +606,7 @@ __global__ __launch_bounds__(W * kWave) void k_wide_down(const uint8_t *__restri
                                                             int d, int B, const int32_t *__restrict__ idx,
                                                             const int32_t *__restrict__ counts,
                                                             const int32_t *__restrict__ slot_of, int f, int n_slots,
-                                                            const uint16_t *__restrict__ h_hi,
-                                                            const uint16_t *__restrict__ h_lo, int hs,
+                                                            const uint16_t *__restrict__ hl, int hs,
                                                             float *__restrict__ part, int C,
                                                             int32_t *__restrict__ tickets,
                                                             const uint16_t *__restrict__ b_down,
@@ -662,9 +664,9 @@ __global__ __launch_bounds__(W * kWave) void k_wide_down(const uint8_t *__restri
                     qs[q][v] = *reinterpret_cast<const uint16_t *>(rw + d / 2 + (cq / 32) * 2);
                 }
             }
-            const size_t ho = (size_t)r * hs + (size_t)sq * 16 + 4 * g;
-            ahi[q] = *reinterpret_cast<const uint2 *>(h_hi + ho);
-            alo[q] = *reinterpret_cast<const uint2 *>(h_lo + ho);
+            const uint4 hv = ld16(hl + ((size_t)(sq * 4 + g) * 16 + r) * 8);   // positions 4g..4g+3, token r
+            ahi[q] = make_uint2(hv.x, hv.y);
+            alo[q] = make_uint2(hv.z, hv.w);
         }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {

@@ -200,8 +200,10 @@ int pi_layer_path(const pi_predictor *pred, const pi_ffn *ffn, int32_t batch);
  * Returns the byte offset of the table inside a pi_sparse_ffn workspace and sets *kind:
  *  1 = slab x chunk kernels (batch <= 2): fp32 h at offset + 4*(b*d_ffn + k);
  *  2 = two-kernel form: fp32 h at offset + 4*(b*max(n_slots, 1) + k);
- *  3 = MFMA form (the batches named above): h = hi + lo, fp16 hi at offset + 2*(b*hs + k) and fp16 lo at
- *      offset + L + 2*(b*hs + k), hs = max(n_slots, 1) rounded up to 32, L = 32*hs rounded up to 256.
+ *  3 = MFMA form (the batches named above): h = hi + lo, in 16-byte units: unit u = (k/4)*16 + b at
+ *      offset + 16*u holds the fp16 hi parts of positions 4(k/4) .. +3 of token b, then their fp16
+ *      lo parts (hi at offset + 16*u + 2*(k%4), lo 8 bytes further); max(n_slots, 1) rounded up to 32
+ *      positions (64 bytes each).
  * Positions k >= counts[0] hold stale values.  Returns (size_t)-1 on invalid arguments. */
 size_t pi_sparse_ffn_h_offset(const pi_ffn *ffn, int32_t batch, int32_t *kind);
 

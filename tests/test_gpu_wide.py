@@ -218,3 +218,41 @@ def test_h_beyond_fp16_range_is_reported(gated, wtype, entry):
             torch.cuda.synchronize()
             st = _abi.workspace_status(ws)
         assert bool(st & _abi.PI_STATUS_H_RANGE) == expect, (listed.tolist(), st)
+
+
+@pytest.mark.parametrize("d,f,gated,wtype,B", [(1024, 900, False, F16, 8), (512, 700, True, F16, 5),
+                                                (2048, 600, False, Q4, 16), (264, 333, False, F16, 12)])
+def test_h_table_matches_the_listed_rows(d, f, gated, wtype, B):
+    """The diagnostic h table of the MFMA form (pi_sparse_ffn_h_offset kind 3, read by
+    _abi.sparse_ffn_h) holds, for list position k and token b, the neuron's h: act(W_in x_b + b_up) or
+    max(0, W_gate x_b) (W_up x_b), from the rows decoded by the oracle, in fp64."""
+    announce(f"h table d={d} f={f} gated={gated} wtype={wtype} B={B}")
+    cfg, w_in, w_dn, b_up, b_down = _layer(d, f, gated, 0, seed=900 + d + B, wtype=wtype)
+    dl = DeviceLayer(p1=np.zeros((8, d), np.uint16), p2=np.zeros((f, 8), np.uint16), c=np.zeros(f, np.uint16),
+                     w_in=w_in, w_down_t=w_dn, d_model=d, d_ffn=f, gated=gated, wtype=wtype, b_up=b_up, b_down=b_down)
+    rng = np.random.default_rng(d * 7 + B)
+    idx = np.sort(rng.choice(f, size=f // 3, replace=False)).astype(np.int32)
+    x = synth.normal_f16(5, 0, synth.T_X, B, d, 1.0)
+    ws = torch.zeros(_abi.pi_workspace_bytes(None, dl.ffn, B), dtype=torch.uint8, device="cuda")
+    assert _abi.pi_sparse_ffn_h_offset(dl.ffn, B)[1] == 3                # the MFMA form runs
+    y = torch.empty((B, d), dtype=torch.float32, device="cuda")
+    counts = to_dev(np.array([idx.size, idx.size], np.int32))
+    _abi.pi_sparse_ffn(dl.ffn, to_dev(x), B, to_dev(idx), counts, y, ws)
+    torch.cuda.synchronize()
+    h, ok = _abi.sparse_ffn_h(dl.ffn, B, ws, idx.size)
+    h = h.cpu().numpy().astype(np.float64)
+    xf = np.array([[oracle.half(int(v)) for v in row] for row in x], np.float64)      # [B][d]
+    rb = oracle.row_bytes(wtype, d)
+    ref = np.empty((B, idx.size))
+    for k, i in enumerate(idx):
+        row = w_in[i].view(np.uint8)
+        if gated:
+            g_ = xf @ oracle.decode_row(row[:rb], wtype, d)
+            u_ = xf @ oracle.decode_row(row[rb:2 * rb], wtype, d)
+            ref[:, k] = np.maximum(g_, 0.0) * u_
+        else:
+            u_ = xf @ oracle.decode_row(row[:rb], wtype, d) + oracle.half(int(b_up[i]))
+            ref[:, k] = np.maximum(u_, 0.0)
+    scale = max(1.0, float(np.abs(ref).max()))
+    assert bool(ok.all())
+    assert np.abs(h - ref).max() <= 2e-3 * scale, np.abs(h - ref).max()
