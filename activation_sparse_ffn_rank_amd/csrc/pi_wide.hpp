@@ -640,12 +640,19 @@ __global__ __launch_bounds__(W * kWave) void k_wide_down(const uint8_t *__restri
 #pragma unroll
     for (int e = 0; e < CPL; ++e) acc[e] = f4{0.f, 0.f, 0.f, 0.f};
 
-    for (int st0 = w_lo; st0 < w_hi; st0 += 4) {                 // four steps per slot lookup
-        const int p = st0 * 16 + lane;                           // this lane's lookup position
-        const int sl = (p < w_hi * 16 && p < n) ? slot_of_id(idx[p], slot_of, f, n_slots) : -1;
+    const __amdgpu_buffer_rsrc_t rh = buf_rsrc(hl, (uint32_t)hs * 64u);          // the h table
+    // slots are looked up 64 positions (four steps) at a time, one lane per position; the lookup of
+    // the next four steps goes out right after this step's row loads
+    auto lookup = [&](int s0) {
+        const int p = s0 * 16 + lane;
+        return (p < w_hi * 16 && p < n) ? slot_of_id(idx[p], slot_of, f, n_slots) : -1;
+    };
+    int sl_next = lookup(w_lo);
+    for (int st0 = w_lo; st0 < w_hi; st0 += 4) {
+        const int sl = sl_next;
         // every load of the four steps goes out before the first MFMA; a step past the wave's run
         // (its positions looked up as -1) reads slot 0 and the last valid step's h, and is zeroed
-        int sv[4][4];
+        uint32_t okm = 0u;                                       // bit 4q + v: row (q, v) listed and resident
         uint4 wv[4][4];                                          // fp16: 8 columns
         uint2 qc[4][4];                                          // Q4_0: 16 columns of codes
         uint32_t qs[4][4];                                       // Q4_0: their block scale
@@ -655,8 +662,9 @@ __global__ __launch_bounds__(W * kWave) void k_wide_down(const uint8_t *__restri
             const int sq = min(st0 + q, w_hi - 1);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                sv[q][v] = __shfl(sl, q * 16 + 4 * g + v);
-                const uint8_t *rw = w_dn + (int64_t)(sv[q][v] >= 0 ? sv[q][v] : 0) * row_bytes;
+                const int sqv = __shfl(sl, q * 16 + 4 * g + v);
+                okm |= (sqv >= 0 ? 1u : 0u) << (4 * q + v);
+                const uint8_t *rw = w_dn + (int64_t)(sqv >= 0 ? sqv : 0) * row_bytes;
                 if (WT == WT_F16) {
                     wv[q][v] = ld16(rw + (int64_t)cq * 2);
                 } else {
@@ -664,10 +672,11 @@ __global__ __launch_bounds__(W * kWave) void k_wide_down(const uint8_t *__restri
                     qs[q][v] = *reinterpret_cast<const uint16_t *>(rw + d / 2 + (cq / 32) * 2);
                 }
             }
-            const uint4 hv = ld16(hl + ((size_t)(sq * 4 + g) * 16 + r) * 8);   // positions 4g..4g+3, token r
+            const uint4 hv = bld16(rh, ((uint32_t)(sq * 4 + g) * 16u + (uint32_t)r) * 16u);  // positions 4g..+3, token r
             ahi[q] = make_uint2(hv.x, hv.y);
             alo[q] = make_uint2(hv.z, hv.w);
         }
+        sl_next = lookup(st0 + 4);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             if (st0 + q >= w_hi) {                               // wave-uniform
@@ -677,7 +686,7 @@ __global__ __launch_bounds__(W * kWave) void k_wide_down(const uint8_t *__restri
             uint32_t wq[4][NW];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
-                const bool okv = sv[q][v] >= 0 && colok;
+                const bool okv = ((okm >> (4 * q + v)) & 1u) && colok;
                 if (WT == WT_F16) {
                     const uint4 u = okv ? wv[q][v] : zero4();
                     wq[v][0] = u.x; wq[v][1] = u.y; wq[v][2] = u.z; wq[v][3] = u.w;
