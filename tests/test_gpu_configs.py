@@ -18,7 +18,7 @@ from gpu_util import announce, check_layer_against_oracle
 
 pytestmark = pytest.mark.gpu
 
-CASES = [(2, 1), (3, 1), (3, 4), (4, 1), (5, 1), (5, 8)]
+CASES = [(2, 1), (2, 16), (3, 1), (3, 4), (4, 1), (5, 1), (5, 8), (5, 16)]
 
 
 @pytest.fixture(scope="module", autouse=True)
