@@ -162,6 +162,39 @@ def ffn_kernel_names(h_kind: int, B: int, cfg, synth):
     return f"kind {h_kind}", []
 
 
+def layer_kernel_names(path: int, h_kind: int, B: int, cfg, synth, placed: bool):
+    """(label, rocprof name prefixes) of the kernels one pi_ffn_layer_from_hidden call runs (the layer
+    after the first predictor matrix), by the layer's path and its sparse FFN form."""
+    ffn_label, ffn_prefixes = ffn_kernel_names(h_kind, B, cfg, synth)
+    g = "true" if cfg.gated else "false"
+    w = 1 if cfg.wtype == synth.F16 else 2
+    if path == 1:
+        rest_label, rest_prefixes = "k_layer_tail", [f"void pik::k_layer_tail<{B}, {g}, {w},"]
+    elif h_kind == 1:
+        # the layer's own form at batch <= 2: logits, mask and up rows in one kernel, then the down
+        # rows on h by neuron id
+        rest_label = "k_pred_up + k_down_split + k_sum_split"
+        rest_prefixes = [f"void pik::k_pred_up<{B}, {g}, {w},", f"void pik::k_down_split<{B}, {g}, {w}, true>",
+                         "pik::k_sum_split("]
+    else:
+        # the second predictor matrix on MFMA from batch 3 (d_ffn >= 16384) or 6 (z staged in LDS up
+        # to rank 1024), then the list from its flag words; the staged kernel's grid also lays out x
+        # for the Q4_0 up step, so the layer runs no k_wide_xmf of its own
+        mfma = B >= (3 if cfg.f >= 16384 else 6)
+        pl2 = ("k_pred_l2_mfma_s" if cfg.r <= 1024 else "k_pred_l2_mfma") if mfma else "k_pred_l2"
+        in_label, in_prefixes = ffn_label, ffn_prefixes
+        q4_wide = h_kind == 3 and cfg.wtype != synth.F16
+        if mfma and cfg.r <= 1024 and h_kind == 3:
+            # the staged predictor's grid lays out x: no k_wide_xmf launch in the layer
+            in_label = in_label.replace("k_wide_xmf + ", "")
+            in_prefixes = [q for q in in_prefixes if q != "pik::k_wide_xmf("]
+        # with every neuron resident, the Q4_0 up step lists the positions from the flag words itself
+        cb_label, cb_prefixes = ("", []) if (q4_wide and not placed) else ("k_compact_bits + ", ["pik::k_compact_bits("])
+        rest_label = f"{pl2} + {cb_label}{in_label}"
+        rest_prefixes = [f"void pik::{pl2}<"] + cb_prefixes + in_prefixes
+    return rest_label, rest_prefixes
+
+
 # ---------------------------------------------------------------------------------- one workload
 
 def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=False, hots=None):
@@ -285,32 +318,7 @@ def measure(torch, synth, _abi, cfg, layers, B, W, K, R, dev, stream, *, wide=Fa
                   + vec_bytes)
     hidden_bytes = 2 * cfg.r * cfg.d + 2 * B * cfg.d + 4 * B * cfg.r
     ffn_label, ffn_prefixes = ffn_kernel_names(h_kind, B, cfg, synth)
-    g = "true" if cfg.gated else "false"
-    w = 1 if cfg.wtype == synth.F16 else 2
-    if path == 1:
-        rest_label, rest_prefixes = "k_layer_tail", [f"void pik::k_layer_tail<{B}, {g}, {w},"]
-    elif h_kind == 1:
-        # the layer's own form at batch <= 2: logits, mask and up rows in one kernel, then the down
-        # rows on h by neuron id
-        rest_label = "k_pred_up + k_down_split + k_sum_split"
-        rest_prefixes = [f"void pik::k_pred_up<{B}, {g}, {w},", f"void pik::k_down_split<{B}, {g}, {w}, true>",
-                         "pik::k_sum_split("]
-    else:
-        # the second predictor matrix on MFMA from batch 3 (d_ffn >= 16384) or 6 (z staged in LDS up
-        # to rank 1024), then the list from its flag words; the staged kernel's grid also lays out x
-        # for the Q4_0 up step, so the layer runs no k_wide_xmf of its own
-        mfma = B >= (3 if cfg.f >= 16384 else 6)
-        pl2 = ("k_pred_l2_mfma_s" if cfg.r <= 1024 else "k_pred_l2_mfma") if mfma else "k_pred_l2"
-        in_label, in_prefixes = ffn_label, ffn_prefixes
-        q4_wide = h_kind == 3 and cfg.wtype != synth.F16
-        if mfma and cfg.r <= 1024 and h_kind == 3:
-            # the staged predictor's grid lays out x: no k_wide_xmf launch in the layer
-            in_label = in_label.replace("k_wide_xmf + ", "")
-            in_prefixes = [q for q in in_prefixes if q != "pik::k_wide_xmf("]
-        # with every neuron resident, the Q4_0 up step lists the positions from the flag words itself
-        cb_label, cb_prefixes = ("", []) if (q4_wide and hots is None) else ("k_compact_bits + ", ["pik::k_compact_bits("])
-        rest_label = f"{pl2} + {cb_label}{in_label}"
-        rest_prefixes = [f"void pik::{pl2}<"] + cb_prefixes + in_prefixes
+    rest_label, rest_prefixes = layer_kernel_names(path, h_kind, B, cfg, synth, placed=hots is not None)
     step_bytes = (pred_bytes + float(ffn_touched.mean())) * L
     ms_per_step = elapsed_ms / K
 
