@@ -38,7 +38,7 @@ int launch_down_sum(SplitArgs &a, hipStream_t st) {
     else
         hipLaunchKernelGGL((k_down_split<B, GATED, WT, false>), dim3(a.S * a.C), dim3(kSplitThreads), lds, st, a);
     if (hipGetLastError() != hipSuccess) return 1;
-    hipLaunchKernelGGL(k_sum_split, dim3((Bd + kSplitThreads - 1) / kSplitThreads), dim3(kSplitThreads), 0, st,
+    hipLaunchKernelGGL(k_sum_split, dim3((Bd + kWave - 1) / kWave), dim3(kWave), 0, st,
                        a.ypart, a.C, Bd, a.d, a.b_down, a.y);
     return hipGetLastError() == hipSuccess ? 0 : 1;
 }
